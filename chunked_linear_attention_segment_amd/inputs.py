@@ -1,0 +1,154 @@
+"""Seeded synthetic inputs for the Memory Caching prefill / decode workloads.
+
+This module only draws random numbers and rounds them to the storage dtype; it holds
+none of the method's arithmetic.  It serves both the HIP path and the CPU oracle, which
+receive exactly the same values (bf16 values are carried here as float32 arrays whose
+entries are exactly representable in bf16).
+
+Recipes (shapes follow the workloads of the Memory Caching paper's experiments: context
+lengths up to 64K, segment lengths 64..512, head dim 64/128):
+  "proj"   x ~ N(0,1) [B,L,d_in] shared by the heads; per head W_q, W_k, W_v, W_u ~
+           N(0, 1/d_in); q, k, v, u = x W (the input projections of Eq. 4a / Eq. 10).
+  "l2norm" q, k ~ N(0,1) then L2-normalised per token per head; v ~ N(0,1);
+           x ~ N(0,1) shared; u = x W_u with W_u ~ N(0, 1/d_in).
+Draw order for a seed: x, then W_q, W_k, W_v, W_u (proj) or q, k, v, W_u (l2norm).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    L: int
+    d_k: int
+    d_v: int
+    d_g: int
+    seg_len: int
+    phi: str = "identity"       # "identity" | "elu1"
+    dtype: str = "bf16"         # "f32" | "bf16"
+    x_heads: int = 1            # 1: X shared by heads; H: per-head X
+    recipe: str = "proj"        # "proj" | "l2norm"
+    top_k: int = 0              # SSC only
+    op: str = "grm"             # "grm" | "ssc" | "decode"
+    # decode only
+    n_cached: int = 0
+    count_on: int = 0
+
+
+WORKLOADS = {
+    "grm_f32_L512": Workload("grm_f32_L512", 1, 1, 512, 64, 64, 64, 64, "identity", "f32"),
+    "grm_bf16_L4K_elu": Workload("grm_bf16_L4K_elu", 4, 16, 4096, 128, 128, 128, 256, "elu1"),
+    "ssc_bf16_L16K_k4": Workload("ssc_bf16_L16K_k4", 2, 16, 16384, 128, 128, 128, 256,
+                                 "identity", top_k=4, op="ssc"),
+    "grm_bf16_L64K": Workload("grm_bf16_L64K", 1, 32, 65536, 128, 128, 128, 512, "identity",
+                              recipe="l2norm"),
+    "decode_bf16_64x32_n256": Workload("decode_bf16_64x32_n256", 64, 32, 1, 128, 128, 128, 256,
+                                       "identity", op="decode", n_cached=256, count_on=100,
+                                       recipe="l2norm"),
+}
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returned as float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def _store(a: np.ndarray, dtype: str) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return round_bf16(a) if dtype == "bf16" else a
+
+
+def _l2n(a: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(a.astype(np.float64) ** 2, axis=-1, keepdims=True))
+    return (a / np.maximum(n, 1e-30)).astype(np.float32)
+
+
+def make_prefill(w: Workload, seed: int = 0, L: int | None = None, B: int | None = None,
+                 H: int | None = None) -> dict:
+    """Q, K [B,H,L,dk]; V [B,H,L,dv]; U [B,H,L,dg]; X [B,xh,L,dg] as float32 arrays.
+
+    L, B, H may override the workload's sizes (same recipe, smaller draw)."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    L = w.L if L is None else L
+    rng = np.random.default_rng(seed)
+    din = w.d_g
+    xh = 1 if w.x_heads == 1 else H
+    x = rng.standard_normal((B, xh, L, din), dtype=np.float32)
+    sd = np.float32(1.0 / np.sqrt(din))
+    if w.recipe == "proj":
+        Wq = rng.standard_normal((H, din, w.d_k), dtype=np.float32) * sd
+        Wk = rng.standard_normal((H, din, w.d_k), dtype=np.float32) * sd
+        Wv = rng.standard_normal((H, din, w.d_v), dtype=np.float32) * sd
+        Wu = rng.standard_normal((H, din, w.d_g), dtype=np.float32) * sd
+        xs = x if xh == H else np.broadcast_to(x, (B, H, L, din))
+        q = np.einsum("bhld,hde->bhle", xs, Wq, optimize=True)
+        k = np.einsum("bhld,hde->bhle", xs, Wk, optimize=True)
+        v = np.einsum("bhld,hde->bhle", xs, Wv, optimize=True)
+        u = np.einsum("bhld,hde->bhle", xs, Wu, optimize=True)
+    elif w.recipe == "l2norm":
+        q = _l2n(rng.standard_normal((B, H, L, w.d_k), dtype=np.float32))
+        k = _l2n(rng.standard_normal((B, H, L, w.d_k), dtype=np.float32))
+        v = rng.standard_normal((B, H, L, w.d_v), dtype=np.float32)
+        Wu = rng.standard_normal((H, din, w.d_g), dtype=np.float32) * sd
+        u = np.empty((B, H, L, w.d_g), dtype=np.float32)
+        for h in range(H):
+            xb = x[:, 0 if xh == 1 else h]
+            u[:, h] = xb @ Wu[h]
+    else:
+        raise ValueError(w.recipe)
+    return {"Q": _store(q, w.dtype), "K": _store(k, w.dtype), "V": _store(v, w.dtype),
+            "U": _store(u, w.dtype), "X": _store(x, w.dtype)}
+
+
+def make_decode(w: Workload, seed: int = 0, B: int | None = None, H: int | None = None,
+                n_cap: int | None = None, n_cached: int | None = None,
+                count_on: int | None = None) -> dict:
+    """Host-side decode inputs (small sizes; the full-size cache is drawn on the device).
+
+    Cache (stored in the workload dtype): M^(i) ~ N(0, C/d) (a sum of C products of unit-norm k and
+    N(0,1) v); P_i ~ N(0, 1/C); online M_on ~ N(0, c/d) fp32 and x sum ~ N(0, c) for
+    c = count_on tokens already in the online segment.  New token: q, k unit-norm,
+    v, x ~ N(0,1), u = x W_u with W_u ~ N(0, 1/d)."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    n = w.n_cached if n_cached is None else n_cached
+    cap = (n + 2) if n_cap is None else n_cap
+    cnt = w.count_on if count_on is None else count_on
+    C, dk, dv, dg = w.seg_len, w.d_k, w.d_v, w.d_g
+    xh = 1 if w.x_heads == 1 else H
+    rng = np.random.default_rng(seed)
+    Mc = np.zeros((B, H, cap, dv, dk), dtype=np.float32)
+    Mc[:, :, :n] = rng.standard_normal((B, H, n, dv, dk), dtype=np.float32) * np.float32(
+        np.sqrt(C / dk))
+    Mc = _store(Mc, w.dtype)
+    Pc = np.zeros((B, xh, cap, dg), dtype=np.float32)
+    Pc[:, :, :n] = rng.standard_normal((B, xh, n, dg), dtype=np.float32) * np.float32(
+        1.0 / np.sqrt(C))
+    M_on = rng.standard_normal((B, H, dv, dk), dtype=np.float32) * np.float32(
+        np.sqrt(max(cnt, 0) / dk))
+    xsum = rng.standard_normal((B, xh, dg), dtype=np.float32) * np.float32(np.sqrt(max(cnt, 0)))
+    if cnt == 0:
+        M_on[:] = 0
+        xsum[:] = 0
+    x = rng.standard_normal((B, xh, dg), dtype=np.float32)
+    q = _l2n(rng.standard_normal((B, H, dk), dtype=np.float32))
+    k = _l2n(rng.standard_normal((B, H, dk), dtype=np.float32))
+    v = rng.standard_normal((B, H, dv), dtype=np.float32)
+    Wu = rng.standard_normal((H, dg, dg), dtype=np.float32) * np.float32(1.0 / np.sqrt(dg))
+    u = np.empty((B, H, dg), dtype=np.float32)
+    for h in range(H):
+        u[:, h] = x[:, 0 if xh == 1 else h] @ Wu[h]
+    st = w.dtype
+    return {"q": _store(q, st), "k": _store(k, st), "v": _store(v, st), "u": _store(u, st),
+            "x": _store(x, st), "M_on": M_on, "xsum": xsum, "count": cnt,
+            "M_cache": Mc, "P_cache": Pc, "n_cached": n}

@@ -1,0 +1,330 @@
+"""Pins for the fp64 oracle: each checks it against something other than itself.
+
+Every test here runs on the CPU.  The pins are chosen so that a plausible slip in the
+oracle (a dropped term, a wrong sign or index, a transposed operand, read-before-update,
+an off-by-one segment, the wrong pool) fails at least one of them:
+
+  worked examples   hand-derived values (tests/golden/*.json)
+  N = 1             plain causal linear attention (the RNN end point of the segmentation)
+  residual          ungated residual memory collapses to plain linear attention for matrix
+                    memory (the sum of the segment states is the full state)
+  SSC, k >= N-1     equals GRM
+  brute force       token-pair form y_t = sum_{r<=t} gamma_t^{seg(r)} (q_t.k_r) v_r, L <= 64
+  C = 1             softmax attention with queries u, keys x (torch SDPA)
+  segment-constant  block-causal softmax attention over segment keys (torch SDPA)
+  U = 0             uniform gate: y_t = LA_t / (s+1)
+  soup              Memory Soup equals GRM for linear memory
+  invariants        simplex gate, linearity in V, head independence, causality
+  decode            prefill(L) + one decode step == last row of prefill(L+1)
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _phi(z, phi):
+    return z if phi == "identity" else np.where(z > 0, z + 1.0, np.exp(np.minimum(z, 0.0)))
+
+
+def _causal_la(Q, K, V, phi="identity"):
+    """Textbook causal unnormalised linear attention, attention form, per (b, h)."""
+    qh, kh = _phi(Q, phi), _phi(K, phi)
+    L = Q.shape[-2]
+    S = qh @ np.swapaxes(kh, -1, -2)
+    S = S * np.tril(np.ones((L, L)))
+    return S @ V
+
+
+def _rand(B, H, L, dk, dv, dg, xh=1, seed=0, scale_u=1.0):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((B, H, L, dk))
+    K = rng.standard_normal((B, H, L, dk))
+    V = rng.standard_normal((B, H, L, dv))
+    U = rng.standard_normal((B, H, L, dg)) * scale_u
+    X = rng.standard_normal((B, xh, L, dg))
+    return Q, K, V, U, X
+
+
+def _scalar_case(fix):
+    def val(z):
+        return {"ln2": math.log(2.0), "ln3": math.log(3.0)}.get(z, z) if isinstance(z, str) else z
+    inp = fix["inputs"]
+    arr = lambda n: np.array([float(val(z)) for z in inp[n]]).reshape(1, 1, -1, 1)
+    return arr("q"), arr("k"), arr("v"), arr("u"), arr("x")
+
+
+def test_golden_grm_worked_example():
+    fix = json.load(open(os.path.join(GOLD, "grm_worked_example.json")))
+    q, k, v, u, x = _scalar_case(fix)
+    out = oracle.prefill(q, k, v, u, x, seg_len=2, mode="grm", want_states=True)
+    np.testing.assert_allclose(out["Y"].ravel(), fix["expected_y"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(out["M"].ravel(), fix["expected_states"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(out["P"].ravel(), fix["expected_means"], rtol=0, atol=1e-14)
+
+
+def test_golden_ssc_tie_worked_example():
+    fix = json.load(open(os.path.join(GOLD, "ssc_tie_worked_example.json")))
+    q, k, v, u, x = _scalar_case(fix)
+    ssc = oracle.prefill(q, k, v, u, x, seg_len=2, mode="ssc", top_k=1)
+    np.testing.assert_allclose(ssc["Y"].ravel(), fix["expected_y_ssc"], rtol=0, atol=1e-14)
+    assert ssc["idx"][0, 0].tolist() == fix["expected_idx_ssc"]
+    grm = oracle.prefill(q, k, v, u, x, seg_len=2, mode="grm")
+    np.testing.assert_allclose(grm["Y"].ravel(), fix["expected_y_grm"], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("phi", ["identity", "elu1"])
+def test_single_segment_is_linear_attention(phi):
+    Q, K, V, U, X = _rand(2, 3, 40, 8, 6, 5, seed=1)
+    out = oracle.prefill(Q, K, V, U, X, seg_len=40, phi=phi)
+    np.testing.assert_allclose(out["Y"], _causal_la(Q, K, V, phi), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("C", [1, 3, 8, 16])
+def test_residual_collapses_to_linear_attention(C):
+    Q, K, V, U, X = _rand(1, 2, 48, 6, 7, 4, seed=2)
+    out = oracle.prefill(Q, K, V, U, X, seg_len=C, mode="residual")
+    np.testing.assert_allclose(out["Y"], _causal_la(Q, K, V), rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("C,k", [(8, 7), (8, 9), (16, 2)])
+def test_ssc_with_all_segments_equals_grm(C, k):
+    Q, K, V, U, X = _rand(1, 2, 64, 5, 5, 6, seed=3)
+    N = 64 // C
+    grm = oracle.prefill(Q, K, V, U, X, seg_len=C, mode="grm", want_gamma=True)
+    ssc = oracle.prefill(Q, K, V, U, X, seg_len=C, mode="ssc", top_k=k, want_gamma=True)
+    if k >= N - 1:
+        np.testing.assert_array_equal(ssc["Y"], grm["Y"])
+        np.testing.assert_array_equal(ssc["gamma"], grm["gamma"])
+        s = np.arange(64) // C
+        for t in range(64):
+            exp = list(range(min(s[t], k))) + [-1] * (k - min(s[t], k))
+            assert ssc["idx"][0, 0, t].tolist() == exp
+    else:
+        assert not np.allclose(ssc["Y"], grm["Y"])
+
+
+def _brute(Q, K, V, U, X, C, phi="identity", mode="grm", top_k=0):
+    """Token-pair evaluation with no states: y_t = sum_{r<=t} w_{t,seg(r)} (q_t.k_r) v_r."""
+    B, H, L, _ = Q.shape
+    xh = X.shape[1]
+    qh, kh = _phi(Q, phi), _phi(K, phi)
+    Y = np.zeros(V.shape)
+    IDX = []
+    for b in range(B):
+        for h in range(H):
+            x = X[b, 0 if xh == 1 else h]
+            means = [x[i * C:(i + 1) * C].mean(axis=0) for i in range((L + C - 1) // C)]
+            for t in range(L):
+                s, j = divmod(t, C)
+                scores = [float(U[b, h, t] @ means[i]) for i in range(s)]
+                online = float(U[b, h, t] @ x[s * C:t + 1].mean(axis=0))
+                if mode == "ssc":
+                    order = sorted(range(s), key=lambda i: (-scores[i], i))
+                    chosen = sorted(order[:top_k])
+                    IDX.append(chosen + [-1] * (top_k - len(chosen)))
+                else:
+                    chosen = list(range(s))
+                logits = np.array([scores[i] for i in chosen] + [online])
+                w = torch.softmax(torch.tensor(logits, dtype=torch.float64), 0).numpy()
+                weight = dict(zip(chosen + [s], w))
+                for r in range(t + 1):
+                    g = weight.get(r // C, 0.0)
+                    Y[b, h, t] += g * float(qh[b, h, t] @ kh[b, h, r]) * V[b, h, r]
+    return Y, IDX
+
+
+@pytest.mark.parametrize("L,C,phi,xh", [(64, 8, "identity", 1), (60, 16, "elu1", 2),
+                                        (37, 5, "identity", 2), (48, 4, "elu1", 1)])
+def test_brute_force_grm(L, C, phi, xh):
+    Q, K, V, U, X = _rand(1, 2, L, 4, 3, 5, xh=xh, seed=4)
+    out = oracle.prefill(Q, K, V, U, X, seg_len=C, phi=phi, mode="grm")
+    Yb, _ = _brute(Q, K, V, U, X, C, phi)
+    np.testing.assert_allclose(out["Y"], Yb, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("L,C,k", [(64, 4, 3), (63, 8, 2), (40, 4, 1)])
+def test_brute_force_ssc(L, C, k):
+    Q, K, V, U, X = _rand(1, 2, L, 4, 3, 5, seed=5, scale_u=3.0)
+    out = oracle.prefill(Q, K, V, U, X, seg_len=C, mode="ssc", top_k=k)
+    Yb, Ib = _brute(Q, K, V, U, X, C, mode="ssc", top_k=k)
+    np.testing.assert_allclose(out["Y"], Yb, rtol=1e-11, atol=1e-11)
+    np.testing.assert_array_equal(out["idx"].reshape(-1, k), np.array(Ib))
+
+
+def _sdpa(q, k, v, mask):
+    t = lambda a: torch.tensor(a, dtype=torch.float64)
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=torch.tensor(mask), scale=1.0).numpy()
+
+
+def test_segment_length_one_is_softmax_attention():
+    """C = 1, q = k = e1: y_t = sum_{i<=t} softmax_i(<u_t, x_i>) v_i (causal SDPA, scale 1)."""
+    L, d = 50, 6
+    rng = np.random.default_rng(6)
+    U = rng.standard_normal((1, 1, L, d))
+    X = rng.standard_normal((1, 1, L, d))
+    V = rng.standard_normal((1, 1, L, 4))
+    e1 = np.zeros((1, 1, L, 3))
+    e1[..., 0] = 1.0
+    out = oracle.prefill(e1, e1, V, U, X, seg_len=1)
+    ref = _sdpa(U, X, V, np.tril(np.ones((L, L), dtype=bool)))
+    np.testing.assert_allclose(out["Y"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_segment_constant_pool_is_block_causal_attention():
+    """x constant inside each segment, q = k = e1, v non-zero only at segment starts:
+    y_t = sum_{i<=s} softmax_i(<u_t, c_i>) v_{iC}.  Pins the segment means and the
+    online prefix mean (its divisor is the count of tokens seen)."""
+    C, N, d = 8, 6, 5
+    L = C * N
+    rng = np.random.default_rng(7)
+    c = rng.standard_normal((N, d))
+    X = np.repeat(c, C, axis=0).reshape(1, 1, L, d)
+    U = rng.standard_normal((1, 1, L, d)) * 2
+    V = np.zeros((1, 1, L, 3))
+    vs = rng.standard_normal((N, 3))
+    V[0, 0, ::C] = vs
+    e1 = np.zeros((1, 1, L, 2))
+    e1[..., 0] = 1.0
+    out = oracle.prefill(e1, e1, V, U, X, seg_len=C)
+    mask = np.arange(N)[None, :] <= (np.arange(L) // C)[:, None]
+    ref = _sdpa(U, c.reshape(1, 1, N, d), vs.reshape(1, 1, N, 3), mask)
+    np.testing.assert_allclose(out["Y"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_gate_input_gives_uniform_weights():
+    Q, K, V, U, X = _rand(1, 2, 45, 4, 4, 4, seed=8)
+    C = 6
+    out = oracle.prefill(Q, K, V, 0 * U, X, seg_len=C, want_gamma=True)
+    s = np.arange(45) // C
+    np.testing.assert_allclose(out["Y"], _causal_la(Q, K, V) / (s + 1)[None, None, :, None],
+                               rtol=1e-12, atol=1e-12)
+    g = out["gamma"][0, 0]
+    for t in range(45):
+        np.testing.assert_allclose(g[t, :s[t] + 1], 1.0 / (s[t] + 1), rtol=1e-14)
+        assert np.all(g[t, s[t] + 1:] == 0)
+
+
+def test_first_segment_reads_only_online_memory():
+    Q, K, V, U, X = _rand(1, 1, 32, 4, 4, 4, seed=9)
+    out = oracle.prefill(Q, K, V, U, X, seg_len=16, want_online=True)
+    np.testing.assert_array_equal(out["Y"][0, 0, :16], out["O_on"][0, 0, :16])
+    np.testing.assert_allclose(out["O_on"][..., :16, :], _causal_la(Q, K, V)[..., :16, :],
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_memory_soup_equals_grm_for_linear_memory():
+    Q, K, V, U, X = _rand(2, 2, 40, 5, 4, 3, seed=10)
+    grm = oracle.prefill(Q, K, V, U, X, seg_len=8, mode="grm")
+    soup = oracle.prefill(Q, K, V, U, X, seg_len=8, mode="soup")
+    np.testing.assert_allclose(soup["Y"], grm["Y"], rtol=1e-12, atol=1e-12)
+
+
+def test_states_and_means_are_segment_sums():
+    Q, K, V, U, X = _rand(1, 2, 30, 3, 4, 5, xh=2, seed=11)
+    C = 8
+    out = oracle.prefill(Q, K, V, U, X, seg_len=C, want_states=True)
+    for i in range(4):
+        sl = slice(i * C, min((i + 1) * C, 30))
+        np.testing.assert_allclose(out["M"][:, :, i],
+                                   np.swapaxes(V[:, :, sl], -1, -2) @ K[:, :, sl], rtol=1e-12)
+        np.testing.assert_allclose(out["P"][:, :, i], X[:, :, sl].mean(axis=2), rtol=1e-12)
+
+
+def test_gate_is_on_the_simplex_and_rows_subset_matches():
+    Q, K, V, U, X = _rand(2, 2, 50, 4, 4, 4, seed=12, scale_u=5)
+    full = oracle.prefill(Q, K, V, U, X, seg_len=7, want_gamma=True)
+    g = full["gamma"]
+    assert np.all(g >= 0) and np.all(g <= 1)
+    np.testing.assert_allclose(g.sum(-1), 1.0, rtol=1e-13)
+    rows = np.array([0, 6, 7, 20, 49])
+    part = oracle.prefill(Q, K, V, U, X, seg_len=7, rows=rows, want_gamma=True)
+    np.testing.assert_array_equal(part["Y"], full["Y"][:, :, rows])
+    np.testing.assert_array_equal(part["gamma"], full["gamma"][:, :, rows])
+
+
+def test_linear_in_values_and_heads_independent():
+    Q, K, V, U, X = _rand(1, 3, 33, 4, 4, 4, xh=3, seed=13)
+    V2 = np.random.default_rng(14).standard_normal(V.shape)
+    y1 = oracle.prefill(Q, K, V, U, X, seg_len=5)["Y"]
+    y2 = oracle.prefill(Q, K, V2, U, X, seg_len=5)["Y"]
+    y12 = oracle.prefill(Q, K, 2 * V - 3 * V2, U, X, seg_len=5)["Y"]
+    np.testing.assert_allclose(y12, 2 * y1 - 3 * y2, rtol=1e-11, atol=1e-11)
+    perm = [2, 0, 1]
+    yp = oracle.prefill(Q[:, perm], K[:, perm], V[:, perm], U[:, perm], X[:, perm], seg_len=5)["Y"]
+    np.testing.assert_array_equal(yp, y1[:, perm])
+
+
+def test_causal():
+    Q, K, V, U, X = _rand(1, 1, 40, 4, 4, 4, seed=15)
+    base = oracle.prefill(Q, K, V, U, X, seg_len=8)["Y"]
+    t0 = 21
+    Q2, K2, V2, U2, X2 = (a.copy() for a in (Q, K, V, U, X))
+    for a in (Q2, K2, V2, U2, X2):
+        a[..., t0 + 1:, :] += 10.0
+    pert = oracle.prefill(Q2, K2, V2, U2, X2, seg_len=8)["Y"]
+    np.testing.assert_array_equal(pert[..., :t0 + 1, :], base[..., :t0 + 1, :])
+    assert not np.allclose(pert[..., t0 + 1:, :], base[..., t0 + 1:, :])
+
+
+def test_ssc_ties_pick_lowest_index():
+    C, L = 4, 32
+    Q, K, V, U, X = _rand(1, 1, L, 4, 4, 4, seed=16)
+    X[..., 8:12, :] = X[..., 0:4, :]   # segment 2 duplicates segment 0 (equal scores)
+    X[..., 20:24, :] = X[..., 0:4, :]  # and segment 5
+    U[..., 24:, :] = X[..., 0:4, :].mean(axis=2, keepdims=True) * 50  # make them win
+    out = oracle.prefill(Q, K, V, U, X, seg_len=C, mode="ssc", top_k=1)
+    assert np.all(out["idx"][0, 0, 24:, 0] == 0)
+    out2 = oracle.prefill(Q, K, V, U, X, seg_len=C, mode="ssc", top_k=2)
+    assert np.all(out2["idx"][0, 0, 24:] == [0, 2])
+
+
+@pytest.mark.parametrize("L,C", [(20, 8), (23, 8), (15, 8), (16, 4)])
+def test_prefill_then_decode_equals_longer_prefill(L, C):
+    B, H, dk, dv, dg = 2, 2, 4, 3, 5
+    Q, K, V, U, X = _rand(B, H, L + 1, dk, dv, dg, seed=17)
+    full = oracle.prefill(Q, K, V, U, X, seg_len=C, mode="grm", want_states=True)
+    pre = oracle.prefill(Q[:, :, :L], K[:, :, :L], V[:, :, :L], U[:, :, :L], X[:, :, :L],
+                         seg_len=C, want_states=True)
+    nfull, cnt = divmod(L, C)
+    cap = nfull + 2
+    Mc = np.zeros((B, H, cap, dv, dk))
+    Pc = np.zeros((B, 1, cap, dg))
+    Mc[:, :, :nfull] = pre["M"][:, :, :nfull]
+    Pc[:, :, :nfull] = pre["P"][:, :, :nfull]
+    M_on = pre["M"][:, :, nfull] if cnt else np.zeros((B, H, dv, dk))
+    xsum = pre["P"][:, :, nfull] * cnt if cnt else np.zeros((B, 1, dg))
+    st = oracle.DecodeState(M_on, xsum.reshape(B, 1, dg), cnt, Mc, Pc, nfull)
+    y = oracle.decode_step(st, Q[:, :, L], K[:, :, L], V[:, :, L], U[:, :, L], X[:, :, L],
+                           seg_len=C)
+    np.testing.assert_allclose(y, full["Y"][:, :, L], rtol=1e-12, atol=1e-12)
+    if (L + 1) % C == 0:
+        assert st.n_cached[0] == nfull + 1 and st.count[0] == 0
+        np.testing.assert_allclose(st.M_cache[:, :, nfull], full["M"][:, :, nfull], rtol=1e-12)
+        np.testing.assert_allclose(st.P_cache[:, :, nfull], full["P"][:, :, nfull], rtol=1e-12)
+        assert np.all(st.M_on == 0) and np.all(st.xsum == 0)
+    else:
+        assert st.n_cached[0] == nfull and st.count[0] == cnt + 1
+
+
+def test_decode_residual_is_linear_attention_read():
+    B, H, dk, dv, dg, C = 1, 2, 4, 4, 3, 4
+    rng = np.random.default_rng(18)
+    n = 3
+    Mc = np.zeros((B, H, 5, dv, dk))
+    Mc[:, :, :n] = rng.standard_normal((B, H, n, dv, dk))
+    st = oracle.DecodeState(rng.standard_normal((B, H, dv, dk)), rng.standard_normal((B, 1, dg)),
+                            1, Mc, rng.standard_normal((B, 1, 5, dg)), n)
+    q, k = rng.standard_normal((B, H, dk)), rng.standard_normal((B, H, dk))
+    v, u, x = rng.standard_normal((B, H, dv)), rng.standard_normal((B, H, dg)), rng.standard_normal((B, 1, dg))
+    total = Mc[:, :, :n].sum(2) + st.M_on + v[..., :, None] * k[..., None, :]
+    y = oracle.decode_step(st, q, k, v, u, x, seg_len=C, mode="residual")
+    np.testing.assert_allclose(y, np.einsum("bhcr,bhr->bhc", total, q), rtol=1e-12)
