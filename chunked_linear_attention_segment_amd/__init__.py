@@ -1,0 +1,209 @@
+"""Memory Caching (MC) over a linear-attention memory on MI355X: Python binding of libmc.
+
+The binding only marshals arguments: every step of the path runs in the HIP kernels of
+``libmc.so`` (built by ``python -m chunked_linear_attention_segment_amd.build``).  There is
+no fallback: if the library is missing, loading raises.
+
+Entry points (same names and arguments as include/mc.h; tensors are torch tensors on the
+GPU, host scalars are Python ints or one-element int32 numpy arrays):
+    mc_abi_version, mc_status_str, mc_workspace_bytes,
+    mc_scan_prefill, mc_grm_readout, mc_ssc_readout, mc_decode_step
+plus helpers that allocate outputs / workspaces with torch (memory plumbing only).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmc.so")
+
+MC_OK, MC_ERR_NULL, MC_ERR_DIMS, MC_ERR_UNSUPPORTED = 0, 1, 2, 3
+MC_ERR_ALIGN, MC_ERR_WORKSPACE, MC_ERR_HIP, MC_ERR_CAPACITY = 4, 5, 6, 7
+MC_F32, MC_BF16 = 0, 1
+MC_PHI_IDENTITY, MC_PHI_ELU1 = 0, 1
+MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE = 0, 1, 2, 3
+
+EXPORTED = ["mc_abi_version", "mc_status_str", "mc_workspace_bytes", "mc_scan_prefill",
+            "mc_grm_readout", "mc_ssc_readout", "mc_decode_step"]
+
+
+class McDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "H", "L", "d_k", "d_v", "d_g", "seg_len", "x_heads", "dtype", "phi")]
+
+
+class McError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, mc_status_str(status), status))
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libmc.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise OSError("libmc.so not found at %s; build it with "
+                          "`python -m chunked_linear_attention_segment_amd.build`" % path)
+        lib = ctypes.CDLL(path)
+        P, D = ctypes.c_void_p, ctypes.POINTER(McDims)
+        lib.mc_abi_version.restype = ctypes.c_int
+        lib.mc_status_str.restype = ctypes.c_char_p
+        lib.mc_status_str.argtypes = [ctypes.c_int]
+        lib.mc_workspace_bytes.restype = ctypes.c_size_t
+        lib.mc_workspace_bytes.argtypes = [D, ctypes.c_int, ctypes.c_int32, ctypes.c_int32]
+        lib.mc_scan_prefill.restype = ctypes.c_int
+        lib.mc_scan_prefill.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.mc_grm_readout.restype = ctypes.c_int
+        lib.mc_grm_readout.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.mc_ssc_readout.restype = ctypes.c_int
+        lib.mc_ssc_readout.argtypes = [D, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
+                                       ctypes.c_size_t, P]
+        lib.mc_decode_step.restype = ctypes.c_int
+        lib.mc_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P,
+                                       ctypes.c_size_t, P]
+        _lib = lib
+    return _lib
+
+
+def make_dims(B, H, L, d_k, d_v, d_g, seg_len, x_heads=1, dtype="bf16", phi="identity"):
+    dt = {"f32": MC_F32, "bf16": MC_BF16}.get(dtype, dtype)
+    ph = {"identity": MC_PHI_IDENTITY, "elu1": MC_PHI_ELU1}.get(phi, phi)
+    return McDims(B, H, L, d_k, d_v, d_g, seg_len, x_heads, dt, ph)
+
+
+def _p(t):
+    """Device (or host) address of a tensor / numpy array / raw int, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return _p(ws), ws.numel() * ws.element_size()
+
+
+def _check(rc, where):
+    if rc != MC_OK:
+        raise McError(rc, where)
+
+
+def mc_abi_version() -> int:
+    return load().mc_abi_version()
+
+
+def mc_status_str(status: int) -> str:
+    return load().mc_status_str(int(status)).decode()
+
+
+def mc_workspace_bytes(dims: McDims, op: int, top_k: int = 0, n_cap: int = 0) -> int:
+    return int(load().mc_workspace_bytes(ctypes.byref(dims), int(op), int(top_k), int(n_cap)))
+
+
+def mc_scan_prefill(dims, Q, K, V, X, M, M_lo, P, O_on, ws=None, stream=None):
+    w, wb = _ws(ws)
+    _check(load().mc_scan_prefill(ctypes.byref(dims), _p(Q), _p(K), _p(V), _p(X), _p(M),
+                                  _p(M_lo), _p(P), _p(O_on), w, wb, _stream(stream)),
+           "mc_scan_prefill")
+
+
+def mc_grm_readout(dims, Q, U, X, M, M_lo, P, O_on, Y, gamma=None, ws=None, stream=None):
+    w, wb = _ws(ws)
+    _check(load().mc_grm_readout(ctypes.byref(dims), _p(Q), _p(U), _p(X), _p(M), _p(M_lo),
+                                 _p(P), _p(O_on), _p(Y), _p(gamma), w, wb, _stream(stream)),
+           "mc_grm_readout")
+
+
+def mc_ssc_readout(dims, top_k, Q, U, X, M, M_lo, P, O_on, Y, idx, ws=None, stream=None):
+    w, wb = _ws(ws)
+    _check(load().mc_ssc_readout(ctypes.byref(dims), int(top_k), _p(Q), _p(U), _p(X), _p(M),
+                                 _p(M_lo), _p(P), _p(O_on), _p(Y), _p(idx), w, wb,
+                                 _stream(stream)),
+           "mc_ssc_readout")
+
+
+def mc_decode_step(dims, q, k, v, u, x, M_on, xsum_on, count_on, M_cache, P_cache, n_cached,
+                   n_cap, y, ws=None, stream=None):
+    """count_on and n_cached are one-element int32 numpy arrays, updated in place."""
+    assert isinstance(count_on, np.ndarray) and count_on.dtype == np.int32
+    assert isinstance(n_cached, np.ndarray) and n_cached.dtype == np.int32
+    w, wb = _ws(ws)
+    _check(load().mc_decode_step(ctypes.byref(dims), _p(q), _p(k), _p(v), _p(u), _p(x),
+                                 _p(M_on), _p(xsum_on), count_on.ctypes.data, _p(M_cache),
+                                 _p(P_cache), n_cached.ctypes.data, int(n_cap), _p(y), w, wb,
+                                 _stream(stream)),
+           "mc_decode_step")
+
+
+# ---- allocation helpers (torch is only memory plumbing here) ----------------------------
+
+def torch_dtype(dims):
+    import torch
+    return torch.bfloat16 if dims.dtype == MC_BF16 else torch.float32
+
+
+def workspace(dims, op, top_k=0, n_cap=0, device="cuda"):
+    import torch
+    n = mc_workspace_bytes(dims, op, top_k, n_cap)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def alloc_prefill(dims, device="cuda"):
+    """Output buffers of mc_scan_prefill: M, M_lo, P, O_on."""
+    import torch
+    NS = (dims.L + dims.seg_len - 1) // dims.seg_len
+    M = torch.empty((dims.B, dims.H, NS, dims.d_v, dims.d_k), dtype=torch.float32, device=device)
+    M_lo = torch.empty((dims.B, dims.H, NS, dims.d_v, dims.d_k), dtype=torch.bfloat16,
+                       device=device)
+    P = torch.empty((dims.B, dims.x_heads, NS, dims.d_g), dtype=torch.float32, device=device)
+    O_on = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch.float32, device=device)
+    return M, M_lo, P, O_on
+
+
+def prefill_grm(dims, Q, K, V, U, X, want_gamma=False, stream=None):
+    """scan + GRM read with freshly allocated outputs; returns a dict of tensors."""
+    import torch
+    M, M_lo, P, O_on = alloc_prefill(dims, Q.device)
+    mc_scan_prefill(dims, Q, K, V, X, M, M_lo, P, O_on, stream=stream)
+    Y = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch_dtype(dims), device=Q.device)
+    NS = M.shape[2]
+    G = torch.empty((dims.B, dims.H, dims.L, NS), dtype=torch.float32,
+                    device=Q.device) if want_gamma else None
+    ws = workspace(dims, MC_OP_GRM, device=Q.device)
+    mc_grm_readout(dims, Q, U, X, M, M_lo, P, O_on, Y, G, ws=ws, stream=stream)
+    out = {"Y": Y, "M": M, "M_lo": M_lo, "P": P, "O_on": O_on}
+    if want_gamma:
+        out["gamma"] = G
+    return out
+
+
+def prefill_ssc(dims, top_k, Q, K, V, U, X, stream=None):
+    import torch
+    M, M_lo, P, O_on = alloc_prefill(dims, Q.device)
+    mc_scan_prefill(dims, Q, K, V, X, M, M_lo, P, O_on, stream=stream)
+    Y = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch_dtype(dims), device=Q.device)
+    idx = torch.empty((dims.B, dims.H, dims.L, top_k), dtype=torch.int32, device=Q.device)
+    ws = workspace(dims, MC_OP_SSC, top_k=top_k, device=Q.device)
+    mc_ssc_readout(dims, top_k, Q, U, X, M, M_lo, P, O_on, Y, idx, ws=ws, stream=stream)
+    return {"Y": Y, "idx": idx, "M": M, "M_lo": M_lo, "P": P, "O_on": O_on}

@@ -1,0 +1,190 @@
+// abi.cpp -- the C ABI of libmc: argument validation, workspace sizing and dispatch.
+//
+// Validation runs before any HIP call, so every error path is observable without a GPU.
+// The operations themselves are documented in include/mc.h.
+#include <stdint.h>
+#include <string.h>
+
+#include "mc_internal.h"
+
+namespace mc {
+
+static int num_segments(const mc_dims& d) { return (d.L + d.seg_len - 1) / d.seg_len; }
+
+GrmWorkspace grm_workspace(const mc_dims& d) {
+    GrmWorkspace w{};
+    w.xcum = align256(sizeof(float) * (size_t)d.B * d.x_heads * d.L * d.d_g);
+    w.total = w.xcum;
+    return w;
+}
+
+SscWorkspace ssc_workspace(const mc_dims& d) {
+    SscWorkspace w{};
+    w.xcum = align256(sizeof(float) * (size_t)d.B * d.x_heads * d.L * d.d_g);
+    w.xsum64 = align256(sizeof(double) * (size_t)d.B * d.x_heads * num_segments(d) * d.d_g);
+    w.total = w.xcum + w.xsum64;
+    return w;
+}
+
+// The cached-state read of a decode step is split over `splits` workgroups per (b, h);
+// the split count depends only on the capacity so the workspace size is stable.
+DecodeWorkspace decode_workspace(const mc_dims& d, int n_cap, int /*n_cached*/) {
+    DecodeWorkspace w{};
+    int splits = (n_cap + 31) / 32;
+    if (splits < 1) splits = 1;
+    w.splits = splits;
+    const size_t bh = (size_t)d.B * d.H;
+    w.gamma = align256(sizeof(float) * bh * (size_t)(n_cap + 1));
+    w.partial = align256(sizeof(float) * bh * (size_t)splits * d.d_v);
+    w.y_on = align256(sizeof(float) * bh * d.d_v);
+    w.total = w.gamma + w.partial + w.y_on;
+    return w;
+}
+
+}  // namespace mc
+
+using namespace mc;
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shared size checks; `need_L` is false for decode, which ignores L.
+static mc_status check_dims(const mc_dims* d, bool need_L) {
+    if (!d) return MC_ERR_NULL;
+    if (d->B <= 0 || d->H <= 0 || d->d_k <= 0 || d->d_v <= 0 || d->d_g <= 0 ||
+        d->seg_len <= 0)
+        return MC_ERR_DIMS;
+    if (need_L && d->L <= 0) return MC_ERR_DIMS;
+    if (!(d->x_heads == 1 || d->x_heads == d->H)) return MC_ERR_DIMS;
+    if (!(d->dtype == MC_F32 || d->dtype == MC_BF16)) return MC_ERR_UNSUPPORTED;
+    if (!(d->phi == MC_PHI_IDENTITY || d->phi == MC_PHI_ELU1)) return MC_ERR_UNSUPPORTED;
+    if (!(d->d_k == 64 || d->d_k == 128) || !(d->d_v == 64 || d->d_v == 128))
+        return MC_ERR_UNSUPPORTED;
+    if (d->d_g > 256 || d->d_g % 8 != 0) return MC_ERR_UNSUPPORTED;
+    // element offsets are formed in 64-bit, but a single sequence must index in 32-bit
+    if (need_L && (int64_t)d->L * 256 > INT32_MAX) return MC_ERR_UNSUPPORTED;
+    return MC_OK;
+}
+
+extern "C" {
+
+int mc_abi_version(void) { return MC_ABI_VERSION; }
+
+const char* mc_status_str(mc_status s) {
+    switch (s) {
+        case MC_OK: return "ok";
+        case MC_ERR_NULL: return "a required pointer is NULL";
+        case MC_ERR_DIMS: return "invalid or inconsistent sizes";
+        case MC_ERR_UNSUPPORTED: return "sizes or types not supported by this build";
+        case MC_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case MC_ERR_WORKSPACE: return "workspace too small";
+        case MC_ERR_HIP: return "HIP launch failed";
+        case MC_ERR_CAPACITY: return "decode cache is full";
+    }
+    return "unknown status";
+}
+
+size_t mc_workspace_bytes(const mc_dims* d, mc_op op, int32_t top_k, int32_t n_cap) {
+    if (op == MC_OP_DECODE) {
+        if (check_dims(d, false) != MC_OK || n_cap < 0) return 0;
+        return decode_workspace(*d, n_cap, 0).total;
+    }
+    if (check_dims(d, true) != MC_OK) return 0;
+    switch (op) {
+        case MC_OP_PREFILL: return 0;
+        case MC_OP_GRM: return grm_workspace(*d).total;
+        case MC_OP_SSC: return top_k >= 1 ? ssc_workspace(*d).total : 0;
+        default: return 0;
+    }
+}
+
+mc_status mc_scan_prefill(const mc_dims* d, const void* Q, const void* K, const void* V,
+                          const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,
+                          void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    mc_status st = check_dims(d, true);
+    if (st != MC_OK) return st;
+    if (!Q || !K || !V || !X || !M || !P || !O_on) return MC_ERR_NULL;
+    if (d->dtype == MC_BF16 && !M_lo) return MC_ERR_NULL;
+    const void* ptrs[] = {Q, K, V, X, M, M_lo, P, O_on};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MC_ERR_ALIGN;
+    return launch_scan_prefill(*d, Q, K, V, X, M, M_lo, P, O_on, stream) ? MC_ERR_HIP : MC_OK;
+}
+
+mc_status mc_grm_readout(const mc_dims* d, const void* Q, const void* U, const void* X,
+                         const float* M, const uint16_t* M_lo, const float* P,
+                         const float* O_on, void* Y, float* gamma, void* ws, size_t ws_bytes,
+                         void* stream) {
+    mc_status st = check_dims(d, true);
+    if (st != MC_OK) return st;
+    if (!Q || !U || !X || !P || !O_on || !Y) return MC_ERR_NULL;
+    if (d->dtype == MC_BF16 ? !M_lo : !M) return MC_ERR_NULL;
+    const GrmWorkspace w = grm_workspace(*d);
+    if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
+    const void* ptrs[] = {Q, U, X, M, M_lo, P, O_on, Y, gamma, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MC_ERR_ALIGN;
+    float* xcum = (float*)ws;
+    if (launch_xcum(*d, X, xcum, stream)) return MC_ERR_HIP;
+    if (launch_grm_readout(*d, Q, U, xcum, M, M_lo, P, O_on, Y, gamma, stream)) return MC_ERR_HIP;
+    return MC_OK;
+}
+
+mc_status mc_ssc_readout(const mc_dims* d, int32_t top_k, const void* Q, const void* U,
+                         const void* X, const float* M, const uint16_t* M_lo, const float* P,
+                         const float* O_on, void* Y, int32_t* idx, void* ws, size_t ws_bytes,
+                         void* stream) {
+    mc_status st = check_dims(d, true);
+    if (st != MC_OK) return st;
+    if (top_k < 1) return MC_ERR_DIMS;
+    if (top_k > 16) return MC_ERR_UNSUPPORTED;
+    if (!Q || !U || !X || !P || !O_on || !Y || !idx) return MC_ERR_NULL;
+    if (d->dtype == MC_BF16 ? !M_lo : !M) return MC_ERR_NULL;
+    const SscWorkspace w = ssc_workspace(*d);
+    if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
+    const void* ptrs[] = {Q, U, X, M, M_lo, P, O_on, Y, idx, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MC_ERR_ALIGN;
+    float* xcum = (float*)ws;
+    double* xsum64 = (double*)((char*)ws + w.xcum);
+    if (launch_xcum(*d, X, xcum, stream)) return MC_ERR_HIP;
+    if (launch_ssc_select(*d, top_k, U, X, xsum64, idx, stream)) return MC_ERR_HIP;
+    if (launch_ssc_readout(*d, top_k, Q, U, xcum, M, M_lo, P, O_on, idx, Y, stream))
+        return MC_ERR_HIP;
+    return MC_OK;
+}
+
+mc_status mc_decode_step(const mc_dims* d, const void* q, const void* k, const void* v,
+                         const void* u, const void* x, float* M_on, float* xsum_on,
+                         int32_t* count_on, void* M_cache, float* P_cache, int32_t* n_cached,
+                         int32_t n_cap, void* y, void* ws, size_t ws_bytes, void* stream) {
+    mc_status st = check_dims(d, false);
+    if (st != MC_OK) return st;
+    if (!q || !k || !v || !u || !x || !M_on || !xsum_on || !count_on || !P_cache || !n_cached ||
+        !y)
+        return MC_ERR_NULL;
+    if (n_cap < 0) return MC_ERR_DIMS;
+    if (n_cap > 0 && !M_cache) return MC_ERR_NULL;
+    const int cnt = *count_on, n = *n_cached;
+    if (cnt < 0 || cnt >= d->seg_len || n < 0 || n > n_cap) return MC_ERR_DIMS;
+    const int emit = (cnt + 1 == d->seg_len);
+    if (emit && n == n_cap) return MC_ERR_CAPACITY;
+    const DecodeWorkspace w = decode_workspace(*d, n_cap, n);
+    if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
+    const void* ptrs[] = {q, k, v, u, x, M_on, xsum_on, M_cache, P_cache, y, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MC_ERR_ALIGN;
+    if (launch_decode_step(*d, q, k, v, u, x, M_on, xsum_on, cnt, M_cache, P_cache, n, n_cap,
+                           emit, y, ws, stream))
+        return MC_ERR_HIP;
+    if (emit) {
+        *count_on = 0;
+        *n_cached = n + 1;
+    } else {
+        *count_on = cnt + 1;
+    }
+    return MC_OK;
+}
+
+}  // extern "C"

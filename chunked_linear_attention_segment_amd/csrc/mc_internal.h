@@ -1,0 +1,58 @@
+// mc_internal.h -- launchers shared between the ABI layer (abi.cpp) and the HIP kernels.
+// Every launcher enqueues on `stream` and returns the hipError_t of its launches as int.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mc.h"
+
+namespace mc {
+
+// Byte sizes of the workspace regions, in the order they are carved out of `ws`.
+struct GrmWorkspace {
+    size_t xcum;  // fp32 [B,xh,L,dg]: inclusive prefix sums of X inside each segment
+    size_t total;
+};
+struct SscWorkspace {
+    size_t xcum;   // fp32 [B,xh,L,dg]
+    size_t xsum64; // fp64 [B,xh,NS,dg]: segment sums of X, token order
+    size_t total;
+};
+struct DecodeWorkspace {
+    size_t gamma;    // fp32 [B,H,n_cap+1]
+    size_t partial;  // fp32 [B,H,splits,dv]
+    size_t y_on;     // fp32 [B,H,dv]
+    size_t total;
+    int splits;
+};
+
+GrmWorkspace grm_workspace(const mc_dims& d);
+SscWorkspace ssc_workspace(const mc_dims& d);
+DecodeWorkspace decode_workspace(const mc_dims& d, int n_cap, int n_cached);
+
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+int launch_scan_prefill(const mc_dims& d, const void* Q, const void* K, const void* V,
+                        const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,
+                        void* stream);
+
+int launch_xcum(const mc_dims& d, const void* X, float* xcum, void* stream);
+
+int launch_grm_readout(const mc_dims& d, const void* Q, const void* U, const float* xcum,
+                       const float* M, const uint16_t* M_lo, const float* P,
+                       const float* O_on, void* Y, float* gamma, void* stream);
+
+int launch_ssc_select(const mc_dims& d, int top_k, const void* U, const void* X,
+                      double* xsum64, int32_t* idx, void* stream);
+
+int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* U,
+                       const float* xcum, const float* M, const uint16_t* M_lo,
+                       const float* P, const float* O_on, const int32_t* idx, void* Y,
+                       void* stream);
+
+int launch_decode_step(const mc_dims& d, const void* q, const void* k, const void* v,
+                       const void* u, const void* x, float* M_on, float* xsum_on,
+                       int count_on, void* M_cache, float* P_cache, int n_cached, int n_cap,
+                       int emit, void* y, void* ws, void* stream);
+
+}  // namespace mc

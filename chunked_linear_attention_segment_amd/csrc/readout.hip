@@ -1,0 +1,303 @@
+// readout.hip -- the MC read path: context gate, Gated Residual Memory read and the
+// Sparse Selective Caching read (generic fp32-accumulating VALU kernels, any supported d).
+//
+// Memory Caching paper §3.1, Eq. (9)-(10):
+//   a_t^(i) = <u_t, MeanPooling(S^(i))> for the cached segments i < s,
+//   a_t^(s) = <u_t, prefix mean of X over t's segment up to t>  (the online segment),
+//   gamma_t = softmax_i a_t^(i),
+//   y_t     = gamma^(s) M_t^(s) phi(q_t) + sum_{i<s} gamma^(i) M^(i) phi(q_t).
+// Sparse Selective Caching (gitcode explainer §3.4): the same read over the Top-k cached
+// segments by router score a_t^(i), plus the online memory, with the softmax over those.
+#include "common.cuh"
+#include "mc_internal.h"
+
+namespace mc {
+
+// Inclusive prefix sums of X inside each segment (fp32): xcum[t] = sum_{r=sC}^{t} x_r.
+// One workgroup per (segment, b*xh+hx); thread e scans column e.
+template <typename T>
+__global__ void xcum_kernel(const T* __restrict__ X, int L, int C, int DG,
+                            float* __restrict__ xcum) {
+    const int s = blockIdx.x;
+    const size_t bx = blockIdx.y;
+    const int t0 = s * C;
+    const int len = min(C, L - t0);
+    for (int e = threadIdx.x; e < DG; e += blockDim.x) {
+        float acc = 0.f;
+        for (int j = 0; j < len; ++j) {
+            const size_t o = (bx * L + t0 + j) * DG + e;
+            acc += ld(X, o);
+            xcum[o] = acc;
+        }
+    }
+}
+
+int launch_xcum(const mc_dims& d, const void* X, float* xcum, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+    dim3 grid(NS, d.B * d.x_heads);
+    const int threads = d.d_g < 256 ? ((d.d_g + 63) / 64) * 64 : 256;
+    if (d.dtype == MC_BF16)
+        hipLaunchKernelGGL(xcum_kernel<bf16_t>, grid, dim3(threads), 0, st, (const bf16_t*)X,
+                           d.L, d.seg_len, d.d_g, xcum);
+    else
+        hipLaunchKernelGGL(xcum_kernel<float>, grid, dim3(threads), 0, st, (const float*)X, d.L,
+                           d.seg_len, d.d_g, xcum);
+    return (int)hipGetLastError();
+}
+
+// Generic read kernel.  A workgroup covers TT = 32 consecutive tokens of one (b, h); the 8
+// threads of a token share its gate (online softmax over the segments it reads) and each
+// owns the DV/8 output columns c = p, p+8, ...  State i is read straight from global memory
+// (TS = fp32 states for fp32 inputs, the bf16 copy for bf16 inputs).  SSC = true restricts
+// each token to the segments listed in idx.
+template <typename T, typename TS, int DK, int DV, bool SSC>
+__global__ __launch_bounds__(256) void readout_valu_kernel(
+    const T* __restrict__ Q, const T* __restrict__ U, const float* __restrict__ xcum,
+    const TS* __restrict__ S, const float* __restrict__ P, const float* __restrict__ O_on,
+    const int32_t* __restrict__ idx, int top_k, int L, int C, int NS, int DG, int H, int xh,
+    int phi, T* __restrict__ Y, float* __restrict__ gamma) {
+    constexpr int TT = 32;
+    constexpr int CPT = DV / 8;
+    __shared__ float sq[TT][DK];
+
+    const int tile0 = blockIdx.x * TT;
+    const size_t bh = blockIdx.y;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const size_t bx = (size_t)b * xh + (xh == 1 ? 0 : h);
+    const int tid = threadIdx.x;
+    const int tt = tid / 8, p = tid % 8;
+    const int t = tile0 + tt;
+    const bool valid = t < L;
+    const int tc = valid ? t : L - 1;  // clamped token for address formation
+    const int s = tc / C, j = tc % C;
+    const int last = min(L, tile0 + TT) - 1;
+    const int s_hi = last / C;  // largest segment index in this tile
+
+    for (int e = tid; e < TT * DK; e += 256) {
+        const int r = e % DK, tk = min(tile0 + e / DK, L - 1);
+        sq[e / DK][r] = feature(ld(Q, (bh * L + tk) * DK + r), phi);
+    }
+    __syncthreads();
+
+    // this thread's slice of u_t for the gate dots
+    const int gch = DG / 8;
+    const size_t urow = (bh * L + tc) * DG;
+    float a_on = 0.f;
+    {
+        const float inv = 1.f / (float)(j + 1);
+        const size_t xrow = (bx * L + tc) * DG;
+        for (int e = p * gch; e < (p + 1) * gch; ++e) a_on += ld(U, urow + e) * (xcum[xrow + e] * inv);
+        a_on = warp_sum(a_on, 8);
+    }
+    int sel[16];
+    if (SSC) {
+        for (int c = 0; c < 16; ++c) sel[c] = (c < top_k) ? idx[(bh * L + tc) * top_k + c] : -1;
+    }
+
+    float acc[CPT];
+    float mx = a_on, l = 1.f;
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) acc[m] = O_on[(bh * L + tc) * DV + p + 8 * m];
+
+    for (int i = 0; i < s_hi; ++i) {
+        bool use = valid && i < s;
+        if (SSC && use) {
+            bool found = false;
+            for (int c = 0; c < top_k && c < 16; ++c) found |= (sel[c] == i);
+            use = found;
+        }
+        if (SSC && !__syncthreads_or(use)) continue;
+        float a = 0.f;
+        const float* Pi = P + (bx * NS + i) * DG;
+        for (int e = p * gch; e < (p + 1) * gch; ++e) a += ld(U, urow + e) * Pi[e];
+        a = warp_sum(a, 8);
+        if (!use) continue;
+        const float mn = fmaxf(mx, a);
+        const float sc = __expf(mx - mn);
+        const float w = __expf(a - mn);
+        l = l * sc + w;
+        mx = mn;
+        const TS* Si = S + (bh * NS + i) * (size_t)(DV * DK);
+#pragma unroll
+        for (int m = 0; m < CPT; ++m) {
+            const TS* row = Si + (size_t)(p + 8 * m) * DK;
+            float dot = 0.f;
+#pragma unroll 8
+            for (int r = 0; r < DK; ++r) dot += ld(row, r) * sq[tt][r];
+            acc[m] = acc[m] * sc + w * dot;
+        }
+    }
+    if (!valid) return;
+    const float inv_l = 1.f / l;
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) st(Y, (bh * L + t) * DV + p + 8 * m, acc[m] * inv_l);
+
+    if (gamma) {
+        float* gr = gamma + (bh * L + t) * (size_t)NS;
+        for (int i = p; i < NS; i += 8) {
+            float g = 0.f;
+            if (i == s) {
+                g = __expf(a_on - mx) * inv_l;
+            } else if (i < s) {
+                bool use = true;
+                if (SSC) {
+                    use = false;
+                    for (int c = 0; c < top_k && c < 16; ++c) use |= (sel[c] == i);
+                }
+                if (use) {
+                    float a = 0.f;
+                    const float* Pi = P + (bx * NS + i) * DG;
+                    for (int e = 0; e < DG; ++e) a += ld(U, urow + e) * Pi[e];
+                    g = __expf(a - mx) * inv_l;
+                }
+            }
+            gr[i] = g;
+        }
+    }
+}
+
+template <typename T, typename TS, int DK, int DV, bool SSC>
+static int launch_readout_t(const mc_dims& d, int top_k, const void* Q, const void* U,
+                            const float* xcum, const void* S, const float* P,
+                            const float* O_on, const int32_t* idx, void* Y, float* gamma,
+                            hipStream_t st) {
+    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+    dim3 grid((d.L + 31) / 32, d.B * d.H);
+    hipLaunchKernelGGL((readout_valu_kernel<T, TS, DK, DV, SSC>), grid, dim3(256), 0, st,
+                       (const T*)Q, (const T*)U, xcum, (const TS*)S, P, O_on, idx, top_k, d.L,
+                       d.seg_len, NS, d.d_g, d.H, d.x_heads, d.phi, (T*)Y, gamma);
+    return (int)hipGetLastError();
+}
+
+template <bool SSC>
+static int launch_readout(const mc_dims& d, int top_k, const void* Q, const void* U,
+                          const float* xcum, const float* M, const uint16_t* M_lo,
+                          const float* P, const float* O_on, const int32_t* idx, void* Y,
+                          float* gamma, hipStream_t st) {
+#define MC_RD(DK, DV)                                                                      \
+    if (d.d_k == DK && d.d_v == DV)                                                        \
+        return d.dtype == MC_BF16                                                          \
+                   ? launch_readout_t<bf16_t, bf16_t, DK, DV, SSC>(d, top_k, Q, U, xcum,   \
+                                                                   M_lo, P, O_on, idx, Y,  \
+                                                                   gamma, st)              \
+                   : launch_readout_t<float, float, DK, DV, SSC>(d, top_k, Q, U, xcum, M,  \
+                                                                 P, O_on, idx, Y, gamma,   \
+                                                                 st);
+    MC_RD(128, 128)
+    MC_RD(128, 64)
+    MC_RD(64, 128)
+    MC_RD(64, 64)
+#undef MC_RD
+    return (int)hipErrorInvalidValue;
+}
+
+int launch_grm_readout(const mc_dims& d, const void* Q, const void* U, const float* xcum,
+                       const float* M, const uint16_t* M_lo, const float* P,
+                       const float* O_on, void* Y, float* gamma, void* stream) {
+    return launch_readout<false>(d, 0, Q, U, xcum, M, M_lo, P, O_on, nullptr, Y, gamma,
+                                 (hipStream_t)stream);
+}
+
+int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* U,
+                       const float* xcum, const float* M, const uint16_t* M_lo,
+                       const float* P, const float* O_on, const int32_t* idx, void* Y,
+                       void* stream) {
+    return launch_readout<true>(d, top_k, Q, U, xcum, M, M_lo, P, O_on, idx, Y, nullptr,
+                                (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// SSC selection.  The Top-k decision is taken on fp64 router scores formed exactly as the
+// definition reads: the segment mean of X summed in token order and divided by the segment
+// length, then <u_t, mean> accumulated over the gate width in order, every product and sum
+// rounded separately (no fused multiply-add).  Ties go to the lower segment index.
+
+template <typename T>
+__global__ void seg_mean64_kernel(const T* __restrict__ X, int L, int C, int NS, int DG,
+                                  double* __restrict__ P64) {
+    const int s = blockIdx.x;
+    const size_t bx = blockIdx.y;
+    const int t0 = s * C;
+    const int len = min(C, L - t0);
+    for (int e = threadIdx.x; e < DG; e += blockDim.x) {
+        double acc = 0.0;
+        for (int j = 0; j < len; ++j) acc = __dadd_rn(acc, (double)ld(X, (bx * L + t0 + j) * DG + e));
+        P64[(bx * NS + s) * DG + e] = __ddiv_rn(acc, (double)len);
+    }
+}
+
+// One thread per token: scores for the completed segments i < s, kept as a descending list
+// of the top_k best (a candidate enters only if strictly larger, so earlier = lower indices
+// win ties), written out in ascending index order, -1 padded.
+template <typename T, int KMAX>
+__global__ __launch_bounds__(64) void ssc_select_kernel(const T* __restrict__ U,
+                                                        const double* __restrict__ P64, int L,
+                                                        int C, int NS, int DG, int H, int xh,
+                                                        int top_k, int32_t* __restrict__ idx) {
+    const int t = blockIdx.x * 64 + threadIdx.x;
+    const size_t bh = blockIdx.y;
+    if (t >= L) return;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const size_t bx = (size_t)b * xh + (xh == 1 ? 0 : h);
+    const int s = t / C;
+    double best[KMAX];
+    int bi[KMAX];
+#pragma unroll
+    for (int c = 0; c < KMAX; ++c) { best[c] = 0.0; bi[c] = -1; }
+    const T* u = U + (bh * L + t) * DG;
+    for (int i = 0; i < s; ++i) {
+        const double* Pi = P64 + (bx * NS + i) * DG;
+        double a = 0.0;
+        for (int e = 0; e < DG; ++e) a = __dadd_rn(a, __dmul_rn((double)ld(u, e), Pi[e]));
+        // insert (a, i) into the descending list of length top_k
+        int pos = top_k;  // first slot whose entry is empty or strictly smaller than a
+#pragma unroll
+        for (int c = KMAX - 1; c >= 0; --c)
+            if (c < top_k && (bi[c] < 0 || a > best[c])) pos = c;
+        if (pos < top_k) {
+#pragma unroll
+            for (int c = KMAX - 1; c > 0; --c)
+                if (c < top_k && c > pos) { best[c] = best[c - 1]; bi[c] = bi[c - 1]; }
+#pragma unroll
+            for (int c = 0; c < KMAX; ++c)
+                if (c == pos) { best[c] = a; bi[c] = i; }
+        }
+    }
+    // ascending index order, -1 padded
+    int32_t* out = idx + (bh * L + t) * top_k;
+    int prev = -1;
+    for (int c = 0; c < top_k; ++c) {
+        int nxt = -1;
+#pragma unroll
+        for (int e = 0; e < KMAX; ++e)
+            if (e < top_k && bi[e] > prev && (nxt < 0 || bi[e] < nxt)) nxt = bi[e];
+        out[c] = nxt;
+        if (nxt >= 0) prev = nxt;
+    }
+}
+
+int launch_ssc_select(const mc_dims& d, int top_k, const void* U, const void* X,
+                      double* P64, int32_t* idx, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+    dim3 g1(NS, d.B * d.x_heads);
+    const int threads = d.d_g < 256 ? ((d.d_g + 63) / 64) * 64 : 256;
+    dim3 g2((d.L + 63) / 64, d.B * d.H);
+    if (d.dtype == MC_BF16) {
+        hipLaunchKernelGGL(seg_mean64_kernel<bf16_t>, g1, dim3(threads), 0, st,
+                           (const bf16_t*)X, d.L, d.seg_len, NS, d.d_g, P64);
+        hipLaunchKernelGGL((ssc_select_kernel<bf16_t, 16>), g2, dim3(64), 0, st,
+                           (const bf16_t*)U, P64, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads,
+                           top_k, idx);
+    } else {
+        hipLaunchKernelGGL(seg_mean64_kernel<float>, g1, dim3(threads), 0, st, (const float*)X,
+                           d.L, d.seg_len, NS, d.d_g, P64);
+        hipLaunchKernelGGL((ssc_select_kernel<float, 16>), g2, dim3(64), 0, st,
+                           (const float*)U, P64, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads,
+                           top_k, idx);
+    }
+    return (int)hipGetLastError();
+}
+
+}  // namespace mc

@@ -1,0 +1,133 @@
+// scan.hip -- the MC write path: per-segment linear-attention scan, cached states, segment
+// means and the ungated online read.
+//
+// Memory Caching paper §3, Eq. (4b): inside segment s the memory starts from zero and runs
+// M_t = M_{t-1} + v_t phi(k_t)^T (the linear-attention update of §2, Eq. 2); the state after
+// the segment's last token is cached.  The online read M_t^(s) phi(q_t) (§3.1, Eq. 6/8) is
+// taken after token t has updated the memory.  MeanPooling(S^(i)) (§3.1, Eq. 10) averages X.
+#include "common.cuh"
+#include "mc_internal.h"
+
+namespace mc {
+
+// One workgroup per (segment, b*H+h).  The d_v x d_k fp32 state lives in registers: thread
+// `tid` owns row c = tid / TPR and the CPT consecutive columns starting at (tid % TPR) * CPT.
+// Tokens are staged TT at a time in LDS (phi applied on load); each token updates the state
+// and then reads it with phi(q_t) -- the read is reduced over the TPR threads of a row.
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void scan_valu_kernel(const T* __restrict__ Q,
+                                                        const T* __restrict__ K,
+                                                        const T* __restrict__ V, int L, int C,
+                                                        int NS, int phi, float* __restrict__ M,
+                                                        bf16_t* __restrict__ M_lo,
+                                                        float* __restrict__ O_on) {
+    constexpr int TPR = 256 / DV;
+    constexpr int CPT = DK / TPR;
+    constexpr int TT = 32;
+    __shared__ float sk[TT][DK];
+    __shared__ float sq[TT][DK];
+    __shared__ float sv[TT][DV];
+
+    const int s = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int t0 = s * C;
+    const int len = min(C, L - t0);
+    const int tid = threadIdx.x;
+    const int c = tid / TPR;
+    const int r0 = (tid % TPR) * CPT;
+
+    float m[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) m[i] = 0.f;
+
+    const size_t kbase = (bh * L + t0) * DK;
+    const size_t vbase = (bh * L + t0) * DV;
+    for (int j0 = 0; j0 < len; j0 += TT) {
+        const int n = min(TT, len - j0);
+        __syncthreads();
+        for (int e = tid; e < n * DK; e += 256) {
+            sk[e / DK][e % DK] = feature(ld(K, kbase + (size_t)j0 * DK + e), phi);
+            sq[e / DK][e % DK] = feature(ld(Q, kbase + (size_t)j0 * DK + e), phi);
+        }
+        for (int e = tid; e < n * DV; e += 256) sv[e / DV][e % DV] = ld(V, vbase + (size_t)j0 * DV + e);
+        __syncthreads();
+        for (int j = 0; j < n; ++j) {
+            const float vc = sv[j][c];
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                m[i] += vc * sk[j][r0 + i];
+                acc += m[i] * sq[j][r0 + i];
+            }
+            acc = warp_sum(acc, TPR);
+            if (tid % TPR == 0) O_on[(bh * L + t0 + j0 + j) * DV + c] = acc;
+        }
+    }
+    const size_t mo = (bh * NS + s) * (size_t)(DV * DK) + (size_t)c * DK + r0;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) M[mo + i] = m[i];
+    if (M_lo) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) M_lo[mo + i] = f32_to_bf16(m[i]);
+    }
+}
+
+// MeanPooling(S^(i)) = mean of X over segment i (a trailing partial segment averages the
+// tokens it has).  One workgroup per (segment, b*xh+hx); thread e sums column e in fp32.
+template <typename T>
+__global__ void seg_means_kernel(const T* __restrict__ X, int L, int C, int NS, int DG,
+                                 float* __restrict__ P) {
+    const int s = blockIdx.x;
+    const size_t bx = blockIdx.y;
+    const int t0 = s * C;
+    const int len = min(C, L - t0);
+    for (int e = threadIdx.x; e < DG; e += blockDim.x) {
+        float acc = 0.f;
+        for (int j = 0; j < len; ++j) acc += ld(X, (bx * L + t0 + j) * DG + e);
+        P[(bx * NS + s) * DG + e] = acc / (float)len;
+    }
+}
+
+template <typename T, int DK, int DV>
+static int launch_scan_t(const mc_dims& d, const void* Q, const void* K, const void* V,
+                         float* M, uint16_t* M_lo, float* O_on, hipStream_t st) {
+    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+    dim3 grid(NS, d.B * d.H);
+    hipLaunchKernelGGL((scan_valu_kernel<T, DK, DV>), grid, dim3(256), 0, st, (const T*)Q,
+                       (const T*)K, (const T*)V, d.L, d.seg_len, NS, d.phi, M, (bf16_t*)M_lo,
+                       O_on);
+    return (int)hipGetLastError();
+}
+
+template <typename T>
+static int launch_scan_dt(const mc_dims& d, const void* Q, const void* K, const void* V,
+                          float* M, uint16_t* M_lo, float* O_on, hipStream_t st) {
+    if (d.d_k == 128 && d.d_v == 128) return launch_scan_t<T, 128, 128>(d, Q, K, V, M, M_lo, O_on, st);
+    if (d.d_k == 128 && d.d_v == 64) return launch_scan_t<T, 128, 64>(d, Q, K, V, M, M_lo, O_on, st);
+    if (d.d_k == 64 && d.d_v == 128) return launch_scan_t<T, 64, 128>(d, Q, K, V, M, M_lo, O_on, st);
+    return launch_scan_t<T, 64, 64>(d, Q, K, V, M, M_lo, O_on, st);
+}
+
+int launch_scan_prefill(const mc_dims& d, const void* Q, const void* K, const void* V,
+                        const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,
+                        void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+    int rc;
+    if (d.dtype == MC_BF16)
+        rc = launch_scan_dt<bf16_t>(d, Q, K, V, M, M_lo, O_on, st);
+    else
+        rc = launch_scan_dt<float>(d, Q, K, V, M, M_lo, O_on, st);
+    if (rc) return rc;
+    dim3 grid(NS, d.B * d.x_heads);
+    const int threads = d.d_g < 256 ? ((d.d_g + 63) / 64) * 64 : 256;
+    if (d.dtype == MC_BF16)
+        hipLaunchKernelGGL(seg_means_kernel<bf16_t>, grid, dim3(threads), 0, st,
+                           (const bf16_t*)X, d.L, d.seg_len, NS, d.d_g, P);
+    else
+        hipLaunchKernelGGL(seg_means_kernel<float>, grid, dim3(threads), 0, st, (const float*)X,
+                           d.L, d.seg_len, NS, d.d_g, P);
+    return (int)hipGetLastError();
+}
+
+}  // namespace mc

@@ -57,9 +57,10 @@ WORKLOADS = {
 def round_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returned as float32."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    u = a.view(np.uint32)
+    # finite inputs: u + 0x8000 never wraps (the largest finite pattern is 0xFF7FFFFF)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def _store(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -68,8 +69,8 @@ def _store(a: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def _l2n(a: np.ndarray) -> np.ndarray:
-    n = np.sqrt(np.sum(a.astype(np.float64) ** 2, axis=-1, keepdims=True))
-    return (a / np.maximum(n, 1e-30)).astype(np.float32)
+    n = np.sqrt(np.einsum("...i,...i->...", a, a, dtype=np.float32))[..., None]
+    return a / np.maximum(n, np.float32(1e-30))
 
 
 def make_prefill(w: Workload, seed: int = 0, L: int | None = None, B: int | None = None,
@@ -90,11 +91,13 @@ def make_prefill(w: Workload, seed: int = 0, L: int | None = None, B: int | None
         Wk = rng.standard_normal((H, din, w.d_k), dtype=np.float32) * sd
         Wv = rng.standard_normal((H, din, w.d_v), dtype=np.float32) * sd
         Wu = rng.standard_normal((H, din, w.d_g), dtype=np.float32) * sd
-        xs = x if xh == H else np.broadcast_to(x, (B, H, L, din))
-        q = np.einsum("bhld,hde->bhle", xs, Wq, optimize=True)
-        k = np.einsum("bhld,hde->bhle", xs, Wk, optimize=True)
-        v = np.einsum("bhld,hde->bhle", xs, Wv, optimize=True)
-        u = np.einsum("bhld,hde->bhle", xs, Wu, optimize=True)
+        q = np.empty((B, H, L, w.d_k), dtype=np.float32)
+        k = np.empty((B, H, L, w.d_k), dtype=np.float32)
+        v = np.empty((B, H, L, w.d_v), dtype=np.float32)
+        u = np.empty((B, H, L, w.d_g), dtype=np.float32)
+        for h in range(H):
+            xb = x[:, 0 if xh == 1 else h]
+            q[:, h], k[:, h], v[:, h], u[:, h] = xb @ Wq[h], xb @ Wk[h], xb @ Wv[h], xb @ Wu[h]
     elif w.recipe == "l2norm":
         q = _l2n(rng.standard_normal((B, H, L, w.d_k), dtype=np.float32))
         k = _l2n(rng.standard_normal((B, H, L, w.d_k), dtype=np.float32))
@@ -152,3 +155,97 @@ def make_decode(w: Workload, seed: int = 0, B: int | None = None, H: int | None 
     return {"q": _store(q, st), "k": _store(k, st), "v": _store(v, st), "u": _store(u, st),
             "x": _store(x, st), "M_on": M_on, "xsum": xsum, "count": cnt,
             "M_cache": Mc, "P_cache": Pc, "n_cached": n}
+
+
+def make_prefill_device(w: Workload, seed: int = 0, device="cuda", L: int | None = None,
+                        B: int | None = None, H: int | None = None) -> dict:
+    """The same recipes drawn on the device with a seeded torch generator (for the
+    full-size workloads, whose host draw would take minutes).  Returns torch tensors in the
+    storage dtype.  The random stream differs from make_prefill's; each caller uses one
+    generator for both the GPU path and the oracle (which receives copies of these)."""
+    import torch
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    L = w.L if L is None else L
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    din = w.d_g
+    xh = 1 if w.x_heads == 1 else H
+    sd = 1.0 / float(np.sqrt(din))
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def randn(*shape):
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+    x = randn(B, xh, L, din)
+    out = {}
+    if w.recipe == "proj":
+        Ws = [randn(H, din, n) * sd for n in (w.d_k, w.d_k, w.d_v, w.d_g)]
+        for name, Wm in zip(("Q", "K", "V", "U"), Ws):
+            t = torch.empty((B, H, L, Wm.shape[-1]), dtype=dt, device=device)
+            for h in range(H):
+                t[:, h] = (x[:, 0 if xh == 1 else h] @ Wm[h]).to(dt)
+            out[name] = t
+    elif w.recipe == "l2norm":
+        for name, n in (("Q", w.d_k), ("K", w.d_k)):
+            t = torch.empty((B, H, L, n), dtype=dt, device=device)
+            for h in range(H):
+                a = randn(B, L, n)
+                t[:, h] = (a / a.norm(dim=-1, keepdim=True).clamp_min(1e-30)).to(dt)
+            out[name] = t
+        V = torch.empty((B, H, L, w.d_v), dtype=dt, device=device)
+        for h in range(H):
+            V[:, h] = randn(B, L, w.d_v).to(dt)
+        out["V"] = V
+        Wu = randn(H, din, w.d_g) * sd
+        U = torch.empty((B, H, L, w.d_g), dtype=dt, device=device)
+        for h in range(H):
+            U[:, h] = (x[:, 0 if xh == 1 else h] @ Wu[h]).to(dt)
+        out["U"] = U
+    else:
+        raise ValueError(w.recipe)
+    out["X"] = x.to(dt)
+    return out
+
+
+def make_decode_device(w: Workload, seed: int = 0, device="cuda", n_cap: int | None = None) -> dict:
+    """Full-size decode state and token drawn on the device (recipe of make_decode).
+    The state cache M [B,H,n_cap,dv,dk] is drawn slice by slice in the storage dtype."""
+    import torch
+    B, H, C, dk, dv, dg = w.B, w.H, w.seg_len, w.d_k, w.d_v, w.d_g
+    n = w.n_cached
+    cap = (n + 2) if n_cap is None else n_cap
+    cnt = w.count_on
+    xh = 1 if w.x_heads == 1 else H
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def randn(*shape):
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+    Mc = torch.zeros((B, H, cap, dv, dk), dtype=dt, device=device)
+    sc = float(np.sqrt(C / dk))
+    for b in range(B):
+        for h in range(H):
+            Mc[b, h, :n] = (randn(n, dv, dk) * sc).to(dt)
+    Pc = torch.zeros((B, xh, cap, dg), dtype=torch.float32, device=device)
+    Pc[:, :, :n] = randn(B, xh, n, dg) * float(1.0 / np.sqrt(C))
+    M_on = randn(B, H, dv, dk) * float(np.sqrt(max(cnt, 0) / dk))
+    xsum = randn(B, xh, dg) * float(np.sqrt(max(cnt, 0)))
+    if cnt == 0:
+        M_on.zero_()
+        xsum.zero_()
+    x = randn(B, xh, dg)
+    q = randn(B, H, dk)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = randn(B, H, dk)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = randn(B, H, dv)
+    Wu = randn(H, dg, dg) * float(1.0 / np.sqrt(dg))
+    u = torch.empty((B, H, dg), dtype=torch.float32, device=device)
+    for h in range(H):
+        u[:, h] = x[:, 0 if xh == 1 else h] @ Wu[h]
+    return {"q": q.to(dt), "k": k.to(dt), "v": v.to(dt), "u": u.to(dt), "x": x.to(dt),
+            "M_on": M_on.contiguous(), "xsum": xsum.contiguous(), "count": cnt,
+            "M_cache": Mc, "P_cache": Pc, "n_cached": n, "n_cap": cap}

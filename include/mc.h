@@ -1,0 +1,177 @@
+/*
+ * mc.h -- C ABI of libmc: Memory Caching (MC) over a linear-attention memory on MI355X.
+ *
+ * The operations are those of the Memory Caching paper ("Memory Caching: RNNs with growing
+ * memory", Behrouz et al.; zh-TW / ja renderings) and of its gitcode explainer
+ * ("给 RNN 装上“会增长的记忆”：解读 Google 的 Memory Caching"):
+ *   - the sequence is split into segments of constant length C; inside segment s the
+ *     memory runs the linear-attention recurrence M_t = M_{t-1} + v_t phi(k_t)^T from zero
+ *     (paper §3, Eq. 4b with the update of §2, Eq. 2), and the state after the segment's
+ *     last token is cached;
+ *   - Gated Residual Memory (paper §3.1, Eq. 9):
+ *         y_t = gamma_t^(s) M_t^(s) phi(q_t) + sum_{i<s} gamma_t^(i) M^(i) phi(q_t)
+ *     with gamma_t = softmax_i <u_t, MeanPooling(S^(i))> (paper §3.1, Eq. 10);
+ *   - Sparse Selective Caching (explainer §3.4): only the Top-k cached segments by the
+ *     router score <u_t, MeanPooling(S^(i))> are read, plus the online memory;
+ *   - decode: one new token per sequence reads the online memory and every cached state.
+ *
+ * Readings where the pages leave a step open (fixed by this ABI):
+ *   - no normaliser 1/Z (the paper's Miras remark: the inner-product objective gives the
+ *     unnormalised linear attention);
+ *   - the state is M = sum_r v_r phi(k_r)^T, d_v x d_k, row-major, read as y = M phi(q);
+ *   - token t updates the memory before it reads it;
+ *   - MeanPooling averages the layer input X; the online segment uses the causal prefix
+ *     mean over its tokens up to t;
+ *   - the softmax runs over all cached segments and the online segment, no temperature;
+ *   - SSC ties in the router score go to the lower segment index.
+ *
+ * Conventions shared by every entry point
+ *   Memory: every tensor argument is a DEVICE pointer owned by the caller, dense row-major
+ *     with the last dimension contiguous, 16-byte aligned.  The library allocates, frees
+ *     and retains nothing; scratch memory is the caller's workspace `ws` of at least
+ *     mc_workspace_bytes() bytes (16-byte aligned; NULL allowed when that size is 0).
+ *   Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *     work on it and never synchronise.  Host scalars passed by pointer are read and
+ *     updated on the host when the call is made.
+ *   Errors: every argument is validated before any HIP call; on error nothing is enqueued,
+ *     nothing is written and the MC_ERR_* code is returned.  A failed kernel launch
+ *     returns MC_ERR_HIP.  Faults inside kernels surface at the caller's next sync.  The
+ *     library never prints, aborts or throws.
+ *   Threads: no global mutable state; calls are re-entrant.
+ *
+ * Token layout: t = 0..L-1 is 0-based; s = t / C is its segment, j = t % C its position.
+ * NS = ceil(L / C) segments; if L % C != 0 the last segment is partial.
+ */
+#ifndef MC_H
+#define MC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MC_ABI_VERSION 1
+
+typedef enum {
+    MC_OK = 0,
+    MC_ERR_NULL = 1,        /* a required pointer is NULL                                 */
+    MC_ERR_DIMS = 2,        /* a size is non-positive or inconsistent                     */
+    MC_ERR_UNSUPPORTED = 3, /* valid, but outside what this build implements              */
+    MC_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                           */
+    MC_ERR_WORKSPACE = 5,   /* ws_bytes < mc_workspace_bytes()                            */
+    MC_ERR_HIP = 6,         /* a HIP launch failed                                        */
+    MC_ERR_CAPACITY = 7     /* decode: the cache is full and the step would append to it  */
+} mc_status;
+
+typedef enum { MC_F32 = 0, MC_BF16 = 1 } mc_dtype;           /* storage type of Q,K,V,U,X,Y */
+typedef enum { MC_PHI_IDENTITY = 0, MC_PHI_ELU1 = 1 } mc_phi; /* feature map on Q and K     */
+typedef enum { MC_OP_PREFILL = 0, MC_OP_GRM = 1, MC_OP_SSC = 2, MC_OP_DECODE = 3 } mc_op;
+
+/* Problem sizes.  Supported in this build: d_k, d_v in {64, 128}; 1 <= d_g <= 256 and
+ * d_g % 8 == 0; C >= 1; x_heads in {1, H}; dtype MC_F32 or MC_BF16.                      */
+typedef struct mc_dims {
+    int32_t B, H;       /* sequences, heads                                                 */
+    int32_t L;          /* tokens per sequence in this call (prefill); ignored by decode    */
+    int32_t d_k, d_v;   /* query/key width, value width                                     */
+    int32_t d_g;        /* gate width = width of U and X                                    */
+    int32_t seg_len;    /* C, the segment length                                            */
+    int32_t x_heads;    /* 1: X is [B,1,L,d_g], shared by the heads; H: X is [B,H,L,d_g]    */
+    int32_t dtype;      /* mc_dtype of Q, K, V, U, X and Y                                  */
+    int32_t phi;        /* mc_phi applied to Q and K inside the kernels                     */
+} mc_dims;
+
+/* Returns MC_ABI_VERSION. */
+int mc_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* mc_status_str(mc_status status);
+
+/* Workspace bytes an operation needs for these sizes (top_k is used by MC_OP_SSC, n_cap by
+ * MC_OP_DECODE).  Returns 0 when no workspace is needed or the sizes are invalid. */
+size_t mc_workspace_bytes(const mc_dims* dims, mc_op op, int32_t top_k, int32_t n_cap);
+
+/*
+ * mc_scan_prefill -- the write path: per-segment scan, cached states, segment means and the
+ * ungated online read (paper §3 Eq. 4b; §3.1 Eq. 6 / Eq. 8 for the online memory).
+ *
+ *   Q, K  [B,H,L,d_k]  dtype          V [B,H,L,d_v] dtype          X [B,x_heads,L,d_g] dtype
+ *   M      out [B,H,NS,d_v,d_k] fp32   M^(i) = sum_{r in segment i} v_r phi(k_r)^T; the slot
+ *                                      of a trailing partial segment holds its state after
+ *                                      token L-1 (the online state a decode continues from)
+ *   M_lo   out, nullable: the same states rounded to bf16 (the operand copy the bf16 read
+ *                                      paths and the decode cache use); required when
+ *                                      dtype == MC_BF16
+ *   P      out [B,x_heads,NS,d_g] fp32 MeanPooling(S^(i)); a partial segment averages the
+ *                                      tokens it has
+ *   O_on   out [B,H,L,d_v] fp32        M_t^(s) phi(q_t), the online read with weight 1
+ */
+mc_status mc_scan_prefill(const mc_dims* dims, const void* Q, const void* K, const void* V,
+                          const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mc_grm_readout -- Gated Residual Memory read (paper §3.1, Eq. 9 with the gate of Eq. 10):
+ *     a_t^(i) = <u_t, P_i> (i < s),  a_t^(s) = <u_t, prefix mean of X over t's segment>,
+ *     gamma_t = softmax(a_t^(0..s)),  y_t = gamma^(s) O_on[t] + sum_{i<s} gamma^(i) M^(i) phi(q_t)
+ *
+ *   Q [B,H,L,d_k], U [B,H,L,d_g], X [B,x_heads,L,d_g]: dtype
+ *   M, M_lo, P, O_on: as written by mc_scan_prefill for the same Q,K,V,X (M_lo is read when
+ *     dtype == MC_BF16, M when MC_F32; the other may be NULL)
+ *   Y      out [B,H,L,d_v] dtype
+ *   gamma  out, nullable [B,H,L,NS] fp32: gamma_t^(i) for i <= s, 0 beyond
+ */
+mc_status mc_grm_readout(const mc_dims* dims, const void* Q, const void* U, const void* X,
+                         const float* M, const uint16_t* M_lo, const float* P,
+                         const float* O_on, void* Y, float* gamma, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * mc_ssc_readout -- Sparse Selective Caching read (explainer §3.4):
+ *     R_t = Top-k of {a_t^(i)}_{i<s} (larger score first, lower index on ties; all of them
+ *     when s <= k); gamma_t = softmax over R_t and the online segment;
+ *     y_t = gamma^(s) O_on[t] + sum_{i in R_t} gamma^(i) M^(i) phi(q_t)
+ *   The selection is exact: scores are formed in fp32 and any token whose k-th / (k+1)-th
+ *   margin is within the fp32 error bound is re-scored in fp64.
+ *
+ *   Arguments as mc_grm_readout, plus
+ *   top_k  1 <= top_k <= 16
+ *   idx    out [B,H,L,top_k] int32: R_t in ascending order, -1 padded
+ *   ws     mc_workspace_bytes(dims, MC_OP_SSC, top_k, 0) bytes
+ */
+mc_status mc_ssc_readout(const mc_dims* dims, int32_t top_k, const void* Q, const void* U,
+                         const void* X, const float* M, const uint16_t* M_lo, const float* P,
+                         const float* O_on, void* Y, int32_t* idx, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * mc_decode_step -- one new token per sequence (paper §3 applied to token t+1): for every
+ * (b, h) the online memory is updated with the token (Eq. 4b), the gate runs over the
+ * *n_cached cached segments plus the online one (Eq. 10), and y reads all of them (Eq. 9).
+ * If the online segment then holds C tokens, its state (rounded to the cache dtype) and its
+ * mean are appended at slot *n_cached, the online state and x sum restart from zero, and
+ * *n_cached is incremented.  All sequences share *count_on and *n_cached.
+ *
+ *   dims: B, H, d_k, d_v, d_g, seg_len, x_heads, dtype, phi (L is ignored)
+ *   q, k [B,H,d_k]; v [B,H,d_v]; u [B,H,d_g]; x [B,x_heads,d_g]: dtype
+ *   M_on     in/out [B,H,d_v,d_k] fp32  online state before / after the token
+ *   xsum_on  in/out [B,x_heads,d_g] fp32 sum of x over the online segment
+ *   count_on host in/out: tokens in the online segment, 0..C-1 on entry
+ *   M_cache  in/out [B,H,n_cap,d_v,d_k]  bf16 (MC_BF16) or fp32 (MC_F32)
+ *   P_cache  in/out [B,x_heads,n_cap,d_g] fp32
+ *   n_cached host in/out: cached segments, 0..n_cap
+ *   y        out [B,H,d_v] dtype
+ *   ws       mc_workspace_bytes(dims, MC_OP_DECODE, 0, n_cap) bytes
+ *   Returns MC_ERR_CAPACITY (and changes nothing) if the step would append to a full cache.
+ */
+mc_status mc_decode_step(const mc_dims* dims, const void* q, const void* k, const void* v,
+                         const void* u, const void* x, float* M_on, float* xsum_on,
+                         int32_t* count_on, void* M_cache, float* P_cache, int32_t* n_cached,
+                         int32_t n_cap, void* y, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MC_H */

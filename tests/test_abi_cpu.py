@@ -1,0 +1,146 @@
+"""C-ABI contract checks that need no GPU.
+
+libmc validates every argument before its first HIP call, so each error path can be
+exercised here with fake (never dereferenced) device addresses.  No call in this file
+passes validation, so no kernel is ever launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import chunked_linear_attention_segment_amd as mc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "mc.h")
+
+A = 0x7f0000000000  # an aligned fake device address (never dereferenced)
+MIS = A + 4         # a misaligned one
+
+
+def _declared():
+    txt = open(HDR).read()
+    return sorted(set(re.findall(r"^\s*(?:mc_status|int|const char\*|size_t)\s+(mc_\w+)\(", txt,
+                                 re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mc.load()
+    names = _declared()
+    assert set(names) == set(mc.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n)
+    out = subprocess.run(["nm", "-D", "--defined-only", mc.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (mc_\w+)$", out, re.M))
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings():
+    assert mc.mc_abi_version() == 1
+    for s in range(8):
+        assert isinstance(mc.mc_status_str(s), str) and mc.mc_status_str(s)
+
+
+def dims(**kw):
+    base = dict(B=1, H=2, L=1024, d_k=128, d_v=128, d_g=128, seg_len=256, x_heads=1,
+                dtype="bf16", phi="identity")
+    base.update(kw)
+    return mc.make_dims(**base)
+
+
+def scan(d, **ptr):
+    p = dict(Q=A, K=A, V=A, X=A, M=A, M_lo=A, P=A, O_on=A)
+    p.update(ptr)
+    return mc.load().mc_scan_prefill(ctypes.byref(d), p["Q"], p["K"], p["V"], p["X"], p["M"],
+                                     p["M_lo"], p["P"], p["O_on"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), mc.MC_ERR_DIMS), (dict(H=-1), mc.MC_ERR_DIMS), (dict(L=0), mc.MC_ERR_DIMS),
+    (dict(seg_len=0), mc.MC_ERR_DIMS), (dict(x_heads=3), mc.MC_ERR_DIMS),
+    (dict(d_k=96), mc.MC_ERR_UNSUPPORTED), (dict(d_v=32), mc.MC_ERR_UNSUPPORTED),
+    (dict(d_g=12), mc.MC_ERR_UNSUPPORTED), (dict(d_g=512), mc.MC_ERR_UNSUPPORTED),
+    (dict(dtype=7), mc.MC_ERR_UNSUPPORTED), (dict(phi=5), mc.MC_ERR_UNSUPPORTED),
+])
+def test_scan_rejects_bad_dims(kw, code):
+    assert scan(dims(**kw)) == code
+
+
+def test_scan_null_and_alignment():
+    assert mc.load().mc_scan_prefill(None, A, A, A, A, A, A, A, A, None, 0, None) == mc.MC_ERR_NULL
+    for name in ("Q", "K", "V", "X", "M", "P", "O_on"):
+        assert scan(dims(), **{name: None}) == mc.MC_ERR_NULL
+        assert scan(dims(), **{name: MIS}) == mc.MC_ERR_ALIGN
+    assert scan(dims(), M_lo=None) == mc.MC_ERR_NULL          # bf16 needs the operand copy
+    assert scan(dims(dtype="f32"), M_lo=MIS) == mc.MC_ERR_ALIGN
+
+
+def grm(d, ws_bytes, **ptr):
+    p = dict(Q=A, U=A, X=A, M=A, M_lo=A, P=A, O_on=A, Y=A, gamma=None, ws=A)
+    p.update(ptr)
+    return mc.load().mc_grm_readout(ctypes.byref(d), p["Q"], p["U"], p["X"], p["M"], p["M_lo"],
+                                    p["P"], p["O_on"], p["Y"], p["gamma"], p["ws"], ws_bytes,
+                                    None)
+
+
+def test_grm_workspace_and_pointers():
+    d = dims()
+    need = mc.mc_workspace_bytes(d, mc.MC_OP_GRM)
+    assert need >= 4 * 1 * 1024 * 128
+    assert grm(d, need - 1) == mc.MC_ERR_WORKSPACE
+    assert grm(d, need, ws=None) == mc.MC_ERR_WORKSPACE
+    assert grm(d, need, Y=None) == mc.MC_ERR_NULL
+    assert grm(d, need, M_lo=None) == mc.MC_ERR_NULL            # bf16 reads M_lo
+    assert grm(dims(dtype="f32"), need, M=None) == mc.MC_ERR_NULL  # fp32 reads M
+    assert grm(d, need, gamma=MIS) == mc.MC_ERR_ALIGN
+    assert grm(dims(L=-5), need) == mc.MC_ERR_DIMS
+
+
+def test_ssc_arguments():
+    d = dims()
+    lib = mc.load()
+    need = mc.mc_workspace_bytes(d, mc.MC_OP_SSC, 4)
+    assert need > mc.mc_workspace_bytes(d, mc.MC_OP_GRM)
+
+    def call(k, ws_bytes, idx=A):
+        return lib.mc_ssc_readout(ctypes.byref(d), k, A, A, A, A, A, A, A, A, idx, A, ws_bytes,
+                                  None)
+    assert call(0, need) == mc.MC_ERR_DIMS
+    assert call(17, need) == mc.MC_ERR_UNSUPPORTED
+    assert call(4, need, idx=None) == mc.MC_ERR_NULL
+    assert call(4, need - 8) == mc.MC_ERR_WORKSPACE
+
+
+def test_decode_arguments_and_capacity():
+    d = dims(L=1)
+    lib = mc.load()
+    C = d.seg_len
+    n_cap = 8
+    need = mc.mc_workspace_bytes(d, mc.MC_OP_DECODE, 0, n_cap)
+    assert need > 0
+
+    def call(count, n, cap=n_cap, ws_bytes=need, y=A):
+        cnt = np.array([count], np.int32)
+        nc = np.array([n], np.int32)
+        rc = lib.mc_decode_step(ctypes.byref(d), A, A, A, A, A, A, A, cnt.ctypes.data, A, A,
+                                nc.ctypes.data, cap, y, A, ws_bytes, None)
+        return rc, int(cnt[0]), int(nc[0])
+    assert call(C - 1, n_cap) == (mc.MC_ERR_CAPACITY, C - 1, n_cap)  # unchanged on error
+    assert call(C, 0)[0] == mc.MC_ERR_DIMS
+    assert call(-1, 0)[0] == mc.MC_ERR_DIMS
+    assert call(3, n_cap + 1)[0] == mc.MC_ERR_DIMS
+    assert call(3, 2, ws_bytes=need - 1)[0] == mc.MC_ERR_WORKSPACE
+    assert call(3, 2, y=None)[0] == mc.MC_ERR_NULL
+    assert call(3, 2, y=MIS)[0] == mc.MC_ERR_ALIGN
+
+
+def test_workspace_sizes_scale_with_inputs():
+    small = mc.mc_workspace_bytes(dims(L=512), mc.MC_OP_GRM)
+    big = mc.mc_workspace_bytes(dims(L=4096), mc.MC_OP_GRM)
+    assert big >= 8 * small - 256
+    assert mc.mc_workspace_bytes(dims(B=0), mc.MC_OP_GRM) == 0
+    assert mc.mc_workspace_bytes(dims(), mc.MC_OP_PREFILL) == 0
