@@ -1,0 +1,258 @@
+"""Benchmark of the Memory Caching hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+
+A step is one GRM prefill of the L=64K workload (B=1, H=32, d=128, segment 512, bf16
+inputs, fp32 accumulation): mc_scan_prefill (per-segment scan, cached states, means, online
+read) followed by mc_grm_readout (gate + gamma-weighted read of every cached state), with
+all inputs resident in HBM.  Prints one JSON line; `value` is prefill tokens/s.  The same
+line carries the decode step of the 64x32-sequence, 256-cached-state workload (cached-state
+read GB/s), the roofline of the dominant kernel and the fp64 oracle's CPU rate.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MC-GRM prefill tokens/s (L=64K,H=32,d=128); decode cached-state HBM GB/s"
+
+
+def readout_flops(B, H, L, C, dk, dv, dg):
+    """Algorithmic FLOPs of the GRM read of one prefill: per (b,h), every token of segment s
+    reads s cached states (2*dk*dv each) and forms s+1 gate logits (2*dg each)."""
+    N = -(-L // C)
+    read = 0
+    gate = 0
+    for s in range(N):
+        n_tok = min(C, L - s * C)
+        read += n_tok * s * 2 * dk * dv
+        gate += n_tok * (s + 1) * 2 * dg
+    return B * H * (read + gate)
+
+
+def scan_flops(B, H, L, C, dk, dv):
+    """State emit (2*dk*dv per token) + causal online read inside each segment
+    (2*dk + 2*dv per token pair r <= t in the same segment)."""
+    N = -(-L // C)
+    pairs = 0
+    for s in range(N):
+        n = min(C, L - s * C)
+        pairs += n * (n + 1) // 2
+    return B * H * (L * 2 * dk * dv + pairs * 2 * (dk + dv))
+
+
+def decode_bytes(B, H, n, dk, dv, dg, elt):
+    """Algorithmic HBM bytes of one decode step: every cached state once, the online state
+    read and written, the cached means once per sequence."""
+    return B * H * n * dk * dv * elt + B * H * dk * dv * 4 * 2 + B * n * dg * 4
+
+
+def src_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "chunked_linear_attention_segment_amd", "csrc"))):
+        with open(os.path.join(ROOT, "chunked_linear_attention_segment_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+        ent = rec.get(kernel, {}).get(workload)
+        if ent and ent.get("src_hash") == src_hash():
+            return ent["bytes_per_launch"]
+    except Exception:
+        return None
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (every box has one "
+              "GPU); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import chunked_linear_attention_segment_amd as mc
+    from chunked_linear_attention_segment_amd.inputs import (WORKLOADS, make_decode_device,
+                                                             make_prefill_device)
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    w = WORKLOADS["grm_bf16_L64K"]
+    B, H, L, C, dk, dv, dg = w.B, w.H, w.L, w.seg_len, w.d_k, w.d_v, w.d_g
+    d = mc.make_dims(B, H, L, dk, dv, dg, C, 1, w.dtype, w.phi)
+    inp = make_prefill_device(w, seed=0, device=dev)
+    M, M_lo, P, O_on = mc.alloc_prefill(d, dev)
+    Y = torch.empty((B, H, L, dv), dtype=torch.bfloat16, device=dev)
+    ws = mc.workspace(d, mc.MC_OP_GRM, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mc.mc_scan_prefill(d, inp["Q"], inp["K"], inp["V"], inp["X"], M, M_lo, P, O_on,
+                           stream=stream)
+        mc.mc_grm_readout(d, inp["Q"], inp["U"], inp["X"], M, M_lo, P, O_on, Y, None, ws=ws,
+                          stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step wall time, and per-call HIP events on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        mc.mc_scan_prefill(d, inp["Q"], inp["K"], inp["V"], inp["X"], M, M_lo, P, O_on,
+                           stream=stream)
+        ev[i][1].record(stream)
+        mc.mc_grm_readout(d, inp["Q"], inp["U"], inp["X"], M, M_lo, P, O_on, Y, None, ws=ws,
+                          stream=stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    scan_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    read_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = B * L / (ms_per_step / 1e3)
+
+    fl_read = readout_flops(B, H, L, C, dk, dv, dg)
+    achieved = fl_read / (read_ms / 1e3) / 1e12
+    traffic = load_traffic("grm_readout", w.name)
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded device draw: q,k unit-norm, v,x ~ N(0,1), u = x W_u)",
+        "config": {"workload": w.name, "B": B, "H": H, "L": L, "d_k": dk, "d_v": dv, "d_g": dg,
+                   "seg_len": C, "phi": w.phi, "steps_timed": "mc_scan_prefill + mc_grm_readout"},
+        "kernels_ms": {"mc_scan_prefill": round(scan_ms, 4), "mc_grm_readout": round(read_ms, 4)},
+        "roofline": {"kernel": "mc_grm_readout (gate + gamma-weighted read)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "algorithmic_flops": fl_read},
+    }
+    del M, M_lo, P, O_on, Y, ws, inp
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        wd = WORKLOADS["decode_bf16_64x32_n256"]
+        dd = mc.make_dims(wd.B, wd.H, 1, wd.d_k, wd.d_v, wd.d_g, wd.seg_len, 1, wd.dtype, wd.phi)
+        di = make_decode_device(wd, seed=0, device=dev)
+        cap = di["n_cap"]
+        wsd = mc.workspace(dd, mc.MC_OP_DECODE, n_cap=cap, device=dev)
+        yd = torch.empty((wd.B, wd.H, wd.d_v), dtype=torch.bfloat16, device=dev)
+        M_on0 = di["M_on"].clone()
+        xs0 = di["xsum"].clone()
+
+        def dstep():
+            # restore the online state so every timed step does identical work
+            cnt = np.array([wd.count_on], np.int32)
+            nc = np.array([wd.n_cached], np.int32)
+            mc.mc_decode_step(dd, di["q"], di["k"], di["v"], di["u"], di["x"], di["M_on"],
+                              di["xsum"], cnt, di["M_cache"], di["P_cache"], nc, cap, yd, ws=wsd,
+                              stream=stream)
+
+        for _ in range(args.warmup):
+            dstep()
+        torch.cuda.synchronize()
+        dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+        for i in range(args.steps):
+            di["M_on"].copy_(M_on0)
+            di["xsum"].copy_(xs0)
+            dev_ev[i][0].record(stream)
+            dstep()
+            dev_ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        dms = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
+        by = decode_bytes(wd.B, wd.H, wd.n_cached, wd.d_k, wd.d_v, wd.d_g, 2)
+        gbs = by / (dms / 1e3) / 1e9
+        rec["decode"] = {"workload": wd.name, "metric": "decode cached-state HBM GB/s",
+                         "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(dms, 4),
+                         "tokens_per_s": round(wd.B / (dms / 1e3), 1),
+                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                      "traffic": load_traffic("decode_step", wd.name),
+                                      "algorithmic_bytes": by}}
+        del di, wsd, yd
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, rows_sample):
+    """The fp64 oracle on the host cores, on a bounded sample of the same workload: a group
+    of heads (one per thread) runs the full-length scan and evaluates `rows_sample` evenly
+    spaced rows; a second run with one row gives the scan's fixed cost, and the per-row cost
+    is extrapolated to all L rows and all heads."""
+    import torch
+
+    import oracle
+    from chunked_linear_attention_segment_amd.inputs import make_prefill_device
+
+    cores = min(16, os.cpu_count() or 1)
+    Hs = cores
+    inp = make_prefill_device(w, seed=0, device="cuda", H=Hs)
+    host = {k: v.to(torch.float64).cpu().numpy() for k, v in inp.items()}
+    del inp
+    L = w.L
+    rows = np.linspace(0, L - 1, rows_sample).astype(np.int32)
+    rows = np.unique(rows)
+    t0 = time.perf_counter()
+    oracle.prefill(host["Q"], host["K"], host["V"], host["U"], host["X"], seg_len=w.seg_len,
+                   phi=w.phi, rows=np.array([L - 1], np.int32), n_threads=cores)
+    t_scan = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.prefill(host["Q"], host["K"], host["V"], host["U"], host["X"], seg_len=w.seg_len,
+                   phi=w.phi, rows=rows, n_threads=cores)
+    t_rows = time.perf_counter() - t0
+    per_row = max(t_rows - t_scan, 0.0) / len(rows)
+    t_full_group = t_scan + per_row * L          # Hs heads, all L rows
+    t_full = t_full_group * (w.H / Hs) * w.B
+    return {"value": round(w.B * L / t_full, 2), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d of %d heads (one per thread), full-length scan, %d evenly spaced rows "
+                      "of %d; scan %.2fs + rows %.2fs, extrapolated linearly in rows and heads"
+                      % (Hs, w.H, len(rows), L, t_scan, t_rows - t_scan)}
+
+
+if __name__ == "__main__":
+    main()

@@ -192,17 +192,68 @@ static int launch_readout(const mc_dims& d, int top_k, const void* Q, const void
     return (int)hipErrorInvalidValue;
 }
 
+// gamma_t^(i) written out on request (a diagnostic output of the bf16 path, whose fused
+// kernel never materialises the weights): one thread per token, fp32, straight from
+// the definition.
+template <typename T>
+__global__ void gamma_kernel(const T* __restrict__ U, const float* __restrict__ xcum,
+                             const float* __restrict__ P, int L, int C, int NS, int DG, int H,
+                             int xh, float* __restrict__ gamma) {
+    const int t = blockIdx.x * 64 + threadIdx.x;
+    const size_t bh = blockIdx.y;
+    if (t >= L) return;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const size_t bx = (size_t)b * xh + (xh == 1 ? 0 : h);
+    const int s = t / C, j = t % C;
+    const T* u = U + (bh * L + t) * DG;
+    const float* xr = xcum + (bx * L + t) * DG;
+    float a_on = 0.f;
+    for (int e = 0; e < DG; ++e) a_on += ld(u, e) * (xr[e] / (float)(j + 1));
+    auto logit = [&](int i) {
+        const float* Pi = P + (bx * NS + i) * DG;
+        float a = 0.f;
+        for (int e = 0; e < DG; ++e) a += ld(u, e) * Pi[e];
+        return a;
+    };
+    float mx = a_on;
+    for (int i = 0; i < s; ++i) mx = fmaxf(mx, logit(i));
+    float z = __expf(a_on - mx);
+    for (int i = 0; i < s; ++i) z += __expf(logit(i) - mx);
+    float* gr = gamma + (bh * L + t) * (size_t)NS;
+    for (int i = 0; i < NS; ++i)
+        gr[i] = i < s ? __expf(logit(i) - mx) / z : (i == s ? __expf(a_on - mx) / z : 0.f);
+}
+
+int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* U,
+                     const float* xcum, const uint16_t* M_lo, const float* P,
+                     const float* O_on, const int32_t* idx, void* Y, void* stream);
+
 int launch_grm_readout(const mc_dims& d, const void* Q, const void* U, const float* xcum,
                        const float* M, const uint16_t* M_lo, const float* P,
                        const float* O_on, void* Y, float* gamma, void* stream) {
-    return launch_readout<false>(d, 0, Q, U, xcum, M, M_lo, P, O_on, nullptr, Y, gamma,
-                                 (hipStream_t)stream);
+    if (d.dtype != MC_BF16)
+        return launch_readout<false>(d, 0, Q, U, xcum, M, M_lo, P, O_on, nullptr, Y, gamma,
+                                     (hipStream_t)stream);
+    int rc = launch_read_mfma(d, false, 0, Q, U, xcum, M_lo, P, O_on, nullptr, Y, stream);
+    if (rc < 0)
+        rc = launch_readout<false>(d, 0, Q, U, xcum, M, M_lo, P, O_on, nullptr, Y, nullptr,
+                                   (hipStream_t)stream);
+    if (rc || !gamma) return rc;
+    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+    hipLaunchKernelGGL(gamma_kernel<bf16_t>, dim3((d.L + 63) / 64, d.B * d.H), dim3(64), 0,
+                       (hipStream_t)stream, (const bf16_t*)U, xcum, P, d.L, d.seg_len, NS,
+                       d.d_g, d.H, d.x_heads, gamma);
+    return (int)hipGetLastError();
 }
 
 int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* U,
                        const float* xcum, const float* M, const uint16_t* M_lo,
                        const float* P, const float* O_on, const int32_t* idx, void* Y,
                        void* stream) {
+    if (d.dtype == MC_BF16) {
+        const int rc = launch_read_mfma(d, true, top_k, Q, U, xcum, M_lo, P, O_on, idx, Y, stream);
+        if (rc >= 0) return rc;
+    }
     return launch_readout<true>(d, top_k, Q, U, xcum, M, M_lo, P, O_on, idx, Y, nullptr,
                                 (hipStream_t)stream);
 }
