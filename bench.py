@@ -89,7 +89,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=32768)
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
+                    help="profiling aid: run only one workload (the JSON line then lacks the "
+                         "other part)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="profiling aid: copy a MIB-sized device buffer 3 times and exit (the "
+                         "reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (every box has one "
@@ -104,6 +110,21 @@ def main():
 
     torch.cuda.set_device(0)
     dev = "cuda"
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return
+    if args.only == "decode":
+        rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup}
+        run_decode(args, rec, dev)
+        print(json.dumps(rec), flush=True)
+        return
     w = WORKLOADS["grm_bf16_L64K"]
     B, H, L, C, dk, dv, dg = w.B, w.H, w.L, w.seg_len, w.d_k, w.d_v, w.d_g
     d = mc.make_dims(B, H, L, dk, dv, dg, C, 1, w.dtype, w.phi)
@@ -169,7 +190,21 @@ def main():
     del M, M_lo, P, O_on, Y, ws, inp
     torch.cuda.empty_cache()
 
-    if not args.no_decode:
+    if not args.no_decode and args.only == "all":
+        run_decode(args, rec, dev)
+
+    if not args.no_cpu and args.only == "all":
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(rec), flush=True)
+
+
+def run_decode(args, rec, dev):
+    import torch
+
+    import chunked_linear_attention_segment_amd as mc
+    from chunked_linear_attention_segment_amd.inputs import WORKLOADS, make_decode_device
+    stream = torch.cuda.current_stream()
+    if True:
         wd = WORKLOADS["decode_bf16_64x32_n256"]
         dd = mc.make_dims(wd.B, wd.H, 1, wd.d_k, wd.d_v, wd.d_g, wd.seg_len, 1, wd.dtype, wd.phi)
         di = make_decode_device(wd, seed=0, device=dev)
@@ -212,10 +247,6 @@ def main():
                                       "algorithmic_bytes": by}}
         del di, wsd, yd
         torch.cuda.empty_cache()
-
-    if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
-    print(json.dumps(rec), flush=True)
 
 
 def cpu_baseline(w, rows_sample):

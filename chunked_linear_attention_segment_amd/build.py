@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "scan.hip", "readout.hip", "decode.hip", "grm_mfma.hip", "ssc_mfma.hip"]
+SOURCES = ["abi.cpp", "scan.hip", "readout.hip", "decode.hip", "grm_mfma.hip", "scan_mfma.hip"]
 
 # Packed-fp32 VALU ops are kept out of the device code (the host pass warns that it does
 # not know the feature; that warning is harmless).

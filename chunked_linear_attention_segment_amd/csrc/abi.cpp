@@ -13,16 +13,16 @@ static int num_segments(const mc_dims& d) { return (d.L + d.seg_len - 1) / d.seg
 
 GrmWorkspace grm_workspace(const mc_dims& d) {
     GrmWorkspace w{};
-    w.xcum = align256(sizeof(float) * (size_t)d.B * d.x_heads * d.L * d.d_g);
-    w.total = w.xcum;
+    w.aon = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
+    w.total = w.aon;
     return w;
 }
 
 SscWorkspace ssc_workspace(const mc_dims& d) {
     SscWorkspace w{};
-    w.xcum = align256(sizeof(float) * (size_t)d.B * d.x_heads * d.L * d.d_g);
+    w.aon = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
     w.xsum64 = align256(sizeof(double) * (size_t)d.B * d.x_heads * num_segments(d) * d.d_g);
-    w.total = w.xcum + w.xsum64;
+    w.total = w.aon + w.xsum64;
     return w;
 }
 
@@ -125,9 +125,9 @@ mc_status mc_grm_readout(const mc_dims* d, const void* Q, const void* U, const v
     const void* ptrs[] = {Q, U, X, M, M_lo, P, O_on, Y, gamma, ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MC_ERR_ALIGN;
-    float* xcum = (float*)ws;
-    if (launch_xcum(*d, X, xcum, stream)) return MC_ERR_HIP;
-    if (launch_grm_readout(*d, Q, U, xcum, M, M_lo, P, O_on, Y, gamma, stream)) return MC_ERR_HIP;
+    float* aon = (float*)ws;
+    if (launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
+    if (launch_grm_readout(*d, Q, U, aon, M, M_lo, P, O_on, Y, gamma, stream)) return MC_ERR_HIP;
     return MC_OK;
 }
 
@@ -146,11 +146,11 @@ mc_status mc_ssc_readout(const mc_dims* d, int32_t top_k, const void* Q, const v
     const void* ptrs[] = {Q, U, X, M, M_lo, P, O_on, Y, idx, ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MC_ERR_ALIGN;
-    float* xcum = (float*)ws;
-    double* xsum64 = (double*)((char*)ws + w.xcum);
-    if (launch_xcum(*d, X, xcum, stream)) return MC_ERR_HIP;
+    float* aon = (float*)ws;
+    double* xsum64 = (double*)((char*)ws + w.aon);
+    if (launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
     if (launch_ssc_select(*d, top_k, U, X, xsum64, idx, stream)) return MC_ERR_HIP;
-    if (launch_ssc_readout(*d, top_k, Q, U, xcum, M, M_lo, P, O_on, idx, Y, stream))
+    if (launch_ssc_readout(*d, top_k, Q, U, aon, M, M_lo, P, O_on, idx, Y, stream))
         return MC_ERR_HIP;
     return MC_OK;
 }

@@ -2,23 +2,30 @@
 //
 // Memory Caching paper §3.1, Eq. (9)-(10): for token t of segment s
 //     y_t = gamma^(s) M_t^(s) phi(q_t) + sum_{i<s} gamma^(i) M^(i) phi(q_t),
-//     gamma_t = softmax( <u_t, P_0>, ..., <u_t, P_{s-1}>, <u_t, prefix mean of X> ).
-// The online term M_t^(s) phi(q_t) arrives as O_on from the scan.  The same kernel serves
-// Sparse Selective Caching (gitcode explainer §3.4) when SSC = true: a token then weighs
-// only the segments listed for it in idx, the softmax runs over those plus the online one.
+//     gamma_t = softmax( <u_t, P_0>, ..., <u_t, P_{s-1}>, a_on[t] ),
+// a_on[t] = <u_t, prefix mean of X over t's segment> (the online segment's logit).  The
+// online term M_t^(s) phi(q_t) arrives as O_on from the scan.  With SSC = true the kernel is
+// the Sparse Selective Caching read (gitcode explainer §3.4): a token weighs only the
+// segments listed for it in idx, and its softmax runs over those and the online segment.
 //
-// Layout of the computation (transposed, so the per-token gate is a per-lane scalar):
-//   Y^T[c, t] = sum_i w_t^(i) * (M^(i) Qhat^T)[c, t]
-// One workgroup = 256 consecutive tokens of one (b, h), 8 waves.  Wave (cw, tw) owns output
-// rows c in [cw*DV/2, (cw+1)*DV/2) and tokens [64 tw, 64 tw + 64).  Per cached state i:
-//   A = M^(i) (d_v x d_k bf16, staged once in LDS for all waves, XOR-swizzled 16-B chunks),
-//   B = phi(q)^T (kept in registers for the whole kernel),
-//   the 32x32x16 MFMA partial product is scaled by the token's weight w_t^(i) and added to
-//   the fp32 accumulator.
-// The gate runs on MFMA too, in blocks of 32 states: logits^T = P_block (hi + lo bf16 split
-// of the fp32 means) x U^T, then an online softmax per token (running max m_t and sum l_t;
-// the accumulator is rescaled by exp(m_old - m_new) at each block).  The online term enters
-// as the initial accumulator with weight exp(a_on - m) = 1 at m = a_on.
+// Layout (transposed, so a token's gate weight is a per-lane scalar):
+//     Y^T[c, t] = sum_i w_t^(i) (M^(i) Qhat^T)[c, t]
+// A workgroup is 256 consecutive tokens of one (b, h) and 8 waves (two per SIMD); wave
+// (cw, tw) owns value rows [cw*DV/2, (cw+1)*DV/2) and tokens [64 tw, 64 tw + 64).  Per
+// cached state i:
+//   A = M^(i) (d_v x d_k bf16): staged once in LDS for the workgroup by direct global->LDS
+//       loads that stream state i+1 in while state i is read (two buffers); 16-byte chunks
+//       XOR-swizzled per row so the fragment reads are bank-conflict free;
+//   B = phi(q)^T: kept in registers for the whole kernel;
+//   the 32x32x16 MFMA partial product is scaled by the token weights and added to the fp32
+//   accumulator.
+// The gate runs on MFMA in blocks of 32 states: wave w forms logits^T = P_block U^T for
+// tokens [32 w, 32 w + 32) (the fp32 means split into bf16 hi + lo parts, so the
+// logits keep ~16 mantissa bits), then an online softmax per token (running max m_t and sum
+// l_t; the accumulator is rescaled by exp(m_old - m_new) per block).  The weights of block
+// b+1 are formed while block b is still being read (two LDS weight buffers), so the gate
+// costs no extra workgroup barrier.  The online term enters as the initial accumulator with
+// weight exp(a_on - m) = 1 at m = a_on.
 #include "common.cuh"
 #include "mc_internal.h"
 
@@ -34,25 +41,41 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(const u32x4_t& a, const u32x4_t
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// fp32 -> bf16 (round to nearest even) for finite values: the kernel only converts finite
+// data (inputs, means, accumulators), so the NaN branch of the general conversion is left out.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
 }
 
-constexpr int GT = 256;   // tokens per workgroup
-constexpr int GSB = 32;   // states per gate block
-constexpr int GTHREADS = 512;
+constexpr int GT = 256;       // tokens per workgroup
+constexpr int GSB = 32;       // states per gate block
+constexpr int GTHREADS = 512; // 8 waves
 
-template <int DK, int DV, bool SSC>
+// One 16-byte direct global->LDS load per lane: the 16 bytes at base + voff land at LDS
+// address lds_base + 16*lane (lds_base wave-uniform).  Issued as inline assembly so that
+// the compiler does not serialise LDS reads of the other buffer behind it; the kernel waits
+// for these loads itself (s_waitcnt vmcnt) before the barrier that publishes a buffer.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(base)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+template <int DK, int DV>
 struct GrmSmem {
-    static constexpr int DGP = 256;  // padded gate width held in LDS
     bf16_t state[2][DV * DK];
-    bf16_t p_hi[GSB * DGP];
-    bf16_t p_lo[GSB * DGP];
-    float w[GSB][GT];
-    float scale[GT];
-    float m0[GT];
+    float w[2][GSB][GT];   // gate weights of the current / next block
+    float scale[2][GT];    // exp(m_old - m_new) applied when a block starts
     float inv_l[GT];
-    uint32_t any_sel;
+    uint32_t any_sel[2];   // SSC: states of the block some token of the tile selected
 };
 
 // Map the flat block index to (b*H+h, tile).  Blocks are dealt round-robin to the 8 XCDs;
@@ -71,16 +94,17 @@ __device__ __forceinline__ void grm_tile_of_block(int bid, int BH, int T, int& b
 
 template <int DK, int DV, bool SSC>
 __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ U, const float* __restrict__ xcum,
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ U, const float* __restrict__ aon,
     const bf16_t* __restrict__ S, const float* __restrict__ P, const float* __restrict__ O_on,
     const int32_t* __restrict__ idx, int top_k, int BH, int H, int L, int C, int NS, int DG,
     int xh, int phi, bf16_t* __restrict__ Y) {
     constexpr int CPR = DK / 8;        // 16-byte chunks per state row
     constexpr int KS = DK / 16;        // MFMA k-steps over d_k
     constexpr int CB = DV / 64;        // 32-row blocks per wave (a wave owns DV/2 rows)
-    constexpr int STAGE = DV * DK / 8 / GTHREADS;  // 16-byte chunks each thread stages
-    static_assert(STAGE >= 1, "state too small for the staging layout");
-    typedef GrmSmem<DK, DV, SSC> Smem;
+    constexpr int TB = 2;              // 32-token blocks per wave
+    constexpr int STAGE = DV * DK / 8 / GTHREADS;  // direct loads per lane per state
+    static_assert(STAGE >= 1 && DV * DK / 8 % GTHREADS == 0, "staging layout");
+    typedef GrmSmem<DK, DV> Smem;
     __shared__ __attribute__((aligned(16))) char smem_raw[sizeof(Smem)];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
 
@@ -95,24 +119,131 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
     const int tile0 = tile * GT;
     const int last = min(L, tile0 + GT) - 1;
     const int s_hi = last / C;  // states 0..s_hi-1 are read by some token of the tile
+    const int nblk = (s_hi + GSB - 1) / GSB;
 
-    // ---- online logit a_on[t] = <u_t, prefix mean of X> (two threads per token) ----
-    {
-        const int tau = tid >> 1, half = tid & 1;
-        const int t = min(tile0 + tau, L - 1);
-        const float inv = 1.f / (float)(t % C + 1);
-        const bf16_t* ur = U + ((size_t)bh * L + t) * DG;
-        const float* xr = xcum + (bx * L + t) * DG;
-        float a = 0.f;
-        for (int e = half; e < DG; e += 2) a += bf16_to_f32(ur[e]) * (xr[e] * inv);
-        a += __shfl_xor(a, 1, 64);
-        if (half == 0) sm.m0[tau] = a;
+    // ---- direct global -> LDS staging of state i into buffer `buf`: load m of wave w
+    //      fills LDS chunks [(m*waves + w)*64, +64); chunk (c, kc) is stored at kc ^ (c % CPR)
+    //      of row c.  The per-lane byte offsets inside a state are fixed. ----
+    const bf16_t* Sbh = S + (size_t)bh * NS * DV * DK;
+    uint32_t soff[STAGE];
+#pragma unroll
+    for (int m = 0; m < STAGE; ++m) {
+        const int p = (m * (GTHREADS / 64) + wave) * 64 + lane;
+        const int c = p / CPR, kc = (p % CPR) ^ (c % CPR);
+        soff[m] = (uint32_t)((c * DK + kc * 8) * 2);
+    }
+    auto stage = [&](int i, int buf) {
+        const bf16_t* src = Sbh + (size_t)i * DV * DK;
+#pragma unroll
+        for (int m = 0; m < STAGE; ++m) {
+            const int p0 = (m * (GTHREADS / 64) + wave) * 64;
+            const uint32_t base = (uint32_t)(uintptr_t)&sm.state[buf][p0 * 8];
+            lds_dma16(src, soff[m], __builtin_amdgcn_readfirstlane(base));
+        }
+    };
+
+    // ---- gate state: wave w owns the softmax of tokens [32 w, 32 w + 32); both lane
+    //      halves hold the same running max / sum ----
+    constexpr int GB = 1;  // 32-token gate blocks per wave
+    int gtl[GB], gtok[GB], gseg[GB];
+    bool gval[GB];
+    float m_tok[GB], l_tok[GB];
+#pragma unroll
+    for (int g = 0; g < GB; ++g) {
+        gtl[g] = wave * 32 + l32;
+        gval[g] = (tile0 + gtl[g]) < L;
+        gtok[g] = min(tile0 + gtl[g], L - 1);
+        gseg[g] = gtok[g] / C;
+        m_tok[g] = aon[(size_t)bh * L + gtok[g]];
+        l_tok[g] = 1.f;
     }
 
-    // ---- B operand: phi(q)^T fragments of this wave's 64 tokens, kept in registers ----
-    u32x4_t qf[2][KS];
+    // logits of block nb for the lane's tokens, softmax update, weights into buffer nb & 1
+    auto gate = [&](int nb) {
+        const int i0 = nb * GSB, wb = nb & 1;
+        f32x16_t lg[GB];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+        for (int g = 0; g < GB; ++g)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lg[g][r] = 0.f;
+        const bool prow_ok = (i0 + l32) < s_hi;
+        const float* pr = P + (bx * NS + (prow_ok ? i0 + l32 : 0)) * DG;
+        for (int kc = 0; kc < DG / 16; ++kc) {
+            const int e = kc * 16 + hi32 * 8;
+            float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = p0;
+            if (prow_ok) {
+                p0 = *reinterpret_cast<const float4*>(pr + e);
+                p1 = *reinterpret_cast<const float4*>(pr + e + 4);
+            }
+            const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            u32x4_t ah, al;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t h0 = bf16_bits_rne(pv[2 * q]), h1 = bf16_bits_rne(pv[2 * q + 1]);
+                ah[q] = h0 | (h1 << 16);
+                al[q] = pack_bf16x2(pv[2 * q] - __uint_as_float(h0 << 16),
+                                    pv[2 * q + 1] - __uint_as_float(h1 << 16));
+            }
+#pragma unroll
+            for (int g = 0; g < GB; ++g) {
+                const u32x4_t bu = *reinterpret_cast<const u32x4_t*>(
+                    U + ((size_t)bh * L + gtok[g]) * DG + e);
+                lg[g] = mfma32x32x16(ah, bu, lg[g]);
+                lg[g] = mfma32x32x16(al, bu, lg[g]);
+            }
+        }
+        uint32_t wave_any = 0u;
+#pragma unroll
+        for (int g = 0; g < GB; ++g) {
+            uint32_t bits = 0xffffffffu;
+            if (SSC) {
+                bits = 0u;
+                const int32_t* sel = idx + ((size_t)bh * L + gtok[g]) * top_k;
+                for (int c = 0; c < top_k; ++c) {
+                    const int d = sel[c] - i0;
+                    if (sel[c] >= 0 && d >= 0 && d < GSB) bits |= 1u << d;
+                }
+            }
+            float bm = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r / 4) + 4 * hi32 + (r % 4);
+                const bool ok = gval[g] && (i0 + row) < gseg[g] && ((bits >> row) & 1u);
+                lg[g][r] = ok ? lg[g][r] : -INFINITY;
+                bm = fmaxf(bm, lg[g][r]);
+            }
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            const float m_new = fmaxf(m_tok[g], bm);
+            const float sc = __expf(m_tok[g] - m_new);
+            float ps = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r / 4) + 4 * hi32 + (r % 4);
+                const float wv = __expf(lg[g][r] - m_new);  // exp(-inf) = 0 for masked rows
+                ps += wv;
+                sm.w[wb][row][gtl[g]] = wv;
+            }
+            ps += __shfl_xor(ps, 32, 64);
+            l_tok[g] = l_tok[g] * sc + ps;
+            m_tok[g] = m_new;
+            if (hi32 == 0) sm.scale[wb][gtl[g]] = sc;
+            if (SSC) wave_any |= bits;
+        }
+        if (SSC) {
+            for (int o = 1; o < 64; o <<= 1) wave_any |= __shfl_xor(wave_any, o, 64);
+            if (lane == 0 && wave_any) atomicOr(&sm.any_sel[wb], wave_any);
+        }
+    };
+
+    if (SSC && tid < 2) sm.any_sel[tid] = 0u;
+    __syncthreads();
+    if (s_hi > 0) stage(0, 0);
+    if (nblk > 0) gate(0);
+
+    // ---- B operand: phi(q)^T fragments of this wave's 64 tokens, kept in registers ----
+    u32x4_t qf[TB][KS];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
         const int t = min(tile0 + tw * 64 + tb * 32 + l32, L - 1);
         const bf16_t* qr = Q + ((size_t)bh * L + t) * DK + hi32 * 8;
 #pragma unroll
@@ -131,11 +262,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
     }
 
     // ---- accumulator = O_on (the online term, weight 1 relative to m = a_on) ----
-    f32x16_t acc[CB][2];
+    f32x16_t acc[CB][TB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
+        for (int tb = 0; tb < TB; ++tb) {
             const int t = min(tile0 + tw * 64 + tb * 32 + l32, L - 1);
             const float* orow = O_on + ((size_t)bh * L + t) * DV + cw * (DV / 2) + cb * 32 + hi32 * 4;
 #pragma unroll
@@ -148,162 +279,60 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
             }
         }
 
-    // ---- gate state: wave `wave` owns the softmax of tokens [32 wave, 32 wave + 32) ----
-    const int gt = wave * 32 + l32;  // tile-local token of this lane in the gate phase
-    const int gtok = min(tile0 + gt, L - 1);
-    const int gs = gtok / C;
-    const bool gvalid = (tile0 + gt) < L;
-    const int32_t* gsel = SSC ? idx + ((size_t)bh * L + gtok) * top_k : nullptr;
-    __syncthreads();
-    float m_tok = sm.m0[gt], l_tok = 1.f;
-
-    // ---- staging of cached state i into LDS buffer `buf` (XOR swizzle of 16-B chunks) ----
-    const bf16_t* Sbh = S + (size_t)bh * NS * DV * DK;
-    u32x4_t stg[STAGE];
-    auto stage_load = [&](int i) {
-        const bf16_t* src = Sbh + (size_t)i * DV * DK;
+    // ---- the cached states, one workgroup barrier per state ----
+    for (int i = 0; i < s_hi; ++i) {
+        const int buf = i & 1, j = i % GSB, wb = (i / GSB) & 1;
+        // state i has landed for this lane; after the barrier for every lane, every wave is
+        // done with state i-1 and the weights of this block are published
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (i + 1 < s_hi) stage(i + 1, buf ^ 1);
+        if (SSC && j == 0 && tid == 0) sm.any_sel[wb ^ 1] = 0u;
+        if (j == 0) {
 #pragma unroll
-        for (int m = 0; m < STAGE; ++m) {
-            const int q = tid + GTHREADS * m;
-            stg[m] = *reinterpret_cast<const u32x4_t*>(src + (size_t)q * 8);
-        }
-    };
-    auto stage_store = [&](int buf) {
+            for (int tb = 0; tb < TB; ++tb) {
+                const float s = sm.scale[wb][tw * 64 + tb * 32 + l32];
 #pragma unroll
-        for (int m = 0; m < STAGE; ++m) {
-            const int q = tid + GTHREADS * m;
-            const int c = q / CPR, kc = q % CPR;
-            *reinterpret_cast<u32x4_t*>(&sm.state[buf][c * DK + ((kc ^ (c % CPR)) * 8)]) = stg[m];
-        }
-    };
-
-    if (s_hi > 0) {
-        stage_load(0);
-        stage_store(0);
-    }
-    const int nblk = (s_hi + GSB - 1) / GSB;
-    const int gch = (DG + 7) / 8;  // 8-element chunks of the gate width
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int i0 = blk * GSB;
-        // -- stage the means of states [i0, i0+32) as bf16 hi/lo pairs --
-        for (int e = tid; e < GSB * Smem::DGP / 2; e += GTHREADS) {
-            const int r = e / (Smem::DGP / 2), k2 = (e % (Smem::DGP / 2)) * 2;
-            float p0 = 0.f, p1 = 0.f;
-            if (i0 + r < s_hi && k2 < DG) {
-                const float* pr = P + (bx * NS + i0 + r) * DG + k2;
-                p0 = pr[0];
-                p1 = pr[1];
-            }
-            const bf16_t h0 = f32_to_bf16(p0), h1 = f32_to_bf16(p1);
-            const bf16_t l0 = f32_to_bf16(p0 - bf16_to_f32(h0)), l1 = f32_to_bf16(p1 - bf16_to_f32(h1));
-            *reinterpret_cast<uint32_t*>(&sm.p_hi[r * Smem::DGP + k2]) = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            *reinterpret_cast<uint32_t*>(&sm.p_lo[r * Smem::DGP + k2]) = (uint32_t)l0 | ((uint32_t)l1 << 16);
-        }
-        if (SSC && tid == 0) sm.any_sel = 0u;
-        __syncthreads();
-        // -- gate logits for this wave's 32 tokens x 32 states (MFMA, hi + lo) --
-        f32x16_t lg;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) lg[r] = 0.f;
-        const bf16_t* ur = U + ((size_t)bh * L + gtok) * DG;
-        for (int kc = 0; kc < (gch + 1) / 2; ++kc) {
-            const int e = kc * 16 + hi32 * 8;
-            u32x4_t bu = {0u, 0u, 0u, 0u};
-            if (e < DG) bu = *reinterpret_cast<const u32x4_t*>(ur + e);
-            const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(&sm.p_hi[l32 * Smem::DGP + e]);
-            const u32x4_t al = *reinterpret_cast<const u32x4_t*>(&sm.p_lo[l32 * Smem::DGP + e]);
-            lg = mfma32x32x16(ah, bu, lg);
-            lg = mfma32x32x16(al, bu, lg);
-        }
-        // -- online softmax update for the lane's token --
-        uint32_t bits = 0u;
-        if (SSC) {
-            for (int c = 0; c < top_k; ++c) {
-                const int sc_i = gsel[c];
-                const int d = sc_i - i0;
-                if (sc_i >= 0 && d >= 0 && d < GSB) bits |= 1u << d;
+                for (int cb = 0; cb < CB; ++cb) acc[cb][tb] *= s;
             }
         }
-        float bm = -INFINITY;
-        bool ok[16];
+        if (!SSC || ((sm.any_sel[wb] >> j) & 1u)) {
+            float w[TB];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 8 * (r / 4) + 4 * hi32 + (r % 4);
-            ok[r] = gvalid && (i0 + row) < gs && (!SSC || ((bits >> row) & 1u));
-            if (ok[r]) bm = fmaxf(bm, lg[r]);
-        }
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-        const float m_new = fmaxf(m_tok, bm);
-        const float sc = __expf(m_tok - m_new);
-        float ps = 0.f;
+            for (int tb = 0; tb < TB; ++tb) w[tb] = sm.w[wb][j][tw * 64 + tb * 32 + l32];
+            const bf16_t* st = sm.state[buf];
+            f32x16_t pp[CB][TB];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 8 * (r / 4) + 4 * hi32 + (r % 4);
-            const float wv = ok[r] ? __expf(lg[r] - m_new) : 0.f;
-            ps += wv;
-            sm.w[row][gt] = wv;
-        }
-        ps += __shfl_xor(ps, 32, 64);
-        l_tok = l_tok * sc + ps;
-        m_tok = m_new;
-        if (hi32 == 0) sm.scale[gt] = sc;
-        if (SSC) {
-            // union over the workgroup of the states any token selected in this block
-            uint32_t any = bits;
-            for (int o = 1; o < 64; o <<= 1) any |= __shfl_xor(any, o, 64);
-            if (lane == 0 && any) atomicOr(&sm.any_sel, any);
-        }
-        __syncthreads();
-        // -- rescale the accumulator to the new running max --
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const float s = sm.scale[tw * 64 + tb * 32 + l32];
+                for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) acc[cb][tb] *= s;
-        }
-        const uint32_t any_sel = SSC ? sm.any_sel : 0xffffffffu;
-        // -- the 32 states of this block --
-        const int i_end = min(s_hi, i0 + GSB);
-        for (int i = i0; i < i_end; ++i) {
-            const int buf = i & 1;
-            if (i + 1 < s_hi) stage_load(i + 1);
-            if (!SSC || ((any_sel >> (i - i0)) & 1u)) {
-                f32x16_t pp[CB][2];
+                    for (int r = 0; r < 16; ++r) pp[cb][tb][r] = 0.f;
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                    for (int tb = 0; tb < 2; ++tb)
+                for (int cb = 0; cb < CB; ++cb) {
+                    const int c = cw * (DV / 2) + cb * 32 + l32;
+                    const int kc = 2 * ks + hi32;
+                    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&st[c * DK + ((kc ^ (c % CPR)) * 8)]);
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) pp[cb][tb][r] = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) {
-                        const int c = cw * (DV / 2) + cb * 32 + l32;
-                        const int kc = 2 * ks + hi32;
-                        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-                            &sm.state[buf][c * DK + ((kc ^ (c % CPR)) * 8)]);
-#pragma unroll
-                        for (int tb = 0; tb < 2; ++tb) pp[cb][tb] = mfma32x32x16(a, qf[tb][ks], pp[cb][tb]);
-                    }
+                    for (int tb = 0; tb < TB; ++tb) pp[cb][tb] = mfma32x32x16(a, qf[tb][ks], pp[cb][tb]);
                 }
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) {
-                    const float wv = sm.w[i - i0][tw * 64 + tb * 32 + l32];
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) acc[cb][tb] += wv * pp[cb][tb];
-                }
-            }
-            if (i + 1 < s_hi) stage_store(buf ^ 1);
-            __syncthreads();
+                for (int tb = 0; tb < TB; ++tb) acc[cb][tb] += w[tb] * pp[cb][tb];
         }
+        // the next block's weights, while the other waves still read this block's
+        if (j == GSB - 1 && i + 1 < s_hi) gate(i / GSB + 1);
     }
-    if (hi32 == 0) sm.inv_l[gt] = 1.f / l_tok;
+#pragma unroll
+    for (int g = 0; g < GB; ++g)
+        if (hi32 == 0) sm.inv_l[gtl[g]] = 1.f / l_tok[g];
     __syncthreads();
 
     // ---- y = acc / l, stored as bf16 (4 consecutive rows c per register group) ----
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+    for (int tb = 0; tb < TB; ++tb) {
         const int t = tile0 + tw * 64 + tb * 32 + l32;
         if (t >= L) continue;
         const float il = sm.inv_l[tw * 64 + tb * 32 + l32];
@@ -323,30 +352,30 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
 
 template <int DK, int DV, bool SSC>
 static int launch_grm_mfma_t(const mc_dims& d, int top_k, const void* Q, const void* U,
-                             const float* xcum, const uint16_t* M_lo, const float* P,
+                             const float* aon, const uint16_t* M_lo, const float* P,
                              const float* O_on, const int32_t* idx, void* Y, hipStream_t st) {
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     const int T = (d.L + GT - 1) / GT;
     const int BH = d.B * d.H;
     hipLaunchKernelGGL((grm_mfma_kernel<DK, DV, SSC>), dim3(BH * T), dim3(GTHREADS), 0, st,
-                       (const bf16_t*)Q, (const bf16_t*)U, xcum, (const bf16_t*)M_lo, P, O_on,
+                       (const bf16_t*)Q, (const bf16_t*)U, aon, (const bf16_t*)M_lo, P, O_on,
                        idx, top_k, BH, d.H, d.L, d.seg_len, NS, d.d_g, d.x_heads, d.phi,
                        (bf16_t*)Y);
     return (int)hipGetLastError();
 }
 
-// bf16 GRM / SSC read on MFMA.  Returns -1 when the sizes are not covered (caller falls
-// back to the generic kernel), else the HIP status of the launch.
+// bf16 GRM / SSC read on MFMA.  Returns -1 when the sizes are not covered (the caller
+// falls back to the generic kernel), else the HIP status of the launch.
 int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* U,
-                     const float* xcum, const uint16_t* M_lo, const float* P,
+                     const float* aon, const uint16_t* M_lo, const float* P,
                      const float* O_on, const int32_t* idx, void* Y, void* stream) {
-    if (d.dtype != MC_BF16) return -1;
+    if (d.dtype != MC_BF16 || d.d_g % 16 != 0) return -1;
     hipStream_t st = (hipStream_t)stream;
 #define MC_MF(DK, DV)                                                                        \
     if (d.d_k == DK && d.d_v == DV)                                                          \
-        return ssc ? launch_grm_mfma_t<DK, DV, true>(d, top_k, Q, U, xcum, M_lo, P, O_on,    \
+        return ssc ? launch_grm_mfma_t<DK, DV, true>(d, top_k, Q, U, aon, M_lo, P, O_on,     \
                                                      idx, Y, st)                             \
-                   : launch_grm_mfma_t<DK, DV, false>(d, top_k, Q, U, xcum, M_lo, P, O_on,   \
+                   : launch_grm_mfma_t<DK, DV, false>(d, top_k, Q, U, aon, M_lo, P, O_on,    \
                                                       idx, Y, st);
     MC_MF(128, 128)
     MC_MF(128, 64)

@@ -10,11 +10,11 @@ namespace mc {
 
 // Byte sizes of the workspace regions, in the order they are carved out of `ws`.
 struct GrmWorkspace {
-    size_t xcum;  // fp32 [B,xh,L,dg]: inclusive prefix sums of X inside each segment
+    size_t aon;   // fp32 [B,H,L]: online gate logit <u_t, prefix mean of X>
     size_t total;
 };
 struct SscWorkspace {
-    size_t xcum;   // fp32 [B,xh,L,dg]
+    size_t aon;    // fp32 [B,H,L]
     size_t xsum64; // fp64 [B,xh,NS,dg]: segment sums of X, token order
     size_t total;
 };
@@ -36,9 +36,9 @@ int launch_scan_prefill(const mc_dims& d, const void* Q, const void* K, const vo
                         const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,
                         void* stream);
 
-int launch_xcum(const mc_dims& d, const void* X, float* xcum, void* stream);
+int launch_aon(const mc_dims& d, const void* X, const void* U, float* a_on, void* stream);
 
-int launch_grm_readout(const mc_dims& d, const void* Q, const void* U, const float* xcum,
+int launch_grm_readout(const mc_dims& d, const void* Q, const void* U, const float* aon,
                        const float* M, const uint16_t* M_lo, const float* P,
                        const float* O_on, void* Y, float* gamma, void* stream);
 
@@ -46,7 +46,7 @@ int launch_ssc_select(const mc_dims& d, int top_k, const void* U, const void* X,
                       double* xsum64, int32_t* idx, void* stream);
 
 int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* U,
-                       const float* xcum, const float* M, const uint16_t* M_lo,
+                       const float* aon, const float* M, const uint16_t* M_lo,
                        const float* P, const float* O_on, const int32_t* idx, void* Y,
                        void* stream);
 

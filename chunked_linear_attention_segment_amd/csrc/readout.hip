@@ -13,36 +13,74 @@
 
 namespace mc {
 
-// Inclusive prefix sums of X inside each segment (fp32): xcum[t] = sum_{r=sC}^{t} x_r.
-// One workgroup per (segment, b*xh+hx); thread e scans column e.
+// Online gate logit of every token: a_on[b,h,t] = <u_t, prefix mean of X over t's segment>
+// (Memory Caching paper §3.1, Eq. 10 with the causal prefix mean for the online segment).
+// One workgroup per (segment, b, group of 4 heads): the segment's X is walked in chunks of
+// 64 tokens; the inclusive prefix sums of a chunk are formed in LDS (thread e scans column
+// e, carrying the sums of the earlier chunks); then each dot product <u_t, xcum_t> is taken
+// by 16 lanes, each over 8-element slices of the gate width (16-byte loads of U).
 template <typename T>
-__global__ void xcum_kernel(const T* __restrict__ X, int L, int C, int DG,
-                            float* __restrict__ xcum) {
-    const int s = blockIdx.x;
-    const size_t bx = blockIdx.y;
-    const int t0 = s * C;
-    const int len = min(C, L - t0);
-    for (int e = threadIdx.x; e < DG; e += blockDim.x) {
-        float acc = 0.f;
-        for (int j = 0; j < len; ++j) {
-            const size_t o = (bx * L + t0 + j) * DG + e;
-            acc += ld(X, o);
-            xcum[o] = acc;
+__global__ __launch_bounds__(256) void aon_kernel(const T* __restrict__ X,
+                                                  const T* __restrict__ U, int L, int C,
+                                                  int DG, int H, int xh,
+                                                  float* __restrict__ a_on) {
+    __shared__ float xs[64][260];
+    __shared__ float carry[256];
+    const int s = blockIdx.x, b = blockIdx.y, h0 = blockIdx.z * 4;
+    const int t0 = s * C, len = min(C, L - t0);
+    const int tid = threadIdx.x;
+    const int q = tid & 15, slot = tid >> 4;  // 16 lanes per dot product, 16 dots at a time
+    const int nh = min(4, H - h0);
+    // with per-head X each head of the group needs its own prefix sums
+    const int npass = (xh == 1) ? 1 : nh;
+    for (int pass = 0; pass < npass; ++pass) {
+        const int hx = (xh == 1) ? 0 : h0 + pass;
+        const T* Xb = X + ((size_t)b * xh + hx) * L * DG;
+        for (int e = tid; e < DG; e += 256) carry[e] = 0.f;
+        for (int j0 = 0; j0 < len; j0 += 64) {
+            const int n = min(64, len - j0);
+            __syncthreads();
+            for (int e = tid; e < n * DG; e += 256)
+                xs[e / DG][e % DG] = ld(Xb, (size_t)(t0 + j0 + e / DG) * DG + e % DG);
+            __syncthreads();
+            for (int e = tid; e < DG; e += 256) {
+                float acc = carry[e];
+                for (int r = 0; r < n; ++r) {
+                    acc += xs[r][e];
+                    xs[r][e] = acc;
+                }
+                carry[e] = acc;
+            }
+            __syncthreads();
+            const int nhp = (xh == 1) ? nh : 1;  // heads served by this pass
+            for (int item = slot; item < nhp * 64; item += 16) {
+                const int hh = (xh == 1) ? item / 64 : pass, tt = item % 64;
+                if (tt >= n) continue;
+                const int t = t0 + j0 + tt;
+                const T* ur = U + (((size_t)b * H + h0 + hh) * L + t) * DG;
+                float a = 0.f;
+                for (int e0 = q * 8; e0 < DG; e0 += 128) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) a += ld(ur, (size_t)(e0 + e)) * xs[tt][e0 + e];
+                }
+                a = warp_sum(a, 16);
+                if (q == 0) a_on[((size_t)b * H + h0 + hh) * L + t] = a / (float)(j0 + tt + 1);
+            }
         }
+        __syncthreads();
     }
 }
 
-int launch_xcum(const mc_dims& d, const void* X, float* xcum, void* stream) {
+int launch_aon(const mc_dims& d, const void* X, const void* U, float* a_on, void* stream) {
     hipStream_t st = (hipStream_t)stream;
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
-    dim3 grid(NS, d.B * d.x_heads);
-    const int threads = d.d_g < 256 ? ((d.d_g + 63) / 64) * 64 : 256;
+    dim3 grid(NS, d.B, (d.H + 3) / 4);
     if (d.dtype == MC_BF16)
-        hipLaunchKernelGGL(xcum_kernel<bf16_t>, grid, dim3(threads), 0, st, (const bf16_t*)X,
-                           d.L, d.seg_len, d.d_g, xcum);
+        hipLaunchKernelGGL(aon_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)X,
+                           (const bf16_t*)U, d.L, d.seg_len, d.d_g, d.H, d.x_heads, a_on);
     else
-        hipLaunchKernelGGL(xcum_kernel<float>, grid, dim3(threads), 0, st, (const float*)X, d.L,
-                           d.seg_len, d.d_g, xcum);
+        hipLaunchKernelGGL(aon_kernel<float>, grid, dim3(256), 0, st, (const float*)X,
+                           (const float*)U, d.L, d.seg_len, d.d_g, d.H, d.x_heads, a_on);
     return (int)hipGetLastError();
 }
 
@@ -53,7 +91,7 @@ int launch_xcum(const mc_dims& d, const void* X, float* xcum, void* stream) {
 // each token to the segments listed in idx.
 template <typename T, typename TS, int DK, int DV, bool SSC>
 __global__ __launch_bounds__(256) void readout_valu_kernel(
-    const T* __restrict__ Q, const T* __restrict__ U, const float* __restrict__ xcum,
+    const T* __restrict__ Q, const T* __restrict__ U, const float* __restrict__ aon,
     const TS* __restrict__ S, const float* __restrict__ P, const float* __restrict__ O_on,
     const int32_t* __restrict__ idx, int top_k, int L, int C, int NS, int DG, int H, int xh,
     int phi, T* __restrict__ Y, float* __restrict__ gamma) {
@@ -70,7 +108,7 @@ __global__ __launch_bounds__(256) void readout_valu_kernel(
     const int t = tile0 + tt;
     const bool valid = t < L;
     const int tc = valid ? t : L - 1;  // clamped token for address formation
-    const int s = tc / C, j = tc % C;
+    const int s = tc / C;
     const int last = min(L, tile0 + TT) - 1;
     const int s_hi = last / C;  // largest segment index in this tile
 
@@ -83,13 +121,7 @@ __global__ __launch_bounds__(256) void readout_valu_kernel(
     // this thread's slice of u_t for the gate dots
     const int gch = DG / 8;
     const size_t urow = (bh * L + tc) * DG;
-    float a_on = 0.f;
-    {
-        const float inv = 1.f / (float)(j + 1);
-        const size_t xrow = (bx * L + tc) * DG;
-        for (int e = p * gch; e < (p + 1) * gch; ++e) a_on += ld(U, urow + e) * (xcum[xrow + e] * inv);
-        a_on = warp_sum(a_on, 8);
-    }
+    const float a_on = aon[bh * L + tc];
     int sel[16];
     if (SSC) {
         for (int c = 0; c < 16; ++c) sel[c] = (c < top_k) ? idx[(bh * L + tc) * top_k + c] : -1;
@@ -159,29 +191,29 @@ __global__ __launch_bounds__(256) void readout_valu_kernel(
 
 template <typename T, typename TS, int DK, int DV, bool SSC>
 static int launch_readout_t(const mc_dims& d, int top_k, const void* Q, const void* U,
-                            const float* xcum, const void* S, const float* P,
+                            const float* aon, const void* S, const float* P,
                             const float* O_on, const int32_t* idx, void* Y, float* gamma,
                             hipStream_t st) {
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     dim3 grid((d.L + 31) / 32, d.B * d.H);
     hipLaunchKernelGGL((readout_valu_kernel<T, TS, DK, DV, SSC>), grid, dim3(256), 0, st,
-                       (const T*)Q, (const T*)U, xcum, (const TS*)S, P, O_on, idx, top_k, d.L,
+                       (const T*)Q, (const T*)U, aon, (const TS*)S, P, O_on, idx, top_k, d.L,
                        d.seg_len, NS, d.d_g, d.H, d.x_heads, d.phi, (T*)Y, gamma);
     return (int)hipGetLastError();
 }
 
 template <bool SSC>
 static int launch_readout(const mc_dims& d, int top_k, const void* Q, const void* U,
-                          const float* xcum, const float* M, const uint16_t* M_lo,
+                          const float* aon, const float* M, const uint16_t* M_lo,
                           const float* P, const float* O_on, const int32_t* idx, void* Y,
                           float* gamma, hipStream_t st) {
 #define MC_RD(DK, DV)                                                                      \
     if (d.d_k == DK && d.d_v == DV)                                                        \
         return d.dtype == MC_BF16                                                          \
-                   ? launch_readout_t<bf16_t, bf16_t, DK, DV, SSC>(d, top_k, Q, U, xcum,   \
+                   ? launch_readout_t<bf16_t, bf16_t, DK, DV, SSC>(d, top_k, Q, U, aon,   \
                                                                    M_lo, P, O_on, idx, Y,  \
                                                                    gamma, st)              \
-                   : launch_readout_t<float, float, DK, DV, SSC>(d, top_k, Q, U, xcum, M,  \
+                   : launch_readout_t<float, float, DK, DV, SSC>(d, top_k, Q, U, aon, M,  \
                                                                  P, O_on, idx, Y, gamma,   \
                                                                  st);
     MC_RD(128, 128)
@@ -196,7 +228,7 @@ static int launch_readout(const mc_dims& d, int top_k, const void* Q, const void
 // kernel never materialises the weights): one thread per token, fp32, straight from
 // the definition.
 template <typename T>
-__global__ void gamma_kernel(const T* __restrict__ U, const float* __restrict__ xcum,
+__global__ void gamma_kernel(const T* __restrict__ U, const float* __restrict__ aon,
                              const float* __restrict__ P, int L, int C, int NS, int DG, int H,
                              int xh, float* __restrict__ gamma) {
     const int t = blockIdx.x * 64 + threadIdx.x;
@@ -204,11 +236,9 @@ __global__ void gamma_kernel(const T* __restrict__ U, const float* __restrict__ 
     if (t >= L) return;
     const int b = (int)(bh / H), h = (int)(bh % H);
     const size_t bx = (size_t)b * xh + (xh == 1 ? 0 : h);
-    const int s = t / C, j = t % C;
+    const int s = t / C;
     const T* u = U + (bh * L + t) * DG;
-    const float* xr = xcum + (bx * L + t) * DG;
-    float a_on = 0.f;
-    for (int e = 0; e < DG; ++e) a_on += ld(u, e) * (xr[e] / (float)(j + 1));
+    const float a_on = aon[bh * L + t];
     auto logit = [&](int i) {
         const float* Pi = P + (bx * NS + i) * DG;
         float a = 0.f;
@@ -225,36 +255,36 @@ __global__ void gamma_kernel(const T* __restrict__ U, const float* __restrict__ 
 }
 
 int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* U,
-                     const float* xcum, const uint16_t* M_lo, const float* P,
+                     const float* aon, const uint16_t* M_lo, const float* P,
                      const float* O_on, const int32_t* idx, void* Y, void* stream);
 
-int launch_grm_readout(const mc_dims& d, const void* Q, const void* U, const float* xcum,
+int launch_grm_readout(const mc_dims& d, const void* Q, const void* U, const float* aon,
                        const float* M, const uint16_t* M_lo, const float* P,
                        const float* O_on, void* Y, float* gamma, void* stream) {
     if (d.dtype != MC_BF16)
-        return launch_readout<false>(d, 0, Q, U, xcum, M, M_lo, P, O_on, nullptr, Y, gamma,
+        return launch_readout<false>(d, 0, Q, U, aon, M, M_lo, P, O_on, nullptr, Y, gamma,
                                      (hipStream_t)stream);
-    int rc = launch_read_mfma(d, false, 0, Q, U, xcum, M_lo, P, O_on, nullptr, Y, stream);
+    int rc = launch_read_mfma(d, false, 0, Q, U, aon, M_lo, P, O_on, nullptr, Y, stream);
     if (rc < 0)
-        rc = launch_readout<false>(d, 0, Q, U, xcum, M, M_lo, P, O_on, nullptr, Y, nullptr,
+        rc = launch_readout<false>(d, 0, Q, U, aon, M, M_lo, P, O_on, nullptr, Y, nullptr,
                                    (hipStream_t)stream);
     if (rc || !gamma) return rc;
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     hipLaunchKernelGGL(gamma_kernel<bf16_t>, dim3((d.L + 63) / 64, d.B * d.H), dim3(64), 0,
-                       (hipStream_t)stream, (const bf16_t*)U, xcum, P, d.L, d.seg_len, NS,
+                       (hipStream_t)stream, (const bf16_t*)U, aon, P, d.L, d.seg_len, NS,
                        d.d_g, d.H, d.x_heads, gamma);
     return (int)hipGetLastError();
 }
 
 int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* U,
-                       const float* xcum, const float* M, const uint16_t* M_lo,
+                       const float* aon, const float* M, const uint16_t* M_lo,
                        const float* P, const float* O_on, const int32_t* idx, void* Y,
                        void* stream) {
     if (d.dtype == MC_BF16) {
-        const int rc = launch_read_mfma(d, true, top_k, Q, U, xcum, M_lo, P, O_on, idx, Y, stream);
+        const int rc = launch_read_mfma(d, true, top_k, Q, U, aon, M_lo, P, O_on, idx, Y, stream);
         if (rc >= 0) return rc;
     }
-    return launch_readout<true>(d, top_k, Q, U, xcum, M, M_lo, P, O_on, idx, Y, nullptr,
+    return launch_readout<true>(d, top_k, Q, U, aon, M, M_lo, P, O_on, idx, Y, nullptr,
                                 (hipStream_t)stream);
 }
 

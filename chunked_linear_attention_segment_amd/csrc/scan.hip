@@ -108,13 +108,19 @@ static int launch_scan_dt(const mc_dims& d, const void* Q, const void* K, const 
     return launch_scan_t<T, 64, 64>(d, Q, K, V, M, M_lo, O_on, st);
 }
 
+int launch_scan_mfma(const mc_dims& d, const void* Q, const void* K, const void* V, float* M,
+                     uint16_t* M_lo, float* O_on, void* stream);
+
 int launch_scan_prefill(const mc_dims& d, const void* Q, const void* K, const void* V,
                         const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,
                         void* stream) {
     hipStream_t st = (hipStream_t)stream;
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
-    int rc;
-    if (d.dtype == MC_BF16)
+    int rc = -1;
+    if (d.dtype == MC_BF16) rc = launch_scan_mfma(d, Q, K, V, M, M_lo, O_on, stream);
+    if (rc >= 0) {
+        if (rc) return rc;
+    } else if (d.dtype == MC_BF16)
         rc = launch_scan_dt<bf16_t>(d, Q, K, V, M, M_lo, O_on, st);
     else
         rc = launch_scan_dt<float>(d, Q, K, V, M, M_lo, O_on, st);

@@ -1,0 +1,267 @@
+// scan_mfma.hip -- the MC write path on bf16 MFMA (gfx950): per-segment chunked scan.
+//
+// Memory Caching paper §3, Eq. (4b): inside segment s the memory starts from zero and runs
+// M_t = M_{t-1} + v_t phi(k_t)^T; its state after the segment's last token is cached, and
+// token t reads the memory after its own update (§3.1, Eq. 6/8): O_on[t] = M_t^(s) phi(q_t).
+//
+// One workgroup per (segment, b*H+h); the segment is walked in chunks of CH = 64 tokens.
+// With M_prev the state before the chunk, for every token t of the chunk
+//     O_on[t] = M_prev phi(q_t) + sum_{r <= t in chunk} (phi(q_t) . phi(k_r)) v_r
+//     M      += sum_{r in chunk} v_r phi(k_r)^T
+// all on 32x32x16 bf16 MFMA with fp32 accumulation.  Wave w (DV/32 waves) owns value rows
+// cv in [32w, 32w+32): it keeps the fp32 state M^T[d][cv] of those rows in its accumulator
+// registers for the whole segment, and its bf16 copy doubles as the A operand of the
+// M_prev phi(q) term -- the accumulator's row order is reproduced in the k order of the
+// phi(q) operand, so no shuffle is needed.  phi(k) and v are staged transposed in LDS (the
+// token index is the contraction index of the state update); the causal score block
+// S^T[r][t] = phi(k_r) . phi(q_t) goes through LDS as bf16.
+#include "common.cuh"
+#include "mc_internal.h"
+
+namespace mc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16_t scan_mfma(const u32x4_t& a, const u32x4_t& b,
+                                              const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pk2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// phi applied to 4 bf16 values held in two 32-bit words.
+__device__ __forceinline__ u32x2_t phi4(u32x2_t v, int phi) {
+    if (!phi) return v;
+    u32x2_t o;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const float x0 = __uint_as_float(v[e] << 16);
+        const float x1 = __uint_as_float(v[e] & 0xffff0000u);
+        o[e] = pk2(feature(x0, 1), feature(x1, 1));
+    }
+    return o;
+}
+
+constexpr int CH = 64;    // tokens per chunk
+constexpr int TPAD = 72;  // row stride (elements) of the token-indexed LDS tiles
+
+template <int DK, int DV>
+__global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    int L, int C, int NS, int phi, float* __restrict__ M, bf16_t* __restrict__ M_lo,
+    float* __restrict__ O_on) {
+    constexpr int NT = DV * 2;      // threads: one wave per 32 value rows
+    constexpr int DB = DK / 32;     // 32-row blocks of d
+    constexpr int KSD = DK / 16;    // k-steps over d
+    __shared__ __attribute__((aligned(16))) bf16_t kt[DK][TPAD];  // phi(k)^T  [d][r]
+    __shared__ __attribute__((aligned(16))) bf16_t vt[DV][TPAD];  // v^T       [cv][r]
+    __shared__ __attribute__((aligned(16))) bf16_t sc[CH][TPAD];  // masked scores [t][r]
+
+    const int s = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int t0 = s * C;
+    const int len = min(C, L - t0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, half = lane >> 5;
+
+    f32x16_t mt[DB];  // M^T[d][cv] for this wave's 32 value rows, fp32
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt[db][r] = 0.f;
+    u32x4_t ma[KSD];  // bf16 copy of M_prev in A-operand form (k-step k = rows 16k..16k+15)
+
+    const bf16_t* Qs = Q + (bh * L + t0) * DK;
+    const bf16_t* Ks = K + (bh * L + t0) * DK;
+    const bf16_t* Vs = V + (bh * L + t0) * DV;
+
+    for (int j0 = 0; j0 < len; j0 += CH) {
+        const int n = min(CH, len - j0);
+        // ---- phi(q) B-fragments (k order of the accumulator rows) for both token blocks ----
+        u32x4_t qb[2][KSD];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const int tl = tb * 32 + l32;
+            const bool ok = tl < n;
+            const bf16_t* qr = Qs + (size_t)(j0 + (ok ? tl : 0)) * DK + half * 4;
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
+                if (ok) {
+                    lo = phi4(*reinterpret_cast<const u32x2_t*>(qr + ks * 16), phi);
+                    hi = phi4(*reinterpret_cast<const u32x2_t*>(qr + ks * 16 + 8), phi);
+                }
+                qb[tb][ks] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+            }
+        }
+        // ---- O^T = M_prev phi(q)^T (first term of the online read) ----
+        f32x16_t ot[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ot[tb][r] = 0.f;
+        if (j0 > 0) {
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) ot[tb] = scan_mfma(ma[ks], qb[tb][ks], ot[tb]);
+        }
+        // ---- stage phi(k)^T and v^T (token pairs packed in 32-bit LDS words) ----
+        for (int it = tid; it < (CH / 2) * (DK / 8); it += NT) {
+            const int p = it % (CH / 2), dc = (it / (CH / 2)) * 8;
+            const int r0 = 2 * p, r1 = 2 * p + 1;
+            u32x4_t a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+            if (r0 < n) a = *reinterpret_cast<const u32x4_t*>(Ks + (size_t)(j0 + r0) * DK + dc);
+            if (r1 < n) b = *reinterpret_cast<const u32x4_t*>(Ks + (size_t)(j0 + r1) * DK + dc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float a0 = __uint_as_float(a[e] << 16), a1 = __uint_as_float(a[e] & 0xffff0000u);
+                float b0 = __uint_as_float(b[e] << 16), b1 = __uint_as_float(b[e] & 0xffff0000u);
+                if (phi) {
+                    a0 = r0 < n ? feature(a0, 1) : 0.f;
+                    a1 = r0 < n ? feature(a1, 1) : 0.f;
+                    b0 = r1 < n ? feature(b0, 1) : 0.f;
+                    b1 = r1 < n ? feature(b1, 1) : 0.f;
+                }
+                *reinterpret_cast<uint32_t*>(&kt[dc + 2 * e][r0]) = pk2(a0, b0);
+                *reinterpret_cast<uint32_t*>(&kt[dc + 2 * e + 1][r0]) = pk2(a1, b1);
+            }
+        }
+        for (int it = tid; it < (CH / 2) * (DV / 8); it += NT) {
+            const int p = it % (CH / 2), dc = (it / (CH / 2)) * 8;
+            const int r0 = 2 * p, r1 = 2 * p + 1;
+            u32x4_t a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+            if (r0 < n) a = *reinterpret_cast<const u32x4_t*>(Vs + (size_t)(j0 + r0) * DV + dc);
+            if (r1 < n) b = *reinterpret_cast<const u32x4_t*>(Vs + (size_t)(j0 + r1) * DV + dc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                *reinterpret_cast<uint32_t*>(&vt[dc + 2 * e][r0]) =
+                    (a[e] & 0xffffu) | (b[e] << 16);
+                *reinterpret_cast<uint32_t*>(&vt[dc + 2 * e + 1][r0]) =
+                    (a[e] >> 16) | (b[e] & 0xffff0000u);
+            }
+        }
+        // ---- causal scores S^T[r][t] = phi(k_r).phi(q_t), r <= t: blocks (rb,tb) = (0,0),
+        //      (0,1), (1,1) dealt to the waves; block (1,0) is all masked and never read ----
+        for (int blk = wave; blk < 3; blk += NT / 64) {
+            const int rb = blk == 2 ? 1 : 0, tb = blk == 0 ? 0 : 1;
+            const int rl = rb * 32 + l32;
+            const bool ok = rl < n;
+            const bf16_t* kr = Ks + (size_t)(j0 + (ok ? rl : 0)) * DK + half * 4;
+            f32x16_t sacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
+                if (ok) {
+                    lo = phi4(*reinterpret_cast<const u32x2_t*>(kr + ks * 16), phi);
+                    hi = phi4(*reinterpret_cast<const u32x2_t*>(kr + ks * 16 + 8), phi);
+                }
+                sacc = scan_mfma(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, tb ? qb[1][ks] : qb[0][ks],
+                                 sacc);
+            }
+            const int t = tb * 32 + l32;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int r = rb * 32 + 8 * g + 4 * half;
+                float v0 = (r + 0 <= t) ? sacc[4 * g + 0] : 0.f;
+                float v1 = (r + 1 <= t) ? sacc[4 * g + 1] : 0.f;
+                float v2 = (r + 2 <= t) ? sacc[4 * g + 2] : 0.f;
+                float v3 = (r + 3 <= t) ? sacc[4 * g + 3] : 0.f;
+                *reinterpret_cast<u32x2_t*>(&sc[t][r]) = u32x2_t{pk2(v0, v1), pk2(v2, v3)};
+            }
+        }
+        __syncthreads();
+        // ---- O^T += v^T S^T (intra-chunk term) and M^T += phi(k)^T v (state update) ----
+        const int cv = wave * 32 + l32;
+        u32x4_t va[CH / 16];
+#pragma unroll
+        for (int ks = 0; ks < CH / 16; ++ks)
+            va[ks] = *reinterpret_cast<const u32x4_t*>(&vt[cv][ks * 16 + half * 8]);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const int t = tb * 32 + l32;
+#pragma unroll
+            for (int ks = 0; ks < (tb + 1) * 2; ++ks) {
+                const u32x4_t sb = *reinterpret_cast<const u32x4_t*>(&sc[t][ks * 16 + half * 8]);
+                ot[tb] = scan_mfma(va[ks], sb, ot[tb]);
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int d = db * 32 + l32;
+#pragma unroll
+            for (int ks = 0; ks < CH / 16; ++ks) {
+                const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(&kt[d][ks * 16 + half * 8]);
+                mt[db] = scan_mfma(ka, va[ks], mt[db]);
+            }
+        }
+        // ---- online read out: O_on[t][cv] (4 consecutive cv per register group) ----
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const int tl = tb * 32 + l32;
+            if (tl < n) {
+                float* orow = O_on + (bh * L + t0 + j0 + tl) * DV + wave * 32 + half * 4;
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<float4*>(orow + 8 * g) =
+                        make_float4(ot[tb][4 * g], ot[tb][4 * g + 1], ot[tb][4 * g + 2],
+                                    ot[tb][4 * g + 3]);
+            }
+        }
+        // ---- bf16 copy of the updated state as the next chunk's A operand ----
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                ma[2 * db + hh] = u32x4_t{pk2(mt[db][8 * hh + 0], mt[db][8 * hh + 1]),
+                                          pk2(mt[db][8 * hh + 2], mt[db][8 * hh + 3]),
+                                          pk2(mt[db][8 * hh + 4], mt[db][8 * hh + 5]),
+                                          pk2(mt[db][8 * hh + 6], mt[db][8 * hh + 7])};
+        __syncthreads();
+    }
+    // ---- emit the segment state: M[cv][d] (fp32 and bf16), 4 consecutive d per group ----
+    const int cv = wave * 32 + l32;
+    const size_t mo = ((bh * NS + s) * DV + cv) * (size_t)DK;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + 8 * g + 4 * half;
+            *reinterpret_cast<float4*>(M + mo + d) =
+                make_float4(mt[db][4 * g], mt[db][4 * g + 1], mt[db][4 * g + 2], mt[db][4 * g + 3]);
+            *reinterpret_cast<u32x2_t*>(M_lo + mo + d) =
+                u32x2_t{pk2(mt[db][4 * g], mt[db][4 * g + 1]), pk2(mt[db][4 * g + 2], mt[db][4 * g + 3])};
+        }
+}
+
+template <int DK, int DV>
+static int launch_scan_mfma_t(const mc_dims& d, const void* Q, const void* K, const void* V,
+                              float* M, uint16_t* M_lo, float* O_on, hipStream_t st) {
+    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+    hipLaunchKernelGGL((scan_mfma_kernel<DK, DV>), dim3(NS, d.B * d.H), dim3(DV * 2), 0, st,
+                       (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, d.L, d.seg_len, NS,
+                       d.phi, M, (bf16_t*)M_lo, O_on);
+    return (int)hipGetLastError();
+}
+
+// bf16 scan on MFMA; -1 when the sizes are not covered (the caller uses the generic kernel).
+int launch_scan_mfma(const mc_dims& d, const void* Q, const void* K, const void* V, float* M,
+                     uint16_t* M_lo, float* O_on, void* stream) {
+    if (d.dtype != MC_BF16 || !M_lo) return -1;
+    hipStream_t st = (hipStream_t)stream;
+    if (d.d_k == 128 && d.d_v == 128) return launch_scan_mfma_t<128, 128>(d, Q, K, V, M, M_lo, O_on, st);
+    if (d.d_k == 128 && d.d_v == 64) return launch_scan_mfma_t<128, 64>(d, Q, K, V, M, M_lo, O_on, st);
+    if (d.d_k == 64 && d.d_v == 128) return launch_scan_mfma_t<64, 128>(d, Q, K, V, M, M_lo, O_on, st);
+    if (d.d_k == 64 && d.d_v == 64) return launch_scan_mfma_t<64, 64>(d, Q, K, V, M, M_lo, O_on, st);
+    return -1;
+}
+
+}  // namespace mc

@@ -90,7 +90,7 @@ def grm(d, ws_bytes, **ptr):
 def test_grm_workspace_and_pointers():
     d = dims()
     need = mc.mc_workspace_bytes(d, mc.MC_OP_GRM)
-    assert need >= 4 * 1 * 1024 * 128
+    assert need >= 4 * 2 * 1024
     assert grm(d, need - 1) == mc.MC_ERR_WORKSPACE
     assert grm(d, need, ws=None) == mc.MC_ERR_WORKSPACE
     assert grm(d, need, Y=None) == mc.MC_ERR_NULL
