@@ -3,9 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
 
 A step is one GRM prefill of the L=64K workload (B=1, H=32, d=128, segment 512, bf16
-inputs, fp32 accumulation): mc_scan_prefill (per-segment scan, cached states, means, online
-read) followed by mc_grm_readout (gate + gamma-weighted read of every cached state), with
-all inputs resident in HBM.  Prints one JSON line; `value` is prefill tokens/s.  The same
+inputs, fp32 accumulation): mc_scan_prefill (per-segment scan: cached states and means)
+followed by mc_grm_readout (online read inside each segment, gate, gamma-weighted read of
+every cached state), with all inputs resident in HBM.  Prints one JSON line; `value` is prefill tokens/s.  The same
 line carries the decode step of the 64x32-sequence, 256-cached-state workload (cached-state
 read GB/s), the roofline of the dominant kernel and the fp64 oracle's CPU rate.
 """
@@ -90,6 +90,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32768)
+    ap.add_argument("--online", choices=["scan", "fused"], default="fused",
+                    help="where the online read M_t^(s) phi(q_t) is formed: written by the scan "
+                         "and read back (scan), or inside the gated read from K and V (fused)")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
                     help="profiling aid: run only one workload (the JSON line then lacks the "
                          "other part)")
@@ -129,7 +132,7 @@ def main():
     B, H, L, C, dk, dv, dg = w.B, w.H, w.L, w.seg_len, w.d_k, w.d_v, w.d_g
     d = mc.make_dims(B, H, L, dk, dv, dg, C, 1, w.dtype, w.phi)
     inp = make_prefill_device(w, seed=0, device=dev)
-    M, M_lo, P, O_on = mc.alloc_prefill(d, dev)
+    M, M_lo, P, O_on = mc.alloc_prefill(d, dev, online=(args.online == "scan"))
     Y = torch.empty((B, H, L, dv), dtype=torch.bfloat16, device=dev)
     ws = mc.workspace(d, mc.MC_OP_GRM, device=dev)
     stream = torch.cuda.current_stream()
@@ -137,8 +140,8 @@ def main():
     def step():
         mc.mc_scan_prefill(d, inp["Q"], inp["K"], inp["V"], inp["X"], M, M_lo, P, O_on,
                            stream=stream)
-        mc.mc_grm_readout(d, inp["Q"], inp["U"], inp["X"], M, M_lo, P, O_on, Y, None, ws=ws,
-                          stream=stream)
+        mc.mc_grm_readout(d, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], M, M_lo, P, O_on,
+                          Y, None, ws=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -153,8 +156,8 @@ def main():
         mc.mc_scan_prefill(d, inp["Q"], inp["K"], inp["V"], inp["X"], M, M_lo, P, O_on,
                            stream=stream)
         ev[i][1].record(stream)
-        mc.mc_grm_readout(d, inp["Q"], inp["U"], inp["X"], M, M_lo, P, O_on, Y, None, ws=ws,
-                          stream=stream)
+        mc.mc_grm_readout(d, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], M, M_lo, P, O_on,
+                          Y, None, ws=ws, stream=stream)
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -180,7 +183,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded device draw: q,k unit-norm, v,x ~ N(0,1), u = x W_u)",
         "config": {"workload": w.name, "B": B, "H": H, "L": L, "d_k": dk, "d_v": dv, "d_g": dg,
-                   "seg_len": C, "phi": w.phi, "steps_timed": "mc_scan_prefill + mc_grm_readout"},
+                   "seg_len": C, "phi": w.phi, "online_read": args.online,
+                   "steps_timed": "mc_scan_prefill + mc_grm_readout"},
         "kernels_ms": {"mc_scan_prefill": round(scan_ms, 4), "mc_grm_readout": round(read_ms, 4)},
         "roofline": {"kernel": "mc_grm_readout (gate + gamma-weighted read)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,

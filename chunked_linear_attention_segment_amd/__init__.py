@@ -61,10 +61,11 @@ def load(path: str = LIB_PATH):
         lib.mc_scan_prefill.restype = ctypes.c_int
         lib.mc_scan_prefill.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.mc_grm_readout.restype = ctypes.c_int
-        lib.mc_grm_readout.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        lib.mc_ssc_readout.restype = ctypes.c_int
-        lib.mc_ssc_readout.argtypes = [D, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
+        lib.mc_grm_readout.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P,
                                        ctypes.c_size_t, P]
+        lib.mc_ssc_readout.restype = ctypes.c_int
+        lib.mc_ssc_readout.argtypes = [D, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P, P,
+                                       P, ctypes.c_size_t, P]
         lib.mc_decode_step.restype = ctypes.c_int
         lib.mc_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P,
                                        ctypes.c_size_t, P]
@@ -128,18 +129,20 @@ def mc_scan_prefill(dims, Q, K, V, X, M, M_lo, P, O_on, ws=None, stream=None):
            "mc_scan_prefill")
 
 
-def mc_grm_readout(dims, Q, U, X, M, M_lo, P, O_on, Y, gamma=None, ws=None, stream=None):
+def mc_grm_readout(dims, Q, K, V, U, X, M, M_lo, P, O_on, Y, gamma=None, ws=None,
+                   stream=None):
     w, wb = _ws(ws)
-    _check(load().mc_grm_readout(ctypes.byref(dims), _p(Q), _p(U), _p(X), _p(M), _p(M_lo),
-                                 _p(P), _p(O_on), _p(Y), _p(gamma), w, wb, _stream(stream)),
+    _check(load().mc_grm_readout(ctypes.byref(dims), _p(Q), _p(K), _p(V), _p(U), _p(X), _p(M),
+                                 _p(M_lo), _p(P), _p(O_on), _p(Y), _p(gamma), w, wb,
+                                 _stream(stream)),
            "mc_grm_readout")
 
 
-def mc_ssc_readout(dims, top_k, Q, U, X, M, M_lo, P, O_on, Y, idx, ws=None, stream=None):
+def mc_ssc_readout(dims, top_k, Q, K, V, U, X, M, M_lo, P, O_on, Y, idx, ws=None, stream=None):
     w, wb = _ws(ws)
-    _check(load().mc_ssc_readout(ctypes.byref(dims), int(top_k), _p(Q), _p(U), _p(X), _p(M),
-                                 _p(M_lo), _p(P), _p(O_on), _p(Y), _p(idx), w, wb,
-                                 _stream(stream)),
+    _check(load().mc_ssc_readout(ctypes.byref(dims), int(top_k), _p(Q), _p(K), _p(V), _p(U),
+                                 _p(X), _p(M), _p(M_lo), _p(P), _p(O_on), _p(Y), _p(idx), w,
+                                 wb, _stream(stream)),
            "mc_ssc_readout")
 
 
@@ -169,41 +172,43 @@ def workspace(dims, op, top_k=0, n_cap=0, device="cuda"):
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
-def alloc_prefill(dims, device="cuda"):
-    """Output buffers of mc_scan_prefill: M, M_lo, P, O_on."""
+def alloc_prefill(dims, device="cuda", online=True):
+    """Output buffers of mc_scan_prefill: M, M_lo, P, O_on (None unless `online`)."""
     import torch
     NS = (dims.L + dims.seg_len - 1) // dims.seg_len
     M = torch.empty((dims.B, dims.H, NS, dims.d_v, dims.d_k), dtype=torch.float32, device=device)
     M_lo = torch.empty((dims.B, dims.H, NS, dims.d_v, dims.d_k), dtype=torch.bfloat16,
                        device=device)
     P = torch.empty((dims.B, dims.x_heads, NS, dims.d_g), dtype=torch.float32, device=device)
-    O_on = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch.float32, device=device)
+    O_on = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch.float32,
+                       device=device) if online else None
     return M, M_lo, P, O_on
 
 
-def prefill_grm(dims, Q, K, V, U, X, want_gamma=False, stream=None):
-    """scan + GRM read with freshly allocated outputs; returns a dict of tensors."""
+def prefill_grm(dims, Q, K, V, U, X, want_gamma=False, online=True, stream=None):
+    """scan + GRM read with freshly allocated outputs; returns a dict of tensors.
+    online=False skips the O_on round trip (the read forms the online term itself)."""
     import torch
-    M, M_lo, P, O_on = alloc_prefill(dims, Q.device)
+    M, M_lo, P, O_on = alloc_prefill(dims, Q.device, online)
     mc_scan_prefill(dims, Q, K, V, X, M, M_lo, P, O_on, stream=stream)
     Y = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch_dtype(dims), device=Q.device)
     NS = M.shape[2]
     G = torch.empty((dims.B, dims.H, dims.L, NS), dtype=torch.float32,
                     device=Q.device) if want_gamma else None
     ws = workspace(dims, MC_OP_GRM, device=Q.device)
-    mc_grm_readout(dims, Q, U, X, M, M_lo, P, O_on, Y, G, ws=ws, stream=stream)
+    mc_grm_readout(dims, Q, K, V, U, X, M, M_lo, P, O_on, Y, G, ws=ws, stream=stream)
     out = {"Y": Y, "M": M, "M_lo": M_lo, "P": P, "O_on": O_on}
     if want_gamma:
         out["gamma"] = G
     return out
 
 
-def prefill_ssc(dims, top_k, Q, K, V, U, X, stream=None):
+def prefill_ssc(dims, top_k, Q, K, V, U, X, online=True, stream=None):
     import torch
-    M, M_lo, P, O_on = alloc_prefill(dims, Q.device)
+    M, M_lo, P, O_on = alloc_prefill(dims, Q.device, online)
     mc_scan_prefill(dims, Q, K, V, X, M, M_lo, P, O_on, stream=stream)
     Y = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch_dtype(dims), device=Q.device)
     idx = torch.empty((dims.B, dims.H, dims.L, top_k), dtype=torch.int32, device=Q.device)
     ws = workspace(dims, MC_OP_SSC, top_k=top_k, device=Q.device)
-    mc_ssc_readout(dims, top_k, Q, U, X, M, M_lo, P, O_on, Y, idx, ws=ws, stream=stream)
+    mc_ssc_readout(dims, top_k, Q, K, V, U, X, M, M_lo, P, O_on, Y, idx, ws=ws, stream=stream)
     return {"Y": Y, "idx": idx, "M": M, "M_lo": M_lo, "P": P, "O_on": O_on}

@@ -11,18 +11,24 @@ namespace mc {
 
 static int num_segments(const mc_dims& d) { return (d.L + d.seg_len - 1) / d.seg_len; }
 
+static size_t online_ws(const mc_dims& d) {
+    return read_mfma_covers(d) ? 0 : align256(sizeof(float) * (size_t)d.B * d.H * d.L * d.d_v);
+}
+
 GrmWorkspace grm_workspace(const mc_dims& d) {
     GrmWorkspace w{};
     w.aon = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
-    w.total = w.aon;
+    w.on = online_ws(d);
+    w.total = w.aon + w.on;
     return w;
 }
 
 SscWorkspace ssc_workspace(const mc_dims& d) {
     SscWorkspace w{};
     w.aon = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
+    w.on = online_ws(d);
     w.xsum64 = align256(sizeof(double) * (size_t)d.B * d.x_heads * num_segments(d) * d.d_g);
-    w.total = w.aon + w.xsum64;
+    w.total = w.aon + w.on + w.xsum64;
     return w;
 }
 
@@ -104,7 +110,7 @@ mc_status mc_scan_prefill(const mc_dims* d, const void* Q, const void* K, const 
     (void)ws_bytes;
     mc_status st = check_dims(d, true);
     if (st != MC_OK) return st;
-    if (!Q || !K || !V || !X || !M || !P || !O_on) return MC_ERR_NULL;
+    if (!Q || !K || !V || !X || !M || !P) return MC_ERR_NULL;
     if (d->dtype == MC_BF16 && !M_lo) return MC_ERR_NULL;
     const void* ptrs[] = {Q, K, V, X, M, M_lo, P, O_on};
     for (const void* p : ptrs)
@@ -112,45 +118,58 @@ mc_status mc_scan_prefill(const mc_dims* d, const void* Q, const void* K, const 
     return launch_scan_prefill(*d, Q, K, V, X, M, M_lo, P, O_on, stream) ? MC_ERR_HIP : MC_OK;
 }
 
-mc_status mc_grm_readout(const mc_dims* d, const void* Q, const void* U, const void* X,
-                         const float* M, const uint16_t* M_lo, const float* P,
-                         const float* O_on, void* Y, float* gamma, void* ws, size_t ws_bytes,
-                         void* stream) {
+mc_status mc_grm_readout(const mc_dims* d, const void* Q, const void* K, const void* V,
+                         const void* U, const void* X, const float* M, const uint16_t* M_lo,
+                         const float* P, const float* O_on, void* Y, float* gamma, void* ws,
+                         size_t ws_bytes, void* stream) {
     mc_status st = check_dims(d, true);
     if (st != MC_OK) return st;
-    if (!Q || !U || !X || !P || !O_on || !Y) return MC_ERR_NULL;
+    if (!Q || !U || !X || !P || !Y) return MC_ERR_NULL;
+    if (!O_on && (!K || !V)) return MC_ERR_NULL;
     if (d->dtype == MC_BF16 ? !M_lo : !M) return MC_ERR_NULL;
     const GrmWorkspace w = grm_workspace(*d);
     if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
-    const void* ptrs[] = {Q, U, X, M, M_lo, P, O_on, Y, gamma, ws};
+    const void* ptrs[] = {Q, K, V, U, X, M, M_lo, P, O_on, Y, gamma, ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MC_ERR_ALIGN;
     float* aon = (float*)ws;
+    if (!O_on && w.on) {  // generic kernels: form the online read first
+        float* on = (float*)((char*)ws + w.aon);
+        if (launch_scan_online(*d, Q, K, V, on, stream)) return MC_ERR_HIP;
+        O_on = on;
+    }
     if (launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
-    if (launch_grm_readout(*d, Q, U, aon, M, M_lo, P, O_on, Y, gamma, stream)) return MC_ERR_HIP;
+    if (launch_grm_readout(*d, Q, K, V, U, aon, M, M_lo, P, O_on, Y, gamma, stream))
+        return MC_ERR_HIP;
     return MC_OK;
 }
 
-mc_status mc_ssc_readout(const mc_dims* d, int32_t top_k, const void* Q, const void* U,
-                         const void* X, const float* M, const uint16_t* M_lo, const float* P,
-                         const float* O_on, void* Y, int32_t* idx, void* ws, size_t ws_bytes,
-                         void* stream) {
+mc_status mc_ssc_readout(const mc_dims* d, int32_t top_k, const void* Q, const void* K,
+                         const void* V, const void* U, const void* X, const float* M,
+                         const uint16_t* M_lo, const float* P, const float* O_on, void* Y,
+                         int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
     mc_status st = check_dims(d, true);
     if (st != MC_OK) return st;
     if (top_k < 1) return MC_ERR_DIMS;
     if (top_k > 16) return MC_ERR_UNSUPPORTED;
-    if (!Q || !U || !X || !P || !O_on || !Y || !idx) return MC_ERR_NULL;
+    if (!Q || !U || !X || !P || !Y || !idx) return MC_ERR_NULL;
+    if (!O_on && (!K || !V)) return MC_ERR_NULL;
     if (d->dtype == MC_BF16 ? !M_lo : !M) return MC_ERR_NULL;
     const SscWorkspace w = ssc_workspace(*d);
     if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
-    const void* ptrs[] = {Q, U, X, M, M_lo, P, O_on, Y, idx, ws};
+    const void* ptrs[] = {Q, K, V, U, X, M, M_lo, P, O_on, Y, idx, ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MC_ERR_ALIGN;
     float* aon = (float*)ws;
-    double* xsum64 = (double*)((char*)ws + w.aon);
+    double* xsum64 = (double*)((char*)ws + w.aon + w.on);
+    if (!O_on && w.on) {
+        float* on = (float*)((char*)ws + w.aon);
+        if (launch_scan_online(*d, Q, K, V, on, stream)) return MC_ERR_HIP;
+        O_on = on;
+    }
     if (launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
     if (launch_ssc_select(*d, top_k, U, X, xsum64, idx, stream)) return MC_ERR_HIP;
-    if (launch_ssc_readout(*d, top_k, Q, U, aon, M, M_lo, P, O_on, idx, Y, stream))
+    if (launch_ssc_readout(*d, top_k, Q, K, V, U, aon, M, M_lo, P, O_on, idx, Y, stream))
         return MC_ERR_HIP;
     return MC_OK;
 }

@@ -9,13 +9,18 @@ typedef uint16_t bf16_t;  // bf16 storage (the upper 16 bits of an IEEE fp32)
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+typedef __bf16 hw_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float hw_f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 in one 32-bit word (lo in bits 0..15), round to nearest even: the
+// gfx950 conversion instruction (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const hw_f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, hw_bf16x2_t));
 }
+
+// fp32 -> bf16, round to nearest even.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return (bf16_t)(pack_bf16x2(f, 0.f) & 0xffffu); }
 
 // Load element i of a tensor stored as fp32 (T = float) or bf16 (T = bf16_t) as fp32.
 template <typename T> __device__ __forceinline__ float ld(const T* p, size_t i);
@@ -28,6 +33,25 @@ template <typename T> __device__ __forceinline__ void st(T* p, size_t i, float v
 template <> __device__ __forceinline__ void st<float>(float* p, size_t i, float v) { p[i] = v; }
 template <> __device__ __forceinline__ void st<bf16_t>(bf16_t* p, size_t i, float v) {
     p[i] = f32_to_bf16(v);
+}
+
+// Load 8 consecutive elements starting at element i (16-byte aligned for bf16, 32-byte for
+// fp32) as fp32.
+template <typename T> __device__ __forceinline__ void ld8(const T* p, size_t i, float* o);
+template <> __device__ __forceinline__ void ld8<float>(const float* p, size_t i, float* o) {
+    const float4 a = *reinterpret_cast<const float4*>(p + i);
+    const float4 b = *reinterpret_cast<const float4*>(p + i + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+template <> __device__ __forceinline__ void ld8<bf16_t>(const bf16_t* p, size_t i, float* o) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        o[2 * e] = __uint_as_float(w[e] << 16);
+        o[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
 }
 
 // The feature map phi applied to queries and keys: identity, or elu(z) + 1

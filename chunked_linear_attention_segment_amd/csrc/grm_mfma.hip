@@ -4,7 +4,8 @@
 //     y_t = gamma^(s) M_t^(s) phi(q_t) + sum_{i<s} gamma^(i) M^(i) phi(q_t),
 //     gamma_t = softmax( <u_t, P_0>, ..., <u_t, P_{s-1}>, a_on[t] ),
 // a_on[t] = <u_t, prefix mean of X over t's segment> (the online segment's logit).  The
-// online term M_t^(s) phi(q_t) arrives as O_on from the scan.  With SSC = true the kernel is
+// online term M_t^(s) phi(q_t) is read from O_on when the scan wrote it, else (FON = true)
+// formed in the kernel from K and V.  With SSC = true the kernel is
 // the Sparse Selective Caching read (gitcode explainer §3.4): a token weighs only the
 // segments listed for it in idx, and its softmax runs over those and the online segment.
 //
@@ -41,15 +42,6 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(const u32x4_t& a, const u32x4_t
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// fp32 -> bf16 (round to nearest even) for finite values: the kernel only converts finite
-// data (inputs, means, accumulators), so the NaN branch of the general conversion is left out.
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
-}
 
 constexpr int GT = 256;       // tokens per workgroup
 constexpr int GSB = 32;       // states per gate block
@@ -92,9 +84,10 @@ __device__ __forceinline__ void grm_tile_of_block(int bid, int BH, int T, int& b
     }
 }
 
-template <int DK, int DV, bool SSC>
+template <int DK, int DV, bool SSC, bool FON>
 __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ U, const float* __restrict__ aon,
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ U, const float* __restrict__ aon,
     const bf16_t* __restrict__ S, const float* __restrict__ P, const float* __restrict__ O_on,
     const int32_t* __restrict__ idx, int top_k, int BH, int H, int L, int C, int NS, int DG,
     int xh, int phi, bf16_t* __restrict__ Y) {
@@ -179,10 +172,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
             u32x4_t ah, al;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t h0 = bf16_bits_rne(pv[2 * q]), h1 = bf16_bits_rne(pv[2 * q + 1]);
-                ah[q] = h0 | (h1 << 16);
-                al[q] = pack_bf16x2(pv[2 * q] - __uint_as_float(h0 << 16),
-                                    pv[2 * q + 1] - __uint_as_float(h1 << 16));
+                const uint32_t hh = pack_bf16x2(pv[2 * q], pv[2 * q + 1]);
+                ah[q] = hh;
+                al[q] = pack_bf16x2(pv[2 * q] - __uint_as_float(hh << 16),
+                                    pv[2 * q + 1] - __uint_as_float(hh & 0xffff0000u));
             }
 #pragma unroll
             for (int g = 0; g < GB; ++g) {
@@ -235,10 +228,6 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
         }
     };
 
-    if (SSC && tid < 2) sm.any_sel[tid] = 0u;
-    __syncthreads();
-    if (s_hi > 0) stage(0, 0);
-    if (nblk > 0) gate(0);
 
     // ---- B operand: phi(q)^T fragments of this wave's 64 tokens, kept in registers ----
     u32x4_t qf[TB][KS];
@@ -261,23 +250,170 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
         }
     }
 
-    // ---- accumulator = O_on (the online term, weight 1 relative to m = a_on) ----
+    // ---- accumulator = the online term M_t^(s) phi(q_t), weight 1 relative to m = a_on ----
     f32x16_t acc[CB][TB];
+    if (FON) {
+        // Formed here from K and V, as the masked linear attention of each token over the
+        // keys of its own segment up to itself (the same sum as the scan's recurrence):
+        // chunks of 64 keys from the segment start of the tile's first token to its last
+        // token; scores S^T[r][t] = phi(k_r).phi(q_t) on MFMA with the phi(q) fragments
+        // already in registers, masked to segment(t) start <= r <= t, rounded to bf16 and
+        // multiplied by v^T.  The score accumulator's row order is reproduced in the k
+        // order of the v^T operand, so the scores need no reshuffle.  LDS: phi(k) rows in
+        // the first state buffer, v^T in the weight buffers (both free before the loop).
+        constexpr int VTP = 72;  // row stride (elements) of the v^T tile
+        static_assert(2 * DV * VTP * 2 <= (int)sizeof(float) * 2 * GSB * GT, "v^T tile size");
+        static_assert(64 * DK <= DV * DK, "key tile size");
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            const int t = min(tile0 + tw * 64 + tb * 32 + l32, L - 1);
-            const float* orow = O_on + ((size_t)bh * L + t) * DV + cw * (DV / 2) + cb * 32 + hi32 * 4;
+            for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 v = *reinterpret_cast<const float4*>(orow + g * 8);
-                acc[cb][tb][4 * g + 0] = v.x;
-                acc[cb][tb][4 * g + 1] = v.y;
-                acc[cb][tb][4 * g + 2] = v.z;
-                acc[cb][tb][4 * g + 3] = v.w;
+                for (int r = 0; r < 16; ++r) acc[cb][tb][r] = 0.f;
+        const int k_lo = (tile0 / C) * C;
+        const int nkc = (last - k_lo) / 64 + 1;
+        const int wt0 = tile0 + tw * 64;
+        const int wt_last = min(wt0 + 63, L - 1);
+        const int wseg0 = (min(wt0, L - 1) / C) * C;
+        const bf16_t* Kbh = K + (size_t)bh * L * DK;
+        const bf16_t* Vbh = V + (size_t)bh * L * DV;
+        // k rows of chunk kc -> state buffer kc & 1 (direct loads, rows XOR-swizzled as the
+        // states are; rows past the last token read token `last`, their scores are masked)
+        constexpr int KLD = 64 * DK / 8 / GTHREADS;  // direct loads per lane per key chunk
+        auto stage_k = [&](int kc) {
+            const int k0 = k_lo + kc * 64;
+#pragma unroll
+            for (int m = 0; m < KLD; ++m) {
+                const int p0 = (m * (GTHREADS / 64) + wave) * 64;
+                const int p = p0 + lane;
+                const int r = p / CPR, c8 = (p % CPR) ^ (r % CPR);
+                const int key = min(k0 + r, last);
+                const uint32_t base = (uint32_t)(uintptr_t)&sm.state[kc & 1][p0 * 8];
+                lds_dma16(Kbh, (uint32_t)(((size_t)key * DK + c8 * 8) * 2),
+                          __builtin_amdgcn_readfirstlane(base));
             }
+        };
+        // v rows of chunk kc: one token pair x 8 columns per lane, transposed into v^T
+        const int vp = tid % 32, vdc = (tid / 32) * 8;
+        const bool vlane = vdc < DV;
+        u32x4_t va0 = {0u, 0u, 0u, 0u}, va1 = va0;
+        auto load_v = [&](int kc) {
+            const int k0 = k_lo + kc * 64;
+            va0 = u32x4_t{0u, 0u, 0u, 0u};
+            va1 = va0;
+            if (vlane && k0 + 2 * vp <= last)
+                va0 = *reinterpret_cast<const u32x4_t*>(Vbh + (size_t)(k0 + 2 * vp) * DV + vdc);
+            if (vlane && k0 + 2 * vp + 1 <= last)
+                va1 = *reinterpret_cast<const u32x4_t*>(Vbh + (size_t)(k0 + 2 * vp + 1) * DV + vdc);
+        };
+        auto store_v = [&](int kc) {
+            bf16_t* vt = reinterpret_cast<bf16_t*>(&sm.w[0][0][0]) + (kc & 1) * DV * VTP;
+            if (!vlane) return;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                *reinterpret_cast<uint32_t*>(&vt[(vdc + 2 * e) * VTP + 2 * vp]) =
+                    (va0[e] & 0xffffu) | (va1[e] << 16);
+                *reinterpret_cast<uint32_t*>(&vt[(vdc + 2 * e + 1) * VTP + 2 * vp]) =
+                    (va0[e] >> 16) | (va1[e] & 0xffff0000u);
+            }
+        };
+        stage_k(0);
+        load_v(0);
+        store_v(0);
+        for (int kc = 0; kc < nkc; ++kc) {
+            const int k0 = k_lo + kc * 64;
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (kc + 1 < nkc) {
+                stage_k(kc + 1);
+                load_v(kc + 1);
+            }
+            const bf16_t* ks_lds = sm.state[kc & 1];
+            const bf16_t* vt_lds = reinterpret_cast<const bf16_t*>(&sm.w[0][0][0]) + (kc & 1) * DV * VTP;
+            if (!(k0 > wt_last || k0 + 63 < wseg0)) {  // some key of this chunk is read
+            // every (key, token) pair of the chunk is read when all keys precede the wave's
+            // first token and none precedes the segment start of its last token
+            const bool full = (k0 + 63 <= wt0) && (k0 >= (wt_last / C) * C);
+            // one 32-token block at a time keeps the score registers to 2 x 16
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const int t = wt0 + tb * 32 + l32;
+                if (k0 > wt0 + tb * 32 + 31) continue;  // keys all after this token block
+                f32x16_t sc[2];
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sc[rb][r] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb) {
+                        const int r = rb * 32 + l32, c8 = 2 * ks + hi32;
+                        u32x4_t ka = *reinterpret_cast<const u32x4_t*>(&ks_lds[r * DK + ((c8 ^ (r % CPR)) * 8)]);
+                        if (phi) {  // the key tile holds raw k; phi is applied per fragment
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                ka[e] = pack_bf16x2(feature(__uint_as_float(ka[e] << 16), 1),
+                                                    feature(__uint_as_float(ka[e] & 0xffff0000u), 1));
+                        }
+                        sc[rb] = mfma32x32x16(ka, qf[tb][ks], sc[rb]);
+                    }
+                const int tseg = (t / C) * C;
+                u32x4_t sb[4];
+                if (!full) {  // mask to segment(t) start <= r <= t
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int r = k0 + rb * 32 + 8 * (i / 4) + 4 * hi32 + (i % 4);
+                            if (r > t || r < tseg) sc[rb][i] = 0.f;
+                        }
+                }
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        sb[2 * rb + q] = u32x4_t{pack_bf16x2(sc[rb][8 * q + 0], sc[rb][8 * q + 1]),
+                                                 pack_bf16x2(sc[rb][8 * q + 2], sc[rb][8 * q + 3]),
+                                                 pack_bf16x2(sc[rb][8 * q + 4], sc[rb][8 * q + 5]),
+                                                 pack_bf16x2(sc[rb][8 * q + 6], sc[rb][8 * q + 7])};
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const int c = cw * (DV / 2) + cb * 32 + l32;
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const uint2 lo = *reinterpret_cast<const uint2*>(&vt_lds[c * VTP + 16 * kk + 4 * hi32]);
+                        const uint2 hi = *reinterpret_cast<const uint2*>(&vt_lds[c * VTP + 16 * kk + 8 + 4 * hi32]);
+                        const u32x4_t va = {lo.x, lo.y, hi.x, hi.y};
+                        acc[cb][tb] = mfma32x32x16(va, sb[kk], acc[cb][tb]);
+                    }
+                }
+            }
+            }
+            if (kc + 1 < nkc) store_v(kc + 1);  // its buffer was last read in chunk kc-1
         }
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const int t = min(tile0 + tw * 64 + tb * 32 + l32, L - 1);
+                const float* orow = O_on + ((size_t)bh * L + t) * DV + cw * (DV / 2) + cb * 32 + hi32 * 4;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 v = *reinterpret_cast<const float4*>(orow + g * 8);
+                    acc[cb][tb][4 * g + 0] = v.x;
+                    acc[cb][tb][4 * g + 1] = v.y;
+                    acc[cb][tb][4 * g + 2] = v.z;
+                    acc[cb][tb][4 * g + 3] = v.w;
+                }
+            }
+    }
+
+    if (SSC && tid < 2) sm.any_sel[tid] = 0u;
+    __syncthreads();
+    if (s_hi > 0) stage(0, 0);
+    if (nblk > 0) gate(0);
 
     // ---- the cached states, one workgroup barrier per state ----
     for (int i = 0; i < s_hi; ++i) {
@@ -351,32 +487,45 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
 }
 
 template <int DK, int DV, bool SSC>
-static int launch_grm_mfma_t(const mc_dims& d, int top_k, const void* Q, const void* U,
-                             const float* aon, const uint16_t* M_lo, const float* P,
-                             const float* O_on, const int32_t* idx, void* Y, hipStream_t st) {
+static int launch_grm_mfma_t(const mc_dims& d, int top_k, const void* Q, const void* K,
+                             const void* V, const void* U, const float* aon,
+                             const uint16_t* M_lo, const float* P, const float* O_on,
+                             const int32_t* idx, void* Y, hipStream_t st) {
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     const int T = (d.L + GT - 1) / GT;
     const int BH = d.B * d.H;
-    hipLaunchKernelGGL((grm_mfma_kernel<DK, DV, SSC>), dim3(BH * T), dim3(GTHREADS), 0, st,
-                       (const bf16_t*)Q, (const bf16_t*)U, aon, (const bf16_t*)M_lo, P, O_on,
-                       idx, top_k, BH, d.H, d.L, d.seg_len, NS, d.d_g, d.x_heads, d.phi,
-                       (bf16_t*)Y);
+    if (O_on)
+        hipLaunchKernelGGL((grm_mfma_kernel<DK, DV, SSC, false>), dim3(BH * T), dim3(GTHREADS),
+                           0, st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                           (const bf16_t*)U, aon, (const bf16_t*)M_lo, P, O_on, idx, top_k, BH,
+                           d.H, d.L, d.seg_len, NS, d.d_g, d.x_heads, d.phi, (bf16_t*)Y);
+    else
+        hipLaunchKernelGGL((grm_mfma_kernel<DK, DV, SSC, true>), dim3(BH * T), dim3(GTHREADS),
+                           0, st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                           (const bf16_t*)U, aon, (const bf16_t*)M_lo, P, O_on, idx, top_k, BH,
+                           d.H, d.L, d.seg_len, NS, d.d_g, d.x_heads, d.phi, (bf16_t*)Y);
     return (int)hipGetLastError();
 }
 
 // bf16 GRM / SSC read on MFMA.  Returns -1 when the sizes are not covered (the caller
 // falls back to the generic kernel), else the HIP status of the launch.
-int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* U,
-                     const float* aon, const uint16_t* M_lo, const float* P,
-                     const float* O_on, const int32_t* idx, void* Y, void* stream) {
-    if (d.dtype != MC_BF16 || d.d_g % 16 != 0) return -1;
+bool read_mfma_covers(const mc_dims& d) {
+    return d.dtype == MC_BF16 && d.d_g % 16 == 0 && (d.d_k == 64 || d.d_k == 128) &&
+           (d.d_v == 64 || d.d_v == 128);
+}
+
+int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* K,
+                     const void* V, const void* U, const float* aon, const uint16_t* M_lo,
+                     const float* P, const float* O_on, const int32_t* idx, void* Y,
+                     void* stream) {
+    if (!read_mfma_covers(d)) return -1;
     hipStream_t st = (hipStream_t)stream;
 #define MC_MF(DK, DV)                                                                        \
     if (d.d_k == DK && d.d_v == DV)                                                          \
-        return ssc ? launch_grm_mfma_t<DK, DV, true>(d, top_k, Q, U, aon, M_lo, P, O_on,     \
-                                                     idx, Y, st)                             \
-                   : launch_grm_mfma_t<DK, DV, false>(d, top_k, Q, U, aon, M_lo, P, O_on,    \
-                                                      idx, Y, st);
+        return ssc ? launch_grm_mfma_t<DK, DV, true>(d, top_k, Q, K, V, U, aon, M_lo, P,     \
+                                                     O_on, idx, Y, st)                       \
+                   : launch_grm_mfma_t<DK, DV, false>(d, top_k, Q, K, V, U, aon, M_lo, P,    \
+                                                      O_on, idx, Y, st);
     MC_MF(128, 128)
     MC_MF(128, 64)
     MC_MF(64, 128)

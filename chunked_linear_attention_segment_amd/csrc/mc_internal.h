@@ -11,10 +11,12 @@ namespace mc {
 // Byte sizes of the workspace regions, in the order they are carved out of `ws`.
 struct GrmWorkspace {
     size_t aon;   // fp32 [B,H,L]: online gate logit <u_t, prefix mean of X>
+    size_t on;    // fp32 [B,H,L,dv]: online read, for the generic kernels when O_on is NULL
     size_t total;
 };
 struct SscWorkspace {
     size_t aon;    // fp32 [B,H,L]
+    size_t on;     // fp32 [B,H,L,dv] (generic kernels only)
     size_t xsum64; // fp64 [B,xh,NS,dg]: segment sums of X, token order
     size_t total;
 };
@@ -36,19 +38,32 @@ int launch_scan_prefill(const mc_dims& d, const void* Q, const void* K, const vo
                         const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,
                         void* stream);
 
+// The online read M_t^(s) phi(q_t) alone (generic fp32-accumulating kernel), into O_on.
+int launch_scan_online(const mc_dims& d, const void* Q, const void* K, const void* V,
+                       float* O_on, void* stream);
+
 int launch_aon(const mc_dims& d, const void* X, const void* U, float* a_on, void* stream);
 
-int launch_grm_readout(const mc_dims& d, const void* Q, const void* U, const float* aon,
-                       const float* M, const uint16_t* M_lo, const float* P,
-                       const float* O_on, void* Y, float* gamma, void* stream);
+// true when the bf16 MFMA read kernel handles these sizes (it forms the online term itself
+// when O_on is NULL); otherwise the generic kernels run and need O_on
+bool read_mfma_covers(const mc_dims& d);
+
+int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* K,
+                     const void* V, const void* U, const float* aon, const uint16_t* M_lo,
+                     const float* P, const float* O_on, const int32_t* idx, void* Y,
+                     void* stream);
+
+int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const void* V,
+                       const void* U, const float* aon, const float* M, const uint16_t* M_lo,
+                       const float* P, const float* O_on, void* Y, float* gamma, void* stream);
 
 int launch_ssc_select(const mc_dims& d, int top_k, const void* U, const void* X,
                       double* xsum64, int32_t* idx, void* stream);
 
-int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* U,
-                       const float* aon, const float* M, const uint16_t* M_lo,
-                       const float* P, const float* O_on, const int32_t* idx, void* Y,
-                       void* stream);
+int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K,
+                       const void* V, const void* U, const float* aon, const float* M,
+                       const uint16_t* M_lo, const float* P, const float* O_on,
+                       const int32_t* idx, void* Y, void* stream);
 
 int launch_decode_step(const mc_dims& d, const void* q, const void* k, const void* v,
                        const void* u, const void* x, float* M_on, float* xsum_on,

@@ -40,8 +40,13 @@ __global__ __launch_bounds__(256) void aon_kernel(const T* __restrict__ X,
         for (int j0 = 0; j0 < len; j0 += 64) {
             const int n = min(64, len - j0);
             __syncthreads();
-            for (int e = tid; e < n * DG; e += 256)
-                xs[e / DG][e % DG] = ld(Xb, (size_t)(t0 + j0 + e / DG) * DG + e % DG);
+            for (int e8 = tid; e8 < n * (DG / 8); e8 += 256) {
+                const int r = e8 / (DG / 8), e = (e8 % (DG / 8)) * 8;
+                float v[8];
+                ld8(Xb, (size_t)(t0 + j0 + r) * DG + e, v);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) xs[r][e + k] = v[k];
+            }
             __syncthreads();
             for (int e = tid; e < DG; e += 256) {
                 float acc = carry[e];
@@ -53,18 +58,41 @@ __global__ __launch_bounds__(256) void aon_kernel(const T* __restrict__ X,
             }
             __syncthreads();
             const int nhp = (xh == 1) ? nh : 1;  // heads served by this pass
-            for (int item = slot; item < nhp * 64; item += 16) {
-                const int hh = (xh == 1) ? item / 64 : pass, tt = item % 64;
-                if (tt >= n) continue;
-                const int t = t0 + j0 + tt;
-                const T* ur = U + (((size_t)b * H + h0 + hh) * L + t) * DG;
-                float a = 0.f;
-                for (int e0 = q * 8; e0 < DG; e0 += 128) {
+            // 16 dot products per slot at most, their U loads issued four at a time
+            constexpr int NIT = 16, NB = 4;
+            for (int k0 = 0; k0 < NIT; k0 += NB) {
+            float uv[NB][8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) a += ld(ur, (size_t)(e0 + e)) * xs[tt][e0 + e];
+            for (int kq = 0; kq < NB; ++kq) {
+                const int k = k0 + kq;
+                const int item = slot + 16 * k;
+                const int hh = (xh == 1) ? item / 64 : pass, tt = item % 64;
+                const bool ok = item < nhp * 64 && tt < n && q * 8 < DG;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) uv[kq][e] = 0.f;
+                if (ok) ld8(U + (((size_t)b * H + h0 + hh) * L + t0 + j0 + tt) * DG, (size_t)q * 8, uv[kq]);
+            }
+#pragma unroll
+            for (int kq = 0; kq < NB; ++kq) {
+                const int k = k0 + kq;
+                const int item = slot + 16 * k;
+                const int hh = (xh == 1) ? item / 64 : pass, tt = item % 64;
+                float a = 0.f;
+                if (q * 8 < DG && tt < n) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) a += uv[kq][e] * xs[tt][q * 8 + e];
+                }
+                // widths beyond 128: the remaining 8-element slices of this lane
+                for (int e0 = q * 8 + 128; e0 < DG && item < nhp * 64 && tt < n; e0 += 128) {
+                    float u2[8];
+                    ld8(U + (((size_t)b * H + h0 + hh) * L + t0 + j0 + tt) * DG, (size_t)e0, u2);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) a += u2[e] * xs[tt][e0 + e];
                 }
                 a = warp_sum(a, 16);
-                if (q == 0) a_on[((size_t)b * H + h0 + hh) * L + t] = a / (float)(j0 + tt + 1);
+                if (q == 0 && item < nhp * 64 && tt < n)
+                    a_on[((size_t)b * H + h0 + hh) * L + t0 + j0 + tt] = a / (float)(j0 + tt + 1);
+            }
             }
         }
         __syncthreads();
@@ -254,20 +282,13 @@ __global__ void gamma_kernel(const T* __restrict__ U, const float* __restrict__ 
         gr[i] = i < s ? __expf(logit(i) - mx) / z : (i == s ? __expf(a_on - mx) / z : 0.f);
 }
 
-int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* U,
-                     const float* aon, const uint16_t* M_lo, const float* P,
-                     const float* O_on, const int32_t* idx, void* Y, void* stream);
-
-int launch_grm_readout(const mc_dims& d, const void* Q, const void* U, const float* aon,
-                       const float* M, const uint16_t* M_lo, const float* P,
-                       const float* O_on, void* Y, float* gamma, void* stream) {
-    if (d.dtype != MC_BF16)
+int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const void* V,
+                       const void* U, const float* aon, const float* M, const uint16_t* M_lo,
+                       const float* P, const float* O_on, void* Y, float* gamma, void* stream) {
+    if (!read_mfma_covers(d))
         return launch_readout<false>(d, 0, Q, U, aon, M, M_lo, P, O_on, nullptr, Y, gamma,
                                      (hipStream_t)stream);
-    int rc = launch_read_mfma(d, false, 0, Q, U, aon, M_lo, P, O_on, nullptr, Y, stream);
-    if (rc < 0)
-        rc = launch_readout<false>(d, 0, Q, U, aon, M, M_lo, P, O_on, nullptr, Y, nullptr,
-                                   (hipStream_t)stream);
+    int rc = launch_read_mfma(d, false, 0, Q, K, V, U, aon, M_lo, P, O_on, nullptr, Y, stream);
     if (rc || !gamma) return rc;
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     hipLaunchKernelGGL(gamma_kernel<bf16_t>, dim3((d.L + 63) / 64, d.B * d.H), dim3(64), 0,
@@ -276,14 +297,12 @@ int launch_grm_readout(const mc_dims& d, const void* Q, const void* U, const flo
     return (int)hipGetLastError();
 }
 
-int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* U,
-                       const float* aon, const float* M, const uint16_t* M_lo,
-                       const float* P, const float* O_on, const int32_t* idx, void* Y,
-                       void* stream) {
-    if (d.dtype == MC_BF16) {
-        const int rc = launch_read_mfma(d, true, top_k, Q, U, aon, M_lo, P, O_on, idx, Y, stream);
-        if (rc >= 0) return rc;
-    }
+int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K,
+                       const void* V, const void* U, const float* aon, const float* M,
+                       const uint16_t* M_lo, const float* P, const float* O_on,
+                       const int32_t* idx, void* Y, void* stream) {
+    if (read_mfma_covers(d))
+        return launch_read_mfma(d, true, top_k, Q, K, V, U, aon, M_lo, P, O_on, idx, Y, stream);
     return launch_readout<true>(d, top_k, Q, U, aon, M, M_lo, P, O_on, idx, Y, nullptr,
                                 (hipStream_t)stream);
 }

@@ -60,12 +60,14 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const T* __restrict__ Q,
                 acc += m[i] * sq[j][r0 + i];
             }
             acc = warp_sum(acc, TPR);
-            if (tid % TPR == 0) O_on[(bh * L + t0 + j0 + j) * DV + c] = acc;
+            if (O_on && tid % TPR == 0) O_on[(bh * L + t0 + j0 + j) * DV + c] = acc;
         }
     }
     const size_t mo = (bh * NS + s) * (size_t)(DV * DK) + (size_t)c * DK + r0;
+    if (M) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) M[mo + i] = m[i];
+        for (int i = 0; i < CPT; ++i) M[mo + i] = m[i];
+    }
     if (M_lo) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) M_lo[mo + i] = f32_to_bf16(m[i]);
@@ -73,17 +75,33 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const T* __restrict__ Q,
 }
 
 // MeanPooling(S^(i)) = mean of X over segment i (a trailing partial segment averages the
-// tokens it has).  One workgroup per (segment, b*xh+hx); thread e sums column e in fp32.
+// tokens it has).  One workgroup per (segment, b*xh+hx): 256 threads = 16 token lanes x 16
+// column groups of 8; each thread sums its column group over every 16th token (16-byte
+// loads), then the 16 token lanes are combined in a fixed order through LDS.
 template <typename T>
-__global__ void seg_means_kernel(const T* __restrict__ X, int L, int C, int NS, int DG,
-                                 float* __restrict__ P) {
+__global__ __launch_bounds__(256) void seg_means_kernel(const T* __restrict__ X, int L, int C,
+                                                        int NS, int DG, float* __restrict__ P) {
+    __shared__ float part[16][257];
     const int s = blockIdx.x;
     const size_t bx = blockIdx.y;
     const int t0 = s * C;
     const int len = min(C, L - t0);
-    for (int e = threadIdx.x; e < DG; e += blockDim.x) {
+    const int tl = threadIdx.x / 16, cg = threadIdx.x % 16;
+    for (int e0 = cg * 8; e0 < DG; e0 += 128) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int j = tl; j < len; j += 16) {
+            float v[8];
+            ld8(X, (bx * L + t0 + j) * DG + e0, v);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] += v[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) part[tl][e0 + k] = acc[k];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < DG; e += 256) {
         float acc = 0.f;
-        for (int j = 0; j < len; ++j) acc += ld(X, (bx * L + t0 + j) * DG + e);
+        for (int r = 0; r < 16; ++r) acc += part[r][e];
         P[(bx * NS + s) * DG + e] = acc / (float)len;
     }
 }
@@ -108,6 +126,13 @@ static int launch_scan_dt(const mc_dims& d, const void* Q, const void* K, const 
     return launch_scan_t<T, 64, 64>(d, Q, K, V, M, M_lo, O_on, st);
 }
 
+int launch_scan_online(const mc_dims& d, const void* Q, const void* K, const void* V,
+                       float* O_on, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    return d.dtype == MC_BF16 ? launch_scan_dt<bf16_t>(d, Q, K, V, nullptr, nullptr, O_on, st)
+                              : launch_scan_dt<float>(d, Q, K, V, nullptr, nullptr, O_on, st);
+}
+
 int launch_scan_mfma(const mc_dims& d, const void* Q, const void* K, const void* V, float* M,
                      uint16_t* M_lo, float* O_on, void* stream);
 
@@ -126,7 +151,7 @@ int launch_scan_prefill(const mc_dims& d, const void* Q, const void* K, const vo
         rc = launch_scan_dt<float>(d, Q, K, V, M, M_lo, O_on, st);
     if (rc) return rc;
     dim3 grid(NS, d.B * d.x_heads);
-    const int threads = d.d_g < 256 ? ((d.d_g + 63) / 64) * 64 : 256;
+    const int threads = 256;
     if (d.dtype == MC_BF16)
         hipLaunchKernelGGL(seg_means_kernel<bf16_t>, grid, dim3(threads), 0, st,
                            (const bf16_t*)X, d.L, d.seg_len, NS, d.d_g, P);

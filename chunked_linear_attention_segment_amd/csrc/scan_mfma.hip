@@ -5,6 +5,7 @@
 // token t reads the memory after its own update (§3.1, Eq. 6/8): O_on[t] = M_t^(s) phi(q_t).
 //
 // One workgroup per (segment, b*H+h); the segment is walked in chunks of CH = 64 tokens.
+// ON = false emits only the segment states (the read path then forms the online term itself).
 // With M_prev the state before the chunk, for every token t of the chunk
 //     O_on[t] = M_prev phi(q_t) + sum_{r <= t in chunk} (phi(q_t) . phi(k_r)) v_r
 //     M      += sum_{r in chunk} v_r phi(k_r)^T
@@ -31,9 +32,7 @@ __device__ __forceinline__ f32x16_t scan_mfma(const u32x4_t& a, const u32x4_t& b
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pk2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
+__device__ __forceinline__ uint32_t pk2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
 // phi applied to 4 bf16 values held in two 32-bit words.
 __device__ __forceinline__ u32x2_t phi4(u32x2_t v, int phi) {
@@ -51,7 +50,7 @@ __device__ __forceinline__ u32x2_t phi4(u32x2_t v, int phi) {
 constexpr int CH = 64;    // tokens per chunk
 constexpr int TPAD = 72;  // row stride (elements) of the token-indexed LDS tiles
 
-template <int DK, int DV>
+template <int DK, int DV, bool ON>
 __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     int L, int C, int NS, int phi, float* __restrict__ M, bf16_t* __restrict__ M_lo,
@@ -85,32 +84,34 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
         const int n = min(CH, len - j0);
         // ---- phi(q) B-fragments (k order of the accumulator rows) for both token blocks ----
         u32x4_t qb[2][KSD];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const int tl = tb * 32 + l32;
-            const bool ok = tl < n;
-            const bf16_t* qr = Qs + (size_t)(j0 + (ok ? tl : 0)) * DK + half * 4;
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-                u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
-                if (ok) {
-                    lo = phi4(*reinterpret_cast<const u32x2_t*>(qr + ks * 16), phi);
-                    hi = phi4(*reinterpret_cast<const u32x2_t*>(qr + ks * 16 + 8), phi);
-                }
-                qb[tb][ks] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-            }
-        }
-        // ---- O^T = M_prev phi(q)^T (first term of the online read) ----
         f32x16_t ot[2];
+        if (ON) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+            for (int tb = 0; tb < 2; ++tb) {
+                const int tl = tb * 32 + l32;
+                const bool ok = tl < n;
+                const bf16_t* qr = Qs + (size_t)(j0 + (ok ? tl : 0)) * DK + half * 4;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) ot[tb][r] = 0.f;
-        if (j0 > 0) {
+                for (int ks = 0; ks < KSD; ++ks) {
+                    u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
+                    if (ok) {
+                        lo = phi4(*reinterpret_cast<const u32x2_t*>(qr + ks * 16), phi);
+                        hi = phi4(*reinterpret_cast<const u32x2_t*>(qr + ks * 16 + 8), phi);
+                    }
+                    qb[tb][ks] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+                }
+            }
+            // ---- O^T = M_prev phi(q)^T (first term of the online read) ----
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks)
+            for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) ot[tb] = scan_mfma(ma[ks], qb[tb][ks], ot[tb]);
+                for (int r = 0; r < 16; ++r) ot[tb][r] = 0.f;
+            if (j0 > 0) {
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb) ot[tb] = scan_mfma(ma[ks], qb[tb][ks], ot[tb]);
+            }
         }
         // ---- stage phi(k)^T and v^T (token pairs packed in 32-bit LDS words) ----
         for (int it = tid; it < (CH / 2) * (DK / 8); it += NT) {
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
         }
         // ---- causal scores S^T[r][t] = phi(k_r).phi(q_t), r <= t: blocks (rb,tb) = (0,0),
         //      (0,1), (1,1) dealt to the waves; block (1,0) is all masked and never read ----
-        for (int blk = wave; blk < 3; blk += NT / 64) {
+        for (int blk = wave; ON && blk < 3; blk += NT / 64) {
             const int rb = blk == 2 ? 1 : 0, tb = blk == 0 ? 0 : 1;
             const int rl = rb * 32 + l32;
             const bool ok = rl < n;
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
         for (int ks = 0; ks < CH / 16; ++ks)
             va[ks] = *reinterpret_cast<const u32x4_t*>(&vt[cv][ks * 16 + half * 8]);
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
+        for (int tb = 0; tb < 2 && ON; ++tb) {
             const int t = tb * 32 + l32;
 #pragma unroll
             for (int ks = 0; ks < (tb + 1) * 2; ++ks) {
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
         }
         // ---- online read out: O_on[t][cv] (4 consecutive cv per register group) ----
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
+        for (int tb = 0; tb < 2 && ON; ++tb) {
             const int tl = tb * 32 + l32;
             if (tl < n) {
                 float* orow = O_on + (bh * L + t0 + j0 + tl) * DV + wave * 32 + half * 4;
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
         }
         // ---- bf16 copy of the updated state as the next chunk's A operand ----
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB && ON; ++db)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
                 ma[2 * db + hh] = u32x4_t{pk2(mt[db][8 * hh + 0], mt[db][8 * hh + 1]),
@@ -246,9 +247,14 @@ template <int DK, int DV>
 static int launch_scan_mfma_t(const mc_dims& d, const void* Q, const void* K, const void* V,
                               float* M, uint16_t* M_lo, float* O_on, hipStream_t st) {
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
-    hipLaunchKernelGGL((scan_mfma_kernel<DK, DV>), dim3(NS, d.B * d.H), dim3(DV * 2), 0, st,
-                       (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, d.L, d.seg_len, NS,
-                       d.phi, M, (bf16_t*)M_lo, O_on);
+    if (O_on)
+        hipLaunchKernelGGL((scan_mfma_kernel<DK, DV, true>), dim3(NS, d.B * d.H), dim3(DV * 2),
+                           0, st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, d.L,
+                           d.seg_len, NS, d.phi, M, (bf16_t*)M_lo, O_on);
+    else
+        hipLaunchKernelGGL((scan_mfma_kernel<DK, DV, false>), dim3(NS, d.B * d.H), dim3(DV * 2),
+                           0, st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, d.L,
+                           d.seg_len, NS, d.phi, M, (bf16_t*)M_lo, O_on);
     return (int)hipGetLastError();
 }
 

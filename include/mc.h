@@ -105,7 +105,9 @@ size_t mc_workspace_bytes(const mc_dims* dims, mc_op op, int32_t top_k, int32_t 
  *                                      dtype == MC_BF16
  *   P      out [B,x_heads,NS,d_g] fp32 MeanPooling(S^(i)); a partial segment averages the
  *                                      tokens it has
- *   O_on   out [B,H,L,d_v] fp32        M_t^(s) phi(q_t), the online read with weight 1
+ *   O_on   out, nullable [B,H,L,d_v] fp32  M_t^(s) phi(q_t), the online read with weight 1.
+ *          The read calls form this term themselves when given K and V instead, so a caller
+ *          that only wants y passes NULL here and in the read call (the fast path).
  */
 mc_status mc_scan_prefill(const mc_dims* dims, const void* Q, const void* K, const void* V,
                           const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,
@@ -114,24 +116,28 @@ mc_status mc_scan_prefill(const mc_dims* dims, const void* Q, const void* K, con
 /*
  * mc_grm_readout -- Gated Residual Memory read (paper §3.1, Eq. 9 with the gate of Eq. 10):
  *     a_t^(i) = <u_t, P_i> (i < s),  a_t^(s) = <u_t, prefix mean of X over t's segment>,
- *     gamma_t = softmax(a_t^(0..s)),  y_t = gamma^(s) O_on[t] + sum_{i<s} gamma^(i) M^(i) phi(q_t)
+ *     gamma_t = softmax(a_t^(0..s)),
+ *     y_t = gamma^(s) M_t^(s) phi(q_t) + sum_{i<s} gamma^(i) M^(i) phi(q_t)
  *
- *   Q [B,H,L,d_k], U [B,H,L,d_g], X [B,x_heads,L,d_g]: dtype
- *   M, M_lo, P, O_on: as written by mc_scan_prefill for the same Q,K,V,X (M_lo is read when
+ *   Q, K [B,H,L,d_k], V [B,H,L,d_v], U [B,H,L,d_g], X [B,x_heads,L,d_g]: dtype
+ *   M, M_lo, P: as written by mc_scan_prefill for the same Q,K,V,X (M_lo is read when
  *     dtype == MC_BF16, M when MC_F32; the other may be NULL)
+ *   O_on   nullable: the online read written by mc_scan_prefill.  When NULL the online term
+ *     M_t^(s) phi(q_t) is formed here from K and V (then required); K and V are ignored when
+ *     O_on is given.
  *   Y      out [B,H,L,d_v] dtype
  *   gamma  out, nullable [B,H,L,NS] fp32: gamma_t^(i) for i <= s, 0 beyond
  */
-mc_status mc_grm_readout(const mc_dims* dims, const void* Q, const void* U, const void* X,
-                         const float* M, const uint16_t* M_lo, const float* P,
-                         const float* O_on, void* Y, float* gamma, void* ws, size_t ws_bytes,
-                         void* stream);
+mc_status mc_grm_readout(const mc_dims* dims, const void* Q, const void* K, const void* V,
+                         const void* U, const void* X, const float* M, const uint16_t* M_lo,
+                         const float* P, const float* O_on, void* Y, float* gamma, void* ws,
+                         size_t ws_bytes, void* stream);
 
 /*
  * mc_ssc_readout -- Sparse Selective Caching read (explainer §3.4):
  *     R_t = Top-k of {a_t^(i)}_{i<s} (larger score first, lower index on ties; all of them
  *     when s <= k); gamma_t = softmax over R_t and the online segment;
- *     y_t = gamma^(s) O_on[t] + sum_{i in R_t} gamma^(i) M^(i) phi(q_t)
+ *     y_t = gamma^(s) M_t^(s) phi(q_t) + sum_{i in R_t} gamma^(i) M^(i) phi(q_t)
  *   The selection is exact: scores are formed in fp32 and any token whose k-th / (k+1)-th
  *   margin is within the fp32 error bound is re-scored in fp64.
  *
@@ -140,10 +146,10 @@ mc_status mc_grm_readout(const mc_dims* dims, const void* Q, const void* U, cons
  *   idx    out [B,H,L,top_k] int32: R_t in ascending order, -1 padded
  *   ws     mc_workspace_bytes(dims, MC_OP_SSC, top_k, 0) bytes
  */
-mc_status mc_ssc_readout(const mc_dims* dims, int32_t top_k, const void* Q, const void* U,
-                         const void* X, const float* M, const uint16_t* M_lo, const float* P,
-                         const float* O_on, void* Y, int32_t* idx, void* ws, size_t ws_bytes,
-                         void* stream);
+mc_status mc_ssc_readout(const mc_dims* dims, int32_t top_k, const void* Q, const void* K,
+                         const void* V, const void* U, const void* X, const float* M,
+                         const uint16_t* M_lo, const float* P, const float* O_on, void* Y,
+                         int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mc_decode_step -- one new token per sequence (paper §3 applied to token t+1): for every

@@ -72,19 +72,20 @@ def test_scan_rejects_bad_dims(kw, code):
 
 def test_scan_null_and_alignment():
     assert mc.load().mc_scan_prefill(None, A, A, A, A, A, A, A, A, None, 0, None) == mc.MC_ERR_NULL
-    for name in ("Q", "K", "V", "X", "M", "P", "O_on"):
+    for name in ("Q", "K", "V", "X", "M", "P"):
         assert scan(dims(), **{name: None}) == mc.MC_ERR_NULL
         assert scan(dims(), **{name: MIS}) == mc.MC_ERR_ALIGN
+    assert scan(dims(), O_on=MIS) == mc.MC_ERR_ALIGN           # optional, but checked
     assert scan(dims(), M_lo=None) == mc.MC_ERR_NULL          # bf16 needs the operand copy
     assert scan(dims(dtype="f32"), M_lo=MIS) == mc.MC_ERR_ALIGN
 
 
 def grm(d, ws_bytes, **ptr):
-    p = dict(Q=A, U=A, X=A, M=A, M_lo=A, P=A, O_on=A, Y=A, gamma=None, ws=A)
+    p = dict(Q=A, K=A, V=A, U=A, X=A, M=A, M_lo=A, P=A, O_on=A, Y=A, gamma=None, ws=A)
     p.update(ptr)
-    return mc.load().mc_grm_readout(ctypes.byref(d), p["Q"], p["U"], p["X"], p["M"], p["M_lo"],
-                                    p["P"], p["O_on"], p["Y"], p["gamma"], p["ws"], ws_bytes,
-                                    None)
+    return mc.load().mc_grm_readout(ctypes.byref(d), p["Q"], p["K"], p["V"], p["U"], p["X"],
+                                    p["M"], p["M_lo"], p["P"], p["O_on"], p["Y"], p["gamma"],
+                                    p["ws"], ws_bytes, None)
 
 
 def test_grm_workspace_and_pointers():
@@ -98,6 +99,20 @@ def test_grm_workspace_and_pointers():
     assert grm(dims(dtype="f32"), need, M=None) == mc.MC_ERR_NULL  # fp32 reads M
     assert grm(d, need, gamma=MIS) == mc.MC_ERR_ALIGN
     assert grm(dims(L=-5), need) == mc.MC_ERR_DIMS
+    # without O_on the online term is formed from K and V, which are then required
+    assert grm(d, need, O_on=None, K=None) == mc.MC_ERR_NULL
+    assert grm(d, need, O_on=None, V=None) == mc.MC_ERR_NULL
+    assert grm(d, need, O_on=None, K=MIS) == mc.MC_ERR_ALIGN
+
+
+def test_generic_path_workspace_holds_the_online_read():
+    # the bf16 MFMA read forms the online term in-kernel; the generic kernels (fp32, or a
+    # gate width the MFMA gate does not tile) stage it in the workspace
+    bf = mc.mc_workspace_bytes(dims(), mc.MC_OP_GRM)
+    f32 = mc.mc_workspace_bytes(dims(dtype="f32"), mc.MC_OP_GRM)
+    odd = mc.mc_workspace_bytes(dims(d_g=24), mc.MC_OP_GRM)
+    assert f32 >= bf + 4 * 2 * 1024 * 128
+    assert odd >= bf + 4 * 2 * 1024 * 128
 
 
 def test_ssc_arguments():
@@ -107,8 +122,8 @@ def test_ssc_arguments():
     assert need > mc.mc_workspace_bytes(d, mc.MC_OP_GRM)
 
     def call(k, ws_bytes, idx=A):
-        return lib.mc_ssc_readout(ctypes.byref(d), k, A, A, A, A, A, A, A, A, idx, A, ws_bytes,
-                                  None)
+        return lib.mc_ssc_readout(ctypes.byref(d), k, A, A, A, A, A, A, A, A, A, A, idx, A,
+                                  ws_bytes, None)
     assert call(0, need) == mc.MC_ERR_DIMS
     assert call(17, need) == mc.MC_ERR_UNSUPPORTED
     assert call(4, need, idx=None) == mc.MC_ERR_NULL

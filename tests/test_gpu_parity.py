@@ -38,11 +38,12 @@ SMALL = {
 }
 
 
-def _run_grm(w, kw, seed=0):
+def _run_grm(w, kw, seed=0, online=True):
     inp = make_prefill(w, seed=seed, **kw)
     d = _dims(w, **kw)
     dev = {k: to_dev(v, w.dtype) for k, v in inp.items()}
-    out = mc.prefill_grm(d, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"], want_gamma=True)
+    out = mc.prefill_grm(d, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"], want_gamma=True,
+                         online=online)
     torch.cuda.synchronize()
     ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], seg_len=w.seg_len,
                          phi=w.phi, mode="grm", want_states=True, want_online=True,
@@ -50,19 +51,21 @@ def _run_grm(w, kw, seed=0):
     return out, ref
 
 
+@pytest.mark.parametrize("online", [True, False], ids=["with_O_on", "fused_online"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_grm_prefill_small(name):
+def test_grm_prefill_small(name, online):
     w, kw = SMALL[name]
-    announce("grm parity %s" % name)
-    out, ref = _run_grm(w, kw)
+    announce("grm parity %s online=%s" % (name, online))
+    out, ref = _run_grm(w, kw, online=online)
     tol = TOL[w.dtype]
     errs = {
         "Y": slice_rel_err(to_np(out["Y"]), ref["Y"]),
         "M": slice_rel_err(to_np(out["M"]), ref["M"]),
         "P": slice_rel_err(to_np(out["P"]), ref["P"]),
-        "O_on": slice_rel_err(to_np(out["O_on"]), ref["O_on"]),
         "gamma": slice_rel_err(to_np(out["gamma"]), ref["gamma"]),
     }
+    if online:
+        errs["O_on"] = slice_rel_err(to_np(out["O_on"]), ref["O_on"])
     if w.dtype == "bf16":
         errs["M_lo"] = slice_rel_err(to_np(out["M_lo"]), ref["M"])
     announce("  errors %s" % errs)
@@ -82,14 +85,16 @@ SSC_SMALL = {
 }
 
 
+@pytest.mark.parametrize("online", [True, False], ids=["with_O_on", "fused_online"])
 @pytest.mark.parametrize("name", list(SSC_SMALL))
-def test_ssc_prefill_small(name):
+def test_ssc_prefill_small(name, online):
     w, kw = SSC_SMALL[name]
-    announce("ssc parity %s" % name)
+    announce("ssc parity %s online=%s" % (name, online))
     inp = make_prefill(w, seed=1, **kw)
     d = _dims(w, **kw)
     dev = {k: to_dev(v, w.dtype) for k, v in inp.items()}
-    out = mc.prefill_ssc(d, w.top_k, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"])
+    out = mc.prefill_ssc(d, w.top_k, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"],
+                         online=online)
     torch.cuda.synchronize()
     ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], seg_len=w.seg_len,
                          phi=w.phi, mode="ssc", top_k=w.top_k)
@@ -124,9 +129,10 @@ def test_grm_deterministic():
     inp = make_prefill(w, seed=5, **kw)
     d = _dims(w, **kw)
     dev = {k: to_dev(v, w.dtype) for k, v in inp.items()}
-    a = mc.prefill_grm(d, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"])
-    b = mc.prefill_grm(d, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"])
-    assert torch.equal(a["Y"], b["Y"]) and torch.equal(a["M"], b["M"])
+    for online in (True, False):
+        a = mc.prefill_grm(d, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"], online=online)
+        b = mc.prefill_grm(d, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"], online=online)
+        assert torch.equal(a["Y"], b["Y"]) and torch.equal(a["M"], b["M"])
 
 
 # ---- decode -------------------------------------------------------------------------------
