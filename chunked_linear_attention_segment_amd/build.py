@@ -1,9 +1,10 @@
-"""Build libmc.so (the C-ABI library) in-tree with hipcc for gfx950.
+"""Build libmc.so (the C-ABI library) and libmcpeak.so (the benchmark's ceiling kernels)
+in-tree with hipcc for gfx950.
 
     python -m chunked_linear_attention_segment_amd.build
 
 Every source is compiled on each call (the build check compiles even where a library is
-already present); objects go to _build/ and the library next to this file.
+already present); objects go to _build/ and the libraries next to this file.
 """
 from __future__ import annotations
 
@@ -16,11 +17,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmc.so")
+PEAK_OUT = os.path.join(HERE, "libmcpeak.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "scan.hip", "readout.hip", "decode.hip", "grm_mfma.hip", "scan_mfma.hip"]
+PEAK_SOURCES = ["peak.hip"]
 
 # Packed-fp32 VALU ops are kept out of the device code (the host pass warns that it does
 # not know the feature; that warning is harmless).
@@ -41,19 +44,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp%d" % os.getpid()
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PEAK_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], OUT)
+    _link([objs[s] for s in PEAK_SOURCES], PEAK_OUT)
     if verbose:
-        print("built", OUT)
+        print("built", OUT, PEAK_OUT)
     return OUT
 
 
