@@ -15,8 +15,9 @@
 // (cw, tw) owns value rows [cw*DV/2, (cw+1)*DV/2) and tokens [64 tw, 64 tw + 64).  Per
 // cached state i:
 //   A = M^(i) (d_v x d_k bf16): staged once in LDS for the workgroup by direct global->LDS
-//       loads that stream state i+1 in while state i is read (two buffers); 16-byte chunks
-//       XOR-swizzled per row so the fragment reads are bank-conflict free;
+//       loads that stream state i+1 in while state i is read (two buffers); each load
+//       instruction copies whole rows (coalesced), and 16-byte chunks are XOR-swizzled per
+//       row so the fragment reads are bank-conflict free;
 //   B = phi(q)^T: kept in registers for the whole kernel;
 //   the 32x32x16 MFMA partial product is scaled by the token weights and added to the fp32
 //   accumulator.
@@ -84,17 +85,17 @@ __device__ __forceinline__ void grm_tile_of_block(int bid, int BH, int T, int& b
     }
 }
 
-template <int DK, int DV, bool SSC, bool FON>
+template <int DK, int DV, bool SSC, bool FON, int PHI>
 __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ U, const float* __restrict__ aon,
     const bf16_t* __restrict__ S, const float* __restrict__ P, const float* __restrict__ O_on,
     const int32_t* __restrict__ idx, int top_k, int BH, int H, int L, int C, int NS, int DG,
-    int xh, int phi, bf16_t* __restrict__ Y) {
-    constexpr int CPR = DK / 8;        // 16-byte chunks per state row
+    int xh, bf16_t* __restrict__ Y) {
     constexpr int KS = DK / 16;        // MFMA k-steps over d_k
     constexpr int CB = DV / 64;        // 32-row blocks per wave (a wave owns DV/2 rows)
     constexpr int TB = 2;              // 32-token blocks per wave
+    constexpr int CPR = DK / 8;        // 16-byte chunks per state row
     constexpr int STAGE = DV * DK / 8 / GTHREADS;  // direct loads per lane per state
     static_assert(STAGE >= 1 && DV * DK / 8 % GTHREADS == 0, "staging layout");
     typedef GrmSmem<DK, DV> Smem;
@@ -115,8 +116,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
     const int nblk = (s_hi + GSB - 1) / GSB;
 
     // ---- direct global -> LDS staging of state i into buffer `buf`: load m of wave w
-    //      fills LDS chunks [(m*waves + w)*64, +64); chunk (c, kc) is stored at kc ^ (c % CPR)
-    //      of row c.  The per-lane byte offsets inside a state are fixed. ----
+    //      fills LDS chunks [(m*waves + w)*64, +64) -- whole rows, so each load instruction
+    //      reads contiguous memory; chunk (c, kc) is stored at kc ^ (c % CPR) of row c.  The
+    //      per-lane byte offsets inside a state are fixed. ----
     const bf16_t* Sbh = S + (size_t)bh * NS * DV * DK;
     uint32_t soff[STAGE];
 #pragma unroll
@@ -125,6 +127,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
         const int c = p / CPR, kc = (p % CPR) ^ (c % CPR);
         soff[m] = (uint32_t)((c * DK + kc * 8) * 2);
     }
+    // A-fragment reads: row c = (its 32-row block) + l32 and chunk 2 ks + hi32 sit at byte
+    // 16 * ((2 ks + hi32) ^ (l32 % CPR)) of the row (CPR divides 32).  `swz` is made opaque
+    // once per loop iteration (asm below) so the compiler recomputes these offsets with one
+    // xor per fragment instead of keeping all of them live in registers across the loop.
+    uint32_t swz = (uint32_t)(l32 % CPR);
     auto stage = [&](int i, int buf) {
         const bf16_t* src = Sbh + (size_t)i * DV * DK;
 #pragma unroll
@@ -159,15 +166,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
         for (int g = 0; g < GB; ++g)
 #pragma unroll
             for (int r = 0; r < 16; ++r) lg[g][r] = 0.f;
-        const bool prow_ok = (i0 + l32) < s_hi;
-        const float* pr = P + (bx * NS + (prow_ok ? i0 + l32 : 0)) * DG;
-        for (int kc = 0; kc < DG / 16; ++kc) {
-            const int e = kc * 16 + hi32 * 8;
-            float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = p0;
-            if (prow_ok) {
-                p0 = *reinterpret_cast<const float4*>(pr + e);
-                p1 = *reinterpret_cast<const float4*>(pr + e + 4);
-            }
+        // one 16-wide k-step: P rows split into bf16 hi + lo (the logits keep ~16 mantissa
+        // bits), times the U fragment of the lane's token
+        auto kstep = [&](const float4& p0, const float4& p1, const u32x4_t (&bu)[GB]) {
             const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
             u32x4_t ah, al;
 #pragma unroll
@@ -179,11 +180,25 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
             }
 #pragma unroll
             for (int g = 0; g < GB; ++g) {
-                const u32x4_t bu = *reinterpret_cast<const u32x4_t*>(
-                    U + ((size_t)bh * L + gtok[g]) * DG + e);
-                lg[g] = mfma32x32x16(ah, bu, lg[g]);
-                lg[g] = mfma32x32x16(al, bu, lg[g]);
+                lg[g] = mfma32x32x16(ah, bu[g], lg[g]);
+                lg[g] = mfma32x32x16(al, bu[g], lg[g]);
             }
+        };
+        const bool prow_ok = (i0 + l32) < s_hi;
+        const float* pr = P + (bx * NS + (prow_ok ? i0 + l32 : 0)) * DG + hi32 * 8;
+        for (int kc = 0; kc < DG / 16; ++kc) {
+            const int e = kc * 16;
+            float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = p0;
+            if (prow_ok) {
+                p0 = *reinterpret_cast<const float4*>(pr + e);
+                p1 = *reinterpret_cast<const float4*>(pr + e + 4);
+            }
+            u32x4_t bu[GB];
+#pragma unroll
+            for (int g = 0; g < GB; ++g)
+                bu[g] = *reinterpret_cast<const u32x4_t*>(
+                    U + ((size_t)bh * L + gtok[g]) * DG + e + hi32 * 8);
+            kstep(p0, p1, bu);
         }
         uint32_t wave_any = 0u;
 #pragma unroll
@@ -197,11 +212,15 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
                     if (sel[c] >= 0 && d >= 0 && d < GSB) bits |= 1u << d;
                 }
             }
+            // accumulator row 8*(r/4) + 4*hi32 + r%4 is state i0 + that row: the per-r part is
+            // an immediate compared against one per-lane limit
+            const int lim = gval[g] ? gseg[g] - i0 - 4 * hi32 : 0;
+            const uint32_t bsh = bits >> (4 * hi32);
             float bm = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = 8 * (r / 4) + 4 * hi32 + (r % 4);
-                const bool ok = gval[g] && (i0 + row) < gseg[g] && ((bits >> row) & 1u);
+                const int rr = 8 * (r / 4) + (r % 4);
+                const bool ok = rr < lim && ((bsh >> rr) & 1u);
                 lg[g][r] = ok ? lg[g][r] : -INFINITY;
                 bm = fmaxf(bm, lg[g][r]);
             }
@@ -238,7 +257,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4_t v = *reinterpret_cast<const u32x4_t*>(qr + ks * 16);
-            if (phi) {
+            if (PHI) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float x0 = __uint_as_float(v[e] << 16);
@@ -277,8 +296,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
         const int wseg0 = (min(wt0, L - 1) / C) * C;
         const bf16_t* Kbh = K + (size_t)bh * L * DK;
         const bf16_t* Vbh = V + (size_t)bh * L * DV;
-        // k rows of chunk kc -> state buffer kc & 1 (direct loads, rows XOR-swizzled as the
-        // states are; rows past the last token read token `last`, their scores are masked)
+        // k rows of chunk kc -> state buffer kc & 1 (direct loads of whole rows, chunks
+        // XOR-swizzled as the states are; rows past the last token read token `last`, their
+        // scores are masked)
         constexpr int KLD = 64 * DK / 8 / GTHREADS;  // direct loads per lane per key chunk
         auto stage_k = [&](int kc) {
             const int k0 = k_lo + kc * 64;
@@ -322,6 +342,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
         store_v(0);
         for (int kc = 0; kc < nkc; ++kc) {
             const int k0 = k_lo + kc * 64;
+            asm volatile("" : "+v"(swz));
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
             if (kc + 1 < nkc) {
                 stage_k(kc + 1);
@@ -347,9 +368,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb) {
-                        const int r = rb * 32 + l32, c8 = 2 * ks + hi32;
-                        u32x4_t ka = *reinterpret_cast<const u32x4_t*>(&ks_lds[r * DK + ((c8 ^ (r % CPR)) * 8)]);
-                        if (phi) {  // the key tile holds raw k; phi is applied per fragment
+                        u32x4_t ka = *reinterpret_cast<const u32x4_t*>(
+                            &ks_lds[(rb * 32 + l32) * DK + (((2 * ks + hi32) ^ swz) * 8)]);
+                        if (PHI) {  // the key tile holds raw k; phi is applied per fragment
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
                                 ka[e] = pack_bf16x2(feature(__uint_as_float(ka[e] << 16), 1),
@@ -360,12 +381,14 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
                 const int tseg = (t / C) * C;
                 u32x4_t sb[4];
                 if (!full) {  // mask to segment(t) start <= r <= t
+                    // key r = k0 + 4*hi32 + (an immediate per accumulator element)
+                    const int hi_lim = t - k0 - 4 * hi32, lo_lim = tseg - k0 - 4 * hi32;
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                         for (int i = 0; i < 16; ++i) {
-                            const int r = k0 + rb * 32 + 8 * (i / 4) + 4 * hi32 + (i % 4);
-                            if (r > t || r < tseg) sc[rb][i] = 0.f;
+                            const int rr = rb * 32 + 8 * (i / 4) + (i % 4);
+                            if (rr > hi_lim || rr < lo_lim) sc[rb][i] = 0.f;
                         }
                 }
 #pragma unroll
@@ -418,6 +441,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
     // ---- the cached states, one workgroup barrier per state ----
     for (int i = 0; i < s_hi; ++i) {
         const int buf = i & 1, j = i % GSB, wb = (i / GSB) & 1;
+        asm volatile("" : "+v"(swz));
         // state i has landed for this lane; after the barrier for every lane, every wave is
         // done with state i-1 and the weights of this block are published
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -447,9 +471,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
-                    const int c = cw * (DV / 2) + cb * 32 + l32;
-                    const int kc = 2 * ks + hi32;
-                    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&st[c * DK + ((kc ^ (c % CPR)) * 8)]);
+                    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+                        &st[(cw * (DV / 2) + cb * 32 + l32) * DK + (((2 * ks + hi32) ^ swz) * 8)]);
 #pragma unroll
                     for (int tb = 0; tb < TB; ++tb) pp[cb][tb] = mfma32x32x16(a, qf[tb][ks], pp[cb][tb]);
                 }
@@ -486,24 +509,37 @@ __global__ __launch_bounds__(GTHREADS, 1) void grm_mfma_kernel(
     }
 }
 
+template <int DK, int DV, bool SSC, bool FON, int PHI>
+static void launch_grm_mfma_k(const mc_dims& d, int top_k, const void* Q, const void* K,
+                              const void* V, const void* U, const float* aon,
+                              const uint16_t* M_lo, const float* P, const float* O_on,
+                              const int32_t* idx, void* Y, hipStream_t st) {
+    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+    const int T = (d.L + GT - 1) / GT;
+    const int BH = d.B * d.H;
+    hipLaunchKernelGGL((grm_mfma_kernel<DK, DV, SSC, FON, PHI>), dim3(BH * T), dim3(GTHREADS), 0,
+                       st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
+                       (const bf16_t*)U, aon, (const bf16_t*)M_lo, P, O_on, idx, top_k, BH, d.H,
+                       d.L, d.seg_len, NS, d.d_g, d.x_heads, (bf16_t*)Y);
+}
+
 template <int DK, int DV, bool SSC>
 static int launch_grm_mfma_t(const mc_dims& d, int top_k, const void* Q, const void* K,
                              const void* V, const void* U, const float* aon,
                              const uint16_t* M_lo, const float* P, const float* O_on,
                              const int32_t* idx, void* Y, hipStream_t st) {
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
-    const int T = (d.L + GT - 1) / GT;
-    const int BH = d.B * d.H;
+    // the online term is formed in the kernel (from K and V) when the scan did not write it;
+    // the feature map is a template argument so the key fragments' loop has no branches
     if (O_on)
-        hipLaunchKernelGGL((grm_mfma_kernel<DK, DV, SSC, false>), dim3(BH * T), dim3(GTHREADS),
-                           0, st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                           (const bf16_t*)U, aon, (const bf16_t*)M_lo, P, O_on, idx, top_k, BH,
-                           d.H, d.L, d.seg_len, NS, d.d_g, d.x_heads, d.phi, (bf16_t*)Y);
+        d.phi ? launch_grm_mfma_k<DK, DV, SSC, false, 1>(d, top_k, Q, K, V, U, aon, M_lo, P,
+                                                         O_on, idx, Y, st)
+              : launch_grm_mfma_k<DK, DV, SSC, false, 0>(d, top_k, Q, K, V, U, aon, M_lo, P,
+                                                         O_on, idx, Y, st);
     else
-        hipLaunchKernelGGL((grm_mfma_kernel<DK, DV, SSC, true>), dim3(BH * T), dim3(GTHREADS),
-                           0, st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                           (const bf16_t*)U, aon, (const bf16_t*)M_lo, P, O_on, idx, top_k, BH,
-                           d.H, d.L, d.seg_len, NS, d.d_g, d.x_heads, d.phi, (bf16_t*)Y);
+        d.phi ? launch_grm_mfma_k<DK, DV, SSC, true, 1>(d, top_k, Q, K, V, U, aon, M_lo, P,
+                                                        O_on, idx, Y, st)
+              : launch_grm_mfma_k<DK, DV, SSC, true, 0>(d, top_k, Q, K, V, U, aon, M_lo, P,
+                                                        O_on, idx, Y, st);
     return (int)hipGetLastError();
 }
 
