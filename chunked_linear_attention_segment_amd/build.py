@@ -22,8 +22,13 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "scan.hip", "readout.hip", "decode.hip", "grm_mfma.hip", "scan_mfma.hip"]
+SOURCES = ["abi.cpp", "scan.hip", "readout.hip", "decode.hip", "read_mfma.hip", "scan_mfma.hip"]
 PEAK_SOURCES = ["peak.hip"]
+# Per-file flags.  The gated read is written in the exact issue order it needs (each MFMA
+# followed by the VALU work of the next k-step, LDS reads two k-steps ahead); the machine
+# schedulers would regroup it, so they are off for that file.
+FILE_FLAGS = {"read_mfma.hip": ["-mllvm", "-enable-misched=false",
+                                "-mllvm", "-enable-post-misched=false"]}
 
 # Packed-fp32 VALU ops are kept out of the device code (the host pass warns that it does
 # not know the feature; that warning is harmless).
@@ -34,7 +39,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wall", "-Wno-
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC] + [f for f in FLAGS if not f.startswith("--offload-arch")] + \
               ["-x", "c++", "-c", os.path.join(CSRC, src), "-o", obj]
