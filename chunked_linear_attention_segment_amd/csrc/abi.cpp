@@ -15,11 +15,17 @@ static size_t online_ws(const mc_dims& d) {
     return read_mfma_covers(d) ? 0 : align256(sizeof(float) * (size_t)d.B * d.H * d.L * d.d_v);
 }
 
+static size_t xps_ws(const mc_dims& d) {
+    return read_mfma_covers(d) ? align256(sizeof(float) * (size_t)d.B * d.x_heads * d.L * d.d_g)
+                               : 0;
+}
+
 GrmWorkspace grm_workspace(const mc_dims& d) {
     GrmWorkspace w{};
     w.aon = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
     w.on = online_ws(d);
-    w.total = w.aon + w.on;
+    w.xps = xps_ws(d);
+    w.total = w.aon + w.on + w.xps;
     return w;
 }
 
@@ -27,8 +33,9 @@ SscWorkspace ssc_workspace(const mc_dims& d) {
     SscWorkspace w{};
     w.aon = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
     w.on = online_ws(d);
+    w.xps = xps_ws(d);
     w.xsum64 = align256(sizeof(double) * (size_t)d.B * d.x_heads * num_segments(d) * d.d_g);
-    w.total = w.aon + w.on + w.xsum64;
+    w.total = w.aon + w.on + w.xps + w.xsum64;
     return w;
 }
 
@@ -133,13 +140,16 @@ mc_status mc_grm_readout(const mc_dims* d, const void* Q, const void* K, const v
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MC_ERR_ALIGN;
     float* aon = (float*)ws;
+    float* xps = (float*)((char*)ws + w.aon + w.on);
     if (!O_on && w.on) {  // generic kernels: form the online read first
         float* on = (float*)((char*)ws + w.aon);
         if (launch_scan_online(*d, Q, K, V, on, stream)) return MC_ERR_HIP;
         O_on = on;
     }
-    if (launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
-    if (launch_grm_readout(*d, Q, K, V, U, aon, M, M_lo, P, O_on, Y, gamma, stream))
+    const bool mfma = read_mfma_covers(*d);
+    if (mfma && launch_xps(*d, X, xps, stream)) return MC_ERR_HIP;
+    if ((!mfma || gamma) && launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
+    if (launch_grm_readout(*d, Q, K, V, U, aon, xps, M, M_lo, P, O_on, Y, gamma, stream))
         return MC_ERR_HIP;
     return MC_OK;
 }
@@ -161,15 +171,18 @@ mc_status mc_ssc_readout(const mc_dims* d, int32_t top_k, const void* Q, const v
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MC_ERR_ALIGN;
     float* aon = (float*)ws;
-    double* xsum64 = (double*)((char*)ws + w.aon + w.on);
+    float* xps = (float*)((char*)ws + w.aon + w.on);
+    double* xsum64 = (double*)((char*)ws + w.aon + w.on + w.xps);
     if (!O_on && w.on) {
         float* on = (float*)((char*)ws + w.aon);
         if (launch_scan_online(*d, Q, K, V, on, stream)) return MC_ERR_HIP;
         O_on = on;
     }
-    if (launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
+    const bool mfma = read_mfma_covers(*d);
+    if (mfma && launch_xps(*d, X, xps, stream)) return MC_ERR_HIP;
+    if (!mfma && launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
     if (launch_ssc_select(*d, top_k, U, X, xsum64, idx, stream)) return MC_ERR_HIP;
-    if (launch_ssc_readout(*d, top_k, Q, K, V, U, aon, M, M_lo, P, O_on, idx, Y, stream))
+    if (launch_ssc_readout(*d, top_k, Q, K, V, U, aon, xps, M, M_lo, P, O_on, idx, Y, stream))
         return MC_ERR_HIP;
     return MC_OK;
 }

@@ -10,13 +10,15 @@ namespace mc {
 
 // Byte sizes of the workspace regions, in the order they are carved out of `ws`.
 struct GrmWorkspace {
-    size_t aon;   // fp32 [B,H,L]: online gate logit <u_t, prefix mean of X>
+    size_t aon;   // fp32 [B,H,L]: online gate logit <u_t, prefix mean of X> (generic kernels)
     size_t on;    // fp32 [B,H,L,dv]: online read, for the generic kernels when O_on is NULL
+    size_t xps;   // fp32 [B,xh,L,dg]: segment-causal prefix sums of X (MFMA read)
     size_t total;
 };
 struct SscWorkspace {
-    size_t aon;    // fp32 [B,H,L]
+    size_t aon;    // fp32 [B,H,L] (generic kernels)
     size_t on;     // fp32 [B,H,L,dv] (generic kernels only)
+    size_t xps;    // fp32 [B,xh,L,dg] (MFMA read)
     size_t xsum64; // fp64 [B,xh,NS,dg]: segment sums of X, token order
     size_t total;
 };
@@ -44,24 +46,32 @@ int launch_scan_online(const mc_dims& d, const void* Q, const void* K, const voi
 
 int launch_aon(const mc_dims& d, const void* X, const void* U, float* a_on, void* stream);
 
-// true when the bf16 MFMA read kernel handles these sizes (it forms the online term itself
-// when O_on is NULL); otherwise the generic kernels run and need O_on
+// xps[b, xh, t, :] = sum of X over t's segment from its first token up to t (fp32)
+int launch_xps(const mc_dims& d, const void* X, float* xps, void* stream);
+
+// true when the bf16 MFMA read kernel handles these sizes (given K and V instead of O_on it
+// forms the online term and the online logit itself); otherwise the generic kernels run and
+// need O_on and a_on
 bool read_mfma_covers(const mc_dims& d);
 
+// The MFMA read forms the online logit itself from xps (launch_xps); the generic kernels
+// and the optional gamma output use a_on (launch_aon).
 int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* K,
-                     const void* V, const void* U, const float* aon, const uint16_t* M_lo,
+                     const void* V, const void* U, const float* xps, const uint16_t* M_lo,
                      const float* P, const float* O_on, const int32_t* idx, void* Y,
                      void* stream);
 
 int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const void* V,
-                       const void* U, const float* aon, const float* M, const uint16_t* M_lo,
-                       const float* P, const float* O_on, void* Y, float* gamma, void* stream);
+                       const void* U, const float* aon, const float* xps, const float* M,
+                       const uint16_t* M_lo, const float* P, const float* O_on, void* Y,
+                       float* gamma, void* stream);
 
 int launch_ssc_select(const mc_dims& d, int top_k, const void* U, const void* X,
                       double* xsum64, int32_t* idx, void* stream);
 
 int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K,
-                       const void* V, const void* U, const float* aon, const float* M,
+                       const void* V, const void* U, const float* aon, const float* xps,
+                       const float* M,
                        const uint16_t* M_lo, const float* P, const float* O_on,
                        const int32_t* idx, void* Y, void* stream);
 

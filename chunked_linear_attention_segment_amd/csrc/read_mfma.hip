@@ -4,7 +4,8 @@
 // Memory Caching paper §3.1, Eq. (9)-(10): for token t of segment s
 //     y_t = gamma^(s) M_t^(s) phi(q_t) + sum_{i<s} gamma^(i) M^(i) phi(q_t),
 //     gamma_t = softmax( <u_t, P_0>, ..., <u_t, P_{s-1}>, a_on[t] ),
-// a_on[t] = <u_t, prefix mean of X over t's segment> (the online segment's logit).  With
+// a_on[t] = <u_t, prefix mean of X over t's segment> (the online segment's logit), formed here
+// from xps, the segment-causal prefix sums of X.  With
 // SSC = true it is the Sparse Selective Caching read (gitcode explainer §3.4): a token weighs
 // only the segments listed for it in idx, and its softmax runs over those and the online
 // segment.  The online term M_t^(s) phi(q_t) is formed here from K and V (FON = true) as the
@@ -112,7 +113,7 @@ __device__ __forceinline__ void tile_of_block(int bid, int BH, int T, int& bh, i
 template <int DK, int DV, bool SSC, bool FON, int PHI>
 __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ U, const float* __restrict__ aon, const bf16_t* __restrict__ S,
+    const bf16_t* __restrict__ U, const float* __restrict__ xps, const bf16_t* __restrict__ S,
     const float* __restrict__ P, const float* __restrict__ O_on,
     const int32_t* __restrict__ idx, int top_k, int BH, int H, int L, int C, int NS, int DG,
     int xh, bf16_t* __restrict__ Y) {
@@ -167,10 +168,37 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
                         U + ((size_t)bh * L + tok[tb]) * DG + kc * 16 + hi32 * 8);
     };
     load_u();
-    float m[TB], l[TB], won[TB];
+    // online logit a_on = <u_t, xps_t> / (j + 1): the lane half hi32 holds the u values
+    // 16 kc + 8 hi32 .. + 8 of its U fragments; the halves are summed
+    float m[TB], l[TB], won[TB], a_on[TB];
+    float4 xv[TB][DG_MAX / 16][2];  // every load issued before the first product
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-        m[tb] = aon[(size_t)bh * L + tok[tb]];
+        const float* xr = xps + (bx * L + tok[tb]) * DG + hi32 * 8;
+#pragma unroll
+        for (int kc = 0; kc < DG_MAX / 16; ++kc)
+            if (kc < DG / 16) {
+                xv[tb][kc][0] = *reinterpret_cast<const float4*>(xr + kc * 16);
+                xv[tb][kc][1] = *reinterpret_cast<const float4*>(xr + kc * 16 + 4);
+            }
+    }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        float dot = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < DG_MAX / 16; ++kc) {
+            if (kc < DG / 16) {
+                const float4 x0 = xv[tb][kc][0], x1 = xv[tb][kc][1];
+                const ru32x4_t u = ub[tb][kc];
+                dot += __uint_as_float(u[0] << 16) * x0.x + __uint_as_float(u[0] & 0xffff0000u) * x0.y;
+                dot += __uint_as_float(u[1] << 16) * x0.z + __uint_as_float(u[1] & 0xffff0000u) * x0.w;
+                dot += __uint_as_float(u[2] << 16) * x1.x + __uint_as_float(u[2] & 0xffff0000u) * x1.y;
+                dot += __uint_as_float(u[3] << 16) * x1.z + __uint_as_float(u[3] & 0xffff0000u) * x1.w;
+            }
+        }
+        dot += __shfl_xor(dot, 32, 64);
+        a_on[tb] = dot / (float)(tok[tb] - seg[tb] * C + 1);
+        m[tb] = a_on[tb];
         l[tb] = 0.f;
     }
 
@@ -310,7 +338,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
         weights(0, true);
     }
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) won[tb] = __expf(aon[(size_t)bh * L + tok[tb]] - m[tb]);
+    for (int tb = 0; tb < TB; ++tb) won[tb] = __expf(a_on[tb] - m[tb]);
 
     __syncthreads();  // the staged means are consumed (region A is free)
 
@@ -420,25 +448,34 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
                 // keys all after the block's tokens, or all before its earliest segment start
                 if (k0 > tlast[tb] || k0 + 63 < tseg0[tb]) continue;
                 const bool full = (k0 + 63 <= tfirst[tb]) && (k0 >= (tlast[tb] / C) * C);
+                // scores S^T = phi(K) phi(Q)^T; K fragments read one k-step ahead
+                auto kfrag = [&](int ks, int rb) {
+                    ru32x4_t ka = *reinterpret_cast<const ru32x4_t*>(
+                        &kt[(rb * 32 + l32) * DK + (((2 * ks + hi32) ^ swz) * 8)]);
+                    if (PHI) {  // the key tile holds raw k
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            ka[e] = pack_bf16x2(feature(__uint_as_float(ka[e] << 16), 1),
+                                                feature(__uint_as_float(ka[e] & 0xffff0000u), 1));
+                    }
+                    return ka;
+                };
                 rf32x16_t sc[2];
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sc[rb][r] = 0.f;
+                ru32x4_t kf[2][2];
+                kf[0][0] = kfrag(0, 0);
+                kf[0][1] = kfrag(0, 1);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                    for (int rb = 0; rb < 2; ++rb) {
-                        ru32x4_t ka = *reinterpret_cast<const ru32x4_t*>(
-                            &kt[(rb * 32 + l32) * DK + (((2 * ks + hi32) ^ swz) * 8)]);
-                        if (PHI) {  // the key tile holds raw k
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                ka[e] = pack_bf16x2(feature(__uint_as_float(ka[e] << 16), 1),
-                                                    feature(__uint_as_float(ka[e] & 0xffff0000u), 1));
-                        }
-                        sc[rb] = mfma_bf16(ka, qb[tb][ks], sc[rb]);
+                    if (ks + 1 < KS) {
+                        kf[(ks + 1) & 1][0] = kfrag(ks + 1, 0);
+                        kf[(ks + 1) & 1][1] = kfrag(ks + 1, 1);
                     }
+                    sc[0] = mfma_bf16(kf[ks & 1][0], qb[tb][ks], sc[0]);
+                    sc[1] = mfma_bf16(kf[ks & 1][1], qb[tb][ks], sc[1]);
                 }
                 // mask to segment(t) start <= key <= t; key = k0 + 4*hi32 + (an immediate)
                 const int t = tok[tb];
@@ -466,18 +503,21 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
                             pack_bf16x2(sc[rb][8 * q + 4] * wo, sc[rb][8 * q + 5] * wo),
                             pack_bf16x2(sc[rb][8 * q + 6] * wo, sc[rb][8 * q + 7] * wo)};
                     }
+                // acc += v^T S^T; v^T fragments read one step ahead
+                auto vfrag = [&](int n) {
+                    const int c = (n / 4) * 32 + l32, kk = n % 4;
+                    const uint2 lo = *reinterpret_cast<const uint2*>(
+                        &vt[c * 64 + (((2 * kk) ^ (c & 7)) * 8) + 4 * hi32]);
+                    const uint2 hi = *reinterpret_cast<const uint2*>(
+                        &vt[c * 64 + (((2 * kk + 1) ^ (c & 7)) * 8) + 4 * hi32]);
+                    return ru32x4_t{lo.x, lo.y, hi.x, hi.y};
+                };
+                ru32x4_t vf[2];
+                vf[0] = vfrag(0);
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const int c = cb * 32 + l32;
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        const uint2 lo = *reinterpret_cast<const uint2*>(
-                            &vt[c * 64 + (((2 * kk) ^ (c & 7)) * 8) + 4 * hi32]);
-                        const uint2 hi = *reinterpret_cast<const uint2*>(
-                            &vt[c * 64 + (((2 * kk + 1) ^ (c & 7)) * 8) + 4 * hi32]);
-                        acc[cb][tb] = mfma_bf16(ru32x4_t{lo.x, lo.y, hi.x, hi.y}, sb[kk],
-                                                acc[cb][tb]);
-                    }
+                for (int n = 0; n < CB * 4; ++n) {
+                    if (n + 1 < CB * 4) vf[(n + 1) & 1] = vfrag(n + 1);
+                    acc[n / 4][tb] = mfma_bf16(vf[n & 1], sb[n % 4], acc[n / 4][tb]);
                 }
             }
             if (kc + 1 < nkc) store_v(kc + 1);  // its buffer was last read in chunk kc - 1
@@ -620,29 +660,29 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
 
 template <int DK, int DV, bool SSC, bool FON, int PHI>
 void launch_k(const mc_dims& d, int top_k, const void* Q, const void* K, const void* V,
-              const void* U, const float* aon, const uint16_t* M_lo, const float* P,
+              const void* U, const float* xps, const uint16_t* M_lo, const float* P,
               const float* O_on, const int32_t* idx, void* Y, hipStream_t st) {
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     const int T = (d.L + RT - 1) / RT;
     const int BH = d.B * d.H;
     hipLaunchKernelGGL((grm_read_kernel<DK, DV, SSC, FON, PHI>), dim3(BH * T), dim3(RTHREADS), 0,
                        st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                       (const bf16_t*)U, aon, (const bf16_t*)M_lo, P, O_on, idx, top_k, BH, d.H,
+                       (const bf16_t*)U, xps, (const bf16_t*)M_lo, P, O_on, idx, top_k, BH, d.H,
                        d.L, d.seg_len, NS, d.d_g, d.x_heads, (bf16_t*)Y);
 }
 
 template <int DK, int DV, bool SSC>
 int launch_t(const mc_dims& d, int top_k, const void* Q, const void* K, const void* V,
-             const void* U, const float* aon, const uint16_t* M_lo, const float* P,
+             const void* U, const float* xps, const uint16_t* M_lo, const float* P,
              const float* O_on, const int32_t* idx, void* Y, hipStream_t st) {
     // the online term is formed in the kernel (from K and V) when the scan did not write it;
     // the feature map is a template argument so the key fragments' loop has no branches
     if (O_on)
-        d.phi ? launch_k<DK, DV, SSC, false, 1>(d, top_k, Q, K, V, U, aon, M_lo, P, O_on, idx, Y, st)
-              : launch_k<DK, DV, SSC, false, 0>(d, top_k, Q, K, V, U, aon, M_lo, P, O_on, idx, Y, st);
+        d.phi ? launch_k<DK, DV, SSC, false, 1>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, st)
+              : launch_k<DK, DV, SSC, false, 0>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, st);
     else
-        d.phi ? launch_k<DK, DV, SSC, true, 1>(d, top_k, Q, K, V, U, aon, M_lo, P, O_on, idx, Y, st)
-              : launch_k<DK, DV, SSC, true, 0>(d, top_k, Q, K, V, U, aon, M_lo, P, O_on, idx, Y, st);
+        d.phi ? launch_k<DK, DV, SSC, true, 1>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, st)
+              : launch_k<DK, DV, SSC, true, 0>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, st);
     return (int)hipGetLastError();
 }
 
@@ -655,15 +695,15 @@ bool read_mfma_covers(const mc_dims& d) {
 }
 
 int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* K,
-                     const void* V, const void* U, const float* aon, const uint16_t* M_lo,
+                     const void* V, const void* U, const float* xps, const uint16_t* M_lo,
                      const float* P, const float* O_on, const int32_t* idx, void* Y,
                      void* stream) {
     if (!read_mfma_covers(d)) return -1;
     hipStream_t st = (hipStream_t)stream;
 #define MC_RD(DK, DV)                                                                          \
     if (d.d_k == DK && d.d_v == DV)                                                            \
-        return ssc ? launch_t<DK, DV, true>(d, top_k, Q, K, V, U, aon, M_lo, P, O_on, idx, Y, st) \
-                   : launch_t<DK, DV, false>(d, top_k, Q, K, V, U, aon, M_lo, P, O_on, idx, Y, st);
+        return ssc ? launch_t<DK, DV, true>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, st) \
+                   : launch_t<DK, DV, false>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, st);
     MC_RD(128, 128)
     MC_RD(128, 64)
     MC_RD(64, 128)

@@ -112,6 +112,72 @@ int launch_aon(const mc_dims& d, const void* X, const void* U, float* a_on, void
     return (int)hipGetLastError();
 }
 
+// Segment-causal prefix sums of X in fp32: xps[b, xh, t, e] = sum of X[b, xh, r, e] over r from
+// the first token of t's segment to t (the numerator of the online segment's prefix mean,
+// Memory Caching paper §3.1, Eq. 10).  One workgroup per (segment, b*xh) walks the segment in
+// chunks of 64 tokens; NG groups of d_g threads each scan 64/NG rows of a chunk in registers,
+// and the group totals (LDS) plus the carry of the earlier chunks complete the sums.
+template <typename T, int NG>
+__global__ __launch_bounds__(256) void xps_kernel(const T* __restrict__ X, int L, int C, int DG,
+                                                  float* __restrict__ xps) {
+    constexpr int RG = 64 / NG;
+    __shared__ float tot[NG][256];
+    const int s = blockIdx.x;
+    const size_t base = (size_t)blockIdx.y * L * DG;
+    const int t0 = s * C, t1 = min(L, t0 + C);
+    const int e = threadIdx.x % DG, g = threadIdx.x / DG;
+    const bool act = g < NG;
+    float carry = 0.f;
+    for (int c0 = t0; c0 < t1; c0 += 64) {
+        float pre[RG];
+        float run = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const int t = c0 + g * RG + r;
+            if (act && t < t1) run += ld<T>(X, base + (size_t)t * DG + e);
+            pre[r] = run;
+        }
+        if (act) tot[g][e] = run;
+        __syncthreads();
+        if (act) {
+            float off = carry, all = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) {
+                const float v = tot[gg][e];
+                if (gg < g) off += v;
+                all += v;
+            }
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                const int t = c0 + g * RG + r;
+                if (t < t1) xps[base + (size_t)t * DG + e] = pre[r] + off;
+            }
+            carry += all;
+        }
+        __syncthreads();
+    }
+}
+
+int launch_xps(const mc_dims& d, const void* X, float* xps, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+    const dim3 grid(NS, d.B * d.x_heads);
+#define MC_XPS(T, NG)                                                                          \
+    hipLaunchKernelGGL((xps_kernel<T, NG>), grid, dim3(256), 0, st, (const T*)X, d.L, d.seg_len, \
+                       d.d_g, xps)
+    if (d.dtype == MC_BF16) {
+        if (d.d_g <= 64) MC_XPS(bf16_t, 4);
+        else if (d.d_g <= 128) MC_XPS(bf16_t, 2);
+        else MC_XPS(bf16_t, 1);
+    } else {
+        if (d.d_g <= 64) MC_XPS(float, 4);
+        else if (d.d_g <= 128) MC_XPS(float, 2);
+        else MC_XPS(float, 1);
+    }
+#undef MC_XPS
+    return (int)hipGetLastError();
+}
+
 // Generic read kernel.  A workgroup covers TT = 32 consecutive tokens of one (b, h); the 8
 // threads of a token share its gate (online softmax over the segments it reads) and each
 // owns the DV/8 output columns c = p, p+8, ...  State i is read straight from global memory
@@ -283,12 +349,13 @@ __global__ void gamma_kernel(const T* __restrict__ U, const float* __restrict__ 
 }
 
 int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const void* V,
-                       const void* U, const float* aon, const float* M, const uint16_t* M_lo,
-                       const float* P, const float* O_on, void* Y, float* gamma, void* stream) {
+                       const void* U, const float* aon, const float* xps, const float* M,
+                       const uint16_t* M_lo, const float* P, const float* O_on, void* Y,
+                       float* gamma, void* stream) {
     if (!read_mfma_covers(d))
         return launch_readout<false>(d, 0, Q, U, aon, M, M_lo, P, O_on, nullptr, Y, gamma,
                                      (hipStream_t)stream);
-    int rc = launch_read_mfma(d, false, 0, Q, K, V, U, aon, M_lo, P, O_on, nullptr, Y, stream);
+    int rc = launch_read_mfma(d, false, 0, Q, K, V, U, xps, M_lo, P, O_on, nullptr, Y, stream);
     if (rc || !gamma) return rc;
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     hipLaunchKernelGGL(gamma_kernel<bf16_t>, dim3((d.L + 63) / 64, d.B * d.H), dim3(64), 0,
@@ -298,11 +365,12 @@ int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const voi
 }
 
 int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K,
-                       const void* V, const void* U, const float* aon, const float* M,
+                       const void* V, const void* U, const float* aon, const float* xps,
+                       const float* M,
                        const uint16_t* M_lo, const float* P, const float* O_on,
                        const int32_t* idx, void* Y, void* stream) {
     if (read_mfma_covers(d))
-        return launch_read_mfma(d, true, top_k, Q, K, V, U, aon, M_lo, P, O_on, idx, Y, stream);
+        return launch_read_mfma(d, true, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, stream);
     return launch_readout<true>(d, top_k, Q, U, aon, M, M_lo, P, O_on, idx, Y, nullptr,
                                 (hipStream_t)stream);
 }

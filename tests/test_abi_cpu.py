@@ -105,14 +105,17 @@ def test_grm_workspace_and_pointers():
     assert grm(d, need, O_on=None, K=MIS) == mc.MC_ERR_ALIGN
 
 
-def test_generic_path_workspace_holds_the_online_read():
-    # the bf16 MFMA read forms the online term in-kernel; the generic kernels (fp32, or a
-    # gate width the MFMA gate does not tile) stage it in the workspace
-    bf = mc.mc_workspace_bytes(dims(), mc.MC_OP_GRM)
-    f32 = mc.mc_workspace_bytes(dims(dtype="f32"), mc.MC_OP_GRM)
-    odd = mc.mc_workspace_bytes(dims(d_g=24), mc.MC_OP_GRM)
-    assert f32 >= bf + 4 * 2 * 1024 * 128
-    assert odd >= bf + 4 * 2 * 1024 * 128
+def test_read_workspace_regions():
+    # the bf16 MFMA read forms the online term in-kernel and takes the online logit from
+    # fp32 prefix sums of X; the generic kernels (fp32, or a gate width the MFMA read does not
+    # take) stage the online read and the online logits instead
+    d = dims()
+    B, H, L, dv, dg, xh = d.B, d.H, d.L, d.d_v, d.d_g, d.x_heads
+    aon = 4 * B * H * L
+    bf = mc.mc_workspace_bytes(d, mc.MC_OP_GRM)
+    assert bf >= aon + 4 * B * xh * L * dg
+    for gen in (dims(dtype="f32"), dims(d_g=24), dims(d_g=256)):
+        assert mc.mc_workspace_bytes(gen, mc.MC_OP_GRM) >= aon + 4 * B * H * L * dv
 
 
 def test_ssc_arguments():
