@@ -14,7 +14,7 @@
  *          §3.3 Memory Soup, §3.4 Sparse Selective Caching (router score, Top-k, online
  *          memory always kept).
  *
- * Readings of points the pages leave open (each is listed in the design doc):
+ * Readings of points the pages leave open:
  *   - the memory is the unnormalised linear-attention state ([MC] §2, the Miras remark that
  *     the inner-product objective gives *unnormalised* linear attention): no 1/Z anywhere;
  *   - M = sum_r v_r phi(k_r)^T is d_v x d_k and is read as y = M phi(q) ([MC] Eq. 2, 4b);
