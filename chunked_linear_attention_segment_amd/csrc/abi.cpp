@@ -39,18 +39,16 @@ SscWorkspace ssc_workspace(const mc_dims& d) {
     return w;
 }
 
-// The cached-state read of a decode step is split over `splits` workgroups per (b, h);
-// the split count depends only on the capacity so the workspace size is stable.
+// The cached states of a decode step are read in runs of kDecodeRun states (one workgroup
+// each); the workspace holds the partial softmaxes of a full cache, so its size depends only
+// on n_cap.
 DecodeWorkspace decode_workspace(const mc_dims& d, int n_cap, int /*n_cached*/) {
     DecodeWorkspace w{};
-    int splits = (n_cap + 31) / 32;
-    if (splits < 1) splits = 1;
-    w.splits = splits;
+    w.slots = 1 + (n_cap + kDecodeRun - 1) / kDecodeRun;
     const size_t bh = (size_t)d.B * d.H;
-    w.gamma = align256(sizeof(float) * bh * (size_t)(n_cap + 1));
-    w.partial = align256(sizeof(float) * bh * (size_t)splits * d.d_v);
-    w.y_on = align256(sizeof(float) * bh * d.d_v);
-    w.total = w.gamma + w.partial + w.y_on;
+    w.partial = align256(sizeof(float) * bh * (size_t)w.slots * d.d_v);
+    w.ml = align256(sizeof(float) * bh * (size_t)w.slots * 2);
+    w.total = w.partial + w.ml;
     return w;
 }
 

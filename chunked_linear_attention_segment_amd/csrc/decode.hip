@@ -7,159 +7,247 @@
 // and y = gamma_on M_on phi(q) + sum_i gamma_i M^(i) phi(q).  When the online segment then
 // holds C tokens its state and mean become cache slot n and the online memory restarts.
 //
-// Three launches on the caller's stream:
-//   decode_update_gate  per (b,h): M_on += v phi(k)^T, online read, logits, softmax;
-//                       emission of M_on into the cache
-//   decode_stream       per (split, b,h): gamma-weighted read of a slice of cached states
-//   decode_combine      per (b,h): y = online term + split partials; x-sum update and the
-//                       emission of the segment mean (after every head has read the old sum)
+// Two launches on the caller's stream:
+//   decode_read     1 + R workgroups per (b,h).  Workgroup 0 updates the online memory with
+//                   the token, reads it and forms the online logit from the prefix mean; at a
+//                   segment boundary it moves the state into cache slot n.  Workgroup r >= 1
+//                   takes a contiguous run of cached states: their logits <u, P_i>, a softmax
+//                   local to the run (its max m_r and sum l_r of exp(a_i - m_r)) and the
+//                   weighted read sum_i exp(a_i - m_r) M^(i) phi(q) of the run.
+//   decode_combine  per (b,h): merges the partial softmaxes of the runs into y (the softmax
+//                   over all logits, regrouped); x-sum update and the emission of the segment
+//                   mean (after every head has read the old sum)
+//
+// The cached states are read once, with 16-byte non-temporal loads, so the step streams
+// the cache at HBM rate; everything else is small.
 #include "common.cuh"
 #include "mc_internal.h"
 
 namespace mc {
 
-// Block-wide reductions over 256 threads (4 waves of 64).
-__device__ __forceinline__ float block_max256(float v, float* red) {
-    v = warp_max(v, 64);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kDecodeThreads = 256;
+
+// Block-wide sum over 256 threads (4 waves of 64).
 __device__ __forceinline__ float block_sum256(float v, float* red) {
     v = warp_sum(v, 64);
-    __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-template <typename T, typename TC, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_update_gate_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ u, const T* __restrict__ x, float* __restrict__ M_on,
-    const float* __restrict__ xsum, int count, TC* __restrict__ M_cache,
-    const float* __restrict__ P_cache, int n, int n_cap, int emit, int DG, int H, int xh,
-    int phi, float* __restrict__ gamma, float* __restrict__ y_on) {
-    constexpr int TPR = 256 / DV;
-    constexpr int CPT = DK / TPR;
-    __shared__ float sk[DK], sq[DK], sv[DV], sp[256];
-    __shared__ float red[4];
-    const size_t bh = blockIdx.x;
-    const int b = (int)(bh / H), h = (int)(bh % H);
-    const size_t bx = (size_t)b * xh + (xh == 1 ? 0 : h);
-    const int tid = threadIdx.x;
-    for (int r = tid; r < DK; r += 256) {
-        sk[r] = feature(ld(k, bh * DK + r), phi);
-        sq[r] = feature(ld(q, bh * DK + r), phi);
-    }
-    for (int c = tid; c < DV; c += 256) sv[c] = ld(v, bh * DV + c);
-    // prefix mean of the online segment including the new token
-    const float inv = 1.f / (float)(count + 1);
-    for (int e = tid; e < DG; e += 256) sp[e] = (xsum[bx * DG + e] + ld(x, bx * DG + e)) * inv;
-    __syncthreads();
-
-    // online memory update and read (row c, columns r0..r0+CPT-1 of this thread)
-    const int c = tid / TPR, r0 = (tid % TPR) * CPT;
-    float* mrow = M_on + (bh * DV + c) * DK + r0;
-    float acc = 0.f;
-    float mloc[CPT];
+// <16-byte chunk of a cached state row, matching slice of phi(q)>
+template <typename TC> __device__ __forceinline__ float chunk_dot(u32x4_t c, const float* qv);
+template <> __device__ __forceinline__ float chunk_dot<bf16_t>(u32x4_t c, const float* qv) {
+    float d = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        mloc[i] = mrow[i] + sv[c] * sk[r0 + i];
-        acc += mloc[i] * sq[r0 + i];
+    for (int e = 0; e < 4; ++e) {
+        d += __uint_as_float(c[e] << 16) * qv[2 * e];
+        d += __uint_as_float(c[e] & 0xffff0000u) * qv[2 * e + 1];
     }
-    acc = warp_sum(acc, TPR);
-    if (emit) {
-        TC* dst = M_cache + ((bh * n_cap + n) * DV + c) * (size_t)DK + r0;
+    return d;
+}
+template <> __device__ __forceinline__ float chunk_dot<float>(u32x4_t c, const float* qv) {
+    float d = 0.f;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) { st(dst, i, mloc[i]); mrow[i] = 0.f; }
-    } else {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) mrow[i] = mloc[i];
-    }
-
-    // logits: a_i = <u, P_i> for the n cached segments, a_on = <u, prefix mean>
-    const T* ub = u + bh * DG;
-    float a_on = 0.f;
-    for (int e = 0; e < DG; ++e) a_on += ld(ub, e) * sp[e];
-    float lmax = a_on;
-    for (int i = tid; i < n; i += 256) {
-        const float* Pi = P_cache + (bx * n_cap + i) * DG;
-        float a = 0.f;
-        for (int e = 0; e < DG; ++e) a += ld(ub, e) * Pi[e];
-        gamma[bh * (n_cap + 1) + i] = a;
-        lmax = fmaxf(lmax, a);
-    }
-    const float mx = block_max256(lmax, red);
-    float lsum = (tid == 0) ? __expf(a_on - mx) : 0.f;
-    for (int i = tid; i < n; i += 256) lsum += __expf(gamma[bh * (n_cap + 1) + i] - mx);
-    const float z = block_sum256(lsum, red);
-    const float inv_z = 1.f / z;
-    for (int i = tid; i < n; i += 256) {
-        float* g = gamma + bh * (n_cap + 1) + i;
-        *g = __expf(*g - mx) * inv_z;
-    }
-    if (tid % TPR == 0) y_on[bh * DV + c] = __expf(a_on - mx) * inv_z * acc;
+    for (int e = 0; e < 4; ++e) d += __uint_as_float(c[e]) * qv[e];
+    return d;
 }
 
-// Streams cached states [sp*per, min(n, (sp+1)*per)) of one (b,h).  Row c of a state is
-// read as DK/8 chunks of 8 elements; thread tid always takes chunk (tid % CPR) of rows
-// tid/CPR + pass*RPP, so its slice of phi(q) stays in registers.
+// Four consecutive fp32 values of the online state stored at cache precision.
+template <typename TC> __device__ __forceinline__ void store4(TC* p, const float* m);
+template <> __device__ __forceinline__ void store4<float>(float* p, const float* m) {
+    *reinterpret_cast<float4*>(p) = make_float4(m[0], m[1], m[2], m[3]);
+}
+template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* m) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]));
+}
+
+struct DecodeArgs {
+    const void *q, *k, *v, *u, *x;
+    float* M_on;
+    const float* xsum;
+    void* M_cache;
+    const float* P_cache;
+    float* partial;  // [B*H, 1 + runs, DV]
+    float* ml;       // [B*H, 1 + runs, 2]: (m, l) of each partial softmax
+    int count, n, n_cap, per, runs, emit, DG, H, xh, phi;
+};
+
+// Workgroup 0 of (b,h): M_on += v phi(k)^T, read with phi(q), online logit; emission.
+// Thread t covers 4-column chunks (t % CPR) of rows t / CPR + p * RPP.
 template <typename T, typename TC, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_stream_kernel(const T* __restrict__ q,
-                                                            const TC* __restrict__ M_cache,
-                                                            const float* __restrict__ gamma,
-                                                            int n, int n_cap, int per, int phi,
-                                                            float* __restrict__ partial,
-                                                            int splits) {
-    constexpr int CPR = DK / 8;        // chunks per row
-    constexpr int RPP = 256 / CPR;     // rows per pass
+__device__ __forceinline__ void decode_online(const DecodeArgs& a, size_t bh) {
+    constexpr int CPR = DK / 4;
+    constexpr int RPP = kDecodeThreads / CPR;
     constexpr int PASSES = DV / RPP;
-    const int sp = blockIdx.x;
-    const size_t bh = blockIdx.y;
+    __shared__ float sk[DK], sq[DK], sv[DV], red[4];
     const int tid = threadIdx.x;
-    const int kc = (tid % CPR) * 8;
-    const int r0 = tid / CPR;
-    float qv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[e] = feature(ld(q, bh * DK + kc + e), phi);
+    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    const size_t bx = (size_t)b * a.xh + (a.xh == 1 ? 0 : h);
+    for (int r = tid; r < DK; r += kDecodeThreads) {
+        sk[r] = feature(ld((const T*)a.k, bh * DK + r), a.phi);
+        sq[r] = feature(ld((const T*)a.q, bh * DK + r), a.phi);
+    }
+    for (int c = tid; c < DV; c += kDecodeThreads) sv[c] = ld((const T*)a.v, bh * DV + c);
+    // online logit: <u, prefix mean of the online segment including the new token>
+    float au = 0.f;
+    if (tid < a.DG)
+        au = ld((const T*)a.u, bh * a.DG + tid) *
+             (a.xsum[bx * a.DG + tid] + ld((const T*)a.x, bx * a.DG + tid));
+    const float a_on = block_sum256(au, red) / (float)(a.count + 1);  // syncs sk, sq, sv too
+
+    const int kc = (tid % CPR) * 4, r0 = tid / CPR;
     float acc[PASSES];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) acc[p] = 0.f;
-    const int i0 = sp * per, i1 = min(n, i0 + per);
-    const float* g = gamma + bh * (n_cap + 1);
-    for (int i = i0; i < i1; ++i) {
-        const TC* Si = M_cache + (bh * n_cap + i) * (size_t)(DV * DK);
-        const float gi = g[i];
+    for (int p = 0; p < PASSES; ++p) {
+        const int c = r0 + p * RPP;
+        float* mrow = a.M_on + (bh * DV + c) * DK + kc;
+        const float4 m4 = *reinterpret_cast<const float4*>(mrow);
+        float m[4] = {m4.x, m4.y, m4.z, m4.w};
+        float d = 0.f;
 #pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const TC* row = Si + (size_t)(r0 + p * RPP) * DK + kc;
-            float d = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) d += ld(row, e) * qv[e];
-            acc[p] += gi * d;
+        for (int e = 0; e < 4; ++e) {
+            m[e] += sv[c] * sk[kc + e];
+            d += m[e] * sq[kc + e];
+        }
+        acc[p] = d;
+        if (a.emit) {
+            TC* dst = (TC*)a.M_cache + ((bh * a.n_cap + a.n) * DV + c) * (size_t)DK + kc;
+            store4<TC>(dst, m);
+            *reinterpret_cast<float4*>(mrow) = make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+            *reinterpret_cast<float4*>(mrow) = make_float4(m[0], m[1], m[2], m[3]);
         }
     }
+    const size_t slot = bh * (size_t)(1 + a.runs);
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const float r = warp_sum(acc[p], CPR);
-        if (tid % CPR == 0) partial[(bh * splits + sp) * DV + r0 + p * RPP] = r;
+        if (tid % CPR == 0) a.partial[slot * DV + r0 + p * RPP] = r;
+    }
+    if (tid == 0) {
+        a.ml[slot * 2] = a_on;
+        a.ml[slot * 2 + 1] = 1.f;
     }
 }
 
+// Workgroup r >= 1 of (b,h): cached states [(r-1)*per, min(n, r*per)).  Thread t always takes
+// the 16-byte chunk t + 256 p of a state (column chunk t % CPR of row t / CPR + p * RPP), so
+// its slice of phi(q) stays in registers; SPI states are loaded per iteration.
+template <typename T, typename TC, int DK, int DV>
+__device__ __forceinline__ void decode_run(const DecodeArgs& a, size_t bh, int r) {
+    constexpr int E = 16 / (int)sizeof(TC);   // elements per 16-byte chunk
+    constexpr int CPR = DK / E;               // chunks per row
+    constexpr int RPP = kDecodeThreads / CPR; // rows per pass
+    constexpr int PASSES = DV / RPP;          // chunks per thread and state
+    constexpr int SCH = DV * DK / E;          // chunks per state
+    constexpr int SPI = PASSES >= 16 ? 1 : 16 / PASSES;
+    __shared__ float su[256], sa[kDecodeRun];
+    const int tid = threadIdx.x;
+    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    const size_t bx = (size_t)b * a.xh + (a.xh == 1 ? 0 : h);
+    const int i0 = (r - 1) * a.per, cnt = min(a.n, i0 + a.per) - i0;  // >= 1 by the grid
+
+    for (int e = tid; e < a.DG; e += kDecodeThreads) su[e] = ld((const T*)a.u, bh * a.DG + e);
+    const int kc = (tid % CPR) * E;
+    float qv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) qv[e] = feature(ld((const T*)a.q, bh * DK + kc + e), a.phi);
+    __syncthreads();
+    // logits of the run: 16 lanes per cached segment
+    {
+        const int g = tid >> 4, l = tid & 15;
+        for (int j = g; j < cnt; j += kDecodeThreads / 16) {
+            const float* Pi = a.P_cache + (bx * a.n_cap + i0 + j) * a.DG;
+            float s = 0.f;
+            for (int e = l; e < a.DG; e += 16) s += su[e] * Pi[e];
+            s = warp_sum(s, 16);
+            if (l == 0) sa[j] = s;
+        }
+    }
+    __syncthreads();
+    float m = -INFINITY;
+    for (int j = 0; j < cnt; ++j) m = fmaxf(m, sa[j]);
+
+    float acc[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) acc[p] = 0.f;
+    const u32x4_t* base =
+        reinterpret_cast<const u32x4_t*>((const TC*)a.M_cache +
+                                         (bh * a.n_cap + i0) * (size_t)(DV * DK)) + tid;
+    int j = 0;
+    for (; j + SPI <= cnt; j += SPI) {
+        u32x4_t c[SPI][PASSES];
+#pragma unroll
+        for (int s = 0; s < SPI; ++s)
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p)
+                c[s][p] = __builtin_nontemporal_load(base + (size_t)(j + s) * SCH + p * 256);
+#pragma unroll
+        for (int s = 0; s < SPI; ++s) {
+            const float w = __expf(sa[j + s] - m);
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p) acc[p] += w * chunk_dot<TC>(c[s][p], qv);
+        }
+    }
+    for (; j < cnt; ++j) {
+        u32x4_t c[PASSES];
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+            c[p] = __builtin_nontemporal_load(base + (size_t)j * SCH + p * 256);
+        const float w = __expf(sa[j] - m);
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) acc[p] += w * chunk_dot<TC>(c[p], qv);
+    }
+    const size_t slot = bh * (size_t)(1 + a.runs) + r;
+    const int r0 = tid / CPR;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const float s = warp_sum(acc[p], CPR);
+        if (tid % CPR == 0) a.partial[slot * DV + r0 + p * RPP] = s;
+    }
+    if (tid == 0) {
+        float l = 0.f;
+        for (int jj = 0; jj < cnt; ++jj) l += __expf(sa[jj] - m);
+        a.ml[slot * 2] = m;
+        a.ml[slot * 2 + 1] = l;
+    }
+}
+
+// One-dimensional grid: block id = bh * (1 + runs) + r.
+template <typename T, typename TC, int DK, int DV>
+__global__ __launch_bounds__(kDecodeThreads) void decode_read_kernel(DecodeArgs a) {
+    const size_t bh = blockIdx.x / (1 + a.runs);
+    const int r = (int)(blockIdx.x % (1 + a.runs));
+    if (r == 0)
+        decode_online<T, TC, DK, DV>(a, bh);
+    else
+        decode_run<T, TC, DK, DV>(a, bh, r);
+}
+
+// y = sum_r e^{m_r - m} Y_r / sum_r e^{m_r - m} l_r with m = max_r m_r: the softmax over all
+// n + 1 logits, summed run by run.
 template <typename T>
-__global__ void decode_combine_kernel(const float* __restrict__ y_on,
-                                      const float* __restrict__ partial, int splits, int DV,
+__global__ void decode_combine_kernel(const float* __restrict__ partial,
+                                      const float* __restrict__ ml, int slots, int DV,
                                       const T* __restrict__ x, float* __restrict__ xsum,
                                       float* __restrict__ P_cache, int n, int n_cap, int emit,
                                       int C, int DG, int H, int xh, T* __restrict__ y) {
     const size_t bh = blockIdx.x;
     const int b = (int)(bh / H), h = (int)(bh % H);
+    const float* mlb = ml + bh * slots * 2;
+    float m = -INFINITY;
+    for (int s = 0; s < slots; ++s) m = fmaxf(m, mlb[2 * s]);
+    float z = 0.f;
+    for (int s = 0; s < slots; ++s) z += __expf(mlb[2 * s] - m) * mlb[2 * s + 1];
+    const float inv_z = 1.f / z;
     for (int c = threadIdx.x; c < DV; c += blockDim.x) {
-        float acc = y_on[bh * DV + c];
-        for (int sp = 0; sp < splits; ++sp) acc += partial[(bh * splits + sp) * DV + c];
-        st(y, bh * DV + c, acc);
+        float acc = 0.f;
+        for (int s = 0; s < slots; ++s)
+            acc += __expf(mlb[2 * s] - m) * partial[(bh * slots + s) * DV + c];
+        st(y, bh * DV + c, acc * inv_z);
     }
     // x-sum of the online segment (shared by the heads when xh == 1: head 0 owns it)
     if (xh == 1 ? h == 0 : true) {
@@ -182,22 +270,23 @@ static int launch_decode_t(const mc_dims& d, const void* q, const void* k, const
                            void* M_cache, float* P_cache, int n, int n_cap, int emit, void* y,
                            void* ws, hipStream_t st) {
     const DecodeWorkspace w = decode_workspace(d, n_cap, n);
-    float* gamma = (float*)ws;
-    float* partial = (float*)((char*)ws + w.gamma);
-    float* y_on = (float*)((char*)ws + w.gamma + w.partial);
-    const int BH = d.B * d.H;
-    hipLaunchKernelGGL((decode_update_gate_kernel<T, TC, DK, DV>), dim3(BH), dim3(256), 0, st,
-                       (const T*)q, (const T*)k, (const T*)v, (const T*)u, (const T*)x, M_on,
-                       xsum, count, (TC*)M_cache, P_cache, n, n_cap, emit, d.d_g, d.H,
-                       d.x_heads, d.phi, gamma, y_on);
-    const int splits = w.splits;
-    const int per = (n_cap + splits - 1) / splits;
-    hipLaunchKernelGGL((decode_stream_kernel<T, TC, DK, DV>), dim3(splits, BH), dim3(256), 0, st,
-                       (const T*)q, (const TC*)M_cache, gamma, n, n_cap, per, d.phi, partial,
-                       splits);
-    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(BH), dim3(128), 0, st, y_on, partial,
-                       splits, d.d_v, (const T*)x, xsum, P_cache, n, n_cap, emit, d.seg_len,
-                       d.d_g, d.H, d.x_heads, (T*)y);
+    DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.u = u; a.x = x;
+    a.M_on = M_on; a.xsum = xsum; a.M_cache = M_cache; a.P_cache = P_cache;
+    a.partial = (float*)ws;
+    a.ml = (float*)((char*)ws + w.partial);
+    a.count = count; a.n = n; a.n_cap = n_cap; a.emit = emit;
+    a.per = kDecodeRun;
+    a.runs = (n + a.per - 1) / a.per;
+    a.DG = d.d_g; a.H = d.H; a.xh = d.x_heads; a.phi = d.phi;
+    const size_t BH = (size_t)d.B * d.H;
+    const size_t blocks = BH * (size_t)(1 + a.runs);
+    if (blocks > 0x7fffffffu || a.runs + 1 > w.slots) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_read_kernel<T, TC, DK, DV>), dim3((unsigned)blocks),
+                       dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3((unsigned)BH), dim3(128), 0, st,
+                       a.partial, a.ml, 1 + a.runs, d.d_v, (const T*)x, xsum, P_cache, n, n_cap,
+                       emit, d.seg_len, d.d_g, d.H, d.x_heads, (T*)y);
     return (int)hipGetLastError();
 }
 

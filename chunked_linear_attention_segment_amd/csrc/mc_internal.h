@@ -22,12 +22,15 @@ struct SscWorkspace {
     size_t xsum64; // fp64 [B,xh,NS,dg]: segment sums of X, token order
     size_t total;
 };
+// Decode: each (b, h) has one partial softmax for the online segment and one per run of
+// kDecodeRun cached states (one workgroup each: many short runs keep every compute unit
+// streaming to the end of the launch); `slots` = 1 + runs at n_cached = n_cap.
+constexpr int kDecodeRun = 8;
 struct DecodeWorkspace {
-    size_t gamma;    // fp32 [B,H,n_cap+1]
-    size_t partial;  // fp32 [B,H,splits,dv]
-    size_t y_on;     // fp32 [B,H,dv]
+    size_t partial;  // fp32 [B,H,slots,dv]: unnormalised reads of the runs
+    size_t ml;       // fp32 [B,H,slots,2]: max logit and sum of exp of each run
     size_t total;
-    int splits;
+    int slots;
 };
 
 GrmWorkspace grm_workspace(const mc_dims& d);

@@ -45,24 +45,25 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* out) {
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-// Streaming read: each thread keeps four 16-byte loads in flight per iteration and folds them
-// with xor; one word per wave is written so the loads cannot be dropped.
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src, size_t n16,
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming read: workgroup g reads the contiguous 16-byte words [g*per, (g+1)*per) with
+// non-temporal loads, four per thread in flight, and folds them with xor; one word per wave is
+// written so the loads cannot be dropped.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ src,
+                                                          size_t n16, size_t per,
                                                           uint32_t* __restrict__ out) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t b0 = (size_t)blockIdx.x * per;
+    const size_t b1 = b0 + per < n16 ? b0 + per : n16;
     uint32_t acc = 0;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 v0 = src[i];
-        const uint4 v1 = src[i + stride];
-        const uint4 v2 = src[i + 2 * stride];
-        const uint4 v3 = src[i + 3 * stride];
-        acc ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
-        acc ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
-    }
-    for (; i < n16; i += stride) {
-        const uint4 v = src[i];
-        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    for (size_t i = b0 + threadIdx.x; i < b1; i += 4 * 256) {
+        u32x4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] = i + u * 256 < b1 ? __builtin_nontemporal_load(src + i + u * 256)
+                                    : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
     if ((threadIdx.x & 63) == 0) out[((size_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6] = acc;
@@ -99,8 +100,10 @@ int mcpeak_stream_out_words(int n_blocks) { return n_blocks * 4; }
 
 int mcpeak_stream_read(const void* src, size_t bytes, int n_blocks, uint32_t* out, void* stream) {
     if (!src || !out || n_blocks <= 0 || (bytes & 15) || ((uintptr_t)src & 15)) return 1;
+    const size_t n16 = bytes / 16;
+    const size_t per = (n16 + n_blocks - 1) / n_blocks;
     hipLaunchKernelGGL(stream_read_kernel, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream,
-                       (const uint4*)src, bytes / 16, out);
+                       (const u32x4_t*)src, n16, per, out);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

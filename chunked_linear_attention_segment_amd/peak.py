@@ -63,8 +63,9 @@ def mfma_bf16_tflops(n_blocks=4096, iters=2048, reps=5):
     return lib.mcpeak_mfma_flops(n_blocks, iters) / (ms / 1e3) / 1e12
 
 
-def hbm_read_gbs(gib=4, n_blocks=8192, reps=5):
-    """Measured HBM streaming-read bandwidth (GB/s) over a `gib` GiB buffer."""
+def hbm_read_gbs(gib=4, n_blocks=16384, reps=5):
+    """Measured HBM streaming-read bandwidth (GB/s) over a `gib` GiB buffer (each of the
+    `n_blocks` workgroups reads one contiguous 1/n_blocks of it)."""
     import torch
     lib = load()
     n = gib << 30

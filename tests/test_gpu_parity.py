@@ -153,12 +153,16 @@ def _gpu_decode_state(inp, dtype):
     return dev
 
 
-@pytest.mark.parametrize("dtype,phi,n,cnt,C", [("bf16", "identity", 7, 3, 16),
-                                               ("f32", "elu1", 5, 0, 8),
-                                               ("bf16", "identity", 0, 2, 16),
-                                               ("f32", "identity", 40, 6, 8)])
-def test_decode_step_small(dtype, phi, n, cnt, C):
-    w = Workload("x", 2, 3, 1, 128, 128, 128, C, phi, dtype, op="decode")
+# n spans: no cached state, one short run, several runs with a ragged last one
+@pytest.mark.parametrize("dtype,phi,n,cnt,C,dk,dv", [("bf16", "identity", 7, 3, 16, 128, 128),
+                                                     ("f32", "elu1", 5, 0, 8, 128, 128),
+                                                     ("bf16", "identity", 0, 2, 16, 128, 128),
+                                                     ("f32", "identity", 40, 6, 8, 128, 128),
+                                                     ("bf16", "elu1", 19, 13, 16, 64, 128),
+                                                     ("bf16", "identity", 45, 5, 8, 64, 64),
+                                                     ("f32", "identity", 33, 4, 8, 128, 64)])
+def test_decode_step_small(dtype, phi, n, cnt, C, dk, dv):
+    w = Workload("x", 2, 3, 1, dk, dv, 128, C, phi, dtype, op="decode")
     cap = n + 3
     inp, d = _decode_case(w, 2, 3, n, cnt, cap, seed=11)
     dev = _gpu_decode_state(inp, dtype)
@@ -168,7 +172,7 @@ def test_decode_step_small(dtype, phi, n, cnt, C):
     ws = mc.workspace(d, mc.MC_OP_DECODE, n_cap=cap)
     # several steps in a row, crossing a segment boundary (emission) when C - cnt <= steps
     for step in range(C - cnt + 2):
-        y = torch.empty((2, 3, 128), dtype=mc.torch_dtype(d), device="cuda")
+        y = torch.empty((2, 3, dv), dtype=mc.torch_dtype(d), device="cuda")
         if step > 0:  # a fresh token each step
             rng = np.random.default_rng(100 + step)
             for key in ("q", "k", "v", "u", "x"):
