@@ -19,9 +19,11 @@
 //     Y^T[c, t] = sum_i M^(i) [c, :] (w_t^(i) phi(q_t))
 // Phases:
 //   1. gate: the means P are staged in LDS; the logits <u_t, P_i> run on MFMA (P split into
-//      bf16 hi + lo parts, so a logit keeps ~16 mantissa bits); a first pass takes the max m_t
-//      over the online and every cached logit, a second writes the softmax numerators
-//      exp(a - m_t) for up to WMAX states to LDS (bf16) and sums l_t;
+//      bf16 hi + lo parts, so a logit keeps ~16 mantissa bits).  One pass over 32-state blocks
+//      keeps a running max m_t (starting from the online logit), writes the softmax numerators
+//      of each block against the max known at that block (bf16, LDS) and sums l_t with
+//      rescaling; the read later scales block b by exp(m_b - m_t).  Tiles with more states
+//      than LDS holds weights for take the max over every logit first instead;
 //   2. online term: chunks of 64 keys; scores phi(k).phi(q) on MFMA, masked to the token's
 //      segment and causal, scaled by the online weight exp(a_on - m_t), times v;
 //   3. cached states: state i (d_v x d_k bf16) is streamed into LDS by direct global->LDS
@@ -279,12 +281,39 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
             }
         }
     };
-    // pass 2 over a super-block: numerators exp(a - m) -> sm.w, sums into l, SSC selection bits
-    auto weights = [&](int sb0, bool from_lds) {
+    // Numerators of a super-block -> sm.w (bf16), sums into l, SSC selection bits.  With
+    // `running` the max is taken on the way (one logits pass): block bi's numerators are
+    // exp(a - mb[bi]) with mb[bi] the max over the online logit and blocks 0..bi, and l is
+    // rescaled whenever the max grows; the state loop multiplies block bi's weights by
+    // exp(mb[bi] - m) once m is final.  Without it m is already final (mb[bi] = m).
+    constexpr int NBLK = WMAX / 32;
+    float mb[NBLK][TB];
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) mb[b][tb] = 0.f;
+    auto weights = [&](int sb0, bool from_lds, bool running) {
         const int n = min(SBS, s_hi - sb0);
-        for (int b0 = 0; b0 < n; b0 += 32) {
+#pragma unroll
+        for (int bi = 0; bi < NBLK; ++bi) {
+            const int b0 = bi * 32;
+            if (b0 >= n) break;
             rf32x16_t lg[TB];
             logits(sb0 + b0, b0, from_lds, lg);
+            if (running) {
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    float bm = -INFINITY;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) bm = fmaxf(bm, lg[tb][r]);
+                    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+                    const float mn = fmaxf(m[tb], bm);
+                    l[tb] *= __expf(m[tb] - mn);
+                    m[tb] = mn;
+                }
+            }
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) mb[bi][tb] = m[tb];
             uint32_t any = 0u;
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
@@ -309,33 +338,35 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     if constexpr (SSC) {
         if (tid < WMAX / 32) sm.any_sel[tid] = 0u;
     }
-    // pass 1: m_t = max over the online logit and every cached logit of the token
-    for (int sb0 = 0; sb0 < s_hi; sb0 += SBS) {
-        const int n = min(SBS, s_hi - sb0);
-        if (sb0 > 0) __syncthreads();  // the previous super-block's means are consumed
-        stage_means(sb0, n);
-        wait_all_and_barrier();
-        for (int b0 = 0; b0 < n; b0 += 32) {
-            rf32x16_t lg[TB];
-            logits(sb0 + b0, b0, true, lg);
+    if (s_hi > SBS) {
+        // more states than one super-block: pass 1 takes m_t over every logit first, so the
+        // numerators of every super-block are final when written
+        for (int sb0 = 0; sb0 < s_hi; sb0 += SBS) {
+            const int n = min(SBS, s_hi - sb0);
+            if (sb0 > 0) __syncthreads();  // the previous super-block's means are consumed
+            stage_means(sb0, n);
+            wait_all_and_barrier();
+            for (int b0 = 0; b0 < n; b0 += 32) {
+                rf32x16_t lg[TB];
+                logits(sb0 + b0, b0, true, lg);
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                float bm = -INFINITY;
+                for (int tb = 0; tb < TB; ++tb) {
+                    float bm = -INFINITY;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) bm = fmaxf(bm, lg[tb][r]);
-                bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-                m[tb] = fmaxf(m[tb], bm);
+                    for (int r = 0; r < 16; ++r) bm = fmaxf(bm, lg[tb][r]);
+                    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+                    m[tb] = fmaxf(m[tb], bm);
+                }
             }
         }
-    }
-    // pass 2 for the first super-block (its means are still staged unless there were more)
-    if (s_hi > 0) {
-        if (s_hi > SBS) {
-            __syncthreads();
-            stage_means(0, SBS);
-            wait_all_and_barrier();
-        }
-        weights(0, true);
+        __syncthreads();
+        stage_means(0, SBS);
+        wait_all_and_barrier();
+        weights(0, true, false);
+    } else if (s_hi > 0) {
+        stage_means(0, s_hi);
+        wait_all_and_barrier();
+        weights(0, true, true);
     }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) won[tb] = __expf(a_on[tb] - m[tb]);
@@ -576,6 +607,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     };
     if (s_hi > 0) stage(0, 0);
     if (s_hi > 1) stage(1, 1);
+    float cf[TB];  // exp(mb[block] - m) of the block being read
     for (int i = 0, buf = 0; i < s_hi; ++i, buf = (buf == NBUF - 1 ? 0 : buf + 1)) {
         const int il = i % SBS;
         asm volatile("" : "+v"(swz));
@@ -592,15 +624,25 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
             }
             load_u();
             __syncthreads();
-            weights(i, false);
+            weights(i, false, false);
             __syncthreads();
+        }
+        if ((il & 31) == 0) {  // entering block il / 32 of the super-block: its correction
+            const int bi = il >> 5;
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                float mbi = mb[0][tb];
+#pragma unroll
+                for (int b = 1; b < NBLK; ++b) mbi = bi == b ? mb[b][tb] : mbi;
+                cf[tb] = __expf(mbi - m[tb]);
+            }
         }
         if constexpr (SSC) {
             if (!((sm.any_sel[il / 32] >> (il % 32)) & 1u)) continue;
         }
         float w[TB];
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) w[tb] = bf16_to_f32(sm.w[il][tl[tb]]);
+        for (int tb = 0; tb < TB; ++tb) w[tb] = bf16_to_f32(sm.w[il][tl[tb]]) * cf[tb];
         const bf16_t* st = sm.a.state[buf];
         // software pipeline in issue order: A fragments two k-steps ahead (three register
         // sets); each MFMA of k-step ks is followed by the three VALU ops that build a quarter

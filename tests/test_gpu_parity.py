@@ -35,6 +35,10 @@ SMALL = {
     "bf16_dk64_dv128_xheadsH": (Workload("x", 1, 3, 640, 64, 128, 64, 128, "identity", "bf16",
                                          x_heads=3), {}),
     "f32_C1_L40": (Workload("x", 1, 2, 40, 64, 64, 32, 1, "identity", "f32"), {}),
+    # more cached states than the read keeps weights for at once (128): the gate takes the
+    # max over every logit first and the weights are refreshed in the middle of the read
+    "bf16_C16_150_segments": (Workload("x", 1, 2, 2400, 64, 64, 128, 16, "identity", "bf16"),
+                              {}),
 }
 
 
@@ -82,6 +86,9 @@ SSC_SMALL = {
                                      top_k=2, op="ssc"), {}),
     "bf16_k_ge_N": (Workload("x", 1, 2, 512, 128, 128, 128, 64, "identity", "bf16", top_k=9,
                              op="ssc"), {}),
+    # more candidate segments than the SSC read keeps weights for at once (96)
+    "bf16_C16_120_segments_k5": (Workload("x", 1, 2, 1920, 64, 64, 64, 16, "elu1", "bf16",
+                                          top_k=5, op="ssc"), {}),
 }
 
 
