@@ -382,6 +382,9 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[cb][tb][r] = 0.f;
     uint32_t swz = (uint32_t)(l32 % CPR);  // XOR of a row's 16-byte chunks (row % CPR = l32 % CPR)
+    // phi(q) of the lane's tokens in fp32 (scaled by each state's weight in the state loop):
+    // k = 16 ks + 8 hi32 + e, the B operand's k order
+    float qf[TB][KS][8];
     if (FON) {
         // phi(q) of the lane's tokens as bf16 B fragments: k = 16 ks + 8 hi32 + e
         ru32x4_t qb[TB][KS];
@@ -553,6 +556,17 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
             }
             if (kc + 1 < nkc) store_v(kc + 1);  // its buffer was last read in chunk kc - 1
         }
+        if (PHI == 0) {  // the raw q fragments are phi(q): widen them instead of reloading q
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        qf[tb][ks][2 * e] = __uint_as_float(qb[tb][ks][e] << 16);
+                        qf[tb][ks][2 * e + 1] = __uint_as_float(qb[tb][ks][e] & 0xffff0000u);
+                    }
+        }
     } else {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
@@ -569,18 +583,17 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
                 }
             }
     }
-    // phi(q) of the lane's tokens in fp32 (scaled by each state's weight in the loop below):
-    // k = 16 ks + 8 hi32 + e, the B operand's k order
-    float qf[TB][KS][8];
+    if (!(FON && PHI == 0)) {  // else widened from the online term's fragments
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        const bf16_t* qr = Q + ((size_t)bh * L + tok[tb]) * DK + hi32 * 8;
+        for (int tb = 0; tb < TB; ++tb) {
+            const bf16_t* qr = Q + ((size_t)bh * L + tok[tb]) * DK + hi32 * 8;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            float v[8];
-            ld8<bf16_t>(qr, ks * 16, v);
+            for (int ks = 0; ks < KS; ++ks) {
+                float v[8];
+                ld8<bf16_t>(qr, ks * 16, v);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qf[tb][ks][e] = PHI ? feature(v[e], 1) : v[e];
+                for (int e = 0; e < 8; ++e) qf[tb][ks][e] = PHI ? feature(v[e], 1) : v[e];
+            }
         }
     }
     wait_all_and_barrier();  // region A is free for the states
