@@ -15,9 +15,12 @@ static size_t online_ws(const mc_dims& d) {
     return read_mfma_covers(d) ? 0 : align256(sizeof(float) * (size_t)d.B * d.H * d.L * d.d_v);
 }
 
+// prefix sums of X for the MFMA read, then the per-chunk partial sums that form them
+static size_t xps_only(const mc_dims& d) {
+    return align256(sizeof(float) * (size_t)d.B * d.x_heads * d.L * d.d_g);
+}
 static size_t xps_ws(const mc_dims& d) {
-    return read_mfma_covers(d) ? align256(sizeof(float) * (size_t)d.B * d.x_heads * d.L * d.d_g)
-                               : 0;
+    return read_mfma_covers(d) ? xps_only(d) + align256(sizeof(float) * xps_tail_floats(d)) : 0;
 }
 
 GrmWorkspace grm_workspace(const mc_dims& d) {
@@ -145,7 +148,8 @@ mc_status mc_grm_readout(const mc_dims* d, const void* Q, const void* K, const v
         O_on = on;
     }
     const bool mfma = read_mfma_covers(*d);
-    if (mfma && launch_xps(*d, X, xps, stream)) return MC_ERR_HIP;
+    if (mfma && launch_xps(*d, X, xps, (float*)((char*)xps + xps_only(*d)), stream))
+        return MC_ERR_HIP;
     if ((!mfma || gamma) && launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
     if (launch_grm_readout(*d, Q, K, V, U, aon, xps, M, M_lo, P, O_on, Y, gamma, stream))
         return MC_ERR_HIP;
@@ -177,7 +181,8 @@ mc_status mc_ssc_readout(const mc_dims* d, int32_t top_k, const void* Q, const v
         O_on = on;
     }
     const bool mfma = read_mfma_covers(*d);
-    if (mfma && launch_xps(*d, X, xps, stream)) return MC_ERR_HIP;
+    if (mfma && launch_xps(*d, X, xps, (float*)((char*)xps + xps_only(*d)), stream))
+        return MC_ERR_HIP;
     if (!mfma && launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
     if (launch_ssc_select(*d, top_k, U, X, xsum64, idx, stream)) return MC_ERR_HIP;
     if (launch_ssc_readout(*d, top_k, Q, K, V, U, aon, xps, M, M_lo, P, O_on, idx, Y, stream))

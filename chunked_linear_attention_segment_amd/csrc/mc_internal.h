@@ -49,8 +49,10 @@ int launch_scan_online(const mc_dims& d, const void* Q, const void* K, const voi
 
 int launch_aon(const mc_dims& d, const void* X, const void* U, float* a_on, void* stream);
 
-// xps[b, xh, t, :] = sum of X over t's segment from its first token up to t (fp32)
-int launch_xps(const mc_dims& d, const void* X, float* xps, void* stream);
+// xps[b, xh, t, :] = sum of X over t's segment from its first token up to t (fp32); `tails`
+// holds xps_tail_floats(d) floats of per-chunk partial sums
+size_t xps_tail_floats(const mc_dims& d);
+int launch_xps(const mc_dims& d, const void* X, float* xps, float* tails, void* stream);
 
 // true when the bf16 MFMA read kernel handles these sizes (given K and V instead of O_on it
 // forms the online term and the online logit itself); otherwise the generic kernels run and

@@ -114,67 +114,68 @@ int launch_aon(const mc_dims& d, const void* X, const void* U, float* a_on, void
 
 // Segment-causal prefix sums of X in fp32: xps[b, xh, t, e] = sum of X[b, xh, r, e] over r from
 // the first token of t's segment to t (the numerator of the online segment's prefix mean,
-// Memory Caching paper §3.1, Eq. 10).  One workgroup per (segment, b*xh) walks the segment in
-// chunks of 64 tokens; NG groups of d_g threads each scan 64/NG rows of a chunk in registers,
-// and the group totals (LDS) plus the carry of the earlier chunks complete the sums.
-template <typename T, int NG>
+// Memory Caching paper §3.1, Eq. 10).  The sequence is cut into chunks of XCH tokens, one
+// workgroup per (chunk, b*xh) and one thread per column, which scans its column of the chunk
+// in registers and restarts at every segment start.  Two launches:
+//   TAIL = true   tails[chunk, e]: the chunk's sum over its rows in the segment of its last
+//                 row (the whole chunk unless a segment starts inside it)
+//   TAIL = false  the carry of the chunk's first segment (the tails of the earlier chunks that
+//                 segment spans) plus the in-chunk scan, written to xps
+constexpr int XCH = 64;
+
+template <typename T, bool TAIL>
 __global__ __launch_bounds__(256) void xps_kernel(const T* __restrict__ X, int L, int C, int DG,
+                                                  float* __restrict__ tails,
                                                   float* __restrict__ xps) {
-    constexpr int RG = 64 / NG;
-    __shared__ float tot[NG][256];
-    const int s = blockIdx.x;
-    const size_t base = (size_t)blockIdx.y * L * DG;
-    const int t0 = s * C, t1 = min(L, t0 + C);
-    const int e = threadIdx.x % DG, g = threadIdx.x / DG;
-    const bool act = g < NG;
-    float carry = 0.f;
-    for (int c0 = t0; c0 < t1; c0 += 64) {
-        float pre[RG];
-        float run = 0.f;
+    const int c = blockIdx.x, nch = gridDim.x;
+    const size_t bx = blockIdx.y;
+    const int e = threadIdx.x;
+    if (e >= DG) return;  // no barriers below
+    const int c0 = c * XCH, c1 = min(L, c0 + XCH);
+    const T* Xb = X + bx * (size_t)L * DG;
+    float v[XCH];
 #pragma unroll
-        for (int r = 0; r < RG; ++r) {
-            const int t = c0 + g * RG + r;
-            if (act && t < t1) run += ld<T>(X, base + (size_t)t * DG + e);
-            pre[r] = run;
-        }
-        if (act) tot[g][e] = run;
-        __syncthreads();
-        if (act) {
-            float off = carry, all = 0.f;
-#pragma unroll
-            for (int gg = 0; gg < NG; ++gg) {
-                const float v = tot[gg][e];
-                if (gg < g) off += v;
-                all += v;
-            }
-#pragma unroll
-            for (int r = 0; r < RG; ++r) {
-                const int t = c0 + g * RG + r;
-                if (t < t1) xps[base + (size_t)t * DG + e] = pre[r] + off;
-            }
-            carry += all;
-        }
-        __syncthreads();
+    for (int r = 0; r < XCH; ++r) v[r] = c0 + r < c1 ? ld<T>(Xb, (size_t)(c0 + r) * DG + e) : 0.f;
+    float run = 0.f;
+    if (!TAIL) {
+        const int ss = (c0 / C) * C;  // start of the segment of the chunk's first row
+#pragma unroll 16
+        for (int cc = c - 1; cc >= 0 && (cc + 1) * XCH > ss; --cc)
+            run += tails[(bx * nch + cc) * DG + e];
     }
+    float* out = xps + (bx * L + c0) * DG + e;
+#pragma unroll
+    for (int r = 0; r < XCH; ++r) {
+        const int t = c0 + r;
+        if (t < c1) {
+            if (t % C == 0) run = 0.f;
+            run += v[r];
+            if (!TAIL) out[(size_t)r * DG] = run;
+        }
+    }
+    if (TAIL) tails[(bx * nch + c) * DG + e] = run;
 }
 
-int launch_xps(const mc_dims& d, const void* X, float* xps, void* stream) {
+size_t xps_tail_floats(const mc_dims& d) {
+    return (size_t)d.B * d.x_heads * ((d.L + XCH - 1) / XCH) * d.d_g;
+}
+
+int launch_xps(const mc_dims& d, const void* X, float* xps, float* tails, void* stream) {
     hipStream_t st = (hipStream_t)stream;
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
-    const dim3 grid(NS, d.B * d.x_heads);
-#define MC_XPS(T, NG)                                                                          \
-    hipLaunchKernelGGL((xps_kernel<T, NG>), grid, dim3(256), 0, st, (const T*)X, d.L, d.seg_len, \
-                       d.d_g, xps)
+    if (d.d_g > 256) return (int)hipErrorInvalidValue;
+    const dim3 grid((d.L + XCH - 1) / XCH, d.B * d.x_heads);
+    const dim3 block((d.d_g + 63) / 64 * 64);
     if (d.dtype == MC_BF16) {
-        if (d.d_g <= 64) MC_XPS(bf16_t, 4);
-        else if (d.d_g <= 128) MC_XPS(bf16_t, 2);
-        else MC_XPS(bf16_t, 1);
+        hipLaunchKernelGGL((xps_kernel<bf16_t, true>), grid, block, 0, st, (const bf16_t*)X, d.L,
+                           d.seg_len, d.d_g, tails, xps);
+        hipLaunchKernelGGL((xps_kernel<bf16_t, false>), grid, block, 0, st, (const bf16_t*)X, d.L,
+                           d.seg_len, d.d_g, tails, xps);
     } else {
-        if (d.d_g <= 64) MC_XPS(float, 4);
-        else if (d.d_g <= 128) MC_XPS(float, 2);
-        else MC_XPS(float, 1);
+        hipLaunchKernelGGL((xps_kernel<float, true>), grid, block, 0, st, (const float*)X, d.L,
+                           d.seg_len, d.d_g, tails, xps);
+        hipLaunchKernelGGL((xps_kernel<float, false>), grid, block, 0, st, (const float*)X, d.L,
+                           d.seg_len, d.d_g, tails, xps);
     }
-#undef MC_XPS
     return (int)hipGetLastError();
 }
 
