@@ -242,28 +242,36 @@ def run_decode(args, rec, dev):
         M_on0 = di["M_on"].clone()
         xs0 = di["xsum"].clone()
 
-        def dstep():
-            # restore the online state so every timed step does identical work
+        def dstep(u):
+            # the online state is restored before each timed step so every step does identical
+            # work; u=None is the post-training (uniform-weight) read
             cnt = np.array([wd.count_on], np.int32)
             nc = np.array([wd.n_cached], np.int32)
-            mc.mc_decode_step(dd, di["q"], di["k"], di["v"], di["u"], di["x"], di["M_on"],
+            mc.mc_decode_step(dd, di["q"], di["k"], di["v"], u, di["x"], di["M_on"],
                               di["xsum"], cnt, di["M_cache"], di["P_cache"], nc, cap, yd, ws=wsd,
                               stream=stream)
 
-        for _ in range(args.warmup):
-            dstep()
-        torch.cuda.synchronize()
-        dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        def timed(u):
+            for _ in range(args.warmup):
+                di["M_on"].copy_(M_on0)
+                di["xsum"].copy_(xs0)
+                dstep(u)
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(args.steps)]
-        for i in range(args.steps):
-            di["M_on"].copy_(M_on0)
-            di["xsum"].copy_(xs0)
-            dev_ev[i][0].record(stream)
-            dstep()
-            dev_ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        dms = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
+            for i in range(args.steps):
+                di["M_on"].copy_(M_on0)
+                di["xsum"].copy_(xs0)
+                ev[i][0].record(stream)
+                dstep(u)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+        dms = timed(di["u"])
+        ams = timed(None)
         by = decode_bytes(wd.B, wd.H, wd.n_cached, wd.d_k, wd.d_v, wd.d_g, 2)
+        by_avg = by - wd.B * wd.n_cached * wd.d_g * 4  # no means are read
         gbs = by / (dms / 1e3) / 1e9
         rec["decode"] = {"workload": wd.name, "metric": "decode cached-state HBM GB/s",
                          "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(dms, 4),
@@ -272,7 +280,11 @@ def run_decode(args, rec, dev):
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": round(gbs / PEAK_HBM_GBS, 4),
                                       "traffic": load_traffic("decode_step", wd.name),
-                                      "algorithmic_bytes": by}}
+                                      "algorithmic_bytes": by},
+                         "average_read": {"what": "post-training read (u = NULL: uniform weights)",
+                                          "ms_per_step": round(ams, 4),
+                                          "value": round(by_avg / (ams / 1e3) / 1e9, 1),
+                                          "unit": "GB/s"}}
         del di, wsd, yd
         torch.cuda.empty_cache()
 

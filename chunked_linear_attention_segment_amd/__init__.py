@@ -148,7 +148,8 @@ def mc_ssc_readout(dims, top_k, Q, K, V, U, X, M, M_lo, P, O_on, Y, idx, ws=None
 
 def mc_decode_step(dims, q, k, v, u, x, M_on, xsum_on, count_on, M_cache, P_cache, n_cached,
                    n_cap, y, ws=None, stream=None):
-    """count_on and n_cached are one-element int32 numpy arrays, updated in place."""
+    """count_on and n_cached are one-element int32 numpy arrays, updated in place.  u=None
+    reads the plain mean of the memories (memory caching applied after pre-training)."""
     assert isinstance(count_on, np.ndarray) and count_on.dtype == np.int32
     assert isinstance(n_cached, np.ndarray) and n_cached.dtype == np.int32
     w, wb = _ws(ws)

@@ -196,8 +196,8 @@ mc_status mc_decode_step(const mc_dims* d, const void* q, const void* k, const v
                          int32_t n_cap, void* y, void* ws, size_t ws_bytes, void* stream) {
     mc_status st = check_dims(d, false);
     if (st != MC_OK) return st;
-    if (!q || !k || !v || !u || !x || !M_on || !xsum_on || !count_on || !P_cache || !n_cached ||
-        !y)
+    // u may be NULL: uniform weights over the memories (post-training memory caching)
+    if (!q || !k || !v || !x || !M_on || !xsum_on || !count_on || !P_cache || !n_cached || !y)
         return MC_ERR_NULL;
     if (n_cap < 0) return MC_ERR_DIMS;
     if (n_cap > 0 && !M_cache) return MC_ERR_NULL;

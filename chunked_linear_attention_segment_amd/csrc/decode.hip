@@ -6,6 +6,9 @@
 // <u, MeanPooling> of every cached segment and of the online segment (its prefix mean),
 // and y = gamma_on M_on phi(q) + sum_i gamma_i M^(i) phi(q).  When the online segment then
 // holds C tokens its state and mean become cache slot n and the online memory restarts.
+// Without u every logit is 0 and the read is the plain mean of the n + 1 memories: memory
+// caching applied after pre-training (the paper's appendix on the MC variants), which
+// decodes with an average of the cached memories and no learned weights.
 //
 // Two launches on the caller's stream:
 //   decode_read     1 + R workgroups per (b,h).  Workgroup 0 updates the online memory with
@@ -93,7 +96,7 @@ __device__ __forceinline__ void decode_online(const DecodeArgs& a, size_t bh) {
     for (int c = tid; c < DV; c += kDecodeThreads) sv[c] = ld((const T*)a.v, bh * DV + c);
     // online logit: <u, prefix mean of the online segment including the new token>
     float au = 0.f;
-    if (tid < a.DG)
+    if (tid < a.DG && a.u)  // without u every logit is 0: the uniform (post-training) read
         au = ld((const T*)a.u, bh * a.DG + tid) *
              (a.xsum[bx * a.DG + tid] + ld((const T*)a.x, bx * a.DG + tid));
     const float a_on = block_sum256(au, red) / (float)(a.count + 1);  // syncs sk, sq, sv too
@@ -150,7 +153,8 @@ __device__ __forceinline__ void decode_run(const DecodeArgs& a, size_t bh, int r
     const size_t bx = (size_t)b * a.xh + (a.xh == 1 ? 0 : h);
     const int i0 = (r - 1) * a.per, cnt = min(a.n, i0 + a.per) - i0;  // >= 1 by the grid
 
-    for (int e = tid; e < a.DG; e += kDecodeThreads) su[e] = ld((const T*)a.u, bh * a.DG + e);
+    for (int e = tid; e < a.DG; e += kDecodeThreads)
+        su[e] = a.u ? ld((const T*)a.u, bh * a.DG + e) : 0.f;
     const int kc = (tid % CPR) * E;
     float qv[E];
 #pragma unroll
@@ -162,7 +166,8 @@ __device__ __forceinline__ void decode_run(const DecodeArgs& a, size_t bh, int r
         for (int j = g; j < cnt; j += kDecodeThreads / 16) {
             const float* Pi = a.P_cache + (bx * a.n_cap + i0 + j) * a.DG;
             float s = 0.f;
-            for (int e = l; e < a.DG; e += 16) s += su[e] * Pi[e];
+            if (a.u)
+                for (int e = l; e < a.DG; e += 16) s += su[e] * Pi[e];
             s = warp_sum(s, 16);
             if (l == 0) sa[j] = s;
         }

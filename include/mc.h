@@ -161,6 +161,10 @@ mc_status mc_ssc_readout(const mc_dims* dims, int32_t top_k, const void* Q, cons
  *
  *   dims: B, H, d_k, d_v, d_g, seg_len, x_heads, dtype, phi (L is ignored)
  *   q, k [B,H,d_k]; v [B,H,d_v]; u [B,H,d_g]; x [B,x_heads,d_g]: dtype
+ *   u may be NULL: every logit is then 0 and y is the plain mean of the n_cached + 1
+ *            memories -- memory caching applied after pre-training (the paper's appendix on
+ *            the MC variants: decoding averages the cached memories, no learned weights).
+ *            The cache bookkeeping (x sums, means, emission) is unchanged.
  *   M_on     in/out [B,H,d_v,d_k] fp32  online state before / after the token
  *   xsum_on  in/out [B,x_heads,d_g] fp32 sum of x over the online segment
  *   count_on host in/out: tokens in the online segment, 0..C-1 on entry

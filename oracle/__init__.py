@@ -21,8 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mc_oracle.c")
 _LIB = os.path.join(_HERE, "libmc_oracle.so")
 
-GRM, SSC, RESIDUAL, SOUP = 0, 1, 2, 3
-_MODES = {"grm": GRM, "ssc": SSC, "residual": RESIDUAL, "soup": SOUP}
+GRM, SSC, RESIDUAL, SOUP, AVERAGE = 0, 1, 2, 3, 4
+_MODES = {"grm": GRM, "ssc": SSC, "residual": RESIDUAL, "soup": SOUP, "average": AVERAGE}
 
 
 def build(force: bool = False) -> str:

@@ -13,6 +13,9 @@
  *   [EXP]  "给 RNN 装上“会增长的记忆”：解读 Google 的 Memory Caching" (gitcode explainer):
  *          §3.3 Memory Soup, §3.4 Sparse Selective Caching (router score, Top-k, online
  *          memory always kept).
+ *   [MC-A] the appendix of [MC] on the MC variants, its paragraph on memory caching applied
+ *          after pre-training: decoding reads an average of the cached memories, with no
+ *          learned weights.
  *
  * Readings of points the pages leave open:
  *   - the memory is the unnormalised linear-attention state ([MC] §2, the Miras remark that
@@ -41,7 +44,7 @@
 #include <omp.h>
 #endif
 
-enum { MCO_GRM = 0, MCO_SSC = 1, MCO_RESIDUAL = 2, MCO_SOUP = 3 };
+enum { MCO_GRM = 0, MCO_SSC = 1, MCO_RESIDUAL = 2, MCO_SOUP = 3, MCO_AVERAGE = 4 };
 enum { MCO_OK = 0, MCO_EARG = 1, MCO_ENOMEM = 2 };
 
 /* phi of [MC] Eq. (2): identity, or elu(z)+1 = z+1 for z>0, e^z otherwise. */
@@ -265,7 +268,8 @@ int mco_prefill(const int32_t* dims, int mode, int top_k,
  * In/out: M_on [B,H,dv,dk], xsum [B,xh,dg], *count (tokens already in the online segment,
  * 0..C-1 on entry), M_cache [B,H,n_cap,dv,dk], P_cache [B,xh,n_cap,dg], *n_cached.
  * Out: y [B,H,dv]; gamma (nullable) [B,H,n_cap+1] (entry n_cap is the online weight).
- * mode: MCO_GRM or MCO_RESIDUAL.
+ * mode: MCO_GRM, MCO_RESIDUAL or MCO_AVERAGE ([MC-A]: every one of the n + 1 memories
+ * weighs 1 / (n + 1); u is not read).
  */
 int mco_decode_step(const int32_t* dims, int mode, const double* q, const double* k,
                     const double* v, const double* u, const double* x, double* M_on,
@@ -275,7 +279,7 @@ int mco_decode_step(const int32_t* dims, int mode, const double* q, const double
     const int C = dims[5], xh = dims[6], phi = dims[7];
     if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0 || dg <= 0 || C <= 0) return MCO_EARG;
     if (!(xh == 1 || xh == H)) return MCO_EARG;
-    if (!(mode == MCO_GRM || mode == MCO_RESIDUAL)) return MCO_EARG;
+    if (!(mode == MCO_GRM || mode == MCO_RESIDUAL || mode == MCO_AVERAGE)) return MCO_EARG;
     const int cnt = *count, n = *n_cached;
     if (cnt < 0 || cnt >= C || n < 0 || n > n_cap) return MCO_EARG;
     const int emit = (cnt + 1 == C);
@@ -315,6 +319,9 @@ int mco_decode_step(const int32_t* dims, int mode, const double* q, const double
         }
         if (mode == MCO_RESIDUAL) {
             for (int i = 0; i <= n; ++i) g[i] = 1.0;
+        } else if (mode == MCO_AVERAGE) {
+            /* [MC-A]: the plain mean over the n cached memories and the online one */
+            for (int i = 0; i <= n; ++i) g[i] = 1.0 / (double)(n + 1);
         } else {
             double mx = a[0];
             for (int i = 1; i <= n; ++i) mx = fmax(mx, a[i]);

@@ -210,6 +210,46 @@ def test_decode_step_small(dtype, phi, n, cnt, C, dk, dv):
         st.M_cache = to_np(dev["M_cache"]).copy()
 
 
+@pytest.mark.parametrize("dtype,n,cnt,C", [("bf16", 37, 5, 8), ("f32", 0, 3, 8),
+                                            ("bf16", 9, 14, 16)])
+def test_decode_average_small(dtype, n, cnt, C):
+    """Post-training decode (u = NULL): the plain mean of the memories, several steps in a
+    row across a segment boundary, against the oracle's average mode."""
+    w = Workload("x", 2, 3, 1, 128, 128, 128, C, "identity", dtype, op="decode")
+    cap = n + 3
+    inp, d = _decode_case(w, 2, 3, n, cnt, cap, seed=31)
+    dev = _gpu_decode_state(inp, dtype)
+    st = oracle.DecodeState(inp["M_on"], inp["xsum"], cnt, inp["M_cache"], inp["P_cache"], n)
+    count = np.array([cnt], np.int32)
+    ncached = np.array([n], np.int32)
+    ws = mc.workspace(d, mc.MC_OP_DECODE, n_cap=cap)
+    for step in range(C - cnt + 1):
+        announce("decode average %s n=%d step %d" % (dtype, int(ncached[0]), step))
+        if step > 0:
+            rng = np.random.default_rng(200 + step)
+            for key in ("q", "k", "v", "x"):
+                arr = rng.standard_normal(inp[key].shape).astype(np.float32)
+                if dtype == "bf16":
+                    from chunked_linear_attention_segment_amd.inputs import round_bf16
+                    arr = round_bf16(arr)
+                inp[key] = arr
+                dev[key] = to_dev(arr, dtype)
+        y = torch.empty((2, 3, 128), dtype=mc.torch_dtype(d), device="cuda")
+        mc.mc_decode_step(d, dev["q"], dev["k"], dev["v"], None, dev["x"], dev["M_on"],
+                          dev["xsum"], count, dev["M_cache"], dev["P_cache"], ncached, cap, y,
+                          ws=ws)
+        torch.cuda.synchronize()
+        yref = oracle.decode_step(st, inp["q"], inp["k"], inp["v"], inp["u"], inp["x"],
+                                  seg_len=C, mode="average")
+        assert int(count[0]) == int(st.count[0]) and int(ncached[0]) == int(st.n_cached[0])
+        assert slice_rel_err(to_np(y), yref) <= TOL[dtype]
+        nn = int(ncached[0])
+        if nn:
+            assert slice_rel_err(to_np(dev["P_cache"])[:, :, :nn], st.P_cache[:, :, :nn],
+                                 lead=3) <= 1e-5
+        st.M_cache = to_np(dev["M_cache"]).copy()
+
+
 def test_prefill_then_decode_matches_longer_prefill():
     """Prefill L tokens, hand the trailing partial segment to decode, step one token:
     equals row L of a prefill over L+1 tokens (bf16, identity)."""

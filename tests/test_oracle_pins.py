@@ -16,6 +16,7 @@ an off-by-one segment, the wrong pool) fails at least one of them:
   soup              Memory Soup equals GRM for linear memory
   invariants        simplex gate, linearity in V, head independence, causality
   decode            prefill(L) + one decode step == last row of prefill(L+1)
+  decode, average   LA read / (number of memories); equals the gated step with u = 0
 """
 import json
 import math
@@ -328,3 +329,40 @@ def test_decode_residual_is_linear_attention_read():
     total = Mc[:, :, :n].sum(2) + st.M_on + v[..., :, None] * k[..., None, :]
     y = oracle.decode_step(st, q, k, v, u, x, seg_len=C, mode="residual")
     np.testing.assert_allclose(y, np.einsum("bhcr,bhr->bhc", total, q), rtol=1e-12)
+
+
+@pytest.mark.parametrize("L,C", [(20, 8), (23, 8), (15, 8)])
+def test_decode_average_is_linear_attention_over_memory_count(L, C):
+    """Post-training decode (uniform weights over the n cached memories and the online one):
+    the memories of a prefilled sequence sum to its full linear-attention state, so the
+    step's output is the attention-form linear-attention read of token L divided by the
+    number of memories; with u = 0 the gated step gives the same weights."""
+    B, H, dk, dv, dg = 2, 2, 4, 3, 5
+    Q, K, V, U, X = _rand(B, H, L + 1, dk, dv, dg, seed=23)
+    pre = oracle.prefill(Q[:, :, :L], K[:, :, :L], V[:, :, :L], U[:, :, :L], X[:, :, :L],
+                         seg_len=C, want_states=True)
+    nfull, cnt = divmod(L, C)
+    cap = nfull + 2
+
+    def state():
+        Mc = np.zeros((B, H, cap, dv, dk))
+        Pc = np.zeros((B, 1, cap, dg))
+        Mc[:, :, :nfull] = pre["M"][:, :, :nfull]
+        Pc[:, :, :nfull] = pre["P"][:, :, :nfull]
+        M_on = pre["M"][:, :, nfull].copy() if cnt else np.zeros((B, H, dv, dk))
+        xsum = (pre["P"][:, :, nfull] * cnt).reshape(B, 1, dg) if cnt else np.zeros((B, 1, dg))
+        return oracle.DecodeState(M_on, xsum, cnt, Mc, Pc, nfull)
+
+    tok = [A[:, :, L] for A in (Q, K, V, U, X)]
+    st = state()
+    y = oracle.decode_step(st, *tok, seg_len=C, mode="average")
+    la = _causal_la(Q, K, V)[:, :, L]
+    np.testing.assert_allclose(y, la / (nfull + 1), rtol=1e-11, atol=1e-12)
+    st0 = state()
+    y0 = oracle.decode_step(st0, tok[0], tok[1], tok[2], np.zeros_like(tok[3]), tok[4],
+                            seg_len=C, mode="grm")
+    np.testing.assert_allclose(y, y0, rtol=1e-12, atol=1e-13)
+    # the cache bookkeeping is that of the gated step
+    np.testing.assert_array_equal(st.n_cached, st0.n_cached)
+    np.testing.assert_allclose(st.M_cache, st0.M_cache, rtol=0, atol=0)
+    np.testing.assert_allclose(st.P_cache, st0.P_cache, rtol=0, atol=0)
