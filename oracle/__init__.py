@@ -45,7 +45,8 @@ def _load():
         lib = ctypes.CDLL(build())
         P = ctypes.c_void_p
         lib.mco_prefill.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P,
-                                    ctypes.c_int64, P, P, P, P, P, P, ctypes.c_int]
+                                    ctypes.c_int64, P, P, P, P, P, P, ctypes.c_int, P,
+                                    ctypes.c_int32]
         lib.mco_prefill.restype = ctypes.c_int
         lib.mco_decode_step.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P,
                                         ctypes.c_int32, P, P]
@@ -69,10 +70,12 @@ def max_threads() -> int:
 
 def prefill(Q, K, V, U, X, seg_len: int, phi: str = "identity", mode: str = "grm",
             top_k: int = 0, rows=None, want_states: bool = False, want_online: bool = False,
-            want_gamma: bool = False, n_threads: int = 0) -> dict:
+            want_gamma: bool = False, n_threads: int = 0, seg_offsets=None) -> dict:
     """Evaluate the MC read for every token (or only ``rows``) of every (b, h).
 
     Q, K [B,H,L,dk]; V [B,H,L,dv]; U [B,H,L,dg]; X [B,xh,L,dg] (xh = 1 or H).
+    Segments have length seg_len, or are [seg_offsets[i], seg_offsets[i+1]) when
+    seg_offsets (0 = o_0 < o_1 < ... < o_N = L) is given (seg_len is then ignored).
     Returns a dict with 'Y' [B,H,n_rows,dv] and, on request, 'M' [B,H,NS,dv,dk],
     'P' [B,xh,NS,dg], 'O_on' [B,H,L,dv], 'gamma' [B,H,n_rows,NS], 'idx' [B,H,n_rows,top_k].
     """
@@ -83,8 +86,14 @@ def prefill(Q, K, V, U, X, seg_len: int, phi: str = "identity", mode: str = "grm
     xh = X.shape[1]
     assert K.shape == Q.shape and V.shape[:3] == (B, H, L) and U.shape[:3] == (B, H, L)
     assert X.shape == (B, xh, L, dg)
-    C = int(seg_len)
-    NS = (L + C - 1) // C
+    off = None
+    if seg_offsets is not None:
+        off = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int32))
+        C = 0
+        NS = off.shape[0] - 1
+    else:
+        C = int(seg_len)
+        NS = (L + C - 1) // C
     if rows is not None:
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
         nr = rows.shape[0]
@@ -101,7 +110,8 @@ def prefill(Q, K, V, U, X, seg_len: int, phi: str = "identity", mode: str = "grm
     I = np.full((B, H, nr, max(top_k, 1)), -1, dtype=np.int32) if m == SSC else None
     rc = _load().mco_prefill(_ptr(dims), m, int(top_k), _ptr(Q), _ptr(K), _ptr(V), _ptr(U),
                              _ptr(X), _ptr(rows), int(nr), _ptr(out["Y"]), _ptr(M), _ptr(P),
-                             _ptr(O), _ptr(G), _ptr(I), int(n_threads))
+                             _ptr(O), _ptr(G), _ptr(I), int(n_threads), _ptr(off),
+                             int(NS if off is not None else 0))
     if rc != 0:
         raise ValueError("mco_prefill failed with code %d" % rc)
     if want_states:
@@ -150,3 +160,15 @@ def decode_step(state: DecodeState, q, k, v, u, x, seg_len: int, phi: str = "ide
     if rc != 0:
         raise ValueError("mco_decode_step failed with code %d" % rc)
     return (y, G) if want_gamma else y
+
+
+def log_segments(L: int) -> list:
+    """Offsets of the logarithmic segmentation of a length-L sequence (gitcode explainer §4.2:
+    L in binary, one segment per non-zero bit, of that power-of-two length, largest first;
+    37 -> 32, 4, 1).  Returns [0, o_1, ..., L]."""
+    assert L >= 1
+    off = [0]
+    for b in range(int(L).bit_length() - 1, -1, -1):
+        if (L >> b) & 1:
+            off.append(off[-1] + (1 << b))
+    return off

@@ -83,10 +83,13 @@ static int mco_topk(const double* score, int n, int k, int* chosen) {
  * ([EXP] §3.3: the gamma-weighted average of the memory matrices is formed first and then
  * read once).
  *
+ * Segments: constant length C, or (off != NULL) the n_seg segments [off[i], off[i+1]) with
+ * off[0] = 0 < off[1] < ... < off[n_seg] = L ([MC] Eq. 4b lets the segment lengths L^(s)
+ * differ); C is then not read.
  * rows: ascending token indices to evaluate (NULL = all L tokens); Y [B,H,n_rows,dv].
  * Optional outputs (NULL to skip):
- *   M_out [B,H,NS,dv,dk]  state of segment i after its last token (NS = ceil(L/C); a
- *                         trailing partial segment stores its state after token L-1)
+ *   M_out [B,H,NS,dv,dk]  state of segment i after its last token (NS = ceil(L/C) or n_seg;
+ *                         a trailing partial segment stores its state after token L-1)
  *   P_out [B,xh,NS,dg]    mean of x over segment i (partial segment: over its tokens)
  *   O_on  [B,H,L,dv]      ungated online read M_t^(s) phi(q_t)  (only with rows == NULL)
  *   gamma [B,H,n_rows,NS] weights of segments 0..s (0 for segments not read)
@@ -96,15 +99,21 @@ int mco_prefill(const int32_t* dims, int mode, int top_k,
                 const double* Q, const double* K, const double* V, const double* U,
                 const double* X, const int32_t* rows, int64_t n_rows,
                 double* Y, double* M_out, double* P_out, double* O_on, double* gamma,
-                int32_t* idx, int n_threads) {
+                int32_t* idx, int n_threads, const int32_t* off, int32_t n_seg) {
     const int B = dims[0], H = dims[1], L = dims[2], dk = dims[3], dv = dims[4], dg = dims[5];
     const int C = dims[6], xh = dims[7], phi = dims[8];
-    if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || dg <= 0 || C <= 0) return MCO_EARG;
+    if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || dg <= 0) return MCO_EARG;
+    if (off == NULL && C <= 0) return MCO_EARG;
+    if (off != NULL) {
+        if (n_seg <= 0 || off[0] != 0 || off[n_seg] != L) return MCO_EARG;
+        for (int i = 0; i < n_seg; ++i)
+            if (off[i + 1] <= off[i]) return MCO_EARG;
+    }
     if (!(xh == 1 || xh == H)) return MCO_EARG;
     if (mode < 0 || mode > 3) return MCO_EARG;
     if (mode == MCO_SSC && top_k <= 0) return MCO_EARG;
     if (rows != NULL && O_on != NULL) return MCO_EARG;
-    const int NS = (L + C - 1) / C;
+    const int NS = off ? n_seg : (L + C - 1) / C;
     const int64_t nr = rows ? n_rows : (int64_t)L;
     if (rows)
         for (int64_t a = 0; a < nr; ++a)
@@ -143,8 +152,16 @@ int mco_prefill(const int32_t* dims, int mode, int top_k,
             err = MCO_ENOMEM;
         } else {
             int64_t next = 0; /* position in rows */
+            int s = 0;        /* segment of t */
             for (int t = 0; t < L; ++t) {
-                const int s = t / C, j = t % C;
+                if (off) {
+                    while (t >= off[s + 1]) ++s;
+                } else {
+                    s = t / C;
+                }
+                const int s0 = off ? off[s] : s * C;                    /* its first token */
+                const int s1 = off ? off[s + 1] : (s + 1 < NS ? (s + 1) * C : L); /* one past */
+                const int j = t - s0;
                 if (j == 0) { /* a new segment starts from the zero memory ([MC] Eq. 4b) */
                     memset(Mon, 0, sizeof(double) * dv * dk);
                     memset(xs, 0, sizeof(double) * dg);
@@ -242,7 +259,7 @@ int mco_prefill(const int32_t* dims, int mode, int top_k,
                     if (!want_all) ++next;
                 }
                 /* segment end (or end of input): cache the last state and the segment mean */
-                if (j == C - 1 || t == L - 1) {
+                if (t == s1 - 1 || t == L - 1) {
                     memcpy(Mc + (size_t)s * dv * dk, Mon, sizeof(double) * dv * dk);
                     for (int e = 0; e < dg; ++e) Pc[(size_t)s * dg + e] = xs[e] / (double)(j + 1);
                 }

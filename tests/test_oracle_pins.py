@@ -17,6 +17,8 @@ an off-by-one segment, the wrong pool) fails at least one of them:
   invariants        simplex gate, linearity in V, head independence, causality
   decode            prefill(L) + one decode step == last row of prefill(L+1)
   decode, average   LA read / (number of memories); equals the gated step with u = 0
+  variable segments brute force with arbitrary boundaries; multiples of C equal the
+                    constant-length path; log segmentation of 37 is 32, 4, 1 (the pages' example)
 """
 import json
 import math
@@ -112,21 +114,25 @@ def test_ssc_with_all_segments_equals_grm(C, k):
         assert not np.allclose(ssc["Y"], grm["Y"])
 
 
-def _brute(Q, K, V, U, X, C, phi="identity", mode="grm", top_k=0):
-    """Token-pair evaluation with no states: y_t = sum_{r<=t} w_{t,seg(r)} (q_t.k_r) v_r."""
+def _brute(Q, K, V, U, X, C, phi="identity", mode="grm", top_k=0, off=None):
+    """Token-pair evaluation with no states: y_t = sum_{r<=t} w_{t,seg(r)} (q_t.k_r) v_r.
+    Segments have length C, or are [off[i], off[i+1]) when off is given."""
     B, H, L, _ = Q.shape
     xh = X.shape[1]
     qh, kh = _phi(Q, phi), _phi(K, phi)
+    if off is None:
+        off = list(range(0, L, C)) + [L]
+    seg = np.searchsorted(np.asarray(off), np.arange(L), side="right") - 1
     Y = np.zeros(V.shape)
     IDX = []
     for b in range(B):
         for h in range(H):
             x = X[b, 0 if xh == 1 else h]
-            means = [x[i * C:(i + 1) * C].mean(axis=0) for i in range((L + C - 1) // C)]
+            means = [x[off[i]:off[i + 1]].mean(axis=0) for i in range(len(off) - 1)]
             for t in range(L):
-                s, j = divmod(t, C)
+                s = int(seg[t])
                 scores = [float(U[b, h, t] @ means[i]) for i in range(s)]
-                online = float(U[b, h, t] @ x[s * C:t + 1].mean(axis=0))
+                online = float(U[b, h, t] @ x[off[s]:t + 1].mean(axis=0))
                 if mode == "ssc":
                     order = sorted(range(s), key=lambda i: (-scores[i], i))
                     chosen = sorted(order[:top_k])
@@ -137,7 +143,7 @@ def _brute(Q, K, V, U, X, C, phi="identity", mode="grm", top_k=0):
                 w = torch.softmax(torch.tensor(logits, dtype=torch.float64), 0).numpy()
                 weight = dict(zip(chosen + [s], w))
                 for r in range(t + 1):
-                    g = weight.get(r // C, 0.0)
+                    g = weight.get(int(seg[r]), 0.0)
                     Y[b, h, t] += g * float(qh[b, h, t] @ kh[b, h, r]) * V[b, h, r]
     return Y, IDX
 
@@ -366,3 +372,50 @@ def test_decode_average_is_linear_attention_over_memory_count(L, C):
     np.testing.assert_array_equal(st.n_cached, st0.n_cached)
     np.testing.assert_allclose(st.M_cache, st0.M_cache, rtol=0, atol=0)
     np.testing.assert_allclose(st.P_cache, st0.P_cache, rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("off,phi,xh", [([0, 3, 4, 11, 20, 29], "identity", 1),
+                                        ([0, 1, 2, 3, 13, 14, 29], "elu1", 2),
+                                        ([0, 29], "identity", 1)])
+def test_brute_force_variable_segments(off, phi, xh):
+    L = off[-1]
+    Q, K, V, U, X = _rand(1, 2, L, 4, 3, 5, xh=xh, seed=41, scale_u=2.0)
+    out = oracle.prefill(Q, K, V, U, X, seg_len=0, phi=phi, mode="grm", seg_offsets=off,
+                         want_states=True)
+    Yb, _ = _brute(Q, K, V, U, X, 0, phi, off=off)
+    np.testing.assert_allclose(out["Y"], Yb, rtol=1e-11, atol=1e-11)
+    # states and means are the per-segment sums and means
+    x = X[:, :, :, :]
+    for i in range(len(off) - 1):
+        a, b_ = off[i], off[i + 1]
+        kh = _phi(K[:, :, a:b_], phi)
+        np.testing.assert_allclose(out["M"][:, :, i],
+                                   np.einsum("bhtc,bhtr->bhcr", V[:, :, a:b_], kh), rtol=1e-12)
+        np.testing.assert_allclose(out["P"][:, :, i], x[:, :, a:b_].mean(axis=2), rtol=1e-12)
+    ssc = oracle.prefill(Q, K, V, U, X, seg_len=0, phi=phi, mode="ssc", top_k=2, seg_offsets=off)
+    Ys, Is = _brute(Q, K, V, U, X, 0, phi, mode="ssc", top_k=2, off=off)
+    np.testing.assert_allclose(ssc["Y"], Ys, rtol=1e-11, atol=1e-11)
+    np.testing.assert_array_equal(ssc["idx"].reshape(-1, 2), np.array(Is))
+
+
+@pytest.mark.parametrize("L,C", [(64, 8), (37, 5)])
+def test_offsets_at_multiples_of_C_equal_constant_segments(L, C):
+    Q, K, V, U, X = _rand(2, 2, L, 4, 3, 5, seed=42)
+    off = list(range(0, L, C)) + [L]
+    a = oracle.prefill(Q, K, V, U, X, seg_len=C, want_states=True, want_gamma=True,
+                       want_online=True)
+    b = oracle.prefill(Q, K, V, U, X, seg_len=0, seg_offsets=off, want_states=True,
+                       want_gamma=True, want_online=True)
+    for key in ("Y", "M", "P", "gamma", "O_on"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_log_segments_worked_example():
+    fix = json.load(open(os.path.join(GOLD, "log_segments_worked_example.json")))
+    for case in fix["cases"]:
+        assert oracle.log_segments(case["L"]) == case["offsets"]
+    for L in range(1, 300):
+        off = oracle.log_segments(L)
+        lens = np.diff(off)
+        assert off[0] == 0 and off[-1] == L and len(lens) == bin(L).count("1")
+        assert all(int(n) & (int(n) - 1) == 0 for n in lens) and list(lens) == sorted(lens)[::-1]
