@@ -22,7 +22,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "scan.hip", "readout.hip", "decode.hip", "read_mfma.hip", "scan_mfma.hip"]
+SOURCES = ["abi.cpp", "scan.hip", "readout.hip", "decode.hip", "read_mfma.hip", "scan_mfma.hip",
+           "gate.hip"]
 PEAK_SOURCES = ["peak.hip"]
 # Per-file flags.  The gated read is written in the exact issue order it needs (each MFMA
 # followed by the VALU work of the next k-step, LDS reads two k-steps ahead); the machine

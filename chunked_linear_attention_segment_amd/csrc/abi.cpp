@@ -23,12 +23,28 @@ static size_t xps_ws(const mc_dims& d) {
     return read_mfma_covers(d) ? xps_only(d) + align256(sizeof(float) * xps_tail_floats(d)) : 0;
 }
 
+static size_t gate_w_bytes(const mc_dims& d) {
+    const size_t T = ((size_t)d.L + kGateTile - 1) / kGateTile;
+    return sizeof(uint16_t) * (size_t)d.B * d.H * T * num_segments(d) * kGateTile;
+}
+
+bool gate_pass(const mc_dims& d) {
+    return read_mfma_covers(d) && d.d_k == 128 && d.d_v == 128 &&
+           gate_w_bytes(d) <= kGateMaxBytes;
+}
+
 GrmWorkspace grm_workspace(const mc_dims& d) {
     GrmWorkspace w{};
     w.aon = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
     w.on = online_ws(d);
     w.xps = xps_ws(d);
-    w.total = w.aon + w.on + w.xps;
+    if (gate_pass(d)) {
+        w.w = align256(gate_w_bytes(d));
+        w.won = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
+        w.inv_l = w.won;
+        w.pf = align256(gate_pfrag_bytes(d));
+    }
+    w.total = w.aon + w.on + w.xps + w.w + w.won + w.inv_l + w.pf;
     return w;
 }
 
@@ -151,7 +167,19 @@ mc_status mc_grm_readout(const mc_dims* d, const void* Q, const void* K, const v
     if (mfma && launch_xps(*d, X, xps, (float*)((char*)xps + xps_only(*d)), stream))
         return MC_ERR_HIP;
     if ((!mfma || gamma) && launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
-    if (launch_grm_readout(*d, Q, K, V, U, aon, xps, M, M_lo, P, O_on, Y, gamma, stream))
+    GateWeights gw;
+    if (gate_pass(*d)) {  // the gate as its own pass; the read loads its numerators
+        char* g = (char*)ws + w.aon + w.on + w.xps;
+        uint16_t* W = (uint16_t*)g;
+        float* won = (float*)(g + w.w);
+        float* inv_l = (float*)(g + w.w + w.won);
+        void* pf = g + w.w + w.won + w.inv_l;
+        if (launch_gate_w(*d, U, xps, P, pf, W, won, inv_l, stream)) return MC_ERR_HIP;
+        gw.W = W;
+        gw.won = won;
+        gw.inv_l = inv_l;
+    }
+    if (launch_grm_readout(*d, Q, K, V, U, aon, xps, M, M_lo, P, O_on, gw, Y, gamma, stream))
         return MC_ERR_HIP;
     return MC_OK;
 }

@@ -13,8 +13,27 @@ struct GrmWorkspace {
     size_t aon;   // fp32 [B,H,L]: online gate logit <u_t, prefix mean of X> (generic kernels)
     size_t on;    // fp32 [B,H,L,dv]: online read, for the generic kernels when O_on is NULL
     size_t xps;   // fp32 [B,xh,L,dg]: segment-causal prefix sums of X (MFMA read)
+    size_t w;     // bf16 [B,H,T,NS,kGateTile]: gate numerators per read tile (gate pass)
+    size_t won;   // fp32 [B,H,L]: online weight exp(a_on - m) (gate pass)
+    size_t inv_l; // fp32 [B,H,L]: 1 / softmax denominator (gate pass)
+    size_t pf;    // the means as MFMA fragments (gate pass)
     size_t total;
 };
+
+// The gate pass (gate.hip) writes the softmax numerators per read tile of kGateTile tokens;
+// the gated read then only loads them.  Used for d_k = d_v = 128 bf16 GRM while the
+// numerators fit kGateMaxBytes (longer sequences keep the gate inside the read).
+constexpr int kGateTile = 256;
+constexpr size_t kGateMaxBytes = size_t(4) << 30;
+bool gate_pass(const mc_dims& d);
+struct GateWeights {
+    const uint16_t* W = nullptr;   // null: the read computes the gate itself
+    const float* won = nullptr;
+    const float* inv_l = nullptr;
+};
+size_t gate_pfrag_bytes(const mc_dims& d);  // the means as MFMA fragments (bf16 high + rest)
+int launch_gate_w(const mc_dims& d, const void* U, const float* xps, const float* P,
+                  void* pfrag, uint16_t* W, float* won, float* inv_l, void* stream);
 struct SscWorkspace {
     size_t aon;    // fp32 [B,H,L] (generic kernels)
     size_t on;     // fp32 [B,H,L,dv] (generic kernels only)
@@ -63,13 +82,13 @@ bool read_mfma_covers(const mc_dims& d);
 // and the optional gamma output use a_on (launch_aon).
 int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* K,
                      const void* V, const void* U, const float* xps, const uint16_t* M_lo,
-                     const float* P, const float* O_on, const int32_t* idx, void* Y,
-                     void* stream);
+                     const float* P, const float* O_on, const int32_t* idx,
+                     const GateWeights& gw, void* Y, void* stream);
 
 int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const void* V,
                        const void* U, const float* aon, const float* xps, const float* M,
-                       const uint16_t* M_lo, const float* P, const float* O_on, void* Y,
-                       float* gamma, void* stream);
+                       const uint16_t* M_lo, const float* P, const float* O_on,
+                       const GateWeights& gw, void* Y, float* gamma, void* stream);
 
 int launch_ssc_select(const mc_dims& d, int top_k, const void* U, const void* X,
                       double* xsum64, int32_t* idx, void* stream);

@@ -112,13 +112,16 @@ __device__ __forceinline__ void tile_of_block(int bid, int BH, int T, int& bh, i
     }
 }
 
-template <int DK, int DV, bool SSC, bool FON, int PHI>
+template <int DK, int DV, bool SSC, bool FON, int PHI, bool PRE>
 __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ U, const float* __restrict__ xps, const bf16_t* __restrict__ S,
     const float* __restrict__ P, const float* __restrict__ O_on,
-    const int32_t* __restrict__ idx, int top_k, int BH, int H, int L, int C, int NS, int DG,
-    int xh, bf16_t* __restrict__ Y) {
+    const int32_t* __restrict__ idx, const bf16_t* __restrict__ Wg,
+    const float* __restrict__ won_g, const float* __restrict__ inv_l_g, int top_k, int BH,
+    int H, int L, int C, int NS, int DG, int xh, bf16_t* __restrict__ Y) {
+    static_assert(!(PRE && SSC), "precomputed weights are a GRM mode");
+    static_assert(RT == kGateTile, "the gate pass writes weights per read tile");
     constexpr int KS = DK / 16;  // MFMA k-steps over d_k
     constexpr int CB = DV / 32;  // 32-row blocks of the value dimension
     constexpr int TB = 2;        // 32-token blocks per wave
@@ -169,10 +172,11 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
                     ub[tb][kc] = *reinterpret_cast<const ru32x4_t*>(
                         U + ((size_t)bh * L + tok[tb]) * DG + kc * 16 + hi32 * 8);
     };
-    load_u();
+    if constexpr (!PRE) load_u();
     // online logit a_on = <u_t, xps_t> / (j + 1): the lane half hi32 holds the u values
     // 16 kc + 8 hi32 .. + 8 of its U fragments; the halves are summed
     float m[TB], l[TB], won[TB], a_on[TB];
+    if constexpr (!PRE) {
     float4 xv[TB][DG_MAX / 16][2];  // every load issued before the first product
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
@@ -202,6 +206,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
         a_on[tb] = dot / (float)(tok[tb] - seg[tb] * C + 1);
         m[tb] = a_on[tb];
         l[tb] = 0.f;
+    }
     }
 
     // P rows [i0, i0 + n) -> sm.a.pm: row r at r * DG floats, its 16-byte chunk c stored at
@@ -335,9 +340,32 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
         }
     };
 
+    // PRE: the numerators of a super-block of rows, written by the gate pass, -> sm.w by direct
+    // loads (row i of the tile: RT bf16, token order)
+    const bf16_t* Wt = Wg + ((size_t)bh * T + tile) * NS * RT;
+    auto stage_w = [&](int i0, int n) {
+        const int total = n * (RT / 8);
+        for (int p0 = wave * 64; p0 < total; p0 += RTHREADS) {
+            const uint32_t base = (uint32_t)(uintptr_t)&sm.w[0][p0 * 8];
+            if (p0 + lane < total)
+                dma16(Wt, (uint32_t)(((size_t)i0 * RT + (p0 + lane) * 8) * 2),
+                      __builtin_amdgcn_readfirstlane(base));
+        }
+    };
+
     if constexpr (SSC) {
         if (tid < WMAX / 32) sm.any_sel[tid] = 0u;
     }
+    if constexpr (PRE) {
+        // the gate ran as its own pass: its numerators land in sm.w while the online term
+        // runs; per token the online weight and 1/l (kept in l)
+        if (s_hi > 0) stage_w(0, min(s_hi, SBS));
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            won[tb] = won_g[(size_t)bh * L + tok[tb]];
+            l[tb] = inv_l_g[(size_t)bh * L + tok[tb]];
+        }
+    } else {
     if (s_hi > SBS) {
         // more states than one super-block: pass 1 takes m_t over every logit first, so the
         // numerators of every super-block are final when written
@@ -370,6 +398,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) won[tb] = __expf(a_on[tb] - m[tb]);
+    }
 
     __syncthreads();  // the staged means are consumed (region A is free)
 
@@ -632,15 +661,21 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
             wait_all_and_barrier();
         if (i + 2 < s_hi) stage(i + 2, buf == 0 ? NBUF - 1 : buf - 1);
         if (il == 0 && i > 0) {  // next super-block of weights (means read from P directly)
-            if constexpr (SSC) {
-                if (tid < WMAX / 32) sm.any_sel[tid] = 0u;
+            if constexpr (PRE) {
+                __syncthreads();
+                stage_w(i, min(SBS, s_hi - i));
+                wait_all_and_barrier();
+            } else {
+                if constexpr (SSC) {
+                    if (tid < WMAX / 32) sm.any_sel[tid] = 0u;
+                }
+                load_u();
+                __syncthreads();
+                weights(i, false, false);
+                __syncthreads();
             }
-            load_u();
-            __syncthreads();
-            weights(i, false, false);
-            __syncthreads();
         }
-        if ((il & 31) == 0) {  // entering block il / 32 of the super-block: its correction
+        if (!PRE && (il & 31) == 0) {  // entering block il / 32 of the super-block: its correction
             const int bi = il >> 5;
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
@@ -655,7 +690,8 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
         }
         float w[TB];
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) w[tb] = bf16_to_f32(sm.w[il][tl[tb]]) * cf[tb];
+        for (int tb = 0; tb < TB; ++tb)
+            w[tb] = PRE ? bf16_to_f32(sm.w[il][tl[tb]]) : bf16_to_f32(sm.w[il][tl[tb]]) * cf[tb];
         const bf16_t* st = sm.a.state[buf];
         // software pipeline in issue order: A fragments two k-steps ahead (three register
         // sets); each MFMA of k-step ks is followed by the three VALU ops that build a quarter
@@ -698,7 +734,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
         if (!val[tb]) continue;
-        const float il = 1.f / (l[tb] + won[tb]);
+        const float il = PRE ? l[tb] : 1.f / (l[tb] + won[tb]);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             bf16_t* yr = Y + ((size_t)bh * L + tok[tb]) * DV + cb * 32 + hi32 * 4;
@@ -713,31 +749,35 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     }
 }
 
-template <int DK, int DV, bool SSC, bool FON, int PHI>
+template <int DK, int DV, bool SSC, bool FON, int PHI, bool PRE>
 void launch_k(const mc_dims& d, int top_k, const void* Q, const void* K, const void* V,
               const void* U, const float* xps, const uint16_t* M_lo, const float* P,
-              const float* O_on, const int32_t* idx, void* Y, hipStream_t st) {
+              const float* O_on, const int32_t* idx, const GateWeights& gw, void* Y,
+              hipStream_t st) {
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     const int T = (d.L + RT - 1) / RT;
     const int BH = d.B * d.H;
-    hipLaunchKernelGGL((grm_read_kernel<DK, DV, SSC, FON, PHI>), dim3(BH * T), dim3(RTHREADS), 0,
-                       st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V,
-                       (const bf16_t*)U, xps, (const bf16_t*)M_lo, P, O_on, idx, top_k, BH, d.H,
-                       d.L, d.seg_len, NS, d.d_g, d.x_heads, (bf16_t*)Y);
+    hipLaunchKernelGGL((grm_read_kernel<DK, DV, SSC, FON, PHI, PRE>), dim3(BH * T),
+                       dim3(RTHREADS), 0, st, (const bf16_t*)Q, (const bf16_t*)K,
+                       (const bf16_t*)V, (const bf16_t*)U, xps, (const bf16_t*)M_lo, P, O_on,
+                       idx, (const bf16_t*)gw.W, gw.won, gw.inv_l, top_k, BH, d.H, d.L,
+                       d.seg_len, NS, d.d_g, d.x_heads, (bf16_t*)Y);
 }
 
-template <int DK, int DV, bool SSC>
+template <int DK, int DV, bool SSC, bool PRE>
 int launch_t(const mc_dims& d, int top_k, const void* Q, const void* K, const void* V,
              const void* U, const float* xps, const uint16_t* M_lo, const float* P,
-             const float* O_on, const int32_t* idx, void* Y, hipStream_t st) {
+             const float* O_on, const int32_t* idx, const GateWeights& gw, void* Y,
+             hipStream_t st) {
     // the online term is formed in the kernel (from K and V) when the scan did not write it;
     // the feature map is a template argument so the key fragments' loop has no branches
+#define MC_K(FON, PHI)                                                                         \
+    launch_k<DK, DV, SSC, FON, PHI, PRE>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, gw, Y, st)
     if (O_on)
-        d.phi ? launch_k<DK, DV, SSC, false, 1>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, st)
-              : launch_k<DK, DV, SSC, false, 0>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, st);
+        d.phi ? MC_K(false, 1) : MC_K(false, 0);
     else
-        d.phi ? launch_k<DK, DV, SSC, true, 1>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, st)
-              : launch_k<DK, DV, SSC, true, 0>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, st);
+        d.phi ? MC_K(true, 1) : MC_K(true, 0);
+#undef MC_K
     return (int)hipGetLastError();
 }
 
@@ -751,14 +791,21 @@ bool read_mfma_covers(const mc_dims& d) {
 
 int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* K,
                      const void* V, const void* U, const float* xps, const uint16_t* M_lo,
-                     const float* P, const float* O_on, const int32_t* idx, void* Y,
-                     void* stream) {
+                     const float* P, const float* O_on, const int32_t* idx,
+                     const GateWeights& gw, void* Y, void* stream) {
     if (!read_mfma_covers(d)) return -1;
     hipStream_t st = (hipStream_t)stream;
+    if (gw.W) {  // the gate ran as its own pass (d_k = d_v = 128 GRM)
+        if (ssc || d.d_k != 128 || d.d_v != 128) return -1;
+        return launch_t<128, 128, false, true>(d, 0, Q, K, V, U, xps, M_lo, P, O_on, idx, gw, Y,
+                                               st);
+    }
 #define MC_RD(DK, DV)                                                                          \
     if (d.d_k == DK && d.d_v == DV)                                                            \
-        return ssc ? launch_t<DK, DV, true>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, st) \
-                   : launch_t<DK, DV, false>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, st);
+        return ssc ? launch_t<DK, DV, true, false>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on,    \
+                                                   idx, gw, Y, st)                             \
+                   : launch_t<DK, DV, false, false>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on,  \
+                                                    idx, gw, Y, st);
     MC_RD(128, 128)
     MC_RD(128, 64)
     MC_RD(64, 128)

@@ -351,12 +351,13 @@ __global__ void gamma_kernel(const T* __restrict__ U, const float* __restrict__ 
 
 int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const void* V,
                        const void* U, const float* aon, const float* xps, const float* M,
-                       const uint16_t* M_lo, const float* P, const float* O_on, void* Y,
-                       float* gamma, void* stream) {
+                       const uint16_t* M_lo, const float* P, const float* O_on,
+                       const GateWeights& gw, void* Y, float* gamma, void* stream) {
     if (!read_mfma_covers(d))
         return launch_readout<false>(d, 0, Q, U, aon, M, M_lo, P, O_on, nullptr, Y, gamma,
                                      (hipStream_t)stream);
-    int rc = launch_read_mfma(d, false, 0, Q, K, V, U, xps, M_lo, P, O_on, nullptr, Y, stream);
+    int rc = launch_read_mfma(d, false, 0, Q, K, V, U, xps, M_lo, P, O_on, nullptr, gw, Y,
+                              stream);
     if (rc || !gamma) return rc;
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     hipLaunchKernelGGL(gamma_kernel<bf16_t>, dim3((d.L + 63) / 64, d.B * d.H), dim3(64), 0,
@@ -371,7 +372,8 @@ int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K
                        const uint16_t* M_lo, const float* P, const float* O_on,
                        const int32_t* idx, void* Y, void* stream) {
     if (read_mfma_covers(d))
-        return launch_read_mfma(d, true, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, Y, stream);
+        return launch_read_mfma(d, true, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx,
+                                GateWeights{}, Y, stream);
     return launch_readout<true>(d, top_k, Q, U, aon, M, M_lo, P, O_on, idx, Y, nullptr,
                                 (hipStream_t)stream);
 }

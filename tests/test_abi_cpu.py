@@ -116,13 +116,23 @@ def test_read_workspace_regions():
     assert bf >= aon + 4 * B * xh * L * dg
     for gen in (dims(dtype="f32"), dims(d_g=24), dims(d_g=256)):
         assert mc.mc_workspace_bytes(gen, mc.MC_OP_GRM) >= aon + 4 * B * H * L * dv
+    # d_k = d_v = 128: the gate runs as its own pass and writes its softmax numerators per
+    # read tile of 256 tokens (bf16 [B,H,tiles,NS,256]) plus the online weight and 1/l per token
+    g = dims(d_k=128, d_v=128)
+    NS, T = -(-g.L // g.seg_len), -(-g.L // 256)
+    assert mc.mc_workspace_bytes(g, mc.MC_OP_GRM) >= (
+        4 * g.B * g.H * g.L + 4 * g.B * g.x_heads * g.L * g.d_g
+        + 2 * g.B * g.H * T * NS * 256 + 8 * g.B * g.H * g.L)
 
 
 def test_ssc_arguments():
     d = dims()
     lib = mc.load()
     need = mc.mc_workspace_bytes(d, mc.MC_OP_SSC, 4)
-    assert need > mc.mc_workspace_bytes(d, mc.MC_OP_GRM)
+    # the SSC read adds fp64 segment sums of X to the prefix sums (its gate stays in the read)
+    B, L, xh, dg = d.B, d.L, d.x_heads, d.d_g
+    NS = -(-L // d.seg_len)
+    assert need >= 4 * B * xh * L * dg + 8 * B * xh * NS * dg
 
     def call(k, ws_bytes, idx=A):
         return lib.mc_ssc_readout(ctypes.byref(d), k, A, A, A, A, A, A, A, A, A, A, idx, A,
