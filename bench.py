@@ -28,17 +28,21 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MC-GRM prefill tokens/s (L=64K,H=32,d=128); decode cached-state HBM GB/s"
 
 
-def readout_flops(B, H, L, C, dk, dv, dg):
+def readout_flops(B, H, L, C, dk, dv, dg, online=True):
     """Algorithmic FLOPs of the GRM read of one prefill: per (b,h), every token of segment s
-    reads s cached states (2*dk*dv each) and forms s+1 gate logits (2*dg each)."""
+    reads s cached states (2*dk*dv each) and forms s+1 gate logits (2*dg each); when the read
+    also forms the online term (online=True: O_on = NULL), each token adds 2*(dk+dv) per key
+    of its segment up to itself (causal pairs only)."""
     N = -(-L // C)
     read = 0
     gate = 0
+    pairs = 0
     for s in range(N):
         n_tok = min(C, L - s * C)
         read += n_tok * s * 2 * dk * dv
         gate += n_tok * (s + 1) * 2 * dg
-    return B * H * (read + gate)
+        pairs += n_tok * (n_tok + 1) // 2
+    return B * H * (read + gate + (pairs * 2 * (dk + dv) if online else 0))
 
 
 def scan_flops(B, H, L, C, dk, dv):
@@ -169,7 +173,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = B * L / (ms_per_step / 1e3)
 
-    fl_read = readout_flops(B, H, L, C, dk, dv, dg)
+    fl_read = readout_flops(B, H, L, C, dk, dv, dg, online=(args.online == "fused"))
     achieved = fl_read / (read_ms / 1e3) / 1e12
     traffic = load_traffic("grm_readout", w.name)
     rec = {

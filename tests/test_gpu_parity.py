@@ -39,6 +39,14 @@ SMALL = {
     # max over every logit first and the weights are refreshed in the middle of the read
     "bf16_C16_150_segments": (Workload("x", 1, 2, 2400, 64, 64, 128, 16, "identity", "bf16"),
                               {}),
+    # d = 128: the 512-token read with the gate pass; many segments per tile, ragged tail,
+    # more cached states than one tile of weights rows, elu+1
+    "bf16_d128_C48_ragged_L700": (Workload("x", 1, 2, 700, 128, 128, 128, 48, "elu1", "bf16"),
+                                  {}),
+    "bf16_d128_C16_150_segments": (Workload("x", 1, 2, 2400, 128, 128, 128, 16, "identity",
+                                            "bf16"), {}),
+    "bf16_d128_C512_L1536_elu": (Workload("x", 2, 3, 1536, 128, 128, 64, 512, "elu1", "bf16"),
+                                 {}),
 }
 
 
