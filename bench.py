@@ -193,7 +193,8 @@ def main():
                    "seg_len": C, "phi": w.phi, "online_read": args.online,
                    "steps_timed": "mc_scan_prefill + mc_grm_readout"},
         "kernels_ms": {"mc_scan_prefill": round(scan_ms, 4), "mc_grm_readout": round(read_ms, 4)},
-        "roofline": {"kernel": "mc_grm_readout (gate + gamma-weighted read)", "bound": "mfma",
+        "roofline": {"kernel": "mc_grm_readout (prefix sums, gate pass, gamma-weighted read)",
+                     "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "algorithmic_flops": fl_read},
