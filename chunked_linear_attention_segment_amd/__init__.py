@@ -7,7 +7,8 @@ no fallback: if the library is missing, loading raises.
 Entry points (same names and arguments as include/mc.h; tensors are torch tensors on the
 GPU, host scalars are Python ints or one-element int32 numpy arrays):
     mc_abi_version, mc_status_str, mc_workspace_bytes,
-    mc_scan_prefill, mc_grm_readout, mc_ssc_readout, mc_decode_step
+    mc_scan_prefill, mc_grm_readout, mc_ssc_readout, mc_decode_step,
+    mc_scan_prefill_segs, mc_grm_readout_segs
 plus helpers that allocate outputs / workspaces with torch (memory plumbing only).
 """
 from __future__ import annotations
@@ -27,7 +28,9 @@ MC_PHI_IDENTITY, MC_PHI_ELU1 = 0, 1
 MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE = 0, 1, 2, 3
 
 EXPORTED = ["mc_abi_version", "mc_status_str", "mc_workspace_bytes", "mc_scan_prefill",
-            "mc_grm_readout", "mc_ssc_readout", "mc_decode_step"]
+            "mc_grm_readout", "mc_ssc_readout", "mc_decode_step", "mc_scan_prefill_segs",
+            "mc_grm_readout_segs"]
+MC_MAX_SEGS = 512
 
 
 class McDims(ctypes.Structure):
@@ -66,6 +69,11 @@ def load(path: str = LIB_PATH):
         lib.mc_ssc_readout.restype = ctypes.c_int
         lib.mc_ssc_readout.argtypes = [D, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P, P,
                                        P, ctypes.c_size_t, P]
+        lib.mc_scan_prefill_segs.restype = ctypes.c_int
+        lib.mc_scan_prefill_segs.argtypes = [D, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P]
+        lib.mc_grm_readout_segs.restype = ctypes.c_int
+        lib.mc_grm_readout_segs.argtypes = [D, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
+                                            ctypes.c_size_t, P]
         lib.mc_decode_step.restype = ctypes.c_int
         lib.mc_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P,
                                        ctypes.c_size_t, P]
@@ -146,6 +154,30 @@ def mc_ssc_readout(dims, top_k, Q, K, V, U, X, M, M_lo, P, O_on, Y, idx, ws=None
            "mc_ssc_readout")
 
 
+def _offsets(seg_off):
+    off = np.ascontiguousarray(np.asarray(seg_off, dtype=np.int32))
+    return off, off.shape[0] - 1
+
+
+def mc_scan_prefill_segs(dims, seg_off, Q, K, V, X, M, M_lo, P, O_on, stream=None):
+    """seg_off: host offsets 0 = o_0 < ... < o_n = L (segment i = [o_i, o_{i+1}))."""
+    off, n = _offsets(seg_off)
+    _check(load().mc_scan_prefill_segs(ctypes.byref(dims), off.ctypes.data, n, _p(Q), _p(K),
+                                       _p(V), _p(X), _p(M), _p(M_lo), _p(P), _p(O_on),
+                                       _stream(stream)),
+           "mc_scan_prefill_segs")
+
+
+def mc_grm_readout_segs(dims, seg_off, Q, U, X, M, M_lo, P, O_on, Y, gamma=None, ws=None,
+                        stream=None):
+    off, n = _offsets(seg_off)
+    w, wb = _ws(ws)
+    _check(load().mc_grm_readout_segs(ctypes.byref(dims), off.ctypes.data, n, _p(Q), _p(U),
+                                      _p(X), _p(M), _p(M_lo), _p(P), _p(O_on), _p(Y),
+                                      _p(gamma), w, wb, _stream(stream)),
+           "mc_grm_readout_segs")
+
+
 def mc_decode_step(dims, q, k, v, u, x, M_on, xsum_on, count_on, M_cache, P_cache, n_cached,
                    n_cap, y, ws=None, stream=None):
     """count_on and n_cached are one-element int32 numpy arrays, updated in place.  u=None
@@ -198,6 +230,28 @@ def prefill_grm(dims, Q, K, V, U, X, want_gamma=False, online=True, stream=None)
                     device=Q.device) if want_gamma else None
     ws = workspace(dims, MC_OP_GRM, device=Q.device)
     mc_grm_readout(dims, Q, K, V, U, X, M, M_lo, P, O_on, Y, G, ws=ws, stream=stream)
+    out = {"Y": Y, "M": M, "M_lo": M_lo, "P": P, "O_on": O_on}
+    if want_gamma:
+        out["gamma"] = G
+    return out
+
+
+def prefill_grm_segs(dims, seg_off, Q, K, V, U, X, want_gamma=False, stream=None):
+    """scan + GRM read over the segments [seg_off[i], seg_off[i+1]) with fresh outputs."""
+    import torch
+    NS = len(seg_off) - 1
+    dev = Q.device
+    M = torch.empty((dims.B, dims.H, NS, dims.d_v, dims.d_k), dtype=torch.float32, device=dev)
+    M_lo = torch.empty((dims.B, dims.H, NS, dims.d_v, dims.d_k), dtype=torch.bfloat16,
+                       device=dev)
+    P = torch.empty((dims.B, dims.x_heads, NS, dims.d_g), dtype=torch.float32, device=dev)
+    O_on = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch.float32, device=dev)
+    mc_scan_prefill_segs(dims, seg_off, Q, K, V, X, M, M_lo, P, O_on, stream=stream)
+    Y = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch_dtype(dims), device=dev)
+    G = torch.empty((dims.B, dims.H, dims.L, NS), dtype=torch.float32,
+                    device=dev) if want_gamma else None
+    ws = workspace(dims, MC_OP_GRM, device=dev)
+    mc_grm_readout_segs(dims, seg_off, Q, U, X, M, M_lo, P, O_on, Y, G, ws=ws, stream=stream)
     out = {"Y": Y, "M": M, "M_lo": M_lo, "P": P, "O_on": O_on}
     if want_gamma:
         out["gamma"] = G

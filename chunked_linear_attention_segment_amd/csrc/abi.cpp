@@ -218,6 +218,56 @@ mc_status mc_ssc_readout(const mc_dims* d, int32_t top_k, const void* Q, const v
     return MC_OK;
 }
 
+// Host checks of a segmentation; fills the by-value kernel argument.
+static mc_status check_segs(const mc_dims* d, const int32_t* off, int32_t n_seg, SegArg* sg) {
+    if (!off) return MC_ERR_NULL;
+    if (n_seg < 1) return MC_ERR_DIMS;
+    if (n_seg > MC_MAX_SEGS) return MC_ERR_UNSUPPORTED;
+    if (off[0] != 0 || off[n_seg] != d->L) return MC_ERR_DIMS;
+    for (int i = 0; i < n_seg; ++i)
+        if (off[i + 1] <= off[i]) return MC_ERR_DIMS;
+    sg->n = n_seg;
+    for (int i = 0; i <= n_seg; ++i) sg->off[i] = off[i];
+    return MC_OK;
+}
+
+mc_status mc_scan_prefill_segs(const mc_dims* d, const int32_t* seg_off, int32_t n_seg,
+                               const void* Q, const void* K, const void* V, const void* X,
+                               float* M, uint16_t* M_lo, float* P, float* O_on, void* stream) {
+    mc_status st = check_dims(d, true);
+    if (st != MC_OK) return st;
+    SegArg sg;
+    if ((st = check_segs(d, seg_off, n_seg, &sg)) != MC_OK) return st;
+    if (!Q || !K || !V || !X || !M || !P) return MC_ERR_NULL;
+    if (d->dtype == MC_BF16 && !M_lo) return MC_ERR_NULL;
+    const void* ptrs[] = {Q, K, V, X, M, M_lo, P, O_on};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MC_ERR_ALIGN;
+    return launch_scan_prefill_segs(*d, sg, Q, K, V, X, M, M_lo, P, O_on, stream) ? MC_ERR_HIP
+                                                                                  : MC_OK;
+}
+
+mc_status mc_grm_readout_segs(const mc_dims* d, const int32_t* seg_off, int32_t n_seg,
+                              const void* Q, const void* U, const void* X, const float* M,
+                              const uint16_t* M_lo, const float* P, const float* O_on, void* Y,
+                              float* gamma, void* ws, size_t ws_bytes, void* stream) {
+    mc_status st = check_dims(d, true);
+    if (st != MC_OK) return st;
+    SegArg sg;
+    if ((st = check_segs(d, seg_off, n_seg, &sg)) != MC_OK) return st;
+    if (!Q || !U || !X || !P || !O_on || !Y) return MC_ERR_NULL;
+    if (d->dtype == MC_BF16 ? !M_lo : !M) return MC_ERR_NULL;
+    const GrmWorkspace w = grm_workspace(*d);
+    if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
+    const void* ptrs[] = {Q, U, X, M, M_lo, P, O_on, Y, gamma, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MC_ERR_ALIGN;
+    return launch_grm_readout_segs(*d, sg, Q, U, X, M, M_lo, P, O_on, (float*)ws, Y, gamma,
+                                   stream)
+               ? MC_ERR_HIP
+               : MC_OK;
+}
+
 mc_status mc_decode_step(const mc_dims* d, const void* q, const void* k, const void* v,
                          const void* u, const void* x, float* M_on, float* xsum_on,
                          int32_t* count_on, void* M_cache, float* P_cache, int32_t* n_cached,

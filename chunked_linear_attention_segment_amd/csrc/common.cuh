@@ -60,6 +60,27 @@ __device__ __forceinline__ float feature(float z, int phi) {
     return phi == 0 ? z : (z > 0.f ? z + 1.f : __expf(z));
 }
 
+// Segment boundaries (SegArg, mc_internal.h): first token and length of segment s, and the
+// segment of token t (the largest s with off[s] <= t); n = 0 is the constant length C.
+template <typename SA>
+__device__ __forceinline__ int seg_first(const SA& sg, int s, int C) {
+    return sg.n ? sg.off[s] : s * C;
+}
+template <typename SA>
+__device__ __forceinline__ int seg_length(const SA& sg, int s, int C, int L) {
+    return sg.n ? sg.off[s + 1] - sg.off[s] : min(C, L - s * C);
+}
+template <typename SA>
+__device__ __forceinline__ int seg_of(const SA& sg, int t, int C) {
+    if (!sg.n) return t / C;
+    int lo = 0, hi = sg.n;  // off[lo] <= t < off[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sg.off[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
 __device__ __forceinline__ float warp_sum(float v, int width) {
     for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, width);
     return v;

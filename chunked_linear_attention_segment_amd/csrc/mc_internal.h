@@ -58,6 +58,20 @@ DecodeWorkspace decode_workspace(const mc_dims& d, int n_cap, int n_cached);
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
+// Segment boundaries for the generic kernels, passed to them by value: n = 0 means constant
+// length C; otherwise segment i is [off[i], off[i+1]) for i < n.
+struct SegArg {
+    int32_t n;
+    int32_t off[MC_MAX_SEGS + 1];
+};
+
+int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
+                             const void* V, const void* X, float* M, uint16_t* M_lo, float* P,
+                             float* O_on, void* stream);
+int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* U,
+                            const void* X, const float* M, const uint16_t* M_lo, const float* P,
+                            const float* O_on, float* aon, void* Y, float* gamma, void* stream);
+
 int launch_scan_prefill(const mc_dims& d, const void* Q, const void* K, const void* V,
                         const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,
                         void* stream);

@@ -23,11 +23,11 @@ template <typename T>
 __global__ __launch_bounds__(256) void aon_kernel(const T* __restrict__ X,
                                                   const T* __restrict__ U, int L, int C,
                                                   int DG, int H, int xh,
-                                                  float* __restrict__ a_on) {
+                                                  float* __restrict__ a_on, const SegArg sg) {
     __shared__ float xs[64][260];
     __shared__ float carry[256];
     const int s = blockIdx.x, b = blockIdx.y, h0 = blockIdx.z * 4;
-    const int t0 = s * C, len = min(C, L - t0);
+    const int t0 = seg_first(sg, s, C), len = seg_length(sg, s, C, L);
     const int tid = threadIdx.x;
     const int q = tid & 15, slot = tid >> 4;  // 16 lanes per dot product, 16 dots at a time
     const int nh = min(4, H - h0);
@@ -99,17 +99,23 @@ __global__ __launch_bounds__(256) void aon_kernel(const T* __restrict__ X,
     }
 }
 
-int launch_aon(const mc_dims& d, const void* X, const void* U, float* a_on, void* stream) {
-    hipStream_t st = (hipStream_t)stream;
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+static int launch_aon_sg(const mc_dims& d, const void* X, const void* U, float* a_on,
+                         const SegArg& sg, hipStream_t st) {
+    const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
     dim3 grid(NS, d.B, (d.H + 3) / 4);
     if (d.dtype == MC_BF16)
         hipLaunchKernelGGL(aon_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)X,
-                           (const bf16_t*)U, d.L, d.seg_len, d.d_g, d.H, d.x_heads, a_on);
+                           (const bf16_t*)U, d.L, d.seg_len, d.d_g, d.H, d.x_heads, a_on, sg);
     else
         hipLaunchKernelGGL(aon_kernel<float>, grid, dim3(256), 0, st, (const float*)X,
-                           (const float*)U, d.L, d.seg_len, d.d_g, d.H, d.x_heads, a_on);
+                           (const float*)U, d.L, d.seg_len, d.d_g, d.H, d.x_heads, a_on, sg);
     return (int)hipGetLastError();
+}
+
+static const SegArg kConstSegR{};  // constant segment length
+
+int launch_aon(const mc_dims& d, const void* X, const void* U, float* a_on, void* stream) {
+    return launch_aon_sg(d, X, U, a_on, kConstSegR, (hipStream_t)stream);
 }
 
 // Segment-causal prefix sums of X in fp32: xps[b, xh, t, e] = sum of X[b, xh, r, e] over r from
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(256) void readout_valu_kernel(
     const T* __restrict__ Q, const T* __restrict__ U, const float* __restrict__ aon,
     const TS* __restrict__ S, const float* __restrict__ P, const float* __restrict__ O_on,
     const int32_t* __restrict__ idx, int top_k, int L, int C, int NS, int DG, int H, int xh,
-    int phi, T* __restrict__ Y, float* __restrict__ gamma) {
+    int phi, T* __restrict__ Y, float* __restrict__ gamma, const SegArg sg) {
     constexpr int TT = 32;
     constexpr int CPT = DV / 8;
     __shared__ float sq[TT][DK];
@@ -203,9 +209,9 @@ __global__ __launch_bounds__(256) void readout_valu_kernel(
     const int t = tile0 + tt;
     const bool valid = t < L;
     const int tc = valid ? t : L - 1;  // clamped token for address formation
-    const int s = tc / C;
+    const int s = seg_of(sg, tc, C);
     const int last = min(L, tile0 + TT) - 1;
-    const int s_hi = last / C;  // largest segment index in this tile
+    const int s_hi = seg_of(sg, last, C);  // largest segment index in this tile
 
     for (int e = tid; e < TT * DK; e += 256) {
         const int r = e % DK, tk = min(tile0 + e / DK, L - 1);
@@ -288,12 +294,12 @@ template <typename T, typename TS, int DK, int DV, bool SSC>
 static int launch_readout_t(const mc_dims& d, int top_k, const void* Q, const void* U,
                             const float* aon, const void* S, const float* P,
                             const float* O_on, const int32_t* idx, void* Y, float* gamma,
-                            hipStream_t st) {
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+                            hipStream_t st, const SegArg& sg = kConstSegR) {
+    const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
     dim3 grid((d.L + 31) / 32, d.B * d.H);
     hipLaunchKernelGGL((readout_valu_kernel<T, TS, DK, DV, SSC>), grid, dim3(256), 0, st,
                        (const T*)Q, (const T*)U, aon, (const TS*)S, P, O_on, idx, top_k, d.L,
-                       d.seg_len, NS, d.d_g, d.H, d.x_heads, d.phi, (T*)Y, gamma);
+                       d.seg_len, NS, d.d_g, d.H, d.x_heads, d.phi, (T*)Y, gamma, sg);
     return (int)hipGetLastError();
 }
 
@@ -311,6 +317,31 @@ static int launch_readout(const mc_dims& d, int top_k, const void* Q, const void
                    : launch_readout_t<float, float, DK, DV, SSC>(d, top_k, Q, U, aon, M,  \
                                                                  P, O_on, idx, Y, gamma,   \
                                                                  st);
+    MC_RD(128, 128)
+    MC_RD(128, 64)
+    MC_RD(64, 128)
+    MC_RD(64, 64)
+#undef MC_RD
+    return (int)hipErrorInvalidValue;
+}
+
+// Arbitrary boundaries: online logits, then the generic read with the online term O_on of
+// mc_scan_prefill_segs.
+int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* U,
+                            const void* X, const float* M, const uint16_t* M_lo, const float* P,
+                            const float* O_on, float* aon, void* Y, float* gamma, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    int rc = launch_aon_sg(d, X, U, aon, sg, st);
+    if (rc) return rc;
+#define MC_RD(DK, DV)                                                                      \
+    if (d.d_k == DK && d.d_v == DV)                                                        \
+        return d.dtype == MC_BF16                                                          \
+                   ? launch_readout_t<bf16_t, bf16_t, DK, DV, false>(d, 0, Q, U, aon, M_lo, \
+                                                                     P, O_on, nullptr, Y,  \
+                                                                     gamma, st, sg)        \
+                   : launch_readout_t<float, float, DK, DV, false>(d, 0, Q, U, aon, M, P,  \
+                                                                   O_on, nullptr, Y,       \
+                                                                   gamma, st, sg);
     MC_RD(128, 128)
     MC_RD(128, 64)
     MC_RD(64, 128)

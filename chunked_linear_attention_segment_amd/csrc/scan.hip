@@ -20,7 +20,8 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const T* __restrict__ Q,
                                                         const T* __restrict__ V, int L, int C,
                                                         int NS, int phi, float* __restrict__ M,
                                                         bf16_t* __restrict__ M_lo,
-                                                        float* __restrict__ O_on) {
+                                                        float* __restrict__ O_on,
+                                                        const SegArg sg) {
     constexpr int TPR = 256 / DV;
     constexpr int CPT = DK / TPR;
     constexpr int TT = 32;
@@ -30,8 +31,8 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const T* __restrict__ Q,
 
     const int s = blockIdx.x;
     const size_t bh = blockIdx.y;
-    const int t0 = s * C;
-    const int len = min(C, L - t0);
+    const int t0 = seg_first(sg, s, C);
+    const int len = seg_length(sg, s, C, L);
     const int tid = threadIdx.x;
     const int c = tid / TPR;
     const int r0 = (tid % TPR) * CPT;
@@ -80,12 +81,13 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const T* __restrict__ Q,
 // loads), then the 16 token lanes are combined in a fixed order through LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void seg_means_kernel(const T* __restrict__ X, int L, int C,
-                                                        int NS, int DG, float* __restrict__ P) {
+                                                        int NS, int DG, float* __restrict__ P,
+                                                        const SegArg sg) {
     __shared__ float part[16][257];
     const int s = blockIdx.x;
     const size_t bx = blockIdx.y;
-    const int t0 = s * C;
-    const int len = min(C, L - t0);
+    const int t0 = seg_first(sg, s, C);
+    const int len = seg_length(sg, s, C, L);
     const int tl = threadIdx.x / 16, cg = threadIdx.x % 16;
     for (int e0 = cg * 8; e0 < DG; e0 += 128) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -106,31 +108,57 @@ __global__ __launch_bounds__(256) void seg_means_kernel(const T* __restrict__ X,
     }
 }
 
+static const SegArg kConstSeg{};  // constant segment length
+
 template <typename T, int DK, int DV>
 static int launch_scan_t(const mc_dims& d, const void* Q, const void* K, const void* V,
-                         float* M, uint16_t* M_lo, float* O_on, hipStream_t st) {
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+                         float* M, uint16_t* M_lo, float* O_on, const SegArg& sg,
+                         hipStream_t st) {
+    const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
     dim3 grid(NS, d.B * d.H);
     hipLaunchKernelGGL((scan_valu_kernel<T, DK, DV>), grid, dim3(256), 0, st, (const T*)Q,
                        (const T*)K, (const T*)V, d.L, d.seg_len, NS, d.phi, M, (bf16_t*)M_lo,
-                       O_on);
+                       O_on, sg);
     return (int)hipGetLastError();
 }
 
 template <typename T>
 static int launch_scan_dt(const mc_dims& d, const void* Q, const void* K, const void* V,
-                          float* M, uint16_t* M_lo, float* O_on, hipStream_t st) {
-    if (d.d_k == 128 && d.d_v == 128) return launch_scan_t<T, 128, 128>(d, Q, K, V, M, M_lo, O_on, st);
-    if (d.d_k == 128 && d.d_v == 64) return launch_scan_t<T, 128, 64>(d, Q, K, V, M, M_lo, O_on, st);
-    if (d.d_k == 64 && d.d_v == 128) return launch_scan_t<T, 64, 128>(d, Q, K, V, M, M_lo, O_on, st);
-    return launch_scan_t<T, 64, 64>(d, Q, K, V, M, M_lo, O_on, st);
+                          float* M, uint16_t* M_lo, float* O_on, const SegArg& sg,
+                          hipStream_t st) {
+    if (d.d_k == 128 && d.d_v == 128) return launch_scan_t<T, 128, 128>(d, Q, K, V, M, M_lo, O_on, sg, st);
+    if (d.d_k == 128 && d.d_v == 64) return launch_scan_t<T, 128, 64>(d, Q, K, V, M, M_lo, O_on, sg, st);
+    if (d.d_k == 64 && d.d_v == 128) return launch_scan_t<T, 64, 128>(d, Q, K, V, M, M_lo, O_on, sg, st);
+    return launch_scan_t<T, 64, 64>(d, Q, K, V, M, M_lo, O_on, sg, st);
 }
 
 int launch_scan_online(const mc_dims& d, const void* Q, const void* K, const void* V,
                        float* O_on, void* stream) {
     hipStream_t st = (hipStream_t)stream;
-    return d.dtype == MC_BF16 ? launch_scan_dt<bf16_t>(d, Q, K, V, nullptr, nullptr, O_on, st)
-                              : launch_scan_dt<float>(d, Q, K, V, nullptr, nullptr, O_on, st);
+    return d.dtype == MC_BF16
+               ? launch_scan_dt<bf16_t>(d, Q, K, V, nullptr, nullptr, O_on, kConstSeg, st)
+               : launch_scan_dt<float>(d, Q, K, V, nullptr, nullptr, O_on, kConstSeg, st);
+}
+
+template <typename T>
+static int launch_means(const mc_dims& d, const void* X, float* P, const SegArg& sg,
+                        hipStream_t st) {
+    const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
+    hipLaunchKernelGGL(seg_means_kernel<T>, dim3(NS, d.B * d.x_heads), dim3(256), 0, st,
+                       (const T*)X, d.L, d.seg_len, NS, d.d_g, P, sg);
+    return (int)hipGetLastError();
+}
+
+// Arbitrary boundaries: the generic scan (any dtype) and the means over each segment.
+int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
+                             const void* V, const void* X, float* M, uint16_t* M_lo, float* P,
+                             float* O_on, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    int rc = d.dtype == MC_BF16 ? launch_scan_dt<bf16_t>(d, Q, K, V, M, M_lo, O_on, sg, st)
+                                : launch_scan_dt<float>(d, Q, K, V, M, M_lo, O_on, sg, st);
+    if (rc) return rc;
+    return d.dtype == MC_BF16 ? launch_means<bf16_t>(d, X, P, sg, st)
+                              : launch_means<float>(d, X, P, sg, st);
 }
 
 int launch_scan_mfma(const mc_dims& d, const void* Q, const void* K, const void* V, float* M,
@@ -140,25 +168,17 @@ int launch_scan_prefill(const mc_dims& d, const void* Q, const void* K, const vo
                         const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,
                         void* stream) {
     hipStream_t st = (hipStream_t)stream;
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     int rc = -1;
     if (d.dtype == MC_BF16) rc = launch_scan_mfma(d, Q, K, V, M, M_lo, O_on, stream);
     if (rc >= 0) {
         if (rc) return rc;
     } else if (d.dtype == MC_BF16)
-        rc = launch_scan_dt<bf16_t>(d, Q, K, V, M, M_lo, O_on, st);
+        rc = launch_scan_dt<bf16_t>(d, Q, K, V, M, M_lo, O_on, kConstSeg, st);
     else
-        rc = launch_scan_dt<float>(d, Q, K, V, M, M_lo, O_on, st);
+        rc = launch_scan_dt<float>(d, Q, K, V, M, M_lo, O_on, kConstSeg, st);
     if (rc) return rc;
-    dim3 grid(NS, d.B * d.x_heads);
-    const int threads = 256;
-    if (d.dtype == MC_BF16)
-        hipLaunchKernelGGL(seg_means_kernel<bf16_t>, grid, dim3(threads), 0, st,
-                           (const bf16_t*)X, d.L, d.seg_len, NS, d.d_g, P);
-    else
-        hipLaunchKernelGGL(seg_means_kernel<float>, grid, dim3(threads), 0, st, (const float*)X,
-                           d.L, d.seg_len, NS, d.d_g, P);
-    return (int)hipGetLastError();
+    return d.dtype == MC_BF16 ? launch_means<bf16_t>(d, X, P, kConstSeg, st)
+                              : launch_means<float>(d, X, P, kConstSeg, st);
 }
 
 }  // namespace mc

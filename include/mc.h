@@ -180,6 +180,34 @@ mc_status mc_decode_step(const mc_dims* dims, const void* q, const void* k, cons
                          int32_t* count_on, void* M_cache, float* P_cache, int32_t* n_cached,
                          int32_t n_cap, void* y, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Arbitrary segment boundaries (Memory Caching paper §3, Eq. 4b: segment s has its own
+ * length L^(s); gitcode explainer §4.2: the logarithmic segmentation, one segment per set bit
+ * of L, largest first).  The same write path and GRM read, with segment i holding the tokens
+ * [seg_off[i], seg_off[i+1]) instead of a constant length:
+ *
+ *   seg_off  HOST array of n_seg + 1 int32: 0 = seg_off[0] < seg_off[1] < ... < seg_off[n_seg]
+ *            = L.  It is read when the call is made (passed to the kernels by value), so the
+ *            caller may reuse it at once.  dims->seg_len is ignored (it must still be >= 1).
+ *   n_seg    1 <= n_seg <= MC_MAX_SEGS; NS = n_seg below.
+ *   The other arguments are those of mc_scan_prefill / mc_grm_readout with NS = n_seg, except
+ *   that the read takes the online read O_on written by mc_scan_prefill_segs (required), not
+ *   K and V; its workspace is mc_workspace_bytes(dims, MC_OP_GRM, 0, 0) bytes.
+ *   Both run the fp32-accumulating kernels that take any segmentation.
+ *   Errors as the constant-length calls; offsets that are not strictly increasing from 0 to L
+ *   return MC_ERR_DIMS, more than MC_MAX_SEGS segments MC_ERR_UNSUPPORTED.
+ */
+#define MC_MAX_SEGS 512
+
+mc_status mc_scan_prefill_segs(const mc_dims* dims, const int32_t* seg_off, int32_t n_seg,
+                               const void* Q, const void* K, const void* V, const void* X,
+                               float* M, uint16_t* M_lo, float* P, float* O_on, void* stream);
+
+mc_status mc_grm_readout_segs(const mc_dims* dims, const int32_t* seg_off, int32_t n_seg,
+                              const void* Q, const void* U, const void* X, const float* M,
+                              const uint16_t* M_lo, const float* P, const float* O_on, void* Y,
+                              float* gamma, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

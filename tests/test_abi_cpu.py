@@ -172,3 +172,40 @@ def test_workspace_sizes_scale_with_inputs():
     assert big >= 8 * small - 256
     assert mc.mc_workspace_bytes(dims(B=0), mc.MC_OP_GRM) == 0
     assert mc.mc_workspace_bytes(dims(), mc.MC_OP_PREFILL) == 0
+
+
+def test_segment_offsets_are_validated():
+    # arbitrary boundaries: host offsets 0 = o_0 < ... < o_n = L, at most MC_MAX_SEGS segments
+    d = dims(L=1000)
+    lib = mc.load()
+    ws = mc.mc_workspace_bytes(d, mc.MC_OP_GRM)
+
+    def scan(off, **kw):
+        off = np.ascontiguousarray(np.asarray(off, dtype=np.int32))
+        p = dict(Q=A, K=A, V=A, X=A, M=A, M_lo=A, P=A, O_on=A)
+        p.update(kw)
+        return lib.mc_scan_prefill_segs(ctypes.byref(d), off.ctypes.data, off.shape[0] - 1,
+                                        p["Q"], p["K"], p["V"], p["X"], p["M"], p["M_lo"],
+                                        p["P"], p["O_on"], None)
+
+    def read(off, ws_bytes=ws, **kw):
+        off = np.ascontiguousarray(np.asarray(off, dtype=np.int32))
+        p = dict(Q=A, U=A, X=A, M=A, M_lo=A, P=A, O_on=A, Y=A, gamma=None, ws=A)
+        p.update(kw)
+        return lib.mc_grm_readout_segs(ctypes.byref(d), off.ctypes.data, off.shape[0] - 1,
+                                       p["Q"], p["U"], p["X"], p["M"], p["M_lo"], p["P"],
+                                       p["O_on"], p["Y"], p["gamma"], p["ws"], ws_bytes, None)
+    good = [0, 512, 768, 896, 960, 992, 1000]
+    for bad in ([0, 512, 512, 1000], [1, 512, 1000], [0, 512, 999], [0, 600, 500, 1000], [0]):
+        assert scan(bad) == mc.MC_ERR_DIMS, bad
+        assert read(bad) == mc.MC_ERR_DIMS, bad
+    many = list(range(0, 1000, 1)) + [1000]  # 1000 segments > MC_MAX_SEGS
+    assert scan(many) == mc.MC_ERR_UNSUPPORTED
+    assert read(many) == mc.MC_ERR_UNSUPPORTED
+    assert lib.mc_scan_prefill_segs(ctypes.byref(d), None, 2, A, A, A, A, A, A, A, A,
+                                    None) == mc.MC_ERR_NULL
+    assert scan(good, M_lo=None) == mc.MC_ERR_NULL        # bf16 writes the bf16 copy
+    assert scan(good, X=MIS) == mc.MC_ERR_ALIGN
+    assert read(good, O_on=None) == mc.MC_ERR_NULL        # the read takes the scan's O_on
+    assert read(good, ws_bytes=ws - 1) == mc.MC_ERR_WORKSPACE
+    assert read(good, Y=MIS) == mc.MC_ERR_ALIGN

@@ -289,3 +289,51 @@ def test_prefill_then_decode_matches_longer_prefill():
     assert int(ncached[0]) == 3 and int(count[0]) == 0
     assert slice_rel_err(to_np(Mc[:, :, 2]), ref["M"][:, :, 2]) <= 2e-2
     assert slice_rel_err(to_np(Pc[:, :, 2]), ref["P"][:, :, 2]) <= 1e-5
+
+
+# Arbitrary segment boundaries (mc_scan_prefill_segs / mc_grm_readout_segs) against the
+# oracle's seg_offsets mode: the logarithmic segmentation, random boundaries (including
+# one-token segments), and boundaries at multiples of C (the constant-length read).
+def _random_offsets(L, n, seed):
+    cuts = np.sort(np.random.default_rng(seed).choice(np.arange(1, L), n - 1, replace=False))
+    return [0] + cuts.tolist() + [L]
+
+
+SEG_CASES = {
+    "bf16_log_L1000_d128": (Workload("x", 1, 2, 1000, 128, 128, 128, 1, "identity", "bf16"),
+                            "log"),
+    "f32_log_L777_d64_elu": (Workload("x", 2, 2, 777, 64, 64, 32, 1, "elu1", "f32"), "log"),
+    "bf16_random_L900_d128_elu": (Workload("x", 1, 3, 900, 128, 128, 64, 1, "elu1", "bf16"),
+                                  "random"),
+    "f32_random_L300_d64_xheadsH": (Workload("x", 1, 2, 300, 64, 128, 64, 1, "identity", "f32",
+                                             x_heads=2), "random"),
+    "bf16_multiples_of_64_L640": (Workload("x", 1, 2, 640, 128, 64, 128, 1, "identity",
+                                           "bf16"), "c64"),
+}
+
+
+@pytest.mark.parametrize("name", list(SEG_CASES))
+def test_grm_segment_offsets(name):
+    w, kind = SEG_CASES[name]
+    if kind == "log":
+        off = oracle.log_segments(w.L)
+    elif kind == "random":
+        off = _random_offsets(w.L, 23, seed=5)
+        off = sorted(set(off + [off[1] + 1]))  # a one-token segment
+    else:
+        off = list(range(0, w.L, 64)) + [w.L]
+    announce("grm segment offsets %s: %d segments" % (name, len(off) - 1))
+    inp = make_prefill(w, seed=3)
+    d = _dims(w)
+    dev = {k: to_dev(v, w.dtype) for k, v in inp.items()}
+    out = mc.prefill_grm_segs(d, off, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"],
+                              want_gamma=True)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], seg_len=1,
+                         phi=w.phi, mode="grm", want_states=True, want_online=True,
+                         want_gamma=True, seg_offsets=off)
+    tol = TOL[w.dtype]
+    errs = {k: slice_rel_err(to_np(out[k]), ref[k]) for k in ("Y", "M", "P", "O_on", "gamma")}
+    announce("  errors %s" % errs)
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
