@@ -99,7 +99,9 @@ def main():
     ap.add_argument("--online", choices=["scan", "fused"], default="fused",
                     help="where the online read M_t^(s) phi(q_t) is formed: written by the scan "
                          "and read back (scan), or inside the gated read from K and V (fused)")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
+    ap.add_argument("--no-segs", action="store_true",
+                    help="skip the logarithmic-segmentation prefill line")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "segs"], default="all",
                     help="profiling aid: run only one workload (the JSON line then lacks the "
                          "other part)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -130,9 +132,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
         return
-    if args.only == "decode":
+    if args.only in ("decode", "segs"):
         rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup}
-        run_decode(args, rec, dev)
+        (run_decode if args.only == "decode" else run_log_segments)(args, rec, dev)
         print(json.dumps(rec), flush=True)
         return
     w = WORKLOADS["grm_bf16_L64K"]
@@ -204,6 +206,9 @@ def main():
 
     if not args.no_decode and args.only == "all":
         run_decode(args, rec, dev)
+
+    if not args.no_segs and args.only == "all":
+        run_log_segments(args, rec, dev)
 
     if not args.no_peak and args.only == "all":
         measured_peaks(rec)
@@ -292,6 +297,70 @@ def run_decode(args, rec, dev):
                                           "unit": "GB/s"}}
         del di, wsd, yd
         torch.cuda.empty_cache()
+
+
+def run_log_segments(args, rec, dev):
+    """The logarithmic segmentation (one segment per set bit of L, largest first) of the L=64K
+    workload's shape at L = 65535 (16 segments of 32768 .. 1 tokens): mc_scan_prefill_segs +
+    mc_grm_readout_segs, inputs resident, tokens/s.  These run the fp32-accumulating kernels
+    that take any boundaries; the roofline is the fp32 vector unit."""
+    import torch
+
+    import chunked_linear_attention_segment_amd as mc
+    from chunked_linear_attention_segment_amd.inputs import WORKLOADS, make_prefill_device
+    w = WORKLOADS["grm_bf16_L64K"]
+    L = 65535
+    off = [0]
+    for b in range(L.bit_length() - 1, -1, -1):
+        if (L >> b) & 1:
+            off.append(off[-1] + (1 << b))
+    NS = len(off) - 1
+    B, H, dk, dv, dg = w.B, w.H, w.d_k, w.d_v, w.d_g
+    d = mc.make_dims(B, H, L, dk, dv, dg, 1, 1, w.dtype, w.phi)
+    inp = make_prefill_device(w, seed=0, device=dev, L=L)
+    M = torch.empty((B, H, NS, dv, dk), dtype=torch.float32, device=dev)
+    M_lo = torch.empty((B, H, NS, dv, dk), dtype=torch.bfloat16, device=dev)
+    P = torch.empty((B, 1, NS, dg), dtype=torch.float32, device=dev)
+    O_on = torch.empty((B, H, L, dv), dtype=torch.float32, device=dev)
+    Y = torch.empty((B, H, L, dv), dtype=torch.bfloat16, device=dev)
+    ws = mc.workspace(d, mc.MC_OP_GRM, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mc.mc_scan_prefill_segs(d, off, inp["Q"], inp["K"], inp["V"], inp["X"], M, M_lo, P,
+                                O_on, stream=stream)
+        mc.mc_grm_readout_segs(d, off, inp["Q"], inp["U"], inp["X"], M, M_lo, P, O_on, Y,
+                               None, ws=ws, stream=stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # algorithmic FLOPs: per token, the state update and online read (4 dk dv), the reads of
+    # the completed segments before its own (2 dk dv each) and s + 1 gate logits (2 dg each)
+    fl = 0
+    for s in range(NS):
+        n = off[s + 1] - off[s]
+        fl += n * (4 * dk * dv + s * 2 * dk * dv + (s + 1) * 2 * dg)
+    fl *= B * H
+    tflops = fl / (ms / 1e3) / 1e12
+    rec["log_segments"] = {
+        "workload": "grm_bf16_L64K shape at L=65535, logarithmic segmentation (%d segments)"
+                    % NS,
+        "metric": "prefill tokens/s", "value": round(B * L / (ms / 1e3), 1), "unit": "tokens/s",
+        "ms_per_step": round(ms, 4),
+        "steps_timed": "mc_scan_prefill_segs + mc_grm_readout_segs",
+        "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": 157.3,
+                     "unit": "TFLOP/s", "frac": round(tflops / 157.3, 4),
+                     "algorithmic_flops": fl}}
+    del inp, M, M_lo, P, O_on, Y, ws
+    torch.cuda.empty_cache()
 
 
 def cpu_baseline(w, rows_sample):

@@ -138,3 +138,29 @@ def test_decode_full_size():
                 assert slice_rel_err(to_np(di["M_on"][b:b + 1, h:h + 1]), st.M_on) <= 1e-5
     del di
     torch.cuda.empty_cache()
+
+
+def test_log_segments_full_size():
+    # the logarithmic segmentation at the L=64K workload's shape, L = 65535 (16 segments), as
+    # the benchmark times it (mc_scan_prefill_segs + mc_grm_readout_segs)
+    w = WORKLOADS["grm_bf16_L64K"]
+    L = 65535
+    off = oracle.log_segments(L)
+    announce("full-size log segmentation: H=%d L=%d, %d segments" % (w.H, L, len(off) - 1))
+    inp = make_prefill_device(w, seed=0, L=L)
+    d = mc.make_dims(w.B, w.H, L, w.d_k, w.d_v, w.d_g, 1, 1, w.dtype, w.phi)
+    out = mc.prefill_grm_segs(d, off, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(out["Y"].float()).all()
+    rows = np.unique(np.concatenate([np.array(off[1:-1]) - 1, np.array(off[1:-1]),
+                                     np.random.default_rng(11).integers(0, L, 200)])
+                     ).astype(np.int32)
+    for b, h in [(0, 0), (0, 17)]:
+        hin = _head(inp, b, h)
+        ref = oracle.prefill(hin["Q"], hin["K"], hin["V"], hin["U"], hin["X"], seg_len=1,
+                             phi=w.phi, rows=rows, want_states=True, seg_offsets=off)
+        errs = {"Y": slice_rel_err(to_np(out["Y"][b:b + 1, h:h + 1, rows]), ref["Y"]),
+                "M": slice_rel_err(to_np(out["M"][b:b + 1, h:h + 1]), ref["M"]),
+                "P": slice_rel_err(to_np(out["P"][b:b + 1]), ref["P"])}
+        announce("  (b=%d, h=%d) %d rows: %s" % (b, h, len(rows), errs))
+        assert errs["Y"] <= TOL["bf16"] and errs["M"] <= 1e-4 and errs["P"] <= 1e-4
