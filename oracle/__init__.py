@@ -6,7 +6,8 @@ CPU-baseline leg, never by the product package.  It shares no code with the HIP 
 The arithmetic lives in ``mc_oracle.c`` (plain C, fp64, OpenMP over (b, h)); this module
 only builds it with gcc and marshals numpy arrays.  The functions follow, per token, the
 recurrence and read of the Memory Caching paper (§3 Eq. 4b, §3.1 Eq. 7-10) and the Sparse
-Selective Caching / Memory Soup formulas of the gitcode explainer (§3.3, §3.4); the C file
+Selective Caching / Memory Soup formulas of the gitcode explainer (§3.3, §3.4), and the
+sliding-window linear-attention memory of the paper's SWLA paragraph (Eq. 28-29); the C file
 cites each step.
 """
 from __future__ import annotations
@@ -46,7 +47,7 @@ def _load():
         P = ctypes.c_void_p
         lib.mco_prefill.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P,
                                     ctypes.c_int64, P, P, P, P, P, P, ctypes.c_int, P,
-                                    ctypes.c_int32]
+                                    ctypes.c_int32, P, P, P]
         lib.mco_prefill.restype = ctypes.c_int
         lib.mco_decode_step.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P,
                                         ctypes.c_int32, P, P]
@@ -70,12 +71,15 @@ def max_threads() -> int:
 
 def prefill(Q, K, V, U, X, seg_len: int, phi: str = "identity", mode: str = "grm",
             top_k: int = 0, rows=None, want_states: bool = False, want_online: bool = False,
-            want_gamma: bool = False, n_threads: int = 0, seg_offsets=None) -> dict:
+            want_gamma: bool = False, n_threads: int = 0, seg_offsets=None,
+            swla=None) -> dict:
     """Evaluate the MC read for every token (or only ``rows``) of every (b, h).
 
     Q, K [B,H,L,dk]; V [B,H,L,dv]; U [B,H,L,dg]; X [B,xh,L,dg] (xh = 1 or H).
     Segments have length seg_len, or are [seg_offsets[i], seg_offsets[i+1]) when
     seg_offsets (0 = o_0 < o_1 < ... < o_N = L) is given (seg_len is then ignored).
+    swla = (alpha, beta, lam), each [B,H,L]: the SWLA memory of window 2 (Memory Caching
+    paper, Eq. 28) in place of the linear-attention update.
     Returns a dict with 'Y' [B,H,n_rows,dv] and, on request, 'M' [B,H,NS,dv,dk],
     'P' [B,xh,NS,dg], 'O_on' [B,H,L,dv], 'gamma' [B,H,n_rows,NS], 'idx' [B,H,n_rows,top_k].
     """
@@ -100,6 +104,10 @@ def prefill(Q, K, V, U, X, seg_len: int, phi: str = "identity", mode: str = "grm
     else:
         nr = L
     m = _MODES[mode]
+    gates = [None, None, None]
+    if swla is not None:
+        gates = [_f64(g) for g in swla]
+        assert all(g.shape == (B, H, L) for g in gates)
     dims = np.array([B, H, L, dk, dv, dg, C, xh, 1 if phi in ("elu1", "elu+1") else 0],
                     dtype=np.int32)
     out = {"Y": np.zeros((B, H, nr, dv))}
@@ -111,7 +119,7 @@ def prefill(Q, K, V, U, X, seg_len: int, phi: str = "identity", mode: str = "grm
     rc = _load().mco_prefill(_ptr(dims), m, int(top_k), _ptr(Q), _ptr(K), _ptr(V), _ptr(U),
                              _ptr(X), _ptr(rows), int(nr), _ptr(out["Y"]), _ptr(M), _ptr(P),
                              _ptr(O), _ptr(G), _ptr(I), int(n_threads), _ptr(off),
-                             int(NS if off is not None else 0))
+                             int(NS if off is not None else 0), *(_ptr(g) for g in gates))
     if rc != 0:
         raise ValueError("mco_prefill failed with code %d" % rc)
     if want_states:

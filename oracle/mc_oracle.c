@@ -83,6 +83,13 @@ static int mco_topk(const double* score, int n, int k, int* chosen) {
  * ([EXP] §3.3: the gamma-weighted average of the memory matrices is formed first and then
  * read once).
  *
+ * SWLA memory (alpha != NULL; [MC] §3.1, the sliding-window linear attention paragraph,
+ * Eq. 26 with window c = 2, i.e. Eq. 28): alpha, beta, lam are [B,H,L] per-token scalars and
+ * the update is M_t = alpha_t M_{t-1} + beta_t v_{t-1} phi(k_{t-1})^T + lam_t v_t phi(k_t)^T.
+ * The window stays inside the segment: at a segment's first token there is no previous
+ * token to write (its memory starts from zero, Eq. 4b).  The read (Eq. 29) is unchanged.
+ * With alpha == NULL the update is the linear-attention one (Eq. 2).
+ *
  * Segments: constant length C, or (off != NULL) the n_seg segments [off[i], off[i+1]) with
  * off[0] = 0 < off[1] < ... < off[n_seg] = L ([MC] Eq. 4b lets the segment lengths L^(s)
  * differ); C is then not read.
@@ -99,7 +106,8 @@ int mco_prefill(const int32_t* dims, int mode, int top_k,
                 const double* Q, const double* K, const double* V, const double* U,
                 const double* X, const int32_t* rows, int64_t n_rows,
                 double* Y, double* M_out, double* P_out, double* O_on, double* gamma,
-                int32_t* idx, int n_threads, const int32_t* off, int32_t n_seg) {
+                int32_t* idx, int n_threads, const int32_t* off, int32_t n_seg,
+                const double* alpha, const double* beta, const double* lam) {
     const int B = dims[0], H = dims[1], L = dims[2], dk = dims[3], dv = dims[4], dg = dims[5];
     const int C = dims[6], xh = dims[7], phi = dims[8];
     if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || dg <= 0) return MCO_EARG;
@@ -113,6 +121,7 @@ int mco_prefill(const int32_t* dims, int mode, int top_k,
     if (mode < 0 || mode > 3) return MCO_EARG;
     if (mode == MCO_SSC && top_k <= 0) return MCO_EARG;
     if (rows != NULL && O_on != NULL) return MCO_EARG;
+    if (alpha != NULL && (beta == NULL || lam == NULL)) return MCO_EARG;
     const int NS = off ? n_seg : (L + C - 1) / C;
     const int64_t nr = rows ? n_rows : (int64_t)L;
     if (rows)
@@ -140,6 +149,7 @@ int mco_prefill(const int32_t* dims, int mode, int top_k,
         double* Mon = (double*)calloc((size_t)dv * dk, sizeof(double));     /* online state */
         double* xs = (double*)calloc((size_t)dg, sizeof(double));           /* online x sum */
         double* kh = (double*)malloc(sizeof(double) * dk);
+        double* kp = (double*)malloc(sizeof(double) * dk);
         double* qh = (double*)malloc(sizeof(double) * dk);
         double* pt = (double*)malloc(sizeof(double) * dg);
         double* a = (double*)malloc(sizeof(double) * (NS + 1));
@@ -147,7 +157,7 @@ int mco_prefill(const int32_t* dims, int mode, int top_k,
         int* sel = (int*)malloc(sizeof(int) * (NS + 1));
         double* soup = (double*)malloc(sizeof(double) * dv * dk);
         double* tmp = (double*)malloc(sizeof(double) * dv);
-        if (!Mc || !Pc || !Mon || !xs || !kh || !qh || !pt || !a || !g || !sel || !soup || !tmp) {
+        if (!Mc || !Pc || !Mon || !xs || !kh || !kp || !qh || !pt || !a || !g || !sel || !soup || !tmp) {
 #pragma omp atomic write
             err = MCO_ENOMEM;
         } else {
@@ -166,11 +176,29 @@ int mco_prefill(const int32_t* dims, int mode, int top_k,
                     memset(Mon, 0, sizeof(double) * dv * dk);
                     memset(xs, 0, sizeof(double) * dg);
                 }
-                /* memory update M_t = M_{t-1} + v_t phi(k_t)^T  ([MC] Eq. 2, Eq. 4b) */
                 for (int r = 0; r < dk; ++r) kh[r] = mco_phi(k[(size_t)t * dk + r], phi);
-                for (int c = 0; c < dv; ++c) {
-                    const double vc = v[(size_t)t * dv + c];
-                    for (int r = 0; r < dk; ++r) Mon[(size_t)c * dk + r] += vc * kh[r];
+                if (alpha) {
+                    /* SWLA, window 2 ([MC] Eq. 28): decay the memory, then write the previous
+                     * token of this segment with beta_t and this token with lam_t */
+                    const size_t gi = (size_t)bh * L + t;
+                    for (size_t e = 0; e < (size_t)dv * dk; ++e) Mon[e] *= alpha[gi];
+                    if (j > 0) {
+                        for (int r = 0; r < dk; ++r) kp[r] = mco_phi(k[(size_t)(t - 1) * dk + r], phi);
+                        for (int c = 0; c < dv; ++c) {
+                            const double vc = beta[gi] * v[(size_t)(t - 1) * dv + c];
+                            for (int r = 0; r < dk; ++r) Mon[(size_t)c * dk + r] += vc * kp[r];
+                        }
+                    }
+                    for (int c = 0; c < dv; ++c) {
+                        const double vc = lam[gi] * v[(size_t)t * dv + c];
+                        for (int r = 0; r < dk; ++r) Mon[(size_t)c * dk + r] += vc * kh[r];
+                    }
+                } else {
+                    /* memory update M_t = M_{t-1} + v_t phi(k_t)^T  ([MC] Eq. 2, Eq. 4b) */
+                    for (int c = 0; c < dv; ++c) {
+                        const double vc = v[(size_t)t * dv + c];
+                        for (int r = 0; r < dk; ++r) Mon[(size_t)c * dk + r] += vc * kh[r];
+                    }
                 }
                 for (int e = 0; e < dg; ++e) xs[e] += x[(size_t)t * dg + e];
 
@@ -268,7 +296,7 @@ int mco_prefill(const int32_t* dims, int mode, int top_k,
             if (P_out && (xh == H || h == 0))
                 memcpy(P_out + ((size_t)b * xh + hx) * NS * dg, Pc, sizeof(double) * NS * dg);
         }
-        free(Mc); free(Pc); free(Mon); free(xs); free(kh); free(qh); free(pt);
+        free(Mc); free(Pc); free(Mon); free(xs); free(kh); free(kp); free(qh); free(pt);
         free(a); free(g); free(sel); free(soup); free(tmp);
     }
     return err;

@@ -419,3 +419,136 @@ def test_log_segments_worked_example():
         lens = np.diff(off)
         assert off[0] == 0 and off[-1] == L and len(lens) == bin(L).count("1")
         assert all(int(n) & (int(n) - 1) == 0 for n in lens) and list(lens) == sorted(lens)[::-1]
+
+
+# ---- SWLA memory of window 2 (Memory Caching paper, SWLA paragraph, Eq. 26-29) ----
+
+def _swla_gates(B, H, L, seed, alpha_lo=0.5):
+    rng = np.random.default_rng(seed)
+    alpha = rng.uniform(alpha_lo, 1.0, (B, H, L))
+    beta = rng.uniform(-0.5, 1.0, (B, H, L))
+    lam = rng.uniform(0.2, 1.2, (B, H, L))
+    return alpha, beta, lam
+
+
+def _swla_weight(alpha, beta, lam, a, t, r):
+    """Weight of v_r k_r^T in the memory after token t, both in the segment starting at a:
+    it was written with lam_r at step r and with beta_{r+1} at step r+1 (its second slot in
+    the window), and every later step multiplied it by that step's alpha."""
+    assert a <= r <= t
+    w = lam[r] * np.prod(alpha[r + 1:t + 1])
+    if r + 1 <= t:
+        w += beta[r + 1] * np.prod(alpha[r + 2:t + 1])
+    return w
+
+
+def _brute_swla(Q, K, V, U, X, off, gates, phi="identity"):
+    """Token-pair form of Eq. 29 with the Eq. 28 memory: no recurrence, every (t, r) weight
+    written as products of the gates.  Returns Y, the cached states and the online read."""
+    B, H, L, dk = Q.shape
+    dv = V.shape[-1]
+    xh = X.shape[1]
+    qh, kh = _phi(Q, phi), _phi(K, phi)
+    seg = np.searchsorted(np.asarray(off), np.arange(L), side="right") - 1
+    NS = len(off) - 1
+    Y = np.zeros(V.shape)
+    O = np.zeros(V.shape)
+    M = np.zeros((B, H, NS, dv, dk))
+    for b in range(B):
+        for h in range(H):
+            al, be, la = (g[b, h] for g in gates)
+            x = X[b, 0 if xh == 1 else h]
+            means = [x[off[i]:off[i + 1]].mean(axis=0) for i in range(NS)]
+            for i in range(NS):
+                a, e = off[i], off[i + 1] - 1
+                for r in range(a, e + 1):
+                    M[b, h, i] += _swla_weight(al, be, la, a, e, r) * np.outer(V[b, h, r], kh[b, h, r])
+            for t in range(L):
+                s = int(seg[t])
+                a = off[s]
+                logits = [float(U[b, h, t] @ means[i]) for i in range(s)]
+                logits.append(float(U[b, h, t] @ x[a:t + 1].mean(axis=0)))
+                g = torch.softmax(torch.tensor(logits, dtype=torch.float64), 0).numpy()
+                for r in range(a, t + 1):
+                    O[b, h, t] += (_swla_weight(al, be, la, a, t, r)
+                                   * float(qh[b, h, t] @ kh[b, h, r]) * V[b, h, r])
+                Y[b, h, t] = g[s] * O[b, h, t]
+                for i in range(s):
+                    Y[b, h, t] += g[i] * (M[b, h, i] @ qh[b, h, t])
+    return Y, M, O
+
+
+def test_swla_unit_gates_are_the_linear_attention_memory():
+    # alpha = 1, beta = 0, lam = 1 turns Eq. 28 into the linear-attention update (c = 1)
+    B, H, L = 2, 2, 45
+    Q, K, V, U, X = _rand(B, H, L, 4, 3, 5, seed=51)
+    one, zero = np.ones((B, H, L)), np.zeros((B, H, L))
+    for mode, k in (("grm", 0), ("ssc", 2)):
+        a = oracle.prefill(Q, K, V, U, X, seg_len=8, mode=mode, top_k=k, want_states=True,
+                           want_online=True)
+        b = oracle.prefill(Q, K, V, U, X, seg_len=8, mode=mode, top_k=k, want_states=True,
+                           want_online=True, swla=(one, zero, one))
+        for key in a:
+            np.testing.assert_array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("L,C,off,phi,xh", [(40, 8, None, "identity", 1),
+                                            (37, 6, None, "elu1", 2),
+                                            (29, 0, [0, 1, 3, 11, 12, 29], "identity", 1)])
+def test_brute_force_swla(L, C, off, phi, xh):
+    B, H = 1, 2
+    Q, K, V, U, X = _rand(B, H, L, 4, 3, 5, xh=xh, seed=52, scale_u=2.0)
+    gates = _swla_gates(B, H, L, seed=53)
+    out = oracle.prefill(Q, K, V, U, X, seg_len=C, phi=phi, seg_offsets=off, want_states=True,
+                         want_online=True, swla=gates)
+    o = off if off is not None else list(range(0, L, C)) + [L]
+    Yb, Mb, Ob = _brute_swla(Q, K, V, U, X, o, gates, phi)
+    np.testing.assert_allclose(out["O_on"], Ob, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(out["M"], Mb, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(out["Y"], Yb, rtol=1e-11, atol=1e-11)
+
+
+def test_swla_without_carry_is_a_two_token_window():
+    # alpha = 0 keeps only the window: M_t = beta_t v_{t-1} k_{t-1}^T + lam_t v_t k_t^T, and
+    # the segment's first token has no previous token to write
+    B, H, L, C = 1, 3, 30, 7
+    Q, K, V, U, X = _rand(B, H, L, 4, 3, 5, seed=54)
+    _, beta, lam = _swla_gates(B, H, L, seed=55)
+    out = oracle.prefill(Q, K, V, U, X, seg_len=C, want_online=True, want_states=True,
+                         swla=(np.zeros((B, H, L)), beta, lam))
+    for h in range(H):
+        for t in range(L):
+            exp = lam[0, h, t] * float(Q[0, h, t] @ K[0, h, t]) * V[0, h, t]
+            if t % C:
+                exp = exp + beta[0, h, t] * float(Q[0, h, t] @ K[0, h, t - 1]) * V[0, h, t - 1]
+            np.testing.assert_allclose(out["O_on"][0, h, t], exp, rtol=1e-12, atol=1e-12)
+        for i in range((L + C - 1) // C):
+            e = min(L, (i + 1) * C) - 1
+            exp = lam[0, h, e] * np.outer(V[0, h, e], K[0, h, e])
+            if e % C:
+                exp = exp + beta[0, h, e] * np.outer(V[0, h, e - 1], K[0, h, e - 1])
+            np.testing.assert_allclose(out["M"][0, h, i], exp, rtol=1e-12, atol=1e-12)
+
+
+def test_swla_constant_decay_one_segment_is_decayed_attention():
+    # beta = 0, lam = 1, alpha = a, one segment: y_t = sum_{r<=t} a^(t-r) (q_t.k_r) v_r, the
+    # attention form with a decay mask
+    B, H, L, a = 1, 2, 33, 0.93
+    Q, K, V, U, X = _rand(B, H, L, 4, 3, 5, seed=56)
+    gates = (np.full((B, H, L), a), np.zeros((B, H, L)), np.ones((B, H, L)))
+    out = oracle.prefill(Q, K, V, U, X, seg_len=L, swla=gates)
+    t = np.arange(L)
+    D = np.where(t[:, None] >= t[None, :], a ** (t[:, None] - t[None, :]).clip(0), 0.0)
+    exp = (Q @ np.swapaxes(K, -1, -2) * D) @ V
+    np.testing.assert_allclose(out["Y"], exp, rtol=1e-11, atol=1e-11)
+
+
+def test_swla_soup_equals_grm():
+    # SWLA is a linear memory, so its Memory Soup and GRM variants coincide (the remark after
+    # Eq. 29)
+    B, H, L = 1, 2, 36
+    Q, K, V, U, X = _rand(B, H, L, 4, 3, 5, seed=57)
+    gates = _swla_gates(B, H, L, seed=58)
+    a = oracle.prefill(Q, K, V, U, X, seg_len=6, mode="grm", swla=gates)
+    b = oracle.prefill(Q, K, V, U, X, seg_len=6, mode="soup", swla=gates)
+    np.testing.assert_allclose(a["Y"], b["Y"], rtol=1e-12, atol=1e-12)
