@@ -101,7 +101,10 @@ def main():
                          "and read back (scan), or inside the gated read from K and V (fused)")
     ap.add_argument("--no-segs", action="store_true",
                     help="skip the logarithmic-segmentation prefill line")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "segs"], default="all",
+    ap.add_argument("--no-swla", action="store_true",
+                    help="skip the SWLA-memory prefill line")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "segs", "swla"],
+                    default="all",
                     help="profiling aid: run only one workload (the JSON line then lacks the "
                          "other part)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -132,9 +135,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
         return
-    if args.only in ("decode", "segs"):
+    if args.only in ("decode", "segs", "swla"):
         rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup}
-        (run_decode if args.only == "decode" else run_log_segments)(args, rec, dev)
+        {"decode": run_decode, "segs": run_log_segments, "swla": run_swla}[args.only](
+            args, rec, dev)
         print(json.dumps(rec), flush=True)
         return
     w = WORKLOADS["grm_bf16_L64K"]
@@ -209,6 +213,9 @@ def main():
 
     if not args.no_segs and args.only == "all":
         run_log_segments(args, rec, dev)
+
+    if not args.no_swla and args.only == "all":
+        run_swla(args, rec, dev)
 
     if not args.no_peak and args.only == "all":
         measured_peaks(rec)
@@ -360,6 +367,76 @@ def run_log_segments(args, rec, dev):
                      "unit": "TFLOP/s", "frac": round(tflops / 157.3, 4),
                      "algorithmic_flops": fl}}
     del inp, M, M_lo, P, O_on, Y, ws
+    torch.cuda.empty_cache()
+
+
+def run_swla(args, rec, dev):
+    """The SWLA memory (window 2) at the L=64K workload's shape: mc_scan_prefill_swla (the
+    decayed scan on MFMA, which also writes the online read) + mc_grm_readout taking that
+    online read; inputs and gates resident, tokens/s.  Rooflines: the read against bf16 MFMA
+    (its algorithmic FLOPs without the online term, which the scan forms), the scan against
+    HBM (its algorithmic bytes)."""
+    import torch
+
+    import chunked_linear_attention_segment_amd as mc
+    from chunked_linear_attention_segment_amd.inputs import (WORKLOADS, make_prefill_device,
+                                                             make_swla_gates_device)
+    w = WORKLOADS["grm_bf16_L64K"]
+    B, H, L, C, dk, dv, dg = w.B, w.H, w.L, w.seg_len, w.d_k, w.d_v, w.d_g
+    d = mc.make_dims(B, H, L, dk, dv, dg, C, 1, w.dtype, w.phi)
+    inp = make_prefill_device(w, seed=0, device=dev)
+    g = make_swla_gates_device(B, H, L, seed=1, device=dev)
+    M, M_lo, P, O_on = mc.alloc_prefill(d, dev, online=True)
+    Y = torch.empty((B, H, L, dv), dtype=torch.bfloat16, device=dev)
+    ws = mc.workspace(d, mc.MC_OP_GRM, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def scan():
+        mc.mc_scan_prefill_swla(d, None, g["alpha"], g["beta"], g["lam"], inp["Q"], inp["K"],
+                                inp["V"], inp["X"], M, M_lo, P, O_on, stream=stream)
+
+    def read():
+        mc.mc_grm_readout(d, inp["Q"], None, None, inp["U"], inp["X"], M, M_lo, P, O_on, Y,
+                          None, ws=ws, stream=stream)
+    for _ in range(args.warmup):
+        scan()
+        read()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        scan()
+        e[1].record(stream)
+        read()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    scan_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    read_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    fl_read = readout_flops(B, H, L, C, dk, dv, dg, online=False)
+    tf = fl_read / (read_ms / 1e3) / 1e12
+    NS = -(-L // C)
+    # scan bytes: Q, K, V (bf16) and the three gates read; O_on (fp32), the states (fp32 and
+    # bf16) and the means written; X read once for the means
+    sbytes = B * H * L * (2 * dk * 2 + 2 * dv + 3 * 4 + 4 * dv) + B * H * NS * dv * dk * 6 + \
+        B * L * dg * 2 + B * NS * dg * 4
+    gbs = sbytes / (scan_ms / 1e3) / 1e9
+    rec["swla"] = {
+        "workload": "grm_bf16_L64K shape with the SWLA memory (window 2, per-token decay and "
+                    "window weights)",
+        "metric": "prefill tokens/s", "value": round(B * L / (ms / 1e3), 1), "unit": "tokens/s",
+        "ms_per_step": round(ms, 4),
+        "steps_timed": "mc_scan_prefill_swla + mc_grm_readout (online read from the scan)",
+        "kernels_ms": {"mc_scan_prefill_swla": round(scan_ms, 4),
+                       "mc_grm_readout": round(read_ms, 4)},
+        "roofline": {"kernel": "mc_grm_readout", "bound": "mfma", "achieved": round(tf, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "algorithmic_flops": fl_read},
+        "scan_roofline": {"kernel": "mc_scan_prefill_swla", "bound": "hbm",
+                          "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": sbytes}}
+    del inp, g, M, M_lo, P, O_on, Y, ws
     torch.cuda.empty_cache()
 
 

@@ -29,7 +29,7 @@ MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE = 0, 1, 2, 3
 
 EXPORTED = ["mc_abi_version", "mc_status_str", "mc_workspace_bytes", "mc_scan_prefill",
             "mc_grm_readout", "mc_ssc_readout", "mc_decode_step", "mc_scan_prefill_segs",
-            "mc_grm_readout_segs"]
+            "mc_grm_readout_segs", "mc_scan_prefill_swla"]
 MC_MAX_SEGS = 512
 
 
@@ -74,6 +74,9 @@ def load(path: str = LIB_PATH):
         lib.mc_grm_readout_segs.restype = ctypes.c_int
         lib.mc_grm_readout_segs.argtypes = [D, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
                                             ctypes.c_size_t, P]
+        lib.mc_scan_prefill_swla.restype = ctypes.c_int
+        lib.mc_scan_prefill_swla.argtypes = [D, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
+                                             P, P]
         lib.mc_decode_step.restype = ctypes.c_int
         lib.mc_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P,
                                        ctypes.c_size_t, P]
@@ -178,6 +181,20 @@ def mc_grm_readout_segs(dims, seg_off, Q, U, X, M, M_lo, P, O_on, Y, gamma=None,
            "mc_grm_readout_segs")
 
 
+def mc_scan_prefill_swla(dims, seg_off, alpha, beta, lam, Q, K, V, X, M, M_lo, P, O_on,
+                         stream=None):
+    """SWLA write path (window 2).  seg_off None = segments of dims.seg_len; alpha, beta, lam
+    are [B,H,L] fp32 device tensors."""
+    if seg_off is None:
+        off, n = None, 0
+    else:
+        off, n = _offsets(seg_off)
+    _check(load().mc_scan_prefill_swla(ctypes.byref(dims), None if off is None else off.ctypes.data,
+                                       n, _p(alpha), _p(beta), _p(lam), _p(Q), _p(K), _p(V),
+                                       _p(X), _p(M), _p(M_lo), _p(P), _p(O_on), _stream(stream)),
+           "mc_scan_prefill_swla")
+
+
 def mc_decode_step(dims, q, k, v, u, x, M_on, xsum_on, count_on, M_cache, P_cache, n_cached,
                    n_cap, y, ws=None, stream=None):
     """count_on and n_cached are one-element int32 numpy arrays, updated in place.  u=None
@@ -252,6 +269,34 @@ def prefill_grm_segs(dims, seg_off, Q, K, V, U, X, want_gamma=False, stream=None
                     device=dev) if want_gamma else None
     ws = workspace(dims, MC_OP_GRM, device=dev)
     mc_grm_readout_segs(dims, seg_off, Q, U, X, M, M_lo, P, O_on, Y, G, ws=ws, stream=stream)
+    out = {"Y": Y, "M": M, "M_lo": M_lo, "P": P, "O_on": O_on}
+    if want_gamma:
+        out["gamma"] = G
+    return out
+
+
+def prefill_grm_swla(dims, alpha, beta, lam, Q, K, V, U, X, seg_off=None, want_gamma=False,
+                     stream=None):
+    """SWLA scan + GRM read (constant segments, or the given offsets) with fresh outputs."""
+    import torch
+    dev = Q.device
+    NS = (len(seg_off) - 1) if seg_off is not None else (dims.L + dims.seg_len - 1) // dims.seg_len
+    M = torch.empty((dims.B, dims.H, NS, dims.d_v, dims.d_k), dtype=torch.float32, device=dev)
+    M_lo = torch.empty((dims.B, dims.H, NS, dims.d_v, dims.d_k), dtype=torch.bfloat16,
+                       device=dev)
+    P = torch.empty((dims.B, dims.x_heads, NS, dims.d_g), dtype=torch.float32, device=dev)
+    O_on = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch.float32, device=dev)
+    mc_scan_prefill_swla(dims, seg_off, alpha, beta, lam, Q, K, V, X, M, M_lo, P, O_on,
+                         stream=stream)
+    Y = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch_dtype(dims), device=dev)
+    G = torch.empty((dims.B, dims.H, dims.L, NS), dtype=torch.float32,
+                    device=dev) if want_gamma else None
+    ws = workspace(dims, MC_OP_GRM, device=dev)
+    if seg_off is None:
+        mc_grm_readout(dims, Q, None, None, U, X, M, M_lo, P, O_on, Y, G, ws=ws, stream=stream)
+    else:
+        mc_grm_readout_segs(dims, seg_off, Q, U, X, M, M_lo, P, O_on, Y, G, ws=ws,
+                            stream=stream)
     out = {"Y": Y, "M": M, "M_lo": M_lo, "P": P, "O_on": O_on}
     if want_gamma:
         out["gamma"] = G

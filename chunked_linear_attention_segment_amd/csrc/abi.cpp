@@ -268,6 +268,29 @@ mc_status mc_grm_readout_segs(const mc_dims* d, const int32_t* seg_off, int32_t 
                : MC_OK;
 }
 
+mc_status mc_scan_prefill_swla(const mc_dims* d, const int32_t* seg_off, int32_t n_seg,
+                               const float* alpha, const float* beta, const float* lambda,
+                               const void* Q, const void* K, const void* V, const void* X,
+                               float* M, uint16_t* M_lo, float* P, float* O_on, void* stream) {
+    mc_status st = check_dims(d, true);
+    if (st != MC_OK) return st;
+    SegArg sg{};
+    if (seg_off && (st = check_segs(d, seg_off, n_seg, &sg)) != MC_OK) return st;
+    if (!alpha || !beta || !lambda || !Q || !K || !V || !X || !M || !P || !O_on)
+        return MC_ERR_NULL;
+    if (d->dtype == MC_BF16 && !M_lo) return MC_ERR_NULL;
+    const void* ptrs[] = {alpha, beta, lambda, Q, K, V, X, M, M_lo, P, O_on};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MC_ERR_ALIGN;
+    SwlaGates gt;
+    gt.alpha = alpha;
+    gt.beta = beta;
+    gt.lam = lambda;
+    return launch_scan_prefill_swla(*d, sg, gt, Q, K, V, X, M, M_lo, P, O_on, stream)
+               ? MC_ERR_HIP
+               : MC_OK;
+}
+
 mc_status mc_decode_step(const mc_dims* d, const void* q, const void* k, const void* v,
                          const void* u, const void* x, float* M_on, float* xsum_on,
                          int32_t* count_on, void* M_cache, float* P_cache, int32_t* n_cached,

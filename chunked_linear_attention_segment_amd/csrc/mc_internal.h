@@ -65,6 +65,16 @@ struct SegArg {
     int32_t off[MC_MAX_SEGS + 1];
 };
 
+// SWLA gates ([B,H,L] fp32 each, device): alpha == nullptr means the linear-attention update.
+struct SwlaGates {
+    const float* alpha = nullptr;
+    const float* beta = nullptr;
+    const float* lam = nullptr;
+};
+int launch_scan_prefill_swla(const mc_dims& d, const SegArg& sg, const SwlaGates& gt,
+                             const void* Q, const void* K, const void* V, const void* X,
+                             float* M, uint16_t* M_lo, float* P, float* O_on, void* stream);
+
 int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
                              const void* V, const void* X, float* M, uint16_t* M_lo, float* P,
                              float* O_on, void* stream);

@@ -5,6 +5,9 @@
 // M_t = M_{t-1} + v_t phi(k_t)^T (the linear-attention update of §2, Eq. 2); the state after
 // the segment's last token is cached.  The online read M_t^(s) phi(q_t) (§3.1, Eq. 6/8) is
 // taken after token t has updated the memory.  MeanPooling(S^(i)) (§3.1, Eq. 10) averages X.
+// With SWLA gates (the paper's sliding-window linear attention with window 2, Eq. 28) the
+// update is M_t = alpha_t M_{t-1} + beta_t v_{t-1} phi(k_{t-1})^T + lam_t v_t phi(k_t)^T,
+// the previous token taken only from the same segment.
 #include "common.cuh"
 #include "mc_internal.h"
 
@@ -14,20 +17,21 @@ namespace mc {
 // `tid` owns row c = tid / TPR and the CPT consecutive columns starting at (tid % TPR) * CPT.
 // Tokens are staged TT at a time in LDS (phi applied on load); each token updates the state
 // and then reads it with phi(q_t) -- the read is reduced over the TPR threads of a row.
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, bool SW>
 __global__ __launch_bounds__(256) void scan_valu_kernel(const T* __restrict__ Q,
                                                         const T* __restrict__ K,
                                                         const T* __restrict__ V, int L, int C,
                                                         int NS, int phi, float* __restrict__ M,
                                                         bf16_t* __restrict__ M_lo,
                                                         float* __restrict__ O_on,
-                                                        const SegArg sg) {
+                                                        const SegArg sg, SwlaGates gt) {
     constexpr int TPR = 256 / DV;
     constexpr int CPT = DK / TPR;
     constexpr int TT = 32;
     __shared__ float sk[TT][DK];
     __shared__ float sq[TT][DK];
     __shared__ float sv[TT][DV];
+    __shared__ float sga[SW ? TT : 1], sgb[SW ? TT : 1], sgl[SW ? TT : 1];
 
     const int s = blockIdx.x;
     const size_t bh = blockIdx.y;
@@ -38,8 +42,12 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const T* __restrict__ Q,
     const int r0 = (tid % TPR) * CPT;
 
     float m[CPT];
+    float kp[SW ? CPT : 1];  // SWLA: phi(k) and v of the previous token of the segment
+    float vp = 0.f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) m[i] = 0.f;
+#pragma unroll
+    for (int i = 0; i < (SW ? CPT : 1); ++i) kp[i] = 0.f;
 
     const size_t kbase = (bh * L + t0) * DK;
     const size_t vbase = (bh * L + t0) * DV;
@@ -51,14 +59,33 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const T* __restrict__ Q,
             sq[e / DK][e % DK] = feature(ld(Q, kbase + (size_t)j0 * DK + e), phi);
         }
         for (int e = tid; e < n * DV; e += 256) sv[e / DV][e % DV] = ld(V, vbase + (size_t)j0 * DV + e);
+        if (SW && tid < n) {
+            const size_t gi = bh * L + t0 + j0 + tid;
+            sga[tid] = gt.alpha[gi];
+            sgb[tid] = gt.beta[gi];
+            sgl[tid] = gt.lam[gi];
+        }
         __syncthreads();
         for (int j = 0; j < n; ++j) {
             const float vc = sv[j][c];
             float acc = 0.f;
+            if (SW) {
+                // the segment's first token has no previous token: vp and kp are still zero
+                const float al = sga[j], bv = sgb[j] * vp, lv = sgl[j] * vc;
 #pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                m[i] += vc * sk[j][r0 + i];
-                acc += m[i] * sq[j][r0 + i];
+                for (int i = 0; i < CPT; ++i) {
+                    const float kc = sk[j][r0 + i];
+                    m[i] = al * m[i] + bv * kp[i] + lv * kc;
+                    kp[i] = kc;
+                    acc += m[i] * sq[j][r0 + i];
+                }
+                vp = vc;
+            } else {
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) {
+                    m[i] += vc * sk[j][r0 + i];
+                    acc += m[i] * sq[j][r0 + i];
+                }
             }
             acc = warp_sum(acc, TPR);
             if (O_on && tid % TPR == 0) O_on[(bh * L + t0 + j0 + j) * DV + c] = acc;
@@ -110,26 +137,33 @@ __global__ __launch_bounds__(256) void seg_means_kernel(const T* __restrict__ X,
 
 static const SegArg kConstSeg{};  // constant segment length
 
+static const SwlaGates kNoGates{};
+
 template <typename T, int DK, int DV>
 static int launch_scan_t(const mc_dims& d, const void* Q, const void* K, const void* V,
                          float* M, uint16_t* M_lo, float* O_on, const SegArg& sg,
-                         hipStream_t st) {
+                         const SwlaGates& gt, hipStream_t st) {
     const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
     dim3 grid(NS, d.B * d.H);
-    hipLaunchKernelGGL((scan_valu_kernel<T, DK, DV>), grid, dim3(256), 0, st, (const T*)Q,
-                       (const T*)K, (const T*)V, d.L, d.seg_len, NS, d.phi, M, (bf16_t*)M_lo,
-                       O_on, sg);
+    if (gt.alpha)
+        hipLaunchKernelGGL((scan_valu_kernel<T, DK, DV, true>), grid, dim3(256), 0, st,
+                           (const T*)Q, (const T*)K, (const T*)V, d.L, d.seg_len, NS, d.phi, M,
+                           (bf16_t*)M_lo, O_on, sg, gt);
+    else
+        hipLaunchKernelGGL((scan_valu_kernel<T, DK, DV, false>), grid, dim3(256), 0, st,
+                           (const T*)Q, (const T*)K, (const T*)V, d.L, d.seg_len, NS, d.phi, M,
+                           (bf16_t*)M_lo, O_on, sg, gt);
     return (int)hipGetLastError();
 }
 
 template <typename T>
 static int launch_scan_dt(const mc_dims& d, const void* Q, const void* K, const void* V,
                           float* M, uint16_t* M_lo, float* O_on, const SegArg& sg,
-                          hipStream_t st) {
-    if (d.d_k == 128 && d.d_v == 128) return launch_scan_t<T, 128, 128>(d, Q, K, V, M, M_lo, O_on, sg, st);
-    if (d.d_k == 128 && d.d_v == 64) return launch_scan_t<T, 128, 64>(d, Q, K, V, M, M_lo, O_on, sg, st);
-    if (d.d_k == 64 && d.d_v == 128) return launch_scan_t<T, 64, 128>(d, Q, K, V, M, M_lo, O_on, sg, st);
-    return launch_scan_t<T, 64, 64>(d, Q, K, V, M, M_lo, O_on, sg, st);
+                          hipStream_t st, const SwlaGates& gt = kNoGates) {
+    if (d.d_k == 128 && d.d_v == 128) return launch_scan_t<T, 128, 128>(d, Q, K, V, M, M_lo, O_on, sg, gt, st);
+    if (d.d_k == 128 && d.d_v == 64) return launch_scan_t<T, 128, 64>(d, Q, K, V, M, M_lo, O_on, sg, gt, st);
+    if (d.d_k == 64 && d.d_v == 128) return launch_scan_t<T, 64, 128>(d, Q, K, V, M, M_lo, O_on, sg, gt, st);
+    return launch_scan_t<T, 64, 64>(d, Q, K, V, M, M_lo, O_on, sg, gt, st);
 }
 
 int launch_scan_online(const mc_dims& d, const void* Q, const void* K, const void* V,
@@ -162,14 +196,33 @@ int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, 
 }
 
 int launch_scan_mfma(const mc_dims& d, const void* Q, const void* K, const void* V, float* M,
-                     uint16_t* M_lo, float* O_on, void* stream);
+                     uint16_t* M_lo, float* O_on, const SwlaGates& gt, void* stream);
+
+// SWLA write path: the MFMA scan for constant-length bf16 segments of width 64/128, the
+// generic scan otherwise (and for any offsets), then the means.
+int launch_scan_prefill_swla(const mc_dims& d, const SegArg& sg, const SwlaGates& gt,
+                             const void* Q, const void* K, const void* V, const void* X,
+                             float* M, uint16_t* M_lo, float* P, float* O_on, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    int rc = -1;
+    if (!sg.n && d.dtype == MC_BF16) rc = launch_scan_mfma(d, Q, K, V, M, M_lo, O_on, gt, stream);
+    if (rc >= 0) {
+        if (rc) return rc;
+    } else if (d.dtype == MC_BF16)
+        rc = launch_scan_dt<bf16_t>(d, Q, K, V, M, M_lo, O_on, sg, st, gt);
+    else
+        rc = launch_scan_dt<float>(d, Q, K, V, M, M_lo, O_on, sg, st, gt);
+    if (rc) return rc;
+    return d.dtype == MC_BF16 ? launch_means<bf16_t>(d, X, P, sg, st)
+                              : launch_means<float>(d, X, P, sg, st);
+}
 
 int launch_scan_prefill(const mc_dims& d, const void* Q, const void* K, const void* V,
                         const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,
                         void* stream) {
     hipStream_t st = (hipStream_t)stream;
     int rc = -1;
-    if (d.dtype == MC_BF16) rc = launch_scan_mfma(d, Q, K, V, M, M_lo, O_on, stream);
+    if (d.dtype == MC_BF16) rc = launch_scan_mfma(d, Q, K, V, M, M_lo, O_on, kNoGates, stream);
     if (rc >= 0) {
         if (rc) return rc;
     } else if (d.dtype == MC_BF16)

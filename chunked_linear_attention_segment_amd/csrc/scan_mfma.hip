@@ -16,6 +16,21 @@
 // phi(q) operand, so no shuffle is needed.  phi(k) and v are staged transposed in LDS (the
 // token index is the contraction index of the state update); the causal score block
 // S^T[r][t] = phi(k_r) . phi(q_t) goes through LDS as bf16.
+//
+// SW = true: the SWLA memory of window 2 (the paper's sliding-window linear attention,
+// Eq. 28): M_t = alpha_t M_{t-1} + beta_t v_{t-1} phi(k_{t-1})^T + lam_t v_t phi(k_t)^T, the
+// previous token taken only inside the segment.  Unrolled, the weight of v_r phi(k_r)^T in
+// M_t (r <= t, same segment) is
+//     c[t][r] = lam_t                                       (r = t)
+//     c[t][r] = (alpha_{r+1} lam_r + beta_{r+1}) * alpha_{r+2} ... alpha_t   (r < t).
+// The register state between chunks is Z = alpha_{j0} M_{j0-1} + beta_{j0} v_{j0-1} k_{j0-1}^T
+// (the memory at the chunk's first token minus that token's own write), so inside the chunk
+//     M_t = (alpha_{j0+1} ... alpha_t) Z + sum_{j0 <= r <= t} c[t][r] v_r phi(k_r)^T.
+// Per chunk the weights c[t][r] are formed in LDS as running products down each column
+// (exact for any alpha, zeros included); the online read scales the Z term per token and the
+// scores by c[t][r], and the state update scales Z and weights each key with its final
+// coefficient: c[e][r] at the segment's end e, else that of Z at the next chunk's first
+// token, alpha_{e+1} c[e][r] (+ beta_{e+1} for r = e).
 #include "common.cuh"
 #include "mc_internal.h"
 
@@ -50,17 +65,21 @@ __device__ __forceinline__ u32x2_t phi4(u32x2_t v, int phi) {
 constexpr int CH = 64;    // tokens per chunk
 constexpr int TPAD = 72;  // row stride (elements) of the token-indexed LDS tiles
 
-template <int DK, int DV, bool ON>
+template <int DK, int DV, bool ON, bool SW>
 __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     int L, int C, int NS, int phi, float* __restrict__ M, bf16_t* __restrict__ M_lo,
-    float* __restrict__ O_on) {
+    float* __restrict__ O_on, SwlaGates gt) {
     constexpr int NT = DV * 2;      // threads: one wave per 32 value rows
     constexpr int DB = DK / 32;     // 32-row blocks of d
     constexpr int KSD = DK / 16;    // k-steps over d
+    constexpr int GW = SW ? CH : 1; // SWLA tables (1-element placeholders otherwise)
     __shared__ __attribute__((aligned(16))) bf16_t kt[DK][TPAD];  // phi(k)^T  [d][r]
     __shared__ __attribute__((aligned(16))) bf16_t vt[DV][TPAD];  // v^T       [cv][r]
     __shared__ __attribute__((aligned(16))) bf16_t sc[CH][TPAD];  // masked scores [t][r]
+    __shared__ float cf[GW][GW + 1];  // SWLA weights c[t][r] of the chunk
+    __shared__ float dz[GW];          // SWLA decay of Z at chunk token t: alpha_{j0+1..j0+t}
+    __shared__ float ga[GW + 1], gb[GW + 1], gl[GW];  // the chunk's gates (+ next token's)
 
     const int s = blockIdx.x;
     const size_t bh = blockIdx.y;
@@ -80,8 +99,41 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
     const bf16_t* Ks = K + (bh * L + t0) * DK;
     const bf16_t* Vs = V + (bh * L + t0) * DV;
 
+    const size_t gbase = bh * L + t0;
     for (int j0 = 0; j0 < len; j0 += CH) {
         const int n = min(CH, len - j0);
+        const bool last = j0 + n == len;  // the segment ends in this chunk
+        if (SW) {
+            // gates of the chunk's tokens, zero past its end; slot CH is the next token's
+            if (tid <= CH) {
+                const bool in = j0 + tid < len && tid <= n;
+                ga[tid] = in ? gt.alpha[gbase + j0 + tid] : 0.f;
+                gb[tid] = in ? gt.beta[gbase + j0 + tid] : 0.f;
+                if (tid < CH) gl[tid] = in && tid < n ? gt.lam[gbase + j0 + tid] : 0.f;
+            }
+            __syncthreads();
+            if (tid < CH) {  // column r: c[r][r] = lam_r, then a running product down t
+                const int r = tid;
+                float c = gl[r];
+                cf[r][r] = c;
+                if (r + 1 < CH) {
+                    c = ga[r + 1] * gl[r] + gb[r + 1];
+                    cf[r + 1][r] = c;
+                    for (int t = r + 2; t < CH; ++t) {
+                        c *= ga[t];
+                        cf[t][r] = c;
+                    }
+                }
+            } else if (tid == CH) {
+                float p = 1.f;
+                dz[0] = p;
+                for (int t = 1; t < CH; ++t) {
+                    p *= ga[t];
+                    dz[t] = p;
+                }
+            }
+            __syncthreads();
+        }
         // ---- phi(q) B-fragments (k order of the accumulator rows) for both token blocks ----
         u32x4_t qb[2][KSD];
         f32x16_t ot[2];
@@ -111,8 +163,19 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
                 for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
                     for (int tb = 0; tb < 2; ++tb) ot[tb] = scan_mfma(ma[ks], qb[tb][ks], ot[tb]);
+                if (SW) {  // Z decays by alpha_{j0+1} .. alpha_t before token t reads it
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb) ot[tb] *= dz[tb * 32 + l32];
+                }
             }
         }
+        // SWLA: final weight of each key of the chunk in the state carried out of it
+        float zs = 1.f;  // and the factor on the incoming Z
+        if (SW) zs = last ? dz[n - 1] : ga[CH] * dz[CH - 1];
+        auto key_weight = [&](int r) -> float {
+            if (r >= n) return 0.f;
+            return last ? cf[n - 1][r] : ga[CH] * cf[CH - 1][r] + (r == CH - 1 ? gb[CH] : 0.f);
+        };
         // ---- stage phi(k)^T and v^T (token pairs packed in 32-bit LDS words) ----
         for (int it = tid; it < (CH / 2) * (DK / 8); it += NT) {
             const int p = it % (CH / 2), dc = (it / (CH / 2)) * 8;
@@ -129,6 +192,13 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
                     a1 = r0 < n ? feature(a1, 1) : 0.f;
                     b0 = r1 < n ? feature(b0, 1) : 0.f;
                     b1 = r1 < n ? feature(b1, 1) : 0.f;
+                }
+                if (SW) {
+                    const float w0 = key_weight(r0), w1 = key_weight(r1);
+                    a0 *= w0;
+                    a1 *= w0;
+                    b0 *= w1;
+                    b1 *= w1;
                 }
                 *reinterpret_cast<uint32_t*>(&kt[dc + 2 * e][r0]) = pk2(a0, b0);
                 *reinterpret_cast<uint32_t*>(&kt[dc + 2 * e + 1][r0]) = pk2(a1, b1);
@@ -176,6 +246,12 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
                 float v1 = (r + 1 <= t) ? sacc[4 * g + 1] : 0.f;
                 float v2 = (r + 2 <= t) ? sacc[4 * g + 2] : 0.f;
                 float v3 = (r + 3 <= t) ? sacc[4 * g + 3] : 0.f;
+                if (SW) {
+                    v0 = (r + 0 <= t) ? v0 * cf[t][r + 0] : 0.f;
+                    v1 = (r + 1 <= t) ? v1 * cf[t][r + 1] : 0.f;
+                    v2 = (r + 2 <= t) ? v2 * cf[t][r + 2] : 0.f;
+                    v3 = (r + 3 <= t) ? v3 * cf[t][r + 3] : 0.f;
+                }
                 *reinterpret_cast<u32x2_t*>(&sc[t][r]) = u32x2_t{pk2(v0, v1), pk2(v2, v3)};
             }
         }
@@ -198,6 +274,7 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             const int d = db * 32 + l32;
+            if (SW) mt[db] *= zs;
 #pragma unroll
             for (int ks = 0; ks < CH / 16; ++ks) {
                 const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(&kt[d][ks * 16 + half * 8]);
@@ -245,28 +322,37 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
 
 template <int DK, int DV>
 static int launch_scan_mfma_t(const mc_dims& d, const void* Q, const void* K, const void* V,
-                              float* M, uint16_t* M_lo, float* O_on, hipStream_t st) {
+                              float* M, uint16_t* M_lo, float* O_on, const SwlaGates& gt,
+                              hipStream_t st) {
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
-    if (O_on)
-        hipLaunchKernelGGL((scan_mfma_kernel<DK, DV, true>), dim3(NS, d.B * d.H), dim3(DV * 2),
-                           0, st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, d.L,
-                           d.seg_len, NS, d.phi, M, (bf16_t*)M_lo, O_on);
-    else
-        hipLaunchKernelGGL((scan_mfma_kernel<DK, DV, false>), dim3(NS, d.B * d.H), dim3(DV * 2),
-                           0, st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, d.L,
-                           d.seg_len, NS, d.phi, M, (bf16_t*)M_lo, O_on);
+#define MC_SCAN(ON, SW)                                                                        \
+    hipLaunchKernelGGL((scan_mfma_kernel<DK, DV, ON, SW>), dim3(NS, d.B * d.H), dim3(DV * 2),   \
+                       0, st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, d.L,        \
+                       d.seg_len, NS, d.phi, M, (bf16_t*)M_lo, O_on, gt)
+    if (gt.alpha) {  // SWLA: the read takes the online term from O_on, so it is always written
+        if (!O_on) return (int)hipErrorInvalidValue;
+        MC_SCAN(true, true);
+    } else if (O_on) {
+        MC_SCAN(true, false);
+    } else {
+        MC_SCAN(false, false);
+    }
+#undef MC_SCAN
     return (int)hipGetLastError();
 }
 
 // bf16 scan on MFMA; -1 when the sizes are not covered (the caller uses the generic kernel).
 int launch_scan_mfma(const mc_dims& d, const void* Q, const void* K, const void* V, float* M,
-                     uint16_t* M_lo, float* O_on, void* stream) {
+                     uint16_t* M_lo, float* O_on, const SwlaGates& gt, void* stream) {
     if (d.dtype != MC_BF16 || !M_lo) return -1;
     hipStream_t st = (hipStream_t)stream;
-    if (d.d_k == 128 && d.d_v == 128) return launch_scan_mfma_t<128, 128>(d, Q, K, V, M, M_lo, O_on, st);
-    if (d.d_k == 128 && d.d_v == 64) return launch_scan_mfma_t<128, 64>(d, Q, K, V, M, M_lo, O_on, st);
-    if (d.d_k == 64 && d.d_v == 128) return launch_scan_mfma_t<64, 128>(d, Q, K, V, M, M_lo, O_on, st);
-    if (d.d_k == 64 && d.d_v == 64) return launch_scan_mfma_t<64, 64>(d, Q, K, V, M, M_lo, O_on, st);
+#define MC_SD(DK, DV)                                                                          \
+    if (d.d_k == DK && d.d_v == DV) return launch_scan_mfma_t<DK, DV>(d, Q, K, V, M, M_lo, O_on, gt, st);
+    MC_SD(128, 128)
+    MC_SD(128, 64)
+    MC_SD(64, 128)
+    MC_SD(64, 64)
+#undef MC_SD
     return -1;
 }
 

@@ -249,3 +249,33 @@ def make_decode_device(w: Workload, seed: int = 0, device="cuda", n_cap: int | N
     return {"q": q.to(dt), "k": k.to(dt), "v": v.to(dt), "u": u.to(dt), "x": x.to(dt),
             "M_on": M_on.contiguous(), "xsum": xsum.contiguous(), "count": cnt,
             "M_cache": Mc, "P_cache": Pc, "n_cached": n, "n_cap": cap}
+
+
+# SWLA gates (the Memory Caching paper's sliding-window linear attention, window 2): the
+# decay alpha_t and the window weights beta_t (previous token) and lam_t (current token), one
+# value per token per head.  The pages do not say how a model forms them; uniform draws with
+# a decay close to 1 (a long horizon) and window weights of either sign around 1 stand in.
+SWLA_RANGES = {"alpha": (0.9, 1.0), "beta": (-0.5, 1.0), "lam": (0.25, 1.25)}
+
+
+def make_swla_gates(B: int, H: int, L: int, seed: int = 0, ranges=None) -> dict:
+    """alpha, beta, lam [B,H,L] float32 (host draw, numpy PCG64)."""
+    rg = dict(SWLA_RANGES, **(ranges or {}))
+    rng = np.random.default_rng(seed)
+    return {k: rng.uniform(rg[k][0], rg[k][1], (B, H, L)).astype(np.float32)
+            for k in ("alpha", "beta", "lam")}
+
+
+def make_swla_gates_device(B: int, H: int, L: int, seed: int = 0, device="cuda",
+                           ranges=None) -> dict:
+    """The same gates drawn on the device with a seeded torch generator (full sizes)."""
+    import torch
+    rg = dict(SWLA_RANGES, **(ranges or {}))
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = {}
+    for k in ("alpha", "beta", "lam"):
+        lo, hi = rg[k]
+        out[k] = torch.rand((B, H, L), generator=g, device=device, dtype=torch.float32) * \
+            (hi - lo) + lo
+    return out

@@ -208,6 +208,32 @@ mc_status mc_grm_readout_segs(const mc_dims* dims, const int32_t* seg_off, int32
                               const uint16_t* M_lo, const float* P, const float* O_on, void* Y,
                               float* gamma, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * SWLA memory under Memory Caching (Memory Caching paper, the sliding-window linear
+ * attention paragraph: Eq. 26 with window c = 2, i.e. Eq. 28 for the segment memories and
+ * Eq. 29 for the read).  The write path with the update
+ *     M_t = alpha_t M_{t-1} + beta_t v_{t-1} phi(k_{t-1})^T + lambda_t v_t phi(k_t)^T
+ * in place of the linear-attention one.  The window stays inside the segment: a segment's
+ * first token has no previous token to write, its memory starting from zero (Eq. 4b).  The
+ * read is unchanged (Eq. 29): pass the O_on written here to mc_grm_readout (constant
+ * segments) or mc_grm_readout_segs (offsets), or to mc_ssc_readout.
+ *
+ *   seg_off, n_seg  NULL for segments of dims->seg_len; else host offsets as for
+ *                   mc_scan_prefill_segs.
+ *   alpha, beta, lambda  [B,H,L] fp32 device arrays: the decay and the two window weights of
+ *                   every token of every head (any finite values; alpha = 1, beta = 0,
+ *                   lambda = 1 is the linear-attention memory).
+ *   Q, K, V, X, M, M_lo, P  as for mc_scan_prefill.
+ *   O_on     out [B,H,L,d_v] fp32, required: the online read M_t^(s) phi(q_t); the gated
+ *            read cannot form a decayed online term itself.
+ *   Constant bf16 segments with d_k, d_v in {64, 128} run on MFMA; everything else on the
+ *   fp32-accumulating kernels.  Errors as mc_scan_prefill and mc_scan_prefill_segs.
+ */
+mc_status mc_scan_prefill_swla(const mc_dims* dims, const int32_t* seg_off, int32_t n_seg,
+                               const float* alpha, const float* beta, const float* lambda,
+                               const void* Q, const void* K, const void* V, const void* X,
+                               float* M, uint16_t* M_lo, float* P, float* O_on, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -209,3 +209,30 @@ def test_segment_offsets_are_validated():
     assert read(good, O_on=None) == mc.MC_ERR_NULL        # the read takes the scan's O_on
     assert read(good, ws_bytes=ws - 1) == mc.MC_ERR_WORKSPACE
     assert read(good, Y=MIS) == mc.MC_ERR_ALIGN
+
+
+def test_swla_scan_arguments():
+    # SWLA write path: gates and O_on required, offsets optional and validated like the
+    # segment-offset calls; every check happens before any HIP call
+    d = dims(L=1000)
+    lib = mc.load()
+
+    def scan(off=None, **kw):
+        p = dict(alpha=A, beta=A, lam=A, Q=A, K=A, V=A, X=A, M=A, M_lo=A, P=A, O_on=A)
+        p.update(kw)
+        o = None if off is None else np.ascontiguousarray(np.asarray(off, dtype=np.int32))
+        return lib.mc_scan_prefill_swla(ctypes.byref(d), None if o is None else o.ctypes.data,
+                                        0 if o is None else o.shape[0] - 1, p["alpha"],
+                                        p["beta"], p["lam"], p["Q"], p["K"], p["V"], p["X"],
+                                        p["M"], p["M_lo"], p["P"], p["O_on"], None)
+    for g in ("alpha", "beta", "lam", "O_on", "Q", "M"):
+        assert scan(**{g: None}) == mc.MC_ERR_NULL, g
+    assert scan(M_lo=None) == mc.MC_ERR_NULL
+    assert scan(beta=MIS) == mc.MC_ERR_ALIGN
+    assert scan([0, 400, 400, 1000]) == mc.MC_ERR_DIMS
+    assert scan([0, 400, 999]) == mc.MC_ERR_DIMS
+    assert scan(list(range(0, 1000)) + [1000]) == mc.MC_ERR_UNSUPPORTED
+    bad = dims(L=1000)
+    bad.seg_len = 0
+    assert lib.mc_scan_prefill_swla(ctypes.byref(bad), None, 0, A, A, A, A, A, A, A, A, A, A,
+                                    A, None) == mc.MC_ERR_DIMS

@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 from chunked_linear_attention_segment_amd.inputs import (WORKLOADS, make_decode_device,
-                                                         make_prefill_device)
+                                                         make_prefill_device,
+                                                         make_swla_gates_device)
 from mcutil import TOL, announce, slice_rel_err, to_np
 
 pytestmark = pytest.mark.gpu
@@ -164,3 +165,34 @@ def test_log_segments_full_size():
                 "P": slice_rel_err(to_np(out["P"][b:b + 1]), ref["P"])}
         announce("  (b=%d, h=%d) %d rows: %s" % (b, h, len(rows), errs))
         assert errs["Y"] <= TOL["bf16"] and errs["M"] <= 1e-4 and errs["P"] <= 1e-4
+
+
+def test_swla_full_size():
+    # SWLA memory at the L=64K workload's shape (C = 512), as the benchmark times it:
+    # mc_scan_prefill_swla (MFMA scan) + mc_grm_readout with the scan's online read
+    w = WORKLOADS["grm_bf16_L64K"]
+    announce("full-size SWLA: H=%d L=%d C=%d" % (w.H, w.L, w.seg_len))
+    inp = make_prefill_device(w, seed=0)
+    g = make_swla_gates_device(w.B, w.H, w.L, seed=1)
+    d = mc.make_dims(w.B, w.H, w.L, w.d_k, w.d_v, w.d_g, w.seg_len, 1, w.dtype, w.phi)
+    out = mc.prefill_grm_swla(d, g["alpha"], g["beta"], g["lam"], inp["Q"], inp["K"], inp["V"],
+                              inp["U"], inp["X"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(out["Y"].float()).all()
+    C = w.seg_len
+    rows = np.unique(np.concatenate([np.arange(C - 1, w.L, C), np.arange(0, w.L, C) + 63,
+                                     np.random.default_rng(12).integers(0, w.L, 200)])
+                     ).astype(np.int32)
+    for b, h in [(0, 0), (0, 23)]:
+        hin = _head(inp, b, h)
+        gates = tuple(g[k][b:b + 1, h:h + 1].double().cpu().numpy()
+                      for k in ("alpha", "beta", "lam"))
+        ref = oracle.prefill(hin["Q"], hin["K"], hin["V"], hin["U"], hin["X"], seg_len=C,
+                             phi=w.phi, rows=rows, want_states=True, swla=gates)
+        errs = {"Y": slice_rel_err(to_np(out["Y"][b:b + 1, h:h + 1, rows]), ref["Y"]),
+                "M": slice_rel_err(to_np(out["M"][b:b + 1, h:h + 1]), ref["M"]),
+                "P": slice_rel_err(to_np(out["P"][b:b + 1]), ref["P"])}
+        announce("  (b=%d, h=%d) %d rows: %s" % (b, h, len(rows), errs))
+        assert errs["Y"] <= TOL["bf16"] and errs["M"] <= TOL["bf16"] and errs["P"] <= 1e-4
+    del inp, out
+    torch.cuda.empty_cache()

@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 import oracle
-from chunked_linear_attention_segment_amd.inputs import WORKLOADS, Workload, make_prefill
+from chunked_linear_attention_segment_amd.inputs import (WORKLOADS, Workload, make_prefill,
+                                                         make_swla_gates)
 from mcutil import TOL, announce, slice_rel_err, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
@@ -332,6 +333,61 @@ def test_grm_segment_offsets(name):
     ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], seg_len=1,
                          phi=w.phi, mode="grm", want_states=True, want_online=True,
                          want_gamma=True, seg_offsets=off)
+    tol = TOL[w.dtype]
+    errs = {k: slice_rel_err(to_np(out[k]), ref[k]) for k in ("Y", "M", "P", "O_on", "gamma")}
+    announce("  errors %s" % errs)
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
+
+
+# SWLA memory (window 2) under GRM: the MFMA scan for constant bf16 segments, the generic scan
+# for fp32 and for offsets; the read takes the online term from O_on.
+SWLA_CASES = {
+    "bf16_d128_C256_L700": (Workload("x", 1, 3, 700, 128, 128, 128, 256, "identity", "bf16"),
+                            None, None),
+    "bf16_d64_C48_L300_elu": (Workload("x", 2, 2, 300, 64, 64, 64, 48, "elu1", "bf16"),
+                              None, None),
+    "bf16_d128_C128_strong_decay": (Workload("x", 1, 2, 512, 128, 128, 128, 128, "identity",
+                                             "bf16"), None, {"alpha": (0.0, 0.2)}),
+    "bf16_d128_C192_alpha_0_or_1": (Workload("x", 1, 2, 600, 128, 128, 64, 192, "identity",
+                                             "bf16"), None, "binary"),
+    "bf16_d128v64_C64_L200": (Workload("x", 1, 2, 200, 128, 64, 128, 64, "elu1", "bf16"),
+                              None, None),
+    "f32_d64_C64_L300": (Workload("x", 1, 2, 300, 64, 64, 64, 64, "identity", "f32"), None,
+                         None),
+    "bf16_log_L1000_d128": (Workload("x", 1, 2, 1000, 128, 128, 128, 1, "identity", "bf16"),
+                            "log", None),
+    "f32_random_L500_d128_xheadsH": (Workload("x", 1, 2, 500, 128, 128, 64, 1, "elu1", "f32",
+                                              x_heads=2), "random", None),
+}
+
+
+@pytest.mark.parametrize("name", list(SWLA_CASES))
+def test_swla_grm(name):
+    w, seg, gate_kind = SWLA_CASES[name]
+    off = None
+    if seg == "log":
+        off = oracle.log_segments(w.L)
+    elif seg == "random":
+        off = _random_offsets(w.L, 17, seed=9)
+    inp = make_prefill(w, seed=4)
+    B, H = inp["Q"].shape[:2]
+    if gate_kind == "binary":  # decay switched fully off or on, token by token
+        g = make_swla_gates(B, H, w.L, seed=6)
+        g["alpha"] = (g["alpha"] > 0.95).astype(np.float32)
+    else:
+        g = make_swla_gates(B, H, w.L, seed=6, ranges=gate_kind)
+    announce("swla %s: %s segments" % (name, "constant" if off is None else len(off) - 1))
+    d = _dims(w)
+    dev = {k: to_dev(v, w.dtype) for k, v in inp.items()}
+    gd = {k: to_dev(v) for k, v in g.items()}
+    out = mc.prefill_grm_swla(d, gd["alpha"], gd["beta"], gd["lam"], dev["Q"], dev["K"],
+                              dev["V"], dev["U"], dev["X"], seg_off=off, want_gamma=True)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], seg_len=w.seg_len,
+                         phi=w.phi, mode="grm", want_states=True, want_online=True,
+                         want_gamma=True, seg_offsets=off,
+                         swla=(g["alpha"], g["beta"], g["lam"]))
     tol = TOL[w.dtype]
     errs = {k: slice_rel_err(to_np(out[k]), ref[k]) for k in ("Y", "M", "P", "O_on", "gamma")}
     announce("  errors %s" % errs)
