@@ -417,6 +417,227 @@ int mco_decode_step(const int32_t* dims, int mode, const double* q, const double
     return MCO_OK;
 }
 
+/* derivative of phi ([MC] Eq. 2 feature map): 1, or 1 for z > 0 and e^z otherwise. */
+static double mco_dphi(double z, int phi) {
+    if (phi == 0) return 1.0;
+    return z > 0.0 ? 1.0 : exp(z);
+}
+
+/*
+ * Gradients of the GRM prefill with respect to its inputs: the chain rule applied to the
+ * per-token definitions ([MC] Eq. 4b memories, the Eq. 10 softmax gate, the Eq. 9 read),
+ * for an upstream gradient dY of Y.  With o_i = M^(i) phi(q_t) for the cached segments
+ * i < s and o_s = M_t^(s) phi(q_t) for the online one, y_t = sum_i g_i o_i and
+ *   dg_i = <dy_t, o_i>,  da_i = g_i (dg_i - sum_j g_j dg_j)          (softmax)
+ *   du_t = sum_{i<s} da_i P_i + da_s p_t        (p_t: prefix mean of x in segment s)
+ *   dP_i += da_i u_t,  dp_t = da_s u_t
+ *   dphi(q_t) = sum_{i<s} g_i M^(i)^T dy_t + g_s M_t^(s)^T dy_t
+ *   dM^(i) += g_i dy_t phi(q_t)^T  (i < s),  and for r <= t in segment s (the online memory
+ *   holds v_r phi(k_r)^T): dv_r += g_s <phi(q_t), phi(k_r)> dy_t,
+ *   dphi(k_r) += g_s <dy_t, v_r> phi(q_t).
+ * Then for r in segment i: dv_r += dM^(i) phi(k_r), dphi(k_r) += dM^(i)^T v_r,
+ * dx_r += dP_i / |S_i| + sum_{t >= r in segment i} dp_t / (j_t + 1); finally
+ * dq = dphi(q) phi'(q), dk = dphi(k) phi'(k).
+ *
+ * dims = {B, H, L, dk, dv, dg, C, xh, phi} (segments of constant length C).  Inputs as for
+ * mco_prefill; dY [B,H,L,dv].  Outputs dQ, dK [B,H,L,dk], dV [B,H,L,dv], dU [B,H,L,dg],
+ * dX [B,xh,L,dg] (with xh = 1 the heads' contributions are summed, in head order).
+ */
+int mco_grm_backward(const int32_t* dims, const double* Q, const double* K, const double* V,
+                     const double* U, const double* X, const double* dY, double* dQ,
+                     double* dK, double* dV, double* dU, double* dX, int n_threads) {
+    const int B = dims[0], H = dims[1], L = dims[2], dk = dims[3], dv = dims[4], dg = dims[5];
+    const int C = dims[6], xh = dims[7], phi = dims[8];
+    if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || dg <= 0 || C <= 0) return MCO_EARG;
+    if (!(xh == 1 || xh == H)) return MCO_EARG;
+    const int NS = (L + C - 1) / C;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+    double* dXh = (double*)calloc((size_t)B * H * L * dg, sizeof(double)); /* per-head dx */
+    if (!dXh) return MCO_ENOMEM;
+    int err = MCO_OK;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        const int hx = (xh == 1) ? 0 : h;
+        const double* q = Q + (size_t)bh * L * dk;
+        const double* k = K + (size_t)bh * L * dk;
+        const double* v = V + (size_t)bh * L * dv;
+        const double* u = U + (size_t)bh * L * dg;
+        const double* x = X + ((size_t)b * xh + hx) * L * dg;
+        const double* dy = dY + (size_t)bh * L * dv;
+        double* dq = dQ + (size_t)bh * L * dk;
+        double* dkk = dK + (size_t)bh * L * dk;
+        double* dvv = dV + (size_t)bh * L * dv;
+        double* du = dU + (size_t)bh * L * dg;
+        double* dx = dXh + (size_t)bh * L * dg;
+
+        double* qh = (double*)malloc(sizeof(double) * L * dk);
+        double* kh = (double*)malloc(sizeof(double) * L * dk);
+        double* Mc = (double*)calloc((size_t)NS * dv * dk, sizeof(double));
+        double* dMc = (double*)calloc((size_t)NS * dv * dk, sizeof(double));
+        double* Pc = (double*)calloc((size_t)NS * dg, sizeof(double));
+        double* dPc = (double*)calloc((size_t)NS * dg, sizeof(double));
+        double* Mon = (double*)calloc((size_t)dv * dk, sizeof(double));
+        double* xs = (double*)calloc((size_t)dg, sizeof(double));
+        double* gs = (double*)malloc(sizeof(double) * L);        /* online weight per token */
+        double* wt = (double*)calloc((size_t)L * dg, sizeof(double)); /* dp_t / (j_t + 1) */
+        double* dqh = (double*)calloc((size_t)L * dk, sizeof(double));
+        double* dkh = (double*)calloc((size_t)L * dk, sizeof(double));
+        double* a = (double*)malloc(sizeof(double) * (NS + 1));
+        double* g = (double*)malloc(sizeof(double) * (NS + 1));
+        double* dgm = (double*)malloc(sizeof(double) * (NS + 1));
+        double* o = (double*)malloc(sizeof(double) * (size_t)(NS + 1) * dv);
+        if (!qh || !kh || !Mc || !dMc || !Pc || !dPc || !Mon || !xs || !gs || !wt || !dqh ||
+            !dkh || !a || !g || !dgm || !o) {
+#pragma omp atomic write
+            err = MCO_ENOMEM;
+        } else {
+            for (size_t e = 0; e < (size_t)L * dk; ++e) {
+                qh[e] = mco_phi(q[e], phi);
+                kh[e] = mco_phi(k[e], phi);
+            }
+            /* the cached states and means (forward, [MC] Eq. 4b and Eq. 10) */
+            for (int t = 0; t < L; ++t) {
+                const int i = t / C;
+                for (int c = 0; c < dv; ++c)
+                    for (int r = 0; r < dk; ++r)
+                        Mc[((size_t)i * dv + c) * dk + r] += v[(size_t)t * dv + c] * kh[(size_t)t * dk + r];
+                for (int e = 0; e < dg; ++e) Pc[(size_t)i * dg + e] += x[(size_t)t * dg + e];
+            }
+            for (int i = 0; i < NS; ++i) {
+                const int len = (i + 1 < NS ? C : L - i * C);
+                for (int e = 0; e < dg; ++e) Pc[(size_t)i * dg + e] /= (double)len;
+            }
+            for (int t = 0; t < L; ++t) {
+                const int s = t / C, j = t - s * C;
+                if (j == 0) {
+                    memset(Mon, 0, sizeof(double) * dv * dk);
+                    memset(xs, 0, sizeof(double) * dg);
+                }
+                const double* kt = kh + (size_t)t * dk;
+                const double* qt = qh + (size_t)t * dk;
+                const double* ut = u + (size_t)t * dg;
+                const double* dyt = dy + (size_t)t * dv;
+                for (int c = 0; c < dv; ++c)
+                    for (int r = 0; r < dk; ++r) Mon[(size_t)c * dk + r] += v[(size_t)t * dv + c] * kt[r];
+                for (int e = 0; e < dg; ++e) xs[e] += x[(size_t)t * dg + e];
+                /* gate (forward) */
+                for (int i = 0; i < s; ++i) {
+                    double acc = 0.0;
+                    for (int e = 0; e < dg; ++e) acc += ut[e] * Pc[(size_t)i * dg + e];
+                    a[i] = acc;
+                }
+                {
+                    double acc = 0.0;
+                    for (int e = 0; e < dg; ++e) acc += ut[e] * (xs[e] / (double)(j + 1));
+                    a[s] = acc;
+                }
+                double mx = a[0];
+                for (int i = 1; i <= s; ++i) mx = fmax(mx, a[i]);
+                double z = 0.0;
+                for (int i = 0; i <= s; ++i) { g[i] = exp(a[i] - mx); z += g[i]; }
+                for (int i = 0; i <= s; ++i) g[i] /= z;
+                gs[t] = g[s];
+                /* the reads o_i and their gradients dg_i */
+                for (int i = 0; i <= s; ++i) {
+                    const double* Mi = (i < s) ? Mc + (size_t)i * dv * dk : Mon;
+                    double dgi = 0.0;
+                    for (int c = 0; c < dv; ++c) {
+                        double acc = 0.0;
+                        for (int r = 0; r < dk; ++r) acc += Mi[(size_t)c * dk + r] * qt[r];
+                        o[(size_t)i * dv + c] = acc;
+                        dgi += dyt[c] * acc;
+                    }
+                    dgm[i] = dgi;
+                }
+                double D = 0.0;
+                for (int i = 0; i <= s; ++i) D += g[i] * dgm[i];
+                /* softmax backward, then the gate's inputs */
+                for (int e = 0; e < dg; ++e) du[(size_t)t * dg + e] = 0.0;
+                for (int i = 0; i <= s; ++i) {
+                    const double dai = g[i] * (dgm[i] - D);
+                    for (int e = 0; e < dg; ++e) {
+                        const double pe = (i < s) ? Pc[(size_t)i * dg + e] : xs[e] / (double)(j + 1);
+                        du[(size_t)t * dg + e] += dai * pe;
+                        if (i < s)
+                            dPc[(size_t)i * dg + e] += dai * ut[e];
+                        else
+                            wt[(size_t)t * dg + e] = dai * ut[e] / (double)(j + 1);
+                    }
+                }
+                /* dphi(q_t) and the cached states' gradients */
+                for (int i = 0; i <= s; ++i) {
+                    const double* Mi = (i < s) ? Mc + (size_t)i * dv * dk : Mon;
+                    for (int c = 0; c < dv; ++c)
+                        for (int r = 0; r < dk; ++r)
+                            dqh[(size_t)t * dk + r] += g[i] * Mi[(size_t)c * dk + r] * dyt[c];
+                    if (i < s) {
+                        double* dMi = dMc + (size_t)i * dv * dk;
+                        for (int c = 0; c < dv; ++c)
+                            for (int r = 0; r < dk; ++r) dMi[(size_t)c * dk + r] += g[i] * dyt[c] * qt[r];
+                    }
+                }
+            }
+            /* the online memory's pairs r <= t of one segment */
+            for (int t = 0; t < L; ++t) {
+                const int s0 = (t / C) * C;
+                const double* qt = qh + (size_t)t * dk;
+                const double* dyt = dy + (size_t)t * dv;
+                for (int r = s0; r <= t; ++r) {
+                    double qk = 0.0, dyv = 0.0;
+                    for (int e = 0; e < dk; ++e) qk += qt[e] * kh[(size_t)r * dk + e];
+                    for (int c = 0; c < dv; ++c) dyv += dyt[c] * v[(size_t)r * dv + c];
+                    for (int c = 0; c < dv; ++c) dvv[(size_t)r * dv + c] += gs[t] * qk * dyt[c];
+                    for (int e = 0; e < dk; ++e) dkh[(size_t)r * dk + e] += gs[t] * dyv * qt[e];
+                }
+            }
+            /* the cached states' gradients reach the tokens of their segment */
+            for (int r = 0; r < L; ++r) {
+                const int i = r / C;
+                const double* dMi = dMc + (size_t)i * dv * dk;
+                for (int c = 0; c < dv; ++c)
+                    for (int e = 0; e < dk; ++e) {
+                        dvv[(size_t)r * dv + c] += dMi[(size_t)c * dk + e] * kh[(size_t)r * dk + e];
+                        dkh[(size_t)r * dk + e] += dMi[(size_t)c * dk + e] * v[(size_t)r * dv + c];
+                    }
+            }
+            /* x: segment means and the online prefix means */
+            for (int i = 0; i < NS; ++i) {
+                const int r0 = i * C, r1 = (i + 1 < NS ? (i + 1) * C : L);
+                for (int e = 0; e < dg; ++e) {
+                    double tail = 0.0;
+                    for (int r = r1 - 1; r >= r0; --r) {
+                        tail += wt[(size_t)r * dg + e];
+                        dx[(size_t)r * dg + e] = dPc[(size_t)i * dg + e] / (double)(r1 - r0) + tail;
+                    }
+                }
+            }
+            for (size_t e = 0; e < (size_t)L * dk; ++e) {
+                dq[e] = dqh[e] * mco_dphi(q[e], phi);
+                dkk[e] = dkh[e] * mco_dphi(k[e], phi);
+            }
+        }
+        free(qh); free(kh); free(Mc); free(dMc); free(Pc); free(dPc); free(Mon); free(xs);
+        free(gs); free(wt); free(dqh); free(dkh); free(a); free(g); free(dgm); free(o);
+    }
+    if (err == MCO_OK) {
+        memset(dX, 0, sizeof(double) * (size_t)B * xh * L * dg);
+        for (int bh = 0; bh < B * H; ++bh) {
+            const int b = bh / H, h = bh % H;
+            double* dst = dX + ((size_t)b * xh + (xh == 1 ? 0 : h)) * L * dg;
+            const double* src = dXh + (size_t)bh * L * dg;
+            for (size_t e = 0; e < (size_t)L * dg; ++e) dst[e] += src[e];
+        }
+    }
+    free(dXh);
+    return err;
+}
+
 /* Number of threads OpenMP will use (1 without OpenMP). */
 int mco_max_threads(void) {
 #ifdef _OPENMP

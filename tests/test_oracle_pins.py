@@ -19,6 +19,11 @@ an off-by-one segment, the wrong pool) fails at least one of them:
   decode, average   LA read / (number of memories); equals the gated step with u = 0
   variable segments brute force with arbitrary boundaries; multiples of C equal the
                     constant-length path; log segmentation of 37 is 32, 4, 1 (the pages' example)
+  SWLA              unit gates give the linear-attention memory; token-pair brute force with
+                    gate products; alpha = 0 is a two-token window; constant decay is masked
+                    attention; soup = GRM
+  backward          central differences of the forward oracle (every coordinate); torch
+                    autograd of an independent token-pair form
 """
 import json
 import math
@@ -552,3 +557,72 @@ def test_swla_soup_equals_grm():
     a = oracle.prefill(Q, K, V, U, X, seg_len=6, mode="grm", swla=gates)
     b = oracle.prefill(Q, K, V, U, X, seg_len=6, mode="soup", swla=gates)
     np.testing.assert_allclose(a["Y"], b["Y"], rtol=1e-12, atol=1e-12)
+
+
+# ---- backward of the GRM prefill: gradients of sum(Y * dY) ----
+
+def _loss(Q, K, V, U, X, dY, C, phi):
+    return float((oracle.prefill(Q, K, V, U, X, seg_len=C, phi=phi)["Y"] * dY).sum())
+
+
+@pytest.mark.parametrize("L,C,phi,xh", [(13, 4, "identity", 1), (11, 3, "elu1", 2),
+                                        (9, 9, "identity", 2)])
+def test_backward_matches_finite_differences(L, C, phi, xh):
+    # central differences of the forward oracle, every coordinate of every input
+    B, H = 1, 2
+    Q, K, V, U, X = _rand(B, H, L, 3, 2, 3, xh=xh, seed=61, scale_u=1.5)
+    dY = np.random.default_rng(62).standard_normal(V.shape)
+    got = oracle.grm_backward(Q, K, V, U, X, dY, seg_len=C, phi=phi)
+    eps = 1e-6
+    for name, arr in (("dQ", Q), ("dK", K), ("dV", V), ("dU", U), ("dX", X)):
+        num = np.zeros(arr.shape)
+        for ix in np.ndindex(arr.shape):
+            keep = arr[ix]
+            arr[ix] = keep + eps
+            fp = _loss(Q, K, V, U, X, dY, C, phi)
+            arr[ix] = keep - eps
+            fm = _loss(Q, K, V, U, X, dY, C, phi)
+            arr[ix] = keep
+            num[ix] = (fp - fm) / (2 * eps)
+        np.testing.assert_allclose(got[name], num, rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+def _torch_brute_grm(Q, K, V, U, X, C, phi):
+    """Token-pair form of the GRM read in torch (no states): differentiable by autograd."""
+    B, H, L, _ = Q.shape
+    xh = X.shape[1]
+    f = (lambda z: z) if phi == "identity" else (lambda z: torch.where(z > 0, z + 1.0, torch.exp(torch.clamp(z, max=0.0))))
+    qh, kh = f(Q), f(K)
+    seg = [t // C for t in range(L)]
+    NS = (L + C - 1) // C
+    rows = []
+    for b in range(B):
+        for h in range(H):
+            x = X[b, 0 if xh == 1 else h]
+            means = [x[i * C:min(L, (i + 1) * C)].mean(0) for i in range(NS)]
+            ys = []
+            for t in range(L):
+                s = seg[t]
+                logits = [U[b, h, t] @ means[i] for i in range(s)]
+                logits.append(U[b, h, t] @ x[s * C:t + 1].mean(0))
+                g = torch.softmax(torch.stack(logits), 0)
+                y = 0.0
+                for r in range(t + 1):
+                    y = y + g[seg[r]] * (qh[b, h, t] @ kh[b, h, r]) * V[b, h, r]
+                ys.append(y)
+            rows.append(torch.stack(ys))
+    return torch.stack(rows).reshape(B, H, L, -1)
+
+
+@pytest.mark.parametrize("L,C,phi,xh", [(24, 8, "identity", 1), (19, 5, "elu1", 2)])
+def test_backward_matches_autograd_of_token_pair_form(L, C, phi, xh):
+    B, H = 1, 2
+    Q, K, V, U, X = _rand(B, H, L, 4, 3, 5, xh=xh, seed=63, scale_u=1.5)
+    dY = np.random.default_rng(64).standard_normal(V.shape)
+    ts = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (Q, K, V, U, X)]
+    Y = _torch_brute_grm(*ts, C, phi)
+    (Y * torch.tensor(dY)).sum().backward()
+    got = oracle.grm_backward(Q, K, V, U, X, dY, seg_len=C, phi=phi)
+    for name, t in zip(("dQ", "dK", "dV", "dU", "dX"), ts):
+        np.testing.assert_allclose(got[name], t.grad.numpy(), rtol=1e-10, atol=1e-11,
+                                   err_msg=name)
