@@ -25,11 +25,11 @@ MC_OK, MC_ERR_NULL, MC_ERR_DIMS, MC_ERR_UNSUPPORTED = 0, 1, 2, 3
 MC_ERR_ALIGN, MC_ERR_WORKSPACE, MC_ERR_HIP, MC_ERR_CAPACITY = 4, 5, 6, 7
 MC_F32, MC_BF16 = 0, 1
 MC_PHI_IDENTITY, MC_PHI_ELU1 = 0, 1
-MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE = 0, 1, 2, 3
+MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE, MC_OP_GRM_BACKWARD = 0, 1, 2, 3, 4
 
 EXPORTED = ["mc_abi_version", "mc_status_str", "mc_workspace_bytes", "mc_scan_prefill",
             "mc_grm_readout", "mc_ssc_readout", "mc_decode_step", "mc_scan_prefill_segs",
-            "mc_grm_readout_segs", "mc_scan_prefill_swla"]
+            "mc_grm_readout_segs", "mc_scan_prefill_swla", "mc_grm_backward"]
 MC_MAX_SEGS = 512
 
 
@@ -77,6 +77,8 @@ def load(path: str = LIB_PATH):
         lib.mc_scan_prefill_swla.restype = ctypes.c_int
         lib.mc_scan_prefill_swla.argtypes = [D, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
                                              P, P]
+        lib.mc_grm_backward.restype = ctypes.c_int
+        lib.mc_grm_backward.argtypes = [D] + [P] * 15 + [ctypes.c_size_t, P]
         lib.mc_decode_step.restype = ctypes.c_int
         lib.mc_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P,
                                        ctypes.c_size_t, P]
@@ -193,6 +195,30 @@ def mc_scan_prefill_swla(dims, seg_off, alpha, beta, lam, Q, K, V, X, M, M_lo, P
                                        n, _p(alpha), _p(beta), _p(lam), _p(Q), _p(K), _p(V),
                                        _p(X), _p(M), _p(M_lo), _p(P), _p(O_on), _stream(stream)),
            "mc_scan_prefill_swla")
+
+
+def mc_grm_backward(dims, Q, K, V, U, X, M, M_lo, P, dY, dQ, dK, dV, dU, dX, ws=None,
+                    stream=None):
+    w, wb = _ws(ws)
+    _check(load().mc_grm_backward(ctypes.byref(dims), _p(Q), _p(K), _p(V), _p(U), _p(X), _p(M),
+                                  _p(M_lo), _p(P), _p(dY), _p(dQ), _p(dK), _p(dV), _p(dU),
+                                  _p(dX), w, wb, _stream(stream)),
+           "mc_grm_backward")
+
+
+def grm_backward(dims, Q, K, V, U, X, M, M_lo, P, dY, stream=None):
+    """Gradients of the GRM prefill with fresh fp32 outputs: dict dQ, dK, dV, dU, dX."""
+    import torch
+    dev = Q.device
+    f = dict(dtype=torch.float32, device=dev)
+    B, H, L = dims.B, dims.H, dims.L
+    out = {"dQ": torch.empty((B, H, L, dims.d_k), **f), "dK": torch.empty((B, H, L, dims.d_k), **f),
+           "dV": torch.empty((B, H, L, dims.d_v), **f), "dU": torch.empty((B, H, L, dims.d_g), **f),
+           "dX": torch.empty((B, dims.x_heads, L, dims.d_g), **f)}
+    ws = workspace(dims, MC_OP_GRM_BACKWARD, device=dev)
+    mc_grm_backward(dims, Q, K, V, U, X, M, M_lo, P, dY, out["dQ"], out["dK"], out["dV"],
+                    out["dU"], out["dX"], ws=ws, stream=stream)
+    return out
 
 
 def mc_decode_step(dims, q, k, v, u, x, M_on, xsum_on, count_on, M_cache, P_cache, n_cached,

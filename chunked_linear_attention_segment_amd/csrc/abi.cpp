@@ -58,6 +58,23 @@ SscWorkspace ssc_workspace(const mc_dims& d) {
     return w;
 }
 
+BwdWorkspace bwd_workspace(const mc_dims& d) {
+    BwdWorkspace w{};
+    const size_t bhl = (size_t)d.B * d.H * d.L;
+    const size_t esz = d.dtype == MC_BF16 ? 2 : 4;
+    w.aon = align256(sizeof(float) * bhl);
+    w.xps = xps_only(d);
+    w.xtail = align256(sizeof(float) * xps_tail_floats(d));
+    w.on = align256(sizeof(float) * bhl * d.d_v);
+    w.ot = align256(sizeof(float) * bhl * d.d_k);
+    w.khat = d.phi ? align256(esz * bhl * d.d_k) : 0;
+    w.lse = w.D = w.gs = align256(sizeof(float) * bhl);
+    w.dG = align256(sizeof(float) * bhl * num_segments(d));
+    w.dM = align256(sizeof(float) * (size_t)d.B * d.H * num_segments(d) * d.d_v * d.d_k);
+    w.total = w.aon + w.xps + w.xtail + w.on + w.ot + w.khat + w.lse + w.D + w.gs + w.dG + w.dM;
+    return w;
+}
+
 // The cached states of a decode step are read in runs of kDecodeRun states (one workgroup
 // each); the workspace holds the partial softmaxes of a full cache, so its size depends only
 // on n_cap.
@@ -123,6 +140,7 @@ size_t mc_workspace_bytes(const mc_dims* d, mc_op op, int32_t top_k, int32_t n_c
         case MC_OP_PREFILL: return 0;
         case MC_OP_GRM: return grm_workspace(*d).total;
         case MC_OP_SSC: return top_k >= 1 ? ssc_workspace(*d).total : 0;
+        case MC_OP_GRM_BACKWARD: return bwd_workspace(*d).total;
         default: return 0;
     }
 }
@@ -287,6 +305,49 @@ mc_status mc_scan_prefill_swla(const mc_dims* d, const int32_t* seg_off, int32_t
     gt.beta = beta;
     gt.lam = lambda;
     return launch_scan_prefill_swla(*d, sg, gt, Q, K, V, X, M, M_lo, P, O_on, stream)
+               ? MC_ERR_HIP
+               : MC_OK;
+}
+
+mc_status mc_grm_backward(const mc_dims* d, const void* Q, const void* K, const void* V,
+                          const void* U, const void* X, const float* M, const uint16_t* M_lo,
+                          const float* P, const void* dY, float* dQ, float* dK, float* dV,
+                          float* dU, float* dX, void* ws, size_t ws_bytes, void* stream) {
+    mc_status st = check_dims(d, true);
+    if (st != MC_OK) return st;
+    if (!Q || !K || !V || !U || !X || !P || !dY || !dQ || !dK || !dV || !dU || !dX)
+        return MC_ERR_NULL;
+    if (d->dtype == MC_BF16 ? !M_lo : !M) return MC_ERR_NULL;
+    const BwdWorkspace w = bwd_workspace(*d);
+    if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
+    const void* ptrs[] = {Q, K, V, U, X, M, M_lo, P, dY, dQ, dK, dV, dU, dX, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MC_ERR_ALIGN;
+    char* b = (char*)ws;
+    BwdBuffers bw;
+    bw.aon = (float*)b;
+    b += w.aon;
+    bw.xps = (float*)b;
+    b += w.xps;
+    bw.xtail = (float*)b;
+    b += w.xtail;
+    bw.on = (float*)b;
+    b += w.on;
+    bw.ot = (float*)b;
+    b += w.ot;
+    bw.khat = w.khat ? (void*)b : nullptr;
+    b += w.khat;
+    bw.lse = (float*)b;
+    b += w.lse;
+    bw.D = (float*)b;
+    b += w.D;
+    bw.gs = (float*)b;
+    b += w.gs;
+    bw.dG = (float*)b;
+    b += w.dG;
+    bw.dM = (float*)b;
+    return launch_grm_backward(*d, bw, Q, K, V, U, X, M, M_lo, P, dY, dQ, dK, dV, dU, dX,
+                               stream)
                ? MC_ERR_HIP
                : MC_OK;
 }

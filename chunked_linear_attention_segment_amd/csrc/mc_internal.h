@@ -75,6 +75,29 @@ int launch_scan_prefill_swla(const mc_dims& d, const SegArg& sg, const SwlaGates
                              const void* Q, const void* K, const void* V, const void* X,
                              float* M, uint16_t* M_lo, float* P, float* O_on, void* stream);
 
+// Backward of the GRM prefill (backward.hip): device buffers carved from the workspace.
+struct BwdBuffers {
+    float* aon;    // [B,H,L] online logits
+    float* xps;    // [B,xh,L,dg] segment-causal prefix sums of X
+    float* xtail;  // their per-chunk partial sums
+    float* on;     // [B,H,L,dv] online read M_t^(s) phi(q_t)
+    float* ot;     // [B,H,L,dk] M_t^(s)T dy_t
+    void* khat;    // [B,H,L,dk] phi(K) in the input dtype (elu + 1 only)
+    float* lse;    // [B,H,L] log of the softmax denominator
+    float* D;      // [B,H,L] sum_i gamma_i dgamma_i
+    float* gs;     // [B,H,L] online weight gamma_s
+    float* dG;     // [B,H,L,NS] dgamma, then da
+    float* dM;     // [B,H,NS,dv,dk] gradient of each cached state
+};
+struct BwdWorkspace {
+    size_t aon, xps, xtail, on, ot, khat, lse, D, gs, dG, dM, total;
+};
+BwdWorkspace bwd_workspace(const mc_dims& d);
+int launch_grm_backward(const mc_dims& d, const BwdBuffers& w, const void* Q, const void* K,
+                        const void* V, const void* U, const void* X, const float* M,
+                        const uint16_t* M_lo, const float* P, const void* dY, float* dQ,
+                        float* dK, float* dV, float* dU, float* dX, void* stream);
+
 int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
                              const void* V, const void* X, float* M, uint16_t* M_lo, float* P,
                              float* O_on, void* stream);

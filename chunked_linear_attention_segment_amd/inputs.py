@@ -279,3 +279,11 @@ def make_swla_gates_device(B: int, H: int, L: int, seed: int = 0, device="cuda",
         out[k] = torch.rand((B, H, L), generator=g, device=device, dtype=torch.float32) * \
             (hi - lo) + lo
     return out
+
+
+def make_upstream_grad(B: int, H: int, L: int, d_v: int, seed: int = 0,
+                       dtype: str = "f32") -> np.ndarray:
+    """dY [B,H,L,d_v] ~ N(0,1), the gradient of a loss with respect to the read's output,
+    stored in the input dtype (float32 array of bf16-representable values for bf16)."""
+    rng = np.random.default_rng(seed)
+    return _store(rng.standard_normal((B, H, L, d_v), dtype=np.float32), dtype)

@@ -67,7 +67,13 @@ typedef enum {
 
 typedef enum { MC_F32 = 0, MC_BF16 = 1 } mc_dtype;           /* storage type of Q,K,V,U,X,Y */
 typedef enum { MC_PHI_IDENTITY = 0, MC_PHI_ELU1 = 1 } mc_phi; /* feature map on Q and K     */
-typedef enum { MC_OP_PREFILL = 0, MC_OP_GRM = 1, MC_OP_SSC = 2, MC_OP_DECODE = 3 } mc_op;
+typedef enum {
+    MC_OP_PREFILL = 0,
+    MC_OP_GRM = 1,
+    MC_OP_SSC = 2,
+    MC_OP_DECODE = 3,
+    MC_OP_GRM_BACKWARD = 4
+} mc_op;
 
 /* Problem sizes.  Supported in this build: d_k, d_v in {64, 128}; 1 <= d_g <= 256 and
  * d_g % 8 == 0; C >= 1; x_heads in {1, H}; dtype MC_F32 or MC_BF16.                      */
@@ -233,6 +239,29 @@ mc_status mc_scan_prefill_swla(const mc_dims* dims, const int32_t* seg_off, int3
                                const float* alpha, const float* beta, const float* lambda,
                                const void* Q, const void* K, const void* V, const void* X,
                                float* M, uint16_t* M_lo, float* P, float* O_on, void* stream);
+
+/*
+ * Backward of the GRM prefill (training): the gradients of a loss with respect to Q, K, V,
+ * U and X, given its gradient dY with respect to the output Y of mc_grm_readout (Memory
+ * Caching paper: the Eq. 4b segment memories, the Eq. 10 softmax gate and the Eq. 9 read,
+ * differentiated token by token; the chain rule through phi, the softmax, the segment
+ * means and the causal prefix means of the online segment).  Constant segments of
+ * dims->seg_len.
+ *
+ *   Q, K, V, U, X       the forward inputs (dtype, layouts as mc_grm_readout)
+ *   M, M_lo, P          the states and means mc_scan_prefill wrote for them (M_lo is read
+ *                       for MC_BF16, M for MC_F32; the other may be NULL)
+ *   dY       [B,H,L,d_v] dtype
+ *   dQ, dK   out [B,H,L,d_k] fp32;  dV out [B,H,L,d_v] fp32;  dU out [B,H,L,d_g] fp32
+ *   dX       out [B,x_heads,L,d_g] fp32 (with x_heads = 1 the heads' gradients are summed)
+ *   ws       mc_workspace_bytes(dims, MC_OP_GRM_BACKWARD, 0, 0) bytes
+ *   The forward states are recomputed where needed (the online read and its transpose);
+ *   every sum accumulates in fp32.  Errors as mc_grm_readout.
+ */
+mc_status mc_grm_backward(const mc_dims* dims, const void* Q, const void* K, const void* V,
+                          const void* U, const void* X, const float* M, const uint16_t* M_lo,
+                          const float* P, const void* dY, float* dQ, float* dK, float* dV,
+                          float* dU, float* dX, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

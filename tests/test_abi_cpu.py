@@ -236,3 +236,25 @@ def test_swla_scan_arguments():
     bad.seg_len = 0
     assert lib.mc_scan_prefill_swla(ctypes.byref(bad), None, 0, A, A, A, A, A, A, A, A, A, A,
                                     A, None) == mc.MC_ERR_DIMS
+
+
+def test_backward_arguments():
+    d = dims()
+    lib = mc.load()
+    need = mc.mc_workspace_bytes(d, mc.MC_OP_GRM_BACKWARD)
+    B, H, L, dk, dv = d.B, d.H, d.L, d.d_k, d.d_v
+    NS = -(-L // d.seg_len)
+    # online read and its transpose, dgamma per (token, segment), dM per segment, 3 per token
+    assert need >= 4 * B * H * L * (dv + dk + NS + 3) + 4 * B * H * NS * dv * dk
+
+    def call(ws_bytes=need, **kw):
+        p = dict(Q=A, K=A, V=A, U=A, X=A, M=A, M_lo=A, P=A, dY=A, dQ=A, dK=A, dV=A, dU=A, dX=A,
+                 ws=A)
+        p.update(kw)
+        return lib.mc_grm_backward(ctypes.byref(d), *(p[k] for k in (
+            "Q", "K", "V", "U", "X", "M", "M_lo", "P", "dY", "dQ", "dK", "dV", "dU", "dX",
+            "ws")), ws_bytes, None)
+    for k in ("Q", "K", "V", "U", "X", "P", "dY", "dQ", "dK", "dV", "dU", "dX", "M_lo"):
+        assert call(**{k: None}) == mc.MC_ERR_NULL, k
+    assert call(ws_bytes=need - 1) == mc.MC_ERR_WORKSPACE
+    assert call(dX=MIS) == mc.MC_ERR_ALIGN

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from chunked_linear_attention_segment_amd.inputs import (WORKLOADS, Workload, make_prefill,
-                                                         make_swla_gates)
+                                                         make_swla_gates, make_upstream_grad)
 from mcutil import TOL, announce, slice_rel_err, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
@@ -390,6 +390,41 @@ def test_swla_grm(name):
                          swla=(g["alpha"], g["beta"], g["lam"]))
     tol = TOL[w.dtype]
     errs = {k: slice_rel_err(to_np(out[k]), ref[k]) for k in ("Y", "M", "P", "O_on", "gamma")}
+    announce("  errors %s" % errs)
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
+
+
+# Backward of the GRM prefill: every gradient (fp32 outputs) against the oracle's, from the
+# states and means the forward wrote.
+BWD_CASES = {
+    "f32_d64_C32_L200": Workload("x", 1, 2, 200, 64, 64, 64, 32, "identity", "f32"),
+    "f32_d128_C64_L300_elu_xheadsH": Workload("x", 1, 2, 300, 128, 128, 64, 64, "elu1", "f32",
+                                              x_heads=2),
+    "bf16_d128_C256_L700": Workload("x", 1, 3, 700, 128, 128, 128, 256, "identity", "bf16"),
+    "bf16_d128v64_C48_L333_elu": Workload("x", 2, 2, 333, 128, 64, 64, 48, "elu1", "bf16"),
+    "bf16_d64_C16_L640_many_segments": Workload("x", 1, 2, 640, 64, 64, 32, 16, "identity",
+                                                "bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(BWD_CASES))
+def test_grm_backward(name):
+    w = BWD_CASES[name]
+    announce("grm backward %s" % name)
+    inp = make_prefill(w, seed=8)
+    B, H = inp["Q"].shape[:2]
+    dY = make_upstream_grad(B, H, w.L, w.d_v, seed=9, dtype=w.dtype)
+    d = _dims(w)
+    dev = {k: to_dev(v, w.dtype) for k, v in inp.items()}
+    fwd = mc.prefill_grm(d, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"], online=False)
+    got = mc.grm_backward(d, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"], fwd["M"],
+                          fwd["M_lo"], fwd["P"], to_dev(dY, w.dtype))
+    torch.cuda.synchronize()
+    ref = oracle.grm_backward(inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], dY,
+                              seg_len=w.seg_len, phi=w.phi)
+    tol = TOL[w.dtype]
+    errs = {k: slice_rel_err(to_np(got[k]), ref[k]) for k in ("dQ", "dK", "dV", "dU", "dX")}
     announce("  errors %s" % errs)
     for k, e in errs.items():
         assert e <= tol, (k, e)
