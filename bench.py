@@ -103,7 +103,9 @@ def main():
                     help="skip the logarithmic-segmentation prefill line")
     ap.add_argument("--no-swla", action="store_true",
                     help="skip the SWLA-memory prefill line")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "segs", "swla"],
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward (training) lines")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "segs", "swla", "backward"],
                     default="all",
                     help="profiling aid: run only one workload (the JSON line then lacks the "
                          "other part)")
@@ -135,10 +137,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
         return
-    if args.only in ("decode", "segs", "swla"):
+    if args.only in ("decode", "segs", "swla", "backward"):
         rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup}
-        {"decode": run_decode, "segs": run_log_segments, "swla": run_swla}[args.only](
-            args, rec, dev)
+        {"decode": run_decode, "segs": run_log_segments, "swla": run_swla,
+         "backward": run_backward}[args.only](args, rec, dev)
         print(json.dumps(rec), flush=True)
         return
     w = WORKLOADS["grm_bf16_L64K"]
@@ -216,6 +218,9 @@ def main():
 
     if not args.no_swla and args.only == "all":
         run_swla(args, rec, dev)
+
+    if not args.no_backward and args.only == "all":
+        run_backward(args, rec, dev)
 
     if not args.no_peak and args.only == "all":
         measured_peaks(rec)
@@ -438,6 +443,77 @@ def run_swla(args, rec, dev):
                           "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": sbytes}}
     del inp, g, M, M_lo, P, O_on, Y, ws
     torch.cuda.empty_cache()
+
+
+def backward_flops(B, H, L, C, dk, dv, dg):
+    """Algorithmic FLOPs of the GRM prefill's backward: per (token, cached state read) the
+    state read for dgamma, the dq term and the dM term (2*dk*dv each) and the gate logit, du
+    and dP terms (2*dg each); per (token, key) pair of the online segment the recomputed
+    online read, its dq term and the dv and dk terms (2*(dk+dv) each); per token the cached
+    states' gradients applied to k and v (2*dk*dv each)."""
+    N = -(-L // C)
+    per_state = 0
+    pairs = 0
+    for s in range(N):
+        n = min(C, L - s * C)
+        per_state += n * s
+        pairs += n * (n + 1) // 2
+    return B * H * (per_state * (3 * 2 * dk * dv + 3 * 2 * dg) + pairs * 4 * 2 * (dk + dv)
+                    + L * 2 * 2 * dk * dv)
+
+
+def run_backward(args, rec, dev):
+    """The backward of the GRM prefill (training) at the L=4K workload and the L=64K
+    workload's shape: forward once, then mc_grm_backward timed with HIP events on its stream
+    (inputs, states and dY resident).  tokens/s of the backward alone; algorithmic FLOPs
+    against the fp32 vector peak its kernels run on."""
+    import torch
+
+    import chunked_linear_attention_segment_amd as mc
+    from chunked_linear_attention_segment_amd.inputs import (WORKLOADS, make_prefill_device,
+                                                             make_upstream_grad)
+    out = {}
+    for name in ("grm_bf16_L4K_elu", "grm_bf16_L64K"):
+        w = WORKLOADS[name]
+        B, H, L, C, dk, dv, dg = w.B, w.H, w.L, w.seg_len, w.d_k, w.d_v, w.d_g
+        d = mc.make_dims(B, H, L, dk, dv, dg, C, 1, w.dtype, w.phi)
+        inp = make_prefill_device(w, seed=0, device=dev)
+        dY = torch.from_numpy(make_upstream_grad(B, H, L, dv, seed=1, dtype=w.dtype)).to(
+            dev).to(torch.bfloat16)
+        fwd = mc.prefill_grm(d, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], online=False)
+        f = dict(dtype=torch.float32, device=dev)
+        g = [torch.empty((B, H, L, dk), **f), torch.empty((B, H, L, dk), **f),
+             torch.empty((B, H, L, dv), **f), torch.empty((B, H, L, dg), **f),
+             torch.empty((B, 1, L, dg), **f)]
+        ws = mc.workspace(d, mc.MC_OP_GRM_BACKWARD, device=dev)
+        stream = torch.cuda.current_stream()
+
+        def step():
+            mc.mc_grm_backward(d, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], fwd["M"],
+                               fwd["M_lo"], fwd["P"], dY, *g, ws=ws, stream=stream)
+        steps = max(1, min(args.steps, 3 if L > 8192 else args.steps))
+        for _ in range(min(args.warmup, 1)):
+            step()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        fl = backward_flops(B, H, L, C, dk, dv, dg)
+        tf = fl / (ms / 1e3) / 1e12
+        out[name] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(B * L / (ms / 1e3), 1),
+                     "steps": steps,
+                     "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": 157.3,
+                                  "unit": "TFLOP/s", "frac": round(tf / 157.3, 4),
+                                  "algorithmic_flops": fl}}
+        del inp, dY, fwd, g, ws
+        torch.cuda.empty_cache()
+    rec["backward"] = {"what": "mc_grm_backward: gradients of Q, K, V, U, X (fp32) from dY",
+                       "metric": "backward tokens/s", "workloads": out}
 
 
 def cpu_baseline(w, rows_sample):

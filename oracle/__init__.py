@@ -52,7 +52,8 @@ def _load():
         lib.mco_decode_step.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P,
                                         ctypes.c_int32, P, P]
         lib.mco_decode_step.restype = ctypes.c_int
-        lib.mco_grm_backward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
+        lib.mco_grm_backward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int, P,
+                                         ctypes.c_int64]
         lib.mco_grm_backward.restype = ctypes.c_int
         lib.mco_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -173,21 +174,30 @@ def decode_step(state: DecodeState, q, k, v, u, x, seg_len: int, phi: str = "ide
 
 
 def grm_backward(Q, K, V, U, X, dY, seg_len: int, phi: str = "identity",
-                 n_threads: int = 0) -> dict:
+                 n_threads: int = 0, rows=None) -> dict:
     """Gradients of the GRM prefill (constant segments of seg_len) for the upstream gradient
     dY [B,H,L,dv]: 'dQ', 'dK' [B,H,L,dk], 'dV' [B,H,L,dv], 'dU' [B,H,L,dg], 'dX' [B,xh,L,dg]
-    (heads summed when X is shared)."""
+    (heads summed when X is shared).  With rows, only 'dQ' and 'dU' at those rows."""
     Q, K, V, U, X, dY = (_f64(a) for a in (Q, K, V, U, X, dY))
     B, H, L, dk = Q.shape
     dv, dg, xh = V.shape[-1], U.shape[-1], X.shape[1]
     assert dY.shape == V.shape
     dims = np.array([B, H, L, dk, dv, dg, int(seg_len), xh,
                      1 if phi in ("elu1", "elu+1") else 0], dtype=np.int32)
-    out = {"dQ": np.zeros(Q.shape), "dK": np.zeros(K.shape), "dV": np.zeros(V.shape),
-           "dU": np.zeros(U.shape), "dX": np.zeros(X.shape)}
+    if rows is not None:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        nr = rows.shape[0]
+        out = {"dQ": np.zeros((B, H, nr, dk)), "dU": np.zeros((B, H, nr, dg))}
+        ext = [None, None, None]
+    else:
+        nr = L
+        out = {"dQ": np.zeros(Q.shape), "dK": np.zeros(K.shape), "dV": np.zeros(V.shape),
+               "dU": np.zeros(U.shape), "dX": np.zeros(X.shape)}
+        ext = [out["dK"], out["dV"], out["dX"]]
     rc = _load().mco_grm_backward(_ptr(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(U), _ptr(X),
-                                  _ptr(dY), _ptr(out["dQ"]), _ptr(out["dK"]), _ptr(out["dV"]),
-                                  _ptr(out["dU"]), _ptr(out["dX"]), int(n_threads))
+                                  _ptr(dY), _ptr(out["dQ"]), _ptr(ext[0]), _ptr(ext[1]),
+                                  _ptr(out["dU"]), _ptr(ext[2]), int(n_threads), _ptr(rows),
+                                  int(nr))
     if rc != 0:
         raise ValueError("mco_grm_backward failed with code %d" % rc)
     return out

@@ -442,21 +442,28 @@ static double mco_dphi(double z, int phi) {
  * dims = {B, H, L, dk, dv, dg, C, xh, phi} (segments of constant length C).  Inputs as for
  * mco_prefill; dY [B,H,L,dv].  Outputs dQ, dK [B,H,L,dk], dV [B,H,L,dv], dU [B,H,L,dg],
  * dX [B,xh,L,dg] (with xh = 1 the heads' contributions are summed, in head order).
+ * rows (ascending, n_rows of them) restricts the work to the gradients that belong to single
+ * tokens, dQ and dU [B,H,n_rows,.] at those rows; dK, dV and dX are then not written.
  */
 int mco_grm_backward(const int32_t* dims, const double* Q, const double* K, const double* V,
                      const double* U, const double* X, const double* dY, double* dQ,
-                     double* dK, double* dV, double* dU, double* dX, int n_threads) {
+                     double* dK, double* dV, double* dU, double* dX, int n_threads,
+                     const int32_t* rows, int64_t n_rows) {
     const int B = dims[0], H = dims[1], L = dims[2], dk = dims[3], dv = dims[4], dg = dims[5];
     const int C = dims[6], xh = dims[7], phi = dims[8];
     if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || dg <= 0 || C <= 0) return MCO_EARG;
     if (!(xh == 1 || xh == H)) return MCO_EARG;
     const int NS = (L + C - 1) / C;
+    const int64_t nr = rows ? n_rows : (int64_t)L;
+    if (rows)
+        for (int64_t a = 0; a < nr; ++a)
+            if (rows[a] < 0 || rows[a] >= L || (a > 0 && rows[a] <= rows[a - 1])) return MCO_EARG;
 #ifdef _OPENMP
     if (n_threads > 0) omp_set_num_threads(n_threads);
 #else
     (void)n_threads;
 #endif
-    double* dXh = (double*)calloc((size_t)B * H * L * dg, sizeof(double)); /* per-head dx */
+    double* dXh = (double*)calloc(rows ? 1 : (size_t)B * H * L * dg, sizeof(double));
     if (!dXh) return MCO_ENOMEM;
     int err = MCO_OK;
 
@@ -470,11 +477,12 @@ int mco_grm_backward(const int32_t* dims, const double* Q, const double* K, cons
         const double* u = U + (size_t)bh * L * dg;
         const double* x = X + ((size_t)b * xh + hx) * L * dg;
         const double* dy = dY + (size_t)bh * L * dv;
-        double* dq = dQ + (size_t)bh * L * dk;
-        double* dkk = dK + (size_t)bh * L * dk;
-        double* dvv = dV + (size_t)bh * L * dv;
-        double* du = dU + (size_t)bh * L * dg;
-        double* dx = dXh + (size_t)bh * L * dg;
+        double* dq = dQ + (size_t)bh * nr * dk;
+        double* dkk = rows ? NULL : dK + (size_t)bh * L * dk;
+        double* dvv = rows ? NULL : dV + (size_t)bh * L * dv;
+        double* du = dU + (size_t)bh * nr * dg;
+        double* dx = rows ? NULL : dXh + (size_t)bh * L * dg;
+        int64_t next = 0; /* position in rows */
 
         double* qh = (double*)malloc(sizeof(double) * L * dk);
         double* kh = (double*)malloc(sizeof(double) * L * dk);
@@ -526,6 +534,11 @@ int mco_grm_backward(const int32_t* dims, const double* Q, const double* K, cons
                 for (int c = 0; c < dv; ++c)
                     for (int r = 0; r < dk; ++r) Mon[(size_t)c * dk + r] += v[(size_t)t * dv + c] * kt[r];
                 for (int e = 0; e < dg; ++e) xs[e] += x[(size_t)t * dg + e];
+                int64_t row = t; /* output row of this token */
+                if (rows) {
+                    if (next >= nr || rows[next] != t) continue;
+                    row = next++;
+                }
                 /* gate (forward) */
                 for (int i = 0; i < s; ++i) {
                     double acc = 0.0;
@@ -558,12 +571,12 @@ int mco_grm_backward(const int32_t* dims, const double* Q, const double* K, cons
                 double D = 0.0;
                 for (int i = 0; i <= s; ++i) D += g[i] * dgm[i];
                 /* softmax backward, then the gate's inputs */
-                for (int e = 0; e < dg; ++e) du[(size_t)t * dg + e] = 0.0;
+                for (int e = 0; e < dg; ++e) du[(size_t)row * dg + e] = 0.0;
                 for (int i = 0; i <= s; ++i) {
                     const double dai = g[i] * (dgm[i] - D);
                     for (int e = 0; e < dg; ++e) {
                         const double pe = (i < s) ? Pc[(size_t)i * dg + e] : xs[e] / (double)(j + 1);
-                        du[(size_t)t * dg + e] += dai * pe;
+                        du[(size_t)row * dg + e] += dai * pe;
                         if (i < s)
                             dPc[(size_t)i * dg + e] += dai * ut[e];
                         else
@@ -575,8 +588,8 @@ int mco_grm_backward(const int32_t* dims, const double* Q, const double* K, cons
                     const double* Mi = (i < s) ? Mc + (size_t)i * dv * dk : Mon;
                     for (int c = 0; c < dv; ++c)
                         for (int r = 0; r < dk; ++r)
-                            dqh[(size_t)t * dk + r] += g[i] * Mi[(size_t)c * dk + r] * dyt[c];
-                    if (i < s) {
+                            dqh[(size_t)row * dk + r] += g[i] * Mi[(size_t)c * dk + r] * dyt[c];
+                    if (i < s && !rows) {
                         double* dMi = dMc + (size_t)i * dv * dk;
                         for (int c = 0; c < dv; ++c)
                             for (int r = 0; r < dk; ++r) dMi[(size_t)c * dk + r] += g[i] * dyt[c] * qt[r];
@@ -584,7 +597,7 @@ int mco_grm_backward(const int32_t* dims, const double* Q, const double* K, cons
                 }
             }
             /* the online memory's pairs r <= t of one segment */
-            for (int t = 0; t < L; ++t) {
+            for (int t = 0; t < (rows ? 0 : L); ++t) {
                 const int s0 = (t / C) * C;
                 const double* qt = qh + (size_t)t * dk;
                 const double* dyt = dy + (size_t)t * dv;
@@ -597,7 +610,7 @@ int mco_grm_backward(const int32_t* dims, const double* Q, const double* K, cons
                 }
             }
             /* the cached states' gradients reach the tokens of their segment */
-            for (int r = 0; r < L; ++r) {
+            for (int r = 0; r < (rows ? 0 : L); ++r) {
                 const int i = r / C;
                 const double* dMi = dMc + (size_t)i * dv * dk;
                 for (int c = 0; c < dv; ++c)
@@ -607,7 +620,7 @@ int mco_grm_backward(const int32_t* dims, const double* Q, const double* K, cons
                     }
             }
             /* x: segment means and the online prefix means */
-            for (int i = 0; i < NS; ++i) {
+            for (int i = 0; i < (rows ? 0 : NS); ++i) {
                 const int r0 = i * C, r1 = (i + 1 < NS ? (i + 1) * C : L);
                 for (int e = 0; e < dg; ++e) {
                     double tail = 0.0;
@@ -617,15 +630,18 @@ int mco_grm_backward(const int32_t* dims, const double* Q, const double* K, cons
                     }
                 }
             }
-            for (size_t e = 0; e < (size_t)L * dk; ++e) {
-                dq[e] = dqh[e] * mco_dphi(q[e], phi);
-                dkk[e] = dkh[e] * mco_dphi(k[e], phi);
+            for (int64_t a = 0; a < nr; ++a) {
+                const int t = rows ? rows[a] : (int)a;
+                for (int e = 0; e < dk; ++e)
+                    dq[(size_t)a * dk + e] = dqh[(size_t)a * dk + e] * mco_dphi(q[(size_t)t * dk + e], phi);
             }
+            if (!rows)
+                for (size_t e = 0; e < (size_t)L * dk; ++e) dkk[e] = dkh[e] * mco_dphi(k[e], phi);
         }
         free(qh); free(kh); free(Mc); free(dMc); free(Pc); free(dPc); free(Mon); free(xs);
         free(gs); free(wt); free(dqh); free(dkh); free(a); free(g); free(dgm); free(o);
     }
-    if (err == MCO_OK) {
+    if (err == MCO_OK && !rows) {
         memset(dX, 0, sizeof(double) * (size_t)B * xh * L * dg);
         for (int bh = 0; bh < B * H; ++bh) {
             const int b = bh / H, h = bh % H;

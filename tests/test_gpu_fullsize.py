@@ -13,7 +13,8 @@ import pytest
 import oracle
 from chunked_linear_attention_segment_amd.inputs import (WORKLOADS, make_decode_device,
                                                          make_prefill_device,
-                                                         make_swla_gates_device)
+                                                         make_swla_gates_device,
+                                                         make_upstream_grad)
 from mcutil import TOL, announce, slice_rel_err, to_np
 
 pytestmark = pytest.mark.gpu
@@ -195,4 +196,73 @@ def test_swla_full_size():
         announce("  (b=%d, h=%d) %d rows: %s" % (b, h, len(rows), errs))
         assert errs["Y"] <= TOL["bf16"] and errs["M"] <= TOL["bf16"] and errs["P"] <= 1e-4
     del inp, out
+    torch.cuda.empty_cache()
+
+
+def _backward_inputs(w, seed):
+    inp = make_prefill_device(w, seed=seed)
+    dY = torch.from_numpy(make_upstream_grad(w.B, w.H, w.L, w.d_v, seed=seed + 1,
+                                             dtype=w.dtype)).cuda().to(torch.bfloat16)
+    d = _dims(w)
+    fwd = mc.prefill_grm(d, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], online=False)
+    got = mc.grm_backward(d, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], fwd["M"],
+                          fwd["M_lo"], fwd["P"], dY)
+    torch.cuda.synchronize()
+    return inp, dY, fwd, got
+
+
+def test_backward_full_size_L4K():
+    # every gradient of every head of the L=4K workload (B=4, H=16, C=256, elu+1) against
+    # the oracle, in the launch configuration the benchmark times
+    w = WORKLOADS["grm_bf16_L4K_elu"]
+    announce("full-size backward %s: B=%d H=%d L=%d C=%d" % (w.name, w.B, w.H, w.L, w.seg_len))
+    inp, dY, fwd, got = _backward_inputs(w, seed=2)
+    host = {k: v.to(torch.float64).cpu().numpy() for k, v in inp.items()}
+    ref = oracle.grm_backward(host["Q"], host["K"], host["V"], host["U"], host["X"],
+                              dY.to(torch.float64).cpu().numpy(), seg_len=w.seg_len, phi=w.phi)
+    errs = {k: slice_rel_err(to_np(got[k]), ref[k]) for k in ("dQ", "dK", "dV", "dU", "dX")}
+    announce("  errors %s" % errs)
+    for k, e in errs.items():
+        assert e <= TOL["bf16"], (k, e)
+    del inp, dY, fwd, got
+    torch.cuda.empty_cache()
+
+
+def test_backward_full_size_L64K():
+    # the L=64K workload: per-token gradients (dQ, dU) at sampled rows of two heads against
+    # the oracle, and for the whole input Euler's identity for the inputs Y is linear in
+    # (V, and with phi = identity Q and K): sum(dV*V) = sum(dQ*Q) = sum(dK*K) = sum(dY*Y)
+    w = WORKLOADS["grm_bf16_L64K"]
+    announce("full-size backward %s: H=%d L=%d C=%d" % (w.name, w.H, w.L, w.seg_len))
+    inp, dY, fwd, got = _backward_inputs(w, seed=3)
+    assert all(torch.isfinite(v).all() for v in got.values())
+    Y = torch.empty((w.B, w.H, w.L, w.d_v), dtype=torch.bfloat16, device="cuda")
+    d = _dims(w)
+    mc.mc_grm_readout(d, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], fwd["M"],
+                      fwd["M_lo"], fwd["P"], None, Y, None,
+                      ws=mc.workspace(d, mc.MC_OP_GRM), stream=None)
+    torch.cuda.synchronize()
+
+    def dot(a, b):
+        return float((a.double() * b.double()).sum())
+    ref = dot(dY, Y)
+    # rounding errors (bf16 Y and states) enter every term with its own sign, so the scale of
+    # the deviation is the root of the summed squares, not the sum of magnitudes
+    scale = float(((dY.double() * Y.double()) ** 2).sum().sqrt())
+    for k, x in (("dV", inp["V"]), ("dQ", inp["Q"]), ("dK", inp["K"])):
+        e = abs(dot(got[k], x) - ref) / scale
+        announce("  sum(%s*%s) = %.6g, sum(dY*Y) = %.6g, deviation / rms scale %.3g"
+                 % (k, k[1:], dot(got[k], x), ref, e))
+        assert e <= TOL["bf16"], (k, e)
+    rows = _sample_rows(w.L, w.seg_len, 128, seed=13)
+    for b, h in [(0, 0), (0, 29)]:
+        hin = _head(inp, b, h)
+        r = oracle.grm_backward(hin["Q"], hin["K"], hin["V"], hin["U"], hin["X"],
+                                dY[b:b + 1, h:h + 1].to(torch.float64).cpu().numpy(),
+                                seg_len=w.seg_len, phi=w.phi, rows=rows)
+        errs = {k: slice_rel_err(to_np(got[k][b:b + 1, h:h + 1, rows]), r[k]) for k in ("dQ", "dU")}
+        announce("  (b=%d, h=%d) %d rows: %s" % (b, h, len(rows), errs))
+        for k, e in errs.items():
+            assert e <= TOL["bf16"], (k, e)
+    del inp, dY, fwd, got, Y
     torch.cuda.empty_cache()

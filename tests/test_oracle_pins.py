@@ -626,3 +626,14 @@ def test_backward_matches_autograd_of_token_pair_form(L, C, phi, xh):
     for name, t in zip(("dQ", "dK", "dV", "dU", "dX"), ts):
         np.testing.assert_allclose(got[name], t.grad.numpy(), rtol=1e-10, atol=1e-11,
                                    err_msg=name)
+
+
+def test_backward_rows_are_the_full_gradients_at_those_rows():
+    B, H, L, C = 1, 2, 30, 7
+    Q, K, V, U, X = _rand(B, H, L, 4, 3, 5, seed=65)
+    dY = np.random.default_rng(66).standard_normal(V.shape)
+    full = oracle.grm_backward(Q, K, V, U, X, dY, seg_len=C, phi="elu1")
+    rows = [0, 6, 7, 13, 29]
+    part = oracle.grm_backward(Q, K, V, U, X, dY, seg_len=C, phi="elu1", rows=rows)
+    np.testing.assert_array_equal(part["dQ"], full["dQ"][:, :, rows])
+    np.testing.assert_array_equal(part["dU"], full["dU"][:, :, rows])
