@@ -466,7 +466,7 @@ def run_backward(args, rec, dev):
     """The backward of the GRM prefill (training) at the L=4K workload and the L=64K
     workload's shape: forward once, then mc_grm_backward timed with HIP events on its stream
     (inputs, states and dY resident).  tokens/s of the backward alone; algorithmic FLOPs
-    against the fp32 vector peak its kernels run on."""
+    against the peak of the units its dense contractions run on."""
     import torch
 
     import chunked_linear_attention_segment_amd as mc
@@ -505,10 +505,14 @@ def run_backward(args, rec, dev):
         ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
         fl = backward_flops(B, H, L, C, dk, dv, dg)
         tf = fl / (ms / 1e3) / 1e12
+        # bf16 with d_k = d_v = 128 runs the dense contractions on MFMA; other shapes on the
+        # fp32 vector units
+        mfma = w.dtype == "bf16" and dk == 128 and dv == 128
+        peak = PEAK_BF16_TFLOPS if mfma else 157.3
         out[name] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(B * L / (ms / 1e3), 1),
                      "steps": steps,
-                     "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": 157.3,
-                                  "unit": "TFLOP/s", "frac": round(tf / 157.3, 4),
+                     "roofline": {"bound": "mfma" if mfma else "alu", "achieved": round(tf, 2),
+                                  "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4),
                                   "algorithmic_flops": fl}}
         del inp, dY, fwd, g, ws
         torch.cuda.empty_cache()

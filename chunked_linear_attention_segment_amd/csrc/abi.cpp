@@ -71,7 +71,19 @@ BwdWorkspace bwd_workspace(const mc_dims& d) {
     w.lse = w.D = w.gs = align256(sizeof(float) * bhl);
     w.dG = align256(sizeof(float) * bhl * num_segments(d));
     w.dM = align256(sizeof(float) * (size_t)d.B * d.H * num_segments(d) * d.d_v * d.d_k);
-    w.total = w.aon + w.xps + w.xtail + w.on + w.ot + w.khat + w.lse + w.D + w.gs + w.dG + w.dM;
+    const int RL = bwd_dp_range(d.L);
+    w.dpp = align256(sizeof(float) * (size_t)((d.L + RL - 1) / RL) * num_segments(d) * d.B *
+                     d.x_heads * d.d_g);
+    if (bwd_fast(d)) {  // the swapped read and the gate numerators replace Ot, lse and D
+        w.ot = w.lse = w.D = 0;
+        w.W = align256(gate_w_bytes(d));
+        w.won = w.inv_l = align256(sizeof(float) * bhl);
+        w.pf = align256(gate_pfrag_bytes(d));
+        w.mt = align256(sizeof(uint16_t) * (size_t)d.B * d.H * num_segments(d) * d.d_v * d.d_k);
+        w.dqh = align256(sizeof(uint16_t) * bhl * d.d_k);
+    }
+    w.total = w.aon + w.xps + w.xtail + w.on + w.ot + w.khat + w.lse + w.D + w.gs + w.dG + w.dM +
+              w.dpp + w.W + w.won + w.inv_l + w.pf + w.mt + w.dqh;
     return w;
 }
 
@@ -346,6 +358,20 @@ mc_status mc_grm_backward(const mc_dims* d, const void* Q, const void* K, const 
     bw.dG = (float*)b;
     b += w.dG;
     bw.dM = (float*)b;
+    b += w.dM;
+    bw.dpp = (float*)b;
+    b += w.dpp;
+    bw.W = (uint16_t*)b;
+    b += w.W;
+    bw.won = (float*)b;
+    b += w.won;
+    bw.inv_l = (float*)b;
+    b += w.inv_l;
+    bw.pf = b;
+    b += w.pf;
+    bw.mt = b;
+    b += w.mt;
+    bw.dqh = b;
     return launch_grm_backward(*d, bw, Q, K, V, U, X, M, M_lo, P, dY, dQ, dK, dV, dU, dX,
                                stream)
                ? MC_ERR_HIP

@@ -312,36 +312,80 @@ __global__ __launch_bounds__(256) void bwd_online_kernel(
     }
 }
 
-// dx for segment i of x head bx: dP_i = sum over the group's heads and the tokens after
-// segment i of da_t^(i) u_t, then for r in the segment (in reverse) the prefix-mean terms
-// sum_{t >= r} da_t^(s) u_t / (j_t + 1).  Thread e owns gate column e.
+// dx in three steps (x head bx; with one shared x head its sums run over every head):
+//   bwd_dxw_kernel    w_t = sum_h da_t^(s) u_t / (j_t + 1), the prefix-mean term of token t
+//   bwd_dp_kernel     partial dP_i = sum_h sum_t da_t^(i) u_t over one token range (3-D grid:
+//                     segment, x head, token range; token lanes reduced through LDS)
+//   bwd_dxf_kernel    dP_i from the partials; dx_r = dP_i / |S_i| + sum_{t >= r in S_i} w_t
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_dx_kernel(const T* __restrict__ U,
-                                                     const float* __restrict__ dA, int L, int C,
-                                                     int NS, int DG, int H, int xh,
-                                                     float* __restrict__ dX) {
-    const int i = blockIdx.x;
+__global__ __launch_bounds__(256) void bwd_dxw_kernel(const T* __restrict__ U,
+                                                      const float* __restrict__ dA, int L,
+                                                      int C, int NS, int DG, int H, int xh,
+                                                      float* __restrict__ w) {
+    const int t0 = blockIdx.x * 64;
     const size_t bx = blockIdx.y;
     const int b = (int)(bx / xh), hx = (int)(bx % xh);
+    const int h0 = xh == 1 ? 0 : hx, h1 = xh == 1 ? H : hx + 1;
+    for (int idx = threadIdx.x; idx < 64 * DG; idx += 256) {
+        const int t = t0 + idx / DG, e = idx % DG;
+        if (t >= L) break;
+        const int s = t / C, j = t - s * C;
+        float acc = 0.f;
+        for (int h = h0; h < h1; ++h) {
+            const size_t bh = (size_t)b * H + h;
+            acc += dA[(bh * L + t) * NS + s] * ld(U, (bh * L + t) * DG + e);
+        }
+        w[(bx * L + t) * DG + e] = acc / (float)(j + 1);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dp_kernel(const T* __restrict__ U,
+                                                     const float* __restrict__ dA, int L, int C,
+                                                     int NS, int DG, int H, int xh, int RL,
+                                                     float* __restrict__ part) {
+    __shared__ float red[256];
+    const int i = blockIdx.x;
+    const size_t bx = blockIdx.y;
+    const int rg = blockIdx.z;
+    const int b = (int)(bx / xh), hx = (int)(bx % xh);
+    const int h0 = xh == 1 ? 0 : hx, h1 = xh == 1 ? H : hx + 1;
+    const int TL = 256 / DG;  // token lanes (DG <= 256)
+    const int tid = threadIdx.x, e = tid % DG, tl = tid / DG;
+    const int lo = max(rg * RL, (i + 1) * C), hi = min(L, (rg + 1) * RL);
+    float acc = 0.f;
+    if (tl < TL)
+        for (int h = h0; h < h1; ++h) {
+            const size_t bh = (size_t)b * H + h;
+            for (int t = lo + tl; t < hi; t += TL)
+                acc += dA[(bh * L + t) * NS + i] * ld(U, (bh * L + t) * DG + e);
+        }
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < DG) {
+        float v = 0.f;
+        for (int k = 0; k < TL; ++k) v += red[k * DG + tid];
+        part[(((size_t)rg * NS + i) * gridDim.y + bx) * DG + tid] = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void bwd_dxf_kernel(const float* __restrict__ part,
+                                                      const float* __restrict__ w, int L, int C,
+                                                      int NS, int DG, int NR,
+                                                      float* __restrict__ dX) {
+    const int i = blockIdx.x;
+    const size_t bx = blockIdx.y;
     const int e = threadIdx.x;
     if (e >= DG) return;  // no barriers below
-    const int h0 = xh == 1 ? 0 : hx, h1 = xh == 1 ? H : hx + 1;
     float dp = 0.f;
-    for (int h = h0; h < h1; ++h) {
-        const size_t bh = (size_t)b * H + h;
-        for (int t = (i + 1) * C; t < L; ++t)
-            dp += dA[(bh * L + t) * NS + i] * ld(U, (bh * L + t) * DG + e);
-    }
+    for (int rg = 0; rg < NR; ++rg) dp += part[(((size_t)rg * NS + i) * gridDim.y + bx) * DG + e];
     const int t0 = i * C, len = min(C, L - t0);
     const float base = dp / (float)len;
     float tail = 0.f;
     for (int jj = len - 1; jj >= 0; --jj) {
-        const int t = t0 + jj;
-        for (int h = h0; h < h1; ++h) {
-            const size_t bh = (size_t)b * H + h;
-            tail += dA[(bh * L + t) * NS + i] * ld(U, (bh * L + t) * DG + e) / (float)(jj + 1);
-        }
-        dX[(bx * L + t) * DG + e] = base + tail;
+        const size_t o = (bx * L + t0 + jj) * DG + e;
+        tail += w[o];
+        dX[o] = base + tail;
     }
 }
 
@@ -361,23 +405,35 @@ __global__ void feature_kernel_f32(const float* __restrict__ K, size_t n, int ph
 template <typename T, typename TS, int DK, int DV>
 int launch_bwd_t(const mc_dims& d, const BwdBuffers& w, const void* Q, const void* K,
                  const void* V, const void* U, const void* S, const float* P, const void* dY,
-                 float* dQ, float* dK, float* dV, float* dU, float* dX, hipStream_t st) {
+                 float* dQ, float* dK, float* dV, float* dU, float* dX, bool fast,
+                 hipStream_t st) {
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     const dim3 tiles((d.L + BTT - 1) / BTT, d.B * d.H);
-    hipLaunchKernelGGL((bwd_cached_kernel<T, TS, DK, DV>), tiles, dim3(256), 0, st, (const T*)Q,
-                       (const T*)U, w.aon, (const TS*)S, P, w.on, (const T*)dY, d.L, d.seg_len,
-                       NS, d.d_g, d.H, d.x_heads, d.phi, w.dG, w.lse, w.D, w.gs, dQ);
-    hipLaunchKernelGGL((bwd_gate_kernel<T, DK>), tiles, dim3(256), 0, st, (const T*)Q,
-                       (const T*)U, P, w.xps, w.lse, w.D, w.gs, w.ot, d.L, d.seg_len, NS,
-                       d.d_g, d.H, d.x_heads, d.phi, w.dG, dU, dQ);
-    hipLaunchKernelGGL((bwd_dm_kernel<T, DK, DV>), dim3(NS, d.B * d.H), dim3(256), 0, st,
-                       (const T*)Q, (const T*)U, P, w.lse, (const T*)dY, d.L, d.seg_len, NS,
-                       d.d_g, d.H, d.x_heads, d.phi, w.dM);
+    if (!fast) {  // dgamma, the gate backward and dM on the fp32 vector units
+        hipLaunchKernelGGL((bwd_cached_kernel<T, TS, DK, DV>), tiles, dim3(256), 0, st,
+                           (const T*)Q, (const T*)U, w.aon, (const TS*)S, P, w.on, (const T*)dY,
+                           d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads, d.phi, w.dG, w.lse, w.D,
+                           w.gs, dQ);
+        hipLaunchKernelGGL((bwd_gate_kernel<T, DK>), tiles, dim3(256), 0, st, (const T*)Q,
+                           (const T*)U, P, w.xps, w.lse, w.D, w.gs, w.ot, d.L, d.seg_len, NS,
+                           d.d_g, d.H, d.x_heads, d.phi, w.dG, dU, dQ);
+        hipLaunchKernelGGL((bwd_dm_kernel<T, DK, DV>), dim3(NS, d.B * d.H), dim3(256), 0, st,
+                           (const T*)Q, (const T*)U, P, w.lse, (const T*)dY, d.L, d.seg_len, NS,
+                           d.d_g, d.H, d.x_heads, d.phi, w.dM);
+    }
     hipLaunchKernelGGL((bwd_online_kernel<T, DK, DV>), dim3(NS, d.B * d.H), dim3(256), 0, st,
                        (const T*)Q, (const T*)K, (const T*)V, (const T*)dY, w.gs, w.dM, d.L,
                        d.seg_len, NS, d.phi, dK, dV);
-    hipLaunchKernelGGL((bwd_dx_kernel<T>), dim3(NS, d.B * d.x_heads), dim3(256), 0, st,
-                       (const T*)U, w.dG, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads, dX);
+    // x gradients; the prefix sums of X are no longer needed, so w_t goes in their place
+    const int bxn = d.B * d.x_heads;
+    hipLaunchKernelGGL((bwd_dxw_kernel<T>), dim3((d.L + 63) / 64, bxn), dim3(256), 0, st,
+                       (const T*)U, w.dG, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads, w.xps);
+    const int RL = bwd_dp_range(d.L);
+    const int NR = (d.L + RL - 1) / RL;
+    hipLaunchKernelGGL((bwd_dp_kernel<T>), dim3(NS, bxn, NR), dim3(256), 0, st, (const T*)U,
+                       w.dG, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads, RL, w.dpp);
+    hipLaunchKernelGGL(bwd_dxf_kernel, dim3(NS, bxn), dim3(256), 0, st, w.dpp, w.xps, d.L,
+                       d.seg_len, NS, d.d_g, NR, dX);
     return (int)hipGetLastError();
 }
 
@@ -388,12 +444,11 @@ int launch_grm_backward(const mc_dims& d, const BwdBuffers& w, const void* Q, co
                         const uint16_t* M_lo, const float* P, const void* dY, float* dQ,
                         float* dK, float* dV, float* dU, float* dX, void* stream) {
     hipStream_t st = (hipStream_t)stream;
-    int rc = launch_aon(d, X, U, w.aon, stream);
-    if (!rc) rc = launch_xps(d, X, w.xps, w.xtail, stream);
-    if (!rc) rc = launch_scan_online(d, Q, K, V, w.on, stream);
+    const bool fast = bwd_fast(d);
+    int rc = launch_xps(d, X, w.xps, w.xtail, stream);
     if (rc) return rc;
-    // Ot[t] = M_t^(s)T dy_t: the online scan with q := dy, k := v, v := phi(k), identity map
-    const void* khat = K;
+    // phi(K) in the input dtype: the values of the transposed online read
+    BwdBuffers wb = w;
     if (d.phi) {
         const size_t n = (size_t)d.B * d.H * d.L * d.d_k;
         const int blocks = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
@@ -403,21 +458,35 @@ int launch_grm_backward(const mc_dims& d, const BwdBuffers& w, const void* Q, co
         else
             hipLaunchKernelGGL(feature_kernel_f32, dim3(blocks), dim3(256), 0, st,
                                (const float*)K, n, d.phi, (float*)w.khat);
-        khat = w.khat;
+    } else {
+        wb.khat = nullptr;
     }
-    mc_dims dt = d;
-    dt.d_k = d.d_v;
-    dt.d_v = d.d_k;
-    dt.phi = MC_PHI_IDENTITY;
-    rc = launch_scan_online(dt, dY, V, khat, w.ot, stream);
-    if (rc) return rc;
+    if (fast) {
+        // the forward's gate pass (softmax numerators per read tile), the online read, then
+        // dgamma, dphi(q), the gate backward and dM on MFMA
+        rc = launch_gate_w(d, U, w.xps, P, w.pf, w.W, w.won, w.inv_l, stream);
+        if (!rc) rc = launch_scan_mfma_online(d, Q, K, V, w.on, stream);
+        if (!rc) rc = launch_bwd_fast(d, wb, Q, K, V, U, M, M_lo, P, dY, dQ, dU, stream);
+        if (rc) return rc;
+    } else {
+        rc = launch_aon(d, X, U, w.aon, stream);
+        if (!rc) rc = launch_scan_online(d, Q, K, V, w.on, stream);
+        if (rc) return rc;
+        // Ot[t] = M_t^(s)T dy_t: the online scan with q := dy, k := v, v := phi(k)
+        mc_dims dt = d;
+        dt.d_k = d.d_v;
+        dt.d_v = d.d_k;
+        dt.phi = MC_PHI_IDENTITY;
+        rc = launch_scan_online(dt, dY, V, wb.khat ? wb.khat : K, w.ot, stream);
+        if (rc) return rc;
+    }
 #define MC_BW(DK, DV)                                                                        \
     if (d.d_k == DK && d.d_v == DV)                                                          \
         return d.dtype == MC_BF16                                                            \
                    ? launch_bwd_t<bf16_t, bf16_t, DK, DV>(d, w, Q, K, V, U, M_lo, P, dY, dQ, \
-                                                          dK, dV, dU, dX, st)                \
+                                                          dK, dV, dU, dX, fast, st)          \
                    : launch_bwd_t<float, float, DK, DV>(d, w, Q, K, V, U, M, P, dY, dQ, dK,  \
-                                                        dV, dU, dX, st);
+                                                        dV, dU, dX, fast, st);
     MC_BW(128, 128)
     MC_BW(128, 64)
     MC_BW(64, 128)

@@ -88,11 +88,32 @@ struct BwdBuffers {
     float* gs;     // [B,H,L] online weight gamma_s
     float* dG;     // [B,H,L,NS] dgamma, then da
     float* dM;     // [B,H,NS,dv,dk] gradient of each cached state
+    float* dpp;    // [NR,NS,B*xh,dg] partial sums of dP_i over token ranges
+    // the MFMA path (bf16, d_k = d_v = 128 with the forward gate pass):
+    uint16_t* W;   // gate numerators per read tile (gate pass layout)
+    float* won;    // [B,H,L] online numerator
+    float* inv_l;  // [B,H,L] 1 / softmax denominator
+    void* pf;      // the means as MFMA fragments
+    void* mt;      // [B,H,NS,dk,dv] bf16 transposed states
+    void* dqh;     // [B,H,L,dk] bf16 dphi(q) from the swapped read
 };
 struct BwdWorkspace {
-    size_t aon, xps, xtail, on, ot, khat, lse, D, gs, dG, dM, total;
+    size_t aon, xps, xtail, on, ot, khat, lse, D, gs, dG, dM, dpp;
+    size_t W, won, inv_l, pf, mt, dqh, total;
 };
+// The MFMA backward applies where the forward uses the gate pass (bf16, d_k = d_v = 128).
+inline bool bwd_fast(const mc_dims& d) { return gate_pass(d); }
+int launch_bwd_fast(const mc_dims& d, const BwdBuffers& w, const void* Q, const void* K,
+                    const void* V, const void* U, const float* M, const uint16_t* M_lo,
+                    const float* P, const void* dY, float* dQ, float* dU, void* stream);
+// tokens per range of the dP partial sums: a multiple of 64, at most 64 ranges
+inline int bwd_dp_range(int L) {
+    const int r = (L + 63) / 64;
+    return (r + 63) / 64 * 64;
+}
 BwdWorkspace bwd_workspace(const mc_dims& d);
+int launch_scan_mfma_online(const mc_dims& d, const void* Q, const void* K, const void* V,
+                            float* O_on, void* stream);
 int launch_grm_backward(const mc_dims& d, const BwdBuffers& w, const void* Q, const void* K,
                         const void* V, const void* U, const void* X, const float* M,
                         const uint16_t* M_lo, const float* P, const void* dY, float* dQ,

@@ -306,6 +306,7 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
         __syncthreads();
     }
     // ---- emit the segment state: M[cv][d] (fp32 and bf16), 4 consecutive d per group ----
+    if (!M) return;  // online read only
     const int cv = wave * 32 + l32;
     const size_t mo = ((bh * NS + s) * DV + cv) * (size_t)DK;
 #pragma unroll
@@ -339,6 +340,23 @@ static int launch_scan_mfma_t(const mc_dims& d, const void* Q, const void* K, co
     }
 #undef MC_SCAN
     return (int)hipGetLastError();
+}
+
+// The online read alone (no state output) on the MFMA scan; -1 when the sizes are not covered.
+int launch_scan_mfma_online(const mc_dims& d, const void* Q, const void* K, const void* V,
+                            float* O_on, void* stream) {
+    if (d.dtype != MC_BF16 || !O_on) return -1;
+    hipStream_t st = (hipStream_t)stream;
+    const SwlaGates none{};
+#define MC_SD(DK, DV)                                                                          \
+    if (d.d_k == DK && d.d_v == DV)                                                            \
+        return launch_scan_mfma_t<DK, DV>(d, Q, K, V, nullptr, nullptr, O_on, none, st);
+    MC_SD(128, 128)
+    MC_SD(128, 64)
+    MC_SD(64, 128)
+    MC_SD(64, 64)
+#undef MC_SD
+    return -1;
 }
 
 // bf16 scan on MFMA; -1 when the sizes are not covered (the caller uses the generic kernel).

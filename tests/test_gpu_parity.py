@@ -405,6 +405,11 @@ BWD_CASES = {
     "bf16_d128v64_C48_L333_elu": Workload("x", 2, 2, 333, 128, 64, 64, 48, "elu1", "bf16"),
     "bf16_d64_C16_L640_many_segments": Workload("x", 1, 2, 640, 64, 64, 32, 16, "identity",
                                                 "bf16"),
+    # bf16 with d_k = d_v = 128: the MFMA backward (swapped read, dgamma and dM on MFMA)
+    "bf16_d128_C48_L500_elu": Workload("x", 2, 2, 500, 128, 128, 64, 48, "elu1", "bf16"),
+    "bf16_d128_C512_L1536": Workload("x", 1, 2, 1536, 128, 128, 128, 512, "identity", "bf16"),
+    "bf16_d128_C16_L640_xheadsH": Workload("x", 1, 2, 640, 128, 128, 32, 16, "identity", "bf16",
+                                           x_heads=2),
 }
 
 
