@@ -72,8 +72,9 @@ BwdWorkspace bwd_workspace(const mc_dims& d) {
     w.dG = align256(sizeof(float) * bhl * num_segments(d));
     w.dM = align256(sizeof(float) * (size_t)d.B * d.H * num_segments(d) * d.d_v * d.d_k);
     const int RL = bwd_dp_range(d.L);
-    w.dpp = align256(sizeof(float) * (size_t)((d.L + RL - 1) / RL) * num_segments(d) * d.B *
-                     d.x_heads * d.d_g);
+    const size_t nr = (size_t)((d.L + RL - 1) / RL);  // token ranges (at most 64)
+    w.dpp = align256(sizeof(float) * (bwd_fast(d) ? (size_t)d.H * d.B : nr * d.B * d.x_heads) *
+                     num_segments(d) * d.d_g);
     if (bwd_fast(d)) {  // the swapped read and the gate numerators replace Ot, lse and D
         w.ot = w.lse = w.D = 0;
         w.W = align256(gate_w_bytes(d));
@@ -81,9 +82,10 @@ BwdWorkspace bwd_workspace(const mc_dims& d) {
         w.pf = align256(gate_pfrag_bytes(d));
         w.mt = align256(sizeof(uint16_t) * (size_t)d.B * d.H * num_segments(d) * d.d_v * d.d_k);
         w.dqh = align256(sizeof(uint16_t) * bhl * d.d_k);
+        w.daT = align256(sizeof(float) * bhl * num_segments(d));
     }
     w.total = w.aon + w.xps + w.xtail + w.on + w.ot + w.khat + w.lse + w.D + w.gs + w.dG + w.dM +
-              w.dpp + w.W + w.won + w.inv_l + w.pf + w.mt + w.dqh;
+              w.dpp + w.W + w.won + w.inv_l + w.pf + w.mt + w.dqh + w.daT;
     return w;
 }
 
@@ -372,6 +374,8 @@ mc_status mc_grm_backward(const mc_dims* d, const void* Q, const void* K, const 
     bw.mt = b;
     b += w.mt;
     bw.dqh = b;
+    b += w.dqh;
+    bw.daT = (float*)b;
     return launch_grm_backward(*d, bw, Q, K, V, U, X, M, M_lo, P, dY, dQ, dK, dV, dU, dX,
                                stream)
                ? MC_ERR_HIP

@@ -428,10 +428,14 @@ int launch_bwd_t(const mc_dims& d, const BwdBuffers& w, const void* Q, const voi
     const int bxn = d.B * d.x_heads;
     hipLaunchKernelGGL((bwd_dxw_kernel<T>), dim3((d.L + 63) / 64, bxn), dim3(256), 0, st,
                        (const T*)U, w.dG, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads, w.xps);
+    // dP_i: partial sums over token ranges, or (MFMA path) per head from the dM walk
     const int RL = bwd_dp_range(d.L);
-    const int NR = (d.L + RL - 1) / RL;
-    hipLaunchKernelGGL((bwd_dp_kernel<T>), dim3(NS, bxn, NR), dim3(256), 0, st, (const T*)U,
-                       w.dG, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads, RL, w.dpp);
+    int NR = (d.L + RL - 1) / RL;
+    if (fast)
+        NR = d.x_heads == 1 ? d.H : 1;
+    else
+        hipLaunchKernelGGL((bwd_dp_kernel<T>), dim3(NS, bxn, NR), dim3(256), 0, st, (const T*)U,
+                           w.dG, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads, RL, w.dpp);
     hipLaunchKernelGGL(bwd_dxf_kernel, dim3(NS, bxn), dim3(256), 0, st, w.dpp, w.xps, d.L,
                        d.seg_len, NS, d.d_g, NR, dX);
     return (int)hipGetLastError();

@@ -160,91 +160,165 @@ __global__ __launch_bounds__(256, 1) void bwd_dgamma_kernel(
 constexpr int CHK = 64;    // tokens per chunk of the dM walk
 constexpr int TPAD = 72;   // row stride (bf16) of the token-indexed LDS tiles
 
-// dM^(i) (stored [c][r] like the states) for d_k = d_v = 128: M^T-style accumulation
-// dM^T[r][c] += sum_t phi(q_t)[r] (gamma_t^(i) dy_t[c]); wave w owns value columns
-// c in [32w, 32w+32) and keeps the four 32-row blocks of r in its accumulators.  phi(q)^T and
-// (gamma dy)^T are staged in LDS with token pairs packed in 32-bit words (the token index is
-// the contraction index).  gamma_t^(i) = W_t^(i) / l_t from the forward gate pass.
-__global__ __launch_bounds__(256, 1) void bwd_dm_mfma_kernel(
+constexpr int SPW = 4;  // cached segments per dM workgroup (8 waves: 2 per segment)
+
+// dM^(i) (stored [c][r] like the states) for d_k = d_v = 128 and d_g <= 128, SPW consecutive
+// segments i0.. per workgroup so that each later token is staged once for all of them:
+// dM^T[r][c] += sum_t phi(q_t)[r] (gamma_t^(i) dy_t[c]).  Wave w serves segment i0 + w / 2 and
+// value columns c in [64 (w % 2), +64), keeping the four 32-row blocks of r for its two
+// 32-column blocks in its accumulators.  phi(q)^T (shared) and (gamma^(i) dy)^T (one per
+// segment) are staged in LDS with token pairs packed in 32-bit words (the token index is the
+// contraction index); the next chunk's rows are loaded into registers while the current one
+// is contracted.  gamma_t^(i) = W_t^(i) / l_t from the forward gate pass, zero unless token t
+// lies after segment i.  Alongside, dP_i of this head = sum_t da_t^(i) u_t.
+__global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ dY, const uint16_t* __restrict__ Wg,
-    const float* __restrict__ inv_l, int L, int C, int NS, int phi, float* __restrict__ dM) {
-    __shared__ __attribute__((aligned(16))) bf16_t qt[128][TPAD];  // phi(q)^T [r][t]
-    __shared__ __attribute__((aligned(16))) bf16_t gt[128][TPAD];  // (gamma dy)^T [c][t]
-    __shared__ float sg[CHK];
-    const int i = blockIdx.x;  // low i (the most tokens) is dispatched first
+    const float* __restrict__ inv_l, const bf16_t* __restrict__ U,
+    const float* __restrict__ daT, int L, int C, int NS, int DG, int H, int xh, int phi,
+    float* __restrict__ dM, float* __restrict__ dP) {
+    __shared__ __attribute__((aligned(16))) bf16_t qt[128][TPAD];       // phi(q)^T [r][t]
+    __shared__ __attribute__((aligned(16))) bf16_t gt[SPW][128][TPAD];  // (gamma dy)^T [c][t]
+    __shared__ __attribute__((aligned(16))) bf16_t su[CHK][128];        // u_t
+    __shared__ float sda[SPW][CHK];
+    const int i0 = blockIdx.x * SPW;  // low segments (the most tokens) are dispatched first
     const size_t bh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, half = lane >> 5;
     const int T = (L + kGateTile - 1) / kGateTile;
-    f32x16_t mt[4];
+    const int DG8 = DG / 8;
+    const int nseg = min(SPW, NS - i0);
+    f32x16_t mt[4][2];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt[db][r] = 0.f;
-    for (int j0 = (i + 1) * C; j0 < L; j0 += CHK) {
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt[db][cb][r] = 0.f;
+    // dP: thread (k, e) = (tid / 128, tid % 128) sums column e of segment i0 + k
+    const int kdp = tid >> 7, edp = tid & 127;
+    float dp0 = 0.f, dp1 = 0.f, dp2 = 0.f, dp3 = 0.f;
+
+    // one chunk in registers: staging slot (token pair 2p, 2p+1; columns dc..dc+7) of phi(q)
+    // and dy, the SPW gate weights of both tokens, two slots of u rows, one da
+    u32x4_t rq[2], ry[2], ru[2];
+    float rg[2][SPW], rda = 0.f;
+    auto load = [&](int j0) {
         const int n = min(CHK, L - j0);
-        if (tid < CHK) {
-            const int t = j0 + tid;
-            float g = 0.f;
-            if (tid < n)
-                g = bf16_to_f32(Wg[((bh * T + t / kGateTile) * NS + i) * kGateTile + t % kGateTile]) *
-                    inv_l[bh * L + t];
-            sg[tid] = g;
+        const int p = tid % (CHK / 2), dc = (tid / (CHK / 2)) * 8;
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+            const int r = 2 * p + o, t = j0 + r;
+            u32x4_t q = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int k = 0; k < SPW; ++k) rg[o][k] = 0.f;
+            if (r < n) {
+                const size_t row = bh * L + t;
+                q = *reinterpret_cast<const u32x4_t*>(Q + row * 128 + dc);
+                y = *reinterpret_cast<const u32x4_t*>(dY + row * 128 + dc);
+                const float il = inv_l[row];
+                const int st = t / C;
+                const uint16_t* wr = Wg + ((bh * T + t / kGateTile) * NS) * kGateTile + t % kGateTile;
+#pragma unroll
+                for (int k = 0; k < SPW; ++k)
+                    if (i0 + k < st) rg[o][k] = bf16_to_f32(wr[(size_t)(i0 + k) * kGateTile]) * il;
+            }
+            rq[o] = q;
+            ry[o] = y;
         }
-        __syncthreads();
-        // stage phi(q)^T and (gamma dy)^T, token pairs packed in 32-bit words
-        for (int it = tid; it < (CHK / 2) * 16; it += 256) {
-            const int p = it % (CHK / 2), dc = (it / (CHK / 2)) * 8;
-            const int r0 = 2 * p, r1 = 2 * p + 1;
-            u32x4_t a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-            u32x4_t ya = {0u, 0u, 0u, 0u}, yb = {0u, 0u, 0u, 0u};
-            if (r0 < n) {
-                a = phi8(*reinterpret_cast<const u32x4_t*>(Q + (bh * L + j0 + r0) * 128 + dc), phi);
-                ya = *reinterpret_cast<const u32x4_t*>(dY + (bh * L + j0 + r0) * 128 + dc);
-            }
-            if (r1 < n) {
-                b = phi8(*reinterpret_cast<const u32x4_t*>(Q + (bh * L + j0 + r1) * 128 + dc), phi);
-                yb = *reinterpret_cast<const u32x4_t*>(dY + (bh * L + j0 + r1) * 128 + dc);
-            }
-            const float g0 = sg[r0], g1 = sg[r1];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int it = tid + 512 * k, tt = it / DG8, e8 = (it % DG8) * 8;
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (tt < n) v = *reinterpret_cast<const u32x4_t*>(U + (bh * L + j0 + tt) * DG + e8);
+            ru[k] = v;
+        }
+        {  // da_t^(i0+k): thread (k, tt) = (tid / 64, tid % 64) for tid < SPW * 64
+            const int k = tid / CHK, tt = tid % CHK, t = j0 + tt;
+            rda = (k < nseg && tt < n && t / C > i0 + k) ? daT[(bh * NS + i0 + k) * L + t] : 0.f;
+        }
+    };
+    const int first = (i0 + 1) * C;
+    if (first < L) load(first);
+    for (int j0 = first; j0 < L; j0 += CHK) {
+        const int n = min(CHK, L - j0);
+        {  // registers -> LDS
+            const int p = tid % (CHK / 2), dc = (tid / (CHK / 2)) * 8, r0 = 2 * p;
+            const u32x4_t a = phi8(rq[0], phi), b = phi8(rq[1], phi);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 *reinterpret_cast<uint32_t*>(&qt[dc + 2 * e][r0]) = (a[e] & 0xffffu) | (b[e] << 16);
                 *reinterpret_cast<uint32_t*>(&qt[dc + 2 * e + 1][r0]) = (a[e] >> 16) | (b[e] & 0xffff0000u);
-                *reinterpret_cast<uint32_t*>(&gt[dc + 2 * e][r0]) =
-                    pack_bf16x2(g0 * bf_lo(ya[e]), g1 * bf_lo(yb[e]));
-                *reinterpret_cast<uint32_t*>(&gt[dc + 2 * e + 1][r0]) =
-                    pack_bf16x2(g0 * bf_hi(ya[e]), g1 * bf_hi(yb[e]));
             }
+#pragma unroll
+            for (int k = 0; k < SPW; ++k) {
+                const float g0 = rg[0][k], g1 = rg[1][k];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    *reinterpret_cast<uint32_t*>(&gt[k][dc + 2 * e][r0]) =
+                        pack_bf16x2(g0 * bf_lo(ry[0][e]), g1 * bf_lo(ry[1][e]));
+                    *reinterpret_cast<uint32_t*>(&gt[k][dc + 2 * e + 1][r0]) =
+                        pack_bf16x2(g0 * bf_hi(ry[0][e]), g1 * bf_hi(ry[1][e]));
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int it = tid + 512 * k, tt = it / DG8, e8 = (it % DG8) * 8;
+                if (tt < CHK) *reinterpret_cast<u32x4_t*>(&su[tt][e8]) = ru[k];
+            }
+            if (tid < SPW * CHK) sda[tid / CHK][tid % CHK] = rda;
         }
         __syncthreads();
-        const int cv = wave * 32 + l32;
-        u32x4_t gb[CHK / 16];
+        if (j0 + CHK < L) load(j0 + CHK);  // the next chunk's loads overlap this chunk's work
+        const int k = wave >> 1, c0 = (wave & 1) * 64;
+        u32x4_t gb[2][CHK / 16];
 #pragma unroll
-        for (int ks = 0; ks < CHK / 16; ++ks)
-            gb[ks] = *reinterpret_cast<const u32x4_t*>(&gt[cv][ks * 16 + half * 8]);
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int ks = 0; ks < CHK / 16; ++ks)
+                gb[cb][ks] = *reinterpret_cast<const u32x4_t*>(&gt[k][c0 + cb * 32 + l32][ks * 16 + half * 8]);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
             const int r = db * 32 + l32;
 #pragma unroll
             for (int ks = 0; ks < CHK / 16; ++ks) {
                 const u32x4_t qa = *reinterpret_cast<const u32x4_t*>(&qt[r][ks * 16 + half * 8]);
-                mt[db] = mfma32(qa, gb[ks], mt[db]);
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) mt[db][cb] = mfma32(qa, gb[cb][ks], mt[db][cb]);
             }
+        }
+        if (edp < DG) {
+            int tt = 0;
+            for (; tt + 3 < n; tt += 4) {
+                dp0 += sda[kdp][tt] * bf16_to_f32(su[tt][edp]);
+                dp1 += sda[kdp][tt + 1] * bf16_to_f32(su[tt + 1][edp]);
+                dp2 += sda[kdp][tt + 2] * bf16_to_f32(su[tt + 2][edp]);
+                dp3 += sda[kdp][tt + 3] * bf16_to_f32(su[tt + 3][edp]);
+            }
+            for (; tt < n; ++tt) dp0 += sda[kdp][tt] * bf16_to_f32(su[tt][edp]);
         }
         __syncthreads();
     }
-    // dM[c][r]: lane holds c = 32 wave + l32 and r = 32 db + 8g + 4 half + e
-    const int cv = wave * 32 + l32;
-    float* out = dM + ((bh * NS + i) * 128 + cv) * (size_t)128;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const size_t rgi = xh == 1 ? h : 0, bx = xh == 1 ? b : bh;
+    const size_t nbx = (size_t)(gridDim.y / H) * xh;
+    if (kdp < nseg && edp < DG)
+        dP[((rgi * NS + i0 + kdp) * nbx + bx) * DG + edp] = (dp0 + dp1) + (dp2 + dp3);
+    // dM[c][r]: lane holds c = c0 + 32 cb + l32 and r = 32 db + 8g + 4 half + e
+    const int k = wave >> 1, c0 = (wave & 1) * 64;
+    if (k >= nseg) return;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int cb = 0; cb < 2; ++cb) {
+        float* out = dM + ((bh * NS + i0 + k) * 128 + c0 + cb * 32 + l32) * (size_t)128;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<float4*>(out + db * 32 + 8 * g + 4 * half) =
-                make_float4(mt[db][4 * g], mt[db][4 * g + 1], mt[db][4 * g + 2], mt[db][4 * g + 3]);
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<float4*>(out + db * 32 + 8 * g + 4 * half) =
+                    make_float4(mt[db][cb][4 * g], mt[db][cb][4 * g + 1], mt[db][cb][4 * g + 2],
+                                mt[db][cb][4 * g + 3]);
+    }
 }
 
-// The softmax backward from the forward gate pass: gamma_i = W_t^(i) / l_t (i < s),
+// The softmax backward from the gate pass: gamma_i = W_t^(i) / l_t (i < s),
 // gamma_s = won_t / l_t; dgamma of the online segment <dy_t, O_on[t]>; D_t; da_i written over
 // dgamma; du_t; the online weight for the segment walk; dq = dphi(q) phi'(q) with dphi(q) the
 // bf16 output of the swapped read.  8 threads per token.
@@ -255,8 +329,8 @@ __global__ __launch_bounds__(256) void bwd_gate_fast_kernel(
     const float* __restrict__ won, const float* __restrict__ inv_l,
     const float* __restrict__ O_on, const bf16_t* __restrict__ dY,
     const bf16_t* __restrict__ dqh, int L, int C, int NS, int DG, int DV, int H, int xh,
-    int phi, float* __restrict__ dG, float* __restrict__ gs_o, float* __restrict__ dU,
-    float* __restrict__ dQ) {
+    int phi, float* __restrict__ dG, float* __restrict__ daT, float* __restrict__ gs_o,
+    float* __restrict__ dU, float* __restrict__ dQ) {
     constexpr int CPK = DK / 8;
     const int tile0 = blockIdx.x * 32;
     const size_t bh = blockIdx.y;
@@ -279,19 +353,29 @@ __global__ __launch_bounds__(256) void bwd_gate_fast_kernel(
     float dpart = 0.f;
     for (int i = p; i < s; i += 8) dpart += bf16_to_f32(wrow[(size_t)i * kGateTile]) * il * dG[grow + i];
     const float D = warp_sum(dpart, 8) + gsv * dgs;
-    if (!valid) return;  // no shuffles below
     const int gch = DG / 8;
     float du[32];  // DG <= 256
 #pragma unroll
     for (int k = 0; k < 32; ++k) du[k] = 0.f;
-    for (int i = 0; i < s; ++i) {
-        const float da = bf16_to_f32(wrow[(size_t)i * kGateTile]) * il * (dG[grow + i] - D);
-        const float* Pi = P + (bx * NS + i) * DG + p * gch;
+    // the means, 32 segments at a time through LDS (the tile's largest s bounds the walk)
+    __shared__ float sP[32][256];
+    const int s_hi = (min(L, tile0 + 32) - 1) / C;
+    for (int i0 = 0; i0 < s_hi; i0 += 32) {
+        const int m = min(32, s_hi - i0);
+        __syncthreads();
+        for (int e = tid; e < m * DG; e += 256) sP[e / DG][e % DG] = P[(bx * NS + i0) * DG + e];
+        __syncthreads();
+        for (int ii = 0; ii < m && valid; ++ii) {
+            const int i = i0 + ii;
+            if (i >= s) break;
+            const float da = bf16_to_f32(wrow[(size_t)i * kGateTile]) * il * (dG[grow + i] - D);
 #pragma unroll
-        for (int k = 0; k < 32; ++k)
-            if (k < gch) du[k] += da * Pi[k];
-        if ((i & 7) == p) dG[grow + i] = da;
+            for (int k = 0; k < 32; ++k)
+                if (k < gch) du[k] += da * sP[ii][p * gch + k];
+            if ((i & 7) == p) daT[(bh * NS + i) * L + t] = da;  // segment-major for dM
+        }
     }
+    if (!valid) return;  // no barriers below
     const float das = gsv * (dgs - D);
     if (p == 0) {
         dG[grow + s] = das;
@@ -340,9 +424,11 @@ int launch_bwd_fast(const mc_dims& d, const BwdBuffers& w, const void* Q, const 
     hipLaunchKernelGGL((bwd_gate_fast_kernel<128>), dim3((d.L + 31) / 32, BH), dim3(256), 0, st,
                        (const bf16_t*)Q, (const bf16_t*)U, P, w.xps, w.W, w.won, w.inv_l, w.on,
                        (const bf16_t*)dY, (const bf16_t*)w.dqh, d.L, d.seg_len, NS, d.d_g, d.d_v,
-                       d.H, d.x_heads, d.phi, w.dG, w.gs, dU, dQ);
-    hipLaunchKernelGGL(bwd_dm_mfma_kernel, dim3(NS, BH), dim3(256), 0, st, (const bf16_t*)Q,
-                       (const bf16_t*)dY, w.W, w.inv_l, d.L, d.seg_len, NS, d.phi, w.dM);
+                       d.H, d.x_heads, d.phi, w.dG, w.daT, w.gs, dU, dQ);
+    hipLaunchKernelGGL(bwd_dm_mfma_kernel, dim3((NS + SPW - 1) / SPW, BH), dim3(512), 0, st,
+                       (const bf16_t*)Q,
+                       (const bf16_t*)dY, w.W, w.inv_l, (const bf16_t*)U, w.daT, d.L, d.seg_len,
+                       NS, d.d_g, d.H, d.x_heads, d.phi, w.dM, w.dpp);
     return (int)hipGetLastError();
 }
 

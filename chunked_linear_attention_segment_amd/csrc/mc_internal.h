@@ -96,10 +96,11 @@ struct BwdBuffers {
     void* pf;      // the means as MFMA fragments
     void* mt;      // [B,H,NS,dk,dv] bf16 transposed states
     void* dqh;     // [B,H,L,dk] bf16 dphi(q) from the swapped read
+    float* daT;    // [B,H,NS,L] da_t^(i), segment-major
 };
 struct BwdWorkspace {
     size_t aon, xps, xtail, on, ot, khat, lse, D, gs, dG, dM, dpp;
-    size_t W, won, inv_l, pf, mt, dqh, total;
+    size_t W, won, inv_l, pf, mt, dqh, daT, total;
 };
 // The MFMA backward applies where the forward uses the gate pass (bf16, d_k = d_v = 128).
 inline bool bwd_fast(const mc_dims& d) { return gate_pass(d); }
