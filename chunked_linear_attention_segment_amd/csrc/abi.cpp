@@ -294,8 +294,10 @@ mc_status mc_grm_readout_segs(const mc_dims* d, const int32_t* seg_off, int32_t 
     const void* ptrs[] = {Q, U, X, M, M_lo, P, O_on, Y, gamma, ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MC_ERR_ALIGN;
-    return launch_grm_readout_segs(*d, sg, Q, U, X, M, M_lo, P, O_on, (float*)ws, Y, gamma,
-                                   stream)
+    float* xps = w.xps ? (float*)((char*)ws + w.aon + w.on) : nullptr;
+    float* xtail = xps ? (float*)((char*)xps + xps_only(*d)) : nullptr;
+    return launch_grm_readout_segs(*d, sg, Q, U, X, M, M_lo, P, O_on, (float*)ws, xps, xtail, Y,
+                                   gamma, stream)
                ? MC_ERR_HIP
                : MC_OK;
 }

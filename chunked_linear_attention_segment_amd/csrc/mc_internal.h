@@ -123,9 +123,12 @@ int launch_grm_backward(const mc_dims& d, const BwdBuffers& w, const void* Q, co
 int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
                              const void* V, const void* X, float* M, uint16_t* M_lo, float* P,
                              float* O_on, void* stream);
+// xps / xtail (nullable: the per-segment walk of aon_kernel is used instead) are workspace for
+// the segment-causal prefix sums of X.
 int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* U,
                             const void* X, const float* M, const uint16_t* M_lo, const float* P,
-                            const float* O_on, float* aon, void* Y, float* gamma, void* stream);
+                            const float* O_on, float* aon, float* xps, float* xtail, void* Y,
+                            float* gamma, void* stream);
 
 int launch_scan_prefill(const mc_dims& d, const void* Q, const void* K, const void* V,
                         const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,

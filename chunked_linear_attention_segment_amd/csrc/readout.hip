@@ -132,7 +132,7 @@ constexpr int XCH = 64;
 template <typename T, bool TAIL>
 __global__ __launch_bounds__(256) void xps_kernel(const T* __restrict__ X, int L, int C, int DG,
                                                   float* __restrict__ tails,
-                                                  float* __restrict__ xps) {
+                                                  float* __restrict__ xps, const SegArg sg) {
     const int c = blockIdx.x, nch = gridDim.x;
     const size_t bx = blockIdx.y;
     const int e = threadIdx.x;
@@ -143,18 +143,24 @@ __global__ __launch_bounds__(256) void xps_kernel(const T* __restrict__ X, int L
 #pragma unroll
     for (int r = 0; r < XCH; ++r) v[r] = c0 + r < c1 ? ld<T>(Xb, (size_t)(c0 + r) * DG + e) : 0.f;
     float run = 0.f;
+    int si = seg_of(sg, c0, C);           // segment of the chunk's first row
+    const int ss = seg_first(sg, si, C);  // and its start
     if (!TAIL) {
-        const int ss = (c0 / C) * C;  // start of the segment of the chunk's first row
 #pragma unroll 16
         for (int cc = c - 1; cc >= 0 && (cc + 1) * XCH > ss; --cc)
             run += tails[(bx * nch + cc) * DG + e];
     }
+    int nb = seg_first(sg, si + 1, C);  // the next segment start
     float* out = xps + (bx * L + c0) * DG + e;
 #pragma unroll
     for (int r = 0; r < XCH; ++r) {
         const int t = c0 + r;
         if (t < c1) {
-            if (t % C == 0) run = 0.f;
+            if (t == nb) {
+                run = 0.f;
+                ++si;
+                nb = seg_first(sg, si + 1, C);
+            }
             run += v[r];
             if (!TAIL) out[(size_t)r * DG] = run;
         }
@@ -162,27 +168,52 @@ __global__ __launch_bounds__(256) void xps_kernel(const T* __restrict__ X, int L
     if (TAIL) tails[(bx * nch + c) * DG + e] = run;
 }
 
+// Online logits from the prefix sums: a_on[t] = <u_t, xps_t> / (j_t + 1), 8 threads per token.
+template <typename T>
+__global__ __launch_bounds__(256) void aon_xps_kernel(const T* __restrict__ U,
+                                                      const float* __restrict__ xps, int L,
+                                                      int C, int DG, int H, int xh,
+                                                      float* __restrict__ a_on, const SegArg sg) {
+    const size_t bh = blockIdx.y;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const size_t bx = (size_t)b * xh + (xh == 1 ? 0 : h);
+    const int t = blockIdx.x * 32 + threadIdx.x / 8, p = threadIdx.x % 8;
+    const bool valid = t < L;
+    const int tc = valid ? t : L - 1;
+    const int j = tc - seg_first(sg, seg_of(sg, tc, C), C);
+    const int gch = DG / 8;
+    float a = 0.f;
+    for (int e = p * gch; e < (p + 1) * gch; ++e)
+        a += ld(U, (bh * L + tc) * DG + e) * xps[(bx * L + tc) * DG + e];
+    a = warp_sum(a, 8);
+    if (valid && p == 0) a_on[bh * L + t] = a / (float)(j + 1);
+}
+
 size_t xps_tail_floats(const mc_dims& d) {
     return (size_t)d.B * d.x_heads * ((d.L + XCH - 1) / XCH) * d.d_g;
 }
 
-int launch_xps(const mc_dims& d, const void* X, float* xps, float* tails, void* stream) {
-    hipStream_t st = (hipStream_t)stream;
+static int launch_xps_sg(const mc_dims& d, const void* X, float* xps, float* tails,
+                         const SegArg& sg, hipStream_t st) {
     if (d.d_g > 256) return (int)hipErrorInvalidValue;
     const dim3 grid((d.L + XCH - 1) / XCH, d.B * d.x_heads);
     const dim3 block((d.d_g + 63) / 64 * 64);
     if (d.dtype == MC_BF16) {
         hipLaunchKernelGGL((xps_kernel<bf16_t, true>), grid, block, 0, st, (const bf16_t*)X, d.L,
-                           d.seg_len, d.d_g, tails, xps);
+                           d.seg_len, d.d_g, tails, xps, sg);
         hipLaunchKernelGGL((xps_kernel<bf16_t, false>), grid, block, 0, st, (const bf16_t*)X, d.L,
-                           d.seg_len, d.d_g, tails, xps);
+                           d.seg_len, d.d_g, tails, xps, sg);
     } else {
         hipLaunchKernelGGL((xps_kernel<float, true>), grid, block, 0, st, (const float*)X, d.L,
-                           d.seg_len, d.d_g, tails, xps);
+                           d.seg_len, d.d_g, tails, xps, sg);
         hipLaunchKernelGGL((xps_kernel<float, false>), grid, block, 0, st, (const float*)X, d.L,
-                           d.seg_len, d.d_g, tails, xps);
+                           d.seg_len, d.d_g, tails, xps, sg);
     }
     return (int)hipGetLastError();
+}
+
+int launch_xps(const mc_dims& d, const void* X, float* xps, float* tails, void* stream) {
+    return launch_xps_sg(d, X, xps, tails, kConstSegR, (hipStream_t)stream);
 }
 
 // Generic read kernel.  A workgroup covers TT = 32 consecutive tokens of one (b, h); the 8
@@ -329,9 +360,24 @@ static int launch_readout(const mc_dims& d, int top_k, const void* Q, const void
 // mc_scan_prefill_segs.
 int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* U,
                             const void* X, const float* M, const uint16_t* M_lo, const float* P,
-                            const float* O_on, float* aon, void* Y, float* gamma, void* stream) {
+                            const float* O_on, float* aon, float* xps, float* xtail, void* Y,
+                            float* gamma, void* stream) {
     hipStream_t st = (hipStream_t)stream;
-    int rc = launch_aon_sg(d, X, U, aon, sg, st);
+    int rc;
+    if (xps) {  // prefix sums of X per segment, then the logits token by token
+        rc = launch_xps_sg(d, X, xps, xtail, sg, st);
+        if (rc) return rc;
+        const dim3 grid((d.L + 31) / 32, d.B * d.H);
+        if (d.dtype == MC_BF16)
+            hipLaunchKernelGGL(aon_xps_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)U,
+                               xps, d.L, d.seg_len, d.d_g, d.H, d.x_heads, aon, sg);
+        else
+            hipLaunchKernelGGL(aon_xps_kernel<float>, grid, dim3(256), 0, st, (const float*)U,
+                               xps, d.L, d.seg_len, d.d_g, d.H, d.x_heads, aon, sg);
+        rc = (int)hipGetLastError();
+    } else {
+        rc = launch_aon_sg(d, X, U, aon, sg, st);
+    }
     if (rc) return rc;
 #define MC_RD(DK, DV)                                                                      \
     if (d.d_k == DK && d.d_v == DV)                                                        \

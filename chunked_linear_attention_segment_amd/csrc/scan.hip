@@ -183,12 +183,18 @@ static int launch_means(const mc_dims& d, const void* X, float* P, const SegArg&
     return (int)hipGetLastError();
 }
 
-// Arbitrary boundaries: the generic scan (any dtype) and the means over each segment.
+int launch_scan_mfma_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
+                          const void* V, float* M, uint16_t* M_lo, float* O_on, void* stream);
+
+// Arbitrary boundaries: the MFMA scan for bf16 widths 64/128, else the generic scan (any
+// dtype); then the means over each segment.
 int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
                              const void* V, const void* X, float* M, uint16_t* M_lo, float* P,
                              float* O_on, void* stream) {
     hipStream_t st = (hipStream_t)stream;
-    int rc = d.dtype == MC_BF16 ? launch_scan_dt<bf16_t>(d, Q, K, V, M, M_lo, O_on, sg, st)
+    int rc = launch_scan_mfma_segs(d, sg, Q, K, V, M, M_lo, O_on, stream);
+    if (rc < 0)
+        rc = d.dtype == MC_BF16 ? launch_scan_dt<bf16_t>(d, Q, K, V, M, M_lo, O_on, sg, st)
                                 : launch_scan_dt<float>(d, Q, K, V, M, M_lo, O_on, sg, st);
     if (rc) return rc;
     return d.dtype == MC_BF16 ? launch_means<bf16_t>(d, X, P, sg, st)
@@ -196,16 +202,17 @@ int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, 
 }
 
 int launch_scan_mfma(const mc_dims& d, const void* Q, const void* K, const void* V, float* M,
-                     uint16_t* M_lo, float* O_on, const SwlaGates& gt, void* stream);
+                     uint16_t* M_lo, float* O_on, const SwlaGates& gt, void* stream,
+                     const SegArg* sg = nullptr);
 
-// SWLA write path: the MFMA scan for constant-length bf16 segments of width 64/128, the
-// generic scan otherwise (and for any offsets), then the means.
+// SWLA write path: the MFMA scan for bf16 widths 64/128 (constant segments or offsets), the
+// generic scan otherwise, then the means.
 int launch_scan_prefill_swla(const mc_dims& d, const SegArg& sg, const SwlaGates& gt,
                              const void* Q, const void* K, const void* V, const void* X,
                              float* M, uint16_t* M_lo, float* P, float* O_on, void* stream) {
     hipStream_t st = (hipStream_t)stream;
     int rc = -1;
-    if (!sg.n && d.dtype == MC_BF16) rc = launch_scan_mfma(d, Q, K, V, M, M_lo, O_on, gt, stream);
+    if (d.dtype == MC_BF16) rc = launch_scan_mfma(d, Q, K, V, M, M_lo, O_on, gt, stream, &sg);
     if (rc >= 0) {
         if (rc) return rc;
     } else if (d.dtype == MC_BF16)

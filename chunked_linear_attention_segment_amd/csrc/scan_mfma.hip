@@ -69,7 +69,7 @@ template <int DK, int DV, bool ON, bool SW>
 __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     int L, int C, int NS, int phi, float* __restrict__ M, bf16_t* __restrict__ M_lo,
-    float* __restrict__ O_on, SwlaGates gt) {
+    float* __restrict__ O_on, SwlaGates gt, const SegArg sg) {
     constexpr int NT = DV * 2;      // threads: one wave per 32 value rows
     constexpr int DB = DK / 32;     // 32-row blocks of d
     constexpr int KSD = DK / 16;    // k-steps over d
@@ -83,8 +83,8 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
 
     const int s = blockIdx.x;
     const size_t bh = blockIdx.y;
-    const int t0 = s * C;
-    const int len = min(C, L - t0);
+    const int t0 = seg_first(sg, s, C);
+    const int len = seg_length(sg, s, C, L);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, half = lane >> 5;
 
@@ -321,15 +321,17 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
         }
 }
 
+static const SegArg kConstSegM{};  // constant segment length
+
 template <int DK, int DV>
 static int launch_scan_mfma_t(const mc_dims& d, const void* Q, const void* K, const void* V,
                               float* M, uint16_t* M_lo, float* O_on, const SwlaGates& gt,
-                              hipStream_t st) {
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+                              hipStream_t st, const SegArg& sg = kConstSegM) {
+    const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
 #define MC_SCAN(ON, SW)                                                                        \
     hipLaunchKernelGGL((scan_mfma_kernel<DK, DV, ON, SW>), dim3(NS, d.B * d.H), dim3(DV * 2),   \
                        0, st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, d.L,        \
-                       d.seg_len, NS, d.phi, M, (bf16_t*)M_lo, O_on, gt)
+                       d.seg_len, NS, d.phi, M, (bf16_t*)M_lo, O_on, gt, sg)
     if (gt.alpha) {  // SWLA: the read takes the online term from O_on, so it is always written
         if (!O_on) return (int)hipErrorInvalidValue;
         MC_SCAN(true, true);
@@ -340,6 +342,24 @@ static int launch_scan_mfma_t(const mc_dims& d, const void* Q, const void* K, co
     }
 #undef MC_SCAN
     return (int)hipGetLastError();
+}
+
+// Any segment boundaries (the offsets passed by value), bf16: states, their bf16 copy and the
+// optional online read; -1 when the sizes are not covered.
+int launch_scan_mfma_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
+                          const void* V, float* M, uint16_t* M_lo, float* O_on, void* stream) {
+    if (d.dtype != MC_BF16 || !M_lo) return -1;
+    hipStream_t st = (hipStream_t)stream;
+    const SwlaGates none{};
+#define MC_SD(DK, DV)                                                                          \
+    if (d.d_k == DK && d.d_v == DV)                                                            \
+        return launch_scan_mfma_t<DK, DV>(d, Q, K, V, M, M_lo, O_on, none, st, sg);
+    MC_SD(128, 128)
+    MC_SD(128, 64)
+    MC_SD(64, 128)
+    MC_SD(64, 64)
+#undef MC_SD
+    return -1;
 }
 
 // The online read alone (no state output) on the MFMA scan; -1 when the sizes are not covered.
@@ -359,13 +379,17 @@ int launch_scan_mfma_online(const mc_dims& d, const void* Q, const void* K, cons
     return -1;
 }
 
-// bf16 scan on MFMA; -1 when the sizes are not covered (the caller uses the generic kernel).
+// bf16 scan on MFMA (constant segments, or the offsets sg); -1 when the sizes are not
+// covered (the caller uses the generic kernel).
 int launch_scan_mfma(const mc_dims& d, const void* Q, const void* K, const void* V, float* M,
-                     uint16_t* M_lo, float* O_on, const SwlaGates& gt, void* stream) {
+                     uint16_t* M_lo, float* O_on, const SwlaGates& gt, void* stream,
+                     const SegArg* sg) {
     if (d.dtype != MC_BF16 || !M_lo) return -1;
     hipStream_t st = (hipStream_t)stream;
+    const SegArg& seg = sg ? *sg : kConstSegM;
 #define MC_SD(DK, DV)                                                                          \
-    if (d.d_k == DK && d.d_v == DV) return launch_scan_mfma_t<DK, DV>(d, Q, K, V, M, M_lo, O_on, gt, st);
+    if (d.d_k == DK && d.d_v == DV)                                                            \
+        return launch_scan_mfma_t<DK, DV>(d, Q, K, V, M, M_lo, O_on, gt, st, seg);
     MC_SD(128, 128)
     MC_SD(128, 64)
     MC_SD(64, 128)
