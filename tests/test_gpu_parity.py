@@ -46,6 +46,10 @@ SMALL = {
                                   {}),
     "bf16_d128_C16_150_segments": (Workload("x", 1, 2, 2400, 128, 128, 128, 16, "identity",
                                             "bf16"), {}),
+    # degenerate sizes: one token; one-token segments on the MFMA path
+    "bf16_d128_L1": (Workload("x", 1, 2, 1, 128, 128, 128, 64, "identity", "bf16"), {}),
+    "f32_d64_L1": (Workload("x", 1, 1, 1, 64, 64, 64, 64, "identity", "f32"), {}),
+    "bf16_d128_C1_L80_elu": (Workload("x", 1, 2, 80, 128, 128, 64, 1, "elu1", "bf16"), {}),
     "bf16_d128_C512_L1536_elu": (Workload("x", 2, 3, 1536, 128, 128, 64, 512, "elu1", "bf16"),
                                  {}),
 }
@@ -310,6 +314,8 @@ SEG_CASES = {
                                              x_heads=2), "random"),
     "bf16_multiples_of_64_L640": (Workload("x", 1, 2, 640, 128, 64, 128, 1, "identity",
                                            "bf16"), "c64"),
+    "bf16_max_512_segments_L1100": (Workload("x", 1, 2, 1100, 128, 128, 128, 1, "identity",
+                                             "bf16"), "max"),
 }
 
 
@@ -321,6 +327,8 @@ def test_grm_segment_offsets(name):
     elif kind == "random":
         off = _random_offsets(w.L, 23, seed=5)
         off = sorted(set(off + [off[1] + 1]))  # a one-token segment
+    elif kind == "max":
+        off = _random_offsets(w.L, mc.MC_MAX_SEGS, seed=6)  # the most segments a call takes
     else:
         off = list(range(0, w.L, 64)) + [w.L]
     announce("grm segment offsets %s: %d segments" % (name, len(off) - 1))
@@ -410,6 +418,10 @@ BWD_CASES = {
     "bf16_d128_C512_L1536": Workload("x", 1, 2, 1536, 128, 128, 128, 512, "identity", "bf16"),
     "bf16_d128_C16_L640_xheadsH": Workload("x", 1, 2, 640, 128, 128, 32, 16, "identity", "bf16",
                                            x_heads=2),
+    # degenerate sizes: one token; one-token segments; one segment (no cached state)
+    "bf16_d128_L1": Workload("x", 1, 2, 1, 128, 128, 128, 64, "identity", "bf16"),
+    "bf16_d128_C1_L48_elu": Workload("x", 1, 2, 48, 128, 128, 64, 1, "elu1", "bf16"),
+    "f32_d64_single_segment_L100": Workload("x", 1, 2, 100, 64, 64, 64, 256, "identity", "f32"),
 }
 
 
