@@ -160,7 +160,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dgamma_kernel(
 constexpr int CHK = 64;    // tokens per chunk of the dM walk
 constexpr int TPAD = 72;   // row stride (bf16) of the token-indexed LDS tiles
 
-constexpr int SPW = 4;  // cached segments per dM workgroup (8 waves: 2 per segment)
+constexpr int SPW = 4;        // cached segments per dM workgroup (8 waves: 2 per segment)
+constexpr int DM_SPLIT = 8;   // most workgroups that share one group's later tokens
+constexpr int DM_CHUNKS = 128;  // chunks a workgroup aims for
 
 // dM^(i) (stored [c][r] like the states) for d_k = d_v = 128 and d_g <= 128, SPW consecutive
 // segments i0.. per workgroup so that each later token is staged once for all of them:
@@ -170,7 +172,10 @@ constexpr int SPW = 4;  // cached segments per dM workgroup (8 waves: 2 per segm
 // segment) are staged in LDS with token pairs packed in 32-bit words (the token index is the
 // contraction index); the next chunk's rows are loaded into registers while the current one
 // is contracted.  gamma_t^(i) = W_t^(i) / l_t from the forward gate pass, zero unless token t
-// lies after segment i.  Alongside, dP_i of this head = sum_t da_t^(i) u_t.
+// lies after segment i.  Alongside, dP_i of this head = sum_t da_t^(i) u_t.  The later tokens
+// of a group are split over up to DM_SPLIT workgroups (blockIdx.z) of about DM_CHUNKS chunks,
+// so the first groups do not set the length of the launch; each adds its partial dM and dP
+// into the zero-filled outputs (fp32 atomic adds: the order of the partial sums varies).
 __global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ dY, const uint16_t* __restrict__ Wg,
     const float* __restrict__ inv_l, const bf16_t* __restrict__ U,
@@ -199,8 +204,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
 
     // one chunk in registers: staging slot (token pair 2p, 2p+1; columns dc..dc+7) of phi(q)
     // and dy, the SPW gate weights of both tokens, two slots of u rows, one da
+    // (raw loaded values only: anything computed from them here would wait for the loads)
     u32x4_t rq[2], ry[2], ru[2];
-    float rg[2][SPW], rda = 0.f;
+    uint32_t rw[2][SPW];
+    float ril[2], rda = 0.f;
     auto load = [&](int j0) {
         const int n = min(CHK, L - j0);
         const int p = tid % (CHK / 2), dc = (tid / (CHK / 2)) * 8;
@@ -208,21 +215,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
         for (int o = 0; o < 2; ++o) {
             const int r = 2 * p + o, t = j0 + r;
             u32x4_t q = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+            float il = 0.f;
 #pragma unroll
-            for (int k = 0; k < SPW; ++k) rg[o][k] = 0.f;
+            for (int k = 0; k < SPW; ++k) rw[o][k] = 0u;
             if (r < n) {
                 const size_t row = bh * L + t;
                 q = *reinterpret_cast<const u32x4_t*>(Q + row * 128 + dc);
                 y = *reinterpret_cast<const u32x4_t*>(dY + row * 128 + dc);
-                const float il = inv_l[row];
+                il = inv_l[row];
                 const int st = t / C;
                 const uint16_t* wr = Wg + ((bh * T + t / kGateTile) * NS) * kGateTile + t % kGateTile;
 #pragma unroll
                 for (int k = 0; k < SPW; ++k)
-                    if (i0 + k < st) rg[o][k] = bf16_to_f32(wr[(size_t)(i0 + k) * kGateTile]) * il;
+                    if (i0 + k < st) rw[o][k] = wr[(size_t)(i0 + k) * kGateTile];
             }
             rq[o] = q;
             ry[o] = y;
+            ril[o] = il;
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -236,9 +245,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
             rda = (k < nseg && tt < n && t / C > i0 + k) ? daT[(bh * NS + i0 + k) * L + t] : 0.f;
         }
     };
-    const int first = (i0 + 1) * C;
-    if (first < L) load(first);
-    for (int j0 = first; j0 < L; j0 += CHK) {
+    // this workgroup's share of the group's later tokens: chunks [z cpz, (z + 1) cpz)
+    const int first0 = (i0 + 1) * C;
+    const int nch = first0 < L ? (L - first0 + CHK - 1) / CHK : 0;
+    const int nsplit = min(DM_SPLIT, max(1, (nch + DM_CHUNKS - 1) / DM_CHUNKS));
+    const int cpz = (nch + nsplit - 1) / nsplit;
+    const int z = blockIdx.z;
+    if (z >= nsplit || z * cpz >= nch) return;  // uniform: no work for this split
+    const int first = first0 + z * cpz * CHK;
+    const int stop = min(L, first0 + (z + 1) * cpz * CHK);
+    load(first);
+    for (int j0 = first; j0 < stop; j0 += CHK) {
         const int n = min(CHK, L - j0);
         {  // registers -> LDS
             const int p = tid % (CHK / 2), dc = (tid / (CHK / 2)) * 8, r0 = 2 * p;
@@ -250,7 +267,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
             }
 #pragma unroll
             for (int k = 0; k < SPW; ++k) {
-                const float g0 = rg[0][k], g1 = rg[1][k];
+                const float g0 = bf16_to_f32((bf16_t)rw[0][k]) * ril[0];
+                const float g1 = bf16_to_f32((bf16_t)rw[1][k]) * ril[1];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     *reinterpret_cast<uint32_t*>(&gt[k][dc + 2 * e][r0]) =
@@ -267,7 +285,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
             if (tid < SPW * CHK) sda[tid / CHK][tid % CHK] = rda;
         }
         __syncthreads();
-        if (j0 + CHK < L) load(j0 + CHK);  // the next chunk's loads overlap this chunk's work
+        if (j0 + CHK < stop) load(j0 + CHK);  // the next chunk's loads overlap this chunk's work
         const int k = wave >> 1, c0 = (wave & 1) * 64;
         u32x4_t gb[2][CHK / 16];
 #pragma unroll
@@ -301,7 +319,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
     const size_t rgi = xh == 1 ? h : 0, bx = xh == 1 ? b : bh;
     const size_t nbx = (size_t)(gridDim.y / H) * xh;
     if (kdp < nseg && edp < DG)
-        dP[((rgi * NS + i0 + kdp) * nbx + bx) * DG + edp] = (dp0 + dp1) + (dp2 + dp3);
+        unsafeAtomicAdd(&dP[((rgi * NS + i0 + kdp) * nbx + bx) * DG + edp],
+                        (dp0 + dp1) + (dp2 + dp3));
     // dM[c][r]: lane holds c = c0 + 32 cb + l32 and r = 32 db + 8g + 4 half + e
     const int k = wave >> 1, c0 = (wave & 1) * 64;
     if (k >= nseg) return;
@@ -312,9 +331,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<float4*>(out + db * 32 + 8 * g + 4 * half) =
-                    make_float4(mt[db][cb][4 * g], mt[db][cb][4 * g + 1], mt[db][cb][4 * g + 2],
-                                mt[db][cb][4 * g + 3]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    unsafeAtomicAdd(out + db * 32 + 8 * g + 4 * half + e, mt[db][cb][4 * g + e]);
     }
 }
 
@@ -395,6 +414,12 @@ __global__ __launch_bounds__(256) void bwd_gate_fast_kernel(
     }
 }
 
+__global__ void zero_kernel(float* __restrict__ p, size_t n) {
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n;
+         e += (size_t)gridDim.x * blockDim.x)
+        p[e] = 0.f;
+}
+
 }  // namespace
 
 int launch_bwd_fast(const mc_dims& d, const BwdBuffers& w, const void* Q, const void* K,
@@ -425,7 +450,13 @@ int launch_bwd_fast(const mc_dims& d, const BwdBuffers& w, const void* Q, const 
                        (const bf16_t*)Q, (const bf16_t*)U, P, w.xps, w.W, w.won, w.inv_l, w.on,
                        (const bf16_t*)dY, (const bf16_t*)w.dqh, d.L, d.seg_len, NS, d.d_g, d.d_v,
                        d.H, d.x_heads, d.phi, w.dG, w.daT, w.gs, dU, dQ);
-    hipLaunchKernelGGL(bwd_dm_mfma_kernel, dim3((NS + SPW - 1) / SPW, BH), dim3(512), 0, st,
+    // dM and dP take the partial sums of the split workgroups: zero them first (a kernel, so
+    // the sequence stays capturable)
+    const size_t ndm = (size_t)BH * NS * d.d_v * d.d_k;
+    const size_t ndp = (size_t)d.B * d.H * NS * d.d_g;  // [H or 1][NS][B*xh][dg]
+    hipLaunchKernelGGL(zero_kernel, dim3(2048), dim3(256), 0, st, w.dM, ndm);
+    hipLaunchKernelGGL(zero_kernel, dim3(256), dim3(256), 0, st, w.dpp, ndp);
+    hipLaunchKernelGGL(bwd_dm_mfma_kernel, dim3((NS + SPW - 1) / SPW, BH, DM_SPLIT), dim3(512), 0, st,
                        (const bf16_t*)Q,
                        (const bf16_t*)dY, w.W, w.inv_l, (const bf16_t*)U, w.daT, d.L, d.seg_len,
                        NS, d.d_g, d.H, d.x_heads, d.phi, w.dM, w.dpp);
