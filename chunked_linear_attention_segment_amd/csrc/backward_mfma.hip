@@ -108,27 +108,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dgamma_kernel(
     }
 
     const bf16_t* Sb = M_lo + bh * (size_t)NS * 128 * 128;
-    u32x4_t pre[8];  // one state: 128 rows x 16 chunks of 16 bytes, 8 chunks per thread
-    auto load_state = [&](int i) {
+    // states two ahead: register sets ra / rb alternate (the loop is unrolled by two so that
+    // both stay statically indexed), LDS buffers alternate with the state's parity
+    u32x4_t ra[8], rb[8];
+    auto load_state = [&](int i, u32x4_t* r) {
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(Sb + (size_t)i * 128 * 128);
 #pragma unroll
-        for (int it = 0; it < 8; ++it) pre[it] = src[tid + 256 * it];
+        for (int it = 0; it < 8; ++it) r[it] = src[tid + 256 * it];
     };
-    auto store_state = [&](int buf) {
+    auto store_state = [&](int buf, const u32x4_t* r) {
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
             const int idx = tid + 256 * it;
-            *reinterpret_cast<u32x4_t*>(&ms[buf][idx >> 4][(idx & 15) * 8]) = pre[it];
+            *reinterpret_cast<u32x4_t*>(&ms[buf][idx >> 4][(idx & 15) * 8]) = r[it];
         }
     };
-    load_state(0);
-    store_state(0);
-    __syncthreads();
     const f32x16_t zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
                            0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < s_hi; ++i) {
+    // state i from LDS buffer i & 1: contract, reduce against dy, write dgamma
+    auto step = [&](int i) {
         const int buf = i & 1;
-        if (i + 1 < s_hi) load_state(i + 1);
         f32x16_t acc[4][2];
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
@@ -152,7 +151,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dgamma_kernel(
             if (half == 0 && tok[tb] < L && i < stok[tb])
                 dG[(bh * L + tok[tb]) * NS + i] = part;
         }
-        if (i + 1 < s_hi) store_state(buf ^ 1);
+    };
+    load_state(0, ra);
+    if (1 < s_hi) load_state(1, rb);
+    store_state(0, ra);
+    __syncthreads();
+    for (int i = 0; i < s_hi; i += 2) {
+        // state i is in LDS, state i + 1 in rb; fetch i + 2 into ra
+        if (i + 2 < s_hi) load_state(i + 2, ra);
+        step(i);
+        if (i + 1 < s_hi) store_state((i + 1) & 1, rb);
+        __syncthreads();
+        if (i + 1 >= s_hi) break;
+        // state i + 1 is in LDS, state i + 2 in ra; fetch i + 3 into rb
+        if (i + 3 < s_hi) load_state(i + 3, rb);
+        step(i + 1);
+        if (i + 2 < s_hi) store_state(i & 1, ra);
         __syncthreads();
     }
 }
@@ -361,33 +375,65 @@ __global__ __launch_bounds__(256) void bwd_gate_fast_kernel(
     const int tc = valid ? t : L - 1;
     const int s = tc / C, j = tc - s * C;
     const int T = (L + kGateTile - 1) / kGateTile;
-    const uint16_t* wrow = Wg + ((bh * T + tc / kGateTile) * NS) * kGateTile + tc % kGateTile;
     const size_t grow = (bh * L + tc) * NS;
     const float il = inv_l[bh * L + tc];
-    // dgamma of the online segment and D = sum_i gamma_i dgamma_i (segments dealt over p)
+    // dgamma of the online segment, <dy_t, O_on[t]>: thread p takes DV/8 consecutive columns
+    // (16-byte loads, one round trip)
     float part = 0.f;
-    for (int c = p; c < DV; c += 8) part += bf16_to_f32(dY[(bh * L + tc) * DV + c]) * O_on[(bh * L + tc) * DV + c];
+    {
+        const int cpt = DV / 8, c0 = p * cpt;
+        const bf16_t* dyr = dY + (bh * L + tc) * DV + c0;
+        const float* orow = O_on + (bh * L + tc) * DV + c0;
+        for (int c = 0; c < cpt; c += 8) {
+            const u32x4_t y = *reinterpret_cast<const u32x4_t*>(dyr + c);
+            const float4 o0 = *reinterpret_cast<const float4*>(orow + c);
+            const float4 o1 = *reinterpret_cast<const float4*>(orow + c + 4);
+            part += bf_lo(y[0]) * o0.x + bf_hi(y[0]) * o0.y + bf_lo(y[1]) * o0.z + bf_hi(y[1]) * o0.w +
+                    bf_lo(y[2]) * o1.x + bf_hi(y[2]) * o1.y + bf_lo(y[3]) * o1.z + bf_hi(y[3]) * o1.w;
+        }
+    }
     const float dgs = warp_sum(part, 8);
     const float gsv = won[bh * L + tc] * il;
-    float dpart = 0.f;
-    for (int i = p; i < s; i += 8) dpart += bf16_to_f32(wrow[(size_t)i * kGateTile]) * il * dG[grow + i];
-    const float D = warp_sum(dpart, 8) + gsv * dgs;
     const int gch = DG / 8;
     float du[32];  // DG <= 256
 #pragma unroll
     for (int k = 0; k < 32; ++k) du[k] = 0.f;
-    // the means, 32 segments at a time through LDS (the tile's largest s bounds the walk)
+    // 32 segments at a time through LDS (the tile's largest s bounds the walk): the gate
+    // numerators and dgamma of the tile's 32 tokens, loaded coalesced, and (second pass) the
+    // means.  Pass 1 forms D = sum_i gamma_i dgamma_i, pass 2 da_i = gamma_i (dgamma_i - D).
     __shared__ float sP[32][256];
+    __shared__ float sG[32][33];   // dgamma [token][segment]
+    __shared__ float sWt[32][33];  // numerator [segment][token]
     const int s_hi = (min(L, tile0 + 32) - 1) / C;
+    const uint16_t* wtile = Wg + ((bh * T + tile0 / kGateTile) * NS) * kGateTile + tile0 % kGateTile;
+    auto stage = [&](int i0, int m, bool means) {
+        __syncthreads();
+        if (means)
+            for (int e = tid; e < m * DG; e += 256) sP[e / DG][e % DG] = P[(bx * NS + i0) * DG + e];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int idx = tid + 256 * k, a = idx / 32, c = idx % 32;
+            const int tg = tile0 + a;  // sG: token a, segment i0 + c
+            sG[a][c] = (tg < L && c < m) ? dG[(bh * L + tg) * NS + i0 + c] : 0.f;
+            const int tw = tile0 + c;  // sWt: segment i0 + a, token c
+            sWt[a][c] = (tw < L && a < m) ? bf16_to_f32(wtile[(size_t)(i0 + a) * kGateTile + c]) : 0.f;
+        }
+        __syncthreads();
+    };
+    float dpart = 0.f;
     for (int i0 = 0; i0 < s_hi; i0 += 32) {
         const int m = min(32, s_hi - i0);
-        __syncthreads();
-        for (int e = tid; e < m * DG; e += 256) sP[e / DG][e % DG] = P[(bx * NS + i0) * DG + e];
-        __syncthreads();
+        stage(i0, m, false);
+        for (int ii = p; ii < m && i0 + ii < s; ii += 8) dpart += sWt[ii][tt] * sG[tt][ii];
+    }
+    const float D = warp_sum(dpart, 8) * il + gsv * dgs;
+    for (int i0 = 0; i0 < s_hi; i0 += 32) {
+        const int m = min(32, s_hi - i0);
+        stage(i0, m, true);
         for (int ii = 0; ii < m && valid; ++ii) {
             const int i = i0 + ii;
             if (i >= s) break;
-            const float da = bf16_to_f32(wrow[(size_t)i * kGateTile]) * il * (dG[grow + i] - D);
+            const float da = sWt[ii][tt] * il * (sG[tt][ii] - D);
 #pragma unroll
             for (int k = 0; k < 32; ++k)
                 if (k < gch) du[k] += da * sP[ii][p * gch + k];
