@@ -13,7 +13,9 @@
 //   dx_r = dP_i / |S_i| + sum_{t >= r in segment i} da_t^(s) u_t / (j_t + 1)
 //   dq = dphi(q) phi'(q), dk = dphi(k) phi'(k), phi'(z) = min(phi(z), 1) for elu + 1.
 //
-// The launches, in order (one stream):
+// The launches, in order (one stream), for the generic path (fp32, or widths the MFMA
+// backward does not take; the bf16 d_k = d_v = 128 path replaces the first four lines with
+// the kernels of backward_mfma.hip):
 //   aon, xps            online logits and segment-causal prefix sums of X (forward helpers)
 //   scan_online x2      O_on[t] = M_t^(s) phi(q_t), and Ot[t] = M_t^(s)T dy_t (the same scan
 //                       with q := dy, k := v, v := phi(k))
@@ -23,7 +25,9 @@
 //                       gamma_s Ot[t]) phi'(q)
 //   bwd_dm_kernel       per cached segment i: dM^(i)
 //   bwd_online_kernel   per segment, tokens in reverse: E_r and E_r^T, dv_r and dk_r
-//   bwd_dx_kernel       per segment and x head: dP_i and the prefix-mean terms, dx
+//   bwd_dxw_kernel, bwd_dp_kernel, bwd_dxf_kernel
+//                       the x gradients: per-token prefix-mean terms, partial dP_i over token
+//                       ranges, then dP_i / |S_i| plus the reverse cumulative sums
 // Every kernel accumulates in fp32 registers; all gradients are written in fp32.
 #include "common.cuh"
 #include "mc_internal.h"
