@@ -111,8 +111,13 @@ __global__ __launch_bounds__(256) void bwd_cached_kernel(
         for (int m = 0; m < CPV; ++m) {
             const int c = p + 8 * m;
             float dot = 0.f;
-#pragma unroll 8
-            for (int r = 0; r < DK; ++r) dot += ld(Si, (size_t)c * DK + r) * sq[tt][r];
+#pragma unroll 4
+            for (int r = 0; r < DK; r += 8) {  // 16-byte (bf16) / 32-byte (fp32) row slices
+                float v[8];
+                ld8(Si, (size_t)c * DK + r, v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot += v[e] * sq[tt][r + e];
+            }
             part += sdy[tt][c] * dot;
         }
         const float dgi = warp_sum(part, 8);

@@ -54,6 +54,19 @@ template <> __device__ __forceinline__ void ld8<bf16_t>(const bf16_t* p, size_t 
     }
 }
 
+// Eight consecutive values v[e] * scale stored at p[i..i+8) (16 bytes for bf16, 32 for fp32;
+// i a multiple of 8 from an aligned base).
+template <typename T> __device__ __forceinline__ void st8(T* p, size_t i, const float* v, float scale);
+template <> __device__ __forceinline__ void st8<float>(float* p, size_t i, const float* v, float scale) {
+    *reinterpret_cast<float4*>(p + i) = make_float4(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
+    *reinterpret_cast<float4*>(p + i + 4) = make_float4(v[4] * scale, v[5] * scale, v[6] * scale, v[7] * scale);
+}
+template <> __device__ __forceinline__ void st8<bf16_t>(bf16_t* p, size_t i, const float* v, float scale) {
+    *reinterpret_cast<uint4*>(p + i) =
+        make_uint4(pack_bf16x2(v[0] * scale, v[1] * scale), pack_bf16x2(v[2] * scale, v[3] * scale),
+                   pack_bf16x2(v[4] * scale, v[5] * scale), pack_bf16x2(v[6] * scale, v[7] * scale));
+}
+
 // The feature map phi applied to queries and keys: identity, or elu(z) + 1
 // (z + 1 for z > 0, e^z otherwise) -- linear attention's kernel feature map.
 __device__ __forceinline__ float feature(float z, int phi) {

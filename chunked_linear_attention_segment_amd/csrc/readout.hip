@@ -218,7 +218,8 @@ int launch_xps(const mc_dims& d, const void* X, float* xps, float* tails, void* 
 
 // Generic read kernel.  A workgroup covers TT = 32 consecutive tokens of one (b, h); the 8
 // threads of a token share its gate (online softmax over the segments it reads) and each
-// owns the DV/8 output columns c = p, p+8, ...  State i is read straight from global memory
+// owns DV/8 consecutive output columns c = p DV/8 + m (vector loads of the online read and
+// vector stores of y).  State i is read straight from global memory
 // (TS = fp32 states for fp32 inputs, the bf16 copy for bf16 inputs).  SSC = true restricts
 // each token to the segments listed in idx.
 template <typename T, typename TS, int DK, int DV, bool SSC>
@@ -261,8 +262,15 @@ __global__ __launch_bounds__(256) void readout_valu_kernel(
 
     float acc[CPT];
     float mx = a_on, l = 1.f;
+    const size_t orow = (bh * L + tc) * DV + (size_t)p * CPT;
 #pragma unroll
-    for (int m = 0; m < CPT; ++m) acc[m] = O_on[(bh * L + tc) * DV + p + 8 * m];
+    for (int m = 0; m < CPT; m += 4) {
+        const float4 o = *reinterpret_cast<const float4*>(O_on + orow + m);
+        acc[m] = o.x;
+        acc[m + 1] = o.y;
+        acc[m + 2] = o.z;
+        acc[m + 3] = o.w;
+    }
 
     for (int i = 0; i < s_hi; ++i) {
         bool use = valid && i < s;
@@ -285,17 +293,22 @@ __global__ __launch_bounds__(256) void readout_valu_kernel(
         const TS* Si = S + (bh * NS + i) * (size_t)(DV * DK);
 #pragma unroll
         for (int m = 0; m < CPT; ++m) {
-            const TS* row = Si + (size_t)(p + 8 * m) * DK;
+            const TS* row = Si + (size_t)(p * CPT + m) * DK;
             float dot = 0.f;
-#pragma unroll 8
-            for (int r = 0; r < DK; ++r) dot += ld(row, r) * sq[tt][r];
+#pragma unroll 4
+            for (int r = 0; r < DK; r += 8) {  // 16-byte (bf16) / 32-byte (fp32) row slices
+                float v[8];
+                ld8(row, (size_t)r, v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot += v[e] * sq[tt][r + e];
+            }
             acc[m] = acc[m] * sc + w * dot;
         }
     }
     if (!valid) return;
     const float inv_l = 1.f / l;
 #pragma unroll
-    for (int m = 0; m < CPT; ++m) st(Y, (bh * L + t) * DV + p + 8 * m, acc[m] * inv_l);
+    for (int m = 0; m < CPT; m += 8) st8(Y, (bh * L + t) * DV + (size_t)p * CPT + m, &acc[m], inv_l);
 
     if (gamma) {
         float* gr = gamma + (bh * L + t) * (size_t)NS;
