@@ -314,8 +314,8 @@ def run_decode(args, rec, dev):
 def run_log_segments(args, rec, dev):
     """The logarithmic segmentation (one segment per set bit of L, largest first) of the L=64K
     workload's shape at L = 65535 (16 segments of 32768 .. 1 tokens): mc_scan_prefill_segs +
-    mc_grm_readout_segs, inputs resident, tokens/s.  These run the fp32-accumulating kernels
-    that take any boundaries; the roofline is the fp32 vector unit."""
+    mc_grm_readout_segs, inputs resident, tokens/s (bf16 d = 128: the MFMA scan, its 32768-token
+    segment as pieces, and the MFMA read with the segment table)."""
     import torch
 
     import chunked_linear_attention_segment_amd as mc
@@ -336,11 +336,12 @@ def run_log_segments(args, rec, dev):
     O_on = torch.empty((B, H, L, dv), dtype=torch.float32, device=dev)
     Y = torch.empty((B, H, L, dv), dtype=torch.bfloat16, device=dev)
     ws = mc.workspace(d, mc.MC_OP_GRM, device=dev)
+    wss = mc.workspace_segs(d, NS, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
         mc.mc_scan_prefill_segs(d, off, inp["Q"], inp["K"], inp["V"], inp["X"], M, M_lo, P,
-                                O_on, stream=stream)
+                                O_on, ws=wss, stream=stream)
         mc.mc_grm_readout_segs(d, off, inp["Q"], inp["U"], inp["X"], M, M_lo, P, O_on, Y,
                                None, ws=ws, stream=stream)
     for _ in range(args.warmup):
@@ -355,23 +356,28 @@ def run_log_segments(args, rec, dev):
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     # algorithmic FLOPs: per token, the state update and online read (4 dk dv), the reads of
-    # the completed segments before its own (2 dk dv each) and s + 1 gate logits (2 dg each)
+    # the completed segments before its own (2 dk dv each) and s + 1 gate logits (2 dg each);
+    # algorithmic bytes: Q, K, V, U read and Y written once (bf16), X once per sequence, the
+    # states (fp32 + bf16) and means written.  At about 77 FLOP per byte the step is below the
+    # bf16 ridge (2.5 PFLOP/s / 8 TB/s), so its roofline is HBM.
     fl = 0
     for s in range(NS):
         n = off[s + 1] - off[s]
         fl += n * (4 * dk * dv + s * 2 * dk * dv + (s + 1) * 2 * dg)
     fl *= B * H
-    tflops = fl / (ms / 1e3) / 1e12
+    by = B * H * L * (2 * dk * 2 + 2 * dv * 2 + 2 * dg) + B * L * dg * 2 + \
+        B * H * NS * dv * dk * 6 + B * NS * dg * 4
+    gbs = by / (ms / 1e3) / 1e9
     rec["log_segments"] = {
         "workload": "grm_bf16_L64K shape at L=65535, logarithmic segmentation (%d segments)"
                     % NS,
         "metric": "prefill tokens/s", "value": round(B * L / (ms / 1e3), 1), "unit": "tokens/s",
         "ms_per_step": round(ms, 4),
         "steps_timed": "mc_scan_prefill_segs + mc_grm_readout_segs",
-        "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": 157.3,
-                     "unit": "TFLOP/s", "frac": round(tflops / 157.3, 4),
-                     "algorithmic_flops": fl}}
-    del inp, M, M_lo, P, O_on, Y, ws
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": by, "algorithmic_flops": fl}}
+    del inp, M, M_lo, P, O_on, Y, ws, wss
     torch.cuda.empty_cache()
 
 

@@ -25,7 +25,8 @@ MC_OK, MC_ERR_NULL, MC_ERR_DIMS, MC_ERR_UNSUPPORTED = 0, 1, 2, 3
 MC_ERR_ALIGN, MC_ERR_WORKSPACE, MC_ERR_HIP, MC_ERR_CAPACITY = 4, 5, 6, 7
 MC_F32, MC_BF16 = 0, 1
 MC_PHI_IDENTITY, MC_PHI_ELU1 = 0, 1
-MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE, MC_OP_GRM_BACKWARD = 0, 1, 2, 3, 4
+MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE, MC_OP_GRM_BACKWARD, MC_OP_SCAN_SEGS = \
+    0, 1, 2, 3, 4, 5
 
 EXPORTED = ["mc_abi_version", "mc_status_str", "mc_workspace_bytes", "mc_scan_prefill",
             "mc_grm_readout", "mc_ssc_readout", "mc_decode_step", "mc_scan_prefill_segs",
@@ -70,7 +71,8 @@ def load(path: str = LIB_PATH):
         lib.mc_ssc_readout.argtypes = [D, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P, P,
                                        P, ctypes.c_size_t, P]
         lib.mc_scan_prefill_segs.restype = ctypes.c_int
-        lib.mc_scan_prefill_segs.argtypes = [D, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P]
+        lib.mc_scan_prefill_segs.argtypes = [D, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P,
+                                             ctypes.c_size_t, P]
         lib.mc_grm_readout_segs.restype = ctypes.c_int
         lib.mc_grm_readout_segs.argtypes = [D, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
                                             ctypes.c_size_t, P]
@@ -164,13 +166,22 @@ def _offsets(seg_off):
     return off, off.shape[0] - 1
 
 
-def mc_scan_prefill_segs(dims, seg_off, Q, K, V, X, M, M_lo, P, O_on, stream=None):
-    """seg_off: host offsets 0 = o_0 < ... < o_n = L (segment i = [o_i, o_{i+1}))."""
+def mc_scan_prefill_segs(dims, seg_off, Q, K, V, X, M, M_lo, P, O_on, ws=None, stream=None):
+    """seg_off: host offsets 0 = o_0 < ... < o_n = L (segment i = [o_i, o_{i+1})); ws:
+    mc_workspace_bytes(dims, MC_OP_SCAN_SEGS, n) bytes (see workspace_segs)."""
     off, n = _offsets(seg_off)
+    w, wb = _ws(ws)
     _check(load().mc_scan_prefill_segs(ctypes.byref(dims), off.ctypes.data, n, _p(Q), _p(K),
-                                       _p(V), _p(X), _p(M), _p(M_lo), _p(P), _p(O_on),
+                                       _p(V), _p(X), _p(M), _p(M_lo), _p(P), _p(O_on), w, wb,
                                        _stream(stream)),
            "mc_scan_prefill_segs")
+
+
+def workspace_segs(dims, n_seg, device="cuda"):
+    """Workspace of mc_scan_prefill_segs for n_seg segments (None when none is needed)."""
+    import torch
+    nb = mc_workspace_bytes(dims, MC_OP_SCAN_SEGS, n_seg)
+    return torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
 
 
 def mc_grm_readout_segs(dims, seg_off, Q, U, X, M, M_lo, P, O_on, Y, gamma=None, ws=None,
@@ -289,7 +300,8 @@ def prefill_grm_segs(dims, seg_off, Q, K, V, U, X, want_gamma=False, stream=None
                        device=dev)
     P = torch.empty((dims.B, dims.x_heads, NS, dims.d_g), dtype=torch.float32, device=dev)
     O_on = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch.float32, device=dev)
-    mc_scan_prefill_segs(dims, seg_off, Q, K, V, X, M, M_lo, P, O_on, stream=stream)
+    mc_scan_prefill_segs(dims, seg_off, Q, K, V, X, M, M_lo, P, O_on,
+                         ws=workspace_segs(dims, NS, device=dev), stream=stream)
     Y = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch_dtype(dims), device=dev)
     G = torch.empty((dims.B, dims.H, dims.L, NS), dtype=torch.float32,
                     device=dev) if want_gamma else None

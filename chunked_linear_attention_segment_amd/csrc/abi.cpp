@@ -155,6 +155,8 @@ size_t mc_workspace_bytes(const mc_dims* d, mc_op op, int32_t top_k, int32_t n_c
         case MC_OP_GRM: return grm_workspace(*d).total;
         case MC_OP_SSC: return top_k >= 1 ? ssc_workspace(*d).total : 0;
         case MC_OP_GRM_BACKWARD: return bwd_workspace(*d).total;
+        case MC_OP_SCAN_SEGS:
+            return top_k >= 1 && top_k <= MC_MAX_SEGS ? segs_scan_ws_bytes(*d, top_k) : 0;
         default: return 0;
     }
 }
@@ -265,18 +267,22 @@ static mc_status check_segs(const mc_dims* d, const int32_t* off, int32_t n_seg,
 
 mc_status mc_scan_prefill_segs(const mc_dims* d, const int32_t* seg_off, int32_t n_seg,
                                const void* Q, const void* K, const void* V, const void* X,
-                               float* M, uint16_t* M_lo, float* P, float* O_on, void* stream) {
+                               float* M, uint16_t* M_lo, float* P, float* O_on, void* ws,
+                               size_t ws_bytes, void* stream) {
     mc_status st = check_dims(d, true);
     if (st != MC_OK) return st;
     SegArg sg;
     if ((st = check_segs(d, seg_off, n_seg, &sg)) != MC_OK) return st;
     if (!Q || !K || !V || !X || !M || !P) return MC_ERR_NULL;
     if (d->dtype == MC_BF16 && !M_lo) return MC_ERR_NULL;
-    const void* ptrs[] = {Q, K, V, X, M, M_lo, P, O_on};
+    const size_t need = segs_scan_ws_bytes(*d, n_seg);
+    if (need && (!ws || ws_bytes < need)) return MC_ERR_WORKSPACE;
+    const void* ptrs[] = {Q, K, V, X, M, M_lo, P, O_on, ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MC_ERR_ALIGN;
-    return launch_scan_prefill_segs(*d, sg, Q, K, V, X, M, M_lo, P, O_on, stream) ? MC_ERR_HIP
-                                                                                  : MC_OK;
+    return launch_scan_prefill_segs(*d, sg, Q, K, V, X, M, M_lo, P, O_on, ws, ws_bytes, stream)
+               ? MC_ERR_HIP
+               : MC_OK;
 }
 
 mc_status mc_grm_readout_segs(const mc_dims* d, const int32_t* seg_off, int32_t n_seg,

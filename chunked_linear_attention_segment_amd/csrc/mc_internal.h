@@ -120,9 +120,18 @@ int launch_grm_backward(const mc_dims& d, const BwdBuffers& w, const void* Q, co
                         const uint16_t* M_lo, const float* P, const void* dY, float* dQ,
                         float* dK, float* dV, float* dU, float* dX, void* stream);
 
+// Long segments of the offsets scan are cut into pieces (at most scan_piece_len tokens, each
+// inside one segment) that are scanned in parallel; `first` marks the pieces that start a
+// segment.  The pieces' states and their prefix sums within a segment take workspace.
+struct PieceArg {
+    SegArg sg;
+    uint32_t first[(MC_MAX_SEGS + 32) / 32];
+};
+int scan_piece_len(int L, int n_seg);            // 0: no piece table fits MC_MAX_SEGS
+size_t segs_scan_ws_bytes(const mc_dims& d, int n_seg);
 int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
                              const void* V, const void* X, float* M, uint16_t* M_lo, float* P,
-                             float* O_on, void* stream);
+                             float* O_on, void* ws, size_t ws_bytes, void* stream);
 // xps / xtail (nullable: the per-segment walk of aon_kernel is used instead) are workspace for
 // the segment-causal prefix sums of X.
 int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* U,
@@ -155,7 +164,8 @@ bool read_mfma_covers(const mc_dims& d);
 int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* K,
                      const void* V, const void* U, const float* xps, const uint16_t* M_lo,
                      const float* P, const float* O_on, const int32_t* idx,
-                     const GateWeights& gw, void* Y, void* stream);
+                     const GateWeights& gw, void* Y, void* stream,
+                     const SegArg* sg = nullptr);
 
 int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const void* V,
                        const void* U, const float* aon, const float* xps, const float* M,

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     const float* __restrict__ P, const float* __restrict__ O_on,
     const int32_t* __restrict__ idx, const bf16_t* __restrict__ Wg,
     const float* __restrict__ won_g, const float* __restrict__ inv_l_g, int top_k, int BH,
-    int H, int L, int C, int NS, int DG, int xh, bf16_t* __restrict__ Y) {
+    int H, int L, int C, int NS, int DG, int xh, bf16_t* __restrict__ Y, const SegArg sg) {
     static_assert(!(PRE && SSC), "precomputed weights are a GRM mode");
     static_assert(RT == kGateTile, "the gate pass writes weights per read tile");
     constexpr int KS = DK / 16;  // MFMA k-steps over d_k
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     const int l32 = lane & 31, hi32 = lane >> 5;
     const int tile0 = tile * RT;
     const int last = min(L, tile0 + RT) - 1;
-    const int s_hi = last / C;  // states 0..s_hi-1 are read by some token of the tile
+    const int s_hi = seg_of(sg, last, C);  // states 0..s_hi-1 are read by some token of the tile
     const size_t bx = (size_t)(bh / H) * xh + (xh == 1 ? 0 : bh % H);
     const float* Pbx = P + bx * NS * DG;
 
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
         tl[tb] = 32 * blk + l32;
         val[tb] = tile0 + tl[tb] < L;
         tok[tb] = min(tile0 + tl[tb], L - 1);
-        seg[tb] = tok[tb] / C;
+        seg[tb] = seg_of(sg, tok[tb], C);
     }
 
     // =============================== 1. gate =================================================
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
             }
         }
         dot += __shfl_xor(dot, 32, 64);
-        a_on[tb] = dot / (float)(tok[tb] - seg[tb] * C + 1);
+        a_on[tb] = dot / (float)(tok[tb] - seg_first(sg, seg[tb], C) + 1);
         m[tb] = a_on[tb];
         l[tb] = 0.f;
     }
@@ -753,26 +753,27 @@ template <int DK, int DV, bool SSC, bool FON, int PHI, bool PRE>
 void launch_k(const mc_dims& d, int top_k, const void* Q, const void* K, const void* V,
               const void* U, const float* xps, const uint16_t* M_lo, const float* P,
               const float* O_on, const int32_t* idx, const GateWeights& gw, void* Y,
-              hipStream_t st) {
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+              hipStream_t st, const SegArg& sg) {
+    const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
     const int T = (d.L + RT - 1) / RT;
     const int BH = d.B * d.H;
     hipLaunchKernelGGL((grm_read_kernel<DK, DV, SSC, FON, PHI, PRE>), dim3(BH * T),
                        dim3(RTHREADS), 0, st, (const bf16_t*)Q, (const bf16_t*)K,
                        (const bf16_t*)V, (const bf16_t*)U, xps, (const bf16_t*)M_lo, P, O_on,
                        idx, (const bf16_t*)gw.W, gw.won, gw.inv_l, top_k, BH, d.H, d.L,
-                       d.seg_len, NS, d.d_g, d.x_heads, (bf16_t*)Y);
+                       d.seg_len, NS, d.d_g, d.x_heads, (bf16_t*)Y, sg);
 }
 
 template <int DK, int DV, bool SSC, bool PRE>
 int launch_t(const mc_dims& d, int top_k, const void* Q, const void* K, const void* V,
              const void* U, const float* xps, const uint16_t* M_lo, const float* P,
              const float* O_on, const int32_t* idx, const GateWeights& gw, void* Y,
-             hipStream_t st) {
+             hipStream_t st, const SegArg& sg) {
     // the online term is formed in the kernel (from K and V) when the scan did not write it;
     // the feature map is a template argument so the key fragments' loop has no branches
 #define MC_K(FON, PHI)                                                                         \
-    launch_k<DK, DV, SSC, FON, PHI, PRE>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, gw, Y, st)
+    launch_k<DK, DV, SSC, FON, PHI, PRE>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, gw, Y, st, \
+                                         sg)
     if (O_on)
         d.phi ? MC_K(false, 1) : MC_K(false, 0);
     else
@@ -789,23 +790,29 @@ bool read_mfma_covers(const mc_dims& d) {
            (d.d_k == 64 || d.d_k == 128) && (d.d_v == 64 || d.d_v == 128);
 }
 
+static const SegArg kConstSegRd{};  // constant segment length
+
 int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* K,
                      const void* V, const void* U, const float* xps, const uint16_t* M_lo,
                      const float* P, const float* O_on, const int32_t* idx,
-                     const GateWeights& gw, void* Y, void* stream) {
+                     const GateWeights& gw, void* Y, void* stream, const SegArg* sgp) {
     if (!read_mfma_covers(d)) return -1;
+    // segment offsets: GRM with the online read given (the fused online term and the gate
+    // pass assume a constant length)
+    if (sgp && sgp->n && (ssc || !O_on || gw.W)) return -1;
+    const SegArg& sg = sgp ? *sgp : kConstSegRd;
     hipStream_t st = (hipStream_t)stream;
     if (gw.W) {  // the gate ran as its own pass (d_k = d_v = 128 GRM)
         if (ssc || d.d_k != 128 || d.d_v != 128) return -1;
         return launch_t<128, 128, false, true>(d, 0, Q, K, V, U, xps, M_lo, P, O_on, idx, gw, Y,
-                                               st);
+                                               st, sg);
     }
 #define MC_RD(DK, DV)                                                                          \
     if (d.d_k == DK && d.d_v == DV)                                                            \
         return ssc ? launch_t<DK, DV, true, false>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on,    \
-                                                   idx, gw, Y, st)                             \
+                                                   idx, gw, Y, st, sg)                         \
                    : launch_t<DK, DV, false, false>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on,  \
-                                                    idx, gw, Y, st);
+                                                    idx, gw, Y, st, sg);
     MC_RD(128, 128)
     MC_RD(128, 64)
     MC_RD(64, 128)

@@ -369,6 +369,36 @@ static int launch_readout(const mc_dims& d, int top_k, const void* Q, const void
     return (int)hipErrorInvalidValue;
 }
 
+// gamma_t^(i) written out on request (a diagnostic output of the bf16 path, whose fused
+// kernel never materialises the weights): one thread per token, fp32, straight from
+// the definition.
+template <typename T>
+__global__ void gamma_kernel(const T* __restrict__ U, const float* __restrict__ aon,
+                             const float* __restrict__ P, int L, int C, int NS, int DG, int H,
+                             int xh, float* __restrict__ gamma, const SegArg sg) {
+    const int t = blockIdx.x * 64 + threadIdx.x;
+    const size_t bh = blockIdx.y;
+    if (t >= L) return;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const size_t bx = (size_t)b * xh + (xh == 1 ? 0 : h);
+    const int s = seg_of(sg, t, C);
+    const T* u = U + (bh * L + t) * DG;
+    const float a_on = aon[bh * L + t];
+    auto logit = [&](int i) {
+        const float* Pi = P + (bx * NS + i) * DG;
+        float a = 0.f;
+        for (int e = 0; e < DG; ++e) a += ld(u, e) * Pi[e];
+        return a;
+    };
+    float mx = a_on;
+    for (int i = 0; i < s; ++i) mx = fmaxf(mx, logit(i));
+    float z = __expf(a_on - mx);
+    for (int i = 0; i < s; ++i) z += __expf(logit(i) - mx);
+    float* gr = gamma + (bh * L + t) * (size_t)NS;
+    for (int i = 0; i < NS; ++i)
+        gr[i] = i < s ? __expf(logit(i) - mx) / z : (i == s ? __expf(a_on - mx) / z : 0.f);
+}
+
 // Arbitrary boundaries: online logits, then the generic read with the online term O_on of
 // mc_scan_prefill_segs.
 int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* U,
@@ -377,9 +407,7 @@ int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, c
                             float* gamma, void* stream) {
     hipStream_t st = (hipStream_t)stream;
     int rc;
-    if (xps) {  // prefix sums of X per segment, then the logits token by token
-        rc = launch_xps_sg(d, X, xps, xtail, sg, st);
-        if (rc) return rc;
+    auto logits = [&]() {  // the online logits token by token from the prefix sums
         const dim3 grid((d.L + 31) / 32, d.B * d.H);
         if (d.dtype == MC_BF16)
             hipLaunchKernelGGL(aon_xps_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)U,
@@ -387,7 +415,24 @@ int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, c
         else
             hipLaunchKernelGGL(aon_xps_kernel<float>, grid, dim3(256), 0, st, (const float*)U,
                                xps, d.L, d.seg_len, d.d_g, d.H, d.x_heads, aon, sg);
-        rc = (int)hipGetLastError();
+        return (int)hipGetLastError();
+    };
+    if (xps) {  // prefix sums of X per segment
+        rc = launch_xps_sg(d, X, xps, xtail, sg, st);
+        if (rc) return rc;
+        // bf16 widths 64/128: the MFMA read with the segment table (its gate, online logits
+        // included, in-kernel; the online term from O_on), then gamma on request
+        rc = launch_read_mfma(d, false, 0, Q, nullptr, nullptr, U, xps, M_lo, P, O_on, nullptr,
+                              GateWeights{}, Y, stream, &sg);
+        if (rc >= 0) {
+            if (rc || !gamma) return rc;
+            if ((rc = logits())) return rc;
+            hipLaunchKernelGGL(gamma_kernel<bf16_t>, dim3((d.L + 63) / 64, d.B * d.H), dim3(64),
+                               0, st, (const bf16_t*)U, aon, P, d.L, d.seg_len, sg.n, d.d_g,
+                               d.H, d.x_heads, gamma, sg);
+            return (int)hipGetLastError();
+        }
+        rc = logits();  // not covered: the generic read below
     } else {
         rc = launch_aon_sg(d, X, U, aon, sg, st);
     }
@@ -409,36 +454,6 @@ int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, c
     return (int)hipErrorInvalidValue;
 }
 
-// gamma_t^(i) written out on request (a diagnostic output of the bf16 path, whose fused
-// kernel never materialises the weights): one thread per token, fp32, straight from
-// the definition.
-template <typename T>
-__global__ void gamma_kernel(const T* __restrict__ U, const float* __restrict__ aon,
-                             const float* __restrict__ P, int L, int C, int NS, int DG, int H,
-                             int xh, float* __restrict__ gamma) {
-    const int t = blockIdx.x * 64 + threadIdx.x;
-    const size_t bh = blockIdx.y;
-    if (t >= L) return;
-    const int b = (int)(bh / H), h = (int)(bh % H);
-    const size_t bx = (size_t)b * xh + (xh == 1 ? 0 : h);
-    const int s = t / C;
-    const T* u = U + (bh * L + t) * DG;
-    const float a_on = aon[bh * L + t];
-    auto logit = [&](int i) {
-        const float* Pi = P + (bx * NS + i) * DG;
-        float a = 0.f;
-        for (int e = 0; e < DG; ++e) a += ld(u, e) * Pi[e];
-        return a;
-    };
-    float mx = a_on;
-    for (int i = 0; i < s; ++i) mx = fmaxf(mx, logit(i));
-    float z = __expf(a_on - mx);
-    for (int i = 0; i < s; ++i) z += __expf(logit(i) - mx);
-    float* gr = gamma + (bh * L + t) * (size_t)NS;
-    for (int i = 0; i < NS; ++i)
-        gr[i] = i < s ? __expf(logit(i) - mx) / z : (i == s ? __expf(a_on - mx) / z : 0.f);
-}
-
 int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const void* V,
                        const void* U, const float* aon, const float* xps, const float* M,
                        const uint16_t* M_lo, const float* P, const float* O_on,
@@ -452,7 +467,7 @@ int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const voi
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     hipLaunchKernelGGL(gamma_kernel<bf16_t>, dim3((d.L + 63) / 64, d.B * d.H), dim3(64), 0,
                        (hipStream_t)stream, (const bf16_t*)U, aon, P, d.L, d.seg_len, NS,
-                       d.d_g, d.H, d.x_heads, gamma);
+                       d.d_g, d.H, d.x_heads, gamma, kConstSegR);
     return (int)hipGetLastError();
 }
 

@@ -118,7 +118,17 @@ __global__ __launch_bounds__(256) void seg_means_kernel(const T* __restrict__ X,
     const int tl = threadIdx.x / 16, cg = threadIdx.x % 16;
     for (int e0 = cg * 8; e0 < DG; e0 += 128) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int j = tl; j < len; j += 16) {
+        int j = tl;
+        for (; j + 48 < len; j += 64) {  // four rows in flight per thread
+            float v0[8], v1[8], v2[8], v3[8];
+            ld8(X, (bx * L + t0 + j) * DG + e0, v0);
+            ld8(X, (bx * L + t0 + j + 16) * DG + e0, v1);
+            ld8(X, (bx * L + t0 + j + 32) * DG + e0, v2);
+            ld8(X, (bx * L + t0 + j + 48) * DG + e0, v3);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] += ((v0[k] + v1[k]) + (v2[k] + v3[k]));
+        }
+        for (; j < len; j += 16) {
             float v[8];
             ld8(X, (bx * L + t0 + j) * DG + e0, v);
 #pragma unroll
@@ -184,15 +194,125 @@ static int launch_means(const mc_dims& d, const void* X, float* P, const SegArg&
 }
 
 int launch_scan_mfma_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
-                          const void* V, float* M, uint16_t* M_lo, float* O_on, void* stream);
+                          const void* V, float* M, uint16_t* M_lo, float* O_on, void* stream,
+                          const float* M0 = nullptr);
 
-// Arbitrary boundaries: the MFMA scan for bf16 widths 64/128, else the generic scan (any
-// dtype); then the means over each segment.
+__device__ __forceinline__ bool piece_first(const PieceArg& pa, int j) {
+    return (pa.first[j >> 5] >> (j & 31)) & 1u;
+}
+
+// Prefix sums of the piece states inside each segment: the memory restarts only at a
+// segment start (Eq. 4b), so the memory before piece j is the sum of the earlier pieces of
+// its segment (Pref_j, zero for a segment's first piece) and the segment's state is the sum
+// of all of them.  One workgroup per (segment's first piece j, b*H+h, 1024-element slice of
+// the d_v x d_k state) walks the segment's pieces in order; workgroups of other pieces exit.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void piece_prefix_kernel(const float* __restrict__ Msub,
+                                                           int NP, const PieceArg pa, int NS,
+                                                           float* __restrict__ Pref,
+                                                           float* __restrict__ M,
+                                                           bf16_t* __restrict__ M_lo) {
+    constexpr int N = DV * DK;
+    const int j = blockIdx.x;
+    if (!piece_first(pa, j)) return;  // uniform
+    const size_t bh = blockIdx.y;
+    const int e0 = blockIdx.z * 1024 + threadIdx.x;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int jj = j;
+    do {
+        const float* src = Msub + (bh * NP + jj) * (size_t)N;
+        float* dst = Pref + (bh * NP + jj) * (size_t)N;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            dst[e0 + 256 * k] = acc[k];
+            acc[k] += src[e0 + 256 * k];
+        }
+        ++jj;
+    } while (jj < NP && !piece_first(pa, jj));
+    int seg = -1;  // segments started up to piece j
+    for (int w = 0; w <= (j >> 5); ++w) {
+        uint32_t bits = pa.first[w];
+        if (w == (j >> 5) && (j & 31) != 31) bits &= (2u << (j & 31)) - 1u;
+        seg += __popc(bits);
+    }
+    float* m = M + (bh * NS + seg) * (size_t)N;
+    bf16_t* ml = M_lo + (bh * NS + seg) * (size_t)N;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        m[e0 + 256 * k] = acc[k];
+        ml[e0 + 256 * k] = f32_to_bf16(acc[k]);
+    }
+}
+
+int scan_piece_len(int L, int n_seg) {
+    for (int pl = 512; pl > 0 && pl <= (1 << 30); pl <<= 1)
+        if (n_seg + (L + pl - 1) / pl <= MC_MAX_SEGS) return pl;
+    return 0;
+}
+
+// two fp32 state arrays (pieces, prefix sums) for at most n_seg + ceil(L / piece) pieces;
+// only the bf16 MFMA scan splits segments
+size_t segs_scan_ws_bytes(const mc_dims& d, int n_seg) {
+    const bool mfma = d.dtype == MC_BF16 && (d.d_k == 64 || d.d_k == 128) &&
+                      (d.d_v == 64 || d.d_v == 128);
+    const int pl = scan_piece_len(d.L, n_seg);
+    if (!mfma || !pl) return 0;
+    const size_t np = (size_t)n_seg + (d.L + pl - 1) / pl;
+    return 2 * align256(sizeof(float) * (size_t)d.B * d.H * np * d.d_v * d.d_k);
+}
+
+template <int DK, int DV>
+static int launch_pieces_t(const mc_dims& d, const PieceArg& pa, int NS, float* Msub,
+                           float* Pref, float* M, uint16_t* M_lo, hipStream_t st) {
+    const int NP = pa.sg.n;
+    hipLaunchKernelGGL((piece_prefix_kernel<DK, DV>), dim3(NP, d.B * d.H, DV * DK / 1024),
+                       dim3(256), 0, st, Msub, NP, pa, NS, Pref, M, (bf16_t*)M_lo);
+    return (int)hipGetLastError();
+}
+
+// Arbitrary boundaries: the MFMA scan for bf16 widths 64/128 (segments longer than a piece
+// split into pieces scanned in parallel, then combined), else the generic scan (any dtype);
+// then the means over each segment.
 int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
                              const void* V, const void* X, float* M, uint16_t* M_lo, float* P,
-                             float* O_on, void* stream) {
+                             float* O_on, void* ws, size_t ws_bytes, void* stream) {
     hipStream_t st = (hipStream_t)stream;
-    int rc = launch_scan_mfma_segs(d, sg, Q, K, V, M, M_lo, O_on, stream);
+    int rc = -1;
+    const int pl = scan_piece_len(d.L, sg.n);
+    bool split = false;
+    for (int i = 0; pl && i < sg.n; ++i) split |= sg.off[i + 1] - sg.off[i] > pl;
+    const size_t need = segs_scan_ws_bytes(d, sg.n);
+    if (split && need && ws && ws_bytes >= need) {
+        PieceArg piece{};
+        int np = 0;
+        for (int i = 0; i < sg.n; ++i)
+            for (int a = sg.off[i]; a < sg.off[i + 1]; a += pl) {
+                if (a == sg.off[i]) piece.first[np >> 5] |= 1u << (np & 31);
+                piece.sg.off[np++] = a;
+            }
+        piece.sg.off[np] = d.L;
+        piece.sg.n = np;
+        // the pieces' own states; their prefix sums per segment (and the segments' states);
+        // then, for the online read, the pieces again from the memory before each
+        float* Msub = (float*)ws;
+        float* Pref = (float*)((char*)ws + need / 2);
+        rc = launch_scan_mfma_segs(d, piece.sg, Q, K, V, Msub, nullptr, nullptr, stream);
+        if (rc >= 0) {
+            if (rc) return rc;
+            if (d.d_k == 128 && d.d_v == 128)
+                rc = launch_pieces_t<128, 128>(d, piece, sg.n, Msub, Pref, M, M_lo, st);
+            else if (d.d_k == 128)
+                rc = launch_pieces_t<128, 64>(d, piece, sg.n, Msub, Pref, M, M_lo, st);
+            else if (d.d_v == 128)
+                rc = launch_pieces_t<64, 128>(d, piece, sg.n, Msub, Pref, M, M_lo, st);
+            else
+                rc = launch_pieces_t<64, 64>(d, piece, sg.n, Msub, Pref, M, M_lo, st);
+            if (!rc && O_on)
+                rc = launch_scan_mfma_segs(d, piece.sg, Q, K, V, nullptr, nullptr, O_on, stream,
+                                           Pref);
+        }
+    }
+    if (rc < 0) rc = launch_scan_mfma_segs(d, sg, Q, K, V, M, M_lo, O_on, stream);
     if (rc < 0)
         rc = d.dtype == MC_BF16 ? launch_scan_dt<bf16_t>(d, Q, K, V, M, M_lo, O_on, sg, st)
                                 : launch_scan_dt<float>(d, Q, K, V, M, M_lo, O_on, sg, st);

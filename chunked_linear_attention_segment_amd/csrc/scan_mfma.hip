@@ -69,7 +69,7 @@ template <int DK, int DV, bool ON, bool SW>
 __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     int L, int C, int NS, int phi, float* __restrict__ M, bf16_t* __restrict__ M_lo,
-    float* __restrict__ O_on, SwlaGates gt, const SegArg sg) {
+    float* __restrict__ O_on, SwlaGates gt, const SegArg sg, const float* __restrict__ M0) {
     constexpr int NT = DV * 2;      // threads: one wave per 32 value rows
     constexpr int DB = DK / 32;     // 32-row blocks of d
     constexpr int KSD = DK / 16;    // k-steps over d
@@ -94,6 +94,28 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt[db][r] = 0.f;
     u32x4_t ma[KSD];  // bf16 copy of M_prev in A-operand form (k-step k = rows 16k..16k+15)
+    if (M0) {  // the memory before the segment's first token (a piece of a longer segment)
+        const float* m0 = M0 + ((blockIdx.y * (size_t)NS + blockIdx.x) * DV + wave * 32 + (threadIdx.x & 31)) * DK;
+        const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 v = *reinterpret_cast<const float4*>(m0 + db * 32 + 8 * g + 4 * hf);
+                mt[db][4 * g] = v.x;
+                mt[db][4 * g + 1] = v.y;
+                mt[db][4 * g + 2] = v.z;
+                mt[db][4 * g + 3] = v.w;
+            }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                ma[2 * db + hh] = u32x4_t{pk2(mt[db][8 * hh + 0], mt[db][8 * hh + 1]),
+                                          pk2(mt[db][8 * hh + 2], mt[db][8 * hh + 3]),
+                                          pk2(mt[db][8 * hh + 4], mt[db][8 * hh + 5]),
+                                          pk2(mt[db][8 * hh + 6], mt[db][8 * hh + 7])};
+    }
 
     const bf16_t* Qs = Q + (bh * L + t0) * DK;
     const bf16_t* Ks = K + (bh * L + t0) * DK;
@@ -158,7 +180,7 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) ot[tb][r] = 0.f;
-            if (j0 > 0) {
+            if (j0 > 0 || M0) {
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
@@ -316,8 +338,9 @@ __global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
             const int d = db * 32 + 8 * g + 4 * half;
             *reinterpret_cast<float4*>(M + mo + d) =
                 make_float4(mt[db][4 * g], mt[db][4 * g + 1], mt[db][4 * g + 2], mt[db][4 * g + 3]);
-            *reinterpret_cast<u32x2_t*>(M_lo + mo + d) =
-                u32x2_t{pk2(mt[db][4 * g], mt[db][4 * g + 1]), pk2(mt[db][4 * g + 2], mt[db][4 * g + 3])};
+            if (M_lo)  // (optional: the pieces of a split segment keep only fp32)
+                *reinterpret_cast<u32x2_t*>(M_lo + mo + d) =
+                    u32x2_t{pk2(mt[db][4 * g], mt[db][4 * g + 1]), pk2(mt[db][4 * g + 2], mt[db][4 * g + 3])};
         }
 }
 
@@ -326,12 +349,13 @@ static const SegArg kConstSegM{};  // constant segment length
 template <int DK, int DV>
 static int launch_scan_mfma_t(const mc_dims& d, const void* Q, const void* K, const void* V,
                               float* M, uint16_t* M_lo, float* O_on, const SwlaGates& gt,
-                              hipStream_t st, const SegArg& sg = kConstSegM) {
+                              hipStream_t st, const SegArg& sg = kConstSegM,
+                              const float* M0 = nullptr) {
     const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
 #define MC_SCAN(ON, SW)                                                                        \
     hipLaunchKernelGGL((scan_mfma_kernel<DK, DV, ON, SW>), dim3(NS, d.B * d.H), dim3(DV * 2),   \
                        0, st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, d.L,        \
-                       d.seg_len, NS, d.phi, M, (bf16_t*)M_lo, O_on, gt, sg)
+                       d.seg_len, NS, d.phi, M, (bf16_t*)M_lo, O_on, gt, sg, M0)
     if (gt.alpha) {  // SWLA: the read takes the online term from O_on, so it is always written
         if (!O_on) return (int)hipErrorInvalidValue;
         MC_SCAN(true, true);
@@ -347,13 +371,14 @@ static int launch_scan_mfma_t(const mc_dims& d, const void* Q, const void* K, co
 // Any segment boundaries (the offsets passed by value), bf16: states, their bf16 copy and the
 // optional online read; -1 when the sizes are not covered.
 int launch_scan_mfma_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
-                          const void* V, float* M, uint16_t* M_lo, float* O_on, void* stream) {
-    if (d.dtype != MC_BF16 || !M_lo) return -1;
+                          const void* V, float* M, uint16_t* M_lo, float* O_on, void* stream,
+                          const float* M0) {
+    if (d.dtype != MC_BF16) return -1;  // (M_lo may be NULL: pieces of a split segment)
     hipStream_t st = (hipStream_t)stream;
     const SwlaGates none{};
 #define MC_SD(DK, DV)                                                                          \
     if (d.d_k == DK && d.d_v == DV)                                                            \
-        return launch_scan_mfma_t<DK, DV>(d, Q, K, V, M, M_lo, O_on, none, st, sg);
+        return launch_scan_mfma_t<DK, DV>(d, Q, K, V, M, M_lo, O_on, none, st, sg, M0);
     MC_SD(128, 128)
     MC_SD(128, 64)
     MC_SD(64, 128)

@@ -72,7 +72,8 @@ typedef enum {
     MC_OP_GRM = 1,
     MC_OP_SSC = 2,
     MC_OP_DECODE = 3,
-    MC_OP_GRM_BACKWARD = 4
+    MC_OP_GRM_BACKWARD = 4,
+    MC_OP_SCAN_SEGS = 5
 } mc_op;
 
 /* Problem sizes.  Supported in this build: d_k, d_v in {64, 128}; 1 <= d_g <= 256 and
@@ -95,7 +96,8 @@ int mc_abi_version(void);
 const char* mc_status_str(mc_status status);
 
 /* Workspace bytes an operation needs for these sizes (top_k is used by MC_OP_SSC, n_cap by
- * MC_OP_DECODE).  Returns 0 when no workspace is needed or the sizes are invalid. */
+ * MC_OP_DECODE; MC_OP_SCAN_SEGS, the segment-offset write path, takes the number of segments
+ * in top_k).  Returns 0 when no workspace is needed or the sizes are invalid. */
 size_t mc_workspace_bytes(const mc_dims* dims, mc_op op, int32_t top_k, int32_t n_cap);
 
 /*
@@ -199,7 +201,12 @@ mc_status mc_decode_step(const mc_dims* dims, const void* q, const void* k, cons
  *   The other arguments are those of mc_scan_prefill / mc_grm_readout with NS = n_seg, except
  *   that the read takes the online read O_on written by mc_scan_prefill_segs (required), not
  *   K and V; its workspace is mc_workspace_bytes(dims, MC_OP_GRM, 0, 0) bytes.
- *   Both run the fp32-accumulating kernels that take any segmentation.
+ *   The write path's workspace is mc_workspace_bytes(dims, MC_OP_SCAN_SEGS, n_seg, 0) bytes
+ *   (0 for fp32: NULL allowed): bf16 segments longer than a piece (512 tokens, or the
+ *   smallest power of two above it that keeps the pieces within MC_MAX_SEGS) are scanned as
+ *   pieces in parallel, whose states and prefix sums it holds.
+ *   bf16 inputs of width 64/128 run on MFMA (scan and read); the rest on the
+ *   fp32-accumulating kernels that take any segmentation.
  *   Errors as the constant-length calls; offsets that are not strictly increasing from 0 to L
  *   return MC_ERR_DIMS, more than MC_MAX_SEGS segments MC_ERR_UNSUPPORTED.
  */
@@ -207,7 +214,8 @@ mc_status mc_decode_step(const mc_dims* dims, const void* q, const void* k, cons
 
 mc_status mc_scan_prefill_segs(const mc_dims* dims, const int32_t* seg_off, int32_t n_seg,
                                const void* Q, const void* K, const void* V, const void* X,
-                               float* M, uint16_t* M_lo, float* P, float* O_on, void* stream);
+                               float* M, uint16_t* M_lo, float* P, float* O_on, void* ws,
+                               size_t ws_bytes, void* stream);
 
 mc_status mc_grm_readout_segs(const mc_dims* dims, const int32_t* seg_off, int32_t n_seg,
                               const void* Q, const void* U, const void* X, const float* M,

@@ -184,9 +184,11 @@ def test_segment_offsets_are_validated():
         off = np.ascontiguousarray(np.asarray(off, dtype=np.int32))
         p = dict(Q=A, K=A, V=A, X=A, M=A, M_lo=A, P=A, O_on=A)
         p.update(kw)
+        nb = mc.mc_workspace_bytes(d, mc.MC_OP_SCAN_SEGS, max(1, off.shape[0] - 1))
         return lib.mc_scan_prefill_segs(ctypes.byref(d), off.ctypes.data, off.shape[0] - 1,
                                         p["Q"], p["K"], p["V"], p["X"], p["M"], p["M_lo"],
-                                        p["P"], p["O_on"], None)
+                                        p["P"], p["O_on"], p.get("ws", A), p.get("wsb", nb),
+                                        None)
 
     def read(off, ws_bytes=ws, **kw):
         off = np.ascontiguousarray(np.asarray(off, dtype=np.int32))
@@ -202,8 +204,14 @@ def test_segment_offsets_are_validated():
     many = list(range(0, 1000, 1)) + [1000]  # 1000 segments > MC_MAX_SEGS
     assert scan(many) == mc.MC_ERR_UNSUPPORTED
     assert read(many) == mc.MC_ERR_UNSUPPORTED
-    assert lib.mc_scan_prefill_segs(ctypes.byref(d), None, 2, A, A, A, A, A, A, A, A,
+    assert lib.mc_scan_prefill_segs(ctypes.byref(d), None, 2, A, A, A, A, A, A, A, A, A, 0,
                                     None) == mc.MC_ERR_NULL
+    # bf16: long segments are scanned as pieces whose states take workspace
+    nb = mc.mc_workspace_bytes(d, mc.MC_OP_SCAN_SEGS, len(good) - 1)
+    assert nb >= 2 * 4 * d.B * d.H * (len(good) - 1 + 2) * d.d_v * d.d_k
+    assert scan(good, ws=None) == mc.MC_ERR_WORKSPACE
+    assert scan(good, wsb=nb - 1) == mc.MC_ERR_WORKSPACE
+    assert mc.mc_workspace_bytes(dims(L=1000, dtype="f32"), mc.MC_OP_SCAN_SEGS, 6) == 0
     assert scan(good, M_lo=None) == mc.MC_ERR_NULL        # bf16 writes the bf16 copy
     assert scan(good, X=MIS) == mc.MC_ERR_ALIGN
     assert read(good, O_on=None) == mc.MC_ERR_NULL        # the read takes the scan's O_on

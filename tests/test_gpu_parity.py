@@ -316,6 +316,11 @@ SEG_CASES = {
                                            "bf16"), "c64"),
     "bf16_max_512_segments_L1100": (Workload("x", 1, 2, 1100, 128, 128, 128, 1, "identity",
                                              "bf16"), "max"),
+    # segments longer than a scan piece (512 tokens): scanned as pieces, then combined
+    "bf16_long_segments_L2100": (Workload("x", 1, 2, 2100, 128, 128, 128, 1, "identity", "bf16"),
+                                 "long"),
+    "bf16_long_segments_d64_elu_xheadsH": (Workload("x", 1, 2, 1700, 64, 64, 64, 1, "elu1",
+                                                    "bf16", x_heads=2), "long"),
 }
 
 
@@ -329,6 +334,8 @@ def test_grm_segment_offsets(name):
         off = sorted(set(off + [off[1] + 1]))  # a one-token segment
     elif kind == "max":
         off = _random_offsets(w.L, mc.MC_MAX_SEGS, seed=6)  # the most segments a call takes
+    elif kind == "long":
+        off = [0, 1500, 1600, w.L]  # 3 pieces, 1 piece, 1 or 2 pieces
     else:
         off = list(range(0, w.L, 64)) + [w.L]
     announce("grm segment offsets %s: %d segments" % (name, len(off) - 1))
