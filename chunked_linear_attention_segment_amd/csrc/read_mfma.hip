@@ -460,8 +460,11 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
             }
         };
         // values of chunk kc, transposed into vt[kc & 1] = v^T [DV][64 keys]: lane holds keys
-        // 2 vp, 2 vp + 1 and DV/8 value columns from vdc; a row's 16-byte chunks (8 keys) are
-        // XOR-swizzled by (row % 8)
+        // 2 vp, 2 vp + 1 and DV/8 value columns from vdc.  A row's keys are stored in the MFMA's
+        // k order, so that an A fragment is one 16-byte read: 16-byte chunk 2 kk + h of a row
+        // holds keys 16 kk + 4 h + (0..3) and 16 kk + 8 + 4 h + (0..3).  A row is 128 bytes
+        // (half the banks), so chunks are XOR-swizzled by (row / 2) % 8: the reads of 16
+        // consecutive rows then cover every bank once
         constexpr int VCOLS = DV / 8;
         const int vp = tid % 32, vdc = (tid / 32) * VCOLS;
         ru32x4_t va[2][VCOLS / 8];
@@ -483,13 +486,13 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
             for (int g = 0; g < VCOLS / 8; ++g)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int c0 = vdc + g * 8 + 2 * e;  // value columns c0, c0 + 1
-                    const int kofs = 2 * (vp % 4);
-                    *reinterpret_cast<uint32_t*>(
-                        &vt[c0 * 64 + (((vp / 4) ^ (c0 & 7)) * 8) + kofs]) =
+                    const int c0 = vdc + g * 8 + 2 * e;  // value columns c0, c0 + 1 (c0 even)
+                    // keys 2 vp, 2 vp + 1: group vp / 8, chunk half h, position in the chunk
+                    const int r = vp % 8, h = (r >> 1) & 1, pos = 2 * (r & 1) + 4 * (r >> 2);
+                    const int pc = (((vp / 8) * 2 + h) ^ ((c0 >> 1) & 7)) * 8 + pos;
+                    *reinterpret_cast<uint32_t*>(&vt[c0 * 64 + pc]) =
                         (va[0][g][e] & 0xffffu) | (va[1][g][e] << 16);
-                    *reinterpret_cast<uint32_t*>(
-                        &vt[(c0 + 1) * 64 + (((vp / 4) ^ ((c0 + 1) & 7)) * 8) + kofs]) =
+                    *reinterpret_cast<uint32_t*>(&vt[(c0 + 1) * 64 + pc]) =
                         (va[0][g][e] >> 16) | (va[1][g][e] & 0xffff0000u);
                 }
         };
@@ -511,7 +514,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
                 // keys all after the block's tokens, or all before its earliest segment start
                 if (k0 > tlast[tb] || k0 + 63 < tseg0[tb]) continue;
                 const bool full = (k0 + 63 <= tfirst[tb]) && (k0 >= (tlast[tb] / C) * C);
-                // scores S^T = phi(K) phi(Q)^T; K fragments read one k-step ahead
+                // scores S^T = phi(K) phi(Q)^T; K fragments read two k-steps ahead
                 auto kfrag = [&](int ks, int rb) {
                     ru32x4_t ka = *reinterpret_cast<const ru32x4_t*>(
                         &kt[(rb * 32 + l32) * DK + (((2 * ks + hi32) ^ swz) * 8)]);
@@ -528,17 +531,19 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
                 for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sc[rb][r] = 0.f;
-                ru32x4_t kf[2][2];
+                ru32x4_t kf[3][2];
                 kf[0][0] = kfrag(0, 0);
                 kf[0][1] = kfrag(0, 1);
+                kf[1][0] = kfrag(1, 0);
+                kf[1][1] = kfrag(1, 1);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    if (ks + 1 < KS) {
-                        kf[(ks + 1) & 1][0] = kfrag(ks + 1, 0);
-                        kf[(ks + 1) & 1][1] = kfrag(ks + 1, 1);
+                    if (ks + 2 < KS) {
+                        kf[(ks + 2) % 3][0] = kfrag(ks + 2, 0);
+                        kf[(ks + 2) % 3][1] = kfrag(ks + 2, 1);
                     }
-                    sc[0] = mfma_bf16(kf[ks & 1][0], qb[tb][ks], sc[0]);
-                    sc[1] = mfma_bf16(kf[ks & 1][1], qb[tb][ks], sc[1]);
+                    sc[0] = mfma_bf16(kf[ks % 3][0], qb[tb][ks], sc[0]);
+                    sc[1] = mfma_bf16(kf[ks % 3][1], qb[tb][ks], sc[1]);
                 }
                 // mask to segment(t) start <= key <= t; key = k0 + 4*hi32 + (an immediate)
                 const int t = tok[tb];
@@ -566,21 +571,23 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
                             pack_bf16x2(sc[rb][8 * q + 4] * wo, sc[rb][8 * q + 5] * wo),
                             pack_bf16x2(sc[rb][8 * q + 6] * wo, sc[rb][8 * q + 7] * wo)};
                     }
-                // acc += v^T S^T; v^T fragments read one step ahead
+                // acc += v^T S^T: consecutive MFMAs go to different value blocks (independent
+                // accumulators), v^T fragments read three MFMAs ahead.  Fragment n = (k-step kk,
+                // value block cb) is chunk 2 kk + hi32 of its row
+                constexpr int NV = CB * 4;
                 auto vfrag = [&](int n) {
-                    const int c = (n / 4) * 32 + l32, kk = n % 4;
-                    const uint2 lo = *reinterpret_cast<const uint2*>(
-                        &vt[c * 64 + (((2 * kk) ^ (c & 7)) * 8) + 4 * hi32]);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(
-                        &vt[c * 64 + (((2 * kk + 1) ^ (c & 7)) * 8) + 4 * hi32]);
-                    return ru32x4_t{lo.x, lo.y, hi.x, hi.y};
+                    const int c = (n % CB) * 32 + l32, kk = n / CB;
+                    return *reinterpret_cast<const ru32x4_t*>(
+                        &vt[c * 64 + (((2 * kk + hi32) ^ ((c >> 1) & 7)) * 8)]);
                 };
-                ru32x4_t vf[2];
+                ru32x4_t vf[4];
                 vf[0] = vfrag(0);
+                vf[1] = vfrag(1);
+                vf[2] = vfrag(2);
 #pragma unroll
-                for (int n = 0; n < CB * 4; ++n) {
-                    if (n + 1 < CB * 4) vf[(n + 1) & 1] = vfrag(n + 1);
-                    acc[n / 4][tb] = mfma_bf16(vf[n & 1], sb[n % 4], acc[n / 4][tb]);
+                for (int n = 0; n < NV; ++n) {
+                    if (n + 3 < NV) vf[(n + 3) % 4] = vfrag(n + 3);
+                    acc[n % CB][tb] = mfma_bf16(vf[n % 4], sb[n / CB], acc[n % CB][tb]);
                 }
             }
             if (kc + 1 < nkc) store_v(kc + 1);  // its buffer was last read in chunk kc - 1
