@@ -201,11 +201,29 @@ __device__ __forceinline__ bool piece_first(const PieceArg& pa, int j) {
     return (pa.first[j >> 5] >> (j & 31)) & 1u;
 }
 
+// Index of the segment that starts at piece j (a segment's first piece), and one past its last
+// piece.
+__device__ __forceinline__ int piece_segment(const PieceArg& pa, int j) {
+    int seg = -1;  // segments started up to piece j
+    for (int w = 0; w <= (j >> 5); ++w) {
+        uint32_t bits = pa.first[w];
+        if (w == (j >> 5) && (j & 31) != 31) bits &= (2u << (j & 31)) - 1u;
+        seg += __popc(bits);
+    }
+    return seg;
+}
+__device__ __forceinline__ int piece_end(const PieceArg& pa, int j, int NP) {
+    int e = j + 1;
+    while (e < NP && !piece_first(pa, e)) ++e;
+    return e;
+}
+
 // Prefix sums of the piece states inside each segment: the memory restarts only at a
 // segment start (Eq. 4b), so the memory before piece j is the sum of the earlier pieces of
 // its segment (Pref_j, zero for a segment's first piece) and the segment's state is the sum
 // of all of them.  One workgroup per (segment's first piece j, b*H+h, 1024-element slice of
-// the d_v x d_k state) walks the segment's pieces in order; workgroups of other pieces exit.
+// the d_v x d_k state) walks the segment's pieces in order, loading eight pieces at a time;
+// workgroups of other pieces exit.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void piece_prefix_kernel(const float* __restrict__ Msub,
                                                            int NP, const PieceArg pa, int NS,
@@ -213,34 +231,54 @@ __global__ __launch_bounds__(256) void piece_prefix_kernel(const float* __restri
                                                            float* __restrict__ M,
                                                            bf16_t* __restrict__ M_lo) {
     constexpr int N = DV * DK;
+    constexpr int BATCH = 8;
     const int j = blockIdx.x;
     if (!piece_first(pa, j)) return;  // uniform
     const size_t bh = blockIdx.y;
-    const int e0 = blockIdx.z * 1024 + threadIdx.x;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    int jj = j;
-    do {
-        const float* src = Msub + (bh * NP + jj) * (size_t)N;
-        float* dst = Pref + (bh * NP + jj) * (size_t)N;
+    const int e0 = blockIdx.z * 1024 + 4 * threadIdx.x;
+    const int jend = piece_end(pa, j, NP);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int b = j; b < jend; b += BATCH) {
+        float4 v[BATCH];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            dst[e0 + 256 * k] = acc[k];
-            acc[k] += src[e0 + 256 * k];
-        }
-        ++jj;
-    } while (jj < NP && !piece_first(pa, jj));
-    int seg = -1;  // segments started up to piece j
-    for (int w = 0; w <= (j >> 5); ++w) {
-        uint32_t bits = pa.first[w];
-        if (w == (j >> 5) && (j & 31) != 31) bits &= (2u << (j & 31)) - 1u;
-        seg += __popc(bits);
+        for (int i = 0; i < BATCH; ++i)
+            if (b + i < jend)
+                v[i] = *reinterpret_cast<const float4*>(Msub + (bh * NP + b + i) * (size_t)N + e0);
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i)
+            if (b + i < jend) {
+                *reinterpret_cast<float4*>(Pref + (bh * NP + b + i) * (size_t)N + e0) = acc;
+                acc.x += v[i].x;
+                acc.y += v[i].y;
+                acc.z += v[i].z;
+                acc.w += v[i].w;
+            }
     }
-    float* m = M + (bh * NS + seg) * (size_t)N;
-    bf16_t* ml = M_lo + (bh * NS + seg) * (size_t)N;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        m[e0 + 256 * k] = acc[k];
-        ml[e0 + 256 * k] = f32_to_bf16(acc[k]);
+    const int seg = piece_segment(pa, j);
+    *reinterpret_cast<float4*>(M + (bh * NS + seg) * (size_t)N + e0) = acc;
+    uint2 lo;
+    lo.x = pack_bf16x2(acc.x, acc.y);
+    lo.y = pack_bf16x2(acc.z, acc.w);
+    *reinterpret_cast<uint2*>(M_lo + (bh * NS + seg) * (size_t)N + e0) = lo;
+}
+
+// Segment means from the means of its pieces (P_s = sum over the segment's pieces, in order, of
+// length x mean, over the segment's length).  One workgroup per (segment's first piece,
+// b*x_heads); workgroups of other pieces exit.
+__global__ __launch_bounds__(256) void piece_means_kernel(const float* __restrict__ Pm, int NP,
+                                                          const PieceArg pa, int NS, int DG,
+                                                          float* __restrict__ P) {
+    const int j = blockIdx.x;
+    if (!piece_first(pa, j)) return;  // uniform
+    const size_t bx = blockIdx.y;
+    const int jend = piece_end(pa, j, NP);
+    const int seg = piece_segment(pa, j);
+    const float inv_len = 1.f / (float)(pa.sg.off[jend] - pa.sg.off[j]);
+    for (int e = threadIdx.x; e < DG; e += 256) {
+        float acc = 0.f;
+        for (int q = j; q < jend; ++q)
+            acc += Pm[(bx * NP + q) * DG + e] * (float)(pa.sg.off[q + 1] - pa.sg.off[q]);
+        P[(bx * NS + seg) * DG + e] = acc * inv_len;
     }
 }
 
@@ -250,21 +288,26 @@ int scan_piece_len(int L, int n_seg) {
     return 0;
 }
 
-// two fp32 state arrays (pieces, prefix sums) for at most n_seg + ceil(L / piece) pieces;
-// only the bf16 MFMA scan splits segments
+// two fp32 state arrays (pieces, prefix sums) and the pieces' means of X, for at most
+// n_seg + ceil(L / piece) pieces; only the bf16 MFMA scan splits segments
+static size_t segs_state_bytes(const mc_dims& d, size_t np) {
+    return align256(sizeof(float) * (size_t)d.B * d.H * np * d.d_v * d.d_k);
+}
 size_t segs_scan_ws_bytes(const mc_dims& d, int n_seg) {
     const bool mfma = d.dtype == MC_BF16 && (d.d_k == 64 || d.d_k == 128) &&
                       (d.d_v == 64 || d.d_v == 128);
     const int pl = scan_piece_len(d.L, n_seg);
     if (!mfma || !pl) return 0;
     const size_t np = (size_t)n_seg + (d.L + pl - 1) / pl;
-    return 2 * align256(sizeof(float) * (size_t)d.B * d.H * np * d.d_v * d.d_k);
+    return 2 * segs_state_bytes(d, np) +
+           align256(sizeof(float) * (size_t)d.B * d.x_heads * np * d.d_g);
 }
 
 template <int DK, int DV>
 static int launch_pieces_t(const mc_dims& d, const PieceArg& pa, int NS, float* Msub,
                            float* Pref, float* M, uint16_t* M_lo, hipStream_t st) {
     const int NP = pa.sg.n;
+    static_assert(DV * DK % 1024 == 0, "1024-element slices");
     hipLaunchKernelGGL((piece_prefix_kernel<DK, DV>), dim3(NP, d.B * d.H, DV * DK / 1024),
                        dim3(256), 0, st, Msub, NP, pa, NS, Pref, M, (bf16_t*)M_lo);
     return (int)hipGetLastError();
@@ -272,7 +315,7 @@ static int launch_pieces_t(const mc_dims& d, const PieceArg& pa, int NS, float* 
 
 // Arbitrary boundaries: the MFMA scan for bf16 widths 64/128 (segments longer than a piece
 // split into pieces scanned in parallel, then combined), else the generic scan (any dtype);
-// then the means over each segment.
+// then the means over each segment (split: over the pieces, then combined per segment).
 int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
                              const void* V, const void* X, float* M, uint16_t* M_lo, float* P,
                              float* O_on, void* ws, size_t ws_bytes, void* stream) {
@@ -282,8 +325,9 @@ int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, 
     bool split = false;
     for (int i = 0; pl && i < sg.n; ++i) split |= sg.off[i + 1] - sg.off[i] > pl;
     const size_t need = segs_scan_ws_bytes(d, sg.n);
+    PieceArg piece{};
+    float* Pm = nullptr;  // the pieces' means of X, when the scan ran over pieces
     if (split && need && ws && ws_bytes >= need) {
-        PieceArg piece{};
         int np = 0;
         for (int i = 0; i < sg.n; ++i)
             for (int a = sg.off[i]; a < sg.off[i + 1]; a += pl) {
@@ -294,8 +338,9 @@ int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, 
         piece.sg.n = np;
         // the pieces' own states; their prefix sums per segment (and the segments' states);
         // then, for the online read, the pieces again from the memory before each
+        const size_t sb = segs_state_bytes(d, (size_t)sg.n + (d.L + pl - 1) / pl);
         float* Msub = (float*)ws;
-        float* Pref = (float*)((char*)ws + need / 2);
+        float* Pref = (float*)((char*)ws + sb);
         rc = launch_scan_mfma_segs(d, piece.sg, Q, K, V, Msub, nullptr, nullptr, stream);
         if (rc >= 0) {
             if (rc) return rc;
@@ -310,6 +355,7 @@ int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, 
             if (!rc && O_on)
                 rc = launch_scan_mfma_segs(d, piece.sg, Q, K, V, nullptr, nullptr, O_on, stream,
                                            Pref);
+            if (!rc) Pm = (float*)((char*)ws + 2 * sb);
         }
     }
     if (rc < 0) rc = launch_scan_mfma_segs(d, sg, Q, K, V, M, M_lo, O_on, stream);
@@ -317,6 +363,12 @@ int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, 
         rc = d.dtype == MC_BF16 ? launch_scan_dt<bf16_t>(d, Q, K, V, M, M_lo, O_on, sg, st)
                                 : launch_scan_dt<float>(d, Q, K, V, M, M_lo, O_on, sg, st);
     if (rc) return rc;
+    if (Pm) {  // bf16 (the pieced scan is the MFMA one)
+        if ((rc = launch_means<bf16_t>(d, X, Pm, piece.sg, st))) return rc;
+        hipLaunchKernelGGL(piece_means_kernel, dim3(piece.sg.n, d.B * d.x_heads), dim3(256), 0,
+                           st, Pm, piece.sg.n, piece, sg.n, d.d_g, P);
+        return (int)hipGetLastError();
+    }
     return d.dtype == MC_BF16 ? launch_means<bf16_t>(d, X, P, sg, st)
                               : launch_means<float>(d, X, P, sg, st);
 }

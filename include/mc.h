@@ -204,7 +204,8 @@ mc_status mc_decode_step(const mc_dims* dims, const void* q, const void* k, cons
  *   The write path's workspace is mc_workspace_bytes(dims, MC_OP_SCAN_SEGS, n_seg, 0) bytes
  *   (0 for fp32: NULL allowed): bf16 segments longer than a piece (512 tokens, or the
  *   smallest power of two above it that keeps the pieces within MC_MAX_SEGS) are scanned as
- *   pieces in parallel, whose states and prefix sums it holds.
+ *   pieces in parallel, whose states and prefix sums it holds, with the pieces' means of X
+ *   (a segment's mean is then combined from its pieces' in order).
  *   bf16 inputs of width 64/128 run on MFMA (scan and read); the rest on the
  *   fp32-accumulating kernels that take any segmentation.
  *   Errors as the constant-length calls; offsets that are not strictly increasing from 0 to L
