@@ -65,8 +65,10 @@ __device__ __forceinline__ u32x2_t phi4(u32x2_t v, int phi) {
 constexpr int CH = 64;    // tokens per chunk
 constexpr int TPAD = 72;  // row stride (elements) of the token-indexed LDS tiles
 
+// (SWLA: held to 256 registers, two waves per SIMD, so one workgroup's memory waits are
+// covered by another's work)
 template <int DK, int DV, bool ON, bool SW>
-__global__ __launch_bounds__(DV * 2, 1) void scan_mfma_kernel(
+__global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     int L, int C, int NS, int phi, float* __restrict__ M, bf16_t* __restrict__ M_lo,
     float* __restrict__ O_on, SwlaGates gt, const SegArg sg, const float* __restrict__ M0) {
