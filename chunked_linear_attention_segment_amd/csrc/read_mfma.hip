@@ -33,7 +33,7 @@
 //      (the file is compiled without the machine schedulers): A fragments are read from LDS
 //      two k-steps ahead, and every MFMA is followed by the three VALU ops that build a
 //      quarter of a B fragment of the next k-step, which the matrix unit hides;
-//   4. y = acc / l_t, stored in bf16.
+//   4. y = acc / l_t in bf16 (with the gate pass: staged through LDS into whole-row stores).
 #include "common.cuh"
 #include "mc_internal.h"
 
@@ -738,19 +738,54 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     }
 
     // =============================== 4. y = acc / l =========================================
+    if constexpr (PRE) {
+        // staged through region A (free once every wave is past its last state) so that the
+        // stores write whole rows: token row r of the tile at r * DV, its 16-byte chunk c at
+        // c ^ (r % NCH), which keeps the lanes' writes (32 rows, one chunk) on distinct banks.
+        // (The kernels that form the gate themselves hold more registers here and store
+        // directly.)
+        constexpr int NCH = DV / 8;  // 16-byte chunks per row of y
+        static_assert(RT * DV * sizeof(bf16_t) <= sizeof(sm.a), "y tile fits region A");
+        bf16_t* ys = reinterpret_cast<bf16_t*>(&sm.a);
+        __syncthreads();
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        if (!val[tb]) continue;
-        const float il = PRE ? l[tb] : 1.f / (l[tb] + won[tb]);
+        for (int tb = 0; tb < TB; ++tb) {
+            const int r = tl[tb];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            bf16_t* yr = Y + ((size_t)bh * L + tok[tb]) * DV + cb * 32 + hi32 * 4;
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint2 v;
-                v.x = pack_bf16x2(acc[cb][tb][4 * g + 0] * il, acc[cb][tb][4 * g + 1] * il);
-                v.y = pack_bf16x2(acc[cb][tb][4 * g + 2] * il, acc[cb][tb][4 * g + 3] * il);
-                *reinterpret_cast<uint2*>(yr + g * 8) = v;
+                for (int g = 0; g < 4; ++g) {
+                    uint2 v;
+                    v.x = pack_bf16x2(acc[cb][tb][4 * g + 0] * l[tb], acc[cb][tb][4 * g + 1] * l[tb]);
+                    v.y = pack_bf16x2(acc[cb][tb][4 * g + 2] * l[tb], acc[cb][tb][4 * g + 3] * l[tb]);
+                    const int c = (cb * 4 + g) ^ (r % NCH);
+                    *reinterpret_cast<uint2*>(&ys[r * DV + c * 8 + hi32 * 4]) = v;
+                }
+        }
+        __syncthreads();
+        const int nrow = last - tile0 + 1;  // rows of the tile inside the sequence
+#pragma unroll
+        for (int it = 0; it < RT * NCH / RTHREADS; ++it) {
+            const int idx = it * RTHREADS + tid, r = idx / NCH, c = idx % NCH;
+            if (r < nrow)
+                *reinterpret_cast<uint4*>(Y + ((size_t)bh * L + tile0 + r) * DV + c * 8) =
+                    *reinterpret_cast<const uint4*>(&ys[r * DV + ((c ^ (r % NCH)) * 8)]);
+        }
+    } else {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            if (!val[tb]) continue;
+            const float il = 1.f / (l[tb] + won[tb]);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                bf16_t* yr = Y + ((size_t)bh * L + tok[tb]) * DV + cb * 32 + hi32 * 4;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    uint2 v;
+                    v.x = pack_bf16x2(acc[cb][tb][4 * g + 0] * il, acc[cb][tb][4 * g + 1] * il);
+                    v.y = pack_bf16x2(acc[cb][tb][4 * g + 2] * il, acc[cb][tb][4 * g + 3] * il);
+                    *reinterpret_cast<uint2*>(yr + g * 8) = v;
+                }
             }
         }
     }
