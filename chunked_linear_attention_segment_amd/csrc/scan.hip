@@ -201,16 +201,18 @@ __device__ __forceinline__ bool piece_first(const PieceArg& pa, int j) {
     return (pa.first[j >> 5] >> (j & 31)) & 1u;
 }
 
-// Index of the segment that starts at piece j (a segment's first piece), and one past its last
-// piece.
-__device__ __forceinline__ int piece_segment(const PieceArg& pa, int j) {
-    int seg = -1;  // segments started up to piece j
-    for (int w = 0; w <= (j >> 5); ++w) {
+// The first piece of segment s (the (s+1)-th set bit of the first-piece table), and one past
+// the last piece of the segment that starts at piece j.
+__device__ __forceinline__ int segment_first_piece(const PieceArg& pa, int s) {
+    for (int w = 0;; ++w) {
         uint32_t bits = pa.first[w];
-        if (w == (j >> 5) && (j & 31) != 31) bits &= (2u << (j & 31)) - 1u;
-        seg += __popc(bits);
+        const int c = __popc(bits);
+        if (s < c) {
+            for (; s > 0; --s) bits &= bits - 1u;  // drop the lower set bits
+            return 32 * w + __ffs(bits) - 1;
+        }
+        s -= c;
     }
-    return seg;
 }
 __device__ __forceinline__ int piece_end(const PieceArg& pa, int j, int NP) {
     int e = j + 1;
@@ -221,9 +223,8 @@ __device__ __forceinline__ int piece_end(const PieceArg& pa, int j, int NP) {
 // Prefix sums of the piece states inside each segment: the memory restarts only at a
 // segment start (Eq. 4b), so the memory before piece j is the sum of the earlier pieces of
 // its segment (Pref_j, zero for a segment's first piece) and the segment's state is the sum
-// of all of them.  One workgroup per (segment's first piece j, b*H+h, 1024-element slice of
-// the d_v x d_k state) walks the segment's pieces in order, loading eight pieces at a time;
-// workgroups of other pieces exit.
+// of all of them.  One workgroup per (segment, b*H+h, 1024-element slice of the d_v x d_k
+// state) walks the segment's pieces in order, loading eight pieces at a time.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void piece_prefix_kernel(const float* __restrict__ Msub,
                                                            int NP, const PieceArg pa, int NS,
@@ -232,8 +233,8 @@ __global__ __launch_bounds__(256) void piece_prefix_kernel(const float* __restri
                                                            bf16_t* __restrict__ M_lo) {
     constexpr int N = DV * DK;
     constexpr int BATCH = 8;
-    const int j = blockIdx.x;
-    if (!piece_first(pa, j)) return;  // uniform
+    const int seg = blockIdx.x;
+    const int j = segment_first_piece(pa, seg);
     const size_t bh = blockIdx.y;
     const int e0 = blockIdx.z * 1024 + 4 * threadIdx.x;
     const int jend = piece_end(pa, j, NP);
@@ -254,7 +255,6 @@ __global__ __launch_bounds__(256) void piece_prefix_kernel(const float* __restri
                 acc.w += v[i].w;
             }
     }
-    const int seg = piece_segment(pa, j);
     *reinterpret_cast<float4*>(M + (bh * NS + seg) * (size_t)N + e0) = acc;
     uint2 lo;
     lo.x = pack_bf16x2(acc.x, acc.y);
@@ -263,16 +263,14 @@ __global__ __launch_bounds__(256) void piece_prefix_kernel(const float* __restri
 }
 
 // Segment means from the means of its pieces (P_s = sum over the segment's pieces, in order, of
-// length x mean, over the segment's length).  One workgroup per (segment's first piece,
-// b*x_heads); workgroups of other pieces exit.
+// length x mean, over the segment's length).  One workgroup per (segment, b*x_heads).
 __global__ __launch_bounds__(256) void piece_means_kernel(const float* __restrict__ Pm, int NP,
                                                           const PieceArg pa, int NS, int DG,
                                                           float* __restrict__ P) {
-    const int j = blockIdx.x;
-    if (!piece_first(pa, j)) return;  // uniform
+    const int seg = blockIdx.x;
+    const int j = segment_first_piece(pa, seg);
     const size_t bx = blockIdx.y;
     const int jend = piece_end(pa, j, NP);
-    const int seg = piece_segment(pa, j);
     const float inv_len = 1.f / (float)(pa.sg.off[jend] - pa.sg.off[j]);
     for (int e = threadIdx.x; e < DG; e += 256) {
         float acc = 0.f;
@@ -308,7 +306,7 @@ static int launch_pieces_t(const mc_dims& d, const PieceArg& pa, int NS, float* 
                            float* Pref, float* M, uint16_t* M_lo, hipStream_t st) {
     const int NP = pa.sg.n;
     static_assert(DV * DK % 1024 == 0, "1024-element slices");
-    hipLaunchKernelGGL((piece_prefix_kernel<DK, DV>), dim3(NP, d.B * d.H, DV * DK / 1024),
+    hipLaunchKernelGGL((piece_prefix_kernel<DK, DV>), dim3(NS, d.B * d.H, DV * DK / 1024),
                        dim3(256), 0, st, Msub, NP, pa, NS, Pref, M, (bf16_t*)M_lo);
     return (int)hipGetLastError();
 }
@@ -365,7 +363,7 @@ int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, 
     if (rc) return rc;
     if (Pm) {  // bf16 (the pieced scan is the MFMA one)
         if ((rc = launch_means<bf16_t>(d, X, Pm, piece.sg, st))) return rc;
-        hipLaunchKernelGGL(piece_means_kernel, dim3(piece.sg.n, d.B * d.x_heads), dim3(256), 0,
+        hipLaunchKernelGGL(piece_means_kernel, dim3(sg.n, d.B * d.x_heads), dim3(256), 0,
                            st, Pm, piece.sg.n, piece, sg.n, d.d_g, P);
         return (int)hipGetLastError();
     }
