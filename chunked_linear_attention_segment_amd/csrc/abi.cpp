@@ -135,7 +135,7 @@ const char* mc_status_str(mc_status s) {
         case MC_OK: return "ok";
         case MC_ERR_NULL: return "a required pointer is NULL";
         case MC_ERR_DIMS: return "invalid or inconsistent sizes";
-        case MC_ERR_UNSUPPORTED: return "sizes or types not supported by this build";
+        case MC_ERR_UNSUPPORTED: return "sizes or types not supported by this library";
         case MC_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case MC_ERR_WORKSPACE: return "workspace too small";
         case MC_ERR_HIP: return "HIP launch failed";

@@ -58,7 +58,7 @@ typedef enum {
     MC_OK = 0,
     MC_ERR_NULL = 1,        /* a required pointer is NULL                                 */
     MC_ERR_DIMS = 2,        /* a size is non-positive or inconsistent                     */
-    MC_ERR_UNSUPPORTED = 3, /* valid, but outside what this build implements              */
+    MC_ERR_UNSUPPORTED = 3, /* valid, but outside what this library implements            */
     MC_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                           */
     MC_ERR_WORKSPACE = 5,   /* ws_bytes < mc_workspace_bytes()                            */
     MC_ERR_HIP = 6,         /* a HIP launch failed                                        */
@@ -76,7 +76,7 @@ typedef enum {
     MC_OP_SCAN_SEGS = 5
 } mc_op;
 
-/* Problem sizes.  Supported in this build: d_k, d_v in {64, 128}; 1 <= d_g <= 256 and
+/* Problem sizes.  Supported by this library: d_k, d_v in {64, 128}; 1 <= d_g <= 256 and
  * d_g % 8 == 0; C >= 1; x_heads in {1, H}; dtype MC_F32 or MC_BF16.                      */
 typedef struct mc_dims {
     int32_t B, H;       /* sequences, heads                                                 */
