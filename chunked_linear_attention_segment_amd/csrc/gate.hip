@@ -18,6 +18,8 @@
 // bits; laid out as MFMA fragments once, by pfrag_kernel, for every workgroup to share through
 // the caches), u_t exact in bf16, fp32 accumulation.  Pass 1 takes m_t over every logit, pass 2 writes the
 // numerators, transposed through LDS into 16-byte stores of whole rows.
+#include <type_traits>
+
 #include "common.cuh"
 #include "mc_internal.h"
 
@@ -143,8 +145,11 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
         // logits^T of states i0 .. i0+31 (rows; A = the means' high and remainder fragments)
         // x the wave's 32 tokens.  Accumulator element r is state i0 + 8 (r / 4) + 4 hi32 +
         // r % 4; a state counts for token t when it is a completed segment before t's, others
-        // get -inf.
-        auto logits = [&](int i0) {
+        // get -inf.  Where the fragments come from is a compile-time argument: with both
+        // sources in one loop the compiler waits for every load and store in flight (the next
+        // head's u, the numerators' stores) before each MFMA.
+        auto logits = [&](int i0, auto from_lds) {
+            constexpr bool FL = decltype(from_lds)::value;
             gf32x16_t lg;
 #pragma unroll
             for (int r = 0; r < 16; ++r) lg[r] = 0.f;
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
             for (int kc = 0; kc < GDG_MAX / 16; ++kc) {
                 if (kc >= KC) break;
                 gu32x4_t ah, al;
-                if (lds_pf) {
+                if constexpr (FL) {
                     ah = __builtin_bit_cast(gu32x4_t, pfl[f0 + kc * 128]);
                     al = __builtin_bit_cast(gu32x4_t, pfl[f0 + kc * 128 + 64]);
                 } else {
@@ -169,10 +174,11 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
                 if (!(8 * (r / 4) + (r % 4) < lim)) lg[r] = -INFINITY;
             return lg;
         };
+        auto passes = [&](auto from_lds) {
         // pass 1: m_t over every logit
         float m = a_on;
         for (int i0 = 0; i0 < s_hi; i0 += 32) {
-            const gf32x16_t lg = logits(i0);
+            const gf32x16_t lg = logits(i0, from_lds);
             float bm = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 16; ++r) bm = fmaxf(bm, lg[r]);
@@ -182,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
         // stores of whole rows
         float l = 0.f;
         for (int i0 = 0; i0 < s_hi; i0 += 32) {
-            const gf32x16_t lg = logits(i0);
+            const gf32x16_t lg = logits(i0, from_lds);
             float ps = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -207,6 +213,11 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
             won_out[(size_t)bh * L + tok] = wo;
             inv_l_out[(size_t)bh * L + tok] = 1.f / (l + wo);
         }
+        };
+        if (lds_pf)
+            passes(std::true_type{});
+        else
+            passes(std::false_type{});
     }
 }
 
