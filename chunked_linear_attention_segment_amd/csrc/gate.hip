@@ -150,24 +150,32 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
         // head's u, the numerators' stores) before each MFMA.
         auto logits = [&](int i0, auto from_lds) {
             constexpr bool FL = decltype(from_lds)::value;
-            gf32x16_t lg;
+            // the high and remainder parts accumulate separately (two independent MFMA
+            // chains), and each k-step's fragments are read one step ahead
+            gf32x16_t lg, lr;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) lg[r] = 0.f;
+            for (int r = 0; r < 16; ++r) lg[r] = lr[r] = 0.f;
             const size_t f0 = (size_t)(i0 / 32) * KC * 2 * 64 + lane;
+            auto frag = [&](int kc, gu32x4_t& h, gu32x4_t& r) {
+                if constexpr (FL) {
+                    h = __builtin_bit_cast(gu32x4_t, pfl[f0 + kc * 128]);
+                    r = __builtin_bit_cast(gu32x4_t, pfl[f0 + kc * 128 + 64]);
+                } else {
+                    h = __builtin_bit_cast(gu32x4_t, Pfb[f0 + kc * 128]);
+                    r = __builtin_bit_cast(gu32x4_t, Pfb[f0 + kc * 128 + 64]);
+                }
+            };
+            gu32x4_t fh[2], fr[2];
+            frag(0, fh[0], fr[0]);
 #pragma unroll
             for (int kc = 0; kc < GDG_MAX / 16; ++kc) {
                 if (kc >= KC) break;
-                gu32x4_t ah, al;
-                if constexpr (FL) {
-                    ah = __builtin_bit_cast(gu32x4_t, pfl[f0 + kc * 128]);
-                    al = __builtin_bit_cast(gu32x4_t, pfl[f0 + kc * 128 + 64]);
-                } else {
-                    ah = __builtin_bit_cast(gu32x4_t, Pfb[f0 + kc * 128]);
-                    al = __builtin_bit_cast(gu32x4_t, Pfb[f0 + kc * 128 + 64]);
-                }
-                lg = mfma_gate(ah, ub[kc], lg);
-                lg = mfma_gate(al, ub[kc], lg);
+                if (kc + 1 < KC) frag(kc + 1, fh[(kc + 1) & 1], fr[(kc + 1) & 1]);
+                lg = mfma_gate(fh[kc & 1], ub[kc], lg);
+                lr = mfma_gate(fr[kc & 1], ub[kc], lr);
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lg[r] += lr[r];
             const int lim = seg - i0 - 4 * hi32;
 #pragma unroll
             for (int r = 0; r < 16; ++r)
