@@ -34,6 +34,8 @@
 //      two k-steps ahead, and every MFMA is followed by the three VALU ops that build a
 //      quarter of a B fragment of the next k-step, which the matrix unit hides;
 //   4. y = acc / l_t in bf16 (with the gate pass: staged through LDS into whole-row stores).
+#include <type_traits>
+
 #include "common.cuh"
 #include "mc_internal.h"
 
@@ -224,8 +226,11 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
         }
     };
     // logits^T of 32 states (rows) x the lane's tokens (columns): rows from the staging area
-    // (row0 = the block's first row there) or, when from_lds is false, from P directly
-    auto logits = [&](int i0, int row0, bool from_lds, rf32x16_t (&lg)[TB]) {
+    // (row0 = the block's first row there) or, when from_lds is false, from P directly.  The
+    // source is a compile-time argument: with both in one loop the compiler would wait for every
+    // load in flight before each MFMA.
+    auto logits = [&](int i0, int row0, auto from_lds_c, rf32x16_t (&lg)[TB]) {
+        constexpr bool from_lds = decltype(from_lds_c)::value;
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
             if (kc >= DG / 16) break;
             float pv[8];
             const int c0 = kc * 4 + hi32 * 2;
-            if (from_lds) {
+            if constexpr (from_lds) {
                 const float* pr = &sm.a.pm[(row0 + l32) * DG];
                 const float4 a0 = *reinterpret_cast<const float4*>(pr + ((c0 ^ sw) * 4));
                 const float4 a1 = *reinterpret_cast<const float4*>(pr + (((c0 + 1) ^ sw) * 4));
@@ -297,7 +302,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     for (int b = 0; b < NBLK; ++b)
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) mb[b][tb] = 0.f;
-    auto weights = [&](int sb0, bool from_lds, bool running) {
+    auto weights = [&](int sb0, auto from_lds, bool running) {
         const int n = min(SBS, s_hi - sb0);
 #pragma unroll
         for (int bi = 0; bi < NBLK; ++bi) {
@@ -376,7 +381,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
             wait_all_and_barrier();
             for (int b0 = 0; b0 < n; b0 += 32) {
                 rf32x16_t lg[TB];
-                logits(sb0 + b0, b0, true, lg);
+                logits(sb0 + b0, b0, std::true_type{}, lg);
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
                     float bm = -INFINITY;
@@ -390,11 +395,11 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
         __syncthreads();
         stage_means(0, SBS);
         wait_all_and_barrier();
-        weights(0, true, false);
+        weights(0, std::true_type{}, false);
     } else if (s_hi > 0) {
         stage_means(0, s_hi);
         wait_all_and_barrier();
-        weights(0, true, true);
+        weights(0, std::true_type{}, true);
     }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) won[tb] = __expf(a_on[tb] - m[tb]);
@@ -678,7 +683,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
                 }
                 load_u();
                 __syncthreads();
-                weights(i, false, false);
+                weights(i, std::false_type{}, false);
                 __syncthreads();
             }
         }
