@@ -252,12 +252,23 @@ __global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
             f32x16_t sacc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+            // key fragments loaded two k-steps ahead, unconditionally (kr is a valid row), and
+            // zeroed past the chunk at their use: a conditional load used at once made the
+            // compiler wait for every load and store in flight before each MFMA
+            u32x2_t kl[3], kh[3];
+            auto kload = [&](int ks) {
+                kl[ks % 3] = *reinterpret_cast<const u32x2_t*>(kr + ks * 16);
+                kh[ks % 3] = *reinterpret_cast<const u32x2_t*>(kr + ks * 16 + 8);
+            };
+            kload(0);
+            if (KSD > 1) kload(1);
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
+                if (ks + 2 < KSD) kload(ks + 2);
                 u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
                 if (ok) {
-                    lo = phi4(*reinterpret_cast<const u32x2_t*>(kr + ks * 16), phi);
-                    hi = phi4(*reinterpret_cast<const u32x2_t*>(kr + ks * 16 + 8), phi);
+                    lo = phi4(kl[ks % 3], phi);
+                    hi = phi4(kh[ks % 3], phi);
                 }
                 sacc = scan_mfma(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, tb ? qb[1][ks] : qb[0][ks],
                                  sacc);
