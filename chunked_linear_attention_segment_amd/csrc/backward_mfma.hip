@@ -43,19 +43,20 @@ __device__ __forceinline__ u32x4_t phi8(u32x4_t v, int phi) {
     return o;
 }
 
-// M [BH*NS][DV][DK] fp32 -> MT [BH*NS][DK][DV] bf16, 32 x 32 tiles through LDS.
-__global__ __launch_bounds__(256) void transpose_states_kernel(const float* __restrict__ M,
+// M_lo [BH*NS][DV][DK] bf16 -> MT [BH*NS][DK][DV] bf16, 32 x 32 tiles through LDS.  The
+// values are the bf16 states themselves (no rounding here), so the bf16 call reads M_lo only.
+__global__ __launch_bounds__(256) void transpose_states_kernel(const bf16_t* __restrict__ M_lo,
                                                                int DV, int DK,
                                                                bf16_t* __restrict__ MT) {
-    __shared__ float tile[32][33];
+    __shared__ bf16_t tile[32][34];
     const size_t st = blockIdx.x;
     const int r0 = blockIdx.y * 32, c0 = blockIdx.z * 32;
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-    const float* src = M + st * (size_t)DV * DK;
+    const bf16_t* src = M_lo + st * (size_t)DV * DK;
     bf16_t* dst = MT + st * (size_t)DV * DK;
     for (int y = ty; y < 32; y += 8) tile[y][tx] = src[(size_t)(c0 + y) * DK + r0 + tx];
     __syncthreads();
-    for (int y = ty; y < 32; y += 8) dst[(size_t)(r0 + y) * DV + c0 + tx] = f32_to_bf16(tile[tx][y]);
+    for (int y = ty; y < 32; y += 8) dst[(size_t)(r0 + y) * DV + c0 + tx] = tile[tx][y];
 }
 
 constexpr int DT = 256;     // tokens per dgamma workgroup: 4 waves x 2 blocks of 32
@@ -476,7 +477,7 @@ int launch_bwd_fast(const mc_dims& d, const BwdBuffers& w, const void* Q, const 
     const int BH = d.B * d.H;
     // transposed bf16 states for the swapped read
     hipLaunchKernelGGL(transpose_states_kernel, dim3(BH * NS, d.d_k / 32, d.d_v / 32), dim3(256),
-                       0, st, M, d.d_v, d.d_k, (bf16_t*)w.mt);
+                       0, st, (const bf16_t*)M_lo, d.d_v, d.d_k, (bf16_t*)w.mt);
     // dphi(q) = the gated read with queries dy, keys v, values phi(k), states M^T
     mc_dims ds = d;
     ds.d_k = d.d_v;

@@ -146,8 +146,10 @@ mc_status mc_grm_readout(const mc_dims* dims, const void* Q, const void* K, cons
  *     R_t = Top-k of {a_t^(i)}_{i<s} (larger score first, lower index on ties; all of them
  *     when s <= k); gamma_t = softmax over R_t and the online segment;
  *     y_t = gamma^(s) M_t^(s) phi(q_t) + sum_{i in R_t} gamma^(i) M^(i) phi(q_t)
- *   The selection is exact: scores are formed in fp32 and any token whose k-th / (k+1)-th
- *   margin is within the fp32 error bound is re-scored in fp64.
+ *   The selection is exact: every score is formed in fp64 in the definition's order -- the
+ *   segment's x values summed token by token, divided by its length, then the dot product
+ *   with u_t summed term by term with no fused multiply-add -- and ranked on those values,
+ *   ties going to the lower index.
  *
  *   Arguments as mc_grm_readout, plus
  *   top_k  1 <= top_k <= 16

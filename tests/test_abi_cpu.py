@@ -266,3 +266,10 @@ def test_backward_arguments():
         assert call(**{k: None}) == mc.MC_ERR_NULL, k
     assert call(ws_bytes=need - 1) == mc.MC_ERR_WORKSPACE
     assert call(dX=MIS) == mc.MC_ERR_ALIGN
+    # bf16 reads only the bf16 states: M = NULL passes the pointer checks (the call then stops
+    # at the misaligned dX); fp32 reads only M, so there M = NULL is an error
+    assert call(M=None, dX=MIS) == mc.MC_ERR_ALIGN
+    d.dtype = mc.MC_F32
+    need = mc.mc_workspace_bytes(d, mc.MC_OP_GRM_BACKWARD)
+    assert call(ws_bytes=need, M=None) == mc.MC_ERR_NULL
+    assert call(ws_bytes=need, M_lo=None, dX=MIS) == mc.MC_ERR_ALIGN
