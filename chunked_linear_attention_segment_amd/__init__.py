@@ -22,7 +22,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmc.so")
 
 MC_OK, MC_ERR_NULL, MC_ERR_DIMS, MC_ERR_UNSUPPORTED = 0, 1, 2, 3
-MC_ERR_ALIGN, MC_ERR_WORKSPACE, MC_ERR_HIP, MC_ERR_CAPACITY = 4, 5, 6, 7
+MC_ERR_ALIGN, MC_ERR_WORKSPACE, MC_ERR_HIP, MC_ERR_CAPACITY, MC_ERR_SCRATCH = 4, 5, 6, 7, 8
+MC_NOALLOC_SCRATCH_BYTES = 64 << 20
 MC_F32, MC_BF16 = 0, 1
 MC_PHI_IDENTITY, MC_PHI_ELU1 = 0, 1
 MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE, MC_OP_GRM_BACKWARD, MC_OP_SCAN_SEGS = \
@@ -30,7 +31,8 @@ MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE, MC_OP_GRM_BACKWARD, MC_OP_SCA
 
 EXPORTED = ["mc_abi_version", "mc_status_str", "mc_workspace_bytes", "mc_scan_prefill",
             "mc_grm_readout", "mc_ssc_readout", "mc_decode_step", "mc_scan_prefill_segs",
-            "mc_grm_readout_segs", "mc_scan_prefill_swla", "mc_grm_backward"]
+            "mc_grm_readout_segs", "mc_scan_prefill_swla", "mc_grm_backward",
+            "mc_decode_step_noalloc"]
 MC_MAX_SEGS = 512
 
 
@@ -84,6 +86,9 @@ def load(path: str = LIB_PATH):
         lib.mc_decode_step.restype = ctypes.c_int
         lib.mc_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P,
                                        ctypes.c_size_t, P]
+        lib.mc_decode_step_noalloc.restype = ctypes.c_int
+        lib.mc_decode_step_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int32,
+                                               P, P]
         _lib = lib
     return _lib
 
@@ -244,6 +249,18 @@ def mc_decode_step(dims, q, k, v, u, x, M_on, xsum_on, count_on, M_cache, P_cach
                                  _p(P_cache), n_cached.ctypes.data, int(n_cap), _p(y), w, wb,
                                  _stream(stream)),
            "mc_decode_step")
+
+
+def mc_decode_step_noalloc(dims, q, k, v, u, x, M_on, xsum_on, count_on, M_cache, P_cache,
+                           n_cached, n_cap, y, stream=None):
+    """mc_decode_step with the library's fixed per-GPU scratch instead of a workspace."""
+    assert isinstance(count_on, np.ndarray) and count_on.dtype == np.int32
+    assert isinstance(n_cached, np.ndarray) and n_cached.dtype == np.int32
+    _check(load().mc_decode_step_noalloc(ctypes.byref(dims), _p(q), _p(k), _p(v), _p(u), _p(x),
+                                         _p(M_on), _p(xsum_on), count_on.ctypes.data,
+                                         _p(M_cache), _p(P_cache), n_cached.ctypes.data,
+                                         int(n_cap), _p(y), _stream(stream)),
+           "mc_decode_step_noalloc")
 
 
 # ---- allocation helpers (torch is only memory plumbing here) ----------------------------

@@ -140,6 +140,9 @@ const char* mc_status_str(mc_status s) {
         case MC_ERR_WORKSPACE: return "workspace too small";
         case MC_ERR_HIP: return "HIP launch failed";
         case MC_ERR_CAPACITY: return "decode cache is full";
+        case MC_ERR_SCRATCH:
+            return "the step needs more scratch than the fixed buffer of "
+                   "mc_decode_step_noalloc holds";
     }
     return "unknown status";
 }
@@ -390,10 +393,14 @@ mc_status mc_grm_backward(const mc_dims* d, const void* Q, const void* K, const 
                : MC_OK;
 }
 
-mc_status mc_decode_step(const mc_dims* d, const void* q, const void* k, const void* v,
-                         const void* u, const void* x, float* M_on, float* xsum_on,
-                         int32_t* count_on, void* M_cache, float* P_cache, int32_t* n_cached,
-                         int32_t n_cap, void* y, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// Validation shared by the two decode entry points (before any HIP call).
+static mc_status check_decode(const mc_dims* d, const void* q, const void* k, const void* v,
+                              const void* u, const void* x, const float* M_on,
+                              const float* xsum_on, const int32_t* count_on,
+                              const void* M_cache, const float* P_cache,
+                              const int32_t* n_cached, int32_t n_cap, const void* y) {
     mc_status st = check_dims(d, false);
     if (st != MC_OK) return st;
     // u may be NULL: uniform weights over the memories (post-training memory caching)
@@ -403,22 +410,59 @@ mc_status mc_decode_step(const mc_dims* d, const void* q, const void* k, const v
     if (n_cap > 0 && !M_cache) return MC_ERR_NULL;
     const int cnt = *count_on, n = *n_cached;
     if (cnt < 0 || cnt >= d->seg_len || n < 0 || n > n_cap) return MC_ERR_DIMS;
-    const int emit = (cnt + 1 == d->seg_len);
-    if (emit && n == n_cap) return MC_ERR_CAPACITY;
-    const DecodeWorkspace w = decode_workspace(*d, n_cap, n);
-    if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
-    const void* ptrs[] = {q, k, v, u, x, M_on, xsum_on, M_cache, P_cache, y, ws};
+    if (cnt + 1 == d->seg_len && n == n_cap) return MC_ERR_CAPACITY;
+    const void* ptrs[] = {q, k, v, u, x, M_on, xsum_on, M_cache, P_cache, y};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MC_ERR_ALIGN;
-    if (launch_decode_step(*d, q, k, v, u, x, M_on, xsum_on, cnt, M_cache, P_cache, n, n_cap,
-                           emit, y, ws, stream))
-        return MC_ERR_HIP;
-    if (emit) {
+    return MC_OK;
+}
+
+// The host counters after an enqueued step.
+static void decode_advance(const mc_dims* d, int32_t* count_on, int32_t* n_cached) {
+    if (*count_on + 1 == d->seg_len) {
         *count_on = 0;
-        *n_cached = n + 1;
+        *n_cached += 1;
     } else {
-        *count_on = cnt + 1;
+        *count_on += 1;
     }
+}
+
+extern "C" {
+
+mc_status mc_decode_step(const mc_dims* d, const void* q, const void* k, const void* v,
+                         const void* u, const void* x, float* M_on, float* xsum_on,
+                         int32_t* count_on, void* M_cache, float* P_cache, int32_t* n_cached,
+                         int32_t n_cap, void* y, void* ws, size_t ws_bytes, void* stream) {
+    mc_status st = check_decode(d, q, k, v, u, x, M_on, xsum_on, count_on, M_cache, P_cache,
+                                n_cached, n_cap, y);
+    if (st != MC_OK) return st;
+    const int cnt = *count_on, n = *n_cached;
+    const DecodeWorkspace w = decode_workspace(*d, n_cap, n);
+    if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MC_ERR_ALIGN;
+    if (launch_decode_step(*d, q, k, v, u, x, M_on, xsum_on, cnt, M_cache, P_cache, n, n_cap,
+                           cnt + 1 == d->seg_len, y, ws, n_cap, stream))
+        return MC_ERR_HIP;
+    decode_advance(d, count_on, n_cached);
+    return MC_OK;
+}
+
+mc_status mc_decode_step_noalloc(const mc_dims* d, const void* q, const void* k, const void* v,
+                                 const void* u, const void* x, float* M_on, float* xsum_on,
+                                 int32_t* count_on, void* M_cache, float* P_cache,
+                                 int32_t* n_cached, int32_t n_cap, void* y, void* stream) {
+    mc_status st = check_decode(d, q, k, v, u, x, M_on, xsum_on, count_on, M_cache, P_cache,
+                                n_cached, n_cap, y);
+    if (st != MC_OK) return st;
+    const int cnt = *count_on, n = *n_cached;
+    // the scratch is laid out for the n cached states this step reads
+    if (decode_workspace(*d, n, n).total > MC_NOALLOC_SCRATCH_BYTES) return MC_ERR_SCRATCH;
+    void* scratch = nullptr;
+    if (noalloc_scratch(&scratch)) return MC_ERR_HIP;
+    if (launch_decode_step(*d, q, k, v, u, x, M_on, xsum_on, cnt, M_cache, P_cache, n, n_cap,
+                           cnt + 1 == d->seg_len, y, scratch, n, stream))
+        return MC_ERR_HIP;
+    decode_advance(d, count_on, n_cached);
     return MC_OK;
 }
 

@@ -23,6 +23,8 @@
 //
 // The cached states are read once, with 16-byte non-temporal loads, so the step streams
 // the cache at HBM rate; everything else is small.
+#include <mutex>
+
 #include "common.cuh"
 #include "mc_internal.h"
 
@@ -273,8 +275,8 @@ template <typename T, typename TC, int DK, int DV>
 static int launch_decode_t(const mc_dims& d, const void* q, const void* k, const void* v,
                            const void* u, const void* x, float* M_on, float* xsum, int count,
                            void* M_cache, float* P_cache, int n, int n_cap, int emit, void* y,
-                           void* ws, hipStream_t st) {
-    const DecodeWorkspace w = decode_workspace(d, n_cap, n);
+                           void* ws, int ws_cap, hipStream_t st) {
+    const DecodeWorkspace w = decode_workspace(d, ws_cap, n);
     DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.u = u; a.x = x;
     a.M_on = M_on; a.xsum = xsum; a.M_cache = M_cache; a.P_cache = P_cache;
@@ -298,7 +300,7 @@ static int launch_decode_t(const mc_dims& d, const void* q, const void* k, const
 int launch_decode_step(const mc_dims& d, const void* q, const void* k, const void* v,
                        const void* u, const void* x, float* M_on, float* xsum_on,
                        int count_on, void* M_cache, float* P_cache, int n_cached, int n_cap,
-                       int emit, void* y, void* ws, void* stream) {
+                       int emit, void* y, void* ws, int ws_cap, void* stream) {
     hipStream_t st = (hipStream_t)stream;
 #define MC_DEC(DK, DV)                                                                      \
     if (d.d_k == DK && d.d_v == DV)                                                         \
@@ -306,17 +308,46 @@ int launch_decode_step(const mc_dims& d, const void* q, const void* k, const voi
                    ? launch_decode_t<bf16_t, bf16_t, DK, DV>(d, q, k, v, u, x, M_on,        \
                                                              xsum_on, count_on, M_cache,    \
                                                              P_cache, n_cached, n_cap,      \
-                                                             emit, y, ws, st)               \
+                                                             emit, y, ws, ws_cap, st)       \
                    : launch_decode_t<float, float, DK, DV>(d, q, k, v, u, x, M_on, xsum_on, \
                                                            count_on, M_cache, P_cache,      \
                                                            n_cached, n_cap, emit, y, ws,    \
-                                                           st);
+                                                           ws_cap, st);
     MC_DEC(128, 128)
     MC_DEC(128, 64)
     MC_DEC(64, 128)
     MC_DEC(64, 64)
 #undef MC_DEC
     return (int)hipErrorInvalidValue;
+}
+
+// The decode step's scratch (the partial softmaxes of the runs) for callers that cannot
+// allocate: one fixed buffer per GPU, shared by every call on that GPU.  Host code never
+// uses the array's name as an address: the device address is taken once per device, with
+// that device current, and kept in noalloc_dev.
+static __device__ __align__(256) unsigned char scratch[MC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex noalloc_mu;
+void* noalloc_dev[kMaxDevices];
+}  // namespace
+
+int noalloc_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(noalloc_mu);
+    if (!noalloc_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        if (!p) return (int)hipErrorInvalidSymbol;
+        noalloc_dev[dev] = p;
+    }
+    *out = noalloc_dev[dev];
+    return 0;
 }
 
 }  // namespace mc

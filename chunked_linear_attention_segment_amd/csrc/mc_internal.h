@@ -181,9 +181,14 @@ int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K
                        const uint16_t* M_lo, const float* P, const float* O_on,
                        const int32_t* idx, void* Y, void* stream);
 
+// ws is laid out for a cache of ws_cap states (decode_workspace(d, ws_cap, .)); ws_cap >=
+// n_cached.  The workspace entry point passes n_cap, the scratch entry point n_cached.
 int launch_decode_step(const mc_dims& d, const void* q, const void* k, const void* v,
                        const void* u, const void* x, float* M_on, float* xsum_on,
                        int count_on, void* M_cache, float* P_cache, int n_cached, int n_cap,
-                       int emit, void* y, void* ws, void* stream);
+                       int emit, void* y, void* ws, int ws_cap, void* stream);
+// Device address of the fixed decode scratch (MC_NOALLOC_SCRATCH_BYTES) on the current
+// device, taken with hipGetSymbolAddress on the first call per device.  Returns a hipError_t.
+int noalloc_scratch(void** out);
 
 }  // namespace mc

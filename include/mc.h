@@ -29,7 +29,9 @@
  *   Memory: every tensor argument is a DEVICE pointer owned by the caller, dense row-major
  *     with the last dimension contiguous, 16-byte aligned.  The library allocates, frees
  *     and retains nothing; scratch memory is the caller's workspace `ws` of at least
- *     mc_workspace_bytes() bytes (16-byte aligned; NULL allowed when that size is 0).
+ *     mc_workspace_bytes() bytes (16-byte aligned; NULL allowed when that size is 0).  The
+ *     one exception is mc_decode_step_noalloc, whose scratch is a fixed buffer the library
+ *     holds on each GPU it runs on until the process ends.
  *   Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *     work on it and never synchronise.  Host scalars passed by pointer are read and
  *     updated on the host when the call is made.
@@ -37,7 +39,8 @@
  *     nothing is written and the MC_ERR_* code is returned.  A failed kernel launch
  *     returns MC_ERR_HIP.  Faults inside kernels surface at the caller's next sync.  The
  *     library never prints, aborts or throws.
- *   Threads: no global mutable state; calls are re-entrant.
+ *   Threads: no global mutable state; calls are re-entrant (except that calls of
+ *     mc_decode_step_noalloc on one GPU share its scratch buffer, see there).
  *
  * Token layout: t = 0..L-1 is 0-based; s = t / C is its segment, j = t % C its position.
  * NS = ceil(L / C) segments; if L % C != 0 the last segment is partial.
@@ -62,8 +65,13 @@ typedef enum {
     MC_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                           */
     MC_ERR_WORKSPACE = 5,   /* ws_bytes < mc_workspace_bytes()                            */
     MC_ERR_HIP = 6,         /* a HIP launch failed                                        */
-    MC_ERR_CAPACITY = 7     /* decode: the cache is full and the step would append to it  */
+    MC_ERR_CAPACITY = 7,    /* decode: the cache is full and the step would append to it  */
+    MC_ERR_SCRATCH = 8      /* mc_decode_step_noalloc: the step needs more scratch than
+                               MC_NOALLOC_SCRATCH_BYTES                                    */
 } mc_status;
+
+/* Size of the fixed per-GPU scratch buffer of mc_decode_step_noalloc (64 MiB). */
+#define MC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum { MC_F32 = 0, MC_BF16 = 1 } mc_dtype;           /* storage type of Q,K,V,U,X,Y */
 typedef enum { MC_PHI_IDENTITY = 0, MC_PHI_ELU1 = 1 } mc_phi; /* feature map on Q and K     */
@@ -189,6 +197,32 @@ mc_status mc_decode_step(const mc_dims* dims, const void* q, const void* k, cons
                          const void* u, const void* x, float* M_on, float* xsum_on,
                          int32_t* count_on, void* M_cache, float* P_cache, int32_t* n_cached,
                          int32_t n_cap, void* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mc_decode_step_noalloc -- mc_decode_step without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  It runs the same kernels on the same arguments (all of
+ * them as mc_decode_step, minus ws / ws_bytes) and gives the same results; the scratch they
+ * need (the partial softmaxes of the runs of cached states) is a fixed buffer of
+ * MC_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the process
+ * ends.  The call allocates and frees nothing.
+ *
+ *   The scratch needed is mc_workspace_bytes(dims, MC_OP_DECODE, 0, *n_cached) bytes; if
+ *   that exceeds MC_NOALLOC_SCRATCH_BYTES the call returns MC_ERR_SCRATCH and changes
+ *   nothing (64 sequences x 32 heads x d_v = 128 fit up to 496 cached states).
+ *   The buffer is that of the current device, which must be the device of `stream`.  Every
+ *   call on one GPU uses the same buffer and every region of it that a step reads is first
+ *   written by that step, so nothing carries over between calls; but calls that may run at
+ *   the same time on one GPU (on different streams, or from several host threads without
+ *   ordering) race on it and must be serialised by the caller.
+ *   Errors otherwise as mc_decode_step; a failure to obtain the buffer's device address
+ *   returns MC_ERR_HIP.
+ */
+mc_status mc_decode_step_noalloc(const mc_dims* dims, const void* q, const void* k,
+                                 const void* v, const void* u, const void* x, float* M_on,
+                                 float* xsum_on, int32_t* count_on, void* M_cache,
+                                 float* P_cache, int32_t* n_cached, int32_t n_cap, void* y,
+                                 void* stream);
 
 /*
  * Arbitrary segment boundaries (Memory Caching paper §3, Eq. 4b: segment s has its own

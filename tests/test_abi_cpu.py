@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert mc.mc_abi_version() == 1
-    for s in range(8):
+    for s in range(9):
         assert isinstance(mc.mc_status_str(s), str) and mc.mc_status_str(s)
 
 
@@ -164,6 +164,31 @@ def test_decode_arguments_and_capacity():
     assert call(3, 2, ws_bytes=need - 1)[0] == mc.MC_ERR_WORKSPACE
     assert call(3, 2, y=None)[0] == mc.MC_ERR_NULL
     assert call(3, 2, y=MIS)[0] == mc.MC_ERR_ALIGN
+
+
+def test_decode_noalloc_arguments():
+    # the same validation as mc_decode_step (no workspace argument), plus the limit of the
+    # fixed scratch buffer: 64 x 32 heads of d_v = 128 hold up to 496 cached states
+    lib = mc.load()
+
+    def call(d, count, n, cap, y=A):
+        cnt = np.array([count], np.int32)
+        nc = np.array([n], np.int32)
+        rc = lib.mc_decode_step_noalloc(ctypes.byref(d), A, A, A, A, A, A, A, cnt.ctypes.data,
+                                        A, A, nc.ctypes.data, cap, y, None)
+        return rc, int(cnt[0]), int(nc[0])
+    d = dims(L=1)
+    C = d.seg_len
+    assert call(d, C - 1, 8, 8) == (mc.MC_ERR_CAPACITY, C - 1, 8)
+    assert call(d, C, 0, 8)[0] == mc.MC_ERR_DIMS
+    assert call(d, 3, 9, 8)[0] == mc.MC_ERR_DIMS
+    assert call(d, 3, 2, 8, y=None)[0] == mc.MC_ERR_NULL
+    assert call(d, 3, 2, 8, y=MIS)[0] == mc.MC_ERR_ALIGN
+    big = dims(B=64, H=32, L=1)
+    assert mc.mc_workspace_bytes(big, mc.MC_OP_DECODE, 0, 496) <= mc.MC_NOALLOC_SCRATCH_BYTES
+    assert mc.mc_workspace_bytes(big, mc.MC_OP_DECODE, 0, 497) > mc.MC_NOALLOC_SCRATCH_BYTES
+    assert call(big, 3, 497, 600) == (mc.MC_ERR_SCRATCH, 3, 497)  # unchanged on error
+    assert call(big, 3, 496, 600, y=MIS)[0] == mc.MC_ERR_ALIGN
 
 
 def test_workspace_sizes_scale_with_inputs():
