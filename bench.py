@@ -1,13 +1,17 @@
 """Benchmark of the Memory Caching hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--only LEG]
 
 A step is one GRM prefill of the L=64K workload (B=1, H=32, d=128, segment 512, bf16
 inputs, fp32 accumulation): mc_scan_prefill (per-segment scan: cached states and means)
 followed by mc_grm_readout (online read inside each segment, gate, gamma-weighted read of
-every cached state), with all inputs resident in HBM.  Prints one JSON line; `value` is prefill tokens/s.  The same
-line carries the decode step of the 64x32-sequence, 256-cached-state workload (cached-state
-read GB/s), the roofline of the dominant kernel and the fp64 oracle's CPU rate.
+every cached state), with all inputs resident in HBM.  Prints one JSON line; `value` is
+prefill tokens/s over the K timed steps (wall clock between two synchronisations).  The same
+line carries the other workloads (the L=512 fp32 and L=4K bf16 GRM prefills, the L=16K SSC
+prefill, the decode step of the 64x32-sequence, 256-cached-state workload, the logarithmic
+segmentation, the SWLA memory, the backward), the roofline of the dominant kernel and the
+fp64 oracle's CPU rate.  Per-call times are HIP events on the launch stream; the reported
+figure is their median.
 """
 from __future__ import annotations
 
@@ -25,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 METRIC = "MC-GRM prefill tokens/s (L=64K,H=32,d=128); decode cached-state HBM GB/s"
 
 
@@ -62,6 +67,58 @@ def decode_bytes(B, H, n, dk, dv, dg, elt):
     return B * H * n * dk * dv * elt + B * H * dk * dv * 4 * 2 + B * n * dg * 4
 
 
+def step_flops(B, H, L, C, dk, dv, dg):
+    """Algorithmic FLOPs of a whole GRM prefill step (scan + read with the online term formed
+    in the read): the state emit (2*dk*dv per token) plus readout_flops(online=True)."""
+    return B * H * L * 2 * dk * dv + readout_flops(B, H, L, C, dk, dv, dg, online=True)
+
+
+def ssc_step_work(B, H, L, C, d, dg, k):
+    """Algorithmic FLOPs and HBM bytes of an SSC prefill step: the state emit, the online term
+    (2*(dk+dv) per causal pair of a segment), s+1 gate logits per token and the top-k read
+    (2*d*d per selected state, min(k, s) of them); bytes: Q, K, V, U read and Y written once
+    (bf16), X read once per sequence, the fp32 and bf16 states, the means and the indices
+    written."""
+    N = -(-L // C)
+    pairs = read = gate = 0
+    for s in range(N):
+        n = min(C, L - s * C)
+        pairs += n * (n + 1) // 2
+        read += n * min(k, s) * 2 * d * d
+        gate += n * (s + 1) * 2 * dg
+    fl = B * H * (L * 2 * d * d + pairs * 4 * d + gate + read)
+    by = B * H * L * (2 * d * 2 + 2 * d + 2 * dg + 2 * d + 4 * k) + B * L * dg * 2 + \
+        B * H * N * d * d * 6 + B * N * dg * 4
+    return fl, by
+
+
+def timed_calls(fns, steps, warmup, stream):
+    """Run the callables in order `warmup` times, then `steps` times with a HIP event pair
+    around each on `stream`; returns, per callable, the list of event times (ms) and the wall
+    time of the timed steps (ms per step)."""
+    import torch
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in fns] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for j, f in enumerate(fns):
+            ev[i][j][0].record(stream)
+            f()
+            ev[i][j][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return [[ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]
+            for j in range(len(fns))], wall
+
+
+def med(x):
+    return float(np.median(np.asarray(x)))
+
+
 def src_hash():
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "chunked_linear_attention_segment_amd", "csrc"))):
@@ -72,7 +129,8 @@ def src_hash():
 
 def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel sources (else None)."""
+    the current kernel sources (else None).  The value is a stored profile figure, not a
+    measurement of this run; the JSON line says so next to it."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -84,6 +142,11 @@ def load_traffic(kernel: str, workload: str):
     except Exception:
         return None
     return None
+
+
+TRAFFIC_SOURCE = ("stored, not measured in this run: profiles/traffic.json (rocprofv3 FETCH_SIZE "
+                  "and WRITE_SIZE per launch, scaled by a copy kernel of known size), used only "
+                  "while the kernel sources hash to the value recorded there")
 
 
 def main():
@@ -105,7 +168,10 @@ def main():
                     help="skip the SWLA-memory prefill line")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward (training) lines")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "segs", "swla", "backward"],
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the L=512 fp32, L=4K bf16 and L=16K SSC prefill lines")
+    ap.add_argument("--only", choices=["all", "prefill", "small", "ssc", "decode", "segs", "swla",
+                                       "backward"],
                     default="all",
                     help="profiling aid: run only one workload (the JSON line then lacks the "
                          "other part)")
@@ -137,10 +203,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
         return
-    if args.only in ("decode", "segs", "swla", "backward"):
+    if args.only in ("small", "ssc", "decode", "segs", "swla", "backward"):
         rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup}
-        {"decode": run_decode, "segs": run_log_segments, "swla": run_swla,
-         "backward": run_backward}[args.only](args, rec, dev)
+        {"small": run_small, "ssc": run_ssc, "decode": run_decode, "segs": run_log_segments,
+         "swla": run_swla, "backward": run_backward}[args.only](args, rec, dev)
         print(json.dumps(rec), flush=True)
         return
     w = WORKLOADS["grm_bf16_L64K"]
@@ -152,36 +218,22 @@ def main():
     ws = mc.workspace(d, mc.MC_OP_GRM, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
+    def scan():
         mc.mc_scan_prefill(d, inp["Q"], inp["K"], inp["V"], inp["X"], M, M_lo, P, O_on,
                            stream=stream)
+
+    def read():
         mc.mc_grm_readout(d, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], M, M_lo, P, O_on,
                           Y, None, ws=ws, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # whole-step wall time, and per-call HIP events on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        mc.mc_scan_prefill(d, inp["Q"], inp["K"], inp["V"], inp["X"], M, M_lo, P, O_on,
-                           stream=stream)
-        ev[i][1].record(stream)
-        mc.mc_grm_readout(d, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], M, M_lo, P, O_on,
-                          Y, None, ws=ws, stream=stream)
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    scan_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    read_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    ms_per_step = wall * 1e3 / args.steps
+    # K timed steps between two synchronisations (wall clock: `value`), with a HIP event pair
+    # around each call on the launch stream (per-call medians: the roofline)
+    (scan_t, read_t), ms_per_step = timed_calls([scan, read], args.steps, args.warmup, stream)
+    scan_ms, read_ms = med(scan_t), med(read_t)
     tokens_per_s = B * L / (ms_per_step / 1e3)
 
     fl_read = readout_flops(B, H, L, C, dk, dv, dg, online=(args.online == "fused"))
+    fl_step = step_flops(B, H, L, C, dk, dv, dg)
     achieved = fl_read / (read_ms / 1e3) / 1e12
     traffic = load_traffic("grm_readout", w.name)
     rec = {
@@ -200,15 +252,26 @@ def main():
         "config": {"workload": w.name, "B": B, "H": H, "L": L, "d_k": dk, "d_v": dv, "d_g": dg,
                    "seg_len": C, "phi": w.phi, "online_read": args.online,
                    "steps_timed": "mc_scan_prefill + mc_grm_readout"},
-        "kernels_ms": {"mc_scan_prefill": round(scan_ms, 4), "mc_grm_readout": round(read_ms, 4)},
+        "kernels_ms": {"mc_scan_prefill": round(scan_ms, 4), "mc_grm_readout": round(read_ms, 4),
+                       "statistic": "median of %d HIP-event pairs on the launch stream"
+                                    % args.steps,
+                       "mc_grm_readout_mean": round(float(np.mean(read_t)), 4)},
         "roofline": {"kernel": "mc_grm_readout (prefix sums, gate pass, gamma-weighted read)",
                      "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "algorithmic_flops": fl_read},
+                     "traffic": traffic, "traffic_source": TRAFFIC_SOURCE,
+                     "algorithmic_flops": fl_read,
+                     "step": {"what": "whole step (scan + read), wall clock",
+                              "algorithmic_flops": fl_step,
+                              "achieved": round(fl_step / (ms_per_step / 1e3) / 1e12, 2)}},
     }
     del M, M_lo, P, O_on, Y, ws, inp
     torch.cuda.empty_cache()
+
+    if not args.no_small and args.only == "all":
+        run_small(args, rec, dev)
+        run_ssc(args, rec, dev)
 
     if not args.no_decode and args.only == "all":
         run_decode(args, rec, dev)
@@ -239,13 +302,123 @@ def measured_peaks(rec):
     r = rec["roofline"]
     r["measured_peak"] = round(mf, 1)
     r["frac_of_measured"] = round(r["achieved"] / mf, 4)
+    st = r.get("step")
+    if st:
+        st["frac_of_measured"] = round(st["achieved"] / mf, 4)
     if "decode" in rec:
         rd = rec["decode"]["roofline"]
         rd["measured_peak"] = round(bw, 1)
         rd["frac_of_measured"] = round(rd["achieved"] / bw, 4)
+    for leg in rec.get("small", {}).values():
+        rl = leg["roofline"]
+        if rl["bound"] == "mfma":
+            rl["measured_peak"] = round(mf, 1)
+            rl["frac_of_measured"] = round(rl["achieved"] / mf, 4)
+    if "ssc" in rec:
+        rl = rec["ssc"]["roofline"]
+        t_min = max(rl["algorithmic_flops"] / (mf * 1e12), rl["algorithmic_bytes"] / (bw * 1e9))
+        rl["frac_of_measured"] = round(t_min / (rec["ssc"]["ms_per_step"] / 1e3), 4)
     rec["measured_peaks"] = {"mfma_bf16_tflops": round(mf, 1), "hbm_read_gbs": round(bw, 1),
                              "how": "libmcpeak: 4096 WGs x 4 waves of back-to-back "
                                     "v_mfma_f32_32x32x16_bf16; 4 GiB streaming read"}
+
+
+def run_small(args, rec, dev):
+    """The L=512 fp32 GRM prefill (B=1, H=1, d=64, segment 64; on the fp32 vector kernels, a
+    latency-bound size) and the L=4K bf16 GRM prefill (B=4, H=16, d=128, segment 256, elu+1),
+    each as scan + read with the online term formed in the read; tokens/s of the step and the
+    roofline of the read call (bf16 MFMA) or of the step (fp32 vector units)."""
+    import torch
+
+    import chunked_linear_attention_segment_amd as mc
+    from chunked_linear_attention_segment_amd.inputs import WORKLOADS, make_prefill_device
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in ("grm_f32_L512", "grm_bf16_L4K_elu"):
+        w = WORKLOADS[name]
+        B, H, L, C, dk, dv, dg = w.B, w.H, w.L, w.seg_len, w.d_k, w.d_v, w.d_g
+        d = mc.make_dims(B, H, L, dk, dv, dg, C, 1, w.dtype, w.phi)
+        inp = make_prefill_device(w, seed=0, device=dev)
+        M, M_lo, P, O_on = mc.alloc_prefill(d, dev, online=False)
+        Y = torch.empty((B, H, L, dv), dtype=mc.torch_dtype(d), device=dev)
+        ws = mc.workspace(d, mc.MC_OP_GRM, device=dev)
+
+        def scan():
+            mc.mc_scan_prefill(d, inp["Q"], inp["K"], inp["V"], inp["X"], M, M_lo, P, O_on,
+                               stream=stream)
+
+        def read():
+            mc.mc_grm_readout(d, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], M, M_lo, P,
+                              O_on, Y, None, ws=ws, stream=stream)
+        steps = max(args.steps, 20)
+        (scan_t, read_t), ms = timed_calls([scan, read], steps, args.warmup, stream)
+        fl_read = readout_flops(B, H, L, C, dk, dv, dg, online=True)
+        fl_step = step_flops(B, H, L, C, dk, dv, dg)
+        if w.dtype == "bf16":
+            tf = fl_read / (med(read_t) / 1e3) / 1e12
+            roof = {"kernel": "mc_grm_readout", "bound": "mfma", "achieved": round(tf, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / PEAK_BF16_TFLOPS, 4), "algorithmic_flops": fl_read}
+        else:
+            tf = fl_step / (ms / 1e3) / 1e12
+            roof = {"kernel": "whole step (fp32 vector kernels)", "bound": "alu",
+                    "achieved": round(tf, 4), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / PEAK_FP32_TFLOPS, 6), "algorithmic_flops": fl_step}
+        out[name] = {"metric": "prefill tokens/s", "value": round(B * L / (ms / 1e3), 1),
+                     "unit": "tokens/s", "ms_per_step": round(ms, 4), "steps": steps,
+                     "config": {"B": B, "H": H, "L": L, "d_k": dk, "d_v": dv, "d_g": dg,
+                                "seg_len": C, "phi": w.phi, "dtype": w.dtype},
+                     "kernels_ms": {"mc_scan_prefill": round(med(scan_t), 4),
+                                    "mc_grm_readout": round(med(read_t), 4)},
+                     "roofline": roof}
+        del inp, M, M_lo, P, O_on, Y, ws
+        torch.cuda.empty_cache()
+    rec["small"] = out
+
+
+def run_ssc(args, rec, dev):
+    """The L=16K SSC prefill (B=2, H=16, d=128, segment 256, top-4): mc_scan_prefill +
+    mc_ssc_readout with the online term formed in the read, inputs resident; tokens/s, and the
+    fraction of the binding roofline max(algorithmic FLOPs / MFMA peak, algorithmic bytes / HBM
+    bandwidth) (HBM at this size)."""
+    import torch
+
+    import chunked_linear_attention_segment_amd as mc
+    from chunked_linear_attention_segment_amd.inputs import WORKLOADS, make_prefill_device
+    stream = torch.cuda.current_stream()
+    w = WORKLOADS["ssc_bf16_L16K_k4"]
+    B, H, L, C, dk, dv, dg, k = w.B, w.H, w.L, w.seg_len, w.d_k, w.d_v, w.d_g, w.top_k
+    d = mc.make_dims(B, H, L, dk, dv, dg, C, 1, w.dtype, w.phi)
+    inp = make_prefill_device(w, seed=0, device=dev)
+    M, M_lo, P, O_on = mc.alloc_prefill(d, dev, online=False)
+    Y = torch.empty((B, H, L, dv), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((B, H, L, k), dtype=torch.int32, device=dev)
+    ws = mc.workspace(d, mc.MC_OP_SSC, top_k=k, device=dev)
+
+    def scan():
+        mc.mc_scan_prefill(d, inp["Q"], inp["K"], inp["V"], inp["X"], M, M_lo, P, O_on,
+                           stream=stream)
+
+    def read():
+        mc.mc_ssc_readout(d, k, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], M, M_lo, P,
+                          O_on, Y, idx, ws=ws, stream=stream)
+    (scan_t, read_t), ms = timed_calls([scan, read], args.steps, args.warmup, stream)
+    fl, by = ssc_step_work(B, H, L, C, dk, dg, k)
+    t_min = max(fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
+    rec["ssc"] = {"workload": w.name, "metric": "SSC prefill tokens/s",
+                  "value": round(B * L / (ms / 1e3), 1), "unit": "tokens/s",
+                  "ms_per_step": round(ms, 4), "top_k": k,
+                  "steps_timed": "mc_scan_prefill + mc_ssc_readout",
+                  "kernels_ms": {"mc_scan_prefill": round(med(scan_t), 4),
+                                 "mc_ssc_readout": round(med(read_t), 4)},
+                  "roofline": {"bound": "hbm" if by / PEAK_HBM_GBS / 1e9 > fl / PEAK_BF16_TFLOPS / 1e12
+                               else "mfma",
+                               "what": "whole step against max(FLOPs / 2.5 PFLOP/s, bytes / 8 TB/s)",
+                               "achieved": round(by / (ms / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                               "unit": "GB/s", "frac": round(t_min / (ms / 1e3), 4),
+                               "algorithmic_flops": fl, "algorithmic_bytes": by}}
+    del inp, M, M_lo, P, O_on, Y, idx, ws
+    torch.cuda.empty_cache()
 
 
 def run_decode(args, rec, dev):
@@ -288,7 +461,7 @@ def run_decode(args, rec, dev):
                 dstep(u)
                 ev[i][1].record(stream)
             torch.cuda.synchronize()
-            return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+            return med([a.elapsed_time(b) for a, b in ev])
 
         dms = timed(di["u"])
         ams = timed(None)
@@ -354,7 +527,7 @@ def run_log_segments(args, rec, dev):
         step()
         b.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms = med([a.elapsed_time(b) for a, b in ev])
     # algorithmic FLOPs: per token, the state update and online read (4 dk dv), the reads of
     # the completed segments before its own (2 dk dv each) and s + 1 gate logits (2 dg each);
     # algorithmic bytes: Q, K, V, U read and Y written once (bf16), X once per sequence, the
@@ -423,8 +596,8 @@ def run_swla(args, rec, dev):
         e[2].record(stream)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    scan_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    read_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    scan_ms = med([e[0].elapsed_time(e[1]) for e in ev])
+    read_ms = med([e[1].elapsed_time(e[2]) for e in ev])
     fl_read = readout_flops(B, H, L, C, dk, dv, dg, online=False)
     tf = fl_read / (read_ms / 1e3) / 1e12
     NS = -(-L // C)
@@ -508,7 +681,7 @@ def run_backward(args, rec, dev):
             step()
             b.record(stream)
         torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        ms = med([a.elapsed_time(b) for a, b in ev])
         fl = backward_flops(B, H, L, C, dk, dv, dg)
         tf = fl / (ms / 1e3) / 1e12
         # bf16 with d_k = d_v = 128 runs the dense contractions on MFMA; other shapes on the
@@ -526,18 +699,28 @@ def run_backward(args, rec, dev):
                        "metric": "backward tokens/s", "workloads": out}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, rows_sample):
-    """The fp64 oracle on the host cores, on a bounded sample of the same workload: a group
-    of heads (one per thread) runs the full-length scan and evaluates `rows_sample` evenly
-    spaced rows; a second run with one row gives the scan's fixed cost, and the per-row cost
-    is extrapolated to all L rows and all heads."""
+    """The fp64 oracle on every host core this process may run on, on a bounded sample of the
+    same workload: a group of heads (at most one per thread) runs the full-length scan and
+    evaluates `rows_sample` evenly spaced rows; a second run with one row gives the scan's fixed
+    cost, and the per-row cost is extrapolated to all L rows and all heads."""
     import torch
 
     import oracle
     from chunked_linear_attention_segment_amd.inputs import make_prefill_device
 
-    cores = min(16, os.cpu_count() or 1)
-    Hs = cores
+    cores = len(os.sched_getaffinity(0))
+    Hs = min(cores, w.H)
     inp = make_prefill_device(w, seed=0, device="cuda", H=Hs)
     host = {k: v.to(torch.float64).cpu().numpy() for k, v in inp.items()}
     del inp
@@ -556,9 +739,10 @@ def cpu_baseline(w, rows_sample):
     t_full_group = t_scan + per_row * L          # Hs heads, all L rows
     t_full = t_full_group * (w.H / Hs) * w.B
     return {"value": round(w.B * L / t_full, 2), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
-            "sample": "%d of %d heads (one per thread), full-length scan, %d evenly spaced rows "
-                      "of %d; scan %.2fs + rows %.2fs, extrapolated linearly in rows and heads"
+            "kind": "oracle", "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+            "threads": "OpenMP, %d threads (every core in this process's affinity set)" % cores,
+            "sample": "%d of %d heads, full-length scan, %d evenly spaced rows of %d; scan "
+                      "%.2fs + rows %.2fs, extrapolated linearly in rows and heads"
                       % (Hs, w.H, len(rows), L, t_scan, t_rows - t_scan)}
 
 

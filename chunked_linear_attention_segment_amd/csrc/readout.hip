@@ -503,43 +503,107 @@ __global__ void seg_mean64_kernel(const T* __restrict__ X, int L, int C, int NS,
     }
 }
 
-// One thread per token: scores for the completed segments i < s, kept as a descending list
-// of the top_k best (a candidate enters only if strictly larger, so earlier = lower indices
-// win ties), written out in ascending index order, -1 padded.
+// 64 tokens of one (b, h) per workgroup of 256 threads.  The router score of token t and
+// segment i is <u_t, mean_i> summed over the gate width e = 0, 1, ... in order, every product
+// and every sum rounded separately (the oracle's order).  The tile's u values (exact in fp64)
+// and the means of a chunk of 32 segments are staged in LDS a slab of 64 gate columns at a
+// time; thread (tq, sq) = (tid % 16, tid / 16) accumulates the 4 x 2 scores of tokens
+// 4 tq .. 4 tq + 3 and segments 2 sq, 2 sq + 1 of the chunk, carrying its partial sums across
+// the slabs so every score is one in-order sum.  The chunk's scores go through LDS to thread
+// t < 64, which presents them in segment order to its token's top-k list: a candidate enters
+// only if strictly larger, so the lower index wins ties.  Indices are written in ascending
+// order, -1 padded.
+constexpr int SEL_T = 64;   // tokens per workgroup
+constexpr int SEL_S = 32;   // segments per chunk
+constexpr int SEL_E = 64;   // gate columns per slab
+
 template <typename T, int KMAX>
-__global__ __launch_bounds__(64) void ssc_select_kernel(const T* __restrict__ U,
-                                                        const double* __restrict__ P64, int L,
-                                                        int C, int NS, int DG, int H, int xh,
-                                                        int top_k, int32_t* __restrict__ idx) {
-    const int t = blockIdx.x * 64 + threadIdx.x;
+__global__ __launch_bounds__(256, 2) void ssc_select_kernel(const T* __restrict__ U,
+                                                            const double* __restrict__ P64, int L,
+                                                            int C, int NS, int DG, int H, int xh,
+                                                            int top_k, int32_t* __restrict__ idx) {
+    // column-major slabs: a thread's 4 tokens (2 segments) at one gate column are contiguous;
+    // staged by lanes that take consecutive tokens (segments), so the writes run along a row
+    __shared__ double us[SEL_E][SEL_T];      // u of the tile's tokens, one slab
+    __shared__ double ps[SEL_E][SEL_S];      // means of the chunk's segments, one slab
+    __shared__ double sc[SEL_T][SEL_S + 1];  // the chunk's scores
+    const int tid = threadIdx.x;
     const size_t bh = blockIdx.y;
-    if (t >= L) return;
+    const int t0 = blockIdx.x * SEL_T;
     const int b = (int)(bh / H), h = (int)(bh % H);
     const size_t bx = (size_t)b * xh + (xh == 1 ? 0 : h);
-    const int s = t / C;
+    const int ntok = min(SEL_T, L - t0);
+    const int smax = (t0 + ntok - 1) / C;  // segments 0..smax-1 are candidates for some token
+    const int tq = tid % 16, sq = tid / 16;
+    const int t = t0 + tid;                // the token merged by thread tid < SEL_T
+    const int s_t = t / C;
     double best[KMAX];
     int bi[KMAX];
 #pragma unroll
     for (int c = 0; c < KMAX; ++c) { best[c] = 0.0; bi[c] = -1; }
-    const T* u = U + (bh * L + t) * DG;
-    for (int i = 0; i < s; ++i) {
-        const double* Pi = P64 + (bx * NS + i) * DG;
-        double a = 0.0;
-        for (int e = 0; e < DG; ++e) a = __dadd_rn(a, __dmul_rn((double)ld(u, e), Pi[e]));
-        // insert (a, i) into the descending list of length top_k
-        int pos = top_k;  // first slot whose entry is empty or strictly smaller than a
+    const T* Ut = U + (bh * L + t0) * DG;
+    for (int c0 = 0; c0 < smax; c0 += SEL_S) {
+        const int nseg = min(SEL_S, smax - c0);
+        double acc[4][2];
 #pragma unroll
-        for (int c = KMAX - 1; c >= 0; --c)
-            if (c < top_k && (bi[c] < 0 || a > best[c])) pos = c;
-        if (pos < top_k) {
+        for (int j = 0; j < 4; ++j) acc[j][0] = acc[j][1] = 0.0;
+        for (int e0 = 0; e0 < DG; e0 += SEL_E) {
+            const int ek = min(SEL_E, DG - e0);
+            __syncthreads();  // the previous slab (and chunk merge) is consumed
+            // gate widths are multiples of 8, so a slab is whole groups of 4 columns
+            for (int p = tid; p < (ek / 4) * SEL_T; p += 256) {
+                const int tok = p % SEL_T, e = 4 * (p / SEL_T);
 #pragma unroll
-            for (int c = KMAX - 1; c > 0; --c)
-                if (c < top_k && c > pos) { best[c] = best[c - 1]; bi[c] = bi[c - 1]; }
+                for (int j = 0; j < 4; ++j)
+                    us[e + j][tok] = tok < ntok ? (double)ld(Ut, (size_t)tok * DG + e0 + e + j) : 0.0;
+            }
+            for (int p = tid; p < (ek / 2) * SEL_S; p += 256) {
+                const int seg = p % SEL_S, e = 2 * (p / SEL_S);
+                const double* pr = P64 + (bx * NS + c0 + seg) * DG + e0 + e;
+                ps[e][seg] = seg < nseg ? pr[0] : 0.0;
+                ps[e + 1][seg] = seg < nseg ? pr[1] : 0.0;
+            }
+            __syncthreads();
+            for (int e = 0; e < ek; ++e) {
+                double u[4], pv[2];
 #pragma unroll
-            for (int c = 0; c < KMAX; ++c)
-                if (c == pos) { best[c] = a; bi[c] = i; }
+                for (int j = 0; j < 4; ++j) u[j] = us[e][4 * tq + j];
+                pv[0] = ps[e][2 * sq];
+                pv[1] = ps[e][2 * sq + 1];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+                        acc[j][m] = __dadd_rn(acc[j][m], __dmul_rn(u[j], pv[m]));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) sc[4 * tq + j][2 * sq + m] = acc[j][m];
+        __syncthreads();
+        if (tid < SEL_T && tid < ntok) {
+            for (int m = 0; m < nseg; ++m) {
+                const int i = c0 + m;
+                if (i >= s_t) break;
+                const double a = sc[tid][m];
+                // insert (a, i) into the descending list of length top_k
+                int pos = top_k;  // first slot whose entry is empty or strictly smaller than a
+#pragma unroll
+                for (int c = KMAX - 1; c >= 0; --c)
+                    if (c < top_k && (bi[c] < 0 || a > best[c])) pos = c;
+                if (pos < top_k) {
+#pragma unroll
+                    for (int c = KMAX - 1; c > 0; --c)
+                        if (c < top_k && c > pos) { best[c] = best[c - 1]; bi[c] = bi[c - 1]; }
+#pragma unroll
+                    for (int c = 0; c < KMAX; ++c)
+                        if (c == pos) { best[c] = a; bi[c] = i; }
+                }
+            }
         }
     }
+    if (tid >= SEL_T || tid >= ntok) return;
     // ascending index order, -1 padded
     int32_t* out = idx + (bh * L + t) * top_k;
     int prev = -1;
@@ -559,17 +623,17 @@ int launch_ssc_select(const mc_dims& d, int top_k, const void* U, const void* X,
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     dim3 g1(NS, d.B * d.x_heads);
     const int threads = d.d_g < 256 ? ((d.d_g + 63) / 64) * 64 : 256;
-    dim3 g2((d.L + 63) / 64, d.B * d.H);
+    dim3 g2((d.L + SEL_T - 1) / SEL_T, d.B * d.H);
     if (d.dtype == MC_BF16) {
         hipLaunchKernelGGL(seg_mean64_kernel<bf16_t>, g1, dim3(threads), 0, st,
                            (const bf16_t*)X, d.L, d.seg_len, NS, d.d_g, P64);
-        hipLaunchKernelGGL((ssc_select_kernel<bf16_t, 16>), g2, dim3(64), 0, st,
+        hipLaunchKernelGGL((ssc_select_kernel<bf16_t, 16>), g2, dim3(256), 0, st,
                            (const bf16_t*)U, P64, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads,
                            top_k, idx);
     } else {
         hipLaunchKernelGGL(seg_mean64_kernel<float>, g1, dim3(threads), 0, st, (const float*)X,
                            d.L, d.seg_len, NS, d.d_g, P64);
-        hipLaunchKernelGGL((ssc_select_kernel<float, 16>), g2, dim3(64), 0, st,
+        hipLaunchKernelGGL((ssc_select_kernel<float, 16>), g2, dim3(256), 0, st,
                            (const float*)U, P64, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads,
                            top_k, idx);
     }
