@@ -54,7 +54,13 @@ SscWorkspace ssc_workspace(const mc_dims& d) {
     w.on = online_ws(d);
     w.xps = xps_ws(d);
     w.xsum64 = align256(sizeof(double) * (size_t)d.B * d.x_heads * num_segments(d) * d.d_g);
-    w.total = w.aon + w.on + w.xps + w.xsum64;
+    if (gate_pass(d)) {
+        w.w = align256(gate_w_bytes(d));
+        w.won = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
+        w.inv_l = w.won;
+        w.pf = align256(gate_pfrag_bytes(d));
+    }
+    w.total = w.aon + w.on + w.xps + w.xsum64 + w.w + w.won + w.inv_l + w.pf;
     return w;
 }
 
@@ -250,6 +256,24 @@ mc_status mc_ssc_readout(const mc_dims* d, int32_t top_k, const void* Q, const v
         return MC_ERR_HIP;
     if (!mfma && launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
     if (launch_ssc_select(*d, top_k, U, X, xsum64, idx, stream)) return MC_ERR_HIP;
+    if (gate_pass(*d)) {
+        // the gate as its own pass, masked to the selections; the read then loads its
+        // numerators (the GRM read with zero weight on every segment not selected)
+        char* g = (char*)ws + w.aon + w.on + w.xps + w.xsum64;
+        uint16_t* W = (uint16_t*)g;
+        float* won = (float*)(g + w.w);
+        float* inv_l = (float*)(g + w.w + w.won);
+        void* pf = g + w.w + w.won + w.inv_l;
+        if (launch_gate_w(*d, U, xps, P, pf, W, won, inv_l, stream, idx, top_k)) return MC_ERR_HIP;
+        GateWeights gw;
+        gw.W = W;
+        gw.won = won;
+        gw.inv_l = inv_l;
+        if (launch_grm_readout(*d, Q, K, V, U, aon, xps, M, M_lo, P, O_on, gw, Y, nullptr,
+                               stream))
+            return MC_ERR_HIP;
+        return MC_OK;
+    }
     if (launch_ssc_readout(*d, top_k, Q, K, V, U, aon, xps, M, M_lo, P, O_on, idx, Y, stream))
         return MC_ERR_HIP;
     return MC_OK;

@@ -4,6 +4,8 @@
 //     a_t^(i) = <u_t, P_i>                      (i < s: the completed segments' means)
 //     a_t^(s) = <u_t, prefix mean of X over t's segment up to t>   (the online segment)
 //     gamma_t = softmax(a_t^(0..s)).
+// With SSC selections (the Sparse Selective Caching read, gitcode explainer §3.4) only the
+// token's selected segments and the online one enter the softmax: the others get weight 0.
 // For every read tile of RT consecutive tokens of one (b, h) this pass writes the softmax
 // numerators against the token's own max logit m_t = max_i a_t^(i):
 //     W[b,h,tile][i][t] = bf16(exp(a_t^(i) - m_t))  for the rows i < s_hi of the tile
@@ -68,10 +70,12 @@ constexpr int GW = 128;           // tokens per workgroup: half a read tile, 32 
 constexpr int GDG_MAX = 128;      // widest gate (U fragments held in registers)
 constexpr int GPF_STATES = 128;   // means staged in LDS (more are read from the caches)
 
+template <bool SSC>
 __global__ __launch_bounds__(256, 2) void gate_w_kernel(
     const bf16_t* __restrict__ U, const float* __restrict__ xps, const uint4* __restrict__ Pf,
-    int H, int L, int C, int NS, int DG, int xh, int G, bf16_t* __restrict__ W,
-    float* __restrict__ won_out, float* __restrict__ inv_l_out) {
+    int H, int L, int C, int NS, int DG, int xh, int G, const int32_t* __restrict__ idx,
+    int top_k, bf16_t* __restrict__ W, float* __restrict__ won_out,
+    float* __restrict__ inv_l_out) {
     // the means' fragments of the first GPF_STATES states, staged once for the G heads
     __shared__ __attribute__((aligned(16))) uint4 pfl[GPF_STATES / 32 * (GDG_MAX / 16) * 2 * 64];
     // numerators of one 32-state block, [state][token], before the 16-byte stores
@@ -177,9 +181,22 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) lg[r] += lr[r];
             const int lim = seg - i0 - 4 * hi32;
+            // SSC: only the token's selected segments (its idx row) keep their logits
+            uint32_t sel = 0xffffffffu;
+            if constexpr (SSC) {
+                sel = 0u;
+                const int32_t* row = idx + ((size_t)bh * L + tok) * top_k;
+                for (int c = 0; c < top_k; ++c) {
+                    const int dd = row[c] - i0;
+                    if (row[c] >= 0 && dd >= 0 && dd < 32) sel |= 1u << dd;
+                }
+                sel >>= 4 * hi32;
+            }
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (!(8 * (r / 4) + (r % 4) < lim)) lg[r] = -INFINITY;
+            for (int r = 0; r < 16; ++r) {
+                const int rr = 8 * (r / 4) + (r % 4);
+                if (!(rr < lim && ((sel >> rr) & 1u))) lg[r] = -INFINITY;
+            }
             return lg;
         };
         auto passes = [&](auto from_lds) {
@@ -237,7 +254,8 @@ size_t gate_pfrag_bytes(const mc_dims& d) {
 }
 
 int launch_gate_w(const mc_dims& d, const void* U, const float* xps, const float* P,
-                  void* pfrag, uint16_t* W, float* won, float* inv_l, void* stream) {
+                  void* pfrag, uint16_t* W, float* won, float* inv_l, void* stream,
+                  const int32_t* idx, int top_k) {
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
     const int T = (d.L + GT - 1) / GT;
     const int nf = ((NS + 31) / 32) * (d.d_g / 16) * 64;
@@ -246,9 +264,16 @@ int launch_gate_w(const mc_dims& d, const void* U, const float* xps, const float
     // heads sharing one X (x_heads = 1) are taken G at a time, so a workgroup loads the prefix
     // sums of X once for G heads
     const int G = d.x_heads == 1 ? (d.H % 8 == 0 ? 8 : (d.H % 4 == 0 ? 4 : (d.H % 2 == 0 ? 2 : 1))) : 1;
-    hipLaunchKernelGGL(gate_w_kernel, dim3(T * 2, d.B * d.H / G), dim3(256), 0,
-                       (hipStream_t)stream, (const bf16_t*)U, xps, (const uint4*)pfrag, d.H, d.L,
-                       d.seg_len, NS, d.d_g, d.x_heads, G, (bf16_t*)W, won, inv_l);
+    if (idx)
+        hipLaunchKernelGGL(gate_w_kernel<true>, dim3(T * 2, d.B * d.H / G), dim3(256), 0,
+                           (hipStream_t)stream, (const bf16_t*)U, xps, (const uint4*)pfrag, d.H,
+                           d.L, d.seg_len, NS, d.d_g, d.x_heads, G, idx, top_k, (bf16_t*)W, won,
+                           inv_l);
+    else
+        hipLaunchKernelGGL(gate_w_kernel<false>, dim3(T * 2, d.B * d.H / G), dim3(256), 0,
+                           (hipStream_t)stream, (const bf16_t*)U, xps, (const uint4*)pfrag, d.H,
+                           d.L, d.seg_len, NS, d.d_g, d.x_heads, G, nullptr, 0, (bf16_t*)W, won,
+                           inv_l);
     return (int)hipGetLastError();
 }
 

@@ -32,13 +32,17 @@ struct GateWeights {
     const float* inv_l = nullptr;
 };
 size_t gate_pfrag_bytes(const mc_dims& d);  // the means as MFMA fragments (bf16 high + rest)
+// idx (with top_k) given: the SSC gate, every logit but the token's selected segments and the
+// online one masked out
 int launch_gate_w(const mc_dims& d, const void* U, const float* xps, const float* P,
-                  void* pfrag, uint16_t* W, float* won, float* inv_l, void* stream);
+                  void* pfrag, uint16_t* W, float* won, float* inv_l, void* stream,
+                  const int32_t* idx = nullptr, int top_k = 0);
 struct SscWorkspace {
     size_t aon;    // fp32 [B,H,L] (generic kernels)
     size_t on;     // fp32 [B,H,L,dv] (generic kernels only)
     size_t xps;    // fp32 [B,xh,L,dg] (MFMA read)
     size_t xsum64; // fp64 [B,xh,NS,dg]: segment sums of X, token order
+    size_t w, won, inv_l, pf;  // the gate pass (as GrmWorkspace), masked to the selections
     size_t total;
 };
 // Decode: each (b, h) has one partial softmax for the online segment and one per run of
