@@ -377,10 +377,11 @@ def run_small(args, rec, dev):
 
 
 def run_ssc(args, rec, dev):
-    """The L=16K SSC prefill (B=2, H=16, d=128, segment 256, top-4): mc_scan_prefill +
-    mc_ssc_readout with the online term formed in the read, inputs resident; tokens/s, and the
-    fraction of the binding roofline max(algorithmic FLOPs / MFMA peak, algorithmic bytes / HBM
-    bandwidth) (HBM at this size)."""
+    """The L=16K SSC prefill (B=2, H=16, d=128, segment 256, top-4): mc_scan_prefill (the
+    states and the online term O_on) + mc_ssc_readout (selection, routing of the (token,
+    segment) pairs, and the read of the selected states only), inputs resident; tokens/s, and
+    the fraction of the binding roofline max(algorithmic FLOPs / MFMA peak, algorithmic bytes /
+    HBM bandwidth) (HBM at this size)."""
     import torch
 
     import chunked_linear_attention_segment_amd as mc
@@ -390,7 +391,7 @@ def run_ssc(args, rec, dev):
     B, H, L, C, dk, dv, dg, k = w.B, w.H, w.L, w.seg_len, w.d_k, w.d_v, w.d_g, w.top_k
     d = mc.make_dims(B, H, L, dk, dv, dg, C, 1, w.dtype, w.phi)
     inp = make_prefill_device(w, seed=0, device=dev)
-    M, M_lo, P, O_on = mc.alloc_prefill(d, dev, online=False)
+    M, M_lo, P, O_on = mc.alloc_prefill(d, dev, online=True)
     Y = torch.empty((B, H, L, dv), dtype=torch.bfloat16, device=dev)
     idx = torch.empty((B, H, L, k), dtype=torch.int32, device=dev)
     ws = mc.workspace(d, mc.MC_OP_SSC, top_k=k, device=dev)

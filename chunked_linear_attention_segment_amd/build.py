@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "scan.hip", "readout.hip", "decode.hip", "read_mfma.hip", "scan_mfma.hip",
-           "gate.hip", "backward.hip", "backward_mfma.hip"]
+           "gate.hip", "backward.hip", "backward_mfma.hip", "ssc_gather.hip"]
 PEAK_SOURCES = ["peak.hip"]
 # Per-file flags.  The gated read is written in the exact issue order it needs (each MFMA
 # followed by the VALU work of the next k-step, LDS reads two k-steps ahead); the machine

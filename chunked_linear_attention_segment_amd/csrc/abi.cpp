@@ -48,19 +48,31 @@ GrmWorkspace grm_workspace(const mc_dims& d) {
     return w;
 }
 
-SscWorkspace ssc_workspace(const mc_dims& d) {
+SscWorkspace ssc_workspace(const mc_dims& d, int top_k) {
     SscWorkspace w{};
-    w.aon = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
+    const size_t bhl = (size_t)d.B * d.H * d.L;
+    w.aon = align256(sizeof(float) * bhl);
     w.on = online_ws(d);
     w.xps = xps_ws(d);
-    w.xsum64 = align256(sizeof(double) * (size_t)d.B * d.x_heads * num_segments(d) * d.d_g);
-    if (gate_pass(d)) {
+    w.xsum64 = align256(ssc_means_bytes(d));
+    if (ssc_gather_covers(d, top_k)) {
+        // the routed read: the online term (formed here when the caller passes none), the
+        // normalised online weights, and every tile's pairs sorted by segment
+        const size_t tiles = (size_t)d.B * d.H * ((d.L + kSscTile - 1) / kSscTile);
+        w.on = align256(sizeof(float) * bhl * d.d_v);
+        w.won = align256(sizeof(float) * bhl);
+        w.ptok = align256(sizeof(int32_t) * tiles * kSscTile * top_k);
+        w.pw = align256(sizeof(float) * tiles * kSscTile * top_k);
+        w.poff = align256(sizeof(int32_t) * tiles * (num_segments(d) + 1));
+        w.sf = align256(ssc_frag_states_bytes(d));
+    } else if (gate_pass(d)) {
         w.w = align256(gate_w_bytes(d));
         w.won = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
         w.inv_l = w.won;
         w.pf = align256(gate_pfrag_bytes(d));
     }
-    w.total = w.aon + w.on + w.xps + w.xsum64 + w.w + w.won + w.inv_l + w.pf;
+    w.total = w.aon + w.on + w.xps + w.xsum64 + w.w + w.won + w.inv_l + w.pf + w.ptok + w.pw +
+              w.poff + w.sf;
     return w;
 }
 
@@ -162,7 +174,7 @@ size_t mc_workspace_bytes(const mc_dims* d, mc_op op, int32_t top_k, int32_t n_c
     switch (op) {
         case MC_OP_PREFILL: return 0;
         case MC_OP_GRM: return grm_workspace(*d).total;
-        case MC_OP_SSC: return top_k >= 1 ? ssc_workspace(*d).total : 0;
+        case MC_OP_SSC: return top_k >= 1 ? ssc_workspace(*d, top_k).total : 0;
         case MC_OP_GRM_BACKWARD: return bwd_workspace(*d).total;
         case MC_OP_SCAN_SEGS:
             return top_k >= 1 && top_k <= MC_MAX_SEGS ? segs_scan_ws_bytes(*d, top_k) : 0;
@@ -238,7 +250,7 @@ mc_status mc_ssc_readout(const mc_dims* d, int32_t top_k, const void* Q, const v
     if (!Q || !U || !X || !P || !Y || !idx) return MC_ERR_NULL;
     if (!O_on && (!K || !V)) return MC_ERR_NULL;
     if (d->dtype == MC_BF16 ? !M_lo : !M) return MC_ERR_NULL;
-    const SscWorkspace w = ssc_workspace(*d);
+    const SscWorkspace w = ssc_workspace(*d, top_k);
     if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
     const void* ptrs[] = {Q, K, V, U, X, M, M_lo, P, O_on, Y, idx, ws};
     for (const void* p : ptrs)
@@ -246,6 +258,27 @@ mc_status mc_ssc_readout(const mc_dims* d, int32_t top_k, const void* Q, const v
     float* aon = (float*)ws;
     float* xps = (float*)((char*)ws + w.aon + w.on);
     double* xsum64 = (double*)((char*)ws + w.aon + w.on + w.xps);
+    if (ssc_gather_covers(*d, top_k)) {
+        // routed: the online term, the selection with its weights and the tiles' pairs sorted
+        // by segment, then only the selected states are read
+        if (!O_on) {
+            float* on = (float*)((char*)ws + w.aon);
+            if (launch_scan_mfma_online(*d, Q, K, V, on, stream)) return MC_ERR_HIP;
+            O_on = on;
+        }
+        if (launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
+        char* g = (char*)ws + w.aon + w.on + w.xps + w.xsum64;
+        SscRoute rt;
+        rt.aon = aon;
+        rt.won = (float*)g;
+        rt.ptok = (int32_t*)(g + w.won);
+        rt.pw = (float*)(g + w.won + w.ptok);
+        rt.poff = (int32_t*)(g + w.won + w.ptok + w.pw);
+        rt.Sf = g + w.won + w.ptok + w.pw + w.poff;
+        if (launch_ssc_select(*d, top_k, U, X, xsum64, idx, stream, &rt)) return MC_ERR_HIP;
+        if (launch_ssc_gather(*d, top_k, Q, M_lo, O_on, rt, Y, stream)) return MC_ERR_HIP;
+        return MC_OK;
+    }
     if (!O_on && w.on) {
         float* on = (float*)((char*)ws + w.aon);
         if (launch_scan_online(*d, Q, K, V, on, stream)) return MC_ERR_HIP;

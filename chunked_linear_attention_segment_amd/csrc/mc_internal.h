@@ -41,8 +41,9 @@ struct SscWorkspace {
     size_t aon;    // fp32 [B,H,L] (generic kernels)
     size_t on;     // fp32 [B,H,L,dv] (generic kernels only)
     size_t xps;    // fp32 [B,xh,L,dg] (MFMA read)
-    size_t xsum64; // fp64 [B,xh,NS,dg]: segment sums of X, token order
+    size_t xsum64; // fp64 [B,xh,dg,NS rounded up to 16]: segment means of X (ssc_means_bytes)
     size_t w, won, inv_l, pf;  // the gate pass (as GrmWorkspace), masked to the selections
+    size_t ptok, pw, poff, sf;  // the routed read: the tiles' pairs by segment, fragment-order states
     size_t total;
 };
 // Decode: each (b, h) has one partial softmax for the online segment and one per run of
@@ -57,7 +58,7 @@ struct DecodeWorkspace {
 };
 
 GrmWorkspace grm_workspace(const mc_dims& d);
-SscWorkspace ssc_workspace(const mc_dims& d);
+SscWorkspace ssc_workspace(const mc_dims& d, int top_k);
 DecodeWorkspace decode_workspace(const mc_dims& d, int n_cap, int n_cached);
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -176,8 +177,28 @@ int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const voi
                        const uint16_t* M_lo, const float* P, const float* O_on,
                        const GateWeights& gw, void* Y, float* gamma, void* stream);
 
+// Outputs of the selection for the routed SSC read (launch_ssc_gather): the normalised online
+// weight per token, and per read tile of kSscTile tokens the (token, selected segment) pairs
+// sorted by segment with their normalised weights, and each segment's start in that list.
+constexpr int kSscTile = 256;
+struct SscRoute {
+    const float* aon;  // [B, H, L] the online logits (input, launch_aon)
+    float* won;        // [B, H, L]
+    int32_t* ptok;     // [B*H, T, kSscTile * top_k] tile-local token numbers
+    float* pw;         // [B*H, T, kSscTile * top_k]
+    int32_t* poff;     // [B*H, T, NS + 1]
+    void* Sf;          // the states in MFMA fragment order (ssc_frag_states_bytes)
+};
+size_t ssc_frag_states_bytes(const mc_dims& d);
 int launch_ssc_select(const mc_dims& d, int top_k, const void* U, const void* X,
-                      double* xsum64, int32_t* idx, void* stream);
+                      double* xsum64, int32_t* idx, void* stream,
+                      const SscRoute* route = nullptr);
+size_t ssc_means_bytes(const mc_dims& d);
+// the routed SSC read: per tile, only the selected segments' states, each applied to the
+// tokens that chose it; y = won * O_on + sum of pw * S^T phi(q) (bf16, d_k = d_v = 128)
+bool ssc_gather_covers(const mc_dims& d, int top_k);
+int launch_ssc_gather(const mc_dims& d, int top_k, const void* Q, const uint16_t* M_lo,
+                      const float* O_on, const SscRoute& rt, void* Y, void* stream);
 
 int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K,
                        const void* V, const void* U, const float* aon, const float* xps,

@@ -489,153 +489,409 @@ int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K
 // length, then <u_t, mean> accumulated over the gate width in order, every product and sum
 // rounded separately (no fused multiply-add).  Ties go to the lower segment index.
 
+// Segment means in fp64, stored gate column major: P64T[bx][e][s] for s < NSP (NS rounded up
+// to SEL_W; the padding rows are 0), so that the means of a run of segments at one gate column
+// are contiguous.
 template <typename T>
-__global__ void seg_mean64_kernel(const T* __restrict__ X, int L, int C, int NS, int DG,
-                                  double* __restrict__ P64) {
+__global__ void seg_mean64_kernel(const T* __restrict__ X, int L, int C, int NS, int NSP, int DG,
+                                  double* __restrict__ P64T) {
     const int s = blockIdx.x;
     const size_t bx = blockIdx.y;
     const int t0 = s * C;
-    const int len = min(C, L - t0);
+    const int len = s < NS ? min(C, L - t0) : 0;
     for (int e = threadIdx.x; e < DG; e += blockDim.x) {
         double acc = 0.0;
         for (int j = 0; j < len; ++j) acc = __dadd_rn(acc, (double)ld(X, (bx * L + t0 + j) * DG + e));
-        P64[(bx * NS + s) * DG + e] = __ddiv_rn(acc, (double)len);
+        P64T[(bx * DG + e) * NSP + s] = len > 0 ? __ddiv_rn(acc, (double)len) : 0.0;
     }
 }
 
-// 64 tokens of one (b, h) per workgroup of 256 threads.  The router score of token t and
+// u p and acc + m, each rounded to fp64 on its own: the header
+// functions __dmul_rn / __dadd_rn are plain * and +, which the compiler may contract into
+// one fused multiply-add, so contraction is switched off here explicitly
+__device__ __forceinline__ double dmul_sep(double u, double p) {
+#pragma clang fp contract(off)
+    return u * p;
+}
+__device__ __forceinline__ double dadd_sep(double acc, double m) {
+#pragma clang fp contract(off)
+    return acc + m;
+}
+
+// SEL_T tokens of one (b, h) per workgroup of 4 waves.  The router score of token t and
 // segment i is <u_t, mean_i> summed over the gate width e = 0, 1, ... in order, every product
-// and every sum rounded separately (the oracle's order).  The tile's u values (exact in fp64)
-// and the means of a chunk of 32 segments are staged in LDS a slab of 64 gate columns at a
-// time; thread (tq, sq) = (tid % 16, tid / 16) accumulates the 4 x 2 scores of tokens
-// 4 tq .. 4 tq + 3 and segments 2 sq, 2 sq + 1 of the chunk, carrying its partial sums across
-// the slabs so every score is one in-order sum.  The chunk's scores go through LDS to thread
-// t < 64, which presents them in segment order to its token's top-k list: a candidate enters
-// only if strictly larger, so the lower index wins ties.  Indices are written in ascending
-// order, -1 padded.
-constexpr int SEL_T = 64;   // tokens per workgroup
-constexpr int SEL_S = 32;   // segments per chunk
-constexpr int SEL_E = 64;   // gate columns per slab
+// and every sum rounded separately (the oracle's order).  Lane l of every wave owns tokens
+// 2 l, 2 l + 1, 128 + 2 l and 129 + 2 l of the tile; the waves split the candidate segments in
+// runs of SEL_W (wave w takes segments c0 + SEL_W w .. + SEL_W - 1 of chunk c0), so a wave's
+// means are the same for all its lanes and come through scalar loads, SEL_EB gate columns per
+// batch (a scalar load can only be waited for together with all others in flight, so each
+// wait should cover as much arithmetic as possible).  The tile's u values (exact in fp64) are
+// staged in LDS a slab of SEL_E gate columns at a time and shared by the waves.  Every lane
+// keeps, per token, a top-k list of its wave's candidates, presented in segment order, a
+// candidate entering only if strictly larger, so the lower index wins ties.  The lists of
+// waves 1..3 are then merged into wave 0's under the same order (larger score, then lower
+// index first), and wave 0 writes the indices in ascending order, -1 padded.
+constexpr int SEL_T = 256;  // tokens per workgroup (4 per lane)
+constexpr int SEL_W = 8;    // segments per wave per chunk
+constexpr int SEL_E = 16;   // gate columns per LDS slab
+constexpr int SEL_EB = 4;   // gate columns per batch of scalar loads
+static_assert(SEL_T == kSscTile, "the selection's tiles are the routed read's");
+
+template <int KMAX>
+__device__ __forceinline__ void sel_insert(double (&best)[KMAX], int (&bi)[KMAX], int top_k,
+                                           double a, int i) {
+    // first slot that is empty or holds an entry that (a, i) precedes
+    int pos = top_k;
+#pragma unroll
+    for (int c = KMAX - 1; c >= 0; --c)
+        if (c < top_k && (bi[c] < 0 || a > best[c] || (a == best[c] && i < bi[c]))) pos = c;
+    if (pos >= top_k) return;
+#pragma unroll
+    for (int c = KMAX - 1; c > 0; --c)
+        if (c < top_k && c > pos) { best[c] = best[c - 1]; bi[c] = bi[c - 1]; }
+#pragma unroll
+    for (int c = 0; c < KMAX; ++c)
+        if (c == pos) { best[c] = a; bi[c] = i; }
+}
+
+// The same for a list that only ever receives candidates in ascending index order, whose empty
+// slots hold -inf: (a, i) then precedes an entry exactly when a is strictly larger.  The list
+// stays sorted, so the slots the candidate passes form a prefix of the comparisons from the end.
+template <int KMAX>
+__device__ __forceinline__ void sel_insert_asc(double (&best)[KMAX], int (&bi)[KMAX], int top_k,
+                                               double a, int i) {
+    bool gt[KMAX];
+#pragma unroll
+    for (int c = 0; c < KMAX; ++c) gt[c] = c < top_k && a > best[c];
+#pragma unroll
+    for (int c = KMAX - 1; c >= 0; --c) {
+        if (!gt[c]) continue;
+        const bool from_prev = c > 0 && gt[c - 1];
+        best[c] = from_prev ? best[c > 0 ? c - 1 : 0] : a;
+        bi[c] = from_prev ? bi[c > 0 ? c - 1 : 0] : i;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void ld8_f64(const T* p, double (&v)[8]);
+template <>
+__device__ __forceinline__ void ld8_f64<bf16_t>(const bf16_t* p, double (&v)[8]) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = (double)__uint_as_float(q[j] << 16);
+        v[2 * j + 1] = (double)__uint_as_float(q[j] & 0xffff0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void ld8_f64<float>(const float* p, double (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// local token of lane l's a-th token
+__device__ __forceinline__ int sel_tok(int lane, int a) { return 128 * (a >> 1) + 2 * lane + (a & 1); }
+
+// the routing tail's per-state counters: at most this many segments
+constexpr int SEL_NS_MAX = 4096;
+
+template <int KMAX>
+constexpr int sel_lds_doubles() {
+    // u slab, or: the final lists (SEL_T x KMAX scores and indices) + the per-state counters
+    return SEL_E * SEL_T > SEL_T * KMAX * 3 / 2 + (SEL_NS_MAX + 2) / 2
+               ? SEL_E * SEL_T
+               : SEL_T * KMAX * 3 / 2 + (SEL_NS_MAX + 2) / 2;
+}
+
+// Selection outputs beyond idx, for the routed read (all null: idx only).  Per token: the
+// normalised online weight.  Per read tile of SEL_T tokens (tile = t / SEL_T, T tiles per
+// head): the tile's (token, selected segment) pairs sorted by segment, as tile-local token
+// numbers ptok and normalised weights pw (SEL_T * top_k slots), and the start of each
+// segment's run poff[i] (NS + 1 entries, the last = the number of pairs).
+struct SelRoute {
+    const float* aon;  // [B, H, L] the online logits <u_t, prefix mean of X over t's segment>
+    float* won;        // [B, H, L]
+    int32_t* ptok;     // [B*H, T, SEL_T * top_k]
+    float* pw;         // [B*H, T, SEL_T * top_k]
+    int32_t* poff;     // [B*H, T, NS + 1]
+    int NS;
+};
 
 template <typename T, int KMAX>
-__global__ __launch_bounds__(256, 2) void ssc_select_kernel(const T* __restrict__ U,
-                                                            const double* __restrict__ P64, int L,
-                                                            int C, int NS, int DG, int H, int xh,
-                                                            int top_k, int32_t* __restrict__ idx) {
-    // column-major slabs: a thread's 4 tokens (2 segments) at one gate column are contiguous;
-    // staged by lanes that take consecutive tokens (segments), so the writes run along a row
-    __shared__ double us[SEL_E][SEL_T];      // u of the tile's tokens, one slab
-    __shared__ double ps[SEL_E][SEL_S];      // means of the chunk's segments, one slab
-    __shared__ double sc[SEL_T][SEL_S + 1];  // the chunk's scores
-    const int tid = threadIdx.x;
+__global__ __launch_bounds__(256) void ssc_select_kernel(const T* __restrict__ U,
+                                                         const double* __restrict__ P64T, int L,
+                                                         int C, int NSP, int DG, int H, int xh,
+                                                         int top_k, int32_t* __restrict__ idx,
+                                                         const SelRoute rt) {
+    // u slab [e][token]; after the last chunk the same memory carries the lists being merged
+    __shared__ __attribute__((aligned(16))) double lds[sel_lds_doubles<KMAX>()];
+    double (*us)[SEL_T] = reinterpret_cast<double (*)[SEL_T]>(lds);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t bh = blockIdx.y;
-    const int t0 = blockIdx.x * SEL_T;
+    const int tile = gridDim.x - 1 - blockIdx.x;  // the latest tokens (most candidates) first
+    const int t0 = tile * SEL_T;
     const int b = (int)(bh / H), h = (int)(bh % H);
     const size_t bx = (size_t)b * xh + (xh == 1 ? 0 : h);
     const int ntok = min(SEL_T, L - t0);
     const int smax = (t0 + ntok - 1) / C;  // segments 0..smax-1 are candidates for some token
-    const int tq = tid % 16, sq = tid / 16;
-    const int t = t0 + tid;                // the token merged by thread tid < SEL_T
-    const int s_t = t / C;
-    double best[KMAX];
-    int bi[KMAX];
+    // this lane's tokens' candidate counts (0 for tokens past L)
+    int s_of[4];
 #pragma unroll
-    for (int c = 0; c < KMAX; ++c) { best[c] = 0.0; bi[c] = -1; }
+    for (int a = 0; a < 4; ++a) s_of[a] = sel_tok(lane, a) < ntok ? (t0 + sel_tok(lane, a)) / C : 0;
+    double best[4][KMAX];
+    int bi[4][KMAX];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < KMAX; ++c) { best[a][c] = -INFINITY; bi[a][c] = -1; }
     const T* Ut = U + (bh * L + t0) * DG;
-    for (int c0 = 0; c0 < smax; c0 += SEL_S) {
-        const int nseg = min(SEL_S, smax - c0);
-        double acc[4][2];
+    const double* Pb = P64T + bx * DG * NSP;
+    // which run of a chunk a wave takes rotates from workgroup to workgroup, so that the
+    // SIMDs share the work of chunks whose later runs hold no candidates
+    const int run = (wave + blockIdx.x + blockIdx.y) & 3;
+    for (int c0 = 0; c0 < smax; c0 += 4 * SEL_W) {
+        const int sw = c0 + SEL_W * run;  // this wave's first segment
+        const bool act = sw < smax;
+        double acc[4][SEL_W];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j][0] = acc[j][1] = 0.0;
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int j = 0; j < SEL_W; ++j) acc[a][j] = 0.0;
         for (int e0 = 0; e0 < DG; e0 += SEL_E) {
-            const int ek = min(SEL_E, DG - e0);
-            __syncthreads();  // the previous slab (and chunk merge) is consumed
-            // gate widths are multiples of 8, so a slab is whole groups of 4 columns
-            for (int p = tid; p < (ek / 4) * SEL_T; p += 256) {
-                const int tok = p % SEL_T, e = 4 * (p / SEL_T);
+            const int ek = min(SEL_E, DG - e0);  // a multiple of 8 (gate widths are)
+            __syncthreads();                     // the previous slab is consumed
+            for (int p = tid; p < (ek / 8) * SEL_T; p += 256) {
+                const int tok = p % SEL_T, e = 8 * (p / SEL_T);
+                double v[8];
+                if (tok < ntok)
+                    ld8_f64(Ut + (size_t)tok * DG + e0 + e, v);
+                else
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    us[e + j][tok] = tok < ntok ? (double)ld(Ut, (size_t)tok * DG + e0 + e + j) : 0.0;
-            }
-            for (int p = tid; p < (ek / 2) * SEL_S; p += 256) {
-                const int seg = p % SEL_S, e = 2 * (p / SEL_S);
-                const double* pr = P64 + (bx * NS + c0 + seg) * DG + e0 + e;
-                ps[e][seg] = seg < nseg ? pr[0] : 0.0;
-                ps[e + 1][seg] = seg < nseg ? pr[1] : 0.0;
+                    for (int j = 0; j < 8; ++j) v[j] = 0.0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) us[e + j][tok] = v[j];
             }
             __syncthreads();
-            for (int e = 0; e < ek; ++e) {
-                double u[4], pv[2];
+            if (act) {
+                for (int e = 0; e < ek; e += SEL_EB) {
+                    const double* pr = Pb + (size_t)(e0 + e) * NSP + sw;
+                    double pv[SEL_EB][SEL_W];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) u[j] = us[e][4 * tq + j];
-                pv[0] = ps[e][2 * sq];
-                pv[1] = ps[e][2 * sq + 1];
+                    for (int q = 0; q < SEL_EB; ++q)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                        for (int j = 0; j < SEL_W; ++j) pv[q][j] = pr[(size_t)q * NSP + j];
 #pragma unroll
-                    for (int m = 0; m < 2; ++m)
-                        acc[j][m] = __dadd_rn(acc[j][m], __dmul_rn(u[j], pv[m]));
-            }
-        }
+                    for (int q = 0; q < SEL_EB; ++q) {
+                        const double2 u0 = *reinterpret_cast<const double2*>(&us[e + q][2 * lane]);
+                        const double2 u1 =
+                            *reinterpret_cast<const double2*>(&us[e + q][128 + 2 * lane]);
+                        const double uu[4] = {u0.x, u0.y, u1.x, u1.y};
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+                        for (int a = 0; a < 4; ++a) {
+                            double m[SEL_W];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) sc[4 * tq + j][2 * sq + m] = acc[j][m];
-        __syncthreads();
-        if (tid < SEL_T && tid < ntok) {
-            for (int m = 0; m < nseg; ++m) {
-                const int i = c0 + m;
-                if (i >= s_t) break;
-                const double a = sc[tid][m];
-                // insert (a, i) into the descending list of length top_k
-                int pos = top_k;  // first slot whose entry is empty or strictly smaller than a
+                            for (int j = 0; j < SEL_W; ++j) m[j] = dmul_sep(uu[a], pv[q][j]);
 #pragma unroll
-                for (int c = KMAX - 1; c >= 0; --c)
-                    if (c < top_k && (bi[c] < 0 || a > best[c])) pos = c;
-                if (pos < top_k) {
-#pragma unroll
-                    for (int c = KMAX - 1; c > 0; --c)
-                        if (c < top_k && c > pos) { best[c] = best[c - 1]; bi[c] = bi[c - 1]; }
-#pragma unroll
-                    for (int c = 0; c < KMAX; ++c)
-                        if (c == pos) { best[c] = a; bi[c] = i; }
+                            for (int j = 0; j < SEL_W; ++j) acc[a][j] = dadd_sep(acc[a][j], m[j]);
+                        }
+                    }
                 }
             }
         }
-    }
-    if (tid >= SEL_T || tid >= ntok) return;
-    // ascending index order, -1 padded
-    int32_t* out = idx + (bh * L + t) * top_k;
-    int prev = -1;
-    for (int c = 0; c < top_k; ++c) {
-        int nxt = -1;
+        if (act) {
 #pragma unroll
-        for (int e = 0; e < KMAX; ++e)
-            if (e < top_k && bi[e] > prev && (nxt < 0 || bi[e] < nxt)) nxt = bi[e];
-        out[c] = nxt;
-        if (nxt >= 0) prev = nxt;
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int j = 0; j < SEL_W; ++j)
+                    if (sw + j < s_of[a])
+                        sel_insert_asc<KMAX>(best[a], bi[a], top_k, acc[a][j], sw + j);
+        }
     }
+    // waves 1..3 hand their lists to wave 0 through LDS, one wave at a time
+    double* mb = lds;                                        // [SEL_T][KMAX] scores
+    int* mi = reinterpret_cast<int*>(mb + SEL_T * KMAX);     // [SEL_T][KMAX] indices
+    for (int w = 1; w < 4; ++w) {
+        __syncthreads();
+        if (wave == w) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int c = 0; c < KMAX; ++c) {
+                    mb[sel_tok(lane, a) * KMAX + c] = best[a][c];
+                    mi[sel_tok(lane, a) * KMAX + c] = bi[a][c];
+                }
+        }
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int c = 0; c < KMAX; ++c) {
+                    const int i = mi[sel_tok(lane, a) * KMAX + c];
+                    if (c < top_k && i >= 0)
+                        sel_insert<KMAX>(best[a], bi[a], top_k, mb[sel_tok(lane, a) * KMAX + c], i);
+                }
+        }
+    }
+    // wave 0's lists go to LDS; from here on thread t takes the tile's token t
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < KMAX; ++c) {
+                mb[sel_tok(lane, a) * KMAX + c] = best[a][c];
+                mi[sel_tok(lane, a) * KMAX + c] = bi[a][c];
+            }
+    }
+    __syncthreads();
+    const int t = tid;
+    const bool tv = t < ntok;
+    // the token's selection in ascending index order (-1 padded) with the scores alongside
+    int oi[KMAX];
+    double oa[KMAX];
+    {
+        int li[KMAX];
+        double la[KMAX];
+#pragma unroll
+        for (int c = 0; c < KMAX; ++c) {
+            li[c] = tv && c < top_k ? mi[t * KMAX + c] : -1;
+            la[c] = tv && c < top_k ? mb[t * KMAX + c] : 0.0;
+        }
+        int prev = -1;
+#pragma unroll
+        for (int c = 0; c < KMAX; ++c) {
+            int nxt = -1;
+            double an = 0.0;
+#pragma unroll
+            for (int e = 0; e < KMAX; ++e)
+                if (li[e] > prev && (nxt < 0 || li[e] < nxt)) { nxt = li[e]; an = la[e]; }
+            oi[c] = nxt;
+            oa[c] = an;
+            if (nxt >= 0) prev = nxt;
+        }
+    }
+    if (tv) {
+        int32_t* out = idx + (bh * L + t0 + t) * top_k;
+#pragma unroll
+        for (int c = 0; c < KMAX; ++c)
+            if (c < top_k) out[c] = oi[c];
+    }
+    if (!rt.ptok) return;
+    // softmax over the selected segments' logits (the exact scores) and the online logit;
+    // weights normalised
+    float w[KMAX], won = 0.f;
+    if (tv) {
+        const int tg = t0 + t;
+        const double a_on = (double)rt.aon[bh * L + tg];
+        double m = a_on;
+#pragma unroll
+        for (int c = 0; c < KMAX; ++c)
+            if (oi[c] >= 0) m = fmax(m, oa[c]);
+        won = __expf((float)(a_on - m));
+        float l = won;
+#pragma unroll
+        for (int c = 0; c < KMAX; ++c) {
+            w[c] = oi[c] >= 0 ? __expf((float)(oa[c] - m)) : 0.f;
+            l += w[c];
+        }
+        const float inv = 1.f / l;
+        won *= inv;
+#pragma unroll
+        for (int c = 0; c < KMAX; ++c) w[c] *= inv;
+        rt.won[bh * L + tg] = won;
+    }
+    // counting sort of the tile's (token, segment) pairs by segment
+    const int NS = rt.NS;
+    int* cnt = mi + SEL_T * KMAX;  // NS + 1 counters after the lists
+    for (int i = tid; i <= NS; i += 256) cnt[i] = 0;
+    __syncthreads();
+    int slot[KMAX];
+#pragma unroll
+    for (int c = 0; c < KMAX; ++c) slot[c] = oi[c] >= 0 ? atomicAdd(&cnt[oi[c]], 1) : 0;
+    __syncthreads();
+    if (wave == 0) {  // exclusive prefix sums, 64 segments at a time
+        int carry = 0;
+        for (int base = 0; base < NS; base += 64) {
+            const int v = base + lane < NS ? cnt[base + lane] : 0;
+            int x = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o, 64);
+                if (lane >= o) x += y;
+            }
+            if (base + lane < NS) cnt[base + lane] = carry + x - v;
+            carry += __shfl(x, 63, 64);
+        }
+        if (lane == 0) cnt[NS] = carry;
+    }
+    __syncthreads();
+    const size_t tb = bh * gridDim.x + tile;
+    int32_t* ptok = rt.ptok + tb * SEL_T * top_k;
+    float* pw = rt.pw + tb * SEL_T * top_k;
+#pragma unroll
+    for (int c = 0; c < KMAX; ++c)
+        if (oi[c] >= 0) {
+            const int p = cnt[oi[c]] + slot[c];
+            ptok[p] = t;
+            pw[p] = w[c];
+        }
+    for (int i = tid; i <= NS; i += 256) rt.poff[tb * (NS + 1) + i] = cnt[i];
+}
+
+template <typename T, int KMAX>
+static void launch_select_t(const mc_dims& d, int top_k, const T* U, const double* P64T, int NSP,
+                            int32_t* idx, const SelRoute& rt, hipStream_t st) {
+    dim3 g((d.L + SEL_T - 1) / SEL_T, d.B * d.H);
+    hipLaunchKernelGGL((ssc_select_kernel<T, KMAX>), g, dim3(256), 0, st, U, P64T, d.L,
+                       d.seg_len, NSP, d.d_g, d.H, d.x_heads, top_k, idx, rt);
+}
+
+template <typename T>
+static void launch_select_k(const mc_dims& d, int top_k, const T* U, const double* P64T, int NSP,
+                            int32_t* idx, const SelRoute& rt, hipStream_t st) {
+    if (top_k <= 4)
+        launch_select_t<T, 4>(d, top_k, U, P64T, NSP, idx, rt, st);
+    else if (top_k <= 8)
+        launch_select_t<T, 8>(d, top_k, U, P64T, NSP, idx, rt, st);
+    else
+        launch_select_t<T, 16>(d, top_k, U, P64T, NSP, idx, rt, st);
+}
+
+size_t ssc_means_bytes(const mc_dims& d) {
+    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+    const int NSP = (NS + SEL_W - 1) / SEL_W * SEL_W;
+    return sizeof(double) * (size_t)d.B * d.x_heads * d.d_g * NSP;
 }
 
 int launch_ssc_select(const mc_dims& d, int top_k, const void* U, const void* X,
-                      double* P64, int32_t* idx, void* stream) {
+                      double* P64T, int32_t* idx, void* stream, const SscRoute* route) {
     hipStream_t st = (hipStream_t)stream;
     const int NS = (d.L + d.seg_len - 1) / d.seg_len;
-    dim3 g1(NS, d.B * d.x_heads);
+    const int NSP = (NS + SEL_W - 1) / SEL_W * SEL_W;
+    SelRoute rt{};
+    if (route) {
+        if (NS > SEL_NS_MAX || top_k > 16) return (int)hipErrorInvalidValue;
+        rt.aon = route->aon;
+        rt.won = route->won;
+        rt.ptok = route->ptok;
+        rt.pw = route->pw;
+        rt.poff = route->poff;
+        rt.NS = NS;
+    }
+    dim3 g1(NSP, d.B * d.x_heads);
     const int threads = d.d_g < 256 ? ((d.d_g + 63) / 64) * 64 : 256;
-    dim3 g2((d.L + SEL_T - 1) / SEL_T, d.B * d.H);
     if (d.dtype == MC_BF16) {
         hipLaunchKernelGGL(seg_mean64_kernel<bf16_t>, g1, dim3(threads), 0, st,
-                           (const bf16_t*)X, d.L, d.seg_len, NS, d.d_g, P64);
-        hipLaunchKernelGGL((ssc_select_kernel<bf16_t, 16>), g2, dim3(256), 0, st,
-                           (const bf16_t*)U, P64, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads,
-                           top_k, idx);
+                           (const bf16_t*)X, d.L, d.seg_len, NS, NSP, d.d_g, P64T);
+        launch_select_k<bf16_t>(d, top_k, (const bf16_t*)U, P64T, NSP, idx, rt, st);
     } else {
         hipLaunchKernelGGL(seg_mean64_kernel<float>, g1, dim3(threads), 0, st, (const float*)X,
-                           d.L, d.seg_len, NS, d.d_g, P64);
-        hipLaunchKernelGGL((ssc_select_kernel<float, 16>), g2, dim3(256), 0, st,
-                           (const float*)U, P64, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads,
-                           top_k, idx);
+                           d.L, d.seg_len, NS, NSP, d.d_g, P64T);
+        launch_select_k<float>(d, top_k, (const float*)U, P64T, NSP, idx, rt, st);
     }
     return (int)hipGetLastError();
 }
