@@ -19,7 +19,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmc.so")
+# MC_LIB names another build of the same library (e.g. one with host-side sanitizers)
+LIB_PATH = os.environ.get("MC_LIB") or os.path.join(_HERE, "libmc.so")
 
 MC_OK, MC_ERR_NULL, MC_ERR_DIMS, MC_ERR_UNSUPPORTED = 0, 1, 2, 3
 MC_ERR_ALIGN, MC_ERR_WORKSPACE, MC_ERR_HIP, MC_ERR_CAPACITY, MC_ERR_SCRATCH = 4, 5, 6, 7, 8

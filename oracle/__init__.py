@@ -27,7 +27,11 @@ _MODES = {"grm": GRM, "ssc": SSC, "residual": RESIDUAL, "soup": SOUP, "average":
 
 
 def build(force: bool = False) -> str:
-    """Compile mc_oracle.c into libmc_oracle.so with gcc (IEEE fp64, no contraction)."""
+    """Compile mc_oracle.c into libmc_oracle.so with gcc (IEEE fp64, no contraction).
+    MC_ORACLE_LIB names a library built elsewhere from the same source (e.g. with sanitizers),
+    which is then used as it is."""
+    if os.environ.get("MC_ORACLE_LIB"):
+        return os.environ["MC_ORACLE_LIB"]
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-shared",

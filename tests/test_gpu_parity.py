@@ -155,6 +155,22 @@ def test_grm_deterministic():
         assert torch.equal(a["Y"], b["Y"]) and torch.equal(a["M"], b["M"])
 
 
+def test_ssc_routed_read_deterministic():
+    """The routed SSC read adds every token's terms in a fixed order (the online term, then
+    the selected states by ascending index), so two calls give identical bits."""
+    w, kw = SSC_SMALL["bf16_L2048_C128_k4"]
+    announce("ssc determinism")
+    inp = make_prefill(w, seed=6, **kw)
+    d = _dims(w, **kw)
+    dev = {k: to_dev(v, w.dtype) for k, v in inp.items()}
+    for online in (True, False):
+        a = mc.prefill_ssc(d, w.top_k, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"],
+                           online=online)
+        b = mc.prefill_ssc(d, w.top_k, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"],
+                           online=online)
+        assert torch.equal(a["Y"], b["Y"]) and torch.equal(a["idx"], b["idx"])
+
+
 # ---- decode -------------------------------------------------------------------------------
 
 def _decode_case(w, B, H, n, cnt, cap, seed):
