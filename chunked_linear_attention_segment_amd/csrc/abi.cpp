@@ -287,7 +287,9 @@ mc_status mc_ssc_readout(const mc_dims* d, int32_t top_k, const void* Q, const v
     const bool mfma = read_mfma_covers(*d);
     if (mfma && launch_xps(*d, X, xps, (float*)((char*)xps + xps_only(*d)), stream))
         return MC_ERR_HIP;
-    if (!mfma && launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
+    // the generic read needs the online logits
+    const bool generic = !gate_pass(*d) && !read_mfma_ssc_covers(*d, O_on != nullptr);
+    if (generic && launch_aon(*d, X, U, aon, stream)) return MC_ERR_HIP;
     if (launch_ssc_select(*d, top_k, U, X, xsum64, idx, stream)) return MC_ERR_HIP;
     if (gate_pass(*d)) {
         // the gate as its own pass, masked to the selections; the read then loads its

@@ -166,6 +166,7 @@ bool read_mfma_covers(const mc_dims& d);
 
 // The MFMA read forms the online logit itself from xps (launch_xps); the generic kernels
 // and the optional gamma output use a_on (launch_aon).
+bool read_mfma_ssc_covers(const mc_dims& d, bool online_given);
 int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* K,
                      const void* V, const void* U, const float* xps, const uint16_t* M_lo,
                      const float* P, const float* O_on, const int32_t* idx,

@@ -608,7 +608,9 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
                         qf[tb][ks][2 * e + 1] = __uint_as_float(qb[tb][ks][e] & 0xffff0000u);
                     }
         }
-    } else {
+    } else if constexpr (PRE) {
+        // (the kernels that form the gate themselves add the online term in the epilogue:
+        // seeding the accumulators here would take them out of the accumulation registers)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -784,11 +786,23 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 bf16_t* yr = Y + ((size_t)bh * L + tok[tb]) * DV + cb * 32 + hi32 * 4;
+                // the online term read from O_on (when the kernel did not form it) joins here
+                float4 o[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    o[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if constexpr (!FON)
+                        o[g] = *reinterpret_cast<const float4*>(
+                            O_on + ((size_t)bh * L + tok[tb]) * DV + cb * 32 + hi32 * 4 + g * 8);
+                }
+                const float wo = FON ? 0.f : won[tb];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     uint2 v;
-                    v.x = pack_bf16x2(acc[cb][tb][4 * g + 0] * il, acc[cb][tb][4 * g + 1] * il);
-                    v.y = pack_bf16x2(acc[cb][tb][4 * g + 2] * il, acc[cb][tb][4 * g + 3] * il);
+                    v.x = pack_bf16x2((acc[cb][tb][4 * g + 0] + wo * o[g].x) * il,
+                                      (acc[cb][tb][4 * g + 1] + wo * o[g].y) * il);
+                    v.y = pack_bf16x2((acc[cb][tb][4 * g + 2] + wo * o[g].z) * il,
+                                      (acc[cb][tb][4 * g + 3] + wo * o[g].w) * il);
                     *reinterpret_cast<uint2*>(yr + g * 8) = v;
                 }
             }
@@ -821,10 +835,16 @@ int launch_t(const mc_dims& d, int top_k, const void* Q, const void* K, const vo
 #define MC_K(FON, PHI)                                                                         \
     launch_k<DK, DV, SSC, FON, PHI, PRE>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, gw, Y, st, \
                                          sg)
-    if (O_on)
-        d.phi ? MC_K(false, 1) : MC_K(false, 0);
-    else
+    if (O_on) {
+        // the SSC kernels that form the gate themselves and take the online term given run out
+        // of registers at d_v = 128 (they would spill); their callers take another read
+        if constexpr (SSC && DV == 128)
+            return -1;
+        else
+            d.phi ? MC_K(false, 1) : MC_K(false, 0);
+    } else {
         d.phi ? MC_K(true, 1) : MC_K(true, 0);
+    }
 #undef MC_K
     return (int)hipGetLastError();
 }
@@ -835,6 +855,12 @@ int launch_t(const mc_dims& d, int top_k, const void* Q, const void* K, const vo
 bool read_mfma_covers(const mc_dims& d) {
     return d.dtype == MC_BF16 && d.d_g % 16 == 0 && d.d_g <= DG_MAX &&
            (d.d_k == 64 || d.d_k == 128) && (d.d_v == 64 || d.d_v == 128);
+}
+
+// the SSC read with the gate formed in the kernel: not for d_v = 128 with the online term
+// given (see launch_t)
+bool read_mfma_ssc_covers(const mc_dims& d, bool online_given) {
+    return read_mfma_covers(d) && !(online_given && d.d_v == 128);
 }
 
 static const SegArg kConstSegRd{};  // constant segment length

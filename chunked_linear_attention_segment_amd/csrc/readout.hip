@@ -476,7 +476,7 @@ int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K
                        const float* M,
                        const uint16_t* M_lo, const float* P, const float* O_on,
                        const int32_t* idx, void* Y, void* stream) {
-    if (read_mfma_covers(d))
+    if (read_mfma_ssc_covers(d, O_on != nullptr))
         return launch_read_mfma(d, true, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx,
                                 GateWeights{}, Y, stream);
     return launch_readout<true>(d, top_k, Q, U, aon, M, M_lo, P, O_on, idx, Y, nullptr,
@@ -620,11 +620,10 @@ struct SelRoute {
 };
 
 template <typename T, int KMAX>
-__global__ __launch_bounds__(256) void ssc_select_kernel(const T* __restrict__ U,
-                                                         const double* __restrict__ P64T, int L,
-                                                         int C, int NSP, int DG, int H, int xh,
-                                                         int top_k, int32_t* __restrict__ idx,
-                                                         const SelRoute rt) {
+__device__ __forceinline__ void ssc_select_body(const T* __restrict__ U,
+                                                const double* __restrict__ P64T, int L, int C,
+                                                int NSP, int DG, int H, int xh, int top_k,
+                                                int32_t* __restrict__ idx, const SelRoute& rt) {
     // u slab [e][token]; after the last chunk the same memory carries the lists being merged
     __shared__ __attribute__((aligned(16))) double lds[sel_lds_doubles<KMAX>()];
     double (*us)[SEL_T] = reinterpret_cast<double (*)[SEL_T]>(lds);
@@ -843,11 +842,34 @@ __global__ __launch_bounds__(256) void ssc_select_kernel(const T* __restrict__ U
 }
 
 template <typename T, int KMAX>
+__global__ __launch_bounds__(256) void ssc_select_kernel(const T* __restrict__ U,
+                                                         const double* __restrict__ P64T, int L,
+                                                         int C, int NSP, int DG, int H, int xh,
+                                                         int top_k, int32_t* __restrict__ idx,
+                                                         const SelRoute rt) {
+    ssc_select_body<T, KMAX>(U, P64T, L, C, NSP, DG, H, xh, top_k, idx, rt);
+}
+
+// Lists of up to 16 entries: four tokens' lists take about 200 registers, so this one runs
+// one wave per SIMD with the whole register file.
+template <typename T>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+ssc_select_wide_kernel(const T* __restrict__ U, const double* __restrict__ P64T, int L, int C,
+                       int NSP, int DG, int H, int xh, int top_k, int32_t* __restrict__ idx,
+                       const SelRoute rt) {
+    ssc_select_body<T, 16>(U, P64T, L, C, NSP, DG, H, xh, top_k, idx, rt);
+}
+
+template <typename T, int KMAX>
 static void launch_select_t(const mc_dims& d, int top_k, const T* U, const double* P64T, int NSP,
                             int32_t* idx, const SelRoute& rt, hipStream_t st) {
     dim3 g((d.L + SEL_T - 1) / SEL_T, d.B * d.H);
-    hipLaunchKernelGGL((ssc_select_kernel<T, KMAX>), g, dim3(256), 0, st, U, P64T, d.L,
-                       d.seg_len, NSP, d.d_g, d.H, d.x_heads, top_k, idx, rt);
+    if constexpr (KMAX == 16)
+        hipLaunchKernelGGL((ssc_select_wide_kernel<T>), g, dim3(256), 0, st, U, P64T, d.L,
+                           d.seg_len, NSP, d.d_g, d.H, d.x_heads, top_k, idx, rt);
+    else
+        hipLaunchKernelGGL((ssc_select_kernel<T, KMAX>), g, dim3(256), 0, st, U, P64T, d.L,
+                           d.seg_len, NSP, d.d_g, d.H, d.x_heads, top_k, idx, rt);
 }
 
 template <typename T>

@@ -102,6 +102,10 @@ SSC_SMALL = {
     # more candidate segments than the SSC read keeps weights for at once (96)
     "bf16_C16_120_segments_k5": (Workload("x", 1, 2, 1920, 64, 64, 64, 16, "elu1", "bf16",
                                           top_k=5, op="ssc"), {}),
+    # d_k != d_v: with the online term given, the read kernel that forms the gate itself is
+    # not used at d_v = 128 (the generic read is)
+    "bf16_dk64_dv128_k3": (Workload("x", 1, 2, 1024, 64, 128, 64, 128, "identity", "bf16",
+                                    top_k=3, op="ssc"), {}),
 }
 
 
