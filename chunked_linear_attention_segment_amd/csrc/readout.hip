@@ -597,12 +597,16 @@ __device__ __forceinline__ int sel_tok(int lane, int a) { return 128 * (a >> 1) 
 // the routing tail's per-state counters: at most this many segments
 constexpr int SEL_NS_MAX = 4096;
 
-template <int KMAX>
+template <int KMAX, int TPL>
 constexpr int sel_lds_doubles() {
-    // u slab, or: the final lists (SEL_T x KMAX scores and indices) + the per-state counters
-    return SEL_E * SEL_T > SEL_T * KMAX * 3 / 2 + (SEL_NS_MAX + 2) / 2
-               ? SEL_E * SEL_T
-               : SEL_T * KMAX * 3 / 2 + (SEL_NS_MAX + 2) / 2;
+    // TPL = 4 (one pass over the tile): the u slab, or, after it, the lists being merged and
+    // the final lists (SEL_T x KMAX scores and indices) and the per-state counters.
+    // TPL = 1 (four passes of 64 tokens): the u slab (also the merge area of a pass), then
+    // the final lists, which live across the passes, then the counters.
+    return TPL == 4 ? (SEL_E * SEL_T > SEL_T * KMAX * 3 / 2 + (SEL_NS_MAX + 2) / 2
+                           ? SEL_E * SEL_T
+                           : SEL_T * KMAX * 3 / 2 + (SEL_NS_MAX + 2) / 2)
+                    : SEL_E * SEL_T + SEL_T * KMAX * 3 / 2 + (SEL_NS_MAX + 2) / 2;
 }
 
 // Selection outputs beyond idx, for the routed read (all null: idx only).  Per token: the
@@ -619,14 +623,23 @@ struct SelRoute {
     int NS;
 };
 
-template <typename T, int KMAX>
+// TPL tokens per lane: 4 (lists of up to 8 entries), or 1 with the tile taken in four passes
+// of 64 tokens (lists of 16, which for four tokens would not stay in registers).
+template <typename T, int KMAX, int TPL>
 __device__ __forceinline__ void ssc_select_body(const T* __restrict__ U,
                                                 const double* __restrict__ P64T, int L, int C,
                                                 int NSP, int DG, int H, int xh, int top_k,
                                                 int32_t* __restrict__ idx, const SelRoute& rt) {
-    // u slab [e][token]; after the last chunk the same memory carries the lists being merged
-    __shared__ __attribute__((aligned(16))) double lds[sel_lds_doubles<KMAX>()];
+    static_assert(TPL == 4 || TPL == 1, "tokens per lane");
+    constexpr int NPT = 64 * TPL;     // tokens per pass
+    constexpr int NP = SEL_T / NPT;   // passes
+    __shared__ __attribute__((aligned(16))) double lds[sel_lds_doubles<KMAX, TPL>()];
     double (*us)[SEL_T] = reinterpret_cast<double (*)[SEL_T]>(lds);
+    // merge area of a pass ([pass-local token][KMAX]) and the final lists ([token][KMAX])
+    double* mb = lds;
+    int* mi = reinterpret_cast<int*>(mb + NPT * KMAX);
+    double* fb = TPL == 4 ? lds : lds + SEL_E * SEL_T;
+    int* fi = reinterpret_cast<int*>(fb + SEL_T * KMAX);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t bh = blockIdx.y;
@@ -635,117 +648,134 @@ __device__ __forceinline__ void ssc_select_body(const T* __restrict__ U,
     const int b = (int)(bh / H), h = (int)(bh % H);
     const size_t bx = (size_t)b * xh + (xh == 1 ? 0 : h);
     const int ntok = min(SEL_T, L - t0);
-    const int smax = (t0 + ntok - 1) / C;  // segments 0..smax-1 are candidates for some token
-    // this lane's tokens' candidate counts (0 for tokens past L)
-    int s_of[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) s_of[a] = sel_tok(lane, a) < ntok ? (t0 + sel_tok(lane, a)) / C : 0;
-    double best[4][KMAX];
-    int bi[4][KMAX];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < KMAX; ++c) { best[a][c] = -INFINITY; bi[a][c] = -1; }
     const T* Ut = U + (bh * L + t0) * DG;
     const double* Pb = P64T + bx * DG * NSP;
     // which run of a chunk a wave takes rotates from workgroup to workgroup, so that the
     // SIMDs share the work of chunks whose later runs hold no candidates
     const int run = (wave + blockIdx.x + blockIdx.y) & 3;
-    for (int c0 = 0; c0 < smax; c0 += 4 * SEL_W) {
-        const int sw = c0 + SEL_W * run;  // this wave's first segment
-        const bool act = sw < smax;
-        double acc[4][SEL_W];
+    // tile token of lane's a-th token in pass ps, and its place in the merge area
+    auto tok_of = [&](int ps, int a) { return TPL == 4 ? sel_tok(lane, a) : NPT * ps + lane; };
+    auto loc_of = [&](int a) { return TPL == 4 ? sel_tok(lane, a) : lane; };
+    for (int ps = 0; ps < NP; ++ps) {
+        const int pt0 = NPT * ps;  // first tile token of the pass
+        const int pn = min(NPT, ntok - pt0);
+        if (pn <= 0) break;
+        const int smax = (t0 + pt0 + pn - 1) / C;  // segments 0..smax-1 are candidates
+        int s_of[TPL];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < TPL; ++a)
+            s_of[a] = tok_of(ps, a) < ntok ? (t0 + tok_of(ps, a)) / C : 0;
+        double best[TPL][KMAX];
+        int bi[TPL][KMAX];
 #pragma unroll
-            for (int j = 0; j < SEL_W; ++j) acc[a][j] = 0.0;
-        for (int e0 = 0; e0 < DG; e0 += SEL_E) {
-            const int ek = min(SEL_E, DG - e0);  // a multiple of 8 (gate widths are)
-            __syncthreads();                     // the previous slab is consumed
-            for (int p = tid; p < (ek / 8) * SEL_T; p += 256) {
-                const int tok = p % SEL_T, e = 8 * (p / SEL_T);
-                double v[8];
-                if (tok < ntok)
-                    ld8_f64(Ut + (size_t)tok * DG + e0 + e, v);
-                else
+        for (int a = 0; a < TPL; ++a)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) v[j] = 0.0;
+            for (int c = 0; c < KMAX; ++c) { best[a][c] = -INFINITY; bi[a][c] = -1; }
+        for (int c0 = 0; c0 < smax; c0 += 4 * SEL_W) {
+            const int sw = c0 + SEL_W * run;  // this wave's first segment
+            const bool act = sw < smax;
+            double acc[TPL][SEL_W];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) us[e + j][tok] = v[j];
-            }
-            __syncthreads();
-            if (act) {
-                for (int e = 0; e < ek; e += SEL_EB) {
-                    const double* pr = Pb + (size_t)(e0 + e) * NSP + sw;
-                    double pv[SEL_EB][SEL_W];
+            for (int a = 0; a < TPL; ++a)
 #pragma unroll
-                    for (int q = 0; q < SEL_EB; ++q)
+                for (int j = 0; j < SEL_W; ++j) acc[a][j] = 0.0;
+            for (int e0 = 0; e0 < DG; e0 += SEL_E) {
+                const int ek = min(SEL_E, DG - e0);  // a multiple of 8 (gate widths are)
+                __syncthreads();                     // the previous slab is consumed
+                for (int p = tid; p < (ek / 8) * NPT; p += 256) {
+                    const int tok = pt0 + p % NPT, e = 8 * (p / NPT);
+                    double v[8];
+                    if (tok < ntok)
+                        ld8_f64(Ut + (size_t)tok * DG + e0 + e, v);
+                    else
 #pragma unroll
-                        for (int j = 0; j < SEL_W; ++j) pv[q][j] = pr[(size_t)q * NSP + j];
+                        for (int j = 0; j < 8; ++j) v[j] = 0.0;
 #pragma unroll
-                    for (int q = 0; q < SEL_EB; ++q) {
-                        const double2 u0 = *reinterpret_cast<const double2*>(&us[e + q][2 * lane]);
-                        const double2 u1 =
-                            *reinterpret_cast<const double2*>(&us[e + q][128 + 2 * lane]);
-                        const double uu[4] = {u0.x, u0.y, u1.x, u1.y};
+                    for (int j = 0; j < 8; ++j) us[e + j][tok] = v[j];
+                }
+                __syncthreads();
+                if (act) {
+                    for (int e = 0; e < ek; e += SEL_EB) {
+                        const double* pr = Pb + (size_t)(e0 + e) * NSP + sw;
+                        double pv[SEL_EB][SEL_W];
 #pragma unroll
-                        for (int a = 0; a < 4; ++a) {
-                            double m[SEL_W];
+                        for (int q = 0; q < SEL_EB; ++q)
 #pragma unroll
-                            for (int j = 0; j < SEL_W; ++j) m[j] = dmul_sep(uu[a], pv[q][j]);
+                            for (int j = 0; j < SEL_W; ++j) pv[q][j] = pr[(size_t)q * NSP + j];
 #pragma unroll
-                            for (int j = 0; j < SEL_W; ++j) acc[a][j] = dadd_sep(acc[a][j], m[j]);
+                        for (int q = 0; q < SEL_EB; ++q) {
+                            double uu[TPL];
+                            if constexpr (TPL == 4) {
+                                const double2 u0 =
+                                    *reinterpret_cast<const double2*>(&us[e + q][2 * lane]);
+                                const double2 u1 =
+                                    *reinterpret_cast<const double2*>(&us[e + q][128 + 2 * lane]);
+                                uu[0] = u0.x;
+                                uu[1] = u0.y;
+                                uu[2 % TPL] = u1.x;
+                                uu[3 % TPL] = u1.y;
+                            } else {
+                                uu[0] = us[e + q][pt0 + lane];
+                            }
+#pragma unroll
+                            for (int a = 0; a < TPL; ++a) {
+                                double m[SEL_W];
+#pragma unroll
+                                for (int j = 0; j < SEL_W; ++j) m[j] = dmul_sep(uu[a], pv[q][j]);
+#pragma unroll
+                                for (int j = 0; j < SEL_W; ++j)
+                                    acc[a][j] = dadd_sep(acc[a][j], m[j]);
+                            }
                         }
                     }
                 }
             }
+            if (act) {
+#pragma unroll
+                for (int a = 0; a < TPL; ++a)
+#pragma unroll
+                    for (int j = 0; j < SEL_W; ++j)
+                        if (sw + j < s_of[a])
+                            sel_insert_asc<KMAX>(best[a], bi[a], top_k, acc[a][j], sw + j);
+            }
         }
-        if (act) {
+        // waves 1..3 hand their lists to wave 0 through LDS, one wave at a time
+        for (int w = 1; w < 4; ++w) {
+            __syncthreads();
+            if (wave == w) {
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+                for (int a = 0; a < TPL; ++a)
 #pragma unroll
-                for (int j = 0; j < SEL_W; ++j)
-                    if (sw + j < s_of[a])
-                        sel_insert_asc<KMAX>(best[a], bi[a], top_k, acc[a][j], sw + j);
+                    for (int c = 0; c < KMAX; ++c) {
+                        mb[loc_of(a) * KMAX + c] = best[a][c];
+                        mi[loc_of(a) * KMAX + c] = bi[a][c];
+                    }
+            }
+            __syncthreads();
+            if (wave == 0) {
+#pragma unroll
+                for (int a = 0; a < TPL; ++a)
+#pragma unroll
+                    for (int c = 0; c < KMAX; ++c) {
+                        const int i = mi[loc_of(a) * KMAX + c];
+                        if (c < top_k && i >= 0)
+                            sel_insert<KMAX>(best[a], bi[a], top_k, mb[loc_of(a) * KMAX + c], i);
+                    }
+            }
         }
-    }
-    // waves 1..3 hand their lists to wave 0 through LDS, one wave at a time
-    double* mb = lds;                                        // [SEL_T][KMAX] scores
-    int* mi = reinterpret_cast<int*>(mb + SEL_T * KMAX);     // [SEL_T][KMAX] indices
-    for (int w = 1; w < 4; ++w) {
-        __syncthreads();
-        if (wave == w) {
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int c = 0; c < KMAX; ++c) {
-                    mb[sel_tok(lane, a) * KMAX + c] = best[a][c];
-                    mi[sel_tok(lane, a) * KMAX + c] = bi[a][c];
-                }
-        }
+        // wave 0's lists go to the final lists
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < TPL; ++a)
 #pragma unroll
                 for (int c = 0; c < KMAX; ++c) {
-                    const int i = mi[sel_tok(lane, a) * KMAX + c];
-                    if (c < top_k && i >= 0)
-                        sel_insert<KMAX>(best[a], bi[a], top_k, mb[sel_tok(lane, a) * KMAX + c], i);
+                    fb[tok_of(ps, a) * KMAX + c] = best[a][c];
+                    fi[tok_of(ps, a) * KMAX + c] = bi[a][c];
                 }
         }
     }
-    // wave 0's lists go to LDS; from here on thread t takes the tile's token t
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int c = 0; c < KMAX; ++c) {
-                mb[sel_tok(lane, a) * KMAX + c] = best[a][c];
-                mi[sel_tok(lane, a) * KMAX + c] = bi[a][c];
-            }
-    }
+    // from here on thread t takes the tile's token t
     __syncthreads();
     const int t = tid;
     const bool tv = t < ntok;
@@ -757,8 +787,8 @@ __device__ __forceinline__ void ssc_select_body(const T* __restrict__ U,
         double la[KMAX];
 #pragma unroll
         for (int c = 0; c < KMAX; ++c) {
-            li[c] = tv && c < top_k ? mi[t * KMAX + c] : -1;
-            la[c] = tv && c < top_k ? mb[t * KMAX + c] : 0.0;
+            li[c] = tv && c < top_k ? fi[t * KMAX + c] : -1;
+            la[c] = tv && c < top_k ? fb[t * KMAX + c] : 0.0;
         }
         int prev = -1;
 #pragma unroll
@@ -805,7 +835,7 @@ __device__ __forceinline__ void ssc_select_body(const T* __restrict__ U,
     }
     // counting sort of the tile's (token, segment) pairs by segment
     const int NS = rt.NS;
-    int* cnt = mi + SEL_T * KMAX;  // NS + 1 counters after the lists
+    int* cnt = fi + SEL_T * KMAX;  // NS + 1 counters after the final lists
     for (int i = tid; i <= NS; i += 256) cnt[i] = 0;
     __syncthreads();
     int slot[KMAX];
@@ -847,17 +877,15 @@ __global__ __launch_bounds__(256) void ssc_select_kernel(const T* __restrict__ U
                                                          int C, int NSP, int DG, int H, int xh,
                                                          int top_k, int32_t* __restrict__ idx,
                                                          const SelRoute rt) {
-    ssc_select_body<T, KMAX>(U, P64T, L, C, NSP, DG, H, xh, top_k, idx, rt);
+    ssc_select_body<T, KMAX, 4>(U, P64T, L, C, NSP, DG, H, xh, top_k, idx, rt);
 }
 
-// Lists of up to 16 entries: four tokens' lists take about 200 registers, so this one runs
-// one wave per SIMD with the whole register file.
+// lists of up to 16 entries: one token per lane, the tile in four passes
 template <typename T>
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void
-ssc_select_wide_kernel(const T* __restrict__ U, const double* __restrict__ P64T, int L, int C,
-                       int NSP, int DG, int H, int xh, int top_k, int32_t* __restrict__ idx,
-                       const SelRoute rt) {
-    ssc_select_body<T, 16>(U, P64T, L, C, NSP, DG, H, xh, top_k, idx, rt);
+__global__ __launch_bounds__(256) void ssc_select_wide_kernel(
+    const T* __restrict__ U, const double* __restrict__ P64T, int L, int C, int NSP, int DG,
+    int H, int xh, int top_k, int32_t* __restrict__ idx, const SelRoute rt) {
+    ssc_select_body<T, 16, 1>(U, P64T, L, C, NSP, DG, H, xh, top_k, idx, rt);
 }
 
 template <typename T, int KMAX>
