@@ -119,29 +119,88 @@ def med(x):
     return float(np.median(np.asarray(x)))
 
 
-def src_hash():
+# The sources each stored traffic figure depends on (the call's kernels and what they include)
+CALL_SOURCES = {
+    "grm_readout": ["abi.cpp", "common.cuh", "mc_internal.h", "gate.hip", "read_mfma.hip",
+                    "readout.hip"],
+    "decode_step": ["abi.cpp", "common.cuh", "mc_internal.h", "decode.hip"],
+    "ssc_readout": ["abi.cpp", "common.cuh", "mc_internal.h", "readout.hip", "ssc_gather.hip"],
+}
+# the kernels of each call, by name fragment, as rocprofv3 lists them
+CALL_KERNELS = {
+    "grm_readout": ["xps_kernel", "pfrag_kernel", "gate_w_kernel", "grm_read_kernel"],
+    "decode_step": ["decode_read_kernel", "decode_combine_kernel"],
+    "ssc_readout": ["aon_kernel", "seg_mean64_kernel", "ssc_select", "frag_states_kernel",
+                    "ssc_gather_kernel"],
+}
+
+
+def src_hash(files):
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "chunked_linear_attention_segment_amd", "csrc"))):
+    for f in sorted(files):
         with open(os.path.join(ROOT, "chunked_linear_attention_segment_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel sources (else None).  The value is a stored profile figure, not a
+def load_traffic(call: str, workload: str):
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it was taken on the
+    call's current kernel sources (else None).  The value is a stored profile figure, not a
     measurement of this run; the JSON line says so next to it."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         rec = json.load(open(p))
-        ent = rec.get(kernel, {}).get(workload)
-        if ent and ent.get("src_hash") == src_hash():
+        ent = rec.get(call, {}).get(workload)
+        if ent and ent.get("src_hash") == src_hash(CALL_SOURCES[call]):
             return ent["bytes_per_launch"]
     except Exception:
         return None
     return None
+
+
+def counters_summary(root: str, calib_mib: int) -> None:
+    """Write profiles/traffic.json from rocprofv3 counter runs under `root`: one directory per
+    (counter, run) named fetch_<run> / write_<run>, runs prefill, decode, ssc and calib (the
+    copy kernel of calib_mib MiB).  Per kernel, the mean FETCH_SIZE / WRITE_SIZE (KiB) per
+    dispatch, scaled by what the copy kernel reads for its known bytes; per call, the sum over
+    its kernels (each runs once per call)."""
+    import csv
+    import glob
+
+    def per_kernel(run):
+        disp = {}
+        for f in glob.glob(os.path.join(root, run, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                k = disp.setdefault(r["Kernel_Name"], {})
+                k[r["Dispatch_Id"]] = k.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return {n: sum(v.values()) / len(v) for n, v in disp.items()}
+
+    n = calib_mib << 20
+    cf, cw = per_kernel("fetch_calib"), per_kernel("write_calib")
+    copy = [k for k in cf if "copy16" in k][0]
+    fetch_factor, write_factor = n / (cf[copy] * 1024), n / (cw[copy] * 1024)
+    out = {"calibration": {"kernel": "libmcpeak copy16_kernel, %d MiB read + %d MiB written"
+                           % (calib_mib, calib_mib),
+                           "fetch_factor": fetch_factor, "write_factor": write_factor}}
+    for call, run, workload in (("grm_readout", "prefill", "grm_bf16_L64K"),
+                                ("decode_step", "decode", "decode_bf16_64x32_n256"),
+                                ("ssc_readout", "ssc", "ssc_bf16_L16K_k4")):
+        f, w = per_kernel("fetch_" + run), per_kernel("write_" + run)
+        kern = {}
+        for name in f:
+            if any(frag in name for frag in CALL_KERNELS[call]) and name in w:
+                short = name.replace("(anonymous namespace)::", "").split("(")[0]
+                short = short.replace("void ", "")
+                kern[short] = {"fetch_kib": f[name], "write_kib": w[name],
+                               "bytes": f[name] * 1024 * fetch_factor + w[name] * 1024 * write_factor}
+        out[call] = {workload: {"kernels": kern,
+                                "bytes_per_launch": sum(k["bytes"] for k in kern.values()),
+                                "src_hash": src_hash(CALL_SOURCES[call])}}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 TRAFFIC_SOURCE = ("stored, not measured in this run: profiles/traffic.json (rocprofv3 FETCH_SIZE "
@@ -178,7 +237,15 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="profiling aid: copy a MIB-sized device buffer 3 times and exit (the "
                          "reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--counters-summary", metavar="DIR",
+                    help="write profiles/traffic.json from the rocprofv3 FETCH_SIZE / "
+                         "WRITE_SIZE runs under DIR (fetch_<run>, write_<run> for prefill, "
+                         "decode, ssc and calib, the copy kernel of --calibrate-copy MiB) and "
+                         "exit")
     args = ap.parse_args()
+    if args.counters_summary:
+        counters_summary(args.counters_summary, args.calibrate_copy or 1024)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1",
               file=sys.stderr)
@@ -417,7 +484,9 @@ def run_ssc(args, rec, dev):
                                "what": "whole step against max(FLOPs / 2.5 PFLOP/s, bytes / 8 TB/s)",
                                "achieved": round(by / (ms / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                                "unit": "GB/s", "frac": round(t_min / (ms / 1e3), 4),
-                               "algorithmic_flops": fl, "algorithmic_bytes": by}}
+                               "algorithmic_flops": fl, "algorithmic_bytes": by,
+                               "traffic_readout": load_traffic("ssc_readout", w.name),
+                               "traffic_source": TRAFFIC_SOURCE}}
     del inp, M, M_lo, P, O_on, Y, idx, ws
     torch.cuda.empty_cache()
 
