@@ -9,9 +9,10 @@
 //   dgamma_t^(i) = <dy_t, M^(i) phi(q_t)>: bwd_dgamma_kernel, per 256-token tile, streams the
 //     states through LDS and contracts each with the tile's phi(q) on MFMA, then reduces the
 //     products against dy in registers.
-//   dM^(i) = sum_t gamma_t^(i) dy_t phi(q_t)^T: bwd_dm_mfma_kernel, per cached segment, walks
-//     the later tokens in chunks of 64 (the scan's state-update contraction with phi(q) in
-//     place of phi(k) and gamma dy in place of v).
+//   dM^(i) = sum_t gamma_t^(i) dy_t phi(q_t)^T: bwd_dm_mfma_kernel, per group of four cached
+//     segments and range of later tokens, walks the tokens in chunks of 64 (the scan's
+//     state-update contraction with phi(q) in place of phi(k) and gamma dy in place of v),
+//     and dP_i = sum_t da_t^(i) u_t beside it; dM is stored transposed.
 //   bwd_gate_fast_kernel: the softmax backward from the gate numerators W, 1/l and the online
 //     weight (gamma_i = W_i / l), dgamma of the online segment, du_t and dq.
 #include "common.cuh"
@@ -173,39 +174,115 @@ __global__ __launch_bounds__(256, 1) void bwd_dgamma_kernel(
 }
 
 constexpr int CHK = 64;    // tokens per chunk of the dM walk
-constexpr int TPAD = 72;   // row stride (bf16) of the token-indexed LDS tiles
+constexpr int TPAD = 72;   // row stride (bf16) of the token-indexed LDS tiles: 144 bytes
 
-constexpr int SPW = 4;        // cached segments per dM workgroup (8 waves: 2 per segment)
-constexpr int DM_SPLIT = 8;   // most workgroups that share one group's later tokens
-constexpr int DM_CHUNKS = 128;  // chunks a workgroup aims for
+constexpr int SPW = 4;          // cached segments per dM workgroup (8 waves: 2 per segment)
+constexpr int DM_CHUNKS = 128;  // chunks of 64 tokens per token range of the dM walk
 
-// dM^(i) (stored [c][r] like the states) for d_k = d_v = 128 and d_g <= 128, SPW consecutive
-// segments i0.. per workgroup so that each later token is staged once for all of them:
-// dM^T[r][c] += sum_t phi(q_t)[r] (gamma_t^(i) dy_t[c]).  Wave w serves segment i0 + w / 2 and
-// value columns c in [64 (w % 2), +64), keeping the four 32-row blocks of r for its two
-// 32-column blocks in its accumulators.  phi(q)^T (shared) and (gamma^(i) dy)^T (one per
-// segment) are staged in LDS with token pairs packed in 32-bit words (the token index is the
-// contraction index); the next chunk's rows are loaded into registers while the current one
-// is contracted.  gamma_t^(i) = W_t^(i) / l_t from the forward gate pass, zero unless token t
-// lies after segment i.  Alongside, dP_i of this head = sum_t da_t^(i) u_t.  The later tokens
-// of a group are split over up to DM_SPLIT workgroups (blockIdx.z) of about DM_CHUNKS chunks,
-// so the first groups do not set the length of the launch; each adds its partial dM and dP
-// into the zero-filled outputs (fp32 atomic adds: the order of the partial sums varies).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// dM^(i) (stored transposed, [r][c]) for d_k = d_v = 128 and d_g <= 128, SPW consecutive
+// segments i0.. (a group) per workgroup: dM^T[r][c] += sum_t phi(q_t)[r] (gamma_t^(i) dy_t[c]),
+// and dP_i of this head = sum_t da_t^(i) u_t.  A chunk of 64 later tokens is staged once in LDS
+// for all the segments, transposed so that the token index (the contraction index) runs along
+// the rows: phi(q)^T, dy^T, u^T (token pairs packed in 32-bit words), gamma_t^(i0+k) =
+// W_t^(i0+k) / l_t from the forward gate pass (zero unless token t lies after segment i0+k)
+// and da_t^(i0+k) split into a bf16 high part and the bf16 rest.  Wave w serves segment
+// i0 + w / 2 and value columns c in [64 (w % 2), +64): it scales its own dy^T fragments by
+// gamma in registers and keeps the four 32-row blocks of r for its two 32-column blocks in
+// its accumulators.  dP runs on 16x16x32 MFMAs: rows 0..3 the high parts of the SPW segments'
+// da, rows 4..7 the rest (rows 8..15 zero), columns the 16 gate columns of wave w; the two
+// halves are added at the end.  The tiles are double-buffered and the next chunk's rows are
+// loaded into registers while the current one is contracted, so a chunk takes one barrier.
+//
+// Work items: the token axis is cut into ranges of DM_CHUNKS chunks; a workgroup takes one
+// (token range, group, head) and walks the range's tokens after the group (items whose range
+// ends before the group's later tokens begin exit at once).  Items are numbered head fastest,
+// so the workgroups dealt round-robin to the 8 XCDs run, on each XCD, the same range and
+// groups of a few heads side by side: their token chunks are read from HBM about once per
+// head and served to the other groups from that XCD's L2.  Every item adds its partial dM
+// and dP into the zero-filled outputs (fp32 atomic adds, the order of the partial sums
+// varies); dM^T puts the 32 lanes of a row block on one 128-byte line.
 __global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ dY, const uint16_t* __restrict__ Wg,
     const float* __restrict__ inv_l, const bf16_t* __restrict__ U,
-    const float* __restrict__ daT, int L, int C, int NS, int DG, int H, int xh, int phi,
+    const float* __restrict__ daT, int BH, int L, int C, int NS, int DG, int H, int xh, int phi,
     float* __restrict__ dM, float* __restrict__ dP) {
-    __shared__ __attribute__((aligned(16))) bf16_t qt[128][TPAD];       // phi(q)^T [r][t]
-    __shared__ __attribute__((aligned(16))) bf16_t gt[SPW][128][TPAD];  // (gamma dy)^T [c][t]
-    __shared__ __attribute__((aligned(16))) bf16_t su[CHK][128];        // u_t
-    __shared__ float sda[SPW][CHK];
-    const int i0 = blockIdx.x * SPW;  // low segments (the most tokens) are dispatched first
-    const size_t bh = blockIdx.y;
+    __shared__ __attribute__((aligned(16))) bf16_t qt[2][128][TPAD];  // phi(q)^T [r][t]
+    __shared__ __attribute__((aligned(16))) bf16_t yt[2][128][TPAD];  // dy^T [c][t]
+    __shared__ __attribute__((aligned(16))) bf16_t ut[2][128][TPAD];  // u^T [e][t]
+    __shared__ __attribute__((aligned(16))) float sg[2][SPW][CHK];     // gamma [segment][t]
+    __shared__ __attribute__((aligned(16))) bf16_t sda[2][16][TPAD];   // da split [row][t]
+    const int NG = (NS + SPW - 1) / SPW;
+    const size_t bh = blockIdx.x % BH;
+    const int grp = (blockIdx.x / BH) % NG, range = blockIdx.x / BH / NG;
+    const int i0 = grp * SPW;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, half = lane >> 5;
+    const int l16 = lane & 15, q4 = lane >> 4;
     const int T = (L + kGateTile - 1) / kGateTile;
-    const int DG8 = DG / 8;
     const int nseg = min(SPW, NS - i0);
+
+    // the chunks [c_lo, c_hi) of the range that hold tokens after the group (64-token chunks
+    // from token 0; the tokens of the first chunk up to segment i0 + k have gamma = da = 0)
+    const int first0 = (i0 + 1) * C;
+    const int c_lo = max(range * DM_CHUNKS, first0 / CHK);
+    const int c_hi = min((range + 1) * DM_CHUNKS, (L + CHK - 1) / CHK);
+    if (first0 >= L || c_lo >= c_hi) return;  // uniform: no later token in this range
+    const int first = c_lo * CHK;
+    const int nchunk = c_hi - c_lo;
+
+    // staging roles: token pair (2p, 2p + 1) and columns dc..dc + 7 of q, dy and u; threads
+    // 0..255 one gamma (segment kg, token tg), threads 256..511 one da
+    const int p = tid & 31, dc = (tid >> 5) * 8;
+    const int dcu = min(dc, DG - 8);  // u columns clamped into the row (stored only if dc < DG)
+    const int kg = (tid >> 6) & 3, tg = tid & 63;
+    const int ig = min(i0 + kg, NS - 1);
+    // one chunk in registers (raw loaded values only: anything computed from them here would
+    // wait for the loads).  Rows past L are read at L - 1 and cancelled by gamma = da = 0.
+    u32x4_t rq[2], ry[2], ru[2];
+    uint32_t rw = 0u;
+    float rx = 0.f;  // 1 / l_t (threads 0..255) or da (threads 256..511)
+    auto load = [&](int j0) {
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+            const size_t row = bh * L + min(j0 + 2 * p + o, L - 1);
+            rq[o] = *reinterpret_cast<const u32x4_t*>(Q + row * 128 + dc);
+            ry[o] = *reinterpret_cast<const u32x4_t*>(dY + row * 128 + dc);
+            ru[o] = *reinterpret_cast<const u32x4_t*>(U + row * DG + dcu);
+        }
+        // every thread issues the same loads (no branch around a load)
+        const int t = min(j0 + tg, L - 1);
+        rw = Wg[((bh * T + t / kGateTile) * NS + ig) * kGateTile + t % kGateTile];
+        rx = *(tid < 256 ? inv_l + bh * L + t : daT + (bh * NS + ig) * L + t);
+    };
+    auto pack_pairs = [&](bf16_t (*dst)[TPAD], const u32x4_t& a, const u32x4_t& b) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            *reinterpret_cast<uint32_t*>(&dst[dc + 2 * e][2 * p]) = (a[e] & 0xffffu) | (b[e] << 16);
+            *reinterpret_cast<uint32_t*>(&dst[dc + 2 * e + 1][2 * p]) =
+                (a[e] >> 16) | (b[e] & 0xffff0000u);
+        }
+    };
+    auto stage = [&](int buf, int j0) {
+        pack_pairs(qt[buf], phi8(rq[0], phi), phi8(rq[1], phi));
+        pack_pairs(yt[buf], ry[0], ry[1]);
+        if (dc < DG) pack_pairs(ut[buf], ru[0], ru[1]);
+        const int t = j0 + tg;
+        const bool later = t < L && t / C > i0 + kg && kg < nseg;
+        if (tid < 256) {
+            sg[buf][kg][tg] = later ? bf16_to_f32((bf16_t)rw) * rx : 0.f;
+        } else {
+            const float da = later ? rx : 0.f;
+            const bf16_t hi = f32_to_bf16(da);
+            sda[buf][kg][tg] = hi;
+            sda[buf][SPW + kg][tg] = f32_to_bf16(da - bf16_to_f32(hi));
+        }
+    };
+
     f32x16_t mt[4][2];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -213,143 +290,80 @@ __global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mt[db][cb][r] = 0.f;
-    // dP: thread (k, e) = (tid / 128, tid % 128) sums column e of segment i0 + k
-    const int kdp = tid >> 7, edp = tid & 127;
-    float dp0 = 0.f, dp1 = 0.f, dp2 = 0.f, dp3 = 0.f;
+    f32x4_t pacc = {0.f, 0.f, 0.f, 0.f};
+    const int k = wave >> 1, c0 = (wave & 1) * 64, e0 = wave * 16;
 
-    // one chunk in registers: staging slot (token pair 2p, 2p+1; columns dc..dc+7) of phi(q)
-    // and dy, the SPW gate weights of both tokens, two slots of u rows, one da
-    // (raw loaded values only: anything computed from them here would wait for the loads)
-    u32x4_t rq[2], ry[2], ru[2];
-    uint32_t rw[2][SPW];
-    float ril[2], rda = 0.f;
-    auto load = [&](int j0) {
-        const int n = min(CHK, L - j0);
-        const int p = tid % (CHK / 2), dc = (tid / (CHK / 2)) * 8;
-#pragma unroll
-        for (int o = 0; o < 2; ++o) {
-            const int r = 2 * p + o, t = j0 + r;
-            u32x4_t q = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-            float il = 0.f;
-#pragma unroll
-            for (int k = 0; k < SPW; ++k) rw[o][k] = 0u;
-            if (r < n) {
-                const size_t row = bh * L + t;
-                q = *reinterpret_cast<const u32x4_t*>(Q + row * 128 + dc);
-                y = *reinterpret_cast<const u32x4_t*>(dY + row * 128 + dc);
-                il = inv_l[row];
-                const int st = t / C;
-                const uint16_t* wr = Wg + ((bh * T + t / kGateTile) * NS) * kGateTile + t % kGateTile;
-#pragma unroll
-                for (int k = 0; k < SPW; ++k)
-                    if (i0 + k < st) rw[o][k] = wr[(size_t)(i0 + k) * kGateTile];
-            }
-            rq[o] = q;
-            ry[o] = y;
-            ril[o] = il;
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int it = tid + 512 * k, tt = it / DG8, e8 = (it % DG8) * 8;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (tt < n) v = *reinterpret_cast<const u32x4_t*>(U + (bh * L + j0 + tt) * DG + e8);
-            ru[k] = v;
-        }
-        {  // da_t^(i0+k): thread (k, tt) = (tid / 64, tid % 64) for tid < SPW * 64
-            const int k = tid / CHK, tt = tid % CHK, t = j0 + tt;
-            rda = (k < nseg && tt < n && t / C > i0 + k) ? daT[(bh * NS + i0 + k) * L + t] : 0.f;
-        }
-    };
-    // this workgroup's share of the group's later tokens: chunks [z cpz, (z + 1) cpz)
-    const int first0 = (i0 + 1) * C;
-    const int nch = first0 < L ? (L - first0 + CHK - 1) / CHK : 0;
-    const int nsplit = min(DM_SPLIT, max(1, (nch + DM_CHUNKS - 1) / DM_CHUNKS));
-    const int cpz = (nch + nsplit - 1) / nsplit;
-    const int z = blockIdx.z;
-    if (z >= nsplit || z * cpz >= nch) return;  // uniform: no work for this split
-    const int first = first0 + z * cpz * CHK;
-    const int stop = min(L, first0 + (z + 1) * cpz * CHK);
+    // rows 8..15 of the da tiles stay zero
+    for (int e = tid; e < 2 * 8 * TPAD; e += 512)
+        sda[e / (8 * TPAD)][8 + (e / TPAD) % 8][e % TPAD] = (bf16_t)0;
     load(first);
-    for (int j0 = first; j0 < stop; j0 += CHK) {
-        const int n = min(CHK, L - j0);
-        {  // registers -> LDS
-            const int p = tid % (CHK / 2), dc = (tid / (CHK / 2)) * 8, r0 = 2 * p;
-            const u32x4_t a = phi8(rq[0], phi), b = phi8(rq[1], phi);
+    stage(0, first);
+    if (nchunk > 1) load(first + CHK);
+    __syncthreads();
+    for (int ch = 0; ch < nchunk; ++ch) {
+        const int buf = ch & 1;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                *reinterpret_cast<uint32_t*>(&qt[dc + 2 * e][r0]) = (a[e] & 0xffffu) | (b[e] << 16);
-                *reinterpret_cast<uint32_t*>(&qt[dc + 2 * e + 1][r0]) = (a[e] >> 16) | (b[e] & 0xffff0000u);
-            }
+        for (int ks = 0; ks < CHK / 16; ++ks) {
+            const int t8 = ks * 16 + half * 8;
+            const float4 g0 = *reinterpret_cast<const float4*>(&sg[buf][k][t8]);
+            const float4 g1 = *reinterpret_cast<const float4*>(&sg[buf][k][t8 + 4]);
+            const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            u32x4_t gb[2];
 #pragma unroll
-            for (int k = 0; k < SPW; ++k) {
-                const float g0 = bf16_to_f32((bf16_t)rw[0][k]) * ril[0];
-                const float g1 = bf16_to_f32((bf16_t)rw[1][k]) * ril[1];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    *reinterpret_cast<uint32_t*>(&gt[k][dc + 2 * e][r0]) =
-                        pack_bf16x2(g0 * bf_lo(ry[0][e]), g1 * bf_lo(ry[1][e]));
-                    *reinterpret_cast<uint32_t*>(&gt[k][dc + 2 * e + 1][r0]) =
-                        pack_bf16x2(g0 * bf_hi(ry[0][e]), g1 * bf_hi(ry[1][e]));
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int it = tid + 512 * k, tt = it / DG8, e8 = (it % DG8) * 8;
-                if (tt < CHK) *reinterpret_cast<u32x4_t*>(&su[tt][e8]) = ru[k];
-            }
-            if (tid < SPW * CHK) sda[tid / CHK][tid % CHK] = rda;
-        }
-        __syncthreads();
-        if (j0 + CHK < stop) load(j0 + CHK);  // the next chunk's loads overlap this chunk's work
-        const int k = wave >> 1, c0 = (wave & 1) * 64;
-        u32x4_t gb[2][CHK / 16];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int ks = 0; ks < CHK / 16; ++ks)
-                gb[cb][ks] = *reinterpret_cast<const u32x4_t*>(&gt[k][c0 + cb * 32 + l32][ks * 16 + half * 8]);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int r = db * 32 + l32;
-#pragma unroll
-            for (int ks = 0; ks < CHK / 16; ++ks) {
-                const u32x4_t qa = *reinterpret_cast<const u32x4_t*>(&qt[r][ks * 16 + half * 8]);
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) mt[db][cb] = mfma32(qa, gb[cb][ks], mt[db][cb]);
-            }
-        }
-        if (edp < DG) {
-            int tt = 0;
-            for (; tt + 3 < n; tt += 4) {
-                dp0 += sda[kdp][tt] * bf16_to_f32(su[tt][edp]);
-                dp1 += sda[kdp][tt + 1] * bf16_to_f32(su[tt + 1][edp]);
-                dp2 += sda[kdp][tt + 2] * bf16_to_f32(su[tt + 2][edp]);
-                dp3 += sda[kdp][tt + 3] * bf16_to_f32(su[tt + 3][edp]);
-            }
-            for (; tt < n; ++tt) dp0 += sda[kdp][tt] * bf16_to_f32(su[tt][edp]);
-        }
-        __syncthreads();
-    }
-    const int b = (int)(bh / H), h = (int)(bh % H);
-    const size_t rgi = xh == 1 ? h : 0, bx = xh == 1 ? b : bh;
-    const size_t nbx = (size_t)(gridDim.y / H) * xh;
-    if (kdp < nseg && edp < DG)
-        unsafeAtomicAdd(&dP[((rgi * NS + i0 + kdp) * nbx + bx) * DG + edp],
-                        (dp0 + dp1) + (dp2 + dp3));
-    // dM[c][r]: lane holds c = c0 + 32 cb + l32 and r = 32 db + 8g + 4 half + e
-    const int k = wave >> 1, c0 = (wave & 1) * 64;
-    if (k >= nseg) return;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        float* out = dM + ((bh * NS + i0 + k) * 128 + c0 + cb * 32 + l32) * (size_t)128;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
+            for (int cb = 0; cb < 2; ++cb) {
+                const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(&yt[buf][c0 + cb * 32 + l32][t8]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    unsafeAtomicAdd(out + db * 32 + 8 * g + 4 * half + e, mt[db][cb][4 * g + e]);
+                    gb[cb][e] = pack_bf16x2(g[2 * e] * bf_lo(raw[e]), g[2 * e + 1] * bf_hi(raw[e]));
+            }
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const u32x4_t qa = *reinterpret_cast<const u32x4_t*>(&qt[buf][db * 32 + l32][t8]);
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) mt[db][cb] = mfma32(qa, gb[cb], mt[db][cb]);
+            }
+        }
+        if (e0 < DG) {
+#pragma unroll
+            for (int ks = 0; ks < CHK / 32; ++ks) {
+                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&sda[buf][l16][ks * 32 + q4 * 8]);
+                const u32x4_t b = *reinterpret_cast<const u32x4_t*>(&ut[buf][e0 + l16][ks * 32 + q4 * 8]);
+                pacc = mfma16(a, b, pacc);
+            }
+        }
+        if (ch + 1 < nchunk) {
+            // the other buffer was last read before the previous barrier
+            stage(buf ^ 1, first + (ch + 1) * CHK);
+            if (ch + 2 < nchunk) load(first + (ch + 2) * CHK);
+        }
+        __syncthreads();
     }
+    // dP: lane l16 of rows 0..3 (lanes 0..15) plus the rest in rows 4..7 (lanes 16..31)
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const size_t rgi = xh == 1 ? h : 0, bx = xh == 1 ? b : bh;
+    const size_t nbx = (size_t)(BH / H) * xh;
+    f32x4_t rest;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rest[j] = __shfl_down(pacc[j], 16);
+    if (e0 < DG && q4 == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (j < nseg)
+                unsafeAtomicAdd(&dP[((rgi * NS + i0 + j) * nbx + bx) * DG + e0 + l16], pacc[j] + rest[j]);
+    }
+    // dM^T[r][c]: lane holds c = c0 + 32 cb + l32 and r = 32 db + 8g + 4 half + e
+    if (k >= nseg) return;
+    float* out = dM + (bh * NS + i0 + k) * (size_t)(128 * 128) + c0 + l32;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    unsafeAtomicAdd(out + (size_t)(db * 32 + 8 * g + 4 * half + e) * 128 + cb * 32,
+                                    mt[db][cb][4 * g + e]);
 }
 
 // The softmax backward from the gate pass: gamma_i = W_t^(i) / l_t (i < s),
@@ -503,10 +517,10 @@ int launch_bwd_fast(const mc_dims& d, const BwdBuffers& w, const void* Q, const 
     const size_t ndp = (size_t)d.B * d.H * NS * d.d_g;  // [H or 1][NS][B*xh][dg]
     hipLaunchKernelGGL(zero_kernel, dim3(2048), dim3(256), 0, st, w.dM, ndm);
     hipLaunchKernelGGL(zero_kernel, dim3(256), dim3(256), 0, st, w.dpp, ndp);
-    hipLaunchKernelGGL(bwd_dm_mfma_kernel, dim3((NS + SPW - 1) / SPW, BH, DM_SPLIT), dim3(512), 0, st,
-                       (const bf16_t*)Q,
-                       (const bf16_t*)dY, w.W, w.inv_l, (const bf16_t*)U, w.daT, d.L, d.seg_len,
-                       NS, d.d_g, d.H, d.x_heads, d.phi, w.dM, w.dpp);
+    const int nranges = ((d.L + CHK - 1) / CHK + DM_CHUNKS - 1) / DM_CHUNKS;
+    hipLaunchKernelGGL(bwd_dm_mfma_kernel, dim3(nranges * ((NS + SPW - 1) / SPW) * BH), dim3(512),
+                       0, st, (const bf16_t*)Q, (const bf16_t*)dY, w.W, w.inv_l, (const bf16_t*)U,
+                       w.daT, BH, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads, d.phi, w.dM, w.dpp);
     return (int)hipGetLastError();
 }
 

@@ -92,7 +92,7 @@ struct BwdBuffers {
     float* D;      // [B,H,L] sum_i gamma_i dgamma_i
     float* gs;     // [B,H,L] online weight gamma_s
     float* dG;     // [B,H,L,NS] dgamma, then da
-    float* dM;     // [B,H,NS,dv,dk] gradient of each cached state
+    float* dM;     // [B,H,NS,dv,dk] gradient of each cached state ([B,H,NS,dk,dv] on MFMA)
     float* dpp;    // [NR,NS,B*xh,dg] partial sums of dP_i over token ranges
     // the MFMA path (bf16, d_k = d_v = 128 with the forward gate pass):
     uint16_t* W;   // gate numerators per read tile (gate pass layout)

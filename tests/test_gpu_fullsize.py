@@ -275,17 +275,18 @@ def test_backward_full_size_L64K():
 
 
 def test_backward_split_dm_walk():
-    # The dM / dP walk gives each group of four cached segments up to 8 workgroups when its
-    # later tokens span more than 128 chunks of 64 (8192 tokens); their partial sums are added
-    # into dM and dP.  At L = 20480, C = 512 the groups starting at segments 0 and 4 have 312
-    # and 280 later chunks (3 workgroups each) and the next four groups 2 each, so every
+    # The dM / dP walk cuts the token axis into ranges of 128 chunks of 64 tokens (8192
+    # tokens); each group of four cached segments gets one workgroup per range that holds
+    # some of its later tokens, and their partial sums are added into dM and dP.  At
+    # L = 20480, C = 512 the first four groups span 3 ranges, the next four 2, so every
     # gradient, compared element by element with the oracle, depends on the split sums.  The
     # fp32 states are not passed (M = NULL): the bf16 call reads only their bf16 copy.
     from chunked_linear_attention_segment_amd.inputs import Workload
     w = Workload("bwd_split", 1, 2, 20480, 128, 128, 128, 512, "identity", "bf16",
                  recipe="l2norm")
-    later_chunks = [(w.L - (i0 + 1) * w.seg_len + 63) // 64 for i0 in range(0, 24, 4)]
-    assert [-(-n // 128) for n in later_chunks] == [3, 3, 2, 2, 2, 2]
+    items = [len({c // 128 for c in range((i0 + 1) * w.seg_len // 64, -(-w.L // 64))})
+             for i0 in range(0, 40, 4)]
+    assert items == [3, 3, 3, 3, 2, 2, 2, 2, 1, 1]
     announce("backward, split dM walk: B=%d H=%d L=%d C=%d" % (w.B, w.H, w.L, w.seg_len))
     inp = make_prefill_device(w, seed=4)
     dY = torch.from_numpy(make_upstream_grad(w.B, w.H, w.L, w.d_v, seed=5,
