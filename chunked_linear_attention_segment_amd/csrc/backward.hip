@@ -256,13 +256,12 @@ __global__ __launch_bounds__(256) void bwd_dm_kernel(
 
 // Per segment, tokens in reverse: E = dM^(i) + sum_{t >= r} gamma_t^(s) dy_t phi(q_t)^T kept
 // twice -- E (row c per thread group, for dv_r = E phi(k_r)) and E^T (row r per thread group,
-// for dphi(k_r) = E^T v_r) -- so both reads reduce only within a thread group.  dM is stored
-// [c][r] (dmt = 0, like the states) or transposed [r][c] (dmt = 1, the MFMA walk's layout).
+// for dphi(k_r) = E^T v_r) -- so both reads reduce only within a thread group.
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void bwd_online_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dY, const float* __restrict__ gs_i, const float* __restrict__ dM,
-    int dmt, int L, int C, int NS, int phi, float* __restrict__ dK, float* __restrict__ dV) {
+    int L, int C, int NS, int phi, float* __restrict__ dK, float* __restrict__ dV) {
     constexpr int TA = 256 / DV, CA = DK / TA;  // E:   row c = tid / TA, columns ra..ra+CA
     constexpr int TB = 256 / DK, CB = DV / TB;  // E^T: row r = tid / TB, columns cb..cb+CB
     __shared__ float sq[BTT][DK];
@@ -279,9 +278,9 @@ __global__ __launch_bounds__(256) void bwd_online_kernel(
     const float* dMi = dM + (bh * NS + s) * (size_t)(DV * DK);
     float ea[CA], eb[CB];
 #pragma unroll
-    for (int k = 0; k < CA; ++k) ea[k] = dmt ? dMi[(size_t)(ra + k) * DV + c] : dMi[(size_t)c * DK + ra + k];
+    for (int k = 0; k < CA; ++k) ea[k] = dMi[(size_t)c * DK + ra + k];
 #pragma unroll
-    for (int k = 0; k < CB; ++k) eb[k] = dmt ? dMi[(size_t)r * DV + cb + k] : dMi[(size_t)(cb + k) * DK + r];
+    for (int k = 0; k < CB; ++k) eb[k] = dMi[(size_t)(cb + k) * DK + r];
     const int ntile = (len + BTT - 1) / BTT;
     for (int tile = ntile - 1; tile >= 0; --tile) {
         const int j0 = t0 + tile * BTT;
@@ -431,9 +430,14 @@ int launch_bwd_t(const mc_dims& d, const BwdBuffers& w, const void* Q, const voi
                            (const T*)Q, (const T*)U, P, w.lse, (const T*)dY, d.L, d.seg_len, NS,
                            d.d_g, d.H, d.x_heads, d.phi, w.dM);
     }
-    hipLaunchKernelGGL((bwd_online_kernel<T, DK, DV>), dim3(NS, d.B * d.H), dim3(256), 0, st,
-                       (const T*)Q, (const T*)K, (const T*)V, (const T*)dY, w.gs, w.dM,
-                       fast ? 1 : 0, d.L, d.seg_len, NS, d.phi, dK, dV);
+    if (fast) {
+        const int rc = launch_bwd_online_mfma(d, w, Q, K, V, dY, dK, dV, st);
+        if (rc) return rc;
+    } else {
+        hipLaunchKernelGGL((bwd_online_kernel<T, DK, DV>), dim3(NS, d.B * d.H), dim3(256), 0, st,
+                           (const T*)Q, (const T*)K, (const T*)V, (const T*)dY, w.gs, w.dM,
+                           d.L, d.seg_len, NS, d.phi, dK, dV);
+    }
     // x gradients; the prefix sums of X are no longer needed, so w_t goes in their place
     const int bxn = d.B * d.x_heads;
     hipLaunchKernelGGL((bwd_dxw_kernel<T>), dim3((d.L + 63) / 64, bxn), dim3(256), 0, st,

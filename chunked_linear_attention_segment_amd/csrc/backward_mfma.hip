@@ -366,6 +366,226 @@ __global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
                                     mt[db][cb][4 * g + e]);
 }
 
+constexpr int OT = 64;     // tokens per r tile and per t tile of the online-segment backward
+constexpr int NPAD = 136;  // row stride (bf16) of the token-major LDS tiles: 272 bytes
+
+// dM^T (fp32, [r][c]) -> dM (bf16, [c][r]) per cached state, 32 x 32 tiles through LDS
+__global__ __launch_bounds__(256) void dm_cr_kernel(const float* __restrict__ dMT,
+                                                   bf16_t* __restrict__ dMc) {
+    __shared__ float tile[32][33];
+    const size_t st = blockIdx.x;
+    const int r0 = blockIdx.y * 32, c0 = blockIdx.z * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    const float* src = dMT + st * (128 * 128);
+    bf16_t* dst = dMc + st * (128 * 128);
+    for (int y = ty; y < 32; y += 8) tile[y][tx] = src[(size_t)(r0 + y) * 128 + c0 + tx];
+    __syncthreads();
+    for (int y = ty; y < 32; y += 8) dst[(size_t)(c0 + y) * 128 + r0 + tx] = f32_to_bf16(tile[tx][y]);
+}
+
+// The online segment's share of dK and dV for d_k = d_v = 128 (bf16), on MFMA.  For token r
+// of segment s, E_r = dM^(s) + sum_{t >= r in s} gamma_t^(s) dy_t phi(q_t)^T, dv_r = E_r phi(k_r)
+// and dphi(k_r) = E_r^T v_r; over a tile of 64 r tokens that is
+//   dV^T[c][r]      = sum_j dM[c][j] phi(k_r)[j] + sum_{t >= r} dy_t[c] P[t][r],
+//                     P[t][r] = gamma_t <phi(q_t), phi(k_r)>
+//   dphi(K)^T[j][r] = sum_c dM[c][j] v_r[c]      + sum_{t >= r} phi(q_t)[j] B[t][r],
+//                     B[t][r] = gamma_t <dy_t, v_r>
+// (the flash-attention backward's dK/dV loop without the softmax).  A workgroup takes one r
+// tile and walks the segment's t tiles from its own on; waves 0..3 form dV, waves 4..7
+// dphi(K), wave (r block rb, t block tb) of each side the 32 x 32 block P or B of its r and
+// t blocks (8 MFMAs over the features), masked (t >= r, t in the segment) and scaled in
+// registers, where it is already the B operand of the token contraction: the k index of the
+// second product is permuted the same way on both sides (the A operand, dy^T or phi(q)^T
+// staged in LDS with tokens along the rows, is read as two 4-token runs per k step).  The
+// two t-block waves of an r block each keep the four 32-row blocks (c or j) of their partial
+// sums and add them through LDS at the end.  The dM term (bf16 copies of dM: [c][j] for dV,
+// the fp32 [j][c] rounded on load for dK) is split between the two t-block waves.  phi(q)
+// and dy of a t tile are staged twice (token-major for the first product, transposed for
+// the second), double-buffered, the next tile loaded into registers during the current one.
+__global__ __launch_bounds__(512, 1) void bwd_online_mfma_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kh, const bf16_t* __restrict__ K,
+    const bf16_t* __restrict__ V, const bf16_t* __restrict__ dY, const float* __restrict__ gs,
+    const float* __restrict__ dMT, const bf16_t* __restrict__ dMc, int BH, int L, int C, int NS,
+    int phi, float* __restrict__ dK, float* __restrict__ dV) {
+    // one LDS block: phi(q) [t][j] and dy [t][c] token-major, phi(q)^T [j][t] and dy^T [c][t],
+    // gamma_t (0 past the segment), two buffers each; after the walk its first 64 KB hold
+    // the partial sums handed between waves
+    constexpr int NB = 2 * OT * NPAD * 2, TB = 2 * 128 * TPAD * 2;
+    static_assert(2 * NB >= 4 * 4 * 16 * 64 * 4, "reduction area");
+    __shared__ uint4 lds[(2 * NB + 2 * TB + 2 * OT * 4) / 16];
+    unsigned char* lb = reinterpret_cast<unsigned char*>(lds);
+    bf16_t(*qn)[OT][NPAD] = reinterpret_cast<bf16_t(*)[OT][NPAD]>(lb);
+    bf16_t(*yn)[OT][NPAD] = reinterpret_cast<bf16_t(*)[OT][NPAD]>(lb + NB);
+    bf16_t(*qtt)[128][TPAD] = reinterpret_cast<bf16_t(*)[128][TPAD]>(lb + 2 * NB);
+    bf16_t(*ytt)[128][TPAD] = reinterpret_cast<bf16_t(*)[128][TPAD]>(lb + 2 * NB + TB);
+    float(*sgo)[OT] = reinterpret_cast<float(*)[OT]>(lb + 2 * NB + 2 * TB);
+    // r tiles slowest: the first r tiles of every segment (the most t tiles) go first
+    const int nsb = NS * BH;
+    const int R = blockIdx.x / nsb;
+    const size_t bh = (blockIdx.x % nsb) % BH;
+    const int s = (blockIdx.x % nsb) / BH;
+    const int t0 = s * C, n = min(C, L - t0);
+    const int r0 = R * OT;
+    if (r0 >= n) return;  // uniform: the segment has no r tile R
+    const int NT = (n + OT - 1) / OT;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, half = lane >> 5;
+    const bool kside = wave >= 4;  // waves 4..7: dphi(K); 0..3: dV
+    const int rb = (wave >> 1) & 1, tb = wave & 1;
+    const int rr = r0 + rb * 32 + l32;  // this lane's r (segment-relative; rows past the
+                                        // segment are read clamped, their sums not stored)
+    const size_t rrow = bh * L + min(t0 + rr, L - 1);
+
+    // phi(k_r) (dV side) or v_r (dK side): the fixed B operand, k = 16 ks + 8 half + 0..7
+    u32x4_t kv[8];
+    {
+        const bf16_t* src = (kside ? V : Kh) + rrow * 128 + half * 8;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) kv[ks] = *reinterpret_cast<const u32x4_t*>(src + ks * 16);
+    }
+    const f32x16_t zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
+                           0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    f32x16_t acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = zero;
+
+    // staging roles: token pair (2p, 2p + 1) of the tile, features 8 fg .. + 7
+    const int p = tid & 31, fg = tid >> 5;
+    u32x4_t rq[2], ry[2];
+    float rg = 0.f;
+    auto load = [&](int tt0) {
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+            const size_t row = bh * L + min(t0 + tt0 + 2 * p + o, L - 1);
+            rq[o] = *reinterpret_cast<const u32x4_t*>(Q + row * 128 + fg * 8);
+            ry[o] = *reinterpret_cast<const u32x4_t*>(dY + row * 128 + fg * 8);
+        }
+        rg = gs[bh * L + min(t0 + tt0 + (tid & 63), L - 1)];
+    };
+    auto stage = [&](int buf, int tt0) {
+        const u32x4_t a = phi8(rq[0], phi), b = phi8(rq[1], phi);
+        *reinterpret_cast<u32x4_t*>(&qn[buf][2 * p][fg * 8]) = a;
+        *reinterpret_cast<u32x4_t*>(&qn[buf][2 * p + 1][fg * 8]) = b;
+        *reinterpret_cast<u32x4_t*>(&yn[buf][2 * p][fg * 8]) = ry[0];
+        *reinterpret_cast<u32x4_t*>(&yn[buf][2 * p + 1][fg * 8]) = ry[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int rw = fg * 8 + 2 * e;
+            *reinterpret_cast<uint32_t*>(&qtt[buf][rw][2 * p]) = (a[e] & 0xffffu) | (b[e] << 16);
+            *reinterpret_cast<uint32_t*>(&qtt[buf][rw + 1][2 * p]) = (a[e] >> 16) | (b[e] & 0xffff0000u);
+            *reinterpret_cast<uint32_t*>(&ytt[buf][rw][2 * p]) = (ry[0][e] & 0xffffu) | (ry[1][e] << 16);
+            *reinterpret_cast<uint32_t*>(&ytt[buf][rw + 1][2 * p]) =
+                (ry[0][e] >> 16) | (ry[1][e] & 0xffff0000u);
+        }
+        if (tid < OT) sgo[buf][tid] = tt0 + tid < n ? rg : 0.f;
+    };
+
+    load(r0);
+    stage(0, r0);
+    if (R + 1 < NT) load(r0 + OT);
+    // the dM term: blocks 2 tb and 2 tb + 1 of the c (dV) or j (dK) rows
+    {
+        const size_t st = (bh * NS + s) * (size_t)(128 * 128);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if ((b >> 1) != tb) continue;  // uniform
+            const int m = b * 32 + l32;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                u32x4_t a;
+                if (!kside) {
+                    a = *reinterpret_cast<const u32x4_t*>(dMc + st + m * 128 + ks * 16 + half * 8);
+                } else {
+                    const float4 f0 = *reinterpret_cast<const float4*>(dMT + st + m * 128 + ks * 16 + half * 8);
+                    const float4 f1 = *reinterpret_cast<const float4*>(dMT + st + m * 128 + ks * 16 + half * 8 + 4);
+                    a[0] = pack_bf16x2(f0.x, f0.y);
+                    a[1] = pack_bf16x2(f0.z, f0.w);
+                    a[2] = pack_bf16x2(f1.x, f1.y);
+                    a[3] = pack_bf16x2(f1.z, f1.w);
+                }
+                acc[b] = mfma32(a, kv[ks], acc[b]);
+            }
+        }
+    }
+    __syncthreads();
+    for (int T = R; T < NT; ++T) {
+        const int buf = (T - R) & 1;
+        const int tt0 = T * OT;
+        if (!(T == R && tb < rb)) {  // uniform: a t block wholly before the r block is masked
+            // first product: D[t][r] over the 128 features (phi(q) phi(k)^T or dy v^T)
+            const bf16_t(*an)[NPAD] = kside ? yn[buf] : qn[buf];
+            f32x16_t sa = zero;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const u32x4_t a =
+                    *reinterpret_cast<const u32x4_t*>(&an[tb * 32 + l32][ks * 16 + half * 8]);
+                sa = mfma32(a, kv[ks], sa);
+            }
+            // lane holds r = rr and t = tt0 + 32 tb + 8 g + 4 half + e (value 4 g + e)
+            u32x4_t pf[2];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int tl = tb * 32 + 8 * g + 4 * half;
+                const float4 gv = *reinterpret_cast<const float4*>(&sgo[buf][tl]);
+                const float gg[4] = {gv.x, gv.y, gv.z, gv.w};
+                float pv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pv[e] = tt0 + tl + e >= rr ? sa[4 * g + e] * gg[e] : 0.f;
+                pf[g >> 1][(g & 1) * 2] = pack_bf16x2(pv[0], pv[1]);
+                pf[g >> 1][(g & 1) * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
+            }
+            // second product over the block's 32 tokens: k step kk holds, in slots 0..3 and
+            // 4..7, the tokens 16 kk + 4 half + 0..3 and 16 kk + 8 + 4 half + 0..3
+            const bf16_t(*at)[TPAD] = kside ? qtt[buf] : ytt[buf];
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int c0 = tb * 32 + 16 * kk + 4 * half;
+                    const uint2 lo = *reinterpret_cast<const uint2*>(&at[b * 32 + l32][c0]);
+                    const uint2 hi = *reinterpret_cast<const uint2*>(&at[b * 32 + l32][c0 + 8]);
+                    const u32x4_t a = {lo.x, lo.y, hi.x, hi.y};
+                    acc[b] = mfma32(a, pf[kk], acc[b]);
+                }
+        }
+        if (T + 1 < NT) {
+            // the other buffer was last read before the previous barrier
+            stage(buf ^ 1, tt0 + OT);
+            if (T + 2 < NT) load(tt0 + 2 * OT);
+        }
+        __syncthreads();
+    }
+    // the t-block-1 waves hand their partial sums to the t-block-0 waves (LDS of the
+    // token-major tiles, free after the last barrier): [side, rb][block][value][lane]
+    float* red = reinterpret_cast<float*>(lb);
+    const int pair = (kside ? 2 : 0) + rb;
+    if (tb == 1) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) red[((pair * 4 + b) * 16 + i) * 64 + lane] = acc[b][i];
+    }
+    __syncthreads();
+    if (tb == 1 || rr >= n) return;
+    const size_t orow = (bh * L + t0 + rr) * 128;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int m = b * 32 + 8 * g + 4 * half;  // c (dV) or j (dK) of values 4 g .. 4 g + 3
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = acc[b][4 * g + e] + red[((pair * 4 + b) * 16 + 4 * g + e) * 64 + lane];
+            if (kside && phi) {
+                const u32x2_t kw = *reinterpret_cast<const u32x2_t*>(K + orow + m);
+                o[0] *= fminf(feature(bf_lo(kw[0]), 1), 1.f);
+                o[1] *= fminf(feature(bf_hi(kw[0]), 1), 1.f);
+                o[2] *= fminf(feature(bf_lo(kw[1]), 1), 1.f);
+                o[3] *= fminf(feature(bf_hi(kw[1]), 1), 1.f);
+            }
+            *reinterpret_cast<float4*>((kside ? dK : dV) + orow + m) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+}
+
 // The softmax backward from the gate pass: gamma_i = W_t^(i) / l_t (i < s),
 // gamma_s = won_t / l_t; dgamma of the online segment <dy_t, O_on[t]>; D_t; da_i written over
 // dgamma; du_t; the online weight for the segment walk; dq = dphi(q) phi'(q) with dphi(q) the
@@ -521,6 +741,21 @@ int launch_bwd_fast(const mc_dims& d, const BwdBuffers& w, const void* Q, const 
     hipLaunchKernelGGL(bwd_dm_mfma_kernel, dim3(nranges * ((NS + SPW - 1) / SPW) * BH), dim3(512),
                        0, st, (const bf16_t*)Q, (const bf16_t*)dY, w.W, w.inv_l, (const bf16_t*)U,
                        w.daT, BH, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads, d.phi, w.dM, w.dpp);
+    return (int)hipGetLastError();
+}
+
+int launch_bwd_online_mfma(const mc_dims& d, const BwdBuffers& w, const void* Q, const void* K,
+                           const void* V, const void* dY, float* dK, float* dV, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+    const int BH = d.B * d.H;
+    // dM in bf16, [c][j], over the transposed states of the swapped read (no longer needed)
+    hipLaunchKernelGGL(dm_cr_kernel, dim3(BH * NS, 4, 4), dim3(256), 0, st, w.dM, (bf16_t*)w.mt);
+    const int rt = (d.seg_len + OT - 1) / OT;  // r tiles of a segment
+    hipLaunchKernelGGL(bwd_online_mfma_kernel, dim3(rt * NS * BH), dim3(512), 0, st,
+                       (const bf16_t*)Q, (const bf16_t*)(d.phi ? w.khat : K), (const bf16_t*)K,
+                       (const bf16_t*)V, (const bf16_t*)dY, w.gs, w.dM, (const bf16_t*)w.mt, BH,
+                       d.L, d.seg_len, NS, d.phi, dK, dV);
     return (int)hipGetLastError();
 }
 

@@ -112,6 +112,9 @@ inline bool bwd_fast(const mc_dims& d) { return gate_pass(d); }
 int launch_bwd_fast(const mc_dims& d, const BwdBuffers& w, const void* Q, const void* K,
                     const void* V, const void* U, const float* M, const uint16_t* M_lo,
                     const float* P, const void* dY, float* dQ, float* dU, void* stream);
+// the online segment's dK and dV for the MFMA backward (dM stored transposed)
+int launch_bwd_online_mfma(const mc_dims& d, const BwdBuffers& w, const void* Q, const void* K,
+                           const void* V, const void* dY, float* dK, float* dV, void* stream);
 // tokens per range of the dP partial sums: a multiple of 64, at most 64 ranges
 inline int bwd_dp_range(int L) {
     const int r = (L + 63) / 64;
