@@ -101,9 +101,11 @@ BwdWorkspace bwd_workspace(const mc_dims& d) {
         w.mt = align256(sizeof(uint16_t) * (size_t)d.B * d.H * num_segments(d) * d.d_v * d.d_k);
         w.dqh = align256(sizeof(uint16_t) * bhl * d.d_k);
         w.daT = align256(sizeof(float) * bhl * num_segments(d));
+        // B fragments of the means: per x head, k step of 16 segments, 4 column blocks, lane
+        w.ptf = align256((size_t)d.B * d.x_heads * ((num_segments(d) + 15) / 16) * 4 * 64 * 32);
     }
     w.total = w.aon + w.xps + w.xtail + w.on + w.ot + w.khat + w.lse + w.D + w.gs + w.dG + w.dM +
-              w.dpp + w.W + w.won + w.inv_l + w.pf + w.mt + w.dqh + w.daT;
+              w.dpp + w.W + w.won + w.inv_l + w.pf + w.mt + w.dqh + w.daT + w.ptf;
     return w;
 }
 
@@ -446,6 +448,8 @@ mc_status mc_grm_backward(const mc_dims* d, const void* Q, const void* K, const 
     bw.dqh = b;
     b += w.dqh;
     bw.daT = (float*)b;
+    b += w.daT;
+    bw.ptf = b;
     return launch_grm_backward(*d, bw, Q, K, V, U, X, M, M_lo, P, dY, dQ, dK, dV, dU, dX,
                                stream)
                ? MC_ERR_HIP

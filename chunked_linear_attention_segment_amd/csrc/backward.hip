@@ -323,14 +323,15 @@ __global__ __launch_bounds__(256) void bwd_online_kernel(
 
 // dx in three steps (x head bx; with one shared x head its sums run over every head):
 //   bwd_dxw_kernel    w_t = sum_h da_t^(s) u_t / (j_t + 1), the prefix-mean term of token t
+//                     (da_t^(s) read from dA [B,H,L,NS], or from [B,H,L] with diag set)
 //   bwd_dp_kernel     partial dP_i = sum_h sum_t da_t^(i) u_t over one token range (3-D grid:
 //                     segment, x head, token range; token lanes reduced through LDS)
 //   bwd_dxf_kernel    dP_i from the partials; dx_r = dP_i / |S_i| + sum_{t >= r in S_i} w_t
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_dxw_kernel(const T* __restrict__ U,
-                                                      const float* __restrict__ dA, int L,
-                                                      int C, int NS, int DG, int H, int xh,
-                                                      float* __restrict__ w) {
+                                                      const float* __restrict__ dA, int diag,
+                                                      int L, int C, int NS, int DG, int H,
+                                                      int xh, float* __restrict__ w) {
     const int t0 = blockIdx.x * 64;
     const size_t bx = blockIdx.y;
     const int b = (int)(bx / xh), hx = (int)(bx % xh);
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(256) void bwd_dxw_kernel(const T* __restrict__ U,
         float acc = 0.f;
         for (int h = h0; h < h1; ++h) {
             const size_t bh = (size_t)b * H + h;
-            acc += dA[(bh * L + t) * NS + s] * ld(U, (bh * L + t) * DG + e);
+            acc += dA[diag ? bh * L + t : (bh * L + t) * NS + s] * ld(U, (bh * L + t) * DG + e);
         }
         w[(bx * L + t) * DG + e] = acc / (float)(j + 1);
     }
@@ -441,7 +442,7 @@ int launch_bwd_t(const mc_dims& d, const BwdBuffers& w, const void* Q, const voi
     // x gradients; the prefix sums of X are no longer needed, so w_t goes in their place
     const int bxn = d.B * d.x_heads;
     hipLaunchKernelGGL((bwd_dxw_kernel<T>), dim3((d.L + 63) / 64, bxn), dim3(256), 0, st,
-                       (const T*)U, w.dG, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads, w.xps);
+                       (const T*)U, w.dG, fast ? 1 : 0, d.L, d.seg_len, NS, d.d_g, d.H, d.x_heads, w.xps);
     // dP_i: partial sums over token ranges, or (MFMA path) per head from the dM walk
     const int RL = bwd_dp_range(d.L);
     int NR = (d.L + RL - 1) / RL;

@@ -13,8 +13,8 @@
 //     segments and range of later tokens, walks the tokens in chunks of 64 (the scan's
 //     state-update contraction with phi(q) in place of phi(k) and gamma dy in place of v),
 //     and dP_i = sum_t da_t^(i) u_t beside it; dM is stored transposed.
-//   bwd_gate_fast_kernel: the softmax backward from the gate numerators W, 1/l and the online
-//     weight (gamma_i = W_i / l), dgamma of the online segment, du_t and dq.
+//   bwd_gate_mfma_kernel: the softmax backward from the gate numerators W, 1/l and the online
+//     weight (gamma_i = W_i / l), dgamma of the online segment, du_t (on MFMA) and dq.
 #include "common.cuh"
 #include "mc_internal.h"
 
@@ -63,13 +63,14 @@ __global__ __launch_bounds__(256) void transpose_states_kernel(const bf16_t* __r
 constexpr int DT = 256;     // tokens per dgamma workgroup: 4 waves x 2 blocks of 32
 constexpr int SROW = 136;   // LDS row stride (bf16) of a staged state: 16 bytes of padding
 
-// dgamma_t^(i) for i < s_t, d_k = d_v = 128.  Wave w owns tokens t0 + 64w .. + 63 (two blocks
+// dgamma_t^(i) for i < s_t, d_k = d_v = 128, written segment-major ([i][t]).  Wave w owns
+// tokens t0 + 64w .. + 63 (two blocks
 // of 32); per state: O^(i) = M^(i) phi(q) as 4 (rows) x 2 (token blocks) accumulator tiles,
 // then dgamma = sum_c dy[c] O[c][t] (16 rows per lane, the two half-waves combined).  States are
 // double-buffered in LDS, loaded one ahead through registers.
 __global__ __launch_bounds__(256, 1) void bwd_dgamma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ dY, const bf16_t* __restrict__ M_lo,
-    int L, int C, int NS, int phi, float* __restrict__ dG) {
+    int L, int C, int NS, int phi, float* __restrict__ dGT) {
     __shared__ __attribute__((aligned(16))) bf16_t ms[2][128][SROW];
     const int ntile = gridDim.x;
     const int tile = ntile - 1 - blockIdx.x;  // the tiles that read the most states first
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dgamma_kernel(
                 for (int r = 0; r < 16; ++r) part += dyv[tb][cb][r] * acc[cb][tb][r];
             part += __shfl_xor(part, 32);
             if (half == 0 && tok[tb] < L && i < stok[tb])
-                dG[(bh * L + tok[tb]) * NS + i] = part;
+                dGT[(bh * NS + i) * (size_t)L + tok[tb]] = part;
         }
     };
     load_state(0, ra);
@@ -586,112 +587,188 @@ __global__ __launch_bounds__(512, 1) void bwd_online_mfma_kernel(
         }
 }
 
-// The softmax backward from the gate pass: gamma_i = W_t^(i) / l_t (i < s),
-// gamma_s = won_t / l_t; dgamma of the online segment <dy_t, O_on[t]>; D_t; da_i written over
-// dgamma; du_t; the online weight for the segment walk; dq = dphi(q) phi'(q) with dphi(q) the
-// bf16 output of the swapped read.  8 threads per token.
-template <int DK>
-__global__ __launch_bounds__(256) void bwd_gate_fast_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ U, const float* __restrict__ P,
-    const float* __restrict__ xps, const uint16_t* __restrict__ Wg,
-    const float* __restrict__ won, const float* __restrict__ inv_l,
-    const float* __restrict__ O_on, const bf16_t* __restrict__ dY,
-    const bf16_t* __restrict__ dqh, int L, int C, int NS, int DG, int DV, int H, int xh,
-    int phi, float* __restrict__ dG, float* __restrict__ daT, float* __restrict__ gs_o,
-    float* __restrict__ dU, float* __restrict__ dQ) {
-    constexpr int CPK = DK / 8;
-    const int tile0 = blockIdx.x * 32;
+constexpr int GTOK = 256;  // tokens per workgroup of the gate backward (one gate tile)
+static_assert(GTOK == kGateTile, "the gate backward reads whole gate tiles");
+
+// The means as B fragments of the du product (k = segment, n = gate column): for x head bx,
+// k step ks, 32-column block eb and lane (l32, half) the 8 values P_i[32 eb + l32],
+// i = 16 ks + 8 half + 0..7, as bf16 high parts then bf16 rests (2 x 16 bytes); zero past NS
+// and d_g.
+__global__ void ptf_kernel(const float* __restrict__ P, int NS, int DG, int NSK, size_t n,
+                           u32x4_t* __restrict__ out) {
+    const size_t d = blockIdx.x * (size_t)blockDim.x + threadIdx.x;  // (bx, ks, eb, lane)
+    if (d >= n) return;
+    const int lane = (int)(d % 64), eb = (int)((d / 64) % 4), ks = (int)((d / 256) % NSK);
+    const size_t bx = d / 256 / NSK;
+    const int e = 32 * eb + (lane & 31), i0 = 16 * ks + 8 * (lane >> 5);
+    u32x4_t hi, lo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float v[2];
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+            const int i = i0 + 2 * q + o;
+            v[o] = i < NS && e < DG ? P[(bx * NS + i) * DG + e] : 0.f;
+        }
+        hi[q] = pack_bf16x2(v[0], v[1]);
+        lo[q] = pack_bf16x2(v[0] - bf_lo(hi[q]), v[1] - bf_hi(hi[q]));
+    }
+    out[2 * d] = hi;
+    out[2 * d + 1] = lo;
+}
+
+// The softmax backward of the gate for d_k = d_v = 128 and d_g <= 128, one 256-token gate
+// tile per workgroup: gamma_i = W_t^(i) / l_t (i < s), gamma_s = won_t / l_t; dgamma of the
+// online segment <dy_t, O_on[t]>; D_t = sum_i gamma_i dgamma_i; da_i = gamma_i (dgamma_i - D)
+// written over dgamma (segment-major, [i][t]); da_s; du_t = sum_i da_i P_i on MFMA plus
+// da_s times the prefix mean x_t; dq = dphi(q) phi'(q) with dphi(q) the bf16 output of the
+// swapped read.  Wave w takes tokens 32 w .. + 31 (lane l32 = token): pass 1 sums D over the
+// segments (half h of the wave the segments 16 ks + 8 h + 0..7), pass 2 forms da for the
+// same segments, which are then the A fragment (bf16 high part and rest) of 32x32x16 MFMAs
+// against the means' fragments (high and rest; the rest times the rest is dropped).
+__global__ __launch_bounds__(512) void bwd_gate_mfma_kernel(
+    const bf16_t* __restrict__ Q, const float* __restrict__ xps, const uint16_t* __restrict__ Wg,
+    const float* __restrict__ won, const float* __restrict__ inv_l, const float* __restrict__ O_on,
+    const bf16_t* __restrict__ dY, const bf16_t* __restrict__ dqh, const u32x4_t* __restrict__ ptf,
+    int L, int C, int NS, int DG, int H, int xh, int phi, float* __restrict__ daT,
+    float* __restrict__ das_o, float* __restrict__ gs_o, float* __restrict__ dU,
+    float* __restrict__ dQ) {
+    __shared__ float s_das[GTOK];
+    const int T = (L + GTOK - 1) / GTOK;
+    const int tile = T - 1 - blockIdx.x;  // the tiles that read the most segments first
     const size_t bh = blockIdx.y;
     const int b = (int)(bh / H), h = (int)(bh % H);
     const size_t bx = (size_t)b * xh + (xh == 1 ? 0 : h);
-    const int tid = threadIdx.x, tt = tid / 8, p = tid % 8;
-    const int t = tile0 + tt;
-    const bool valid = t < L;
-    const int tc = valid ? t : L - 1;
-    const int s = tc / C, j = tc - s * C;
-    const int T = (L + kGateTile - 1) / kGateTile;
-    const size_t grow = (bh * L + tc) * NS;
+    const int t0 = tile * GTOK;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, half = lane >> 5;
+    const int NSK = (NS + 15) / 16;
+    const int s_hi = (min(L, t0 + GTOK) - 1) / C;  // segments read by the tile's last token
+    const int nks = (s_hi + 15) / 16;
+    const uint16_t* wt = Wg + (bh * T + tile) * (size_t)NS * GTOK;  // [i][t - t0]
+    const float* dgt = daT + bh * (size_t)NS * L;                  // [i][t]
+
+    const int tl = wave * 32 + l32;
+    const int t = t0 + tl;
+    const int tc = min(t, L - 1);
+    const int sg = tc / C;
     const float il = inv_l[bh * L + tc];
-    // dgamma of the online segment, <dy_t, O_on[t]>: thread p takes DV/8 consecutive columns
-    // (16-byte loads, one round trip)
+    // dgamma of the online segment: half h takes the 64 columns 64 h ..
     float part = 0.f;
     {
-        const int cpt = DV / 8, c0 = p * cpt;
-        const bf16_t* dyr = dY + (bh * L + tc) * DV + c0;
-        const float* orow = O_on + (bh * L + tc) * DV + c0;
-        for (int c = 0; c < cpt; c += 8) {
-            const u32x4_t y = *reinterpret_cast<const u32x4_t*>(dyr + c);
+        const bf16_t* yr = dY + (bh * L + tc) * 128 + half * 64;
+        const float* orow = O_on + (bh * L + tc) * 128 + half * 64;
+#pragma unroll
+        for (int c = 0; c < 64; c += 8) {
+            const u32x4_t y = *reinterpret_cast<const u32x4_t*>(yr + c);
             const float4 o0 = *reinterpret_cast<const float4*>(orow + c);
             const float4 o1 = *reinterpret_cast<const float4*>(orow + c + 4);
-            part += bf_lo(y[0]) * o0.x + bf_hi(y[0]) * o0.y + bf_lo(y[1]) * o0.z + bf_hi(y[1]) * o0.w +
-                    bf_lo(y[2]) * o1.x + bf_hi(y[2]) * o1.y + bf_lo(y[3]) * o1.z + bf_hi(y[3]) * o1.w;
+            part += bf_lo(y[0]) * o0.x + bf_hi(y[0]) * o0.y + bf_lo(y[1]) * o0.z +
+                    bf_hi(y[1]) * o0.w + bf_lo(y[2]) * o1.x + bf_hi(y[2]) * o1.y +
+                    bf_lo(y[3]) * o1.z + bf_hi(y[3]) * o1.w;
         }
     }
-    const float dgs = warp_sum(part, 8);
+    const float dgs = part + __shfl_xor(part, 32);
+    // pass 1: sum_i W_i dgamma_i over this half's segments, then both halves
+    float dp = 0.f;
+#pragma unroll 2
+    for (int ks = 0; ks < nks; ++ks) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = 16 * ks + 8 * half + j;
+            const int ic = min(i, NS - 1);
+            const float w = bf16_to_f32((bf16_t)wt[(size_t)ic * GTOK + tl]);
+            const float g = dgt[(size_t)ic * L + tc];
+            dp += i < sg ? w * g : 0.f;
+        }
+    }
+    dp += __shfl_xor(dp, 32);
     const float gsv = won[bh * L + tc] * il;
-    const int gch = DG / 8;
-    float du[32];  // DG <= 256
-#pragma unroll
-    for (int k = 0; k < 32; ++k) du[k] = 0.f;
-    // 32 segments at a time through LDS (the tile's largest s bounds the walk): the gate
-    // numerators and dgamma of the tile's 32 tokens, loaded coalesced, and (second pass) the
-    // means.  Pass 1 forms D = sum_i gamma_i dgamma_i, pass 2 da_i = gamma_i (dgamma_i - D).
-    __shared__ float sP[32][256];
-    __shared__ float sG[32][33];   // dgamma [token][segment]
-    __shared__ float sWt[32][33];  // numerator [segment][token]
-    const int s_hi = (min(L, tile0 + 32) - 1) / C;
-    const uint16_t* wtile = Wg + ((bh * T + tile0 / kGateTile) * NS) * kGateTile + tile0 % kGateTile;
-    auto stage = [&](int i0, int m, bool means) {
-        __syncthreads();
-        if (means)
-            for (int e = tid; e < m * DG; e += 256) sP[e / DG][e % DG] = P[(bx * NS + i0) * DG + e];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int idx = tid + 256 * k, a = idx / 32, c = idx % 32;
-            const int tg = tile0 + a;  // sG: token a, segment i0 + c
-            sG[a][c] = (tg < L && c < m) ? dG[(bh * L + tg) * NS + i0 + c] : 0.f;
-            const int tw = tile0 + c;  // sWt: segment i0 + a, token c
-            sWt[a][c] = (tw < L && a < m) ? bf16_to_f32(wtile[(size_t)(i0 + a) * kGateTile + c]) : 0.f;
-        }
-        __syncthreads();
-    };
-    float dpart = 0.f;
-    for (int i0 = 0; i0 < s_hi; i0 += 32) {
-        const int m = min(32, s_hi - i0);
-        stage(i0, m, false);
-        for (int ii = p; ii < m && i0 + ii < s; ii += 8) dpart += sWt[ii][tt] * sG[tt][ii];
-    }
-    const float D = warp_sum(dpart, 8) * il + gsv * dgs;
-    for (int i0 = 0; i0 < s_hi; i0 += 32) {
-        const int m = min(32, s_hi - i0);
-        stage(i0, m, true);
-        for (int ii = 0; ii < m && valid; ++ii) {
-            const int i = i0 + ii;
-            if (i >= s) break;
-            const float da = sWt[ii][tt] * il * (sG[tt][ii] - D);
-#pragma unroll
-            for (int k = 0; k < 32; ++k)
-                if (k < gch) du[k] += da * sP[ii][p * gch + k];
-            if ((i & 7) == p) daT[(bh * NS + i) * L + t] = da;  // segment-major for dM
+    const float Dt = dp * il + gsv * dgs;
+    const float das = gsv * (dgs - Dt);
+    if (half == 0) {
+        s_das[tl] = das;
+        if (t < L) {
+            das_o[bh * L + t] = das;
+            gs_o[bh * L + t] = gsv;
         }
     }
-    if (!valid) return;  // no barriers below
-    const float das = gsv * (dgs - D);
-    if (p == 0) {
-        dG[grow + s] = das;
-        gs_o[bh * L + t] = gsv;
+    // pass 2: da (written over dgamma) and du on MFMA
+    const f32x16_t zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
+                           0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    f32x16_t acc[4];
+#pragma unroll
+    for (int eb = 0; eb < 4; ++eb) acc[eb] = zero;
+    const int neb = (DG + 31) / 32;
+    const u32x4_t* pb = ptf + (bx * NSK) * 4 * 64 * 2;
+    for (int ks = 0; ks < nks; ++ks) {
+        float da[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = 16 * ks + 8 * half + j;
+            const int ic = min(i, NS - 1);
+            const float w = bf16_to_f32((bf16_t)wt[(size_t)ic * GTOK + tl]);
+            const float g = dgt[(size_t)ic * L + tc];
+            da[j] = i < sg ? w * il * (g - Dt) : 0.f;
+        }
+        u32x4_t bhi[4], blo[4];
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb) {
+            const u32x4_t* src = pb + ((size_t)(ks * 4 + eb) * 64 + lane) * 2;
+            bhi[eb] = src[0];
+            blo[eb] = src[1];
+        }
+        if (t < L) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = 16 * ks + 8 * half + j;
+                if (i < sg) daT[(bh * NS + i) * (size_t)L + t] = da[j];
+            }
+        }
+        u32x4_t ahi, alo;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            ahi[q] = pack_bf16x2(da[2 * q], da[2 * q + 1]);
+            alo[q] = pack_bf16x2(da[2 * q] - bf_lo(ahi[q]), da[2 * q + 1] - bf_hi(ahi[q]));
+        }
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb) {
+            if (eb >= neb) continue;  // uniform
+            acc[eb] = mfma32(ahi, bhi[eb], acc[eb]);
+            acc[eb] = mfma32(ahi, blo[eb], acc[eb]);
+            acc[eb] = mfma32(alo, bhi[eb], acc[eb]);
+        }
     }
-    const float* xr = xps + (bx * L + t) * DG + p * gch;
-    const float inv = 1.f / (float)(j + 1);
-    const size_t urow = (bh * L + t) * DG + p * gch;
+    // du_t: lane holds e = 32 eb + l32 and token 32 w + 8 g + 4 half + e' (value 4 g + e');
+    // plus da_s x_t with x_t the prefix mean (prefix sum / (j + 1)) of the token's segment
 #pragma unroll
-    for (int k = 0; k < 32; ++k)
-        if (k < gch) dU[urow + k] = du[k] + das * xr[k] * inv;
+    for (int eb = 0; eb < 4; ++eb) {
+        const int e = 32 * eb + l32;
+        if (eb >= neb || e >= DG) continue;
 #pragma unroll
-    for (int m = 0; m < CPK; ++m) {
-        const size_t o = (bh * L + t) * DK + p + 8 * m;
-        const float f = feature(bf16_to_f32(Q[o]), phi);
-        dQ[o] = bf16_to_f32(dqh[o]) * (phi ? fminf(f, 1.f) : 1.f);
+        for (int v = 0; v < 16; ++v) {
+            const int tt = wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+            const int tv = t0 + tt;
+            if (tv >= L) continue;
+            const int j = tv - (tv / C) * C;
+            dU[(bh * L + tv) * DG + e] =
+                acc[eb][v] + s_das[tt] * xps[(bx * L + tv) * DG + e] / (float)(j + 1);
+        }
+    }
+    // dq = dphi(q) phi'(q), 8 columns per thread and step
+    for (int idx = tid; idx < GTOK * 16; idx += 512) {
+        const int tq = t0 + idx / 16, c8 = (idx % 16) * 8;
+        if (tq >= L) break;
+        const size_t o = (bh * L + tq) * 128 + c8;
+        const u32x4_t g = *reinterpret_cast<const u32x4_t*>(dqh + o);
+        const u32x4_t q = *reinterpret_cast<const u32x4_t*>(Q + o);
+        float r[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r[2 * e] = bf_lo(g[e]) * (phi ? fminf(feature(bf_lo(q[e]), 1), 1.f) : 1.f);
+            r[2 * e + 1] = bf_hi(g[e]) * (phi ? fminf(feature(bf_hi(q[e]), 1), 1.f) : 1.f);
+        }
+        *reinterpret_cast<float4*>(dQ + o) = make_float4(r[0], r[1], r[2], r[3]);
+        *reinterpret_cast<float4*>(dQ + o + 4) = make_float4(r[4], r[5], r[6], r[7]);
     }
 }
 
@@ -726,11 +803,17 @@ int launch_bwd_fast(const mc_dims& d, const BwdBuffers& w, const void* Q, const 
     if (rc) return rc;
     hipLaunchKernelGGL(bwd_dgamma_kernel, dim3((d.L + DT - 1) / DT, BH), dim3(256), 0, st,
                        (const bf16_t*)Q, (const bf16_t*)dY, (const bf16_t*)M_lo, d.L, d.seg_len,
-                       NS, d.phi, w.dG);
-    hipLaunchKernelGGL((bwd_gate_fast_kernel<128>), dim3((d.L + 31) / 32, BH), dim3(256), 0, st,
-                       (const bf16_t*)Q, (const bf16_t*)U, P, w.xps, w.W, w.won, w.inv_l, w.on,
-                       (const bf16_t*)dY, (const bf16_t*)w.dqh, d.L, d.seg_len, NS, d.d_g, d.d_v,
-                       d.H, d.x_heads, d.phi, w.dG, w.daT, w.gs, dU, dQ);
+                       NS, d.phi, w.daT);
+    // the means as the du product's B fragments, then the gate backward (da over dgamma;
+    // da of the online segment into dG, used as [B,H,L])
+    const int nsk = (NS + 15) / 16;
+    const size_t nptf = (size_t)d.B * d.x_heads * nsk * 4 * 64;
+    hipLaunchKernelGGL(ptf_kernel, dim3((unsigned)((nptf + 255) / 256)), dim3(256), 0, st, P, NS,
+                       d.d_g, nsk, nptf, (u32x4_t*)w.ptf);
+    hipLaunchKernelGGL(bwd_gate_mfma_kernel, dim3((d.L + GTOK - 1) / GTOK, BH), dim3(512), 0, st,
+                       (const bf16_t*)Q, w.xps, w.W, w.won, w.inv_l, w.on, (const bf16_t*)dY,
+                       (const bf16_t*)w.dqh, (const u32x4_t*)w.ptf, d.L, d.seg_len, NS, d.d_g,
+                       d.H, d.x_heads, d.phi, w.daT, w.dG, w.gs, dU, dQ);
     // dM and dP take the partial sums of the split workgroups: zero them first (a kernel, so
     // the sequence stays capturable)
     const size_t ndm = (size_t)BH * NS * d.d_v * d.d_k;

@@ -91,7 +91,7 @@ struct BwdBuffers {
     float* lse;    // [B,H,L] log of the softmax denominator
     float* D;      // [B,H,L] sum_i gamma_i dgamma_i
     float* gs;     // [B,H,L] online weight gamma_s
-    float* dG;     // [B,H,L,NS] dgamma, then da
+    float* dG;     // [B,H,L,NS] dgamma, then da (MFMA path: [B,H,L] da of the online segment)
     float* dM;     // [B,H,NS,dv,dk] gradient of each cached state ([B,H,NS,dk,dv] on MFMA)
     float* dpp;    // [NR,NS,B*xh,dg] partial sums of dP_i over token ranges
     // the MFMA path (bf16, d_k = d_v = 128 with the forward gate pass):
@@ -101,11 +101,12 @@ struct BwdBuffers {
     void* pf;      // the means as MFMA fragments
     void* mt;      // [B,H,NS,dk,dv] bf16 transposed states
     void* dqh;     // [B,H,L,dk] bf16 dphi(q) from the swapped read
-    float* daT;    // [B,H,NS,L] da_t^(i), segment-major
+    float* daT;    // [B,H,NS,L] dgamma_t^(i), then da_t^(i), segment-major
+    void* ptf;     // the means as B fragments of the du product
 };
 struct BwdWorkspace {
     size_t aon, xps, xtail, on, ot, khat, lse, D, gs, dG, dM, dpp;
-    size_t W, won, inv_l, pf, mt, dqh, daT, total;
+    size_t W, won, inv_l, pf, mt, dqh, daT, ptf, total;
 };
 // The MFMA backward applies where the forward uses the gate pass (bf16, d_k = d_v = 128).
 inline bool bwd_fast(const mc_dims& d) { return gate_pass(d); }
