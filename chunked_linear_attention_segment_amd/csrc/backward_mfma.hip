@@ -367,7 +367,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dm_mfma_kernel(
                                     mt[db][cb][4 * g + e]);
 }
 
-constexpr int OT = 64;     // tokens per r tile and per t tile of the online-segment backward
+constexpr int OT = 64;     // tokens per t tile of the online-segment backward
+constexpr int RT = 128;    // tokens per r tile
 constexpr int NPAD = 136;  // row stride (bf16) of the token-major LDS tiles: 272 bytes
 
 // dM^T (fp32, [r][c]) -> dM (bf16, [c][r]) per cached state, 32 x 32 tiles through LDS
@@ -386,33 +387,32 @@ __global__ __launch_bounds__(256) void dm_cr_kernel(const float* __restrict__ dM
 
 // The online segment's share of dK and dV for d_k = d_v = 128 (bf16), on MFMA.  For token r
 // of segment s, E_r = dM^(s) + sum_{t >= r in s} gamma_t^(s) dy_t phi(q_t)^T, dv_r = E_r phi(k_r)
-// and dphi(k_r) = E_r^T v_r; over a tile of 64 r tokens that is
+// and dphi(k_r) = E_r^T v_r; over a tile of r tokens that is
 //   dV^T[c][r]      = sum_j dM[c][j] phi(k_r)[j] + sum_{t >= r} dy_t[c] P[t][r],
 //                     P[t][r] = gamma_t <phi(q_t), phi(k_r)>
 //   dphi(K)^T[j][r] = sum_c dM[c][j] v_r[c]      + sum_{t >= r} phi(q_t)[j] B[t][r],
 //                     B[t][r] = gamma_t <dy_t, v_r>
-// (the flash-attention backward's dK/dV loop without the softmax).  A workgroup takes one r
-// tile and walks the segment's t tiles from its own on; waves 0..3 form dV, waves 4..7
-// dphi(K), wave (r block rb, t block tb) of each side the 32 x 32 block P or B of its r and
-// t blocks (8 MFMAs over the features), masked (t >= r, t in the segment) and scaled in
-// registers, where it is already the B operand of the token contraction: the k index of the
-// second product is permuted the same way on both sides (the A operand, dy^T or phi(q)^T
-// staged in LDS with tokens along the rows, is read as two 4-token runs per k step).  The
-// two t-block waves of an r block each keep the four 32-row blocks (c or j) of their partial
-// sums and add them through LDS at the end.  The dM term (bf16 copies of dM: [c][j] for dV,
-// the fp32 [j][c] rounded on load for dK) is split between the two t-block waves.  phi(q)
-// and dy of a t tile are staged twice (token-major for the first product, transposed for
-// the second), double-buffered, the next tile loaded into registers during the current one.
+// (the flash-attention backward's dK/dV loop without the softmax).  A workgroup takes one
+// tile of RT = 128 r tokens and walks the segment's 64-token t tiles from the r tile's start
+// on; waves 0..3 form dV, waves 4..7 dphi(K), wave rb of each side the 32 r tokens
+// 32 rb .. + 31.  Per t tile a wave forms the two 32 x 32 blocks P or B of its r block and
+// the tile's two t blocks (8 MFMAs each over the features), masked (t >= r, t in the
+// segment) and scaled in registers, where they are already the B operand of the token
+// contraction: the k index of the second product is permuted the same way on both sides
+// (the A operand, dy^T or phi(q)^T staged in LDS with tokens along the rows, is read as two
+// 4-token runs per k step); its accumulators hold the four 32-row blocks (c or j) of its r
+// block.  The dM term uses bf16 copies of dM ([c][j] for dV; the fp32 [j][c] rounded on load
+// for dK).  phi(q) and dy of a t tile are staged twice (token-major for the first product,
+// transposed for the second), double-buffered, the next tile loaded into registers during
+// the current one.
 __global__ __launch_bounds__(512, 1) void bwd_online_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kh, const bf16_t* __restrict__ K,
     const bf16_t* __restrict__ V, const bf16_t* __restrict__ dY, const float* __restrict__ gs,
     const float* __restrict__ dMT, const bf16_t* __restrict__ dMc, int BH, int L, int C, int NS,
     int phi, float* __restrict__ dK, float* __restrict__ dV) {
     // one LDS block: phi(q) [t][j] and dy [t][c] token-major, phi(q)^T [j][t] and dy^T [c][t],
-    // gamma_t (0 past the segment), two buffers each; after the walk its first 64 KB hold
-    // the partial sums handed between waves
+    // gamma_t (0 past the segment), two buffers each
     constexpr int NB = 2 * OT * NPAD * 2, TB = 2 * 128 * TPAD * 2;
-    static_assert(2 * NB >= 4 * 4 * 16 * 64 * 4, "reduction area");
     __shared__ uint4 lds[(2 * NB + 2 * TB + 2 * OT * 4) / 16];
     unsigned char* lb = reinterpret_cast<unsigned char*>(lds);
     bf16_t(*qn)[OT][NPAD] = reinterpret_cast<bf16_t(*)[OT][NPAD]>(lb);
@@ -426,13 +426,14 @@ __global__ __launch_bounds__(512, 1) void bwd_online_mfma_kernel(
     const size_t bh = (blockIdx.x % nsb) % BH;
     const int s = (blockIdx.x % nsb) / BH;
     const int t0 = s * C, n = min(C, L - t0);
-    const int r0 = R * OT;
+    const int r0 = R * RT;
     if (r0 >= n) return;  // uniform: the segment has no r tile R
     const int NT = (n + OT - 1) / OT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, half = lane >> 5;
     const bool kside = wave >= 4;  // waves 4..7: dphi(K); 0..3: dV
-    const int rb = (wave >> 1) & 1, tb = wave & 1;
-    const int rr = r0 + rb * 32 + l32;  // this lane's r (segment-relative; rows past the
+    const int rb = wave & 3;
+    const int rbase = r0 + rb * 32;     // the wave's first r
+    const int rr = rbase + l32;         // this lane's r (segment-relative; rows past the
                                         // segment are read clamped, their sums not stored)
     const size_t rrow = bh * L + min(t0 + rr, L - 1);
 
@@ -480,15 +481,15 @@ __global__ __launch_bounds__(512, 1) void bwd_online_mfma_kernel(
         if (tid < OT) sgo[buf][tid] = tt0 + tid < n ? rg : 0.f;
     };
 
-    load(r0);
-    stage(0, r0);
-    if (R + 1 < NT) load(r0 + OT);
-    // the dM term: blocks 2 tb and 2 tb + 1 of the c (dV) or j (dK) rows
+    const int T0 = r0 / OT;  // the t tile holding the r tile's first token
+    load(T0 * OT);
+    stage(0, T0 * OT);
+    if (T0 + 1 < NT) load((T0 + 1) * OT);
+    // the dM term over all four 32-row blocks of c (dV) or j (dK)
     {
         const size_t st = (bh * NS + s) * (size_t)(128 * 128);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            if ((b >> 1) != tb) continue;  // uniform
             const int m = b * 32 + l32;
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
@@ -508,12 +509,18 @@ __global__ __launch_bounds__(512, 1) void bwd_online_mfma_kernel(
         }
     }
     __syncthreads();
-    for (int T = R; T < NT; ++T) {
-        const int buf = (T - R) & 1;
+    for (int T = T0; T < NT; ++T) {
+        const int buf = (T - T0) & 1;
         const int tt0 = T * OT;
-        if (!(T == R && tb < rb)) {  // uniform: a t block wholly before the r block is masked
-            // first product: D[t][r] over the 128 features (phi(q) phi(k)^T or dy v^T)
-            const bf16_t(*an)[NPAD] = kside ? yn[buf] : qn[buf];
+        // first products: D[t][r] over the 128 features (phi(q) phi(k)^T or dy v^T) for the
+        // tile's two t blocks; a block wholly before the wave's r block is masked
+        const bf16_t(*an)[NPAD] = kside ? yn[buf] : qn[buf];
+        u32x4_t pf[2][2];
+        bool live[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            live[tb] = tt0 + tb * 32 + 31 >= rbase;  // uniform
+            if (!live[tb]) continue;
             f32x16_t sa = zero;
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
@@ -522,7 +529,6 @@ __global__ __launch_bounds__(512, 1) void bwd_online_mfma_kernel(
                 sa = mfma32(a, kv[ks], sa);
             }
             // lane holds r = rr and t = tt0 + 32 tb + 8 g + 4 half + e (value 4 g + e)
-            u32x4_t pf[2];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int tl = tb * 32 + 8 * g + 4 * half;
@@ -531,12 +537,16 @@ __global__ __launch_bounds__(512, 1) void bwd_online_mfma_kernel(
                 float pv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) pv[e] = tt0 + tl + e >= rr ? sa[4 * g + e] * gg[e] : 0.f;
-                pf[g >> 1][(g & 1) * 2] = pack_bf16x2(pv[0], pv[1]);
-                pf[g >> 1][(g & 1) * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
+                pf[tb][g >> 1][(g & 1) * 2] = pack_bf16x2(pv[0], pv[1]);
+                pf[tb][g >> 1][(g & 1) * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
             }
-            // second product over the block's 32 tokens: k step kk holds, in slots 0..3 and
-            // 4..7, the tokens 16 kk + 4 half + 0..3 and 16 kk + 8 + 4 half + 0..3
-            const bf16_t(*at)[TPAD] = kside ? qtt[buf] : ytt[buf];
+        }
+        // second products over the tile's tokens: k step kk of block tb holds, in slots 0..3
+        // and 4..7, the tokens 32 tb + 16 kk + 4 half + 0..3 and 32 tb + 16 kk + 8 + 4 half + 0..3
+        const bf16_t(*at)[TPAD] = kside ? qtt[buf] : ytt[buf];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            if (!live[tb]) continue;
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -545,7 +555,7 @@ __global__ __launch_bounds__(512, 1) void bwd_online_mfma_kernel(
                     const uint2 lo = *reinterpret_cast<const uint2*>(&at[b * 32 + l32][c0]);
                     const uint2 hi = *reinterpret_cast<const uint2*>(&at[b * 32 + l32][c0 + 8]);
                     const u32x4_t a = {lo.x, lo.y, hi.x, hi.y};
-                    acc[b] = mfma32(a, pf[kk], acc[b]);
+                    acc[b] = mfma32(a, pf[tb][kk], acc[b]);
                 }
         }
         if (T + 1 < NT) {
@@ -555,18 +565,7 @@ __global__ __launch_bounds__(512, 1) void bwd_online_mfma_kernel(
         }
         __syncthreads();
     }
-    // the t-block-1 waves hand their partial sums to the t-block-0 waves (LDS of the
-    // token-major tiles, free after the last barrier): [side, rb][block][value][lane]
-    float* red = reinterpret_cast<float*>(lb);
-    const int pair = (kside ? 2 : 0) + rb;
-    if (tb == 1) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) red[((pair * 4 + b) * 16 + i) * 64 + lane] = acc[b][i];
-    }
-    __syncthreads();
-    if (tb == 1 || rr >= n) return;
+    if (rr >= n) return;
     const size_t orow = (bh * L + t0 + rr) * 128;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -575,7 +574,7 @@ __global__ __launch_bounds__(512, 1) void bwd_online_mfma_kernel(
             const int m = b * 32 + 8 * g + 4 * half;  // c (dV) or j (dK) of values 4 g .. 4 g + 3
             float o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = acc[b][4 * g + e] + red[((pair * 4 + b) * 16 + 4 * g + e) * 64 + lane];
+            for (int e = 0; e < 4; ++e) o[e] = acc[b][4 * g + e];
             if (kside && phi) {
                 const u32x2_t kw = *reinterpret_cast<const u32x2_t*>(K + orow + m);
                 o[0] *= fminf(feature(bf_lo(kw[0]), 1), 1.f);
@@ -834,7 +833,7 @@ int launch_bwd_online_mfma(const mc_dims& d, const BwdBuffers& w, const void* Q,
     const int BH = d.B * d.H;
     // dM in bf16, [c][j], over the transposed states of the swapped read (no longer needed)
     hipLaunchKernelGGL(dm_cr_kernel, dim3(BH * NS, 4, 4), dim3(256), 0, st, w.dM, (bf16_t*)w.mt);
-    const int rt = (d.seg_len + OT - 1) / OT;  // r tiles of a segment
+    const int rt = (d.seg_len + RT - 1) / RT;  // r tiles of a segment
     hipLaunchKernelGGL(bwd_online_mfma_kernel, dim3(rt * NS * BH), dim3(512), 0, st,
                        (const bf16_t*)Q, (const bf16_t*)(d.phi ? w.khat : K), (const bf16_t*)K,
                        (const bf16_t*)V, (const bf16_t*)dY, w.gs, w.dM, (const bf16_t*)w.mt, BH,
