@@ -336,6 +336,28 @@ __global__ __launch_bounds__(256) void bwd_dxw_kernel(const T* __restrict__ U,
     const size_t bx = blockIdx.y;
     const int b = (int)(bx / xh), hx = (int)(bx % xh);
     const int h0 = xh == 1 ? 0 : hx, h1 = xh == 1 ? H : hx + 1;
+    if (DG % 8 == 0) {  // 8 consecutive columns per thread and step
+        const int g8 = DG / 8;
+        for (int idx = threadIdx.x; idx < 64 * g8; idx += 256) {
+            const int t = t0 + idx / g8, e = (idx % g8) * 8;
+            if (t >= L) break;
+            const int s = t / C, j = t - s * C;
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int h = h0; h < h1; ++h) {
+                const size_t bh = (size_t)b * H + h;
+                const float a = dA[diag ? bh * L + t : (bh * L + t) * NS + s];
+                float u[8];
+                ld8(U, (bh * L + t) * DG + e, u);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] += a * u[k];
+            }
+            const float inv = 1.f / (float)(j + 1);
+            float* o = w + (bx * L + t) * DG + e;
+            *reinterpret_cast<float4*>(o) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+            *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+        }
+        return;
+    }
     for (int idx = threadIdx.x; idx < 64 * DG; idx += 256) {
         const int t = t0 + idx / DG, e = idx % DG;
         if (t >= L) break;
