@@ -503,10 +503,11 @@ int launch_grm_backward(const mc_dims& d, const BwdBuffers& w, const void* Q, co
         wb.khat = nullptr;
     }
     if (fast) {
-        // the forward's gate pass (softmax numerators per read tile), the online read, then
-        // dgamma, dphi(q), the gate backward and dM on MFMA
+        // the forward's gate pass (softmax numerators per read tile), the online read's
+        // product with dy (dgamma of the online segment, into on as [B,H,L]), then dgamma,
+        // dphi(q), the gate backward and dM on MFMA
         rc = launch_gate_w(d, U, w.xps, P, w.pf, w.W, w.won, w.inv_l, stream);
-        if (!rc) rc = launch_scan_mfma_online(d, Q, K, V, w.on, stream);
+        if (!rc) rc = launch_scan_mfma_dgs(d, Q, K, V, dY, w.on, stream);
         if (!rc) rc = launch_bwd_fast(d, wb, Q, K, V, U, M, M_lo, P, dY, dQ, dU, stream);
         if (rc) return rc;
     } else {

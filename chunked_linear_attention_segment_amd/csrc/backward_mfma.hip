@@ -618,17 +618,17 @@ __global__ void ptf_kernel(const float* __restrict__ P, int NS, int DG, int NSK,
 
 // The softmax backward of the gate for d_k = d_v = 128 and d_g <= 128, one 256-token gate
 // tile per workgroup: gamma_i = W_t^(i) / l_t (i < s), gamma_s = won_t / l_t; dgamma of the
-// online segment <dy_t, O_on[t]>; D_t = sum_i gamma_i dgamma_i; da_i = gamma_i (dgamma_i - D)
-// written over dgamma (segment-major, [i][t]); da_s; du_t = sum_i da_i P_i on MFMA plus
-// da_s times the prefix mean x_t; dq = dphi(q) phi'(q) with dphi(q) the bf16 output of the
-// swapped read.  Wave w takes tokens 32 w .. + 31 (lane l32 = token): pass 1 sums D over the
+// online segment <dy_t, O_on[t]> (formed by the online scan); D_t = sum_i gamma_i dgamma_i;
+// da_i = gamma_i (dgamma_i - D) written over dgamma (segment-major, [i][t]); da_s;
+// du_t = sum_i da_i P_i on MFMA plus da_s times the prefix mean x_t; dq = dphi(q) phi'(q)
+// with dphi(q) the bf16 output of the swapped read.  Wave w takes tokens 32 w .. + 31 (lane l32 = token): pass 1 sums D over the
 // segments (half h of the wave the segments 16 ks + 8 h + 0..7), pass 2 forms da for the
 // same segments, which are then the A fragment (bf16 high part and rest) of 32x32x16 MFMAs
 // against the means' fragments (high and rest; the rest times the rest is dropped).
 __global__ __launch_bounds__(512) void bwd_gate_mfma_kernel(
     const bf16_t* __restrict__ Q, const float* __restrict__ xps, const uint16_t* __restrict__ Wg,
-    const float* __restrict__ won, const float* __restrict__ inv_l, const float* __restrict__ O_on,
-    const bf16_t* __restrict__ dY, const bf16_t* __restrict__ dqh, const u32x4_t* __restrict__ ptf,
+    const float* __restrict__ won, const float* __restrict__ inv_l, const float* __restrict__ dgs_i,
+    const bf16_t* __restrict__ dqh, const u32x4_t* __restrict__ ptf,
     int L, int C, int NS, int DG, int H, int xh, int phi, float* __restrict__ daT,
     float* __restrict__ das_o, float* __restrict__ gs_o, float* __restrict__ dU,
     float* __restrict__ dQ) {
@@ -651,22 +651,7 @@ __global__ __launch_bounds__(512) void bwd_gate_mfma_kernel(
     const int tc = min(t, L - 1);
     const int sg = tc / C;
     const float il = inv_l[bh * L + tc];
-    // dgamma of the online segment: half h takes the 64 columns 64 h ..
-    float part = 0.f;
-    {
-        const bf16_t* yr = dY + (bh * L + tc) * 128 + half * 64;
-        const float* orow = O_on + (bh * L + tc) * 128 + half * 64;
-#pragma unroll
-        for (int c = 0; c < 64; c += 8) {
-            const u32x4_t y = *reinterpret_cast<const u32x4_t*>(yr + c);
-            const float4 o0 = *reinterpret_cast<const float4*>(orow + c);
-            const float4 o1 = *reinterpret_cast<const float4*>(orow + c + 4);
-            part += bf_lo(y[0]) * o0.x + bf_hi(y[0]) * o0.y + bf_lo(y[1]) * o0.z +
-                    bf_hi(y[1]) * o0.w + bf_lo(y[2]) * o1.x + bf_hi(y[2]) * o1.y +
-                    bf_lo(y[3]) * o1.z + bf_hi(y[3]) * o1.w;
-        }
-    }
-    const float dgs = part + __shfl_xor(part, 32);
+    const float dgs = dgs_i[bh * L + tc];  // dgamma of the online segment
     // pass 1: sum_i W_i dgamma_i over this half's segments, then both halves
     float dp = 0.f;
 #pragma unroll 2
@@ -810,7 +795,7 @@ int launch_bwd_fast(const mc_dims& d, const BwdBuffers& w, const void* Q, const 
     hipLaunchKernelGGL(ptf_kernel, dim3((unsigned)((nptf + 255) / 256)), dim3(256), 0, st, P, NS,
                        d.d_g, nsk, nptf, (u32x4_t*)w.ptf);
     hipLaunchKernelGGL(bwd_gate_mfma_kernel, dim3((d.L + GTOK - 1) / GTOK, BH), dim3(512), 0, st,
-                       (const bf16_t*)Q, w.xps, w.W, w.won, w.inv_l, w.on, (const bf16_t*)dY,
+                       (const bf16_t*)Q, w.xps, w.W, w.won, w.inv_l, w.on,
                        (const bf16_t*)w.dqh, (const u32x4_t*)w.ptf, d.L, d.seg_len, NS, d.d_g,
                        d.H, d.x_heads, d.phi, w.daT, w.dG, w.gs, dU, dQ);
     // dM and dP take the partial sums of the split workgroups: zero them first (a kernel, so

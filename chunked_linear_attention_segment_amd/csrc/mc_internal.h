@@ -85,7 +85,7 @@ struct BwdBuffers {
     float* aon;    // [B,H,L] online logits
     float* xps;    // [B,xh,L,dg] segment-causal prefix sums of X
     float* xtail;  // their per-chunk partial sums
-    float* on;     // [B,H,L,dv] online read M_t^(s) phi(q_t)
+    float* on;     // [B,H,L,dv] online read M_t^(s) phi(q_t) (MFMA path: [B,H,L] <dy_t, it>)
     float* ot;     // [B,H,L,dk] M_t^(s)T dy_t
     void* khat;    // [B,H,L,dk] phi(K) in the input dtype (elu + 1 only)
     float* lse;    // [B,H,L] log of the softmax denominator
@@ -124,6 +124,9 @@ inline int bwd_dp_range(int L) {
 BwdWorkspace bwd_workspace(const mc_dims& d);
 int launch_scan_mfma_online(const mc_dims& d, const void* Q, const void* K, const void* V,
                             float* O_on, void* stream);
+// dgs[t] = <dy_t, O_on[t]> ([B,H,L]) from the online read, which is not stored
+int launch_scan_mfma_dgs(const mc_dims& d, const void* Q, const void* K, const void* V,
+                         const void* dY, float* dgs, void* stream);
 int launch_grm_backward(const mc_dims& d, const BwdBuffers& w, const void* Q, const void* K,
                         const void* V, const void* U, const void* X, const float* M,
                         const uint16_t* M_lo, const float* P, const void* dY, float* dQ,

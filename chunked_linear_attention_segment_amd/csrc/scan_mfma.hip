@@ -71,7 +71,8 @@ template <int DK, int DV, bool ON, bool SW>
 __global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     int L, int C, int NS, int phi, float* __restrict__ M, bf16_t* __restrict__ M_lo,
-    float* __restrict__ O_on, SwlaGates gt, const SegArg sg, const float* __restrict__ M0) {
+    float* __restrict__ O_on, SwlaGates gt, const SegArg sg, const float* __restrict__ M0,
+    const bf16_t* __restrict__ dY, float* __restrict__ dgs) {
     constexpr int NT = DV * 2;      // threads: one wave per 32 value rows
     constexpr int DB = DK / 32;     // 32-row blocks of d
     constexpr int KSD = DK / 16;    // k-steps over d
@@ -82,6 +83,8 @@ __global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
     __shared__ float cf[GW][GW + 1];  // SWLA weights c[t][r] of the chunk
     __shared__ float dz[GW];          // SWLA decay of Z at chunk token t: alpha_{j0+1..j0+t}
     __shared__ float ga[GW + 1], gb[GW + 1], gl[GW];  // the chunk's gates (+ next token's)
+    // with dgs: each wave's share of <dy_t, O_on[t]> per chunk token (chunk parity buffers)
+    __shared__ float red[ON ? 2 : 1][ON ? DV / 32 : 1][ON ? CH : 1];
 
     const int s = blockIdx.x;
     const size_t bh = blockIdx.y;
@@ -124,8 +127,20 @@ __global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
     const bf16_t* Vs = V + (bh * L + t0) * DV;
 
     const size_t gbase = bh * L + t0;
+    // dgs of the chunk at jp from the waves' shares (read after the barrier that ends it)
+    auto flush_dgs = [&](int jp) {
+        if constexpr (ON) {
+            if (tid < min(CH, len - jp)) {
+                float a = 0.f;
+#pragma unroll
+                for (int w = 0; w < DV / 32; ++w) a += red[(jp / CH) & 1][w][tid];
+                dgs[gbase + jp + tid] = a;
+            }
+        }
+    };
     for (int j0 = 0; j0 < len; j0 += CH) {
         const int n = min(CH, len - j0);
+        if (dgs && j0 > 0) flush_dgs(j0 - CH);
         const bool last = j0 + n == len;  // the segment ends in this chunk
         if (SW) {
             // gates of the chunk's tokens, zero past its end; slot CH is the next token's
@@ -316,11 +331,27 @@ __global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
                 mt[db] = scan_mfma(ka, va[ks], mt[db]);
             }
         }
-        // ---- online read out: O_on[t][cv] (4 consecutive cv per register group) ----
+        // ---- online read out: O_on[t][cv] (4 consecutive cv per register group), or its
+        // product with dy_t summed over the wave's value rows ----
 #pragma unroll
         for (int tb = 0; tb < 2 && ON; ++tb) {
             const int tl = tb * 32 + l32;
-            if (tl < n) {
+            if (dgs) {
+                float part = 0.f;
+                if (tl < n) {
+                    const bf16_t* yrow = dY + (gbase + j0 + tl) * DV + wave * 32 + half * 4;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const u32x2_t y = *reinterpret_cast<const u32x2_t*>(yrow + 8 * g);
+                        part += ot[tb][4 * g] * __uint_as_float(y[0] << 16) +
+                                ot[tb][4 * g + 1] * __uint_as_float(y[0] & 0xffff0000u) +
+                                ot[tb][4 * g + 2] * __uint_as_float(y[1] << 16) +
+                                ot[tb][4 * g + 3] * __uint_as_float(y[1] & 0xffff0000u);
+                    }
+                }
+                part += __shfl_xor(part, 32);
+                if (half == 0) red[(j0 / CH) & 1][wave][tl] = part;
+            } else if (tl < n) {
                 float* orow = O_on + (bh * L + t0 + j0 + tl) * DV + wave * 32 + half * 4;
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
@@ -340,6 +371,7 @@ __global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
                                           pk2(mt[db][8 * hh + 6], mt[db][8 * hh + 7])};
         __syncthreads();
     }
+    if (dgs && len > 0) flush_dgs(((len - 1) / CH) * CH);
     // ---- emit the segment state: M[cv][d] (fp32 and bf16), 4 consecutive d per group ----
     if (!M) return;  // online read only
     const int cv = wave * 32 + l32;
@@ -363,16 +395,18 @@ template <int DK, int DV>
 static int launch_scan_mfma_t(const mc_dims& d, const void* Q, const void* K, const void* V,
                               float* M, uint16_t* M_lo, float* O_on, const SwlaGates& gt,
                               hipStream_t st, const SegArg& sg = kConstSegM,
-                              const float* M0 = nullptr) {
+                              const float* M0 = nullptr, const void* dY = nullptr,
+                              float* dgs = nullptr) {
     const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
 #define MC_SCAN(ON, SW)                                                                        \
     hipLaunchKernelGGL((scan_mfma_kernel<DK, DV, ON, SW>), dim3(NS, d.B * d.H), dim3(DV * 2),   \
                        0, st, (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, d.L,        \
-                       d.seg_len, NS, d.phi, M, (bf16_t*)M_lo, O_on, gt, sg, M0)
+                       d.seg_len, NS, d.phi, M, (bf16_t*)M_lo, O_on, gt, sg, M0,           \
+                       (const bf16_t*)dY, dgs)
     if (gt.alpha) {  // SWLA: the read takes the online term from O_on, so it is always written
         if (!O_on) return (int)hipErrorInvalidValue;
         MC_SCAN(true, true);
-    } else if (O_on) {
+    } else if (O_on || dgs) {
         MC_SCAN(true, false);
     } else {
         MC_SCAN(false, false);
@@ -409,6 +443,25 @@ int launch_scan_mfma_online(const mc_dims& d, const void* Q, const void* K, cons
 #define MC_SD(DK, DV)                                                                          \
     if (d.d_k == DK && d.d_v == DV)                                                            \
         return launch_scan_mfma_t<DK, DV>(d, Q, K, V, nullptr, nullptr, O_on, none, st);
+    MC_SD(128, 128)
+    MC_SD(128, 64)
+    MC_SD(64, 128)
+    MC_SD(64, 64)
+#undef MC_SD
+    return -1;
+}
+
+// The online read's product with dy per token, dgs[t] = <dy_t, O_on[t]> ([B,H,L]), in place
+// of O_on; -1 when the sizes are not covered.
+int launch_scan_mfma_dgs(const mc_dims& d, const void* Q, const void* K, const void* V,
+                         const void* dY, float* dgs, void* stream) {
+    if (d.dtype != MC_BF16 || !dgs) return -1;
+    hipStream_t st = (hipStream_t)stream;
+    const SwlaGates none{};
+#define MC_SD(DK, DV)                                                                          \
+    if (d.d_k == DK && d.d_v == DV)                                                            \
+        return launch_scan_mfma_t<DK, DV>(d, Q, K, V, nullptr, nullptr, nullptr, none, st,     \
+                                          kConstSegM, nullptr, dY, dgs);
     MC_SD(128, 128)
     MC_SD(128, 64)
     MC_SD(64, 128)
