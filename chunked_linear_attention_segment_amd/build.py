@@ -23,13 +23,13 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "scan.hip", "readout.hip", "decode.hip", "read_mfma.hip", "scan_mfma.hip",
-           "gate.hip", "backward.hip", "backward_mfma.hip", "ssc_gather.hip"]
+           "gate.hip", "backward.hip", "backward_mfma.hip", "ssc_gather.hip", "dgamma_mfma.hip"]
 PEAK_SOURCES = ["peak.hip"]
-# Per-file flags.  The gated read is written in the exact issue order it needs (each MFMA
-# followed by the VALU work of the next k-step, LDS reads two k-steps ahead); the machine
-# schedulers would regroup it, so they are off for that file.
-FILE_FLAGS = {"read_mfma.hip": ["-mllvm", "-enable-misched=false",
-                                "-mllvm", "-enable-post-misched=false"]}
+# Per-file flags.  The gated read and the dgamma pass are written in the exact issue order
+# they need (each MFMA followed by the VALU work it hides, LDS reads two k-steps ahead); the
+# machine schedulers would regroup it, so they are off for those files.
+FILE_FLAGS = {name: ["-mllvm", "-enable-misched=false", "-mllvm", "-enable-post-misched=false"]
+              for name in ("read_mfma.hip", "dgamma_mfma.hip")}
 
 # Packed-fp32 VALU ops are kept out of the device code (the host pass warns that it does
 # not know the feature; that warning is harmless).

@@ -6,9 +6,9 @@
 //     Eq. 9 with the roles swapped -- queries dy, keys v, values phi(k), states M^(i)^T, the
 //     same gate -- so it runs on the forward read kernel (grm_read_kernel) with transposed
 //     bf16 states (transpose_states_kernel) and the forward gate pass's softmax numerators.
-//   dgamma_t^(i) = <dy_t, M^(i) phi(q_t)>: bwd_dgamma_kernel, per 256-token tile, streams the
-//     states through LDS and contracts each with the tile's phi(q) on MFMA, then reduces the
-//     products against dy in registers.
+//   dgamma_t^(i) = <dy_t, M^(i) phi(q_t)>: launch_bwd_dgamma (dgamma_mfma.hip), per 256-token
+//     tile, streams the states through LDS and contracts each with the tile's phi(q) on MFMA,
+//     then reduces the products against dy in registers.
 //   dM^(i) = sum_t gamma_t^(i) dy_t phi(q_t)^T: bwd_dm_mfma_kernel, per group of four cached
 //     segments and range of later tokens, walks the tokens in chunks of 64 (the scan's
 //     state-update contraction with phi(q) in place of phi(k) and gamma dy in place of v),
@@ -58,120 +58,6 @@ __global__ __launch_bounds__(256) void transpose_states_kernel(const bf16_t* __r
     for (int y = ty; y < 32; y += 8) tile[y][tx] = src[(size_t)(c0 + y) * DK + r0 + tx];
     __syncthreads();
     for (int y = ty; y < 32; y += 8) dst[(size_t)(r0 + y) * DV + c0 + tx] = tile[tx][y];
-}
-
-constexpr int DT = 256;     // tokens per dgamma workgroup: 4 waves x 2 blocks of 32
-constexpr int SROW = 136;   // LDS row stride (bf16) of a staged state: 16 bytes of padding
-
-// dgamma_t^(i) for i < s_t, d_k = d_v = 128, written segment-major ([i][t]).  Wave w owns
-// tokens t0 + 64w .. + 63 (two blocks
-// of 32); per state: O^(i) = M^(i) phi(q) as 4 (rows) x 2 (token blocks) accumulator tiles,
-// then dgamma = sum_c dy[c] O[c][t] (16 rows per lane, the two half-waves combined).  States are
-// double-buffered in LDS, loaded one ahead through registers.
-__global__ __launch_bounds__(256, 1) void bwd_dgamma_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ dY, const bf16_t* __restrict__ M_lo,
-    int L, int C, int NS, int phi, float* __restrict__ dGT) {
-    __shared__ __attribute__((aligned(16))) bf16_t ms[2][128][SROW];
-    const int ntile = gridDim.x;
-    const int tile = ntile - 1 - blockIdx.x;  // the tiles that read the most states first
-    const size_t bh = blockIdx.y;
-    const int t0 = tile * DT;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, half = lane >> 5;
-    const int s_hi = (min(L, t0 + DT) - 1) / C;
-    if (s_hi == 0) return;  // uniform: no token of the tile reads a cached state
-
-    u32x4_t qb[2][8];
-    float dyv[2][4][16];
-    int tok[2], stok[2];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const int t = t0 + wave * 64 + tb * 32 + l32;
-        const bool ok = t < L;
-        tok[tb] = t;
-        stok[tb] = ok ? t / C : 0;
-        const bf16_t* qr = Q + (bh * L + (ok ? t : 0)) * 128 + half * 8;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (ok) v = phi8(*reinterpret_cast<const u32x4_t*>(qr + ks * 16), phi);
-            qb[tb][ks] = v;
-        }
-        const bf16_t* dr = dY + (bh * L + (ok ? t : 0)) * 128;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2_t w = {0u, 0u};
-                if (ok) w = *reinterpret_cast<const u32x2_t*>(dr + cb * 32 + 8 * g + 4 * half);
-                dyv[tb][cb][4 * g + 0] = bf_lo(w[0]);
-                dyv[tb][cb][4 * g + 1] = bf_hi(w[0]);
-                dyv[tb][cb][4 * g + 2] = bf_lo(w[1]);
-                dyv[tb][cb][4 * g + 3] = bf_hi(w[1]);
-            }
-    }
-
-    const bf16_t* Sb = M_lo + bh * (size_t)NS * 128 * 128;
-    // states two ahead: register sets ra / rb alternate (the loop is unrolled by two so that
-    // both stay statically indexed), LDS buffers alternate with the state's parity
-    u32x4_t ra[8], rb[8];
-    auto load_state = [&](int i, u32x4_t* r) {
-        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(Sb + (size_t)i * 128 * 128);
-#pragma unroll
-        for (int it = 0; it < 8; ++it) r[it] = src[tid + 256 * it];
-    };
-    auto store_state = [&](int buf, const u32x4_t* r) {
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int idx = tid + 256 * it;
-            *reinterpret_cast<u32x4_t*>(&ms[buf][idx >> 4][(idx & 15) * 8]) = r[it];
-        }
-    };
-    const f32x16_t zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
-                           0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    // state i from LDS buffer i & 1: contract, reduce against dy, write dgamma
-    auto step = [&](int i) {
-        const int buf = i & 1;
-        f32x16_t acc[4][2];
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const u32x4_t a =
-                    *reinterpret_cast<const u32x4_t*>(&ms[buf][cb * 32 + l32][ks * 16 + half * 8]);
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
-                    acc[cb][tb] = mfma32(a, qb[tb][ks], ks == 0 ? zero : acc[cb][tb]);
-            }
-        }
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            float part = 0.f;
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) part += dyv[tb][cb][r] * acc[cb][tb][r];
-            part += __shfl_xor(part, 32);
-            if (half == 0 && tok[tb] < L && i < stok[tb])
-                dGT[(bh * NS + i) * (size_t)L + tok[tb]] = part;
-        }
-    };
-    load_state(0, ra);
-    if (1 < s_hi) load_state(1, rb);
-    store_state(0, ra);
-    __syncthreads();
-    for (int i = 0; i < s_hi; i += 2) {
-        // state i is in LDS, state i + 1 in rb; fetch i + 2 into ra
-        if (i + 2 < s_hi) load_state(i + 2, ra);
-        step(i);
-        if (i + 1 < s_hi) store_state((i + 1) & 1, rb);
-        __syncthreads();
-        if (i + 1 >= s_hi) break;
-        // state i + 1 is in LDS, state i + 2 in ra; fetch i + 3 into rb
-        if (i + 3 < s_hi) load_state(i + 3, rb);
-        step(i + 1);
-        if (i + 2 < s_hi) store_state(i & 1, ra);
-        __syncthreads();
-    }
 }
 
 constexpr int CHK = 64;    // tokens per chunk of the dM walk
@@ -785,9 +671,8 @@ int launch_bwd_fast(const mc_dims& d, const BwdBuffers& w, const void* Q, const 
     int rc = launch_read_mfma(ds, false, 0, dY, V, w.khat ? w.khat : K, U, w.xps,
                               (const uint16_t*)w.mt, P, nullptr, nullptr, gw, w.dqh, stream);
     if (rc) return rc;
-    hipLaunchKernelGGL(bwd_dgamma_kernel, dim3((d.L + DT - 1) / DT, BH), dim3(256), 0, st,
-                       (const bf16_t*)Q, (const bf16_t*)dY, (const bf16_t*)M_lo, d.L, d.seg_len,
-                       NS, d.phi, w.daT);
+    rc = launch_bwd_dgamma(d, Q, dY, M_lo, w.daT, stream);
+    if (rc) return rc;
     // the means as the du product's B fragments, then the gate backward (da over dgamma;
     // da of the online segment into dG, used as [B,H,L])
     const int nsk = (NS + 15) / 16;

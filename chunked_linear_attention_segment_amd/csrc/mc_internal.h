@@ -113,6 +113,9 @@ inline bool bwd_fast(const mc_dims& d) { return gate_pass(d); }
 int launch_bwd_fast(const mc_dims& d, const BwdBuffers& w, const void* Q, const void* K,
                     const void* V, const void* U, const float* M, const uint16_t* M_lo,
                     const float* P, const void* dY, float* dQ, float* dU, void* stream);
+// dgamma_t^(i) = <dy_t, M^(i) phi(q_t)> (bf16, d_k = d_v = 128), segment-major [B,H,NS,L]
+int launch_bwd_dgamma(const mc_dims& d, const void* Q, const void* dY, const uint16_t* M_lo,
+                      float* dGT, void* stream);
 // the online segment's dK and dV for the MFMA backward (dM stored transposed)
 int launch_bwd_online_mfma(const mc_dims& d, const BwdBuffers& w, const void* Q, const void* K,
                            const void* V, const void* dY, float* dK, float* dV, void* stream);
