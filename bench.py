@@ -578,7 +578,7 @@ def run_log_segments(args, rec, dev):
     P = torch.empty((B, 1, NS, dg), dtype=torch.float32, device=dev)
     O_on = torch.empty((B, H, L, dv), dtype=torch.float32, device=dev)
     Y = torch.empty((B, H, L, dv), dtype=torch.bfloat16, device=dev)
-    ws = mc.workspace(d, mc.MC_OP_GRM, device=dev)
+    ws = mc.workspace(d, mc.MC_OP_GRM_SEGS, top_k=NS, device=dev)
     wss = mc.workspace_segs(d, NS, device=dev)
     stream = torch.cuda.current_stream()
 

@@ -27,8 +27,8 @@ MC_ERR_ALIGN, MC_ERR_WORKSPACE, MC_ERR_HIP, MC_ERR_CAPACITY, MC_ERR_SCRATCH = 4,
 MC_NOALLOC_SCRATCH_BYTES = 64 << 20
 MC_F32, MC_BF16 = 0, 1
 MC_PHI_IDENTITY, MC_PHI_ELU1 = 0, 1
-MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE, MC_OP_GRM_BACKWARD, MC_OP_SCAN_SEGS = \
-    0, 1, 2, 3, 4, 5
+MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE, MC_OP_GRM_BACKWARD, MC_OP_SCAN_SEGS, \
+    MC_OP_GRM_SEGS = 0, 1, 2, 3, 4, 5, 6
 
 EXPORTED = ["mc_abi_version", "mc_status_str", "mc_workspace_bytes", "mc_scan_prefill",
             "mc_grm_readout", "mc_ssc_readout", "mc_decode_step", "mc_scan_prefill_segs",
@@ -323,7 +323,7 @@ def prefill_grm_segs(dims, seg_off, Q, K, V, U, X, want_gamma=False, stream=None
     Y = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch_dtype(dims), device=dev)
     G = torch.empty((dims.B, dims.H, dims.L, NS), dtype=torch.float32,
                     device=dev) if want_gamma else None
-    ws = workspace(dims, MC_OP_GRM, device=dev)
+    ws = workspace(dims, MC_OP_GRM_SEGS, top_k=NS, device=dev)
     mc_grm_readout_segs(dims, seg_off, Q, U, X, M, M_lo, P, O_on, Y, G, ws=ws, stream=stream)
     out = {"Y": Y, "M": M, "M_lo": M_lo, "P": P, "O_on": O_on}
     if want_gamma:
@@ -347,7 +347,8 @@ def prefill_grm_swla(dims, alpha, beta, lam, Q, K, V, U, X, seg_off=None, want_g
     Y = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch_dtype(dims), device=dev)
     G = torch.empty((dims.B, dims.H, dims.L, NS), dtype=torch.float32,
                     device=dev) if want_gamma else None
-    ws = workspace(dims, MC_OP_GRM, device=dev)
+    ws = workspace(dims, MC_OP_GRM if seg_off is None else MC_OP_GRM_SEGS, top_k=NS,
+                   device=dev)
     if seg_off is None:
         mc_grm_readout(dims, Q, None, None, U, X, M, M_lo, P, O_on, Y, G, ws=ws, stream=stream)
     else:

@@ -23,26 +23,27 @@ static size_t xps_ws(const mc_dims& d) {
     return read_mfma_covers(d) ? xps_only(d) + align256(sizeof(float) * xps_tail_floats(d)) : 0;
 }
 
-static size_t gate_w_bytes(const mc_dims& d) {
+// the gate pass's numerators for NS segments (NS = 0: the constant segment length's count)
+static size_t gate_w_bytes(const mc_dims& d, int NS = 0) {
     const size_t T = ((size_t)d.L + kGateTile - 1) / kGateTile;
-    return sizeof(uint16_t) * (size_t)d.B * d.H * T * num_segments(d) * kGateTile;
+    return sizeof(uint16_t) * (size_t)d.B * d.H * T * (NS ? NS : num_segments(d)) * kGateTile;
 }
 
-bool gate_pass(const mc_dims& d) {
+bool gate_pass(const mc_dims& d, int NS) {
     return read_mfma_covers(d) && d.d_k == 128 && d.d_v == 128 &&
-           gate_w_bytes(d) <= kGateMaxBytes;
+           gate_w_bytes(d, NS) <= kGateMaxBytes;
 }
 
-GrmWorkspace grm_workspace(const mc_dims& d) {
+GrmWorkspace grm_workspace(const mc_dims& d, int n_seg) {
     GrmWorkspace w{};
     w.aon = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
     w.on = online_ws(d);
     w.xps = xps_ws(d);
-    if (gate_pass(d)) {
-        w.w = align256(gate_w_bytes(d));
+    if (gate_pass(d, n_seg)) {
+        w.w = align256(gate_w_bytes(d, n_seg));
         w.won = align256(sizeof(float) * (size_t)d.B * d.H * d.L);
         w.inv_l = w.won;
-        w.pf = align256(gate_pfrag_bytes(d));
+        w.pf = align256(gate_pfrag_bytes(d, n_seg));
     }
     w.total = w.aon + w.on + w.xps + w.w + w.won + w.inv_l + w.pf;
     return w;
@@ -176,6 +177,8 @@ size_t mc_workspace_bytes(const mc_dims* d, mc_op op, int32_t top_k, int32_t n_c
     switch (op) {
         case MC_OP_PREFILL: return 0;
         case MC_OP_GRM: return grm_workspace(*d).total;
+        case MC_OP_GRM_SEGS:
+            return top_k >= 1 && top_k <= MC_MAX_SEGS ? grm_workspace(*d, top_k).total : 0;
         case MC_OP_SSC: return top_k >= 1 ? ssc_workspace(*d, top_k).total : 0;
         case MC_OP_GRM_BACKWARD: return bwd_workspace(*d).total;
         case MC_OP_SCAN_SEGS:
@@ -359,15 +362,27 @@ mc_status mc_grm_readout_segs(const mc_dims* d, const int32_t* seg_off, int32_t 
     if ((st = check_segs(d, seg_off, n_seg, &sg)) != MC_OK) return st;
     if (!Q || !U || !X || !P || !O_on || !Y) return MC_ERR_NULL;
     if (d->dtype == MC_BF16 ? !M_lo : !M) return MC_ERR_NULL;
-    const GrmWorkspace w = grm_workspace(*d);
-    if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
+    // with the workspace for n_seg segments (MC_OP_GRM_SEGS) the gate runs as its own pass;
+    // with the constant-length one (MC_OP_GRM) the read forms it in-kernel
+    const GrmWorkspace w = grm_workspace(*d, n_seg);
+    const bool own_gate = w.w && ws && ws_bytes >= w.total;
+    if (!ws || ws_bytes < (own_gate ? w.total : w.aon + w.on + w.xps)) return MC_ERR_WORKSPACE;
     const void* ptrs[] = {Q, U, X, M, M_lo, P, O_on, Y, gamma, ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MC_ERR_ALIGN;
-    float* xps = w.xps ? (float*)((char*)ws + w.aon + w.on) : nullptr;
+    char* b = (char*)ws;
+    float* xps = w.xps ? (float*)(b + w.aon + w.on) : nullptr;
     float* xtail = xps ? (float*)((char*)xps + xps_only(*d)) : nullptr;
+    SegGate gate;  // the gate pass's buffers (none: the in-kernel gate)
+    if (own_gate) {
+        char* g = b + w.aon + w.on + w.xps;
+        gate.W = (uint16_t*)g;
+        gate.won = (float*)(g + w.w);
+        gate.inv_l = (float*)(g + w.w + w.won);
+        gate.pf = g + w.w + w.won + w.inv_l;
+    }
     return launch_grm_readout_segs(*d, sg, Q, U, X, M, M_lo, P, O_on, (float*)ws, xps, xtail, Y,
-                                   gamma, stream)
+                                   gamma, stream, gate)
                ? MC_ERR_HIP
                : MC_OK;
 }

@@ -6,6 +6,7 @@
 //     gamma_t = softmax(a_t^(0..s)).
 // With SSC selections (the Sparse Selective Caching read, gitcode explainer §3.4) only the
 // token's selected segments and the online one enter the softmax: the others get weight 0.
+// Segment boundaries are the constant length C or the offsets table (by value).
 // For every read tile of RT consecutive tokens of one (b, h) this pass writes the softmax
 // numerators against the token's own max logit m_t = max_i a_t^(i):
 //     W[b,h,tile][i][t] = bf16(exp(a_t^(i) - m_t))  for the rows i < s_hi of the tile
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
     const bf16_t* __restrict__ U, const float* __restrict__ xps, const uint4* __restrict__ Pf,
     int H, int L, int C, int NS, int DG, int xh, int G, const int32_t* __restrict__ idx,
     int top_k, bf16_t* __restrict__ W, float* __restrict__ won_out,
-    float* __restrict__ inv_l_out) {
+    float* __restrict__ inv_l_out, const SegArg sg) {
     // the means' fragments of the first GPF_STATES states, staged once for the G heads
     __shared__ __attribute__((aligned(16))) uint4 pfl[GPF_STATES / 32 * (GDG_MAX / 16) * 2 * 64];
     // numerators of one 32-state block, [state][token], before the 16-byte stores
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
     const int h0 = tile * GT + half * GW;  // first token of this workgroup
     if (h0 >= L) return;                   // (the whole workgroup: no barrier is skipped)
     const int last = min(L, tile * GT + GT) - 1;
-    const int s_hi = last / C;             // rows of W the read of this tile uses
+    const int s_hi = seg_of(sg, last, C);  // rows of W the read of this tile uses
     const size_t bx = (size_t)(bh0 / H) * xh + (xh == 1 ? 0 : bh0 % H);
     const int KC = DG / 16;
     const uint4* Pfb = Pf + bx * ((NS + 31) / 32) * KC * 2 * 64;
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
     const int tl = 32 * wave + l32;        // token within the workgroup
     const bool val = h0 + tl < L;
     const int tok = min(h0 + tl, L - 1);
-    const int seg = tok / C;
+    const int seg = seg_of(sg, tok, C);
     // the token's prefix sum of X (its lane half's 8 of every 16 columns), shared by the heads
     float4 xv[GDG_MAX / 16][2];
     {
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
             }
         }
         dot += __shfl_xor(dot, 32, 64);
-        const float a_on = dot / (float)(tok - seg * C + 1);
+        const float a_on = dot / (float)(tok - seg_first(sg, seg, C) + 1);
         // logits^T of states i0 .. i0+31 (rows; A = the means' high and remainder fragments)
         // x the wave's 32 tokens.  Accumulator element r is state i0 + 8 (r / 4) + 4 hi32 +
         // r % 4; a state counts for token t when it is a completed segment before t's, others
@@ -248,15 +249,18 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
 
 }  // namespace
 
-size_t gate_pfrag_bytes(const mc_dims& d) {
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+static const SegArg kConstSegG{};  // constant segment length
+
+size_t gate_pfrag_bytes(const mc_dims& d, int n_seg) {
+    const int NS = n_seg ? n_seg : (d.L + d.seg_len - 1) / d.seg_len;
     return (size_t)d.B * d.x_heads * ((NS + 31) / 32) * (d.d_g / 16) * 2 * 64 * 16;
 }
 
 int launch_gate_w(const mc_dims& d, const void* U, const float* xps, const float* P,
                   void* pfrag, uint16_t* W, float* won, float* inv_l, void* stream,
-                  const int32_t* idx, int top_k) {
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+                  const int32_t* idx, int top_k, const SegArg* sgp) {
+    const SegArg& sg = sgp ? *sgp : kConstSegG;
+    const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
     const int T = (d.L + GT - 1) / GT;
     const int nf = ((NS + 31) / 32) * (d.d_g / 16) * 64;
     hipLaunchKernelGGL(pfrag_kernel, dim3((nf + 255) / 256, d.B * d.x_heads), dim3(256), 0,
@@ -268,12 +272,12 @@ int launch_gate_w(const mc_dims& d, const void* U, const float* xps, const float
         hipLaunchKernelGGL(gate_w_kernel<true>, dim3(T * 2, d.B * d.H / G), dim3(256), 0,
                            (hipStream_t)stream, (const bf16_t*)U, xps, (const uint4*)pfrag, d.H,
                            d.L, d.seg_len, NS, d.d_g, d.x_heads, G, idx, top_k, (bf16_t*)W, won,
-                           inv_l);
+                           inv_l, sg);
     else
         hipLaunchKernelGGL(gate_w_kernel<false>, dim3(T * 2, d.B * d.H / G), dim3(256), 0,
                            (hipStream_t)stream, (const bf16_t*)U, xps, (const uint4*)pfrag, d.H,
                            d.L, d.seg_len, NS, d.d_g, d.x_heads, G, nullptr, 0, (bf16_t*)W, won,
-                           inv_l);
+                           inv_l, sg);
     return (int)hipGetLastError();
 }
 

@@ -25,18 +25,20 @@ struct GrmWorkspace {
 // numerators fit kGateMaxBytes (longer sequences keep the gate inside the read).
 constexpr int kGateTile = 256;
 constexpr size_t kGateMaxBytes = size_t(4) << 30;
-bool gate_pass(const mc_dims& d);
+// the gate as its own pass (bf16, d_k = d_v = 128) for NS segments (0: the constant length's)
+bool gate_pass(const mc_dims& d, int NS = 0);
 struct GateWeights {
     const uint16_t* W = nullptr;   // null: the read computes the gate itself
     const float* won = nullptr;
     const float* inv_l = nullptr;
 };
-size_t gate_pfrag_bytes(const mc_dims& d);  // the means as MFMA fragments (bf16 high + rest)
+size_t gate_pfrag_bytes(const mc_dims& d, int NS = 0);  // the means as MFMA fragments (bf16 high + rest)
 // idx (with top_k) given: the SSC gate, every logit but the token's selected segments and the
 // online one masked out
+struct SegArg;
 int launch_gate_w(const mc_dims& d, const void* U, const float* xps, const float* P,
                   void* pfrag, uint16_t* W, float* won, float* inv_l, void* stream,
-                  const int32_t* idx = nullptr, int top_k = 0);
+                  const int32_t* idx = nullptr, int top_k = 0, const SegArg* sg = nullptr);
 struct SscWorkspace {
     size_t aon;    // fp32 [B,H,L] (generic kernels)
     size_t on;     // fp32 [B,H,L,dv] (generic kernels only)
@@ -57,7 +59,9 @@ struct DecodeWorkspace {
     int slots;
 };
 
-GrmWorkspace grm_workspace(const mc_dims& d);
+// n_seg > 0: sized for that many segment offsets (the gate pass's buffers included when they
+// fit), else for the constant segment length
+GrmWorkspace grm_workspace(const mc_dims& d, int n_seg = 0);
 SscWorkspace ssc_workspace(const mc_dims& d, int top_k);
 DecodeWorkspace decode_workspace(const mc_dims& d, int n_cap, int n_cached);
 
@@ -149,10 +153,17 @@ int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, 
                              float* O_on, void* ws, size_t ws_bytes, void* stream);
 // xps / xtail (nullable: the per-segment walk of aon_kernel is used instead) are workspace for
 // the segment-causal prefix sums of X.
+// the gate pass's buffers for a read with segment offsets (W == nullptr: the in-kernel gate)
+struct SegGate {
+    uint16_t* W = nullptr;
+    float* won = nullptr;
+    float* inv_l = nullptr;
+    void* pf = nullptr;
+};
 int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* U,
                             const void* X, const float* M, const uint16_t* M_lo, const float* P,
                             const float* O_on, float* aon, float* xps, float* xtail, void* Y,
-                            float* gamma, void* stream);
+                            float* gamma, void* stream, const SegGate& gate = SegGate{});
 
 int launch_scan_prefill(const mc_dims& d, const void* Q, const void* K, const void* V,
                         const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,

@@ -870,9 +870,9 @@ int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const
                      const float* P, const float* O_on, const int32_t* idx,
                      const GateWeights& gw, void* Y, void* stream, const SegArg* sgp) {
     if (!read_mfma_covers(d)) return -1;
-    // segment offsets: GRM with the online read given (the fused online term and the gate
-    // pass assume a constant length)
-    if (sgp && sgp->n && (ssc || !O_on || gw.W)) return -1;
+    // segment offsets: GRM with the online read given (the fused online term assumes a
+    // constant length; the gate pass takes the offsets too)
+    if (sgp && sgp->n && (ssc || !O_on)) return -1;
     const SegArg& sg = sgp ? *sgp : kConstSegRd;
     hipStream_t st = (hipStream_t)stream;
     if (gw.W) {  // the gate ran as its own pass (d_k = d_v = 128 GRM)

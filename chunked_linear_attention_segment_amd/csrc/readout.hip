@@ -404,7 +404,7 @@ __global__ void gamma_kernel(const T* __restrict__ U, const float* __restrict__ 
 int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* U,
                             const void* X, const float* M, const uint16_t* M_lo, const float* P,
                             const float* O_on, float* aon, float* xps, float* xtail, void* Y,
-                            float* gamma, void* stream) {
+                            float* gamma, void* stream, const SegGate& gate) {
     hipStream_t st = (hipStream_t)stream;
     int rc;
     auto logits = [&]() {  // the online logits token by token from the prefix sums
@@ -420,10 +420,20 @@ int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, c
     if (xps) {  // prefix sums of X per segment
         rc = launch_xps_sg(d, X, xps, xtail, sg, st);
         if (rc) return rc;
-        // bf16 widths 64/128: the MFMA read with the segment table (its gate, online logits
-        // included, in-kernel; the online term from O_on), then gamma on request
+        // bf16 widths 64/128: the MFMA read with the segment table (the online term from
+        // O_on; its gate as its own pass when the workspace holds that pass's buffers, else
+        // in-kernel, online logits included), then gamma on request
+        GateWeights gw;
+        if (gate.W && read_mfma_covers(d) && d.d_k == 128 && d.d_v == 128) {
+            rc = launch_gate_w(d, U, xps, P, gate.pf, gate.W, gate.won, gate.inv_l, stream,
+                               nullptr, 0, &sg);
+            if (rc) return rc;
+            gw.W = gate.W;
+            gw.won = gate.won;
+            gw.inv_l = gate.inv_l;
+        }
         rc = launch_read_mfma(d, false, 0, Q, nullptr, nullptr, U, xps, M_lo, P, O_on, nullptr,
-                              GateWeights{}, Y, stream, &sg);
+                              gw, Y, stream, &sg);
         if (rc >= 0) {
             if (rc || !gamma) return rc;
             if ((rc = logits())) return rc;

@@ -81,7 +81,8 @@ typedef enum {
     MC_OP_SSC = 2,
     MC_OP_DECODE = 3,
     MC_OP_GRM_BACKWARD = 4,
-    MC_OP_SCAN_SEGS = 5
+    MC_OP_SCAN_SEGS = 5,
+    MC_OP_GRM_SEGS = 6
 } mc_op;
 
 /* Problem sizes.  Supported by this library: d_k, d_v in {64, 128}; 1 <= d_g <= 256 and
@@ -104,8 +105,9 @@ int mc_abi_version(void);
 const char* mc_status_str(mc_status status);
 
 /* Workspace bytes an operation needs for these sizes (top_k is used by MC_OP_SSC, n_cap by
- * MC_OP_DECODE; MC_OP_SCAN_SEGS, the segment-offset write path, takes the number of segments
- * in top_k).  Returns 0 when no workspace is needed or the sizes are invalid. */
+ * MC_OP_DECODE; MC_OP_SCAN_SEGS, the segment-offset write path, and MC_OP_GRM_SEGS, the
+ * segment-offset read, take the number of segments in top_k).  Returns 0 when no workspace
+ * is needed or the sizes are invalid. */
 size_t mc_workspace_bytes(const mc_dims* dims, mc_op op, int32_t top_k, int32_t n_cap);
 
 /*
@@ -236,7 +238,10 @@ mc_status mc_decode_step_noalloc(const mc_dims* dims, const void* q, const void*
  *   n_seg    1 <= n_seg <= MC_MAX_SEGS; NS = n_seg below.
  *   The other arguments are those of mc_scan_prefill / mc_grm_readout with NS = n_seg, except
  *   that the read takes the online read O_on written by mc_scan_prefill_segs (required), not
- *   K and V; its workspace is mc_workspace_bytes(dims, MC_OP_GRM, 0, 0) bytes.
+ *   K and V.  Its workspace is mc_workspace_bytes(dims, MC_OP_GRM_SEGS, n_seg, 0) bytes; with
+ *   that much (bf16, d_k = d_v = 128) the gate runs as its own pass over the offsets ahead of
+ *   the read, as in mc_grm_readout.  mc_workspace_bytes(dims, MC_OP_GRM, 0, 0) bytes are
+ *   also accepted; the read then forms the gate itself.
  *   The write path's workspace is mc_workspace_bytes(dims, MC_OP_SCAN_SEGS, n_seg, 0) bytes
  *   (0 for fp32: NULL allowed): bf16 segments longer than a piece (512 tokens, or the
  *   smallest power of two above it that keeps the pieces within MC_MAX_SEGS) are scanned as

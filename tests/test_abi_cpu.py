@@ -237,10 +237,22 @@ def test_segment_offsets_are_validated():
     assert scan(good, ws=None) == mc.MC_ERR_WORKSPACE
     assert scan(good, wsb=nb - 1) == mc.MC_ERR_WORKSPACE
     assert mc.mc_workspace_bytes(dims(L=1000, dtype="f32"), mc.MC_OP_SCAN_SEGS, 6) == 0
+    # the read's workspace for n_seg segments holds the gate pass's buffers (bf16, d = 128),
+    # which grow with n_seg; without them (the constant-length size) the read forms the gate
+    # in-kernel, so either size is accepted and less than the read's own buffers is not
+    g6 = mc.mc_workspace_bytes(d, mc.MC_OP_GRM_SEGS, 6)
+    g64 = mc.mc_workspace_bytes(d, mc.MC_OP_GRM_SEGS, 64)
+    aon = 4 * d.B * d.H * d.L
+    assert g64 > g6 > aon + 4 * d.B * d.x_heads * d.L * d.d_g
+    assert g64 - g6 >= 2 * d.B * d.H * ((d.L + 255) // 256) * 256 * (64 - 6)
+    assert mc.mc_workspace_bytes(d, mc.MC_OP_GRM_SEGS, 0) == 0
+    assert mc.mc_workspace_bytes(d, mc.MC_OP_GRM_SEGS, mc.MC_MAX_SEGS + 1) == 0
+    assert read(good, ws_bytes=0) == mc.MC_ERR_WORKSPACE
+    assert read(good, ws=None, ws_bytes=g6) == mc.MC_ERR_WORKSPACE
+    assert read(good, ws_bytes=aon) == mc.MC_ERR_WORKSPACE
     assert scan(good, M_lo=None) == mc.MC_ERR_NULL        # bf16 writes the bf16 copy
     assert scan(good, X=MIS) == mc.MC_ERR_ALIGN
     assert read(good, O_on=None) == mc.MC_ERR_NULL        # the read takes the scan's O_on
-    assert read(good, ws_bytes=ws - 1) == mc.MC_ERR_WORKSPACE
     assert read(good, Y=MIS) == mc.MC_ERR_ALIGN
 
 

@@ -375,6 +375,37 @@ def test_grm_segment_offsets(name):
         assert e <= tol, (k, e)
 
 
+def test_grm_segment_offsets_in_kernel_gate():
+    # The offsets read given only the constant-length workspace (MC_OP_GRM) forms the gate
+    # in-kernel instead of running the gate pass over the offsets; both against the oracle.
+    w = Workload("x", 1, 2, 1000, 128, 128, 128, 1, "identity", "bf16")
+    off = oracle.log_segments(w.L)
+    announce("grm segment offsets, in-kernel gate: %d segments" % (len(off) - 1))
+    inp = make_prefill(w, seed=4)
+    d = _dims(w)
+    dev = {k: to_dev(v, w.dtype) for k, v in inp.items()}
+    NS = len(off) - 1
+    M = torch.empty((1, 2, NS, 128, 128), dtype=torch.float32, device="cuda")
+    M_lo = torch.empty((1, 2, NS, 128, 128), dtype=torch.bfloat16, device="cuda")
+    P = torch.empty((1, 1, NS, 128), dtype=torch.float32, device="cuda")
+    O_on = torch.empty((1, 2, w.L, 128), dtype=torch.float32, device="cuda")
+    mc.mc_scan_prefill_segs(d, off, dev["Q"], dev["K"], dev["V"], dev["X"], M, M_lo, P, O_on,
+                            ws=mc.workspace_segs(d, NS))
+    ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], seg_len=1,
+                         phi=w.phi, mode="grm", seg_offsets=off)
+    outs = {}
+    for op in (mc.MC_OP_GRM, mc.MC_OP_GRM_SEGS):
+        Y = torch.empty((1, 2, w.L, 128), dtype=torch.bfloat16, device="cuda")
+        ws = mc.workspace(d, op, top_k=NS)
+        mc.mc_grm_readout_segs(d, off, dev["Q"], dev["U"], dev["X"], M, M_lo, P, O_on, Y,
+                               None, ws=ws)
+        torch.cuda.synchronize()
+        outs[op] = to_np(Y)
+        e = slice_rel_err(outs[op], ref["Y"])
+        announce("  workspace op %d: Y error %.3g" % (op, e))
+        assert e <= TOL["bf16"], (op, e)
+
+
 # SWLA memory (window 2) under GRM: the MFMA scan for constant bf16 segments, the generic scan
 # for fp32 and for offsets; the read takes the online term from O_on.
 SWLA_CASES = {
