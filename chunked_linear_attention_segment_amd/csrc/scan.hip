@@ -223,28 +223,29 @@ __device__ __forceinline__ int piece_end(const PieceArg& pa, int j, int NP) {
 // Prefix sums of the piece states inside each segment: the memory restarts only at a
 // segment start (Eq. 4b), so the memory before piece j is the sum of the earlier pieces of
 // its segment (Pref_j, zero for a segment's first piece) and the segment's state is the sum
-// of all of them.  One workgroup per (segment, b*H+h, 1024-element slice of the d_v x d_k
-// state) walks the segment's pieces in order, loading eight pieces at a time.
+// of all of them.  One workgroup per (segment, b*H+h, 512-element slice of the d_v x d_k
+// state) walks the segment's pieces in order, sixteen pieces at a time: every load of a batch
+// is issued before the first sum (rows past the segment's last piece are read clamped to it
+// and not used).
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void piece_prefix_kernel(const float* __restrict__ Msub,
+__global__ __launch_bounds__(128) void piece_prefix_kernel(const float* __restrict__ Msub,
                                                            int NP, const PieceArg pa, int NS,
                                                            float* __restrict__ Pref,
                                                            float* __restrict__ M,
                                                            bf16_t* __restrict__ M_lo) {
     constexpr int N = DV * DK;
-    constexpr int BATCH = 8;
+    constexpr int BATCH = 16;
     const int seg = blockIdx.x;
     const int j = segment_first_piece(pa, seg);
     const size_t bh = blockIdx.y;
-    const int e0 = blockIdx.z * 1024 + 4 * threadIdx.x;
+    const int e0 = blockIdx.z * 512 + 4 * threadIdx.x;
     const int jend = piece_end(pa, j, NP);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int b = j; b < jend; b += BATCH) {
         float4 v[BATCH];
 #pragma unroll
         for (int i = 0; i < BATCH; ++i)
-            if (b + i < jend)
-                v[i] = *reinterpret_cast<const float4*>(Msub + (bh * NP + b + i) * (size_t)N + e0);
+            v[i] = *reinterpret_cast<const float4*>(Msub + (bh * NP + min(b + i, jend - 1)) * (size_t)N + e0);
 #pragma unroll
         for (int i = 0; i < BATCH; ++i)
             if (b + i < jend) {
@@ -305,9 +306,9 @@ template <int DK, int DV>
 static int launch_pieces_t(const mc_dims& d, const PieceArg& pa, int NS, float* Msub,
                            float* Pref, float* M, uint16_t* M_lo, hipStream_t st) {
     const int NP = pa.sg.n;
-    static_assert(DV * DK % 1024 == 0, "1024-element slices");
-    hipLaunchKernelGGL((piece_prefix_kernel<DK, DV>), dim3(NS, d.B * d.H, DV * DK / 1024),
-                       dim3(256), 0, st, Msub, NP, pa, NS, Pref, M, (bf16_t*)M_lo);
+    static_assert(DV * DK % 512 == 0, "512-element slices");
+    hipLaunchKernelGGL((piece_prefix_kernel<DK, DV>), dim3(NS, d.B * d.H, DV * DK / 512),
+                       dim3(128), 0, st, Msub, NP, pa, NS, Pref, M, (bf16_t*)M_lo);
     return (int)hipGetLastError();
 }
 
