@@ -78,10 +78,10 @@ __device__ __forceinline__ void scan_dma16(const void* base, uint32_t voff, uint
 constexpr int CH = 64;    // tokens per chunk
 constexpr int TPAD = 72;  // row stride (elements) of the token-indexed LDS tiles
 
-// (SWLA: held to 256 registers, two waves per SIMD, so one workgroup's memory waits are
-// covered by another's work)
+// (held to 256 registers, two waves per SIMD, so one workgroup's memory waits are covered by
+// another's work)
 template <int DK, int DV, bool ON, bool SW>
-__global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
+__global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     int L, int C, int NS, int phi, float* __restrict__ M, bf16_t* __restrict__ M_lo,
     float* __restrict__ O_on, SwlaGates gt, const SegArg sg, const float* __restrict__ M0,
@@ -90,20 +90,27 @@ __global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
     constexpr int DB = DK / 32;     // 32-row blocks of d
     constexpr int KSD = DK / 16;    // k-steps over d
     constexpr int GW = SW ? CH : 1; // SWLA tables (1-element placeholders otherwise)
-    __shared__ __attribute__((aligned(16))) bf16_t kt[DK][TPAD];  // phi(k)^T  [d][r]
-    __shared__ __attribute__((aligned(16))) bf16_t vt[DV][TPAD];  // v^T       [cv][r]
-    __shared__ __attribute__((aligned(16))) bf16_t sc[CH][TPAD];  // masked scores [t][r]
+    // phi(k)^T [d][r], v^T [cv][r] and the masked scores [t][r]; without SWLA the chunk's k,
+    // v and q rows arrive in the same places first (see below)
+    constexpr int KBE = SW || DK * TPAD > CH * DK ? DK * TPAD : CH * DK;
+    constexpr int VBE = SW || DV * TPAD > CH * DV ? DV * TPAD : CH * DV;
+    constexpr int QBE = !ON ? 8 : (SW || CH * TPAD > CH * DK ? CH * TPAD : CH * DK);
+    __shared__ __attribute__((aligned(16))) bf16_t kbuf[KBE];
+    __shared__ __attribute__((aligned(16))) bf16_t vbuf[VBE];
+    __shared__ __attribute__((aligned(16))) bf16_t qbuf[QBE];
+    bf16_t(*kt)[TPAD] = reinterpret_cast<bf16_t(*)[TPAD]>(kbuf);
+    bf16_t(*vt)[TPAD] = reinterpret_cast<bf16_t(*)[TPAD]>(vbuf);
+    bf16_t(*sc)[TPAD] = reinterpret_cast<bf16_t(*)[TPAD]>(qbuf);
     __shared__ float cf[GW][GW + 1];  // SWLA weights c[t][r] of the chunk
     __shared__ float dz[GW];          // SWLA decay of Z at chunk token t: alpha_{j0+1..j0+t}
     __shared__ float ga[GW + 1], gb[GW + 1], gl[GW];  // the chunk's gates (+ next token's)
     // with dgs: each wave's share of <dy_t, O_on[t]> per chunk token (chunk parity buffers)
     __shared__ float red[ON ? 2 : 1][ON ? DV / 32 : 1][ON ? CH : 1];
-    // the chunk's rows as loaded (k, v; q and dy for the online read), 16-byte chunks swizzled
-    // (SWLA, whose weight tables take LDS too, loads the operands from global memory instead)
-    __shared__ __attribute__((aligned(16))) bf16_t kn[SW ? 8 : CH * DK];
-    __shared__ __attribute__((aligned(16))) bf16_t vn[SW ? 8 : CH * DV];
-    __shared__ __attribute__((aligned(16))) bf16_t qn[ON && !SW ? CH * DK : 8];
+    // the chunk's dy rows as loaded (the backward's <dy, O_on>; not SWLA)
     __shared__ __attribute__((aligned(16))) bf16_t yn[ON && !SW ? CH * DV : 8];
+    bf16_t* const kn = kbuf;  // the chunk's k, v, q rows as loaded (not SWLA)
+    bf16_t* const vn = vbuf;
+    bf16_t* const qn = qbuf;
 
     const int s = blockIdx.x;
     const size_t bh = blockIdx.y;
@@ -149,131 +156,151 @@ __global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
     // dgs of the chunk at jp from the waves' shares (read after the barrier that ends it)
     auto flush_dgs = [&](int jp) {
         if constexpr (ON) {
-            if (tid < min(CH, len - jp)) {
+            int tf = tid;  // (re-formed per call, not held across the chunk loop)
+            asm volatile("" : "+v"(tf));
+            if (tf < min(CH, len - jp)) {
                 float a = 0.f;
 #pragma unroll
-                for (int w = 0; w < DV / 32; ++w) a += red[(jp / CH) & 1][w][tid];
-                dgs[gbase + jp + tid] = a;
+                for (int w = 0; w < DV / 32; ++w) a += red[(jp / CH) & 1][w][tf];
+                dgs[gbase + jp + tf] = a;
             }
         }
     };
     if constexpr (!SW) {
-        // The chunk's rows of k, v (and q, dy for the online read) arrive in LDS as whole rows by
-        // direct global->LDS loads; row r's 16-byte chunk c sits at c ^ (r % chunks per row).  Rows
-        // past the chunk are loaded clamped to its last row (their products are masked).
+        // The chunk's rows of k, v and q (and dy) arrive in LDS as whole rows by direct
+        // global->LDS loads; row r's 16-byte chunk c sits at c ^ (r % chunks per row), and rows
+        // past the chunk are loaded clamped to its last row (their products are masked).  The
+        // fragments and the items of the transposed tiles are read into registers; after a
+        // barrier phi(k)^T and the masked scores are written over the k and q rows, after
+        // another v^T over the v rows.  That keeps the workgroup small enough for two per CU, so
+        // one's loads are covered by the other's products.  The next chunk's rows load once the transposed
+        // tiles have been consumed.
         auto tile_at = [&](const bf16_t* tile, int D, int r, int e) -> const bf16_t* {
             const int cpr = D / 8;
             return tile + r * D + ((((e >> 3) ^ (r % cpr)) << 3) | (e & 7));
         };
-        auto dma_tile = [&](const bf16_t* src, int D, bf16_t* tile, int jn, int nn) {
+        // a tile's LDS byte address (the low 32 bits of its generic address), wave-uniform
+        auto lds_base = [](const bf16_t* tile) -> uint32_t {
+            return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)tile);
+        };
+        auto dma_tile = [&](const bf16_t* src, int D, uint32_t tile_base, int jn, int nn) {
             const int cpr = D / 8;
-    #pragma unroll
+            int lo = lane;  // (formed per call, not held across the chunk loop)
+            asm volatile("" : "+v"(lo));
+#pragma unroll
             for (int m = 0; m < CH * (D / 8) / NT; ++m) {
-                const int p = (m * (NT / 64) + wave) * 64 + lane;  // destination chunk
+                const int p = (m * (NT / 64) + wave) * 64 + lo;  // destination chunk
                 const int r = p / cpr, c = (p % cpr) ^ (r % cpr);
                 const uint32_t voff = (uint32_t)(((jn + min(r, nn - 1)) * D + c * 8) * 2);
-                const uint32_t base =
-                    (uint32_t)(uintptr_t)(tile + (m * (NT / 64) + wave) * 64 * 8);
-                scan_dma16(src, voff, __builtin_amdgcn_readfirstlane(base));
+                scan_dma16(src, voff, __builtin_amdgcn_readfirstlane(
+                    tile_base + (uint32_t)((m * (NT / 64) + wave) * 64 * 16)));
             }
         };
-        auto dma_chunk = [&](int jn, int nn) {
-            dma_tile(Ks, DK, kn, jn, nn);
-            dma_tile(Vs, DV, vn, jn, nn);
+        auto dma_kvq = [&](int jn, int nn) {
+            dma_tile(Ks, DK, lds_base(kn), jn, nn);
+            dma_tile(Vs, DV, lds_base(vn), jn, nn);
+            if constexpr (ON) dma_tile(Qs, DK, lds_base(qn), jn, nn);
+        };
+        auto dma_y = [&](int jn, int nn) {
             if constexpr (ON) {
-                dma_tile(Qs, DK, qn, jn, nn);
-                if (dgs) dma_tile(dY + gbase * DV, DV, yn, jn, nn);
+                if (dgs) dma_tile(dY + gbase * DV, DV, lds_base(yn), jn, nn);
             }
         };
+        constexpr int NIK = (CH / 2) * (DK / 8) / NT, NIV = (CH / 2) * (DV / 8) / NT;
+        static_assert(NIK * NT == (CH / 2) * (DK / 8) && NIV * NT == (CH / 2) * (DV / 8),
+                      "staging items per thread");
+        constexpr int SBW = (3 + NT / 64 - 1) / (NT / 64);  // score blocks per wave
         if (len > 0) {
-            dma_chunk(0, min(CH, len));
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
+            dma_kvq(0, min(CH, len));
+            dma_y(0, min(CH, len));
         }
         for (int j0 = 0; j0 < len; j0 += CH) {
             const int n = min(CH, len - j0);
+            const bool more = j0 + CH < len;
+            const int nn = more ? min(CH, len - j0 - CH) : 0;
+            // this chunk's rows have landed for this lane; after the barrier for every lane
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
             if (dgs && j0 > 0) flush_dgs(j0 - CH);
-            const bool last = j0 + n == len;  // the segment ends in this chunk
-            if (SW) {
-                // gates of the chunk's tokens, zero past its end; slot CH is the next token's
-                if (tid <= CH) {
-                    const bool in = j0 + tid < len && tid <= n;
-                    ga[tid] = in ? gt.alpha[gbase + j0 + tid] : 0.f;
-                    gb[tid] = in ? gt.beta[gbase + j0 + tid] : 0.f;
-                    if (tid < CH) gl[tid] = in && tid < n ? gt.lam[gbase + j0 + tid] : 0.f;
-                }
-                __syncthreads();
-                if (tid < CH) {  // column r: c[r][r] = lam_r, then a running product down t
-                    const int r = tid;
-                    float c = gl[r];
-                    cf[r][r] = c;
-                    if (r + 1 < CH) {
-                        c = ga[r + 1] * gl[r] + gb[r + 1];
-                        cf[r + 1][r] = c;
-                        for (int t = r + 2; t < CH; ++t) {
-                            c *= ga[t];
-                            cf[t][r] = c;
-                        }
-                    }
-                } else if (tid == CH) {
-                    float p = 1.f;
-                    dz[0] = p;
-                    for (int t = 1; t < CH; ++t) {
-                        p *= ga[t];
-                        dz[t] = p;
-                    }
-                }
-                __syncthreads();
-            }
-            // ---- phi(q) B-fragments (k order of the accumulator rows) for both token blocks ----
+            // the lane indices as the compiler cannot see them: the LDS addresses below are
+            // formed per chunk, not held in registers across the chunk loop
+            int ln = l32, hf = half, td = tid;
+            asm volatile("" : "+v"(ln), "+v"(hf), "+v"(td));
+            // ---- phi(q) B-fragments (k order of the accumulator rows), O^T = M_prev phi(q)^T ----
             u32x4_t qb[2][KSD];
             f32x16_t ot[2];
             if (ON) {
-    #pragma unroll
+#pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
-                    const int tl = tb * 32 + l32;
+                    const int tl = tb * 32 + ln;
                     const bool ok = tl < n;
-    #pragma unroll
+#pragma unroll
                     for (int ks = 0; ks < KSD; ++ks) {
                         u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
                         if (ok) {
-                            lo = phi4(*reinterpret_cast<const u32x2_t*>(tile_at(qn, DK, tl, ks * 16 + half * 4)), phi);
-                            hi = phi4(*reinterpret_cast<const u32x2_t*>(tile_at(qn, DK, tl, ks * 16 + 8 + half * 4)), phi);
+                            lo = phi4(*reinterpret_cast<const u32x2_t*>(tile_at(qn, DK, tl, ks * 16 + hf * 4)), phi);
+                            hi = phi4(*reinterpret_cast<const u32x2_t*>(tile_at(qn, DK, tl, ks * 16 + 8 + hf * 4)), phi);
                         }
                         qb[tb][ks] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
                     }
                 }
-                // ---- O^T = M_prev phi(q)^T (first term of the online read) ----
-    #pragma unroll
+#pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; ++r) ot[tb][r] = 0.f;
-                if (j0 > 0 || M0) {
-    #pragma unroll
-                    for (int ks = 0; ks < KSD; ++ks)
-    #pragma unroll
-                        for (int tb = 0; tb < 2; ++tb) ot[tb] = scan_mfma(ma[ks], qb[tb][ks], ot[tb]);
-                    if (SW) {  // Z decays by alpha_{j0+1} .. alpha_t before token t reads it
-    #pragma unroll
-                        for (int tb = 0; tb < 2; ++tb) ot[tb] *= dz[tb * 32 + l32];
+                if (j0 > 0 || M0) {  // the A operand is the bf16 copy of M_prev, packed here
+#pragma unroll
+                    for (int ks = 0; ks < KSD; ++ks) {
+                        const int db = ks / 2, hh = ks % 2;
+                        const u32x4_t mk = {pk2(mt[db][8 * hh + 0], mt[db][8 * hh + 1]),
+                                            pk2(mt[db][8 * hh + 2], mt[db][8 * hh + 3]),
+                                            pk2(mt[db][8 * hh + 4], mt[db][8 * hh + 5]),
+                                            pk2(mt[db][8 * hh + 6], mt[db][8 * hh + 7])};
+#pragma unroll
+                        for (int tb = 0; tb < 2; ++tb) ot[tb] = scan_mfma(mk, qb[tb][ks], ot[tb]);
                     }
                 }
             }
-            // SWLA: final weight of each key of the chunk in the state carried out of it
-            float zs = 1.f;  // and the factor on the incoming Z
-            if (SW) zs = last ? dz[n - 1] : ga[CH] * dz[CH - 1];
-            auto key_weight = [&](int r) -> float {
-                if (r >= n) return 0.f;
-                return last ? cf[n - 1][r] : ga[CH] * cf[CH - 1][r] + (r == CH - 1 ? gb[CH] : 0.f);
-            };
-            // ---- stage phi(k)^T and v^T (token pairs packed in 32-bit LDS words) ----
-            for (int it = tid; it < (CH / 2) * (DK / 8); it += NT) {
-                const int p = it % (CH / 2), dc = (it / (CH / 2)) * 8;
+            // ---- the wave's causal score blocks S^T[r][t] = phi(k_r).phi(q_t), r <= t: blocks
+            //      (rb,tb) = (0,0), (0,1), (1,1); block (1,0) is all masked and never read ----
+            f32x16_t sacc[SBW];
+#pragma unroll
+            for (int q = 0; q < SBW; ++q) {
+                const int blk = wave + q * (NT / 64);
+                if (!ON || blk >= 3) continue;
+                const int rb = blk == 2 ? 1 : 0, tb = blk == 0 ? 0 : 1;
+                const int rl = rb * 32 + ln;
+                const bool ok = rl < n;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[q][r] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) {
+                    u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
+                    if (ok) {
+                        lo = phi4(*reinterpret_cast<const u32x2_t*>(tile_at(kn, DK, rl, ks * 16 + hf * 4)), phi);
+                        hi = phi4(*reinterpret_cast<const u32x2_t*>(tile_at(kn, DK, rl, ks * 16 + 8 + hf * 4)), phi);
+                    }
+                    sacc[q] = scan_mfma(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, tb ? qb[1][ks] : qb[0][ks],
+                                        sacc[q]);
+                }
+            }
+            // the items of the transposed tiles: token pair (2p, 2p + 1), columns dc .. dc + 7
+            u32x4_t ki[NIK][2];
+#pragma unroll
+            for (int m = 0; m < NIK; ++m) {
+                const int it = td + m * NT, p = it % (CH / 2), dc = (it / (CH / 2)) * 8;
+                const u32x4_t z = {0u, 0u, 0u, 0u};
+                ki[m][0] = 2 * p < n ? *reinterpret_cast<const u32x4_t*>(tile_at(kn, DK, 2 * p, dc)) : z;
+                ki[m][1] = 2 * p + 1 < n ? *reinterpret_cast<const u32x4_t*>(tile_at(kn, DK, 2 * p + 1, dc)) : z;
+            }
+            __syncthreads();  // the k and q rows have been read: phi(k)^T and the scores go there
+            // ---- phi(k)^T and v^T (token pairs packed in 32-bit words), the masked scores ----
+#pragma unroll
+            for (int m = 0; m < NIK; ++m) {
+                const int it = tid + m * NT, p = it % (CH / 2), dc = (it / (CH / 2)) * 8;
                 const int r0 = 2 * p, r1 = 2 * p + 1;
-                u32x4_t a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-                if (r0 < n) a = *reinterpret_cast<const u32x4_t*>(tile_at(kn, DK, r0, dc));
-                if (r1 < n) b = *reinterpret_cast<const u32x4_t*>(tile_at(kn, DK, r1, dc));
-    #pragma unroll
+                const u32x4_t a = ki[m][0], b = ki[m][1];
+#pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float a0 = __uint_as_float(a[e] << 16), a1 = __uint_as_float(a[e] & 0xffff0000u);
                     float b0 = __uint_as_float(b[e] << 16), b1 = __uint_as_float(b[e] & 0xffff0000u);
@@ -283,101 +310,68 @@ __global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
                         b0 = r1 < n ? feature(b0, 1) : 0.f;
                         b1 = r1 < n ? feature(b1, 1) : 0.f;
                     }
-                    if (SW) {
-                        const float w0 = key_weight(r0), w1 = key_weight(r1);
-                        a0 *= w0;
-                        a1 *= w0;
-                        b0 *= w1;
-                        b1 *= w1;
-                    }
                     *reinterpret_cast<uint32_t*>(&kt[dc + 2 * e][r0]) = pk2(a0, b0);
                     *reinterpret_cast<uint32_t*>(&kt[dc + 2 * e + 1][r0]) = pk2(a1, b1);
                 }
             }
-            for (int it = tid; it < (CH / 2) * (DV / 8); it += NT) {
-                const int p = it % (CH / 2), dc = (it / (CH / 2)) * 8;
-                const int r0 = 2 * p, r1 = 2 * p + 1;
-                u32x4_t a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-                if (r0 < n) a = *reinterpret_cast<const u32x4_t*>(tile_at(vn, DV, r0, dc));
-                if (r1 < n) b = *reinterpret_cast<const u32x4_t*>(tile_at(vn, DV, r1, dc));
-    #pragma unroll
+#pragma unroll
+            for (int q = 0; q < SBW; ++q) {
+                const int blk = wave + q * (NT / 64);
+                if (!ON || blk >= 3) continue;
+                const int rb = blk == 2 ? 1 : 0, tb = blk == 0 ? 0 : 1;
+                const int t = tb * 32 + l32;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int r = rb * 32 + 8 * g + 4 * half;
+                    const float v0 = (r + 0 <= t) ? sacc[q][4 * g + 0] : 0.f;
+                    const float v1 = (r + 1 <= t) ? sacc[q][4 * g + 1] : 0.f;
+                    const float v2 = (r + 2 <= t) ? sacc[q][4 * g + 2] : 0.f;
+                    const float v3 = (r + 3 <= t) ? sacc[q][4 * g + 3] : 0.f;
+                    *reinterpret_cast<u32x2_t*>(&sc[t][r]) = u32x2_t{pk2(v0, v1), pk2(v2, v3)};
+                }
+            }
+            // the v items, then v^T over the v rows once every wave has read its items
+            u32x4_t vi[NIV][2];
+#pragma unroll
+            for (int m = 0; m < NIV; ++m) {
+                const int it = td + m * NT, p = it % (CH / 2), dc = (it / (CH / 2)) * 8;
+                const u32x4_t z = {0u, 0u, 0u, 0u};
+                vi[m][0] = 2 * p < n ? *reinterpret_cast<const u32x4_t*>(tile_at(vn, DV, 2 * p, dc)) : z;
+                vi[m][1] = 2 * p + 1 < n ? *reinterpret_cast<const u32x4_t*>(tile_at(vn, DV, 2 * p + 1, dc)) : z;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < NIV; ++m) {
+                const int it = tid + m * NT, p = it % (CH / 2), dc = (it / (CH / 2)) * 8;
+                const int r0 = 2 * p;
+                const u32x4_t a = vi[m][0], b = vi[m][1];
+#pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    *reinterpret_cast<uint32_t*>(&vt[dc + 2 * e][r0]) =
-                        (a[e] & 0xffffu) | (b[e] << 16);
+                    *reinterpret_cast<uint32_t*>(&vt[dc + 2 * e][r0]) = (a[e] & 0xffffu) | (b[e] << 16);
                     *reinterpret_cast<uint32_t*>(&vt[dc + 2 * e + 1][r0]) =
                         (a[e] >> 16) | (b[e] & 0xffff0000u);
                 }
             }
-            // ---- causal scores S^T[r][t] = phi(k_r).phi(q_t), r <= t: blocks (rb,tb) = (0,0),
-            //      (0,1), (1,1) dealt to the waves; block (1,0) is all masked and never read ----
-            for (int blk = wave; ON && blk < 3; blk += NT / 64) {
-                const int rb = blk == 2 ? 1 : 0, tb = blk == 0 ? 0 : 1;
-                const int rl = rb * 32 + l32;
-                const bool ok = rl < n;
-                f32x16_t sacc;
-    #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-    #pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) {
-                    u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
-                    if (ok) {
-                        lo = phi4(*reinterpret_cast<const u32x2_t*>(tile_at(kn, DK, rl, ks * 16 + half * 4)), phi);
-                        hi = phi4(*reinterpret_cast<const u32x2_t*>(tile_at(kn, DK, rl, ks * 16 + 8 + half * 4)), phi);
-                    }
-                    sacc = scan_mfma(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, tb ? qb[1][ks] : qb[0][ks],
-                                     sacc);
-                }
-                const int t = tb * 32 + l32;
-    #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int r = rb * 32 + 8 * g + 4 * half;
-                    float v0 = (r + 0 <= t) ? sacc[4 * g + 0] : 0.f;
-                    float v1 = (r + 1 <= t) ? sacc[4 * g + 1] : 0.f;
-                    float v2 = (r + 2 <= t) ? sacc[4 * g + 2] : 0.f;
-                    float v3 = (r + 3 <= t) ? sacc[4 * g + 3] : 0.f;
-                    if (SW) {
-                        v0 = (r + 0 <= t) ? v0 * cf[t][r + 0] : 0.f;
-                        v1 = (r + 1 <= t) ? v1 * cf[t][r + 1] : 0.f;
-                        v2 = (r + 2 <= t) ? v2 * cf[t][r + 2] : 0.f;
-                        v3 = (r + 3 <= t) ? v3 * cf[t][r + 3] : 0.f;
-                    }
-                    *reinterpret_cast<u32x2_t*>(&sc[t][r]) = u32x2_t{pk2(v0, v1), pk2(v2, v3)};
-                }
-            }
-            // dy of the lane's tokens at its value rows (dgs), out of the tile before it is reloaded
-            u32x2_t py[2][4];
-            if (ON && dgs) {
-    #pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
-    #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        py[tb][g] = *reinterpret_cast<const u32x2_t*>(
-                            tile_at(yn, DV, tb * 32 + l32, wave * 32 + 8 * g + half * 4));
-            }
             __syncthreads();
-            // every row tile has been read: the next chunk's rows start loading
-            const bool more = j0 + CH < len;
-            if (more) dma_chunk(j0 + CH, min(CH, len - j0 - CH));
             // ---- O^T += v^T S^T (intra-chunk term) and M^T += phi(k)^T v (state update) ----
             const int cv = wave * 32 + l32;
             u32x4_t va[CH / 16];
-    #pragma unroll
+#pragma unroll
             for (int ks = 0; ks < CH / 16; ++ks)
                 va[ks] = *reinterpret_cast<const u32x4_t*>(&vt[cv][ks * 16 + half * 8]);
-    #pragma unroll
+#pragma unroll
             for (int tb = 0; tb < 2 && ON; ++tb) {
                 const int t = tb * 32 + l32;
-    #pragma unroll
+#pragma unroll
                 for (int ks = 0; ks < (tb + 1) * 2; ++ks) {
                     const u32x4_t sb = *reinterpret_cast<const u32x4_t*>(&sc[t][ks * 16 + half * 8]);
                     ot[tb] = scan_mfma(va[ks], sb, ot[tb]);
                 }
             }
-    #pragma unroll
+#pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const int d = db * 32 + l32;
-                if (SW) mt[db] *= zs;
-    #pragma unroll
+#pragma unroll
                 for (int ks = 0; ks < CH / 16; ++ks) {
                     const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(&kt[d][ks * 16 + half * 8]);
                     mt[db] = scan_mfma(ka, va[ks], mt[db]);
@@ -385,15 +379,16 @@ __global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
             }
             // ---- online read out: O_on[t][cv] (4 consecutive cv per register group), or its
             // product with dy_t summed over the wave's value rows ----
-    #pragma unroll
+#pragma unroll
             for (int tb = 0; tb < 2 && ON; ++tb) {
                 const int tl = tb * 32 + l32;
                 if (dgs) {
                     float part = 0.f;
                     if (tl < n) {
-    #pragma unroll
+#pragma unroll
                         for (int g = 0; g < 4; ++g) {
-                            const u32x2_t y = py[tb][g];
+                            const u32x2_t y = *reinterpret_cast<const u32x2_t*>(
+                                tile_at(yn, DV, tb * 32 + ln, wave * 32 + 8 * g + hf * 4));
                             part += ot[tb][4 * g] * __uint_as_float(y[0] << 16) +
                                     ot[tb][4 * g + 1] * __uint_as_float(y[0] & 0xffff0000u) +
                                     ot[tb][4 * g + 2] * __uint_as_float(y[1] << 16) +
@@ -404,25 +399,18 @@ __global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
                     if (half == 0) red[(j0 / CH) & 1][wave][tl] = part;
                 } else if (tl < n) {
                     float* orow = O_on + (bh * L + t0 + j0 + tl) * DV + wave * 32 + half * 4;
-    #pragma unroll
+#pragma unroll
                     for (int g = 0; g < 4; ++g)
                         *reinterpret_cast<float4*>(orow + 8 * g) =
                             make_float4(ot[tb][4 * g], ot[tb][4 * g + 1], ot[tb][4 * g + 2],
                                         ot[tb][4 * g + 3]);
                 }
             }
-            // ---- bf16 copy of the updated state as the next chunk's A operand ----
-    #pragma unroll
-            for (int db = 0; db < DB && ON; ++db)
-    #pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-                    ma[2 * db + hh] = u32x4_t{pk2(mt[db][8 * hh + 0], mt[db][8 * hh + 1]),
-                                              pk2(mt[db][8 * hh + 2], mt[db][8 * hh + 3]),
-                                              pk2(mt[db][8 * hh + 4], mt[db][8 * hh + 5]),
-                                              pk2(mt[db][8 * hh + 6], mt[db][8 * hh + 7])};
-            // the next chunk's rows have landed for this lane; after the barrier for every lane
-            if (more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
+            __syncthreads();  // the transposed tiles, the scores and dy have been read
+            if (more) {
+                dma_kvq(j0 + CH, nn);
+                dma_y(j0 + CH, nn);
+            }
         }
     } else {
         for (int j0 = 0; j0 < len; j0 += CH) {
@@ -662,13 +650,15 @@ __global__ __launch_bounds__(DV * 2, SW ? 2 : 1) void scan_mfma_kernel(
     if (dgs && len > 0) flush_dgs(((len - 1) / CH) * CH);
     // ---- emit the segment state: M[cv][d] (fp32 and bf16), 4 consecutive d per group ----
     if (!M) return;  // online read only
-    const int cv = wave * 32 + l32;
+    int te = tid;  // (the thread index re-formed here, not held across the chunk loop)
+    asm volatile("" : "+v"(te));
+    const int cv = (te >> 6) * 32 + (te & 31), he = (te & 63) >> 5;
     const size_t mo = ((bh * NS + s) * DV + cv) * (size_t)DK;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const int d = db * 32 + 8 * g + 4 * half;
+            const int d = db * 32 + 8 * g + 4 * he;
             *reinterpret_cast<float4*>(M + mo + d) =
                 make_float4(mt[db][4 * g], mt[db][4 * g + 1], mt[db][4 * g + 2], mt[db][4 * g + 3]);
             if (M_lo)  // (optional: the pieces of a split segment keep only fp32)
