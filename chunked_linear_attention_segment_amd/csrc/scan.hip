@@ -226,7 +226,9 @@ __device__ __forceinline__ int piece_end(const PieceArg& pa, int j, int NP) {
 // of all of them.  One workgroup per (segment, b*H+h, 512-element slice of the d_v x d_k
 // state) walks the segment's pieces in order, sixteen pieces at a time: every load of a batch
 // is issued before the first sum (rows past the segment's last piece are read clamped to it
-// and not used).
+// and not used).  The segment is the slowest grid index, so the workgroups of the first
+// segments, which walk the most pieces when the segments shrink along the sequence, are
+// dispatched first.
 template <int DK, int DV>
 __global__ __launch_bounds__(128) void piece_prefix_kernel(const float* __restrict__ Msub,
                                                            int NP, const PieceArg pa, int NS,
@@ -235,10 +237,10 @@ __global__ __launch_bounds__(128) void piece_prefix_kernel(const float* __restri
                                                            bf16_t* __restrict__ M_lo) {
     constexpr int N = DV * DK;
     constexpr int BATCH = 16;
-    const int seg = blockIdx.x;
+    const int seg = blockIdx.z;  // slowest: the longest segments (the first) start first
     const int j = segment_first_piece(pa, seg);
     const size_t bh = blockIdx.y;
-    const int e0 = blockIdx.z * 512 + 4 * threadIdx.x;
+    const int e0 = blockIdx.x * 512 + 4 * threadIdx.x;
     const int jend = piece_end(pa, j, NP);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int b = j; b < jend; b += BATCH) {
@@ -307,7 +309,7 @@ static int launch_pieces_t(const mc_dims& d, const PieceArg& pa, int NS, float* 
                            float* Pref, float* M, uint16_t* M_lo, hipStream_t st) {
     const int NP = pa.sg.n;
     static_assert(DV * DK % 512 == 0, "512-element slices");
-    hipLaunchKernelGGL((piece_prefix_kernel<DK, DV>), dim3(NS, d.B * d.H, DV * DK / 512),
+    hipLaunchKernelGGL((piece_prefix_kernel<DK, DV>), dim3(DV * DK / 512, d.B * d.H, NS),
                        dim3(128), 0, st, Msub, NP, pa, NS, Pref, M, (bf16_t*)M_lo);
     return (int)hipGetLastError();
 }
