@@ -34,6 +34,7 @@
 //      two k-steps ahead, and every MFMA is followed by the three VALU ops that build a
 //      quarter of a B fragment of the next k-step, which the matrix unit hides;
 //   4. y = acc / l_t in bf16 (with the gate pass: staged through LDS into whole-row stores).
+#include <atomic>
 #include <type_traits>
 
 #include "common.cuh"
@@ -114,14 +115,15 @@ __device__ __forceinline__ void tile_of_block(int bid, int BH, int T, int& bh, i
     }
 }
 
+// One 256-token tile: flat block index bid (see tile_of_block), LDS at smem_raw.
 template <int DK, int DV, bool SSC, bool FON, int PHI, bool PRE>
-__global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
+__device__ __forceinline__ void grm_read_tile(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ U, const float* __restrict__ xps, const bf16_t* __restrict__ S,
     const float* __restrict__ P, const float* __restrict__ O_on,
     const int32_t* __restrict__ idx, const bf16_t* __restrict__ Wg,
     const float* __restrict__ won_g, const float* __restrict__ inv_l_g, int top_k, int BH,
-    int H, int L, int C, int NS, int DG, int xh, bf16_t* __restrict__ Y, const SegArg sg) {
+    int H, int L, int C, int NS, int DG, int xh, bf16_t* __restrict__ Y, const SegArg& sg, char* smem_raw, int bid) {
     static_assert(!(PRE && SSC), "precomputed weights are a GRM mode");
     static_assert(RT == kGateTile, "the gate pass writes weights per read tile");
     constexpr int KS = DK / 16;  // MFMA k-steps over d_k
@@ -133,13 +135,16 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     typedef ReadSmem<DK, DV, SSC> Smem;
     constexpr int WMAX = Smem::WMAX;
     static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(16))) char smem_raw[sizeof(Smem)];
     Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
 
     const int T = (L + RT - 1) / RT;
     int bh, tile;
-    tile_of_block(blockIdx.x, BH, T, bh, tile);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    tile_of_block(bid, BH, T, bh, tile);
+    // the thread index re-formed per tile, so that values derived from it are not held in
+    // registers across the tiles of a persistent workgroup
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi32 = lane >> 5;
     const int tile0 = tile * RT;
     const int last = min(L, tile0 + RT) - 1;
@@ -810,6 +815,54 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     }
 }
 
+// The kernel: one tile per workgroup, or (the precomputed-gate read, with a grid of one
+// workgroup per CU) a share of the tiles per workgroup, taken in turn.  Nothing is shared
+// between tiles but the LDS, which the barrier after each tile hands back.
+template <int DK, int DV, bool SSC, bool FON, int PHI, bool PRE>
+__global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ U, const float* __restrict__ xps, const bf16_t* __restrict__ S,
+    const float* __restrict__ P, const float* __restrict__ O_on,
+    const int32_t* __restrict__ idx, const bf16_t* __restrict__ Wg,
+    const float* __restrict__ won_g, const float* __restrict__ inv_l_g, int top_k, int BH,
+    int H, int L, int C, int NS, int DG, int xh, bf16_t* __restrict__ Y, const SegArg sg) {
+    __shared__ __attribute__((aligned(16))) char smem_raw[sizeof(ReadSmem<DK, DV, SSC>)];
+    if constexpr (PRE) {
+        const int nblk = BH * ((L + RT - 1) / RT);
+        // block indices dealt in stripes of the grid, every other stripe in reverse, so that
+        // each workgroup gets an even share of the heavy (early) and light (late) tiles; with
+        // a grid of whole XCD rounds a workgroup's tiles are all of its own XCD
+        const int G = gridDim.x, g = blockIdx.x;
+        const int R = G % 8 == 0 ? 8 : 1, W = G / R, x = g % R, w = g / R;
+        for (int k = 0;; ++k) {
+            const int bid = (k * W + ((k & 1) ? W - 1 - w : w)) * R + x;
+            if (bid >= nblk) break;
+            grm_read_tile<DK, DV, SSC, FON, PHI, PRE>(Q, K, V, U, xps, S, P, O_on, idx, Wg,
+                                                      won_g, inv_l_g, top_k, BH, H, L, C, NS,
+                                                      DG, xh, Y, sg, smem_raw, bid);
+            __syncthreads();
+        }
+    } else {
+        grm_read_tile<DK, DV, SSC, FON, PHI, PRE>(Q, K, V, U, xps, S, P, O_on, idx, Wg, won_g,
+                                                  inv_l_g, top_k, BH, H, L, C, NS, DG, xh, Y,
+                                                  sg, smem_raw, blockIdx.x);
+    }
+}
+
+// Compute units of the current device (0 when the query fails), looked up once per device.
+int cu_count() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cached[kMaxDev];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 template <int DK, int DV, bool SSC, bool FON, int PHI, bool PRE>
 void launch_k(const mc_dims& d, int top_k, const void* Q, const void* K, const void* V,
               const void* U, const float* xps, const uint16_t* M_lo, const float* P,
@@ -818,7 +871,14 @@ void launch_k(const mc_dims& d, int top_k, const void* Q, const void* K, const v
     const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
     const int T = (d.L + RT - 1) / RT;
     const int BH = d.B * d.H;
-    hipLaunchKernelGGL((grm_read_kernel<DK, DV, SSC, FON, PHI, PRE>), dim3(BH * T),
+    // the precomputed-gate read runs one workgroup per CU (a workgroup fills a CU's LDS), each
+    // walking its share of the tiles: no dispatch between tiles, and a CU's tiles stay in order
+    int grid = BH * T;
+    if constexpr (PRE) {
+        const int ncu = cu_count();
+        if (ncu > 0 && grid > ncu) grid = ncu;
+    }
+    hipLaunchKernelGGL((grm_read_kernel<DK, DV, SSC, FON, PHI, PRE>), dim3(grid),
                        dim3(RTHREADS), 0, st, (const bf16_t*)Q, (const bf16_t*)K,
                        (const bf16_t*)V, (const bf16_t*)U, xps, (const bf16_t*)M_lo, P, O_on,
                        idx, (const bf16_t*)gw.W, gw.won, gw.inv_l, top_k, BH, d.H, d.L,
