@@ -19,8 +19,10 @@
 // tokens.  The logits run on bf16
 // MFMA with each mean split into a bf16 high part and a bf16 remainder (about 16 mantissa
 // bits; laid out as MFMA fragments once, by pfrag_kernel, for every workgroup to share through
-// the caches), u_t exact in bf16, fp32 accumulation.  Pass 1 takes m_t over every logit, pass 2 writes the
-// numerators, transposed through LDS into 16-byte stores of whole rows.
+// the caches), u_t exact in bf16, fp32 accumulation.  Up to 128 states the logits stay in
+// registers: m_t is taken over them, then the numerators are written, transposed through LDS
+// into 16-byte stores of whole rows.  With more states pass 1 takes m_t over every logit and
+// pass 2 forms them again for the numerators.
 #include <type_traits>
 
 #include "common.cuh"
@@ -115,9 +117,8 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
                 xv[kc][1] = *reinterpret_cast<const float4*>(xr + kc * 16 + 4);
             }
     }
-    // u_t of head g as the B operand of the logits (token = column, k = 16 kc + 8 hi32 + e);
-    // the next head's are loaded while this head's logits run
-    gu32x4_t ub[GDG_MAX / 16], un[GDG_MAX / 16];
+    // u_t of head g as the B operand of the logits (token = column, k = 16 kc + 8 hi32 + e)
+    gu32x4_t ub[GDG_MAX / 16];
     auto load_u = [&](int g, gu32x4_t (&dst)[GDG_MAX / 16]) {
 #pragma unroll
         for (int kc = 0; kc < GDG_MAX / 16; ++kc)
@@ -125,13 +126,10 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
                 dst[kc] = *reinterpret_cast<const gu32x4_t*>(
                     U + ((size_t)(bh0 + g) * L + tok) * DG + kc * 16 + hi32 * 8);
     };
-    load_u(0, un);
     for (int g = 0; g < G; ++g) {
         const int bh = bh0 + g;
         bf16_t* Wt = W + ((size_t)bh * T + tile) * NS * GT + half * GW;
-#pragma unroll
-        for (int kc = 0; kc < GDG_MAX / 16; ++kc) ub[kc] = un[kc];
-        if (g + 1 < G) load_u(g + 1, un);
+        load_u(g, ub);
         // the online logit <u_t, xps_t> / (j + 1); the lane halves are summed
         float dot = 0.f;
 #pragma unroll
@@ -240,8 +238,51 @@ __global__ __launch_bounds__(256, 2) void gate_w_kernel(
             inv_l_out[(size_t)bh * L + tok] = 1.f / (l + wo);
         }
         };
+        // up to GPF_STATES states (the means staged in LDS): one pass, the logits kept in
+        // registers between the max and the numerators
+        auto one_pass = [&]() {
+            gf32x16_t lgs[GPF_STATES / 32];
+            float m = a_on;
+#pragma unroll
+            for (int b = 0; b < GPF_STATES / 32; ++b) {
+                if (b * 32 >= s_hi) break;
+                lgs[b] = logits(b * 32, std::true_type{});
+                float bm = -INFINITY;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) bm = fmaxf(bm, lgs[b][r]);
+                m = fmaxf(m, fmaxf(bm, __shfl_xor(bm, 32, 64)));
+            }
+            float l = 0.f;
+#pragma unroll
+            for (int b = 0; b < GPF_STATES / 32; ++b) {
+                if (b * 32 >= s_hi) break;
+                float ps = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float wv = val ? __expf(lgs[b][r] - m) : 0.f;
+                    ps += wv;
+                    wt[8 * (r / 4) + 4 * hi32 + (r % 4)][tl] = f32_to_bf16(wv);
+                }
+                l += ps + __shfl_xor(ps, 32, 64);
+                __syncthreads();
+                const int rows = min(32, s_hi - b * 32);
+#pragma unroll
+                for (int q = 0; q < 32 * GW / 8 / 256; ++q) {
+                    const int c = q * 256 + tid, row = c / (GW / 8), col = (c % (GW / 8)) * 8;
+                    if (row < rows)
+                        *reinterpret_cast<uint4*>(Wt + (size_t)(b * 32 + row) * GT + col) =
+                            *reinterpret_cast<const uint4*>(&wt[row][col]);
+                }
+                __syncthreads();
+            }
+            if (val && !hi32) {
+                const float wo = __expf(a_on - m);
+                won_out[(size_t)bh * L + tok] = wo;
+                inv_l_out[(size_t)bh * L + tok] = 1.f / (l + wo);
+            }
+        };
         if (lds_pf)
-            passes(std::true_type{});
+            one_pass();
         else
             passes(std::false_type{});
     }
