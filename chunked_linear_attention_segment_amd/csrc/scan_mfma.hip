@@ -92,9 +92,9 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
     constexpr int GW = SW ? CH : 1; // SWLA tables (1-element placeholders otherwise)
     // phi(k)^T [d][r], v^T [cv][r] and the masked scores [t][r]; without SWLA the chunk's k,
     // v and q rows arrive in the same places first (see below)
-    constexpr int KBE = SW || DK * TPAD > CH * DK ? DK * TPAD : CH * DK;
-    constexpr int VBE = SW || DV * TPAD > CH * DV ? DV * TPAD : CH * DV;
-    constexpr int QBE = !ON ? 8 : (SW || CH * TPAD > CH * DK ? CH * TPAD : CH * DK);
+    constexpr int KBE = DK * TPAD > CH * DK ? DK * TPAD : CH * DK;
+    constexpr int VBE = DV * TPAD > CH * DV ? DV * TPAD : CH * DV;
+    constexpr int QBE = !ON ? 8 : (CH * TPAD > CH * DK ? CH * TPAD : CH * DK);
     __shared__ __attribute__((aligned(16))) bf16_t kbuf[KBE];
     __shared__ __attribute__((aligned(16))) bf16_t vbuf[VBE];
     __shared__ __attribute__((aligned(16))) bf16_t qbuf[QBE];
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
     __shared__ float red[ON ? 2 : 1][ON ? DV / 32 : 1][ON ? CH : 1];
     // the chunk's dy rows as loaded (the backward's <dy, O_on>; not SWLA)
     __shared__ __attribute__((aligned(16))) bf16_t yn[ON && !SW ? CH * DV : 8];
-    bf16_t* const kn = kbuf;  // the chunk's k, v, q rows as loaded (not SWLA)
+    bf16_t* const kn = kbuf;  // the chunk's k, v, q rows as loaded
     bf16_t* const vn = vbuf;
     bf16_t* const qn = qbuf;
 
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
             }
         }
     };
-    if constexpr (!SW) {
+    {
         // The chunk's rows of k, v and q (and dy) arrive in LDS as whole rows by direct
         // global->LDS loads; row r's 16-byte chunk c sits at c ^ (r % chunks per row), and rows
         // past the chunk are loaded clamped to its last row (their products are masked).  The
@@ -202,8 +202,20 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
             if constexpr (ON) dma_tile(Qs, DK, lds_base(qn), jn, nn);
         };
         auto dma_y = [&](int jn, int nn) {
-            if constexpr (ON) {
+            if constexpr (ON && !SW) {
                 if (dgs) dma_tile(dY + gbase * DV, DV, lds_base(yn), jn, nn);
+            }
+        };
+        // SWLA: the gates of a chunk's tokens (slot CH: the token after the chunk; zero past the
+        // segment), loaded into registers a chunk ahead and stored to LDS at the chunk's start
+        float pga = 0.f, pgb = 0.f, pgl = 0.f;
+        auto load_gates = [&](int jn) {
+            if constexpr (SW) {
+                const int nc = min(CH, len - jn);
+                const bool in = tid <= CH && jn + tid < len && tid <= nc;
+                pga = in ? gt.alpha[gbase + jn + tid] : 0.f;
+                pgb = in ? gt.beta[gbase + jn + tid] : 0.f;
+                pgl = in && tid < nc ? gt.lam[gbase + jn + tid] : 0.f;
             }
         };
         constexpr int NIK = (CH / 2) * (DK / 8) / NT, NIV = (CH / 2) * (DV / 8) / NT;
@@ -213,6 +225,7 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
         if (len > 0) {
             dma_kvq(0, min(CH, len));
             dma_y(0, min(CH, len));
+            load_gates(0);
         }
         for (int j0 = 0; j0 < len; j0 += CH) {
             const int n = min(CH, len - j0);
@@ -222,6 +235,44 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (dgs && j0 > 0) flush_dgs(j0 - CH);
+            const bool last = j0 + n == len;  // the segment ends in this chunk
+            if constexpr (SW) {
+                if (tid <= CH) {
+                    ga[tid] = pga;
+                    gb[tid] = pgb;
+                    if (tid < CH) gl[tid] = pgl;
+                }
+                __syncthreads();
+                if (tid < CH) {  // column r: c[r][r] = lam_r, then a running product down t
+                    const int r = tid;
+                    float c = gl[r];
+                    cf[r][r] = c;
+                    if (r + 1 < CH) {
+                        c = ga[r + 1] * gl[r] + gb[r + 1];
+                        cf[r + 1][r] = c;
+                        for (int t = r + 2; t < CH; ++t) {
+                            c *= ga[t];
+                            cf[t][r] = c;
+                        }
+                    }
+                } else if (tid == CH) {
+                    float p = 1.f;
+                    dz[0] = p;
+                    for (int t = 1; t < CH; ++t) {
+                        p *= ga[t];
+                        dz[t] = p;
+                    }
+                }
+                __syncthreads();
+            }
+            // SWLA: final weight of each key of the chunk in the state carried out of it, and
+            // the factor on the incoming state
+            float zs = 1.f;
+            if constexpr (SW) zs = last ? dz[n - 1] : ga[CH] * dz[CH - 1];
+            auto key_weight = [&](int r) -> float {
+                if (r >= n) return 0.f;
+                return last ? cf[n - 1][r] : ga[CH] * cf[CH - 1][r] + (r == CH - 1 ? gb[CH] : 0.f);
+            };
             // the lane indices as the compiler cannot see them: the LDS addresses below are
             // formed per chunk, not held in registers across the chunk loop
             int ln = l32, hf = half, td = tid;
@@ -258,6 +309,10 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
                                             pk2(mt[db][8 * hh + 6], mt[db][8 * hh + 7])};
 #pragma unroll
                         for (int tb = 0; tb < 2; ++tb) ot[tb] = scan_mfma(mk, qb[tb][ks], ot[tb]);
+                    }
+                    if constexpr (SW) {  // the state decays by alpha_{j0+1} .. alpha_t before t reads it
+#pragma unroll
+                        for (int tb = 0; tb < 2; ++tb) ot[tb] *= dz[tb * 32 + ln];
                     }
                 }
             }
@@ -310,6 +365,13 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
                         b0 = r1 < n ? feature(b0, 1) : 0.f;
                         b1 = r1 < n ? feature(b1, 1) : 0.f;
                     }
+                    if constexpr (SW) {
+                        const float w0 = key_weight(r0), w1 = key_weight(r1);
+                        a0 *= w0;
+                        a1 *= w0;
+                        b0 *= w1;
+                        b1 *= w1;
+                    }
                     *reinterpret_cast<uint32_t*>(&kt[dc + 2 * e][r0]) = pk2(a0, b0);
                     *reinterpret_cast<uint32_t*>(&kt[dc + 2 * e + 1][r0]) = pk2(a1, b1);
                 }
@@ -323,10 +385,16 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int r = rb * 32 + 8 * g + 4 * half;
-                    const float v0 = (r + 0 <= t) ? sacc[q][4 * g + 0] : 0.f;
-                    const float v1 = (r + 1 <= t) ? sacc[q][4 * g + 1] : 0.f;
-                    const float v2 = (r + 2 <= t) ? sacc[q][4 * g + 2] : 0.f;
-                    const float v3 = (r + 3 <= t) ? sacc[q][4 * g + 3] : 0.f;
+                    float v0 = (r + 0 <= t) ? sacc[q][4 * g + 0] : 0.f;
+                    float v1 = (r + 1 <= t) ? sacc[q][4 * g + 1] : 0.f;
+                    float v2 = (r + 2 <= t) ? sacc[q][4 * g + 2] : 0.f;
+                    float v3 = (r + 3 <= t) ? sacc[q][4 * g + 3] : 0.f;
+                    if constexpr (SW) {
+                        v0 = (r + 0 <= t) ? v0 * cf[t][r + 0] : 0.f;
+                        v1 = (r + 1 <= t) ? v1 * cf[t][r + 1] : 0.f;
+                        v2 = (r + 2 <= t) ? v2 * cf[t][r + 2] : 0.f;
+                        v3 = (r + 3 <= t) ? v3 * cf[t][r + 3] : 0.f;
+                    }
                     *reinterpret_cast<u32x2_t*>(&sc[t][r]) = u32x2_t{pk2(v0, v1), pk2(v2, v3)};
                 }
             }
@@ -371,6 +439,7 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const int d = db * 32 + l32;
+                if constexpr (SW) mt[db] *= zs;
 #pragma unroll
                 for (int ks = 0; ks < CH / 16; ++ks) {
                     const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(&kt[d][ks * 16 + half * 8]);
@@ -382,7 +451,7 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
 #pragma unroll
             for (int tb = 0; tb < 2 && ON; ++tb) {
                 const int tl = tb * 32 + l32;
-                if (dgs) {
+                if (!SW && dgs) {  // (the backward's pass: never with SWLA gates)
                     float part = 0.f;
                     if (tl < n) {
 #pragma unroll
@@ -410,241 +479,8 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
             if (more) {
                 dma_kvq(j0 + CH, nn);
                 dma_y(j0 + CH, nn);
+                load_gates(j0 + CH);
             }
-        }
-    } else {
-        for (int j0 = 0; j0 < len; j0 += CH) {
-            const int n = min(CH, len - j0);
-            if (dgs && j0 > 0) flush_dgs(j0 - CH);
-            const bool last = j0 + n == len;  // the segment ends in this chunk
-            if (SW) {
-                // gates of the chunk's tokens, zero past its end; slot CH is the next token's
-                if (tid <= CH) {
-                    const bool in = j0 + tid < len && tid <= n;
-                    ga[tid] = in ? gt.alpha[gbase + j0 + tid] : 0.f;
-                    gb[tid] = in ? gt.beta[gbase + j0 + tid] : 0.f;
-                    if (tid < CH) gl[tid] = in && tid < n ? gt.lam[gbase + j0 + tid] : 0.f;
-                }
-                __syncthreads();
-                if (tid < CH) {  // column r: c[r][r] = lam_r, then a running product down t
-                    const int r = tid;
-                    float c = gl[r];
-                    cf[r][r] = c;
-                    if (r + 1 < CH) {
-                        c = ga[r + 1] * gl[r] + gb[r + 1];
-                        cf[r + 1][r] = c;
-                        for (int t = r + 2; t < CH; ++t) {
-                            c *= ga[t];
-                            cf[t][r] = c;
-                        }
-                    }
-                } else if (tid == CH) {
-                    float p = 1.f;
-                    dz[0] = p;
-                    for (int t = 1; t < CH; ++t) {
-                        p *= ga[t];
-                        dz[t] = p;
-                    }
-                }
-                __syncthreads();
-            }
-            // ---- phi(q) B-fragments (k order of the accumulator rows) for both token blocks ----
-            u32x4_t qb[2][KSD];
-            f32x16_t ot[2];
-            if (ON) {
-    #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) {
-                    const int tl = tb * 32 + l32;
-                    const bool ok = tl < n;
-                    const bf16_t* qr = Qs + (size_t)(j0 + (ok ? tl : 0)) * DK + half * 4;
-    #pragma unroll
-                    for (int ks = 0; ks < KSD; ++ks) {
-                        u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
-                        if (ok) {
-                            lo = phi4(*reinterpret_cast<const u32x2_t*>(qr + ks * 16), phi);
-                            hi = phi4(*reinterpret_cast<const u32x2_t*>(qr + ks * 16 + 8), phi);
-                        }
-                        qb[tb][ks] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-                    }
-                }
-                // ---- O^T = M_prev phi(q)^T (first term of the online read) ----
-    #pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
-    #pragma unroll
-                    for (int r = 0; r < 16; ++r) ot[tb][r] = 0.f;
-                if (j0 > 0 || M0) {
-    #pragma unroll
-                    for (int ks = 0; ks < KSD; ++ks)
-    #pragma unroll
-                        for (int tb = 0; tb < 2; ++tb) ot[tb] = scan_mfma(ma[ks], qb[tb][ks], ot[tb]);
-                    if (SW) {  // Z decays by alpha_{j0+1} .. alpha_t before token t reads it
-    #pragma unroll
-                        for (int tb = 0; tb < 2; ++tb) ot[tb] *= dz[tb * 32 + l32];
-                    }
-                }
-            }
-            // SWLA: final weight of each key of the chunk in the state carried out of it
-            float zs = 1.f;  // and the factor on the incoming Z
-            if (SW) zs = last ? dz[n - 1] : ga[CH] * dz[CH - 1];
-            auto key_weight = [&](int r) -> float {
-                if (r >= n) return 0.f;
-                return last ? cf[n - 1][r] : ga[CH] * cf[CH - 1][r] + (r == CH - 1 ? gb[CH] : 0.f);
-            };
-            // ---- stage phi(k)^T and v^T (token pairs packed in 32-bit LDS words) ----
-            for (int it = tid; it < (CH / 2) * (DK / 8); it += NT) {
-                const int p = it % (CH / 2), dc = (it / (CH / 2)) * 8;
-                const int r0 = 2 * p, r1 = 2 * p + 1;
-                u32x4_t a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-                if (r0 < n) a = *reinterpret_cast<const u32x4_t*>(Ks + (size_t)(j0 + r0) * DK + dc);
-                if (r1 < n) b = *reinterpret_cast<const u32x4_t*>(Ks + (size_t)(j0 + r1) * DK + dc);
-    #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float a0 = __uint_as_float(a[e] << 16), a1 = __uint_as_float(a[e] & 0xffff0000u);
-                    float b0 = __uint_as_float(b[e] << 16), b1 = __uint_as_float(b[e] & 0xffff0000u);
-                    if (phi) {
-                        a0 = r0 < n ? feature(a0, 1) : 0.f;
-                        a1 = r0 < n ? feature(a1, 1) : 0.f;
-                        b0 = r1 < n ? feature(b0, 1) : 0.f;
-                        b1 = r1 < n ? feature(b1, 1) : 0.f;
-                    }
-                    if (SW) {
-                        const float w0 = key_weight(r0), w1 = key_weight(r1);
-                        a0 *= w0;
-                        a1 *= w0;
-                        b0 *= w1;
-                        b1 *= w1;
-                    }
-                    *reinterpret_cast<uint32_t*>(&kt[dc + 2 * e][r0]) = pk2(a0, b0);
-                    *reinterpret_cast<uint32_t*>(&kt[dc + 2 * e + 1][r0]) = pk2(a1, b1);
-                }
-            }
-            for (int it = tid; it < (CH / 2) * (DV / 8); it += NT) {
-                const int p = it % (CH / 2), dc = (it / (CH / 2)) * 8;
-                const int r0 = 2 * p, r1 = 2 * p + 1;
-                u32x4_t a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-                if (r0 < n) a = *reinterpret_cast<const u32x4_t*>(Vs + (size_t)(j0 + r0) * DV + dc);
-                if (r1 < n) b = *reinterpret_cast<const u32x4_t*>(Vs + (size_t)(j0 + r1) * DV + dc);
-    #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    *reinterpret_cast<uint32_t*>(&vt[dc + 2 * e][r0]) =
-                        (a[e] & 0xffffu) | (b[e] << 16);
-                    *reinterpret_cast<uint32_t*>(&vt[dc + 2 * e + 1][r0]) =
-                        (a[e] >> 16) | (b[e] & 0xffff0000u);
-                }
-            }
-            // ---- causal scores S^T[r][t] = phi(k_r).phi(q_t), r <= t: blocks (rb,tb) = (0,0),
-            //      (0,1), (1,1) dealt to the waves; block (1,0) is all masked and never read ----
-            for (int blk = wave; ON && blk < 3; blk += NT / 64) {
-                const int rb = blk == 2 ? 1 : 0, tb = blk == 0 ? 0 : 1;
-                const int rl = rb * 32 + l32;
-                const bool ok = rl < n;
-                const bf16_t* kr = Ks + (size_t)(j0 + (ok ? rl : 0)) * DK + half * 4;
-                f32x16_t sacc;
-    #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-                // key fragments loaded two k-steps ahead, unconditionally (kr is a valid row), and
-                // zeroed past the chunk at their use: a conditional load used at once made the
-                // compiler wait for every load and store in flight before each MFMA
-                u32x2_t kl[3], kh[3];
-                auto kload = [&](int ks) {
-                    kl[ks % 3] = *reinterpret_cast<const u32x2_t*>(kr + ks * 16);
-                    kh[ks % 3] = *reinterpret_cast<const u32x2_t*>(kr + ks * 16 + 8);
-                };
-                kload(0);
-                if (KSD > 1) kload(1);
-    #pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) {
-                    if (ks + 2 < KSD) kload(ks + 2);
-                    u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
-                    if (ok) {
-                        lo = phi4(kl[ks % 3], phi);
-                        hi = phi4(kh[ks % 3], phi);
-                    }
-                    sacc = scan_mfma(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, tb ? qb[1][ks] : qb[0][ks],
-                                     sacc);
-                }
-                const int t = tb * 32 + l32;
-    #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int r = rb * 32 + 8 * g + 4 * half;
-                    float v0 = (r + 0 <= t) ? sacc[4 * g + 0] : 0.f;
-                    float v1 = (r + 1 <= t) ? sacc[4 * g + 1] : 0.f;
-                    float v2 = (r + 2 <= t) ? sacc[4 * g + 2] : 0.f;
-                    float v3 = (r + 3 <= t) ? sacc[4 * g + 3] : 0.f;
-                    if (SW) {
-                        v0 = (r + 0 <= t) ? v0 * cf[t][r + 0] : 0.f;
-                        v1 = (r + 1 <= t) ? v1 * cf[t][r + 1] : 0.f;
-                        v2 = (r + 2 <= t) ? v2 * cf[t][r + 2] : 0.f;
-                        v3 = (r + 3 <= t) ? v3 * cf[t][r + 3] : 0.f;
-                    }
-                    *reinterpret_cast<u32x2_t*>(&sc[t][r]) = u32x2_t{pk2(v0, v1), pk2(v2, v3)};
-                }
-            }
-            __syncthreads();
-            // ---- O^T += v^T S^T (intra-chunk term) and M^T += phi(k)^T v (state update) ----
-            const int cv = wave * 32 + l32;
-            u32x4_t va[CH / 16];
-    #pragma unroll
-            for (int ks = 0; ks < CH / 16; ++ks)
-                va[ks] = *reinterpret_cast<const u32x4_t*>(&vt[cv][ks * 16 + half * 8]);
-    #pragma unroll
-            for (int tb = 0; tb < 2 && ON; ++tb) {
-                const int t = tb * 32 + l32;
-    #pragma unroll
-                for (int ks = 0; ks < (tb + 1) * 2; ++ks) {
-                    const u32x4_t sb = *reinterpret_cast<const u32x4_t*>(&sc[t][ks * 16 + half * 8]);
-                    ot[tb] = scan_mfma(va[ks], sb, ot[tb]);
-                }
-            }
-    #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int d = db * 32 + l32;
-                if (SW) mt[db] *= zs;
-    #pragma unroll
-                for (int ks = 0; ks < CH / 16; ++ks) {
-                    const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(&kt[d][ks * 16 + half * 8]);
-                    mt[db] = scan_mfma(ka, va[ks], mt[db]);
-                }
-            }
-            // ---- online read out: O_on[t][cv] (4 consecutive cv per register group), or its
-            // product with dy_t summed over the wave's value rows ----
-    #pragma unroll
-            for (int tb = 0; tb < 2 && ON; ++tb) {
-                const int tl = tb * 32 + l32;
-                if (dgs) {
-                    float part = 0.f;
-                    if (tl < n) {
-                        const bf16_t* yrow = dY + (gbase + j0 + tl) * DV + wave * 32 + half * 4;
-    #pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const u32x2_t y = *reinterpret_cast<const u32x2_t*>(yrow + 8 * g);
-                            part += ot[tb][4 * g] * __uint_as_float(y[0] << 16) +
-                                    ot[tb][4 * g + 1] * __uint_as_float(y[0] & 0xffff0000u) +
-                                    ot[tb][4 * g + 2] * __uint_as_float(y[1] << 16) +
-                                    ot[tb][4 * g + 3] * __uint_as_float(y[1] & 0xffff0000u);
-                        }
-                    }
-                    part += __shfl_xor(part, 32);
-                    if (half == 0) red[(j0 / CH) & 1][wave][tl] = part;
-                } else if (tl < n) {
-                    float* orow = O_on + (bh * L + t0 + j0 + tl) * DV + wave * 32 + half * 4;
-    #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        *reinterpret_cast<float4*>(orow + 8 * g) =
-                            make_float4(ot[tb][4 * g], ot[tb][4 * g + 1], ot[tb][4 * g + 2],
-                                        ot[tb][4 * g + 3]);
-                }
-            }
-            // ---- bf16 copy of the updated state as the next chunk's A operand ----
-    #pragma unroll
-            for (int db = 0; db < DB && ON; ++db)
-    #pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-                    ma[2 * db + hh] = u32x4_t{pk2(mt[db][8 * hh + 0], mt[db][8 * hh + 1]),
-                                              pk2(mt[db][8 * hh + 2], mt[db][8 * hh + 3]),
-                                              pk2(mt[db][8 * hh + 4], mt[db][8 * hh + 5]),
-                                              pk2(mt[db][8 * hh + 6], mt[db][8 * hh + 7])};
-            __syncthreads();
         }
     }
     if (dgs && len > 0) flush_dgs(((len - 1) / CH) * CH);
