@@ -250,6 +250,7 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
                     if (r + 1 < CH) {
                         c = ga[r + 1] * gl[r] + gb[r + 1];
                         cf[r + 1][r] = c;
+#pragma unroll 8
                         for (int t = r + 2; t < CH; ++t) {
                             c *= ga[t];
                             cf[t][r] = c;
@@ -258,6 +259,7 @@ __global__ __launch_bounds__(DV * 2, 2) void scan_mfma_kernel(
                 } else if (tid == CH) {
                     float p = 1.f;
                     dz[0] = p;
+#pragma unroll 8
                     for (int t = 1; t < CH; ++t) {
                         p *= ga[t];
                         dz[t] = p;
