@@ -8,6 +8,8 @@
 //   y_t     = gamma^(s) M_t^(s) phi(q_t) + sum_{i<s} gamma^(i) M^(i) phi(q_t).
 // Sparse Selective Caching (gitcode explainer §3.4): the same read over the Top-k cached
 // segments by router score a_t^(i), plus the online memory, with the softmax over those.
+#include <algorithm>
+
 #include "common.cuh"
 #include "mc_internal.h"
 
@@ -122,12 +124,15 @@ int launch_aon(const mc_dims& d, const void* X, const void* U, float* a_on, void
 // the first token of t's segment to t (the numerator of the online segment's prefix mean,
 // Memory Caching paper §3.1, Eq. 10).  The sequence is cut into chunks of XCH tokens, one
 // workgroup per (chunk, b*xh) and one thread per column, which scans its column of the chunk
-// in registers and restarts at every segment start.  Two launches:
+// in registers and restarts at every segment start.  Three launches:
 //   TAIL = true   tails[chunk, e]: the chunk's sum over its rows in the segment of its last
 //                 row (the whole chunk unless a segment starts inside it)
+//   group sums    of XSC consecutive tails (xps_group_kernel)
 //   TAIL = false  the carry of the chunk's first segment (the tails of the earlier chunks that
-//                 segment spans) plus the in-chunk scan, written to xps
+//                 segment spans, whole groups by their group sums) plus the in-chunk scan,
+//                 written to xps
 constexpr int XCH = 64;
+constexpr int XSC = 16;  // chunks per group of the second level of chunk sums
 
 template <typename T, bool TAIL>
 __global__ __launch_bounds__(256) void xps_kernel(const T* __restrict__ X, int L, int C, int DG,
@@ -146,9 +151,16 @@ __global__ __launch_bounds__(256) void xps_kernel(const T* __restrict__ X, int L
     int si = seg_of(sg, c0, C);           // segment of the chunk's first row
     const int ss = seg_first(sg, si, C);  // and its start
     if (!TAIL) {
-#pragma unroll 16
-        for (int cc = c - 1; cc >= 0 && (cc + 1) * XCH > ss; --cc)
-            run += tails[(bx * nch + cc) * DG + e];
+        // the sums of the segment's earlier chunks cs .. c-1 (chunk cs holds its start): whole
+        // groups of XSC chunks by their group sums, the chunks before and after one by one
+        const float* stails = tails + (size_t)gridDim.y * nch * DG;
+        const int nsc = (nch + XSC - 1) / XSC;
+        const int cs = ss / XCH;
+        const int A = min(c, (cs + XSC - 1) / XSC * XSC), B = max(A, c / XSC * XSC);
+        for (int cc = cs; cc < A; ++cc) run += tails[(bx * nch + cc) * DG + e];
+#pragma unroll 8
+        for (int g = A / XSC; g < B / XSC; ++g) run += stails[(bx * nsc + g) * DG + e];
+        for (int cc = B; cc < c; ++cc) run += tails[(bx * nch + cc) * DG + e];
     }
     int nb = seg_first(sg, si + 1, C);  // the next segment start
     float* out = xps + (bx * L + c0) * DG + e;
@@ -166,6 +178,24 @@ __global__ __launch_bounds__(256) void xps_kernel(const T* __restrict__ X, int L
         }
     }
     if (TAIL) tails[(bx * nch + c) * DG + e] = run;
+}
+
+// Group sums of the chunk sums: group g of (b, x head) = chunks g XSC .. g XSC + XSC - 1.  Only
+// groups that lie inside one segment are read (there the chunk sums are whole-chunk sums).
+__global__ __launch_bounds__(256) void xps_group_kernel(const float* __restrict__ tails,
+                                                        int nch, int DG,
+                                                        float* __restrict__ stails) {
+    const int g = blockIdx.x, nsc = gridDim.x;
+    const size_t bx = blockIdx.y;
+    const int e = threadIdx.x;
+    if (e >= DG) return;
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < XSC; ++i) {
+        const int c = g * XSC + i;
+        if (c < nch) a += tails[(bx * nch + c) * DG + e];
+    }
+    stails[(bx * nsc + g) * DG + e] = a;
 }
 
 // Online logits from the prefix sums: a_on[t] = <u_t, xps_t> / (j_t + 1), 8 threads per token.
@@ -189,26 +219,37 @@ __global__ __launch_bounds__(256) void aon_xps_kernel(const T* __restrict__ U,
     if (valid && p == 0) a_on[bh * L + t] = a / (float)(j + 1);
 }
 
+// chunk sums, then their group sums
 size_t xps_tail_floats(const mc_dims& d) {
-    return (size_t)d.B * d.x_heads * ((d.L + XCH - 1) / XCH) * d.d_g;
+    const size_t nch = (d.L + XCH - 1) / XCH;
+    return (size_t)d.B * d.x_heads * (nch + (nch + XSC - 1) / XSC) * d.d_g;
 }
 
 static int launch_xps_sg(const mc_dims& d, const void* X, float* xps, float* tails,
                          const SegArg& sg, hipStream_t st) {
     if (d.d_g > 256) return (int)hipErrorInvalidValue;
-    const dim3 grid((d.L + XCH - 1) / XCH, d.B * d.x_heads);
+    const int nch = (d.L + XCH - 1) / XCH;
+    const dim3 grid(nch, d.B * d.x_heads);
     const dim3 block((d.d_g + 63) / 64 * 64);
-    if (d.dtype == MC_BF16) {
+    float* stails = tails + (size_t)d.B * d.x_heads * nch * d.d_g;
+    if (d.dtype == MC_BF16)
         hipLaunchKernelGGL((xps_kernel<bf16_t, true>), grid, block, 0, st, (const bf16_t*)X, d.L,
                            d.seg_len, d.d_g, tails, xps, sg);
-        hipLaunchKernelGGL((xps_kernel<bf16_t, false>), grid, block, 0, st, (const bf16_t*)X, d.L,
-                           d.seg_len, d.d_g, tails, xps, sg);
-    } else {
+    else
         hipLaunchKernelGGL((xps_kernel<float, true>), grid, block, 0, st, (const float*)X, d.L,
                            d.seg_len, d.d_g, tails, xps, sg);
+    // the group sums are read only for a segment longer than (XSC - 1) XCH tokens
+    int longest = sg.n ? 0 : d.seg_len;
+    for (int i = 0; i < sg.n; ++i) longest = std::max(longest, sg.off[i + 1] - sg.off[i]);
+    if (longest > (XSC - 1) * XCH)
+        hipLaunchKernelGGL(xps_group_kernel, dim3((nch + XSC - 1) / XSC, d.B * d.x_heads), block,
+                           0, st, tails, nch, d.d_g, stails);
+    if (d.dtype == MC_BF16)
+        hipLaunchKernelGGL((xps_kernel<bf16_t, false>), grid, block, 0, st, (const bf16_t*)X, d.L,
+                           d.seg_len, d.d_g, tails, xps, sg);
+    else
         hipLaunchKernelGGL((xps_kernel<float, false>), grid, block, 0, st, (const float*)X, d.L,
                            d.seg_len, d.d_g, tails, xps, sg);
-    }
     return (int)hipGetLastError();
 }
 
