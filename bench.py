@@ -128,7 +128,8 @@ CALL_SOURCES = {
 }
 # the kernels of each call, by name fragment, as rocprofv3 lists them
 CALL_KERNELS = {
-    "grm_readout": ["xps_kernel", "pfrag_kernel", "gate_w_kernel", "grm_read_kernel"],
+    "grm_readout": ["xps_kernel", "xps_group_kernel", "pfrag_kernel", "gate_w_kernel",
+                    "grm_read_kernel"],
     "decode_step": ["decode_read_kernel", "decode_combine_kernel"],
     "ssc_readout": ["aon_kernel", "seg_mean64_kernel", "ssc_select", "frag_states_kernel",
                     "ssc_gather_kernel"],
