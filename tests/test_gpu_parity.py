@@ -503,3 +503,24 @@ def test_grm_backward(name):
     announce("  errors %s" % errs)
     for k, e in errs.items():
         assert e <= tol, (k, e)
+
+
+def test_grm_backward_bf16_reads_only_bf16_states():
+    """The bf16 backward takes the cached states from their bf16 copy alone: M = NULL is a valid
+    call (the header's contract for bf16), and its gradients match the oracle."""
+    w = BWD_CASES["bf16_d128_C256_L700"]
+    announce("grm backward bf16 with M = NULL")
+    inp = make_prefill(w, seed=8)
+    B, H = inp["Q"].shape[:2]
+    dY = make_upstream_grad(B, H, w.L, w.d_v, seed=9, dtype=w.dtype)
+    d = _dims(w)
+    dev = {k: to_dev(v, w.dtype) for k, v in inp.items()}
+    fwd = mc.prefill_grm(d, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"], online=False)
+    got = mc.grm_backward(d, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"], None,
+                          fwd["M_lo"], fwd["P"], to_dev(dY, w.dtype))
+    torch.cuda.synchronize()
+    ref = oracle.grm_backward(inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], dY,
+                              seg_len=w.seg_len, phi=w.phi)
+    for k in ("dQ", "dK", "dV", "dU", "dX"):
+        e = slice_rel_err(to_np(got[k]), ref[k])
+        assert e <= TOL[w.dtype], (k, e)
