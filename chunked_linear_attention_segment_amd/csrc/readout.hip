@@ -552,7 +552,16 @@ __global__ void seg_mean64_kernel(const T* __restrict__ X, int L, int C, int NS,
     const int len = s < NS ? min(C, L - t0) : 0;
     for (int e = threadIdx.x; e < DG; e += blockDim.x) {
         double acc = 0.0;
-        for (int j = 0; j < len; ++j) acc = __dadd_rn(acc, (double)ld(X, (bx * L + t0 + j) * DG + e));
+        // sixteen rows' loads in flight, then their sums in token order
+        for (int j0 = 0; j0 < len; j0 += 16) {
+            double v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = (double)ld(X, (bx * L + t0 + min(j0 + u, len - 1)) * DG + e);
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (j0 + u < len) acc = __dadd_rn(acc, v[u]);
+        }
         P64T[(bx * DG + e) * NSP + s] = len > 0 ? __ddiv_rn(acc, (double)len) : 0.0;
     }
 }
