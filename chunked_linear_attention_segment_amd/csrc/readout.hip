@@ -144,9 +144,11 @@ __global__ __launch_bounds__(256) void xps_kernel(const T* __restrict__ X, int L
     if (e >= DG) return;  // no barriers below
     const int c0 = c * XCH, c1 = min(L, c0 + XCH);
     const T* Xb = X + bx * (size_t)L * DG;
+    // every row's load issued before the first sum (rows past the end read the last row and
+    // are not summed): a load under a branch would be waited for row by row
     float v[XCH];
 #pragma unroll
-    for (int r = 0; r < XCH; ++r) v[r] = c0 + r < c1 ? ld<T>(Xb, (size_t)(c0 + r) * DG + e) : 0.f;
+    for (int r = 0; r < XCH; ++r) v[r] = ld<T>(Xb, (size_t)min(c0 + r, c1 - 1) * DG + e);
     float run = 0.f;
     int si = seg_of(sg, c0, C);           // segment of the chunk's first row
     const int ss = seg_first(sg, si, C);  // and its start
@@ -157,13 +159,25 @@ __global__ __launch_bounds__(256) void xps_kernel(const T* __restrict__ X, int L
         const int nsc = (nch + XSC - 1) / XSC;
         const int cs = ss / XCH;
         const int A = min(c, (cs + XSC - 1) / XSC * XSC), B = max(A, c / XSC * XSC);
-        for (int cc = cs; cc < A; ++cc) run += tails[(bx * nch + cc) * DG + e];
-#pragma unroll 8
-        for (int g = A / XSC; g < B / XSC; ++g) run += stails[(bx * nsc + g) * DG + e];
-        for (int cc = B; cc < c; ++cc) run += tails[(bx * nch + cc) * DG + e];
+        // rows lo .. hi-1 of a [row][DG] table added in order, eight loads in flight at a time
+        auto add_rows = [&](const float* tab, int lo, int hi) {
+            for (int i0 = lo; i0 < hi; i0 += 8) {
+                float t[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) t[u] = tab[(size_t)min(i0 + u, hi - 1) * DG + e];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (i0 + u < hi) run += t[u];
+            }
+        };
+        add_rows(tails + bx * nch * DG, cs, A);
+        add_rows(stails + bx * nsc * DG, A / XSC, B / XSC);
+        add_rows(tails + bx * nch * DG, B, c);
     }
     int nb = seg_first(sg, si + 1, C);  // the next segment start
     float* out = xps + (bx * L + c0) * DG + e;
+    // the running sums first (in place of the rows), the stores after: stores among the sums
+    // would make every row's load be waited for with all stores before it
 #pragma unroll
     for (int r = 0; r < XCH; ++r) {
         const int t = c0 + r;
@@ -174,8 +188,13 @@ __global__ __launch_bounds__(256) void xps_kernel(const T* __restrict__ X, int L
                 nb = seg_first(sg, si + 1, C);
             }
             run += v[r];
-            if (!TAIL) out[(size_t)r * DG] = run;
+            v[r] = run;
         }
+    }
+    if (!TAIL) {
+#pragma unroll
+        for (int r = 0; r < XCH; ++r)
+            if (c0 + r < c1) out[(size_t)r * DG] = v[r];
     }
     if (TAIL) tails[(bx * nch + c) * DG + e] = run;
 }
