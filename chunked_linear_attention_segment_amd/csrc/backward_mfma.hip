@@ -372,25 +372,41 @@ __global__ __launch_bounds__(512, 1) void bwd_online_mfma_kernel(
     stage(0, T0 * OT);
     if (T0 + 1 < NT) load((T0 + 1) * OT);
     // the dM term over all four 32-row blocks of c (dV) or j (dK)
+    // (the side is chosen outside the loops, so each block's fragment loads are all issued
+    // before its MFMAs: loads under a per-fragment branch were waited for one by one)
     {
         const size_t st = (bh * NS + s) * (size_t)(128 * 128);
+        if (!kside) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int m = b * 32 + l32;
+            for (int b = 0; b < 4; ++b) {
+                const bf16_t* row = dMc + st + (b * 32 + l32) * 128 + half * 8;
+                u32x4_t a[8];
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                u32x4_t a;
-                if (!kside) {
-                    a = *reinterpret_cast<const u32x4_t*>(dMc + st + m * 128 + ks * 16 + half * 8);
-                } else {
-                    const float4 f0 = *reinterpret_cast<const float4*>(dMT + st + m * 128 + ks * 16 + half * 8);
-                    const float4 f1 = *reinterpret_cast<const float4*>(dMT + st + m * 128 + ks * 16 + half * 8 + 4);
-                    a[0] = pack_bf16x2(f0.x, f0.y);
-                    a[1] = pack_bf16x2(f0.z, f0.w);
-                    a[2] = pack_bf16x2(f1.x, f1.y);
-                    a[3] = pack_bf16x2(f1.z, f1.w);
+                for (int ks = 0; ks < 8; ++ks) a[ks] = *reinterpret_cast<const u32x4_t*>(row + ks * 16);
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks) acc[b] = mfma32(a[ks], kv[ks], acc[b]);
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float* row = dMT + st + (b * 32 + l32) * 128 + half * 8;
+#pragma unroll
+                for (int k4 = 0; k4 < 8; k4 += 4) {  // four k-steps' loads at a time
+                    float4 f[4][2];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        f[ks][0] = *reinterpret_cast<const float4*>(row + (k4 + ks) * 16);
+                        f[ks][1] = *reinterpret_cast<const float4*>(row + (k4 + ks) * 16 + 4);
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const u32x4_t a = {pack_bf16x2(f[ks][0].x, f[ks][0].y),
+                                           pack_bf16x2(f[ks][0].z, f[ks][0].w),
+                                           pack_bf16x2(f[ks][1].x, f[ks][1].y),
+                                           pack_bf16x2(f[ks][1].z, f[ks][1].w)};
+                        acc[b] = mfma32(a, kv[k4 + ks], acc[b]);
+                    }
                 }
-                acc[b] = mfma32(a, kv[ks], acc[b]);
             }
         }
     }
@@ -539,16 +555,28 @@ __global__ __launch_bounds__(512) void bwd_gate_mfma_kernel(
     const float il = inv_l[bh * L + tc];
     const float dgs = dgs_i[bh * L + tc];  // dgamma of the online segment
     // pass 1: sum_i W_i dgamma_i over this half's segments, then both halves
+    // the eight (numerator, dgamma) pairs of a k-step are loaded together: the opaque uses
+    // keep the compiler from sinking each load under its i < sg test, where every load was
+    // waited for on its own
+    auto load_wg = [&](int ks, float (&w)[8], float (&g)[8]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int ic = min(16 * ks + 8 * half + j, NS - 1);
+            w[j] = bf16_to_f32((bf16_t)wt[(size_t)ic * GTOK + tl]);
+            g[j] = dgt[(size_t)ic * L + tc];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(w[j]), "+v"(g[j]));
+    };
     float dp = 0.f;
 #pragma unroll 2
     for (int ks = 0; ks < nks; ++ks) {
+        float w[8], g[8];
+        load_wg(ks, w, g);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int i = 16 * ks + 8 * half + j;
-            const int ic = min(i, NS - 1);
-            const float w = bf16_to_f32((bf16_t)wt[(size_t)ic * GTOK + tl]);
-            const float g = dgt[(size_t)ic * L + tc];
-            dp += i < sg ? w * g : 0.f;
+            dp += i < sg ? w[j] * g[j] : 0.f;
         }
     }
     dp += __shfl_xor(dp, 32);
@@ -571,14 +599,12 @@ __global__ __launch_bounds__(512) void bwd_gate_mfma_kernel(
     const int neb = (DG + 31) / 32;
     const u32x4_t* pb = ptf + (bx * NSK) * 4 * 64 * 2;
     for (int ks = 0; ks < nks; ++ks) {
-        float da[8];
+        float da[8], w[8], g[8];
+        load_wg(ks, w, g);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int i = 16 * ks + 8 * half + j;
-            const int ic = min(i, NS - 1);
-            const float w = bf16_to_f32((bf16_t)wt[(size_t)ic * GTOK + tl]);
-            const float g = dgt[(size_t)ic * L + tc];
-            da[j] = i < sg ? w * il * (g - Dt) : 0.f;
+            da[j] = i < sg ? w[j] * il * (g[j] - Dt) : 0.f;
         }
         u32x4_t bhi[4], blo[4];
 #pragma unroll

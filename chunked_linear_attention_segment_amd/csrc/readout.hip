@@ -208,12 +208,13 @@ __global__ __launch_bounds__(256) void xps_group_kernel(const float* __restrict_
     const size_t bx = blockIdx.y;
     const int e = threadIdx.x;
     if (e >= DG) return;
+    float t[XSC];  // every load issued before the first sum
+#pragma unroll
+    for (int i = 0; i < XSC; ++i) t[i] = tails[(bx * nch + min(g * XSC + i, nch - 1)) * DG + e];
     float a = 0.f;
 #pragma unroll
-    for (int i = 0; i < XSC; ++i) {
-        const int c = g * XSC + i;
-        if (c < nch) a += tails[(bx * nch + c) * DG + e];
-    }
+    for (int i = 0; i < XSC; ++i)
+        if (g * XSC + i < nch) a += t[i];
     stails[(bx * nsc + g) * DG + e] = a;
 }
 
