@@ -277,8 +277,15 @@ __global__ __launch_bounds__(256) void piece_means_kernel(const float* __restric
     const float inv_len = 1.f / (float)(pa.sg.off[jend] - pa.sg.off[j]);
     for (int e = threadIdx.x; e < DG; e += 256) {
         float acc = 0.f;
-        for (int q = j; q < jend; ++q)
-            acc += Pm[(bx * NP + q) * DG + e] * (float)(pa.sg.off[q + 1] - pa.sg.off[q]);
+        for (int q0 = j; q0 < jend; q0 += 8) {  // eight pieces' loads in flight, summed in order
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = Pm[(bx * NP + min(q0 + u, jend - 1)) * DG + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (q0 + u < jend)
+                    acc += v[u] * (float)(pa.sg.off[q0 + u + 1] - pa.sg.off[q0 + u]);
+        }
         P[(bx * NS + seg) * DG + e] = acc * inv_len;
     }
 }
