@@ -42,12 +42,24 @@ __global__ __launch_bounds__(256) void aon_kernel(const T* __restrict__ X,
         for (int j0 = 0; j0 < len; j0 += 64) {
             const int n = min(64, len - j0);
             __syncthreads();
-            for (int e8 = tid; e8 < n * (DG / 8); e8 += 256) {
-                const int r = e8 / (DG / 8), e = (e8 % (DG / 8)) * 8;
-                float v[8];
-                ld8(Xb, (size_t)(t0 + j0 + r) * DG + e, v);
+            // four rows' loads in flight per thread (clamped to the chunk), then their stores
+            const int nitem = n * (DG / 8);
+            for (int b0 = 0; b0 < nitem; b0 += 4 * 256) {
+                float v[4][8];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) xs[r][e + k] = v[k];
+                for (int u = 0; u < 4; ++u) {
+                    const int e8 = min(b0 + u * 256 + tid, nitem - 1);
+                    ld8(Xb, (size_t)(t0 + j0 + e8 / (DG / 8)) * DG + (e8 % (DG / 8)) * 8, v[u]);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int e8 = b0 + u * 256 + tid;
+                    if (e8 < nitem) {
+                        const int r = e8 / (DG / 8), e = (e8 % (DG / 8)) * 8;
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) xs[r][e + k] = v[u][k];
+                    }
+                }
             }
             __syncthreads();
             for (int e = tid; e < DG; e += 256) {
@@ -65,14 +77,12 @@ __global__ __launch_bounds__(256) void aon_kernel(const T* __restrict__ X,
             for (int k0 = 0; k0 < NIT; k0 += NB) {
             float uv[NB][8];
 #pragma unroll
-            for (int kq = 0; kq < NB; ++kq) {
+            for (int kq = 0; kq < NB; ++kq) {  // loads clamped to valid rows, used only if ok
                 const int k = k0 + kq;
                 const int item = slot + 16 * k;
-                const int hh = (xh == 1) ? item / 64 : pass, tt = item % 64;
-                const bool ok = item < nhp * 64 && tt < n && q * 8 < DG;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) uv[kq][e] = 0.f;
-                if (ok) ld8(U + (((size_t)b * H + h0 + hh) * L + t0 + j0 + tt) * DG, (size_t)q * 8, uv[kq]);
+                const int hh = min((xh == 1) ? item / 64 : pass, nh - 1), tt = min(item % 64, n - 1);
+                ld8(U + (((size_t)b * H + h0 + hh) * L + t0 + j0 + tt) * DG,
+                    (size_t)min(q * 8, DG - 8), uv[kq]);
             }
 #pragma unroll
             for (int kq = 0; kq < NB; ++kq) {
