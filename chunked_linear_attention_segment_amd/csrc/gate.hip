@@ -307,8 +307,11 @@ int launch_gate_w(const mc_dims& d, const void* U, const float* xps, const float
     hipLaunchKernelGGL(pfrag_kernel, dim3((nf + 255) / 256, d.B * d.x_heads), dim3(256), 0,
                        (hipStream_t)stream, P, NS, d.d_g, (uint4*)pfrag);
     // heads sharing one X (x_heads = 1) are taken G at a time, so a workgroup loads the prefix
-    // sums of X once for G heads
-    const int G = d.x_heads == 1 ? (d.H % 8 == 0 ? 8 : (d.H % 4 == 0 ? 4 : (d.H % 2 == 0 ? 2 : 1))) : 1;
+    // sums of X once for G heads -- fewer heads per workgroup when that leaves too few
+    // workgroups to keep every CU's memory requests in flight (a workgroup walks its heads in
+    // turn)
+    int G = d.x_heads == 1 ? (d.H % 8 == 0 ? 8 : (d.H % 4 == 0 ? 4 : (d.H % 2 == 0 ? 2 : 1))) : 1;
+    while (G > 1 && (size_t)T * 2 * (d.B * d.H / G) < 1024) G /= 2;
     if (idx)
         hipLaunchKernelGGL(gate_w_kernel<true>, dim3(T * 2, d.B * d.H / G), dim3(256), 0,
                            (hipStream_t)stream, (const bf16_t*)U, xps, (const uint4*)pfrag, d.H,
