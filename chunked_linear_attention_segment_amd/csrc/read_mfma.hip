@@ -517,6 +517,23 @@ __device__ __forceinline__ void grm_read_tile(
                 stage_k(kc + 1);
                 load_v(kc + 1);
             }
+            if constexpr (PHI != 0) {
+                // phi(k) in place over the chunk's key tile, once per element (the fragments
+                // are read once per token block); the barrier waits on LDS only, so the next
+                // chunk's loads stay in flight
+                bf16_t* kw = sm.a.kv.k[kc & 1];
+#pragma unroll
+                for (int mm = 0; mm < 64 * DK / 8 / RTHREADS; ++mm) {
+                    ru32x4_t* pk = reinterpret_cast<ru32x4_t*>(kw + (mm * RTHREADS + tid) * 8);
+                    ru32x4_t v = *pk;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = pack_bf16x2(feature(__uint_as_float(v[e] << 16), 1),
+                                           feature(__uint_as_float(v[e] & 0xffff0000u), 1));
+                    *pk = v;
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            }
             const bf16_t* kt = sm.a.kv.k[kc & 1];
             const bf16_t* vt = sm.a.kv.vt[kc & 1];
 #pragma unroll
@@ -525,16 +542,9 @@ __device__ __forceinline__ void grm_read_tile(
                 if (k0 > tlast[tb] || k0 + 63 < tseg0[tb]) continue;
                 const bool full = (k0 + 63 <= tfirst[tb]) && (k0 >= (tlast[tb] / C) * C);
                 // scores S^T = phi(K) phi(Q)^T; K fragments read two k-steps ahead
-                auto kfrag = [&](int ks, int rb) {
-                    ru32x4_t ka = *reinterpret_cast<const ru32x4_t*>(
+                auto kfrag = [&](int ks, int rb) {  // (the key tile holds phi(k))
+                    return *reinterpret_cast<const ru32x4_t*>(
                         &kt[(rb * 32 + l32) * DK + (((2 * ks + hi32) ^ swz) * 8)]);
-                    if (PHI) {  // the key tile holds raw k
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            ka[e] = pack_bf16x2(feature(__uint_as_float(ka[e] << 16), 1),
-                                                feature(__uint_as_float(ka[e] & 0xffff0000u), 1));
-                    }
-                    return ka;
                 };
                 rf32x16_t sc[2];
 #pragma unroll
