@@ -488,7 +488,31 @@ def run_ssc(args, rec, dev):
                                "algorithmic_flops": fl, "algorithmic_bytes": by,
                                "traffic_readout": load_traffic("ssc_readout", w.name),
                                "traffic_source": TRAFFIC_SOURCE}}
-    del inp, M, M_lo, P, O_on, Y, idx, ws
+    # the same shape over random segment boundaries, as many segments as the constant length
+    # gives: mc_scan_prefill_segs + mc_ssc_readout_segs (the routed read with the offsets)
+    NS = -(-L // C)
+    cuts = np.sort(np.random.default_rng(21).choice(np.arange(1, L), NS - 1, replace=False))
+    off = [0] + cuts.tolist() + [L]
+    ds = mc.make_dims(B, H, L, dk, dv, dg, 1, 1, w.dtype, w.phi)
+    wss = mc.workspace_segs(ds, NS, device=dev)
+    wsr = mc.workspace(ds, mc.MC_OP_SSC_SEGS, top_k=k, n_cap=NS, device=dev)
+
+    def scan_segs():
+        mc.mc_scan_prefill_segs(ds, off, inp["Q"], inp["K"], inp["V"], inp["X"], M, M_lo, P,
+                                O_on, ws=wss, stream=stream)
+
+    def read_segs():
+        mc.mc_ssc_readout_segs(ds, off, k, inp["Q"], inp["U"], inp["X"], M, M_lo, P, O_on, Y,
+                               idx, ws=wsr, stream=stream)
+    (scan_s, read_s), ms_s = timed_calls([scan_segs, read_segs], args.steps, args.warmup, stream)
+    rec["ssc_offsets"] = {"workload": "%s shape, %d random segment boundaries" % (w.name, NS),
+                          "metric": "SSC prefill tokens/s",
+                          "value": round(B * L / (ms_s / 1e3), 1), "unit": "tokens/s",
+                          "ms_per_step": round(ms_s, 4), "top_k": k,
+                          "steps_timed": "mc_scan_prefill_segs + mc_ssc_readout_segs",
+                          "kernels_ms": {"mc_scan_prefill_segs": round(med(scan_s), 4),
+                                         "mc_ssc_readout_segs": round(med(read_s), 4)}}
+    del inp, M, M_lo, P, O_on, Y, idx, ws, wss, wsr
     torch.cuda.empty_cache()
 
 

@@ -8,7 +8,8 @@ Entry points (same names and arguments as include/mc.h; tensors are torch tensor
 GPU, host scalars are Python ints or one-element int32 numpy arrays):
     mc_abi_version, mc_status_str, mc_workspace_bytes,
     mc_scan_prefill, mc_grm_readout, mc_ssc_readout, mc_decode_step,
-    mc_scan_prefill_segs, mc_grm_readout_segs
+    mc_scan_prefill_segs, mc_grm_readout_segs, mc_ssc_readout_segs, mc_scan_prefill_swla,
+    mc_grm_backward, mc_decode_step_noalloc
 plus helpers that allocate outputs / workspaces with torch (memory plumbing only).
 """
 from __future__ import annotations
@@ -28,12 +29,12 @@ MC_NOALLOC_SCRATCH_BYTES = 64 << 20
 MC_F32, MC_BF16 = 0, 1
 MC_PHI_IDENTITY, MC_PHI_ELU1 = 0, 1
 MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE, MC_OP_GRM_BACKWARD, MC_OP_SCAN_SEGS, \
-    MC_OP_GRM_SEGS = 0, 1, 2, 3, 4, 5, 6
+    MC_OP_GRM_SEGS, MC_OP_SSC_SEGS = 0, 1, 2, 3, 4, 5, 6, 7
 
 EXPORTED = ["mc_abi_version", "mc_status_str", "mc_workspace_bytes", "mc_scan_prefill",
             "mc_grm_readout", "mc_ssc_readout", "mc_decode_step", "mc_scan_prefill_segs",
-            "mc_grm_readout_segs", "mc_scan_prefill_swla", "mc_grm_backward",
-            "mc_decode_step_noalloc"]
+            "mc_grm_readout_segs", "mc_ssc_readout_segs", "mc_scan_prefill_swla",
+            "mc_grm_backward", "mc_decode_step_noalloc"]
 MC_MAX_SEGS = 512
 
 
@@ -79,6 +80,9 @@ def load(path: str = LIB_PATH):
         lib.mc_grm_readout_segs.restype = ctypes.c_int
         lib.mc_grm_readout_segs.argtypes = [D, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
                                             ctypes.c_size_t, P]
+        lib.mc_ssc_readout_segs.restype = ctypes.c_int
+        lib.mc_ssc_readout_segs.argtypes = [D, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P,
+                                            P, P, P, P, P, ctypes.c_size_t, P]
         lib.mc_scan_prefill_swla.restype = ctypes.c_int
         lib.mc_scan_prefill_swla.argtypes = [D, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
                                              P, P]
@@ -198,6 +202,18 @@ def mc_grm_readout_segs(dims, seg_off, Q, U, X, M, M_lo, P, O_on, Y, gamma=None,
                                       _p(X), _p(M), _p(M_lo), _p(P), _p(O_on), _p(Y),
                                       _p(gamma), w, wb, _stream(stream)),
            "mc_grm_readout_segs")
+
+
+def mc_ssc_readout_segs(dims, seg_off, top_k, Q, U, X, M, M_lo, P, O_on, Y, idx, ws=None,
+                        stream=None):
+    """SSC read over the segments [seg_off[i], seg_off[i+1]); O_on from mc_scan_prefill_segs;
+    ws: mc_workspace_bytes(dims, MC_OP_SSC_SEGS, top_k, n) bytes."""
+    off, n = _offsets(seg_off)
+    w, wb = _ws(ws)
+    _check(load().mc_ssc_readout_segs(ctypes.byref(dims), off.ctypes.data, n, int(top_k),
+                                      _p(Q), _p(U), _p(X), _p(M), _p(M_lo), _p(P), _p(O_on),
+                                      _p(Y), _p(idx), w, wb, _stream(stream)),
+           "mc_ssc_readout_segs")
 
 
 def mc_scan_prefill_swla(dims, seg_off, alpha, beta, lam, Q, K, V, X, M, M_lo, P, O_on,
@@ -358,6 +374,26 @@ def prefill_grm_swla(dims, alpha, beta, lam, Q, K, V, U, X, seg_off=None, want_g
     if want_gamma:
         out["gamma"] = G
     return out
+
+
+def prefill_ssc_segs(dims, seg_off, top_k, Q, K, V, U, X, stream=None):
+    """scan + SSC read over the segments [seg_off[i], seg_off[i+1]) with fresh outputs."""
+    import torch
+    NS = len(seg_off) - 1
+    dev = Q.device
+    M = torch.empty((dims.B, dims.H, NS, dims.d_v, dims.d_k), dtype=torch.float32, device=dev)
+    M_lo = torch.empty((dims.B, dims.H, NS, dims.d_v, dims.d_k), dtype=torch.bfloat16,
+                       device=dev)
+    P = torch.empty((dims.B, dims.x_heads, NS, dims.d_g), dtype=torch.float32, device=dev)
+    O_on = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch.float32, device=dev)
+    mc_scan_prefill_segs(dims, seg_off, Q, K, V, X, M, M_lo, P, O_on,
+                         ws=workspace_segs(dims, NS, device=dev), stream=stream)
+    Y = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch_dtype(dims), device=dev)
+    idx = torch.empty((dims.B, dims.H, dims.L, top_k), dtype=torch.int32, device=dev)
+    ws = workspace(dims, MC_OP_SSC_SEGS, top_k=top_k, n_cap=NS, device=dev)
+    mc_ssc_readout_segs(dims, seg_off, top_k, Q, U, X, M, M_lo, P, O_on, Y, idx, ws=ws,
+                        stream=stream)
+    return {"Y": Y, "idx": idx, "M": M, "M_lo": M_lo, "P": P, "O_on": O_on}
 
 
 def prefill_ssc(dims, top_k, Q, K, V, U, X, online=True, stream=None):

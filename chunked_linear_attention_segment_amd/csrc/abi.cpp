@@ -49,10 +49,25 @@ GrmWorkspace grm_workspace(const mc_dims& d, int n_seg) {
     return w;
 }
 
-SscWorkspace ssc_workspace(const mc_dims& d, int top_k) {
+SscWorkspace ssc_workspace(const mc_dims& d, int top_k, int n_seg) {
     SscWorkspace w{};
     const size_t bhl = (size_t)d.B * d.H * d.L;
     w.aon = align256(sizeof(float) * bhl);
+    if (n_seg > 0) {
+        // offsets: the caller's online read; the online logits, the means, and the routed
+        // read's tables where it applies (else the generic read needs nothing more)
+        w.xsum64 = align256(ssc_means_bytes(d, n_seg));
+        if (ssc_gather_covers(d, top_k, n_seg)) {
+            const size_t tiles = (size_t)d.B * d.H * ((d.L + kSscTile - 1) / kSscTile);
+            w.won = align256(sizeof(float) * bhl);
+            w.ptok = align256(sizeof(int32_t) * tiles * kSscTile * top_k);
+            w.pw = align256(sizeof(float) * tiles * kSscTile * top_k);
+            w.poff = align256(sizeof(int32_t) * tiles * (n_seg + 1));
+            w.sf = align256(ssc_frag_states_bytes(d, n_seg));
+        }
+        w.total = w.aon + w.xsum64 + w.won + w.ptok + w.pw + w.poff + w.sf;
+        return w;
+    }
     w.on = online_ws(d);
     w.xps = xps_ws(d);
     w.xsum64 = align256(ssc_means_bytes(d));
@@ -180,6 +195,10 @@ size_t mc_workspace_bytes(const mc_dims* d, mc_op op, int32_t top_k, int32_t n_c
         case MC_OP_GRM_SEGS:
             return top_k >= 1 && top_k <= MC_MAX_SEGS ? grm_workspace(*d, top_k).total : 0;
         case MC_OP_SSC: return top_k >= 1 ? ssc_workspace(*d, top_k).total : 0;
+        case MC_OP_SSC_SEGS:
+            return top_k >= 1 && top_k <= 16 && n_cap >= 1 && n_cap <= MC_MAX_SEGS
+                       ? ssc_workspace(*d, top_k, n_cap).total
+                       : 0;
         case MC_OP_GRM_BACKWARD: return bwd_workspace(*d).total;
         case MC_OP_SCAN_SEGS:
             return top_k >= 1 && top_k <= MC_MAX_SEGS ? segs_scan_ws_bytes(*d, top_k) : 0;
@@ -383,6 +402,48 @@ mc_status mc_grm_readout_segs(const mc_dims* d, const int32_t* seg_off, int32_t 
     }
     return launch_grm_readout_segs(*d, sg, Q, U, X, M, M_lo, P, O_on, (float*)ws, xps, xtail, Y,
                                    gamma, stream, gate)
+               ? MC_ERR_HIP
+               : MC_OK;
+}
+
+mc_status mc_ssc_readout_segs(const mc_dims* d, const int32_t* seg_off, int32_t n_seg,
+                              int32_t top_k, const void* Q, const void* U, const void* X,
+                              const float* M, const uint16_t* M_lo, const float* P,
+                              const float* O_on, void* Y, int32_t* idx, void* ws,
+                              size_t ws_bytes, void* stream) {
+    mc_status st = check_dims(d, true);
+    if (st != MC_OK) return st;
+    SegArg sg;
+    if ((st = check_segs(d, seg_off, n_seg, &sg)) != MC_OK) return st;
+    if (top_k < 1) return MC_ERR_DIMS;
+    if (top_k > 16) return MC_ERR_UNSUPPORTED;
+    if (!Q || !U || !X || !P || !O_on || !Y || !idx) return MC_ERR_NULL;
+    if (d->dtype == MC_BF16 ? !M_lo : !M) return MC_ERR_NULL;
+    const SscWorkspace w = ssc_workspace(*d, top_k, n_seg);
+    if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
+    const void* ptrs[] = {Q, U, X, M, M_lo, P, O_on, Y, idx, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MC_ERR_ALIGN;
+    float* aon = (float*)ws;
+    double* xsum64 = (double*)((char*)ws + w.aon);
+    if (launch_aon_segs(*d, sg, X, U, aon, stream)) return MC_ERR_HIP;
+    if (ssc_gather_covers(*d, top_k, n_seg)) {
+        // routed: the selection with its weights and the tiles' pairs sorted by segment, then
+        // only the selected states are read
+        char* g = (char*)ws + w.aon + w.xsum64;
+        SscRoute rt;
+        rt.aon = aon;
+        rt.won = (float*)g;
+        rt.ptok = (int32_t*)(g + w.won);
+        rt.pw = (float*)(g + w.won + w.ptok);
+        rt.poff = (int32_t*)(g + w.won + w.ptok + w.pw);
+        rt.Sf = g + w.won + w.ptok + w.pw + w.poff;
+        if (launch_ssc_select(*d, top_k, U, X, xsum64, idx, stream, &rt, &sg)) return MC_ERR_HIP;
+        if (launch_ssc_gather(*d, top_k, Q, M_lo, O_on, rt, Y, stream, &sg)) return MC_ERR_HIP;
+        return MC_OK;
+    }
+    if (launch_ssc_select(*d, top_k, U, X, xsum64, idx, stream, nullptr, &sg)) return MC_ERR_HIP;
+    return launch_ssc_readout_segs(*d, sg, top_k, Q, U, aon, M, M_lo, P, O_on, idx, Y, stream)
                ? MC_ERR_HIP
                : MC_OK;
 }

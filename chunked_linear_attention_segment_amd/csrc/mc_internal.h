@@ -62,7 +62,9 @@ struct DecodeWorkspace {
 // n_seg > 0: sized for that many segment offsets (the gate pass's buffers included when they
 // fit), else for the constant segment length
 GrmWorkspace grm_workspace(const mc_dims& d, int n_seg = 0);
-SscWorkspace ssc_workspace(const mc_dims& d, int top_k);
+// n_seg > 0: for that many segment offsets (the online read is the caller's, the read is the
+// routed one or the generic kernels)
+SscWorkspace ssc_workspace(const mc_dims& d, int top_k, int n_seg = 0);
 DecodeWorkspace decode_workspace(const mc_dims& d, int n_cap, int n_cached);
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -211,16 +213,25 @@ struct SscRoute {
     int32_t* poff;     // [B*H, T, NS + 1]
     void* Sf;          // the states in MFMA fragment order (ssc_frag_states_bytes)
 };
-size_t ssc_frag_states_bytes(const mc_dims& d);
+// n_seg (or sg->n) = 0 below: segments of the constant length
+size_t ssc_frag_states_bytes(const mc_dims& d, int n_seg = 0);
 int launch_ssc_select(const mc_dims& d, int top_k, const void* U, const void* X,
                       double* xsum64, int32_t* idx, void* stream,
-                      const SscRoute* route = nullptr);
-size_t ssc_means_bytes(const mc_dims& d);
+                      const SscRoute* route = nullptr, const SegArg* sg = nullptr);
+size_t ssc_means_bytes(const mc_dims& d, int n_seg = 0);
 // the routed SSC read: per tile, only the selected segments' states, each applied to the
 // tokens that chose it; y = won * O_on + sum of pw * S^T phi(q) (bf16, d_k = d_v = 128)
-bool ssc_gather_covers(const mc_dims& d, int top_k);
+bool ssc_gather_covers(const mc_dims& d, int top_k, int n_seg = 0);
 int launch_ssc_gather(const mc_dims& d, int top_k, const void* Q, const uint16_t* M_lo,
-                      const float* O_on, const SscRoute& rt, void* Y, void* stream);
+                      const float* O_on, const SscRoute& rt, void* Y, void* stream,
+                      const SegArg* sg = nullptr);
+// segment offsets: the online logits, and the generic read restricted to idx
+int launch_aon_segs(const mc_dims& d, const SegArg& sg, const void* X, const void* U,
+                    float* a_on, void* stream);
+int launch_ssc_readout_segs(const mc_dims& d, const SegArg& sg, int top_k, const void* Q,
+                            const void* U, const float* aon, const float* M,
+                            const uint16_t* M_lo, const float* P, const float* O_on,
+                            const int32_t* idx, void* Y, void* stream);
 
 int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K,
                        const void* V, const void* U, const float* aon, const float* xps,

@@ -422,16 +422,16 @@ template <bool SSC>
 static int launch_readout(const mc_dims& d, int top_k, const void* Q, const void* U,
                           const float* aon, const float* M, const uint16_t* M_lo,
                           const float* P, const float* O_on, const int32_t* idx, void* Y,
-                          float* gamma, hipStream_t st) {
+                          float* gamma, hipStream_t st, const SegArg& sg = kConstSegR) {
 #define MC_RD(DK, DV)                                                                      \
     if (d.d_k == DK && d.d_v == DV)                                                        \
         return d.dtype == MC_BF16                                                          \
                    ? launch_readout_t<bf16_t, bf16_t, DK, DV, SSC>(d, top_k, Q, U, aon,   \
                                                                    M_lo, P, O_on, idx, Y,  \
-                                                                   gamma, st)              \
+                                                                   gamma, st, sg)          \
                    : launch_readout_t<float, float, DK, DV, SSC>(d, top_k, Q, U, aon, M,  \
                                                                  P, O_on, idx, Y, gamma,   \
-                                                                 st);
+                                                                 st, sg);
     MC_RD(128, 128)
     MC_RD(128, 64)
     MC_RD(64, 128)
@@ -552,6 +552,21 @@ int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const voi
     return (int)hipGetLastError();
 }
 
+// Arbitrary boundaries without the routed read: the generic read restricted to the selections
+// of idx, with the online term O_on of mc_scan_prefill_segs and the online logits aon.
+int launch_ssc_readout_segs(const mc_dims& d, const SegArg& sg, int top_k, const void* Q,
+                            const void* U, const float* aon, const float* M,
+                            const uint16_t* M_lo, const float* P, const float* O_on,
+                            const int32_t* idx, void* Y, void* stream) {
+    return launch_readout<true>(d, top_k, Q, U, aon, M, M_lo, P, O_on, idx, Y, nullptr,
+                                (hipStream_t)stream, sg);
+}
+
+int launch_aon_segs(const mc_dims& d, const SegArg& sg, const void* X, const void* U,
+                    float* a_on, void* stream) {
+    return launch_aon_sg(d, X, U, a_on, sg, (hipStream_t)stream);
+}
+
 int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K,
                        const void* V, const void* U, const float* aon, const float* xps,
                        const float* M,
@@ -575,11 +590,11 @@ int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K
 // are contiguous.
 template <typename T>
 __global__ void seg_mean64_kernel(const T* __restrict__ X, int L, int C, int NS, int NSP, int DG,
-                                  double* __restrict__ P64T) {
+                                  double* __restrict__ P64T, const SegArg sg) {
     const int s = blockIdx.x;
     const size_t bx = blockIdx.y;
-    const int t0 = s * C;
-    const int len = s < NS ? min(C, L - t0) : 0;
+    const int t0 = s < NS ? seg_first(sg, s, C) : 0;
+    const int len = s < NS ? seg_length(sg, s, C, L) : 0;
     for (int e = threadIdx.x; e < DG; e += blockDim.x) {
         double acc = 0.0;
         // sixteen rows' loads in flight, then their sums in token order
@@ -719,7 +734,8 @@ template <typename T, int KMAX, int TPL>
 __device__ __forceinline__ void ssc_select_body(const T* __restrict__ U,
                                                 const double* __restrict__ P64T, int L, int C,
                                                 int NSP, int DG, int H, int xh, int top_k,
-                                                int32_t* __restrict__ idx, const SelRoute& rt) {
+                                                int32_t* __restrict__ idx, const SelRoute& rt,
+                                                const SegArg& sg) {
     static_assert(TPL == 4 || TPL == 1, "tokens per lane");
     constexpr int NPT = 64 * TPL;     // tokens per pass
     constexpr int NP = SEL_T / NPT;   // passes
@@ -750,11 +766,11 @@ __device__ __forceinline__ void ssc_select_body(const T* __restrict__ U,
         const int pt0 = NPT * ps;  // first tile token of the pass
         const int pn = min(NPT, ntok - pt0);
         if (pn <= 0) break;
-        const int smax = (t0 + pt0 + pn - 1) / C;  // segments 0..smax-1 are candidates
+        const int smax = seg_of(sg, t0 + pt0 + pn - 1, C);  // segments 0..smax-1 are candidates
         int s_of[TPL];
 #pragma unroll
         for (int a = 0; a < TPL; ++a)
-            s_of[a] = tok_of(ps, a) < ntok ? (t0 + tok_of(ps, a)) / C : 0;
+            s_of[a] = tok_of(ps, a) < ntok ? seg_of(sg, t0 + tok_of(ps, a), C) : 0;
         double best[TPL][KMAX];
         int bi[TPL][KMAX];
 #pragma unroll
@@ -966,51 +982,53 @@ __global__ __launch_bounds__(256) void ssc_select_kernel(const T* __restrict__ U
                                                          const double* __restrict__ P64T, int L,
                                                          int C, int NSP, int DG, int H, int xh,
                                                          int top_k, int32_t* __restrict__ idx,
-                                                         const SelRoute rt) {
-    ssc_select_body<T, KMAX, 4>(U, P64T, L, C, NSP, DG, H, xh, top_k, idx, rt);
+                                                         const SelRoute rt, const SegArg sg) {
+    ssc_select_body<T, KMAX, 4>(U, P64T, L, C, NSP, DG, H, xh, top_k, idx, rt, sg);
 }
 
 // lists of up to 16 entries: one token per lane, the tile in four passes
 template <typename T>
 __global__ __launch_bounds__(256) void ssc_select_wide_kernel(
     const T* __restrict__ U, const double* __restrict__ P64T, int L, int C, int NSP, int DG,
-    int H, int xh, int top_k, int32_t* __restrict__ idx, const SelRoute rt) {
-    ssc_select_body<T, 16, 1>(U, P64T, L, C, NSP, DG, H, xh, top_k, idx, rt);
+    int H, int xh, int top_k, int32_t* __restrict__ idx, const SelRoute rt, const SegArg sg) {
+    ssc_select_body<T, 16, 1>(U, P64T, L, C, NSP, DG, H, xh, top_k, idx, rt, sg);
 }
 
 template <typename T, int KMAX>
 static void launch_select_t(const mc_dims& d, int top_k, const T* U, const double* P64T, int NSP,
-                            int32_t* idx, const SelRoute& rt, hipStream_t st) {
+                            int32_t* idx, const SelRoute& rt, const SegArg& sg, hipStream_t st) {
     dim3 g((d.L + SEL_T - 1) / SEL_T, d.B * d.H);
     if constexpr (KMAX == 16)
         hipLaunchKernelGGL((ssc_select_wide_kernel<T>), g, dim3(256), 0, st, U, P64T, d.L,
-                           d.seg_len, NSP, d.d_g, d.H, d.x_heads, top_k, idx, rt);
+                           d.seg_len, NSP, d.d_g, d.H, d.x_heads, top_k, idx, rt, sg);
     else
         hipLaunchKernelGGL((ssc_select_kernel<T, KMAX>), g, dim3(256), 0, st, U, P64T, d.L,
-                           d.seg_len, NSP, d.d_g, d.H, d.x_heads, top_k, idx, rt);
+                           d.seg_len, NSP, d.d_g, d.H, d.x_heads, top_k, idx, rt, sg);
 }
 
 template <typename T>
 static void launch_select_k(const mc_dims& d, int top_k, const T* U, const double* P64T, int NSP,
-                            int32_t* idx, const SelRoute& rt, hipStream_t st) {
+                            int32_t* idx, const SelRoute& rt, const SegArg& sg, hipStream_t st) {
     if (top_k <= 4)
-        launch_select_t<T, 4>(d, top_k, U, P64T, NSP, idx, rt, st);
+        launch_select_t<T, 4>(d, top_k, U, P64T, NSP, idx, rt, sg, st);
     else if (top_k <= 8)
-        launch_select_t<T, 8>(d, top_k, U, P64T, NSP, idx, rt, st);
+        launch_select_t<T, 8>(d, top_k, U, P64T, NSP, idx, rt, sg, st);
     else
-        launch_select_t<T, 16>(d, top_k, U, P64T, NSP, idx, rt, st);
+        launch_select_t<T, 16>(d, top_k, U, P64T, NSP, idx, rt, sg, st);
 }
 
-size_t ssc_means_bytes(const mc_dims& d) {
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+size_t ssc_means_bytes(const mc_dims& d, int n_seg) {
+    const int NS = n_seg ? n_seg : (d.L + d.seg_len - 1) / d.seg_len;
     const int NSP = (NS + SEL_W - 1) / SEL_W * SEL_W;
     return sizeof(double) * (size_t)d.B * d.x_heads * d.d_g * NSP;
 }
 
 int launch_ssc_select(const mc_dims& d, int top_k, const void* U, const void* X,
-                      double* P64T, int32_t* idx, void* stream, const SscRoute* route) {
+                      double* P64T, int32_t* idx, void* stream, const SscRoute* route,
+                      const SegArg* sgp) {
     hipStream_t st = (hipStream_t)stream;
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+    const SegArg& sg = sgp ? *sgp : kConstSegR;
+    const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
     const int NSP = (NS + SEL_W - 1) / SEL_W * SEL_W;
     SelRoute rt{};
     if (route) {
@@ -1026,12 +1044,12 @@ int launch_ssc_select(const mc_dims& d, int top_k, const void* U, const void* X,
     const int threads = d.d_g < 256 ? ((d.d_g + 63) / 64) * 64 : 256;
     if (d.dtype == MC_BF16) {
         hipLaunchKernelGGL(seg_mean64_kernel<bf16_t>, g1, dim3(threads), 0, st,
-                           (const bf16_t*)X, d.L, d.seg_len, NS, NSP, d.d_g, P64T);
-        launch_select_k<bf16_t>(d, top_k, (const bf16_t*)U, P64T, NSP, idx, rt, st);
+                           (const bf16_t*)X, d.L, d.seg_len, NS, NSP, d.d_g, P64T, sg);
+        launch_select_k<bf16_t>(d, top_k, (const bf16_t*)U, P64T, NSP, idx, rt, sg, st);
     } else {
         hipLaunchKernelGGL(seg_mean64_kernel<float>, g1, dim3(threads), 0, st, (const float*)X,
-                           d.L, d.seg_len, NS, NSP, d.d_g, P64T);
-        launch_select_k<float>(d, top_k, (const float*)U, P64T, NSP, idx, rt, st);
+                           d.L, d.seg_len, NS, NSP, d.d_g, P64T, sg);
+        launch_select_k<float>(d, top_k, (const float*)U, P64T, NSP, idx, rt, sg, st);
     }
     return (int)hipGetLastError();
 }

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ssc_gather_kernel(
     const bf16_t* __restrict__ Q, const uint4* __restrict__ Sf, const float* __restrict__ O_on,
     const float* __restrict__ won, const int32_t* __restrict__ ptok,
     const float* __restrict__ pw, const int32_t* __restrict__ poff, int BH, int L, int C, int NS,
-    int top_k, bf16_t* __restrict__ Y) {
+    int top_k, bf16_t* __restrict__ Y, const SegArg sg) {
     constexpr int NT = 64 * NW;
     __shared__ __attribute__((aligned(16))) float out[GT * OSTR];
     // B operand of a pair block: [k group of 8 (16 groups)][pair] 16 bytes each
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ssc_gather_kernel(
     const int32_t* pt = ptok + tb * GT * top_k;
     const float* pwt = pw + tb * GT * top_k;
     const size_t row0 = (size_t)bh * L + t0;
-    const int s_end = (t0 + ntok - 1) / C;  // pairs exist only for segments below this
+    const int s_end = seg_of(sg, t0 + ntok - 1, C);  // pairs exist only for segments below this
     for (int x = tid; x <= s_end; x += NT) offs[x] = poff[tb * (NS + 1) + x];
     __syncthreads();
     if (wave == 0) {  // the block table: one lane per segment, 64 segments at a time
@@ -318,35 +318,41 @@ __global__ __launch_bounds__(64 * NW, 1) void ssc_gather_kernel(
 
 }  // namespace
 
-bool ssc_gather_covers(const mc_dims& d, int top_k) {
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+static int num_segs(const mc_dims& d, int NS) { return NS ? NS : (d.L + d.seg_len - 1) / d.seg_len; }
+
+bool ssc_gather_covers(const mc_dims& d, int top_k, int n_seg) {
+    const int NS = num_segs(d, n_seg);
     return read_mfma_covers(d) && d.d_k == GD && d.d_v == GD && top_k >= 1 && top_k <= 16 &&
            NS <= GNS_MAX;
 }
 
-size_t ssc_frag_states_bytes(const mc_dims& d) {
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+size_t ssc_frag_states_bytes(const mc_dims& d, int n_seg) {
+    const int NS = num_segs(d, n_seg);
     return sizeof(uint16_t) * (size_t)d.B * d.H * NS * GD * GD;
 }
 
+static const SegArg kConstSegS{};  // constant segment length
+
 int launch_ssc_gather(const mc_dims& d, int top_k, const void* Q, const uint16_t* M_lo,
-                      const float* O_on, const SscRoute& rt, void* Y, void* stream) {
-    if (!ssc_gather_covers(d, top_k) || !rt.Sf) return (int)hipErrorInvalidValue;
-    const int NS = (d.L + d.seg_len - 1) / d.seg_len;
+                      const float* O_on, const SscRoute& rt, void* Y, void* stream,
+                      const SegArg* sgp) {
+    const SegArg& sg = sgp ? *sgp : kConstSegS;
+    const int NS = num_segs(d, sg.n);
+    if (!ssc_gather_covers(d, top_k, sg.n) || !rt.Sf) return (int)hipErrorInvalidValue;
     const int T = (d.L + GT - 1) / GT;
     const int BH = d.B * d.H;
-    const size_t n16 = ssc_frag_states_bytes(d) / 16;
+    const size_t n16 = ssc_frag_states_bytes(d, sg.n) / 16;
     hipLaunchKernelGGL(frag_states_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0,
                        (hipStream_t)stream, (const uint4*)M_lo, n16, (uint4*)rt.Sf);
     const dim3 grid(T * BH);
     if (d.phi)
         hipLaunchKernelGGL(ssc_gather_kernel<1>, grid, dim3(64 * NW), 0, (hipStream_t)stream,
                            (const bf16_t*)Q, (const uint4*)rt.Sf, O_on, rt.won, rt.ptok, rt.pw,
-                           rt.poff, BH, d.L, d.seg_len, NS, top_k, (bf16_t*)Y);
+                           rt.poff, BH, d.L, d.seg_len, NS, top_k, (bf16_t*)Y, sg);
     else
         hipLaunchKernelGGL(ssc_gather_kernel<0>, grid, dim3(64 * NW), 0, (hipStream_t)stream,
                            (const bf16_t*)Q, (const uint4*)rt.Sf, O_on, rt.won, rt.ptok, rt.pw,
-                           rt.poff, BH, d.L, d.seg_len, NS, top_k, (bf16_t*)Y);
+                           rt.poff, BH, d.L, d.seg_len, NS, top_k, (bf16_t*)Y, sg);
     return (int)hipGetLastError();
 }
 

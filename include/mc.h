@@ -82,7 +82,8 @@ typedef enum {
     MC_OP_DECODE = 3,
     MC_OP_GRM_BACKWARD = 4,
     MC_OP_SCAN_SEGS = 5,
-    MC_OP_GRM_SEGS = 6
+    MC_OP_GRM_SEGS = 6,
+    MC_OP_SSC_SEGS = 7
 } mc_op;
 
 /* Problem sizes.  Supported by this library: d_k, d_v in {64, 128}; 1 <= d_g <= 256 and
@@ -106,8 +107,9 @@ const char* mc_status_str(mc_status status);
 
 /* Workspace bytes an operation needs for these sizes (top_k is used by MC_OP_SSC, n_cap by
  * MC_OP_DECODE; MC_OP_SCAN_SEGS, the segment-offset write path, and MC_OP_GRM_SEGS, the
- * segment-offset read, take the number of segments in top_k).  Returns 0 when no workspace
- * is needed or the sizes are invalid. */
+ * segment-offset read, take the number of segments in top_k; MC_OP_SSC_SEGS, the
+ * segment-offset SSC read, takes top_k in top_k and the number of segments in n_cap).
+ * Returns 0 when no workspace is needed or the sizes are invalid. */
 size_t mc_workspace_bytes(const mc_dims* dims, mc_op op, int32_t top_k, int32_t n_cap);
 
 /*
@@ -263,6 +265,30 @@ mc_status mc_grm_readout_segs(const mc_dims* dims, const int32_t* seg_off, int32
                               const void* Q, const void* U, const void* X, const float* M,
                               const uint16_t* M_lo, const float* P, const float* O_on, void* Y,
                               float* gamma, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mc_ssc_readout_segs -- the Sparse Selective Caching read of mc_ssc_readout (explainer §3.4)
+ * over arbitrary segment boundaries (Memory Caching paper §3, Eq. 4b: segment s has its own
+ * length).  Token t of segment s selects among the segments i < s; every router score is
+ * formed in fp64 with the segment's x values summed in token order and divided by that
+ * segment's own length, then ranked as in mc_ssc_readout (ties to the lower index).
+ *
+ *   seg_off, n_seg  host offsets as for mc_scan_prefill_segs (NS = n_seg).
+ *   top_k    1 <= top_k <= 16
+ *   Q, U, X, M, M_lo, P  as for mc_grm_readout_segs with NS = n_seg.
+ *   O_on     [B,H,L,d_v] fp32, required: the online read written by mc_scan_prefill_segs
+ *            (or mc_scan_prefill_swla).
+ *   Y        out [B,H,L,d_v] dtype;  idx  out [B,H,L,top_k] int32, ascending, -1 padded
+ *   ws       mc_workspace_bytes(dims, MC_OP_SSC_SEGS, top_k, n_seg) bytes
+ *   bf16 with d_k = d_v = 128 runs the routed read (only the selected states are loaded);
+ *   the rest runs the fp32-accumulating read restricted to the selections.
+ *   Errors as mc_ssc_readout and mc_grm_readout_segs.
+ */
+mc_status mc_ssc_readout_segs(const mc_dims* dims, const int32_t* seg_off, int32_t n_seg,
+                              int32_t top_k, const void* Q, const void* U, const void* X,
+                              const float* M, const uint16_t* M_lo, const float* P,
+                              const float* O_on, void* Y, int32_t* idx, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /*
  * SWLA memory under Memory Caching (Memory Caching paper, the sliding-window linear

@@ -256,6 +256,50 @@ def test_segment_offsets_are_validated():
     assert read(good, Y=MIS) == mc.MC_ERR_ALIGN
 
 
+def test_ssc_segment_offsets_arguments():
+    # the SSC read over arbitrary boundaries: offsets validated as for the GRM read, top_k as
+    # for mc_ssc_readout, O_on required; its workspace holds the online logits, the fp64
+    # means of the n_seg segments and, for the routed read (bf16, d = 128), the tiles' pairs
+    d = dims(L=1000)
+    lib = mc.load()
+    good = [0, 512, 768, 896, 960, 992, 1000]
+    n = len(good) - 1
+    need = mc.mc_workspace_bytes(d, mc.MC_OP_SSC_SEGS, 4, n)
+    T = -(-d.L // 256)
+    assert need >= (4 * d.B * d.H * d.L + 8 * d.B * d.x_heads * d.d_g * n
+                    + 2 * 4 * d.B * d.H * T * 256 * 4 + 2 * d.B * d.H * n * d.d_v * d.d_k)
+    assert mc.mc_workspace_bytes(d, mc.MC_OP_SSC_SEGS, 4, 64) > need
+    assert mc.mc_workspace_bytes(d, mc.MC_OP_SSC_SEGS, 0, n) == 0
+    assert mc.mc_workspace_bytes(d, mc.MC_OP_SSC_SEGS, 17, n) == 0
+    assert mc.mc_workspace_bytes(d, mc.MC_OP_SSC_SEGS, 4, 0) == 0
+    assert mc.mc_workspace_bytes(d, mc.MC_OP_SSC_SEGS, 4, mc.MC_MAX_SEGS + 1) == 0
+    # fp32 runs the generic read: no routing tables
+    f = dims(L=1000, dtype="f32")
+    assert (mc.mc_workspace_bytes(f, mc.MC_OP_SSC_SEGS, 4, n)
+            < mc.mc_workspace_bytes(d, mc.MC_OP_SSC_SEGS, 4, n))
+
+    def call(off, k=4, ws_bytes=need, **kw):
+        off = np.ascontiguousarray(np.asarray(off, dtype=np.int32))
+        p = dict(Q=A, U=A, X=A, M=A, M_lo=A, P=A, O_on=A, Y=A, idx=A, ws=A)
+        p.update(kw)
+        return lib.mc_ssc_readout_segs(ctypes.byref(d), off.ctypes.data, off.shape[0] - 1, k,
+                                       p["Q"], p["U"], p["X"], p["M"], p["M_lo"], p["P"],
+                                       p["O_on"], p["Y"], p["idx"], p["ws"], ws_bytes, None)
+    for bad in ([0, 512, 512, 1000], [1, 512, 1000], [0, 512, 999], [0]):
+        assert call(bad) == mc.MC_ERR_DIMS, bad
+    assert call(list(range(1000)) + [1000]) == mc.MC_ERR_UNSUPPORTED
+    assert call(good, k=0) == mc.MC_ERR_DIMS
+    assert call(good, k=17) == mc.MC_ERR_UNSUPPORTED
+    assert call(good, idx=None) == mc.MC_ERR_NULL
+    assert call(good, O_on=None) == mc.MC_ERR_NULL
+    assert call(good, M_lo=None) == mc.MC_ERR_NULL        # bf16 reads the bf16 copy
+    assert call(good, ws_bytes=need - 1) == mc.MC_ERR_WORKSPACE
+    assert call(good, ws=None) == mc.MC_ERR_WORKSPACE
+    assert call(good, Y=MIS) == mc.MC_ERR_ALIGN
+    assert lib.mc_ssc_readout_segs(ctypes.byref(d), None, 2, 4, A, A, A, A, A, A, A, A, A, A,
+                                   need, None) == mc.MC_ERR_NULL
+
+
 def test_swla_scan_arguments():
     # SWLA write path: gates and O_on required, offsets optional and validated like the
     # segment-offset calls; every check happens before any HIP call

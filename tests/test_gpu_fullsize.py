@@ -97,6 +97,35 @@ def test_ssc_full_size():
     torch.cuda.empty_cache()
 
 
+def test_ssc_segment_offsets_full_size():
+    # the SSC workload's shape with random boundaries, as many segments as its constant length
+    # gives (mc_scan_prefill_segs + mc_ssc_readout_segs, the routed read); every head against
+    # the oracle, indices of every token exactly
+    w = WORKLOADS["ssc_bf16_L16K_k4"]
+    n = -(-w.L // w.seg_len)
+    cuts = np.sort(np.random.default_rng(21).choice(np.arange(1, w.L), n - 1, replace=False))
+    off = [0] + cuts.tolist() + [w.L]
+    announce("full-size SSC with offsets: B=%d H=%d L=%d, %d segments, k=%d"
+             % (w.B, w.H, w.L, n, w.top_k))
+    inp = make_prefill_device(w, seed=2)
+    d = mc.make_dims(w.B, w.H, w.L, w.d_k, w.d_v, w.d_g, 1, w.x_heads, w.dtype, w.phi)
+    out = mc.prefill_ssc_segs(d, off, w.top_k, inp["Q"], inp["K"], inp["V"], inp["U"],
+                              inp["X"])
+    torch.cuda.synchronize()
+    host = {k: v.to(torch.float64).cpu().numpy() for k, v in inp.items()}
+    ref = oracle.prefill(host["Q"], host["K"], host["V"], host["U"], host["X"], seg_len=1,
+                         phi=w.phi, mode="ssc", top_k=w.top_k, seg_offsets=off)
+    got_idx = to_np(out["idx"])
+    n_bad = int((got_idx != ref["idx"]).any(axis=-1).sum())
+    announce("  %d tokens with differing indices" % n_bad)
+    np.testing.assert_array_equal(got_idx, ref["idx"])
+    e = slice_rel_err(to_np(out["Y"]), ref["Y"])
+    announce("  Y error %.3g (max over heads)" % e)
+    assert e <= TOL["bf16"]
+    del inp, out, host, ref
+    torch.cuda.empty_cache()
+
+
 def test_decode_full_size():
     """One step of the 64-sequence x 32-head, 256-cached-state workload (no emission), then
     a step that closes the online segment (emission into slot 256) on the same cache."""

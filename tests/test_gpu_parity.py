@@ -375,6 +375,72 @@ def test_grm_segment_offsets(name):
         assert e <= tol, (k, e)
 
 
+# The SSC read over arbitrary boundaries (mc_ssc_readout_segs): bf16 d = 128 runs the routed
+# read, the rest the generic read restricted to the selections; indices bit-exact.
+SSC_SEG_CASES = {
+    "bf16_log_L1000_d128_k3": (Workload("x", 1, 2, 1000, 128, 128, 128, 1, "identity", "bf16",
+                                        top_k=3, op="ssc"), "log"),
+    "bf16_random_L900_d128_elu_k4": (Workload("x", 2, 2, 900, 128, 128, 64, 1, "elu1", "bf16",
+                                              top_k=4, op="ssc"), "random"),
+    "bf16_max_512_segments_L1100_k8": (Workload("x", 1, 2, 1100, 128, 128, 128, 1, "identity",
+                                                "bf16", top_k=8, op="ssc"), "max"),
+    "bf16_long_segments_L2100_k2": (Workload("x", 1, 2, 2100, 128, 128, 128, 1, "identity",
+                                             "bf16", top_k=2, op="ssc"), "long"),
+    "bf16_multiples_of_64_L1024_k16": (Workload("x", 1, 2, 1024, 128, 128, 128, 1, "elu1",
+                                                "bf16", top_k=16, op="ssc"), "c64"),
+    "f32_random_L300_d64_xheadsH_k2": (Workload("x", 1, 2, 300, 64, 64, 64, 1, "identity",
+                                                "f32", x_heads=2, top_k=2, op="ssc"), "random"),
+    "bf16_dk64_dv128_log_L777_k16": (Workload("x", 1, 2, 777, 64, 128, 64, 1, "elu1", "bf16",
+                                              top_k=16, op="ssc"), "log"),
+}
+
+
+@pytest.mark.parametrize("name", list(SSC_SEG_CASES))
+def test_ssc_segment_offsets(name):
+    w, kind = SSC_SEG_CASES[name]
+    if kind == "log":
+        off = oracle.log_segments(w.L)
+    elif kind == "random":
+        off = _random_offsets(w.L, 23, seed=7)
+        off = sorted(set(off + [off[1] + 1]))  # a one-token segment
+    elif kind == "max":
+        off = _random_offsets(w.L, mc.MC_MAX_SEGS, seed=8)
+    elif kind == "long":
+        off = [0, 1500, 1600, w.L]
+    else:
+        off = list(range(0, w.L, 64)) + [w.L]
+    announce("ssc segment offsets %s: %d segments" % (name, len(off) - 1))
+    inp = make_prefill(w, seed=4)
+    d = _dims(w)
+    dev = {k: to_dev(v, w.dtype) for k, v in inp.items()}
+    out = mc.prefill_ssc_segs(d, off, w.top_k, dev["Q"], dev["K"], dev["V"], dev["U"],
+                              dev["X"])
+    torch.cuda.synchronize()
+    ref = oracle.prefill(inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], seg_len=1,
+                         phi=w.phi, mode="ssc", top_k=w.top_k, seg_offsets=off)
+    np.testing.assert_array_equal(to_np(out["idx"]), ref["idx"])
+    e = slice_rel_err(to_np(out["Y"]), ref["Y"])
+    announce("  Y error %.3g" % e)
+    assert e <= TOL[w.dtype]
+
+
+def test_ssc_segment_offsets_at_multiples_of_C_match_constant_read():
+    # boundaries every C tokens select exactly what the constant-length SSC read selects
+    w = Workload("x", 1, 2, 1000, 128, 128, 128, 64, "identity", "bf16", top_k=4, op="ssc")
+    off = list(range(0, w.L, w.seg_len)) + [w.L]
+    announce("ssc offsets at multiples of %d vs the constant read" % w.seg_len)
+    inp = make_prefill(w, seed=9)
+    d = _dims(w)
+    dev = {k: to_dev(v, w.dtype) for k, v in inp.items()}
+    a = mc.prefill_ssc_segs(d, off, w.top_k, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"])
+    b = mc.prefill_ssc(d, w.top_k, dev["Q"], dev["K"], dev["V"], dev["U"], dev["X"])
+    torch.cuda.synchronize()
+    assert torch.equal(a["idx"], b["idx"])
+    e = slice_rel_err(to_np(a["Y"]), to_np(b["Y"]))
+    announce("  Y difference %.3g" % e)
+    assert e <= TOL[w.dtype]
+
+
 def test_grm_segment_offsets_in_kernel_gate():
     # The offsets read given only the constant-length workspace (MC_OP_GRM) forms the gate
     # in-kernel instead of running the gate pass over the offsets; both against the oracle.
