@@ -581,9 +581,11 @@ def run_decode(args, rec, dev):
 
 def run_log_segments(args, rec, dev):
     """The logarithmic segmentation (one segment per set bit of L, largest first) of the L=64K
-    workload's shape at L = 65535 (16 segments of 32768 .. 1 tokens): mc_scan_prefill_segs +
-    mc_grm_readout_segs, inputs resident, tokens/s (bf16 d = 128: the MFMA scan, its 32768-token
-    segment as pieces, and the MFMA read with the segment table)."""
+    workload's shape at L = 65535 (16 segments of 32768 .. 1 tokens): mc_grm_prefill_segs, the
+    one-call prefill (the MFMA scan of the states with the 32768-token segment as pieces, the
+    gate pass, and the MFMA read forming the online term over the pieces), inputs resident,
+    tokens/s; the two-call form (mc_scan_prefill_segs writing O_on + mc_grm_readout_segs)
+    timed beside it."""
     import torch
 
     import chunked_linear_attention_segment_amd as mc
@@ -605,24 +607,33 @@ def run_log_segments(args, rec, dev):
     Y = torch.empty((B, H, L, dv), dtype=torch.bfloat16, device=dev)
     ws = mc.workspace(d, mc.MC_OP_GRM_SEGS, top_k=NS, device=dev)
     wss = mc.workspace_segs(d, NS, device=dev)
+    ws1 = mc.workspace(d, mc.MC_OP_GRM_PREFILL_SEGS, top_k=NS, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
+        mc.mc_grm_prefill_segs(d, off, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"], M,
+                               M_lo, P, Y, None, ws=ws1, stream=stream)
+
+    def step2():
         mc.mc_scan_prefill_segs(d, off, inp["Q"], inp["K"], inp["V"], inp["X"], M, M_lo, P,
                                 O_on, ws=wss, stream=stream)
         mc.mc_grm_readout_segs(d, off, inp["Q"], inp["U"], inp["X"], M, M_lo, P, O_on, Y,
                                None, ws=ws, stream=stream)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = med([a.elapsed_time(b) for a, b in ev])
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return med([a.elapsed_time(b) for a, b in ev])
+    ms = timed(step)
+    ms2 = timed(step2)
     # algorithmic FLOPs: per token, the state update and online read (4 dk dv), the reads of
     # the completed segments before its own (2 dk dv each) and s + 1 gate logits (2 dg each);
     # algorithmic bytes: Q, K, V, U read and Y written once (bf16), X once per sequence, the
@@ -641,11 +652,12 @@ def run_log_segments(args, rec, dev):
                     % NS,
         "metric": "prefill tokens/s", "value": round(B * L / (ms / 1e3), 1), "unit": "tokens/s",
         "ms_per_step": round(ms, 4),
-        "steps_timed": "mc_scan_prefill_segs + mc_grm_readout_segs",
+        "steps_timed": "mc_grm_prefill_segs",
+        "two_calls_ms_per_step": round(ms2, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes": by, "algorithmic_flops": fl}}
-    del inp, M, M_lo, P, O_on, Y, ws, wss
+    del inp, M, M_lo, P, O_on, Y, ws, wss, ws1
     torch.cuda.empty_cache()
 
 

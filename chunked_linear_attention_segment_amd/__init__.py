@@ -8,7 +8,8 @@ Entry points (same names and arguments as include/mc.h; tensors are torch tensor
 GPU, host scalars are Python ints or one-element int32 numpy arrays):
     mc_abi_version, mc_status_str, mc_workspace_bytes,
     mc_scan_prefill, mc_grm_readout, mc_ssc_readout, mc_decode_step,
-    mc_scan_prefill_segs, mc_grm_readout_segs, mc_ssc_readout_segs, mc_scan_prefill_swla,
+    mc_scan_prefill_segs, mc_grm_readout_segs, mc_grm_prefill_segs, mc_ssc_readout_segs,
+    mc_scan_prefill_swla,
     mc_grm_backward, mc_decode_step_noalloc
 plus helpers that allocate outputs / workspaces with torch (memory plumbing only).
 """
@@ -29,11 +30,12 @@ MC_NOALLOC_SCRATCH_BYTES = 64 << 20
 MC_F32, MC_BF16 = 0, 1
 MC_PHI_IDENTITY, MC_PHI_ELU1 = 0, 1
 MC_OP_PREFILL, MC_OP_GRM, MC_OP_SSC, MC_OP_DECODE, MC_OP_GRM_BACKWARD, MC_OP_SCAN_SEGS, \
-    MC_OP_GRM_SEGS, MC_OP_SSC_SEGS = 0, 1, 2, 3, 4, 5, 6, 7
+    MC_OP_GRM_SEGS, MC_OP_SSC_SEGS, MC_OP_GRM_PREFILL_SEGS = 0, 1, 2, 3, 4, 5, 6, 7, 8
 
 EXPORTED = ["mc_abi_version", "mc_status_str", "mc_workspace_bytes", "mc_scan_prefill",
             "mc_grm_readout", "mc_ssc_readout", "mc_decode_step", "mc_scan_prefill_segs",
-            "mc_grm_readout_segs", "mc_ssc_readout_segs", "mc_scan_prefill_swla",
+            "mc_grm_readout_segs", "mc_grm_prefill_segs", "mc_ssc_readout_segs",
+            "mc_scan_prefill_swla",
             "mc_grm_backward", "mc_decode_step_noalloc"]
 MC_MAX_SEGS = 512
 
@@ -80,6 +82,9 @@ def load(path: str = LIB_PATH):
         lib.mc_grm_readout_segs.restype = ctypes.c_int
         lib.mc_grm_readout_segs.argtypes = [D, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
                                             ctypes.c_size_t, P]
+        lib.mc_grm_prefill_segs.restype = ctypes.c_int
+        lib.mc_grm_prefill_segs.argtypes = [D, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P,
+                                            P, ctypes.c_size_t, P]
         lib.mc_ssc_readout_segs.restype = ctypes.c_int
         lib.mc_ssc_readout_segs.argtypes = [D, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P,
                                             P, P, P, P, P, ctypes.c_size_t, P]
@@ -202,6 +207,18 @@ def mc_grm_readout_segs(dims, seg_off, Q, U, X, M, M_lo, P, O_on, Y, gamma=None,
                                       _p(X), _p(M), _p(M_lo), _p(P), _p(O_on), _p(Y),
                                       _p(gamma), w, wb, _stream(stream)),
            "mc_grm_readout_segs")
+
+
+def mc_grm_prefill_segs(dims, seg_off, Q, K, V, U, X, M, M_lo, P, Y, gamma=None, ws=None,
+                        stream=None):
+    """The whole GRM prefill over the segments [seg_off[i], seg_off[i+1]) in one call; ws:
+    mc_workspace_bytes(dims, MC_OP_GRM_PREFILL_SEGS, n) bytes."""
+    off, n = _offsets(seg_off)
+    w, wb = _ws(ws)
+    _check(load().mc_grm_prefill_segs(ctypes.byref(dims), off.ctypes.data, n, _p(Q), _p(K),
+                                      _p(V), _p(U), _p(X), _p(M), _p(M_lo), _p(P), _p(Y),
+                                      _p(gamma), w, wb, _stream(stream)),
+           "mc_grm_prefill_segs")
 
 
 def mc_ssc_readout_segs(dims, seg_off, top_k, Q, U, X, M, M_lo, P, O_on, Y, idx, ws=None,
@@ -342,6 +359,26 @@ def prefill_grm_segs(dims, seg_off, Q, K, V, U, X, want_gamma=False, stream=None
     ws = workspace(dims, MC_OP_GRM_SEGS, top_k=NS, device=dev)
     mc_grm_readout_segs(dims, seg_off, Q, U, X, M, M_lo, P, O_on, Y, G, ws=ws, stream=stream)
     out = {"Y": Y, "M": M, "M_lo": M_lo, "P": P, "O_on": O_on}
+    if want_gamma:
+        out["gamma"] = G
+    return out
+
+
+def prefill_grm_segs_onecall(dims, seg_off, Q, K, V, U, X, want_gamma=False, stream=None):
+    """mc_grm_prefill_segs with fresh outputs (no O_on is handed over)."""
+    import torch
+    NS = len(seg_off) - 1
+    dev = Q.device
+    M = torch.empty((dims.B, dims.H, NS, dims.d_v, dims.d_k), dtype=torch.float32, device=dev)
+    M_lo = torch.empty((dims.B, dims.H, NS, dims.d_v, dims.d_k), dtype=torch.bfloat16,
+                       device=dev)
+    P = torch.empty((dims.B, dims.x_heads, NS, dims.d_g), dtype=torch.float32, device=dev)
+    Y = torch.empty((dims.B, dims.H, dims.L, dims.d_v), dtype=torch_dtype(dims), device=dev)
+    G = torch.empty((dims.B, dims.H, dims.L, NS), dtype=torch.float32,
+                    device=dev) if want_gamma else None
+    ws = workspace(dims, MC_OP_GRM_PREFILL_SEGS, top_k=NS, device=dev)
+    mc_grm_prefill_segs(dims, seg_off, Q, K, V, U, X, M, M_lo, P, Y, G, ws=ws, stream=stream)
+    out = {"Y": Y, "M": M, "M_lo": M_lo, "P": P}
     if want_gamma:
         out["gamma"] = G
     return out

@@ -92,6 +92,30 @@ SscWorkspace ssc_workspace(const mc_dims& d, int top_k, int n_seg) {
     return w;
 }
 
+// The whole prefill over segment offsets in one call: the offsets scan's workspace, then
+// either the bf16 memories before the pieces and the first-piece table (the read forms the
+// online term itself) or the online read O_on (fp32), whichever is larger, then the read's.
+struct PrefillSegsWorkspace {
+    size_t scan, mid, read, total;
+};
+// The pieces over which the read forms the online term: those of the offsets scan (at least
+// 512 tokens; pieces of one 256-token read tile measured no faster, their scan and prefix
+// passes taking what the shorter walks save).
+constexpr int kFusedPiece = 512;
+static PrefillSegsWorkspace prefill_segs_workspace(const mc_dims& d, int n_seg) {
+    PrefillSegsWorkspace w{};
+    w.scan = align256(segs_scan_ws_bytes(d, n_seg) > segs_scan_ws_bytes(d, n_seg, kFusedPiece)
+                          ? segs_scan_ws_bytes(d, n_seg)
+                          : segs_scan_ws_bytes(d, n_seg, kFusedPiece));
+    const size_t pieces =
+        segs_pref_lo_bytes(d, n_seg, kFusedPiece) + align256(sizeof(int32_t) * n_seg);
+    const size_t on = align256(sizeof(float) * (size_t)d.B * d.H * d.L * d.d_v);
+    w.mid = pieces > on ? pieces : on;
+    w.read = grm_workspace(d, n_seg).total;
+    w.total = w.scan + w.mid + w.read;
+    return w;
+}
+
 BwdWorkspace bwd_workspace(const mc_dims& d) {
     BwdWorkspace w{};
     const size_t bhl = (size_t)d.B * d.H * d.L;
@@ -195,6 +219,9 @@ size_t mc_workspace_bytes(const mc_dims* d, mc_op op, int32_t top_k, int32_t n_c
         case MC_OP_GRM_SEGS:
             return top_k >= 1 && top_k <= MC_MAX_SEGS ? grm_workspace(*d, top_k).total : 0;
         case MC_OP_SSC: return top_k >= 1 ? ssc_workspace(*d, top_k).total : 0;
+        case MC_OP_GRM_PREFILL_SEGS:
+            return top_k >= 1 && top_k <= MC_MAX_SEGS ? prefill_segs_workspace(*d, top_k).total
+                                                      : 0;
         case MC_OP_SSC_SEGS:
             return top_k >= 1 && top_k <= 16 && n_cap >= 1 && n_cap <= MC_MAX_SEGS
                        ? ssc_workspace(*d, top_k, n_cap).total
@@ -401,6 +428,65 @@ mc_status mc_grm_readout_segs(const mc_dims* d, const int32_t* seg_off, int32_t 
         gate.pf = g + w.w + w.won + w.inv_l;
     }
     return launch_grm_readout_segs(*d, sg, Q, U, X, M, M_lo, P, O_on, (float*)ws, xps, xtail, Y,
+                                   gamma, stream, gate)
+               ? MC_ERR_HIP
+               : MC_OK;
+}
+
+mc_status mc_grm_prefill_segs(const mc_dims* d, const int32_t* seg_off, int32_t n_seg,
+                              const void* Q, const void* K, const void* V, const void* U,
+                              const void* X, float* M, uint16_t* M_lo, float* P, void* Y,
+                              float* gamma, void* ws, size_t ws_bytes, void* stream) {
+    mc_status st = check_dims(d, true);
+    if (st != MC_OK) return st;
+    SegArg sg;
+    if ((st = check_segs(d, seg_off, n_seg, &sg)) != MC_OK) return st;
+    if (!Q || !K || !V || !U || !X || !M || !P || !Y) return MC_ERR_NULL;
+    if (d->dtype == MC_BF16 && !M_lo) return MC_ERR_NULL;
+    const PrefillSegsWorkspace w = prefill_segs_workspace(*d, n_seg);
+    if (!ws || ws_bytes < w.total) return MC_ERR_WORKSPACE;
+    const void* ptrs[] = {Q, K, V, U, X, M, M_lo, P, Y, gamma, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MC_ERR_ALIGN;
+    char* b = (char*)ws;
+    char* mid = b + w.scan;
+    char* rd = mid + w.mid;
+    const GrmWorkspace rw = grm_workspace(*d, n_seg);
+    float* xps = rw.xps ? (float*)(rd + rw.aon + rw.on) : nullptr;
+    float* xtail = xps ? (float*)((char*)xps + xps_only(*d)) : nullptr;
+    SegGate gate;
+    if (rw.w) {
+        char* g = rd + rw.aon + rw.on + rw.xps;
+        gate.W = (uint16_t*)g;
+        gate.won = (float*)(g + rw.w);
+        gate.inv_l = (float*)(g + rw.w + rw.won);
+        gate.pf = g + rw.w + rw.won + rw.inv_l;
+    }
+    // the read forms the online term itself after the gate pass (bf16, d = 128), walking each
+    // token's piece, when no segment is longer than a piece or the scan cuts the long ones
+    const int pl = scan_piece_len(d->L, n_seg, kFusedPiece);
+    int longest = 0;
+    for (int i = 0; i < n_seg; ++i)
+        if (seg_off[i + 1] - seg_off[i] > longest) longest = seg_off[i + 1] - seg_off[i];
+    const bool fused = gate.W && (pl > 0 || longest <= 1024);
+    if (fused) {
+        uint16_t* pref_lo = (uint16_t*)mid;
+        int32_t* pfirst = (int32_t*)(mid + segs_pref_lo_bytes(*d, n_seg, kFusedPiece));
+        PieceOnline pon;
+        pon.M0 = pref_lo;
+        pon.pfirst = pfirst;
+        if (launch_scan_prefill_segs(*d, sg, Q, K, V, X, M, M_lo, P, nullptr, b, w.scan, stream,
+                                     &pon, pref_lo, pfirst, kFusedPiece))
+            return MC_ERR_HIP;
+        return launch_grm_readout_segs(*d, sg, Q, U, X, M, M_lo, P, nullptr, (float*)rd, xps,
+                                       xtail, Y, gamma, stream, gate, K, V, &pon)
+                   ? MC_ERR_HIP
+                   : MC_OK;
+    }
+    float* O_on = (float*)mid;
+    if (launch_scan_prefill_segs(*d, sg, Q, K, V, X, M, M_lo, P, O_on, b, w.scan, stream))
+        return MC_ERR_HIP;
+    return launch_grm_readout_segs(*d, sg, Q, U, X, M, M_lo, P, O_on, (float*)rd, xps, xtail, Y,
                                    gamma, stream, gate)
                ? MC_ERR_HIP
                : MC_OK;

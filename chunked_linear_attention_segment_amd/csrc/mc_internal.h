@@ -141,6 +141,18 @@ int launch_grm_backward(const mc_dims& d, const BwdBuffers& w, const void* Q, co
                         const uint16_t* M_lo, const float* P, const void* dY, float* dQ,
                         float* dK, float* dV, float* dU, float* dX, void* stream);
 
+// The online term of a read over segment offsets formed in the read from K and V, with long
+// segments cut into pieces of PL tokens from each segment's start: the read walks a token's
+// piece up to the token and adds M0 of the piece, the memory of the segment's earlier pieces
+// (bf16 [B*H][NP][d_v][d_k]; a segment's first piece has none and its entry is not read);
+// pfirst[s] is the index of segment s's first piece.  PL >= L: no segment is cut.
+struct PieceOnline {
+    const uint16_t* M0 = nullptr;
+    const int32_t* pfirst = nullptr;
+    int PL = 1 << 30;
+    int NP = 0;
+};
+
 // Long segments of the offsets scan are cut into pieces (at most scan_piece_len tokens, each
 // inside one segment) that are scanned in parallel; `first` marks the pieces that start a
 // segment.  The pieces' states and their prefix sums within a segment take workspace.
@@ -148,11 +160,19 @@ struct PieceArg {
     SegArg sg;
     uint32_t first[(MC_MAX_SEGS + 32) / 32];
 };
-int scan_piece_len(int L, int n_seg);            // 0: no piece table fits MC_MAX_SEGS
-size_t segs_scan_ws_bytes(const mc_dims& d, int n_seg);
+// pieces of at least pl_min tokens (a power of two)
+int scan_piece_len(int L, int n_seg, int pl_min = 512);  // 0: no piece table fits MC_MAX_SEGS
+size_t segs_scan_ws_bytes(const mc_dims& d, int n_seg, int pl_min = 512);
+// pon given (with O_on NULL): the bf16 memory before each piece goes to pref_lo (half of a
+// state array of the pieces) and the first-piece table to pfirst (n_seg entries), and pon is
+// filled for the read; left as it is when no segment is cut.
 int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
                              const void* V, const void* X, float* M, uint16_t* M_lo, float* P,
-                             float* O_on, void* ws, size_t ws_bytes, void* stream);
+                             float* O_on, void* ws, size_t ws_bytes, void* stream,
+                             PieceOnline* pon = nullptr, uint16_t* pref_lo = nullptr,
+                             int32_t* pfirst = nullptr, int pl_min = 512);
+// the bf16 memories before the pieces (launch_scan_prefill_segs with pon)
+size_t segs_pref_lo_bytes(const mc_dims& d, int n_seg, int pl_min = 512);
 // xps / xtail (nullable: the per-segment walk of aon_kernel is used instead) are workspace for
 // the segment-causal prefix sums of X.
 // the gate pass's buffers for a read with segment offsets (W == nullptr: the in-kernel gate)
@@ -165,7 +185,9 @@ struct SegGate {
 int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* U,
                             const void* X, const float* M, const uint16_t* M_lo, const float* P,
                             const float* O_on, float* aon, float* xps, float* xtail, void* Y,
-                            float* gamma, void* stream, const SegGate& gate = SegGate{});
+                            float* gamma, void* stream, const SegGate& gate = SegGate{},
+                            const void* K = nullptr, const void* V = nullptr,
+                            const PieceOnline* pon = nullptr);
 
 int launch_scan_prefill(const mc_dims& d, const void* Q, const void* K, const void* V,
                         const void* X, float* M, uint16_t* M_lo, float* P, float* O_on,
@@ -194,7 +216,7 @@ int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const
                      const void* V, const void* U, const float* xps, const uint16_t* M_lo,
                      const float* P, const float* O_on, const int32_t* idx,
                      const GateWeights& gw, void* Y, void* stream,
-                     const SegArg* sg = nullptr);
+                     const SegArg* sg = nullptr, const PieceOnline* pon = nullptr);
 
 int launch_grm_readout(const mc_dims& d, const void* Q, const void* K, const void* V,
                        const void* U, const float* aon, const float* xps, const float* M,

@@ -35,6 +35,7 @@
 //      quarter of a B fragment of the next k-step, which the matrix unit hides;
 //   4. y = acc / l_t in bf16 (with the gate pass: staged through LDS into whole-row stores).
 #include <atomic>
+#include <climits>
 #include <type_traits>
 
 #include "common.cuh"
@@ -116,15 +117,17 @@ __device__ __forceinline__ void tile_of_block(int bid, int BH, int T, int& bh, i
 }
 
 // One 256-token tile: flat block index bid (see tile_of_block), LDS at smem_raw.
-template <int DK, int DV, bool SSC, bool FON, int PHI, bool PRE>
+template <int DK, int DV, bool SSC, bool FON, int PHI, bool PRE, bool PCS>
 __device__ __forceinline__ void grm_read_tile(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ U, const float* __restrict__ xps, const bf16_t* __restrict__ S,
     const float* __restrict__ P, const float* __restrict__ O_on,
     const int32_t* __restrict__ idx, const bf16_t* __restrict__ Wg,
     const float* __restrict__ won_g, const float* __restrict__ inv_l_g, int top_k, int BH,
-    int H, int L, int C, int NS, int DG, int xh, bf16_t* __restrict__ Y, const SegArg& sg, char* smem_raw, int bid) {
+    int H, int L, int C, int NS, int DG, int xh, bf16_t* __restrict__ Y, const SegArg& sg,
+    const PieceOnline& pon, char* smem_raw, int bid) {
     static_assert(!(PRE && SSC), "precomputed weights are a GRM mode");
+    static_assert(!PCS || (FON && sizeof(PieceOnline) > 0), "pieces: the online term formed here");
     static_assert(RT == kGateTile, "the gate pass writes weights per read tile");
     constexpr int KS = DK / 16;  // MFMA k-steps over d_k
     constexpr int CB = DV / 32;  // 32-row blocks of the value dimension
@@ -442,16 +445,28 @@ __device__ __forceinline__ void grm_read_tile(
                 qb[tb][ks] = v;
             }
         }
-        const int k_lo = (tile0 / C) * C;
+        // the first key of token t's online walk: its segment's start, or with pieces the start
+        // of its piece (the memory of the segment's earlier pieces is added below from M0)
+        auto base_of = [&](int t) {
+            if constexpr (PCS) {
+                const int f = sg.off[seg_of(sg, t, C)];
+                return f + (t - f) / pon.PL * pon.PL;
+            } else {
+                return (t / C) * C;
+            }
+        };
+        const int k_lo = base_of(tile0);
         const int nkc = (last - k_lo) / 64 + 1;
         const bf16_t* Kbh = K + (size_t)bh * L * DK;
         const bf16_t* Vbh = V + (size_t)bh * L * DV;
-        int tfirst[TB], tlast[TB], tseg0[TB];
+        int tfirst[TB], tlast[TB], tseg0[TB], tsegl[TB], tbase[TB];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
             tfirst[tb] = tile0 + (tl[tb] - l32);          // the 32-token block's first token
             tlast[tb] = min(tfirst[tb] + 31, L - 1);
-            tseg0[tb] = (min(tfirst[tb], L - 1) / C) * C; // segment start of its first token
+            tseg0[tb] = base_of(min(tfirst[tb], L - 1));  // walk start of its first token
+            tsegl[tb] = base_of(tlast[tb]);               // and of its last
+            tbase[tb] = base_of(tok[tb]);                 // and of the lane's token
         }
         // keys of chunk kc -> k[kc & 1]: whole rows per load instruction, chunks XOR-swizzled by
         // row; keys past the last token read token `last` (their scores are masked)
@@ -540,7 +555,7 @@ __device__ __forceinline__ void grm_read_tile(
             for (int tb = 0; tb < TB; ++tb) {
                 // keys all after the block's tokens, or all before its earliest segment start
                 if (k0 > tlast[tb] || k0 + 63 < tseg0[tb]) continue;
-                const bool full = (k0 + 63 <= tfirst[tb]) && (k0 >= (tlast[tb] / C) * C);
+                const bool full = (k0 + 63 <= tfirst[tb]) && (k0 >= tsegl[tb]);
                 // scores S^T = phi(K) phi(Q)^T; K fragments read two k-steps ahead
                 auto kfrag = [&](int ks, int rb) {  // (the key tile holds phi(k))
                     return *reinterpret_cast<const ru32x4_t*>(
@@ -568,7 +583,7 @@ __device__ __forceinline__ void grm_read_tile(
                 // mask to segment(t) start <= key <= t; key = k0 + 4*hi32 + (an immediate)
                 const int t = tok[tb];
                 if (!full) {
-                    const int hi_lim = t - k0 - 4 * hi32, lo_lim = (t / C) * C - k0 - 4 * hi32;
+                    const int hi_lim = t - k0 - 4 * hi32, lo_lim = tbase[tb] - k0 - 4 * hi32;
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -611,6 +626,55 @@ __device__ __forceinline__ void grm_read_tile(
                 }
             }
             if (kc + 1 < nkc) store_v(kc + 1);  // its buffer was last read in chunk kc - 1
+        }
+        if constexpr (PCS) {
+            // the memory of the earlier pieces of the token's segment, M0 of its piece (bf16
+            // [d_v][d_k], none for a segment's first piece), with the online weight:
+            // acc += M0 bf16(won phi(q)).  The wave takes the distinct pieces of its tokens in
+            // ascending order, a token's weight zero outside its own piece.
+            int pc[TB];
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const int f = sg.off[seg[tb]];
+                const int j = (tok[tb] - f) / pon.PL;
+                pc[tb] = (val[tb] && j > 0) ? pon.pfirst[seg[tb]] + j : INT_MAX;
+            }
+            int cur = -1;
+            for (;;) {
+                int nx = INT_MAX;
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+                    if (pc[tb] > cur) nx = min(nx, pc[tb]);
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) nx = min(nx, __shfl_xor(nx, o, 64));
+                if (nx == INT_MAX) break;
+                cur = nx;
+                ru32x4_t qw[TB][KS];
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const float w = pc[tb] == cur ? won[tb] : 0.f;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            qw[tb][ks][e] =
+                                pack_bf16x2(__uint_as_float(qb[tb][ks][e] << 16) * w,
+                                            __uint_as_float(qb[tb][ks][e] & 0xffff0000u) * w);
+                }
+                const bf16_t* m0 = reinterpret_cast<const bf16_t*>(pon.M0) +
+                                   ((size_t)bh * pon.NP + cur) * (size_t)(DV * DK) + l32 * DK +
+                                   hi32 * 8;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const ru32x4_t a =
+                            *reinterpret_cast<const ru32x4_t*>(m0 + cb * 32 * DK + ks * 16);
+#pragma unroll
+                        for (int tb = 0; tb < TB; ++tb)
+                            acc[cb][tb] = mfma_bf16(a, qw[tb][ks], acc[cb][tb]);
+                    }
+            }
         }
         if (PHI == 0) {  // the raw q fragments are phi(q): widen them instead of reloading q
 #pragma unroll
@@ -828,14 +892,15 @@ __device__ __forceinline__ void grm_read_tile(
 // The kernel: one tile per workgroup, or (the precomputed-gate read, with a grid of one
 // workgroup per CU) a share of the tiles per workgroup, taken in turn.  Nothing is shared
 // between tiles but the LDS, which the barrier after each tile hands back.
-template <int DK, int DV, bool SSC, bool FON, int PHI, bool PRE>
+template <int DK, int DV, bool SSC, bool FON, int PHI, bool PRE, bool PCS>
 __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ U, const float* __restrict__ xps, const bf16_t* __restrict__ S,
     const float* __restrict__ P, const float* __restrict__ O_on,
     const int32_t* __restrict__ idx, const bf16_t* __restrict__ Wg,
     const float* __restrict__ won_g, const float* __restrict__ inv_l_g, int top_k, int BH,
-    int H, int L, int C, int NS, int DG, int xh, bf16_t* __restrict__ Y, const SegArg sg) {
+    int H, int L, int C, int NS, int DG, int xh, bf16_t* __restrict__ Y, const SegArg sg,
+    const PieceOnline pon) {
     __shared__ __attribute__((aligned(16))) char smem_raw[sizeof(ReadSmem<DK, DV, SSC>)];
     if constexpr (PRE) {
         const int nblk = BH * ((L + RT - 1) / RT);
@@ -847,15 +912,15 @@ __global__ __launch_bounds__(RTHREADS, 1) void grm_read_kernel(
         for (int k = 0;; ++k) {
             const int bid = (k * W + ((k & 1) ? W - 1 - w : w)) * R + x;
             if (bid >= nblk) break;
-            grm_read_tile<DK, DV, SSC, FON, PHI, PRE>(Q, K, V, U, xps, S, P, O_on, idx, Wg,
-                                                      won_g, inv_l_g, top_k, BH, H, L, C, NS,
-                                                      DG, xh, Y, sg, smem_raw, bid);
+            grm_read_tile<DK, DV, SSC, FON, PHI, PRE, PCS>(Q, K, V, U, xps, S, P, O_on, idx, Wg,
+                                                           won_g, inv_l_g, top_k, BH, H, L, C,
+                                                           NS, DG, xh, Y, sg, pon, smem_raw, bid);
             __syncthreads();
         }
     } else {
-        grm_read_tile<DK, DV, SSC, FON, PHI, PRE>(Q, K, V, U, xps, S, P, O_on, idx, Wg, won_g,
-                                                  inv_l_g, top_k, BH, H, L, C, NS, DG, xh, Y,
-                                                  sg, smem_raw, blockIdx.x);
+        grm_read_tile<DK, DV, SSC, FON, PHI, PRE, PCS>(Q, K, V, U, xps, S, P, O_on, idx, Wg,
+                                                       won_g, inv_l_g, top_k, BH, H, L, C, NS,
+                                                       DG, xh, Y, sg, pon, smem_raw, blockIdx.x);
     }
 }
 
@@ -873,11 +938,11 @@ int cu_count() {
     return n;
 }
 
-template <int DK, int DV, bool SSC, bool FON, int PHI, bool PRE>
+template <int DK, int DV, bool SSC, bool FON, int PHI, bool PRE, bool PCS>
 void launch_k(const mc_dims& d, int top_k, const void* Q, const void* K, const void* V,
               const void* U, const float* xps, const uint16_t* M_lo, const float* P,
               const float* O_on, const int32_t* idx, const GateWeights& gw, void* Y,
-              hipStream_t st, const SegArg& sg) {
+              hipStream_t st, const SegArg& sg, const PieceOnline& pon) {
     const int NS = sg.n ? sg.n : (d.L + d.seg_len - 1) / d.seg_len;
     const int T = (d.L + RT - 1) / RT;
     const int BH = d.B * d.H;
@@ -888,23 +953,36 @@ void launch_k(const mc_dims& d, int top_k, const void* Q, const void* K, const v
         const int ncu = cu_count();
         if (ncu > 0 && grid > ncu) grid = ncu;
     }
-    hipLaunchKernelGGL((grm_read_kernel<DK, DV, SSC, FON, PHI, PRE>), dim3(grid),
+    hipLaunchKernelGGL((grm_read_kernel<DK, DV, SSC, FON, PHI, PRE, PCS>), dim3(grid),
                        dim3(RTHREADS), 0, st, (const bf16_t*)Q, (const bf16_t*)K,
                        (const bf16_t*)V, (const bf16_t*)U, xps, (const bf16_t*)M_lo, P, O_on,
                        idx, (const bf16_t*)gw.W, gw.won, gw.inv_l, top_k, BH, d.H, d.L,
-                       d.seg_len, NS, d.d_g, d.x_heads, (bf16_t*)Y, sg);
+                       d.seg_len, NS, d.d_g, d.x_heads, (bf16_t*)Y, sg, pon);
 }
 
 template <int DK, int DV, bool SSC, bool PRE>
 int launch_t(const mc_dims& d, int top_k, const void* Q, const void* K, const void* V,
              const void* U, const float* xps, const uint16_t* M_lo, const float* P,
              const float* O_on, const int32_t* idx, const GateWeights& gw, void* Y,
-             hipStream_t st, const SegArg& sg) {
+             hipStream_t st, const SegArg& sg, const PieceOnline* pon = nullptr) {
     // the online term is formed in the kernel (from K and V) when the scan did not write it;
     // the feature map is a template argument so the key fragments' loop has no branches
 #define MC_K(FON, PHI)                                                                         \
-    launch_k<DK, DV, SSC, FON, PHI, PRE>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, gw, Y, st, \
-                                         sg)
+    launch_k<DK, DV, SSC, FON, PHI, PRE, false>(d, top_k, Q, K, V, U, xps, M_lo, P, O_on, idx, \
+                                                gw, Y, st, sg, PieceOnline{})
+    if (pon) {  // segment offsets, the online term formed here over pieces
+        if constexpr (PRE && !SSC) {
+            if (d.phi)
+                launch_k<DK, DV, false, true, 1, true, true>(d, 0, Q, K, V, U, xps, M_lo, P,
+                                                             nullptr, idx, gw, Y, st, sg, *pon);
+            else
+                launch_k<DK, DV, false, true, 0, true, true>(d, 0, Q, K, V, U, xps, M_lo, P,
+                                                             nullptr, idx, gw, Y, st, sg, *pon);
+            return (int)hipGetLastError();
+        } else {
+            return -1;
+        }
+    }
     if (O_on) {
         // the SSC kernels that form the gate themselves and take the online term given run out
         // of registers at d_v = 128 (they would spill); their callers take another read
@@ -938,17 +1016,19 @@ static const SegArg kConstSegRd{};  // constant segment length
 int launch_read_mfma(const mc_dims& d, bool ssc, int top_k, const void* Q, const void* K,
                      const void* V, const void* U, const float* xps, const uint16_t* M_lo,
                      const float* P, const float* O_on, const int32_t* idx,
-                     const GateWeights& gw, void* Y, void* stream, const SegArg* sgp) {
+                     const GateWeights& gw, void* Y, void* stream, const SegArg* sgp,
+                     const PieceOnline* pon) {
     if (!read_mfma_covers(d)) return -1;
-    // segment offsets: GRM with the online read given (the fused online term assumes a
-    // constant length; the gate pass takes the offsets too)
-    if (sgp && sgp->n && (ssc || !O_on)) return -1;
+    // segment offsets: GRM with the online read given, or formed here over pieces after the
+    // gate pass (the gate pass takes the offsets too)
+    if (sgp && sgp->n && (ssc || (!O_on && !(pon && gw.W)))) return -1;
+    if (pon && !(sgp && sgp->n)) return -1;
     const SegArg& sg = sgp ? *sgp : kConstSegRd;
     hipStream_t st = (hipStream_t)stream;
     if (gw.W) {  // the gate ran as its own pass (d_k = d_v = 128 GRM)
         if (ssc || d.d_k != 128 || d.d_v != 128) return -1;
         return launch_t<128, 128, false, true>(d, 0, Q, K, V, U, xps, M_lo, P, O_on, idx, gw, Y,
-                                               st, sg);
+                                               st, sg, O_on ? nullptr : pon);
     }
 #define MC_RD(DK, DV)                                                                          \
     if (d.d_k == DK && d.d_v == DV)                                                            \

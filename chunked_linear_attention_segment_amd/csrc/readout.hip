@@ -475,7 +475,8 @@ __global__ void gamma_kernel(const T* __restrict__ U, const float* __restrict__ 
 int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* U,
                             const void* X, const float* M, const uint16_t* M_lo, const float* P,
                             const float* O_on, float* aon, float* xps, float* xtail, void* Y,
-                            float* gamma, void* stream, const SegGate& gate) {
+                            float* gamma, void* stream, const SegGate& gate, const void* K,
+                            const void* V, const PieceOnline* pon) {
     hipStream_t st = (hipStream_t)stream;
     int rc;
     auto logits = [&]() {  // the online logits token by token from the prefix sums
@@ -503,8 +504,9 @@ int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, c
             gw.won = gate.won;
             gw.inv_l = gate.inv_l;
         }
-        rc = launch_read_mfma(d, false, 0, Q, nullptr, nullptr, U, xps, M_lo, P, O_on, nullptr,
-                              gw, Y, stream, &sg);
+        // (without O_on: the online term formed in the read over pieces, pon)
+        rc = launch_read_mfma(d, false, 0, Q, K, V, U, xps, M_lo, P, O_on, nullptr, gw, Y, stream,
+                              &sg, O_on ? nullptr : pon);
         if (rc >= 0) {
             if (rc || !gamma) return rc;
             if ((rc = logits())) return rc;
@@ -513,6 +515,7 @@ int launch_grm_readout_segs(const mc_dims& d, const SegArg& sg, const void* Q, c
                                d.H, d.x_heads, gamma, sg);
             return (int)hipGetLastError();
         }
+        if (!O_on) return (int)hipErrorInvalidValue;  // the generic read takes O_on
         rc = logits();  // not covered: the generic read below
     } else {
         rc = launch_aon_sg(d, X, U, aon, sg, st);

@@ -228,13 +228,17 @@ __device__ __forceinline__ int piece_end(const PieceArg& pa, int j, int NP) {
 // is issued before the first sum (rows past the segment's last piece are read clamped to it
 // and not used).  The segment is the slowest grid index, so the workgroups of the first
 // segments, which walk the most pieces when the segments shrink along the sequence, are
-// dispatched first.
+// dispatched first.  Pref (fp32, for the online scan) and Pref_lo (bf16, for a read that
+// forms the online term itself) are each written when given; so is pfirst[s], the index of
+// segment s's first piece.
 template <int DK, int DV>
 __global__ __launch_bounds__(128) void piece_prefix_kernel(const float* __restrict__ Msub,
                                                            int NP, const PieceArg pa, int NS,
                                                            float* __restrict__ Pref,
                                                            float* __restrict__ M,
-                                                           bf16_t* __restrict__ M_lo) {
+                                                           bf16_t* __restrict__ M_lo,
+                                                           bf16_t* __restrict__ Pref_lo,
+                                                           int32_t* __restrict__ pfirst) {
     constexpr int N = DV * DK;
     constexpr int BATCH = 16;
     const int seg = blockIdx.z;  // slowest: the longest segments (the first) start first
@@ -242,6 +246,7 @@ __global__ __launch_bounds__(128) void piece_prefix_kernel(const float* __restri
     const size_t bh = blockIdx.y;
     const int e0 = blockIdx.x * 512 + 4 * threadIdx.x;
     const int jend = piece_end(pa, j, NP);
+    if (pfirst && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) pfirst[seg] = j;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int b = j; b < jend; b += BATCH) {
         float4 v[BATCH];
@@ -251,7 +256,14 @@ __global__ __launch_bounds__(128) void piece_prefix_kernel(const float* __restri
 #pragma unroll
         for (int i = 0; i < BATCH; ++i)
             if (b + i < jend) {
-                *reinterpret_cast<float4*>(Pref + (bh * NP + b + i) * (size_t)N + e0) = acc;
+                if (Pref)
+                    *reinterpret_cast<float4*>(Pref + (bh * NP + b + i) * (size_t)N + e0) = acc;
+                if (Pref_lo) {
+                    uint2 a;
+                    a.x = pack_bf16x2(acc.x, acc.y);
+                    a.y = pack_bf16x2(acc.z, acc.w);
+                    *reinterpret_cast<uint2*>(Pref_lo + (bh * NP + b + i) * (size_t)N + e0) = a;
+                }
                 acc.x += v[i].x;
                 acc.y += v[i].y;
                 acc.z += v[i].z;
@@ -290,8 +302,8 @@ __global__ __launch_bounds__(256) void piece_means_kernel(const float* __restric
     }
 }
 
-int scan_piece_len(int L, int n_seg) {
-    for (int pl = 512; pl > 0 && pl <= (1 << 30); pl <<= 1)
+int scan_piece_len(int L, int n_seg, int pl_min) {
+    for (int pl = pl_min; pl > 0 && pl <= (1 << 30); pl <<= 1)
         if (n_seg + (L + pl - 1) / pl <= MC_MAX_SEGS) return pl;
     return 0;
 }
@@ -301,23 +313,32 @@ int scan_piece_len(int L, int n_seg) {
 static size_t segs_state_bytes(const mc_dims& d, size_t np) {
     return align256(sizeof(float) * (size_t)d.B * d.H * np * d.d_v * d.d_k);
 }
-size_t segs_scan_ws_bytes(const mc_dims& d, int n_seg) {
+size_t segs_scan_ws_bytes(const mc_dims& d, int n_seg, int pl_min) {
     const bool mfma = d.dtype == MC_BF16 && (d.d_k == 64 || d.d_k == 128) &&
                       (d.d_v == 64 || d.d_v == 128);
-    const int pl = scan_piece_len(d.L, n_seg);
+    const int pl = scan_piece_len(d.L, n_seg, pl_min);
     if (!mfma || !pl) return 0;
     const size_t np = (size_t)n_seg + (d.L + pl - 1) / pl;
     return 2 * segs_state_bytes(d, np) +
            align256(sizeof(float) * (size_t)d.B * d.x_heads * np * d.d_g);
 }
 
+size_t segs_pref_lo_bytes(const mc_dims& d, int n_seg, int pl_min) {
+    const int pl = scan_piece_len(d.L, n_seg, pl_min);
+    if (!pl) return 0;
+    const size_t np = (size_t)n_seg + (d.L + pl - 1) / pl;
+    return align256(sizeof(uint16_t) * (size_t)d.B * d.H * np * d.d_v * d.d_k);
+}
+
 template <int DK, int DV>
 static int launch_pieces_t(const mc_dims& d, const PieceArg& pa, int NS, float* Msub,
-                           float* Pref, float* M, uint16_t* M_lo, hipStream_t st) {
+                           float* Pref, float* M, uint16_t* M_lo, uint16_t* Pref_lo,
+                           int32_t* pfirst, hipStream_t st) {
     const int NP = pa.sg.n;
     static_assert(DV * DK % 512 == 0, "512-element slices");
     hipLaunchKernelGGL((piece_prefix_kernel<DK, DV>), dim3(DV * DK / 512, d.B * d.H, NS),
-                       dim3(128), 0, st, Msub, NP, pa, NS, Pref, M, (bf16_t*)M_lo);
+                       dim3(128), 0, st, Msub, NP, pa, NS, Pref, M, (bf16_t*)M_lo,
+                       (bf16_t*)Pref_lo, pfirst);
     return (int)hipGetLastError();
 }
 
@@ -326,13 +347,14 @@ static int launch_pieces_t(const mc_dims& d, const PieceArg& pa, int NS, float* 
 // then the means over each segment (split: over the pieces, then combined per segment).
 int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, const void* K,
                              const void* V, const void* X, float* M, uint16_t* M_lo, float* P,
-                             float* O_on, void* ws, size_t ws_bytes, void* stream) {
+                             float* O_on, void* ws, size_t ws_bytes, void* stream,
+                             PieceOnline* pon, uint16_t* pref_lo, int32_t* pfirst, int pl_min) {
     hipStream_t st = (hipStream_t)stream;
     int rc = -1;
-    const int pl = scan_piece_len(d.L, sg.n);
+    const int pl = scan_piece_len(d.L, sg.n, pl_min);
     bool split = false;
     for (int i = 0; pl && i < sg.n; ++i) split |= sg.off[i + 1] - sg.off[i] > pl;
-    const size_t need = segs_scan_ws_bytes(d, sg.n);
+    const size_t need = segs_scan_ws_bytes(d, sg.n, pl_min);
     PieceArg piece{};
     float* Pm = nullptr;  // the pieces' means of X, when the scan ran over pieces
     if (split && need && ws && ws_bytes >= need) {
@@ -352,14 +374,25 @@ int launch_scan_prefill_segs(const mc_dims& d, const SegArg& sg, const void* Q, 
         rc = launch_scan_mfma_segs(d, piece.sg, Q, K, V, Msub, nullptr, nullptr, stream);
         if (rc >= 0) {
             if (rc) return rc;
+            // the fp32 memory before each piece for the online scan, or its bf16 copy for a
+            // read that forms the online term itself
+            float* pr = O_on ? Pref : nullptr;
+            uint16_t* pl16 = pon ? pref_lo : nullptr;
+            int32_t* pf = pon ? pfirst : nullptr;
             if (d.d_k == 128 && d.d_v == 128)
-                rc = launch_pieces_t<128, 128>(d, piece, sg.n, Msub, Pref, M, M_lo, st);
+                rc = launch_pieces_t<128, 128>(d, piece, sg.n, Msub, pr, M, M_lo, pl16, pf, st);
             else if (d.d_k == 128)
-                rc = launch_pieces_t<128, 64>(d, piece, sg.n, Msub, Pref, M, M_lo, st);
+                rc = launch_pieces_t<128, 64>(d, piece, sg.n, Msub, pr, M, M_lo, pl16, pf, st);
             else if (d.d_v == 128)
-                rc = launch_pieces_t<64, 128>(d, piece, sg.n, Msub, Pref, M, M_lo, st);
+                rc = launch_pieces_t<64, 128>(d, piece, sg.n, Msub, pr, M, M_lo, pl16, pf, st);
             else
-                rc = launch_pieces_t<64, 64>(d, piece, sg.n, Msub, Pref, M, M_lo, st);
+                rc = launch_pieces_t<64, 64>(d, piece, sg.n, Msub, pr, M, M_lo, pl16, pf, st);
+            if (!rc && pon) {
+                pon->M0 = pref_lo;
+                pon->pfirst = pfirst;
+                pon->PL = pl;
+                pon->NP = np;
+            }
             if (!rc && O_on)
                 rc = launch_scan_mfma_segs(d, piece.sg, Q, K, V, nullptr, nullptr, O_on, stream,
                                            Pref);

@@ -83,7 +83,8 @@ typedef enum {
     MC_OP_GRM_BACKWARD = 4,
     MC_OP_SCAN_SEGS = 5,
     MC_OP_GRM_SEGS = 6,
-    MC_OP_SSC_SEGS = 7
+    MC_OP_SSC_SEGS = 7,
+    MC_OP_GRM_PREFILL_SEGS = 8
 } mc_op;
 
 /* Problem sizes.  Supported by this library: d_k, d_v in {64, 128}; 1 <= d_g <= 256 and
@@ -108,7 +109,8 @@ const char* mc_status_str(mc_status status);
 /* Workspace bytes an operation needs for these sizes (top_k is used by MC_OP_SSC, n_cap by
  * MC_OP_DECODE; MC_OP_SCAN_SEGS, the segment-offset write path, and MC_OP_GRM_SEGS, the
  * segment-offset read, take the number of segments in top_k; MC_OP_SSC_SEGS, the
- * segment-offset SSC read, takes top_k in top_k and the number of segments in n_cap).
+ * segment-offset SSC read, takes top_k in top_k and the number of segments in n_cap;
+ * MC_OP_GRM_PREFILL_SEGS, the one-call prefill over offsets, the number of segments in top_k).
  * Returns 0 when no workspace is needed or the sizes are invalid. */
 size_t mc_workspace_bytes(const mc_dims* dims, mc_op op, int32_t top_k, int32_t n_cap);
 
@@ -264,6 +266,24 @@ mc_status mc_scan_prefill_segs(const mc_dims* dims, const int32_t* seg_off, int3
 mc_status mc_grm_readout_segs(const mc_dims* dims, const int32_t* seg_off, int32_t n_seg,
                               const void* Q, const void* U, const void* X, const float* M,
                               const uint16_t* M_lo, const float* P, const float* O_on, void* Y,
+                              float* gamma, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mc_grm_prefill_segs -- the whole GRM prefill over segment offsets in one call: the write
+ * path of mc_scan_prefill_segs (M, M_lo, P) and the read of mc_grm_readout_segs (Y, gamma),
+ * with the same offsets, arguments and errors, except that no online read O_on is handed over:
+ * for bf16 with d_k = d_v = 128 (after the gate pass) the read forms the online term
+ * M_t^(s) phi(q_t) itself from K and V (Memory Caching paper §3.1, Eq. 8), walking the keys of
+ * the token's piece -- long segments are cut into pieces as in mc_scan_prefill_segs -- and
+ * adding the memory of the segment's earlier pieces, so the sequence is scanned once.  Other
+ * sizes, and segmentations with a segment longer than 1024 tokens that no piece length
+ * cuts, form O_on in the workspace and read it.
+ *   ws  mc_workspace_bytes(dims, MC_OP_GRM_PREFILL_SEGS, n_seg, 0) bytes (it holds the scan's
+ *       pieces, the memories before them or O_on, and the read's buffers).
+ */
+mc_status mc_grm_prefill_segs(const mc_dims* dims, const int32_t* seg_off, int32_t n_seg,
+                              const void* Q, const void* K, const void* V, const void* U,
+                              const void* X, float* M, uint16_t* M_lo, float* P, void* Y,
                               float* gamma, void* ws, size_t ws_bytes, void* stream);
 
 /*

@@ -256,6 +256,40 @@ def test_segment_offsets_are_validated():
     assert read(good, Y=MIS) == mc.MC_ERR_ALIGN
 
 
+def test_prefill_segs_one_call_arguments():
+    # the one-call prefill over offsets: validation as the two calls it replaces, no O_on
+    # argument; its workspace holds the scan's pieces, the memories before them (or O_on) and
+    # the read's buffers
+    d = dims(L=1000)
+    lib = mc.load()
+    good = [0, 512, 768, 896, 960, 992, 1000]
+    n = len(good) - 1
+    need = mc.mc_workspace_bytes(d, mc.MC_OP_GRM_PREFILL_SEGS, n)
+    assert need >= (mc.mc_workspace_bytes(d, mc.MC_OP_SCAN_SEGS, n)
+                    + mc.mc_workspace_bytes(d, mc.MC_OP_GRM_SEGS, n)
+                    + 4 * d.B * d.H * d.L * d.d_v)
+    assert mc.mc_workspace_bytes(d, mc.MC_OP_GRM_PREFILL_SEGS, 0) == 0
+    assert mc.mc_workspace_bytes(d, mc.MC_OP_GRM_PREFILL_SEGS, mc.MC_MAX_SEGS + 1) == 0
+
+    def call(off, ws_bytes=need, **kw):
+        off = np.ascontiguousarray(np.asarray(off, dtype=np.int32))
+        p = dict(Q=A, K=A, V=A, U=A, X=A, M=A, M_lo=A, P=A, Y=A, gamma=None, ws=A)
+        p.update(kw)
+        return lib.mc_grm_prefill_segs(ctypes.byref(d), off.ctypes.data, off.shape[0] - 1,
+                                       p["Q"], p["K"], p["V"], p["U"], p["X"], p["M"],
+                                       p["M_lo"], p["P"], p["Y"], p["gamma"], p["ws"],
+                                       ws_bytes, None)
+    for bad in ([0, 512, 512, 1000], [1, 512, 1000], [0, 512, 999], [0]):
+        assert call(bad) == mc.MC_ERR_DIMS, bad
+    assert call(list(range(1000)) + [1000]) == mc.MC_ERR_UNSUPPORTED
+    assert call(good, K=None) == mc.MC_ERR_NULL
+    assert call(good, M=None) == mc.MC_ERR_NULL
+    assert call(good, M_lo=None) == mc.MC_ERR_NULL
+    assert call(good, ws_bytes=need - 1) == mc.MC_ERR_WORKSPACE
+    assert call(good, ws=None) == mc.MC_ERR_WORKSPACE
+    assert call(good, gamma=MIS) == mc.MC_ERR_ALIGN
+
+
 def test_ssc_segment_offsets_arguments():
     # the SSC read over arbitrary boundaries: offsets validated as for the GRM read, top_k as
     # for mc_ssc_readout, O_on required; its workspace holds the online logits, the fp64

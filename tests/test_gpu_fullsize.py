@@ -177,19 +177,26 @@ def test_decode_full_size():
     torch.cuda.empty_cache()
 
 
-def test_log_segments_full_size():
-    # the logarithmic segmentation at the L=64K workload's shape, L = 65535 (16 segments), as
-    # the benchmark times it (mc_scan_prefill_segs + mc_grm_readout_segs)
+@pytest.mark.parametrize("calls", ["two_calls", "one_call"])
+def test_log_segments_full_size(calls):
+    # the logarithmic segmentation at the L=64K workload's shape, L = 65535 (16 segments):
+    # mc_scan_prefill_segs + mc_grm_readout_segs, and mc_grm_prefill_segs as the benchmark
+    # times it (the read forms the online term over the 512-token pieces of the long segments)
     w = WORKLOADS["grm_bf16_L64K"]
     L = 65535
     off = oracle.log_segments(L)
-    announce("full-size log segmentation: H=%d L=%d, %d segments" % (w.H, L, len(off) - 1))
+    announce("full-size log segmentation (%s): H=%d L=%d, %d segments"
+             % (calls, w.H, L, len(off) - 1))
     inp = make_prefill_device(w, seed=0, L=L)
     d = mc.make_dims(w.B, w.H, L, w.d_k, w.d_v, w.d_g, 1, 1, w.dtype, w.phi)
-    out = mc.prefill_grm_segs(d, off, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"])
+    run = mc.prefill_grm_segs if calls == "two_calls" else mc.prefill_grm_segs_onecall
+    out = run(d, off, inp["Q"], inp["K"], inp["V"], inp["U"], inp["X"])
     torch.cuda.synchronize()
     assert torch.isfinite(out["Y"].float()).all()
+    # segment boundaries, the ends and starts of the 512-token pieces of the longest segment,
+    # seeded random rows
     rows = np.unique(np.concatenate([np.array(off[1:-1]) - 1, np.array(off[1:-1]),
+                                     np.arange(511, off[1], 512), np.arange(512, off[1], 512),
                                      np.random.default_rng(11).integers(0, L, 200)])
                      ).astype(np.int32)
     for b, h in [(0, 0), (0, 17)]:
