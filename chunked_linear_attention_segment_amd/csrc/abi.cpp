@@ -57,6 +57,7 @@ SscWorkspace ssc_workspace(const mc_dims& d, int top_k, int n_seg) {
         // offsets: the caller's online read; the online logits, the means, and the routed
         // read's tables where it applies (else the generic read needs nothing more)
         w.xsum64 = align256(ssc_means_bytes(d, n_seg));
+        w.xps = xps_only(d) + align256(sizeof(float) * xps_tail_floats(d));
         if (ssc_gather_covers(d, top_k, n_seg)) {
             const size_t tiles = (size_t)d.B * d.H * ((d.L + kSscTile - 1) / kSscTile);
             w.won = align256(sizeof(float) * bhl);
@@ -65,7 +66,7 @@ SscWorkspace ssc_workspace(const mc_dims& d, int top_k, int n_seg) {
             w.poff = align256(sizeof(int32_t) * tiles * (n_seg + 1));
             w.sf = align256(ssc_frag_states_bytes(d, n_seg));
         }
-        w.total = w.aon + w.xsum64 + w.won + w.ptok + w.pw + w.poff + w.sf;
+        w.total = w.aon + w.xsum64 + w.xps + w.won + w.ptok + w.pw + w.poff + w.sf;
         return w;
     }
     w.on = online_ws(d);
@@ -512,11 +513,13 @@ mc_status mc_ssc_readout_segs(const mc_dims* d, const int32_t* seg_off, int32_t 
         if (p && !aligned16(p)) return MC_ERR_ALIGN;
     float* aon = (float*)ws;
     double* xsum64 = (double*)((char*)ws + w.aon);
-    if (launch_aon_segs(*d, sg, X, U, aon, stream)) return MC_ERR_HIP;
+    float* xps = (float*)((char*)ws + w.aon + w.xsum64);
+    if (launch_aon_segs(*d, sg, X, U, aon, stream, xps, (float*)((char*)xps + xps_only(*d))))
+        return MC_ERR_HIP;
     if (ssc_gather_covers(*d, top_k, n_seg)) {
         // routed: the selection with its weights and the tiles' pairs sorted by segment, then
         // only the selected states are read
-        char* g = (char*)ws + w.aon + w.xsum64;
+        char* g = (char*)ws + w.aon + w.xsum64 + w.xps;
         SscRoute rt;
         rt.aon = aon;
         rt.won = (float*)g;

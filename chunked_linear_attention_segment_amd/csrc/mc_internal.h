@@ -248,8 +248,10 @@ int launch_ssc_gather(const mc_dims& d, int top_k, const void* Q, const uint16_t
                       const float* O_on, const SscRoute& rt, void* Y, void* stream,
                       const SegArg* sg = nullptr);
 // segment offsets: the online logits, and the generic read restricted to idx
+// (xps given: through the segment-causal prefix sums of X, tails as for launch_xps, else one
+// workgroup walks each segment)
 int launch_aon_segs(const mc_dims& d, const SegArg& sg, const void* X, const void* U,
-                    float* a_on, void* stream);
+                    float* a_on, void* stream, float* xps = nullptr, float* tails = nullptr);
 int launch_ssc_readout_segs(const mc_dims& d, const SegArg& sg, int top_k, const void* Q,
                             const void* U, const float* aon, const float* M,
                             const uint16_t* M_lo, const float* P, const float* O_on,

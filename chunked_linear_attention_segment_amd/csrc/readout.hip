@@ -241,10 +241,16 @@ __global__ __launch_bounds__(256) void aon_xps_kernel(const T* __restrict__ U,
     const bool valid = t < L;
     const int tc = valid ? t : L - 1;
     const int j = tc - seg_first(sg, seg_of(sg, tc, C), C);
-    const int gch = DG / 8;
+    // thread p takes the 8-element slices p, p + 8, ... of the gate width (16-byte loads of U,
+    // 32-byte loads of the prefix sums)
     float a = 0.f;
-    for (int e = p * gch; e < (p + 1) * gch; ++e)
-        a += ld(U, (bh * L + tc) * DG + e) * xps[(bx * L + tc) * DG + e];
+    for (int e = 8 * p; e < DG; e += 64) {
+        float u[8], x[8];
+        ld8(U + (bh * L + tc) * DG, (size_t)e, u);
+        ld8(xps + (bx * L + tc) * DG, (size_t)e, x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a += u[k] * x[k];
+    }
     a = warp_sum(a, 8);
     if (valid && p == 0) a_on[bh * L + t] = a / (float)(j + 1);
 }
@@ -566,8 +572,20 @@ int launch_ssc_readout_segs(const mc_dims& d, const SegArg& sg, int top_k, const
 }
 
 int launch_aon_segs(const mc_dims& d, const SegArg& sg, const void* X, const void* U,
-                    float* a_on, void* stream) {
-    return launch_aon_sg(d, X, U, a_on, sg, (hipStream_t)stream);
+                    float* a_on, void* stream, float* xps, float* tails) {
+    hipStream_t st = (hipStream_t)stream;
+    if (!xps) return launch_aon_sg(d, X, U, a_on, sg, st);
+    // through the prefix sums: the work per token does not depend on its segment's length
+    int rc = launch_xps_sg(d, X, xps, tails, sg, st);
+    if (rc) return rc;
+    const dim3 grid((d.L + 31) / 32, d.B * d.H);
+    if (d.dtype == MC_BF16)
+        hipLaunchKernelGGL(aon_xps_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)U, xps,
+                           d.L, d.seg_len, d.d_g, d.H, d.x_heads, a_on, sg);
+    else
+        hipLaunchKernelGGL(aon_xps_kernel<float>, grid, dim3(256), 0, st, (const float*)U, xps,
+                           d.L, d.seg_len, d.d_g, d.H, d.x_heads, a_on, sg);
+    return (int)hipGetLastError();
 }
 
 int launch_ssc_readout(const mc_dims& d, int top_k, const void* Q, const void* K,
