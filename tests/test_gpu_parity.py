@@ -341,6 +341,10 @@ SEG_CASES = {
                                  "long"),
     "bf16_long_segments_d64_elu_xheadsH": (Workload("x", 1, 2, 1700, 64, 64, 64, 1, "elu1",
                                                     "bf16", x_heads=2), "long"),
+    # 511 one-token segments and one of 1589: no piece table fits, so the one call forms O_on
+    # in its workspace instead of walking the long segment in the read
+    "bf16_512_segments_one_long_L2100": (Workload("x", 1, 2, 2100, 128, 128, 128, 1,
+                                                  "identity", "bf16"), "max_long"),
 }
 
 
@@ -359,6 +363,8 @@ def test_grm_segment_offsets(name, calls):
         off = _random_offsets(w.L, mc.MC_MAX_SEGS, seed=6)  # the most segments a call takes
     elif kind == "long":
         off = [0, 1500, 1600, w.L]  # 3 pieces, 1 piece, 1 or 2 pieces
+    elif kind == "max_long":
+        off = list(range(0, mc.MC_MAX_SEGS)) + [w.L]
     else:
         off = list(range(0, w.L, 64)) + [w.L]
     announce("grm segment offsets %s (%s): %d segments" % (name, calls, len(off) - 1))
